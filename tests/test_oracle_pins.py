@@ -1,0 +1,493 @@
+"""Pins for the CPU oracle: each checks it against something other than itself
+(printed values, closed forms, textbook tables, library routines, invariants,
+exact expectations).  No GPU needed."""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.linalg
+import scipy.stats
+from scipy.integrate import quad
+
+import oracle.tq_oracle as O
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _gold(name):
+    with open(os.path.join(GOLD, name)) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------- generator
+
+def test_splitmix64_published_vector():
+    g = _gold("lloyd_max_textbook.json")["splitmix64"]
+    assert O.splitmix64_stream(g["seed"], 0, 5) == [int(x) for x in g["outputs"]]
+
+
+def test_rademacher_signs_are_pm1_and_balanced():
+    s = O.rademacher_signs(42, O.TAG_SIGMA, 8192)
+    assert set(np.unique(s)) <= {-1.0, 1.0}
+    assert abs(s.mean()) < 4.0 / math.sqrt(8192)
+    # different tags give different streams
+    assert not np.array_equal(O.rademacher_signs(42, 1, 128), O.rademacher_signs(42, 3, 128))
+
+
+def test_gaussian_matrix_is_standard_normal():
+    S = O.gaussian_matrix(42, O.TAG_S, 128, 128)
+    x = S.ravel()
+    assert np.all(x.astype(np.float32) == x)          # float32 values
+    assert scipy.stats.kstest(x, "norm").pvalue > 1e-3
+    assert abs(x.mean()) < 4 / math.sqrt(x.size)
+    assert abs(x.var() - 1) < 4 * math.sqrt(2 / x.size)
+    # Box-Muller pairs are uncorrelated
+    assert abs(np.corrcoef(x[0::2], x[1::2])[0, 1]) < 4 / math.sqrt(x.size / 2)
+
+
+# ---------------------------------------------------------------- codebook
+
+def test_codebook_two_levels_closed_form():
+    c, t, D = O.lloyd_max_gaussian(2)
+    assert np.allclose(c, [-math.sqrt(2 / math.pi), math.sqrt(2 / math.pi)], atol=1e-14)
+    assert t[0] == 0.0
+    assert abs(D - (1 - 2 / math.pi)) < 1e-14
+
+
+@pytest.mark.parametrize("L", [4, 8])
+def test_codebook_matches_max_1960(L):
+    g = _gold("lloyd_max_textbook.json")["levels_%d" % L]
+    c, t, D = O.lloyd_max_gaussian(L)
+    assert np.allclose(c[L // 2:], g["centroids_pos"], atol=g["tol"])
+    assert np.allclose(t[L // 2:], g["boundary_pos"], atol=g["tol"])
+    assert abs(D - g["D"]) < g["tol"]
+
+
+def test_codebook_16_levels_D():
+    g = _gold("lloyd_max_textbook.json")["levels_16"]
+    assert abs(O.lloyd_max_gaussian(16)[2] - g["D"]) < g["tol"]
+
+
+def test_codebook_table1_band():
+    g = _gold("lloyd_max_textbook.json")["table1_pages"]
+    lo, hi = g["ratio_band"]
+    for b, expected in g["values"].items():
+        _, _, D = O.codebook(int(b))
+        assert lo <= D / expected <= hi, (b, D)
+
+
+@pytest.mark.parametrize("b", [1, 2, 3, 4, 5, 6, 7, 8])
+def test_codebook_fixed_point_and_symmetry(b):
+    """Lloyd-Max conditions checked by numerical integration (scipy.quad), an
+    independent route from the erf-based update the solver iterates."""
+    L = 1 << b
+    c, t, D = O.lloyd_max_gaussian(L)
+    assert np.array_equal(c, -c[::-1])
+    assert np.all(np.diff(c) > 0)
+    assert np.allclose(t, 0.5 * (c[:-1] + c[1:]), atol=1e-15, rtol=0)
+    assert t[L // 2 - 1] == 0.0
+    lo = np.concatenate(([-np.inf], t))
+    hi = np.concatenate((t, [np.inf]))
+    pdf = lambda x: math.exp(-0.5 * x * x) / math.sqrt(2 * math.pi)
+    ks = range(L) if L <= 16 else list(range(0, L, 17)) + [L - 1]
+    for k in ks:
+        m0 = quad(pdf, lo[k], hi[k], epsabs=0, epsrel=1e-12)[0]
+        m1 = quad(lambda x: x * pdf(x), lo[k], hi[k], epsabs=0, epsrel=1e-12)[0]
+        assert abs(m1 / m0 - c[k]) < 1e-9 * max(1.0, abs(c[k])), (b, k)
+    # D by the identity D = 1 - sum c_k^2 P_k at the fixed point
+    P = np.array([quad(pdf, lo[k], hi[k], epsabs=0, epsrel=1e-12)[0] for k in range(L)])
+    assert abs(D - (1 - np.sum(c * c * P))) < 1e-9
+
+
+def test_codebook_b8_below_theorem1_bound():
+    coef = _gold("lloyd_max_textbook.json")["theorem1_pages"]["coef"]
+    for b in range(1, 9):
+        _, _, D = O.codebook(b)
+        assert D <= coef * 4.0 ** (-b)
+    assert abs(O.codebook(8)[2] - 4.1185e-5) < 1e-8
+
+
+def test_codebook_independent_of_start():
+    """The fixed point does not depend on the start: plain Lloyd iteration from
+    uniform quantiles reaches the same centroids (8 levels)."""
+    from scipy.special import ndtri
+    L = 8
+    c = ndtri((np.arange(L) + 0.5) / L) * 1.7
+    for _ in range(3000):
+        c, _, _, _ = O._lloyd_map(c)
+    ref, _, _ = O.lloyd_max_gaussian(L)
+    assert np.allclose(c, ref, atol=1e-10)
+
+
+# ---------------------------------------------------------------- rotation
+
+@pytest.mark.parametrize("d", [2, 8, 64, 128])
+def test_hadamard_is_sylvester(d):
+    assert np.array_equal(O.hadamard(d), scipy.linalg.hadamard(d).astype(np.float64))
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_rotation_orthogonal(d):
+    Pi = O.rotation_matrix(O.rademacher_signs(7, O.TAG_SIGMA, d))
+    assert np.abs(Pi @ Pi.T - np.eye(d)).max() < 1e-12
+    # all-plus signs reduce to the normalised Hadamard matrix
+    assert np.allclose(O.rotation_matrix(np.ones(d)), scipy.linalg.hadamard(d) / math.sqrt(d))
+
+
+def test_rotated_unit_vector_has_norm_sqrt_d():
+    T = O.build_tables(O.KeyConfig(mode="mse", bits=4))
+    k = np.random.default_rng(0).standard_normal((10, 128)) * 7
+    enc = O.encode_keys(k, T)
+    assert np.allclose(np.linalg.norm(enc["y"], axis=1), math.sqrt(128), rtol=1e-12)
+    assert np.allclose(enc["norm"], np.linalg.norm(k, axis=1), rtol=1e-14)
+
+
+# ---------------------------------------------------------------- bucketize
+
+@pytest.mark.parametrize("b", [1, 2, 3, 4, 8])
+def test_bucketize_equals_nearest_centroid(b):
+    c, t, _ = O.codebook(b)
+    rng = np.random.default_rng(b)
+    y = np.concatenate([rng.standard_normal(4000) * 1.5, t, np.nextafter(t, -np.inf),
+                        np.nextafter(t, np.inf), [0.0, -0.0, 9.0, -9.0]])
+    # The fp32 boundary and the midpoint of the fp32 centroids differ by up to
+    # an ulp, and |y - c| rounds in float64: points within 1e-9 of a boundary
+    # are left to test_bucketize_ties_go_up.
+    idx = O.bucketize(y, t)
+    nn = O.nearest_centroid(y, c)
+    near = np.min(np.abs(y[:, None] - t[None, :]), axis=1) < 1e-9
+    assert np.array_equal(idx[~near], nn[~near])
+    assert near.sum() <= 3 * len(t) + 2
+    if b == 1:
+        assert np.array_equal(idx, (y >= 0).astype(np.int64))
+
+
+def test_bucketize_ties_go_up():
+    _, t, _ = O.codebook(2)
+    assert np.array_equal(O.bucketize(t, t), np.arange(1, 4))
+
+
+# ---------------------------------------------------------------- packing
+
+def test_pack_golden_examples():
+    g = _gold("pack_examples.json")
+    for ex in g["two_bit"]:
+        want = ex["bytes"] if "bytes" in ex else [ex["byte"]]
+        got = O.pack_fields(np.array([ex["codes"]]), 2)[0]
+        assert list(got) == want
+    for ex in g["four_bit"] + g["three_bit_as_four"]:
+        assert list(O.pack_fields(np.array([ex["codes"]]), 4)[0]) == [ex["byte"]]
+    for ex in g["signs"]:
+        bits = (np.array(ex["signs"]) > 0).astype(np.uint8)
+        assert list(O.pack_signs(bits[None, :])[0]) == [ex["byte"]]
+
+
+@pytest.mark.parametrize("w", [1, 2, 4, 8])
+def test_pack_round_trip(w):
+    rng = np.random.default_rng(w)
+    codes = rng.integers(0, 1 << w, size=(37, 128))
+    assert np.array_equal(O.unpack_fields(O.pack_fields(codes, w), w, 128), codes)
+    bits = rng.integers(0, 2, size=(37, 128)).astype(np.uint8)
+    assert np.array_equal(O.unpack_signs(O.pack_signs(bits), 128), bits)
+
+
+def test_record_bytes():
+    g = _gold("pack_examples.json")["record_bytes"]
+    assert O.record_bytes(O.KeyConfig(mode="prod", bits=3)) == g["prod3_d128"]
+    assert O.record_bytes(O.KeyConfig(mode="prod", bits=4)) == 84
+    assert O.record_bytes(O.KeyConfig(mode="mse", bits=4)) == 66
+    assert O.record_bytes(O.KeyConfig(mode="mse", bits=8)) == 130
+    assert O.record_bytes(O.KeyConfig(mode="grouped", bits_outlier=4, bits_normal=2)) == 52
+
+
+# ---------------------------------------------------------------- MSE encode
+
+def _sphere_marginal_mse(b, d=128):
+    """Exact E[(y - Q(y))^2] when y = sqrt(d) * (a coordinate of a uniform
+    point on the unit sphere in R^d): density of x = y/sqrt(d) is
+    proportional to (1 - x^2)^((d-3)/2) on [-1, 1]."""
+    c, t, _ = O.codebook(b)
+    lo = np.concatenate(([-math.sqrt(d)], t))
+    hi = np.concatenate((t, [math.sqrt(d)]))
+    logC = math.lgamma(d / 2) - math.lgamma((d - 1) / 2) - 0.5 * math.log(math.pi)
+    f = lambda y: math.exp(logC + 0.5 * (d - 3) * math.log1p(-y * y / d)) / math.sqrt(d)
+    tot = 0.0
+    for k in range(len(c)):
+        tot += quad(lambda y: (y - c[k]) ** 2 * f(y), lo[k], hi[k], epsabs=1e-13, epsrel=1e-11)[0]
+    return tot
+
+
+@pytest.mark.parametrize("b", [1, 2, 3, 4, 8])
+def test_mse_distortion_theorem1_and_exact_expectation(b):
+    coef = _gold("lloyd_max_textbook.json")["theorem1_pages"]["coef"]
+    T = O.build_tables(O.KeyConfig(mode="mse", bits=b, seed=42))
+    u = np.random.default_rng(100 + b).standard_normal((3000, 128))
+    u /= np.linalg.norm(u, axis=1, keepdims=True)
+    enc = O.encode_keys(u, T)
+    uh = O.dequant_keys(enc, T)
+    err = np.sum((u - uh) ** 2, axis=1)
+    assert err.mean() <= coef * 4.0 ** (-b)
+    exact = _sphere_marginal_mse(b)
+    se = err.std() / math.sqrt(err.size)
+    assert abs(err.mean() - exact) < 4 * se + 1e-6 * exact, (err.mean(), exact, se)
+    # the sphere marginal is close to N(0,1): within 2% of D_b
+    assert abs(exact / O.codebook(b)[2] - 1) < 0.02
+
+
+def test_key_built_from_centroids():
+    """k = Pi^T c[idx] / ||c[idx]|| (unit norm).  Then y = sqrt(d) Pi k =
+    lam * c[idx] with lam = sqrt(d) / ||c[idx]|| (close to 1 for the chosen
+    index mix), so: the indices come back, the MSE reconstruction is k / lam,
+    and rho = ||k - k_mse|| = (lam - 1) / lam.  A transposed or unsigned
+    rotation, or a wrong scale, breaks one of these."""
+    T = O.build_tables(O.KeyConfig(mode="prod", bits=3, seed=5))
+    rng = np.random.default_rng(1)
+    rows = []
+    for _ in range(3):
+        inner = rng.permutation(np.r_[np.ones(79, int), np.zeros(49, int)])  # 79 small, 49 large levels
+        sign = rng.integers(0, 2, 128)
+        rows.append(np.where(sign == 1, 2 + (1 - inner), 1 - (1 - inner)))   # 2/3 positive, 1/0 negative
+    idx = np.array(rows)
+    c = T.centroids[idx]
+    cn = np.linalg.norm(c, axis=1, keepdims=True)
+    # Pi = H diag(sigma) / sqrt(d), written here from scipy's Hadamard matrix
+    Pi = scipy.linalg.hadamard(128) * T.sigma[None, :] / math.sqrt(128)
+    k = (c / cn) @ Pi
+    lam = math.sqrt(128) / cn[:, 0]
+    enc = O.encode_keys(k, T)
+    assert np.array_equal(enc["idx"], idx)
+    assert np.allclose(enc["rnorm"], np.abs(lam - 1) / lam, rtol=1e-9, atol=1e-15)
+    mse_only = dict(enc)
+    mse_only["rnorm16"] = np.zeros(3, dtype=np.float16)
+    assert np.all(enc["norm16"] == 1.0)
+    assert np.allclose(O.dequant_keys(mse_only, T), k / lam[:, None], atol=1e-12)
+
+
+def test_zero_key_scores_zero():
+    T = O.build_tables(O.KeyConfig(mode="prod", bits=3))
+    enc = O.encode_keys(np.zeros((1, 128)), T)
+    assert enc["norm16"][0] == 0 and enc["rnorm16"][0] == 0
+    assert np.all(enc["idx"] == 2)                 # y = 0 sits on the middle boundary, goes up
+    q = np.random.default_rng(0).standard_normal((2, 128))
+    assert np.all(O.key_scores(q, enc, T) == 0)
+
+
+# ---------------------------------------------------------------- QJL / prod
+
+def _prod_setup(bits, seed=42):
+    return O.build_tables(O.KeyConfig(mode="prod", bits=bits, seed=seed))
+
+
+def test_prod_unbiased_over_S_draws():
+    """For fixed unit keys, queries, Pi and indices, the mean of q.k_hat over
+    independent Gaussian S is q.k (Theorem 2); the variance matches the
+    closed form ((pi/2)||r||^2||a||^2 - <a,r>^2)/m of the sign estimator,
+    a = Pi q scaled into the residual's units."""
+    T = _prod_setup(3)
+    rng = np.random.default_rng(2)
+    k = rng.standard_normal((4, 128))
+    k /= np.linalg.norm(k, axis=1, keepdims=True)
+    q = rng.standard_normal((4, 128))
+    base = O.encode_keys(k, T)
+    Pi = O.rotation_matrix(T.sigma)
+    true = np.sum(q * k, axis=1)
+    ests = []
+    draws = 3000
+    g = np.random.default_rng(3)
+    for _ in range(draws):
+        T.S = g.standard_normal((128, 128)).astype(np.float32).astype(np.float64)
+        enc = dict(base)
+        enc.update(O.prod_given_idx(base["norm"], base["y"], base["idx"], T))
+        ests.append(np.sum(q * O.dequant_keys(enc, T), axis=1))
+    ests = np.array(ests)
+    mean, sd = ests.mean(0), ests.std(0)
+    assert np.all(np.abs(mean - true) < 4 * sd / math.sqrt(draws)), (mean, true)
+    # variance of the estimate: only the QJL term varies
+    r = base["y"] - T.centroids[base["idx"]]                   # rotated residual, sqrt(d) units
+    a = (q @ Pi.T)                                             # Pi q
+    rn = np.linalg.norm(r, axis=1)
+    an = np.linalg.norm(a, axis=1)
+    ar = np.sum(a * r, axis=1)
+    # estimate of <a, r>/sqrt(d): rho/m sqrt(pi/2) <S a, sign(S r)>, rho = ||r||/sqrt(d)
+    var_theory = ((math.pi / 2) * rn ** 2 * an ** 2 - ar ** 2) / 128 / 128
+    assert np.all(np.abs(sd ** 2 / var_theory - 1) < 0.12), sd ** 2 / var_theory
+
+
+def test_prod_bias_regression_slope_is_zero():
+    """Regress (estimate - truth) on <q, k - k_mse_hat> over many pairs: a
+    wrong QJL constant alpha shows as slope alpha - 1."""
+    T = _prod_setup(3)
+    rng = np.random.default_rng(4)
+    k = rng.standard_normal((3000, 128))
+    k /= np.linalg.norm(k, axis=1, keepdims=True)
+    q = rng.standard_normal((3000, 128))
+    enc = O.encode_keys(k, T)
+    est = np.sum(q * O.dequant_keys(enc, T), axis=1)
+    mse_only = dict(enc)
+    mse_only["rnorm16"] = np.zeros_like(enc["rnorm16"])
+    kmse = O.dequant_keys(mse_only, T)
+    a = np.sum(q * (k - kmse), axis=1)
+    e = est - np.sum(q * k, axis=1)
+    slope = np.sum(e * a) / np.sum(a * a)
+    resid = e - slope * a
+    se = math.sqrt(np.sum(resid ** 2) / (len(a) - 1) / np.sum(a * a))
+    assert abs(slope) < 4 * se + 0.02, (slope, se)
+    # and the QJL term recovers most of the residual's projection
+    qjl = est - np.sum(q * kmse, axis=1)
+    assert np.corrcoef(qjl, a)[0, 1] > 0.5
+
+
+def test_prod_distortion_theorem3_and_scaling():
+    """D_prod = E[(<y,x_hat> - <y,x>)^2] <= sqrt(3) pi^2 ||y||^2 / d * 4^-b
+    for unit x; each extra bit cuts it by more than 2x (about 4x)."""
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((2000, 128))
+    x /= np.linalg.norm(x, axis=1, keepdims=True)
+    y = rng.standard_normal(128)
+    D = {}
+    for b in (2, 3, 4):
+        T = _prod_setup(b)
+        enc = O.encode_keys(x, T)
+        est = O.dequant_keys(enc, T) @ y
+        D[b] = float(np.mean((est - x @ y) ** 2))
+        bound = math.sqrt(3) * math.pi ** 2 * (y @ y) / 128 * 4.0 ** (-b)
+        assert D[b] <= bound, (b, D[b], bound)
+    assert D[2] / D[3] > 2.0 and D[3] / D[4] > 2.0
+
+
+def test_grouped_halves_are_independent_mse():
+    cfg = O.KeyConfig(mode="grouped", bits_outlier=4, bits_normal=2, seed=9)
+    T = O.build_tables(cfg)
+    rng = np.random.default_rng(6)
+    k = rng.standard_normal((500, 128)) * np.r_[np.full(64, 10.0), np.ones(64)]
+    enc = O.encode_keys(k, T)
+    kh = O.dequant_keys(enc, T)
+    for j, b in ((0, 4), (1, 2)):
+        sl = slice(64 * j, 64 * (j + 1))
+        half = O.KeyConfig(d=64, mode="mse", bits=b)
+        Th = O.build_tables(half)
+        Th.sigma = T.halves[j]["sigma"]
+        ench = O.encode_keys(k[:, sl], Th)
+        assert np.array_equal(ench["idx"], enc["idx"][:, sl])
+        assert np.allclose(O.dequant_keys(ench, Th), kh[:, sl], atol=1e-12)
+    rel = np.sum((k - kh) ** 2, axis=1) / np.sum(k * k, axis=1)
+    assert rel.mean() < 0.02
+
+
+def test_packed_record_round_trip_all_modes():
+    rng = np.random.default_rng(8)
+    k = rng.standard_normal((64, 128))
+    for cfg in (O.KeyConfig(mode="prod", bits=3), O.KeyConfig(mode="prod", bits=4),
+                O.KeyConfig(mode="mse", bits=8), O.KeyConfig(mode="grouped")):
+        T = O.build_tables(cfg)
+        enc = O.encode_keys(k, T)
+        rec = O.pack_key_record(enc, T)
+        back = O.unpack_key_record(rec, T)
+        assert np.array_equal(back["idx"], enc["idx"])
+        assert np.allclose(O.dequant_keys(back, T), O.dequant_keys(enc, T))
+        nbytes = sum(v.shape[1] if v.ndim == 2 and v.dtype == np.uint8 else
+                     v.dtype.itemsize * (v.shape[1] if v.ndim == 2 else 1) for v in rec.values())
+        assert nbytes == O.record_bytes(cfg)
+
+
+# ---------------------------------------------------------------- values
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_value_quantisation_error_bound(bits):
+    rng = np.random.default_rng(bits)
+    v = rng.standard_normal((2000, 128)).astype(np.float32)
+    enc = O.encode_values(v, bits)
+    vh = O.dequant_values(enc)
+    s = enc["scale16"].astype(np.float64)
+    z = enc["zero16"].astype(np.float64)
+    vg = v.reshape(2000, 4, 32).astype(np.float64)
+    err = np.abs(vg - vh.reshape(2000, 4, 32))
+    # rounding error is at most s/2; clamping at the ends adds the fp16
+    # rounding of min (z) and of the scale times the top level
+    slack = np.abs(vg.min(-1) - z) + np.abs(vg.max(-1) - (z + ((1 << bits) - 1) * s))
+    assert np.all(err <= (s / 2 + slack)[..., None] + 1e-6)
+    codes = enc["codes"].reshape(2000, 4, 32)
+    am = vg.argmin(-1)
+    ax = vg.argmax(-1)
+    assert np.all(np.take_along_axis(codes, am[..., None], -1) == 0)
+    assert np.all(np.take_along_axis(codes, ax[..., None], -1) == (1 << bits) - 1)
+
+
+def test_value_cosine_at_4_bits_matches_pack_article():
+    """[pack] sec 三: 4-bit values reach cos_sim 0.997."""
+    rng = np.random.default_rng(11)
+    v = rng.standard_normal((4000, 128)).astype(np.float32)
+    vh = O.dequant_values(O.encode_values(v, 4))
+    cos = np.sum(v * vh, 1) / np.linalg.norm(v, axis=1) / np.linalg.norm(vh, axis=1)
+    assert abs(cos.mean() - 0.997) < 0.0006
+    vh2 = O.dequant_values(O.encode_values(v, 2))
+    cos2 = np.sum(v * vh2, 1) / np.linalg.norm(v, axis=1) / np.linalg.norm(vh2, axis=1)
+    assert 0.90 < cos2.mean() < 0.96
+
+
+def test_value_constant_group():
+    v = np.ones((2, 128), dtype=np.float32) * 3.25
+    enc = O.encode_values(v, 2)
+    assert np.all(enc["codes"] == 0) and np.all(enc["scale16"] == 0)
+    assert np.array_equal(O.dequant_values(enc), v.astype(np.float64))
+
+
+# ---------------------------------------------------------------- decode
+
+def test_decode_attention_definitions():
+    import torch
+    rng = np.random.default_rng(12)
+    q = rng.standard_normal((4, 128))
+    k = rng.standard_normal((50, 128))
+    v = rng.standard_normal((50, 128))
+    s, o, lse = O.decode_attention(q, k, v, 37)
+    assert s.shape == (4, 37)
+    p = torch.softmax(torch.from_numpy(q @ k[:37].T / math.sqrt(128)), dim=-1).numpy()
+    assert np.allclose(o, p @ v[:37], atol=1e-12)
+    assert np.allclose(lse, np.log(np.exp(q @ k[:37].T / math.sqrt(128)).sum(-1)))
+    # one token: output is that value
+    _, o1, _ = O.decode_attention(q, k, v, 1)
+    assert np.allclose(o1, np.broadcast_to(v[0], (4, 128)))
+    # equal scores: plain mean
+    _, o2, _ = O.decode_attention(np.zeros((1, 128)), k, v, 50)
+    assert np.allclose(o2[0], v.mean(0))
+    # tokens past ctx_len never matter
+    v2 = v.copy()
+    v2[37:] = 1e6
+    assert np.allclose(O.decode_attention(q, k, v2, 37)[1], o)
+
+
+# ---------------------------------------------------------------- quality
+
+def test_recall_and_rank_correlation_thresholds():
+    """validate_paper.py test_recall_at_scale: recall@8 >= 0.40 (3-bit),
+    >= 0.55 (4-bit), 4-bit better; rank correlation > 0.75 / 0.90."""
+    rng = np.random.default_rng(13)
+    keys = rng.standard_normal((4096, 128)) * 0.1
+    qs = rng.standard_normal((32, 128)) * 0.1
+    true = qs @ keys.T
+    rec, rho = {}, {}
+    for b in (3, 4):
+        T = _prod_setup(b)
+        est = O.key_scores(qs, O.encode_keys(keys, T), T)
+        rec[b] = O.recall_at_k(true, est, 8)
+        rho[b] = np.mean([O.spearman(true[i], est[i]) for i in range(32)])
+    assert rec[3] >= 0.40 and rec[4] >= 0.55 and rec[4] > rec[3], rec
+    assert rho[3] > 0.75 and rho[4] > 0.90, rho
+
+
+def test_needle_argmax_over_dequantised_keys():
+    """validate_paper.py test_needle_retrieval_depths, one KV head."""
+    rng = np.random.default_rng(14)
+    N = 4096
+    for b in (3, 4):
+        T = _prod_setup(b)
+        for depth in (0.1, 0.5, 0.9):
+            keys = rng.standard_normal((N, 128)) * 0.02
+            needle = rng.standard_normal(128) * 3.0
+            pos = int(N * depth)
+            keys[pos] = needle
+            s = O.key_scores(needle[None, :], O.encode_keys(keys, T), T)[0]
+            assert int(np.argmax(s)) == pos
