@@ -1,0 +1,196 @@
+/*
+ * tq.h -- C ABI of libtq, the MI355X (gfx950) TurboQuant KV-cache library.
+ *
+ * The method (as described on the "tqlite" README, the difai.kr tutorial
+ * "实现 TurboQuant (第5部分)", the m.lqnn.cn bit-packing article and the
+ * electron-rare/turboquant validation script):
+ *   keys   -> L2 norm, random rotation Pi = Hadamard x random signs, snap each
+ *             rotated coordinate to a Lloyd-Max Gaussian codebook, optionally a
+ *             1-bit QJL sign sketch of the residual, bit-pack;
+ *   values -> per-token group quantisation at 2 or 4 bits (fp16 scale, zero);
+ *   decode -> estimate q.k straight from the packed bytes, softmax, weighted
+ *             sum of the dequantised values.
+ *
+ * Conventions for every entry point:
+ *   - Pointers are DEVICE memory unless the argument is marked (host).
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Calls only enqueue work on it; none synchronises or allocates device
+ *     memory, and the library keeps no mutable global state (calls from
+ *     several host threads are safe; calls that write the same buffers race
+ *     exactly as the kernels they enqueue would).
+ *   - The caller owns every buffer.
+ *   - Arguments are validated on the host before anything is launched; a bad
+ *     argument returns TQ_ERR_ARG / TQ_ERR_UNSUPPORTED and enqueues nothing.
+ *     A failed launch returns TQ_ERR_HIP.  Faults inside kernels surface at
+ *     the caller's next synchronisation, as for any HIP kernel.
+ *   - No call aborts or throws.
+ *
+ * Packed layouts (the bit-packing article, sections 二, 三, "3 比特怎么办", 四):
+ *   w-bit index / value fields: element j of a row goes to byte j*w/8 at bit
+ *   (j mod 8/w)*w, first element in the lowest bits.  Index widths: 1-bit ->
+ *   1, 2-bit -> 2, 3- and 4-bit -> 4 (3-bit stored as 4-bit), 5..8-bit -> 8.
+ *   QJL sign i of a key goes to byte i/8 with weight 2^(i mod 8) (bit = 1 iff
+ *   the projection is >= 0).  Norms, scales and zeros are IEEE fp16 (RNE).
+ *   Records are structure-of-arrays planes, one row per record:
+ *     idx   [n_records][tq_idx_row_bytes(cfg)]     uint8
+ *     signs [n_records][d/8]                        uint8   (prod only)
+ *     norm  [n_records]  fp16  (grouped: [n_records][2], outlier half first)
+ *     rnorm [n_records]  fp16  residual norm ||k - k_mse_hat||   (prod only)
+ *     codes [n_records][d*bits/8] uint8, scale/zero [n_records][d/group] fp16
+ *   A 128-d prod key with 3 bits is 32 + 16 + 2 + 2 = 52 bytes, the record the
+ *   bit-packing article (sec 四) counts.
+ */
+#ifndef TQ_H_
+#define TQ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TQ_OK = 0,
+  TQ_ERR_ARG = -1,          /* NULL / misaligned pointer, bad size or shape        */
+  TQ_ERR_UNSUPPORTED = -2,  /* valid in principle, not implemented by this build   */
+  TQ_ERR_WORKSPACE = -3,    /* workspace missing or smaller than required          */
+  TQ_ERR_HIP = -4           /* a HIP runtime call failed (no device, launch error) */
+} tq_status;
+
+/* Quantisation modes: the "tqlite" README's mode table (三种量化模式). */
+typedef enum {
+  TQ_MODE_MSE = 0,      /* rotation + Lloyd-Max codebook, d*bits bits per key      */
+  TQ_MODE_PROD = 1,     /* MSE at (bits-1) index bits + 1-bit QJL residual signs   */
+  TQ_MODE_GROUPED = 2   /* two halves, each its own norm, rotation and codebook    */
+} tq_mode;
+
+typedef enum { TQ_F32 = 0, TQ_BF16 = 1, TQ_F16 = 2 } tq_dtype;
+
+typedef struct {
+  int32_t d;            /* head dimension: power of two, 16 <= d <= 256; the
+                           decode kernels support d = 128                          */
+  int32_t mode;         /* tq_mode                                                  */
+  int32_t bits;         /* MSE: index bits 1..8.  PROD: total bits 2..9, the index
+                           takes bits-1 and the QJL sign 1 (the pages disagree on
+                           this split; (b-1)+1 is the reading taken).  Ignored for
+                           GROUPED.                                                 */
+  int32_t bits_outlier; /* GROUPED: index bits 1..8 of channels [0, d/2)           */
+  int32_t bits_normal;  /* GROUPED: index bits 1..8 of channels [d/2, d)           */
+  int32_t reserved;     /* must be 0                                                */
+  uint64_t seed;        /* derives sigma and S; use one seed per layer ("tqlite"
+                           README, 设计要点: independent seed per layer)            */
+} tq_key_config;
+
+/* Bytes of one index row (the idx plane's row pitch) for `cfg`; 0 if invalid. */
+size_t tq_idx_row_bytes(const tq_key_config* cfg);
+
+/*
+ * tq_build_codebook -- (host) build every seed-derived constant of `cfg` into
+ * one self-describing little-endian blob ("tables"):
+ *   - the Lloyd-Max quantiser of N(0,1) with 2^b levels (one per half in
+ *     GROUPED), centroids and boundaries rounded from float64 to float32; the
+ *     "tqlite" README (Lloyd-Max 高斯码本) and the validation script's
+ *     get_codebook(d, bits) / "mse_total" (test_mse_codebook_table1);
+ *   - the random signs sigma of Pi = H diag(sigma) / sqrt(d) ("tqlite" README:
+ *     rotation = Hadamard x random signs);
+ *   - PROD: the QJL matrix S, d x d i.i.d. N(0,1) stored as fp16 (difai.kr
+ *     tutorial, 算法概述: sign(S @ residual)).
+ * sigma and S come from SplitMix64 (Steele, Lea & Flood 2014) seeded with
+ * seed XOR tag*0x9E3779B97F4A7C15 (tags 1 sigma, 2 S, 3 outlier sigma,
+ * 4 normal sigma), S through Box-Muller on 53-bit uniforms.
+ *   blob_host       (host) output buffer, 256-byte aligned size *bytes; NULL to
+ *                   query the size.
+ *   bytes           (host) in: capacity of blob_host; out: bytes required.
+ *   mse_total_host  (host, nullable) out: float64 expected total squared error
+ *                   of a unit vector (Table 1's "mse_total"); two values for
+ *                   GROUPED (outlier half, normal half), else one.
+ * The blob is position independent: upload it to device memory unchanged and
+ * pass the device copy as `tables` below.  Returns TQ_ERR_ARG if *bytes is too
+ * small (and sets *bytes).  Takes well under a second on the host.
+ */
+tq_status tq_build_codebook(const tq_key_config* cfg, void* blob_host, size_t* bytes,
+                            double* mse_total_host);
+
+/*
+ * tq_encode_keys -- quantise and pack n_vec keys.
+ * Per key: n = ||k||; y = H (sigma * k / n) (the 128-point fast Walsh-Hadamard
+ * transform, the "tqlite" README's 已知限制 asking for O(d log d)); each y_j
+ * goes to the Lloyd-Max cell #{t : y_j >= t}; PROD also forms the residual
+ * r = y - c[idx], the signs [S r >= 0] and rho = n ||r|| / sqrt(d).
+ *   tables     device copy of the tq_build_codebook blob for `cfg`.
+ *   keys       [n_vec rows] x d elements of `dtype`, row i at keys + i*row_stride
+ *              elements; 16-byte aligned, row_stride*elemsize a multiple of 16.
+ *   slots      (nullable) int64 [n_vec]: record index that row i is written to;
+ *              a slot outside [0, n_records) skips the row.  NULL: slot = i.
+ *   n_records  rows of every output plane.
+ *   idx, norm  always; signs, rnorm for PROD only (NULL otherwise).
+ * Output planes must be 16-byte aligned.  n_vec == 0 is a no-op.
+ */
+tq_status tq_encode_keys(const tq_key_config* cfg, const void* tables,
+                         const void* keys, int32_t dtype, int64_t n_vec, int64_t row_stride,
+                         const int64_t* slots, int64_t n_records,
+                         uint8_t* idx, uint8_t* signs, uint16_t* norm, uint16_t* rnorm,
+                         void* stream);
+
+/*
+ * tq_encode_values -- per-token group quantisation of n_vec value rows
+ * (bit-packing article sec 二: 2-bit values four per byte; sec 三: 4-bit two per
+ * byte).  For each group of `group` consecutive channels: s = fp16((max-min) /
+ * (2^bits - 1)), z = fp16(min), code = clamp(rint((v - z) / s), 0, 2^bits - 1)
+ * computed in float32 with the fp16-rounded s and z (ties to even); s == 0
+ * gives code 0.
+ *   bits 2 or 4; group 32; d = 128.  Layout and slot rules as tq_encode_keys.
+ */
+tq_status tq_encode_values(int32_t bits, int32_t group, int32_t d,
+                           const void* values, int32_t dtype, int64_t n_vec, int64_t row_stride,
+                           const int64_t* slots, int64_t n_records,
+                           uint8_t* codes, uint16_t* scale, uint16_t* zero, void* stream);
+
+/*
+ * tq_decode_attention -- one decode step of attention over the packed cache.
+ * For query head h of sequence b (KV head h / (Hq/Hkv)), over tokens
+ * t < ctx_len[b]:
+ *   s_t = q . k_hat_t, estimated from the packed bytes as
+ *         (n_t/d) <q', c[idx_t]> + rho_t sqrt(pi/2)/(d sqrt(d)) <S q', 2 bit_t - 1>
+ *         with q' = H (sigma * q)  (difai.kr tutorial, 算法概述: <q,k_hat> +
+ *         sqrt(pi/2) (S@q)^T sign_bits, with the ||r|| and 1/m that make it
+ *         unbiased); MSE/GROUPED keep the first term (per half);
+ *   p = softmax(sm_scale * s), out = sum_t p_t v_hat_t, v_hat = code*s + z.
+ * The split-K scheme (partial max, sum and output per token chunk, merged in
+ * a second kernel) keeps every result deterministic: no atomics.
+ *   q          [B][Hq][d] of q_dtype, contiguous, 16-byte aligned.
+ *   ctx_len    int32 [B]; each 0 <= ctx_len[b] <= max_ctx.  A sequence with
+ *              ctx_len 0 gets out = 0 and lse = -inf.
+ *   key planes [B][Hkv][max_ctx] records, as written by tq_encode_keys with
+ *              slot = (b*Hkv + h)*max_ctx + t.
+ *   value planes: same record indexing; v_bits 2 or 4, v_group 32.
+ *   sm_scale   softmax scale (1/sqrt(d) for standard attention).
+ *   out        [B][Hq][d] float32.
+ *   lse        (nullable) [B][Hq] float32 natural-log sum of exp(sm_scale*s).
+ *   scores     (nullable) [B][Hq][max_ctx] float32 raw s_t (entries with
+ *              t >= ctx_len[b] are not written).
+ *   workspace  device scratch; with workspace == NULL the call only stores the
+ *              required size in *workspace_bytes (host) and returns TQ_OK.
+ * Supported: d = 128; PROD with bits 3 (2-bit index) or 4 (3-bit index in
+ * nibbles); MSE with bits 2 or 4; GROUPED with (4, 2) or (2, 2) or (4, 4)
+ * halves; Hq % Hkv == 0.  Other shapes return TQ_ERR_UNSUPPORTED.
+ */
+tq_status tq_decode_attention(const tq_key_config* cfg, const void* tables,
+                              const void* q, int32_t q_dtype, int32_t B, int32_t Hq, int32_t Hkv,
+                              const int32_t* ctx_len, int32_t max_ctx,
+                              const uint8_t* idx, const uint8_t* signs,
+                              const uint16_t* norm, const uint16_t* rnorm,
+                              int32_t v_bits, int32_t v_group,
+                              const uint8_t* v_codes, const uint16_t* v_scale, const uint16_t* v_zero,
+                              float sm_scale, float* out, float* lse, float* scores,
+                              void* workspace, size_t* workspace_bytes, void* stream);
+
+/* Static description of a status code (never NULL). */
+const char* tq_status_string(int32_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TQ_H_ */

@@ -1,0 +1,15 @@
+"""MI355X-native TurboQuant KV-cache path: key/value encode and packed-domain
+decode attention, as HIP kernels for gfx950 behind the C ABI in include/tq.h.
+
+The Python layer only marshals arguments (torch provides device memory and
+streams); importing it requires the built libtq.so next to this file.
+"""
+from ._lib import (TQ_BF16, TQ_F16, TQ_F32, TQ_MODE_GROUPED, TQ_MODE_MSE, TQ_MODE_PROD, KeyConfig,
+                   TqError, key_config, status_string)
+from .api import (Decoder, Tables, build_codebook, decode_attention, decode_workspace_bytes,
+                  encode_keys, encode_values, idx_row_bytes, key_planes, parse_tables, value_planes)
+
+__all__ = ["KeyConfig", "TqError", "key_config", "status_string", "Tables", "Decoder",
+           "build_codebook", "parse_tables", "encode_keys", "encode_values", "decode_attention",
+           "decode_workspace_bytes", "key_planes", "value_planes", "idx_row_bytes",
+           "TQ_F32", "TQ_BF16", "TQ_F16", "TQ_MODE_MSE", "TQ_MODE_PROD", "TQ_MODE_GROUPED"]

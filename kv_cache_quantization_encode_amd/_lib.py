@@ -1,0 +1,73 @@
+"""ctypes binding of libtq.so (the C ABI declared in include/tq.h).
+
+Argument marshalling only: every step of the method runs in the library's
+HIP kernels.  If the shared library is missing this module raises at import
+time; there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libtq.so")
+
+TQ_OK, TQ_ERR_ARG, TQ_ERR_UNSUPPORTED, TQ_ERR_WORKSPACE, TQ_ERR_HIP = 0, -1, -2, -3, -4
+TQ_MODE_MSE, TQ_MODE_PROD, TQ_MODE_GROUPED = 0, 1, 2
+TQ_F32, TQ_BF16, TQ_F16 = 0, 1, 2
+MODES = {"mse": TQ_MODE_MSE, "prod": TQ_MODE_PROD, "grouped": TQ_MODE_GROUPED}
+
+EXPORTED = ["tq_build_codebook", "tq_encode_keys", "tq_encode_values", "tq_decode_attention",
+            "tq_status_string", "tq_idx_row_bytes"]
+
+
+class TqError(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        super().__init__("%s failed: %s (%d)" % (fn, status_string(status), status))
+
+
+class KeyConfig(ctypes.Structure):
+    _fields_ = [("d", ctypes.c_int32), ("mode", ctypes.c_int32), ("bits", ctypes.c_int32),
+                ("bits_outlier", ctypes.c_int32), ("bits_normal", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("seed", ctypes.c_uint64)]
+
+
+def key_config(d=128, mode="prod", bits=3, seed=42, bits_outlier=4, bits_normal=2) -> KeyConfig:
+    m = MODES[mode] if isinstance(mode, str) else int(mode)
+    return KeyConfig(d, m, bits, bits_outlier, bits_normal, 0, seed)
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libtq.so is not built (run kv_cache_quantization_encode_amd.build)")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    CFG = ctypes.POINTER(KeyConfig)
+    lib.tq_status_string.restype = ctypes.c_char_p
+    lib.tq_status_string.argtypes = [I32]
+    lib.tq_idx_row_bytes.restype = SZ
+    lib.tq_idx_row_bytes.argtypes = [CFG]
+    lib.tq_build_codebook.restype = I32
+    lib.tq_build_codebook.argtypes = [CFG, P, ctypes.POINTER(SZ), ctypes.POINTER(ctypes.c_double)]
+    lib.tq_encode_keys.restype = I32
+    lib.tq_encode_keys.argtypes = [CFG, P, P, I32, I64, I64, P, I64, P, P, P, P, P]
+    lib.tq_encode_values.restype = I32
+    lib.tq_encode_values.argtypes = [I32, I32, I32, P, I32, I64, I64, P, I64, P, P, P, P]
+    lib.tq_decode_attention.restype = I32
+    lib.tq_decode_attention.argtypes = [CFG, P, P, I32, I32, I32, I32, P, I32, P, P, P, P,
+                                        I32, I32, P, P, P, ctypes.c_float, P, P, P, P,
+                                        ctypes.POINTER(SZ), P]
+    return lib
+
+
+lib = _load()
+
+
+def status_string(status: int) -> str:
+    return lib.tq_status_string(int(status)).decode()
+
+
+def check(fn: str, status: int):
+    if status != TQ_OK:
+        raise TqError(fn, status)

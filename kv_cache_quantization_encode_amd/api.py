@@ -1,0 +1,179 @@
+"""Thin Python API over libtq's C ABI.  torch supplies device memory and the
+current HIP stream; every computation happens in the library's kernels."""
+from __future__ import annotations
+
+import ctypes
+import math
+import struct
+
+import numpy as np
+import torch
+
+from ._lib import (TQ_BF16, TQ_F16, TQ_F32, TQ_MODE_GROUPED, TQ_MODE_PROD, KeyConfig, check,
+                   key_config, lib)
+
+_DT = {torch.float32: TQ_F32, torch.bfloat16: TQ_BF16, torch.float16: TQ_F16}
+
+# tq_blob_header (kv_cache_quantization_encode_amd/csrc/tq_tables.h)
+_HDR = struct.Struct("<4I4i" + "2i2i2i" + "2I2I2I2I" + "2i2f2f" + "2I" + "2d")
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def idx_row_bytes(cfg: KeyConfig) -> int:
+    return int(lib.tq_idx_row_bytes(ctypes.byref(cfg)))
+
+
+def build_codebook(cfg: KeyConfig):
+    """Host call: returns (blob as uint8 numpy array, list of mse_total)."""
+    size = ctypes.c_size_t(0)
+    mse = (ctypes.c_double * 2)()
+    check("tq_build_codebook", lib.tq_build_codebook(ctypes.byref(cfg), None, ctypes.byref(size), mse))
+    buf = np.zeros(size.value, dtype=np.uint8)
+    check("tq_build_codebook", lib.tq_build_codebook(ctypes.byref(cfg), buf.ctypes.data_as(ctypes.c_void_p),
+                                                      ctypes.byref(size), mse))
+    n = 2 if cfg.mode == TQ_MODE_GROUPED else 1
+    return buf, [mse[i] for i in range(n)]
+
+
+def parse_tables(blob: np.ndarray) -> dict:
+    """Decode the blob's header and arrays on the host (inspection and tests)."""
+    f = _HDR.unpack_from(blob.tobytes(), 0)
+    h = dict(magic=f[0], version=f[1], total_bytes=f[2], header_bytes=f[3], d=f[4], mode=f[5],
+             m=f[6], n_parts=f[7], part_d=f[8:10], part_bits=f[10:12], part_levels=f[12:14],
+             off_centroids=f[14:16], off_bounds=f[16:18], off_sigma=f[18:20], off_hint=f[20:22],
+             hint_n=f[22:24], hint_lo=f[24:26], hint_scale=f[26:28], off_S=f[28], mse=f[30:32])
+    parts = []
+    for i in range(h["n_parts"]):
+        L = h["part_levels"][i]
+        c = blob[h["off_centroids"][i]:h["off_centroids"][i] + 4 * L].view(np.float32)
+        t = blob[h["off_bounds"][i]:h["off_bounds"][i] + 4 * (L + 1)].view(np.float32)
+        s = blob[h["off_sigma"][i]:h["off_sigma"][i] + 4 * h["part_d"][i]].view(np.float32)
+        hint = blob[h["off_hint"][i]:h["off_hint"][i] + 16 * h["hint_n"][i]].view(np.int32).reshape(-1, 4)
+        parts.append(dict(centroids=c.copy(), bounds=t.copy(), sigma=s.copy(), hint=hint.copy()))
+    h["parts"] = parts
+    if h["mode"] == TQ_MODE_PROD:
+        n = h["m"] * h["d"]
+        h["S"] = blob[h["off_S"]:h["off_S"] + 2 * n].view(np.float16).reshape(h["m"], h["d"]).copy()
+    return h
+
+
+class Tables:
+    """Seed-derived tables of one key configuration, resident on a device."""
+
+    def __init__(self, cfg: KeyConfig, device="cuda"):
+        self.cfg = cfg
+        blob, self.mse = build_codebook(cfg)
+        self.blob = blob
+        self.dev = torch.from_numpy(blob).to(device)
+        self.row_bytes = idx_row_bytes(cfg)
+
+    @property
+    def mode(self):
+        return self.cfg.mode
+
+
+def key_planes(tables: Tables, n_records: int, device="cuda") -> dict:
+    d = tables.cfg.d
+    p = dict(idx=torch.empty((n_records, tables.row_bytes), dtype=torch.uint8, device=device))
+    if tables.mode == TQ_MODE_GROUPED:
+        p["norm"] = torch.empty((n_records, 2), dtype=torch.float16, device=device)
+    else:
+        p["norm"] = torch.empty((n_records,), dtype=torch.float16, device=device)
+    if tables.mode == TQ_MODE_PROD:
+        p["signs"] = torch.empty((n_records, d // 8), dtype=torch.uint8, device=device)
+        p["rnorm"] = torch.empty((n_records,), dtype=torch.float16, device=device)
+    return p
+
+
+def value_planes(bits: int, n_records: int, d=128, group=32, device="cuda") -> dict:
+    return dict(codes=torch.empty((n_records, d * bits // 8), dtype=torch.uint8, device=device),
+                scale=torch.empty((n_records, d // group), dtype=torch.float16, device=device),
+                zero=torch.empty((n_records, d // group), dtype=torch.float16, device=device))
+
+
+def encode_keys(tables: Tables, keys: torch.Tensor, planes: dict | None = None, slots=None,
+                n_records: int | None = None) -> dict:
+    """keys: [n, d] float32/bfloat16/float16 CUDA tensor (rows may be strided)."""
+    assert keys.dim() == 2 and keys.stride(1) == 1
+    n = keys.shape[0]
+    if n_records is None:
+        n_records = n if planes is None else planes["idx"].shape[0]
+    if planes is None:
+        planes = key_planes(tables, n_records, keys.device)
+    st = lib.tq_encode_keys(ctypes.byref(tables.cfg), _ptr(tables.dev), _ptr(keys), _DT[keys.dtype],
+                            n, keys.stride(0), _ptr(slots), n_records, _ptr(planes["idx"]),
+                            _ptr(planes.get("signs")), _ptr(planes["norm"]), _ptr(planes.get("rnorm")),
+                            _stream())
+    check("tq_encode_keys", st)
+    return planes
+
+
+def encode_values(values: torch.Tensor, bits: int, group: int = 32, planes: dict | None = None,
+                  slots=None, n_records: int | None = None) -> dict:
+    assert values.dim() == 2 and values.stride(1) == 1
+    n, d = values.shape
+    if n_records is None:
+        n_records = n if planes is None else planes["codes"].shape[0]
+    if planes is None:
+        planes = value_planes(bits, n_records, d, group, values.device)
+    st = lib.tq_encode_values(bits, group, d, _ptr(values), _DT[values.dtype], n, values.stride(0),
+                              _ptr(slots), n_records, _ptr(planes["codes"]), _ptr(planes["scale"]),
+                              _ptr(planes["zero"]), _stream())
+    check("tq_encode_values", st)
+    return planes
+
+
+def decode_workspace_bytes(tables: Tables, B, Hq, Hkv, max_ctx, q_dtype=torch.bfloat16, v_bits=2) -> int:
+    size = ctypes.c_size_t(0)
+    st = lib.tq_decode_attention(ctypes.byref(tables.cfg), None, None, _DT[q_dtype], B, Hq, Hkv, None,
+                                 max_ctx, None, None, None, None, v_bits, 32, None, None, None,
+                                 ctypes.c_float(1.0), None, None, None, None, ctypes.byref(size), None)
+    check("tq_decode_attention", st)
+    return size.value
+
+
+class Decoder:
+    """Holds the workspace for repeated decode steps of one shape."""
+
+    def __init__(self, tables: Tables, B, Hq, Hkv, max_ctx, v_bits, q_dtype=torch.bfloat16,
+                 device="cuda"):
+        self.tables, self.B, self.Hq, self.Hkv, self.max_ctx, self.v_bits = tables, B, Hq, Hkv, max_ctx, v_bits
+        self.ws_bytes = decode_workspace_bytes(tables, B, Hq, Hkv, max_ctx, q_dtype, v_bits)
+        self.ws = torch.empty(max(self.ws_bytes, 16), dtype=torch.uint8, device=device)
+
+    def __call__(self, q, ctx_len, kp: dict, vp: dict, sm_scale=None, out=None, lse=None,
+                 scores=None):
+        B, Hq, d = q.shape
+        assert (B, Hq) == (self.B, self.Hq) and q.is_contiguous()
+        if sm_scale is None:
+            sm_scale = 1.0 / math.sqrt(d)
+        if out is None:
+            out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+        size = ctypes.c_size_t(self.ws.numel())
+        st = lib.tq_decode_attention(
+            ctypes.byref(self.tables.cfg), _ptr(self.tables.dev), _ptr(q), _DT[q.dtype], B, Hq, self.Hkv,
+            _ptr(ctx_len), self.max_ctx, _ptr(kp["idx"]), _ptr(kp.get("signs")), _ptr(kp["norm"]),
+            _ptr(kp.get("rnorm")), self.v_bits, 32, _ptr(vp["codes"]), _ptr(vp["scale"]), _ptr(vp["zero"]),
+            ctypes.c_float(sm_scale), _ptr(out), _ptr(lse), _ptr(scores), _ptr(self.ws),
+            ctypes.byref(size), _stream())
+        check("tq_decode_attention", st)
+        return out
+
+
+def decode_attention(tables: Tables, q, ctx_len, kp, vp, v_bits, max_ctx, sm_scale=None,
+                     with_lse=False, with_scores=False):
+    B, Hq, d = q.shape
+    Hkv = kp["idx"].shape[0] // (B * max_ctx)
+    dec = Decoder(tables, B, Hq, Hkv, max_ctx, v_bits, q.dtype, q.device)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device) if with_lse else None
+    scores = torch.full((B, Hq, max_ctx), float("nan"), dtype=torch.float32, device=q.device) \
+        if with_scores else None
+    out = dec(q, ctx_len, kp, vp, sm_scale, lse=lse, scores=scores)
+    return out, lse, scores

@@ -1,0 +1,622 @@
+// Split-K decode attention over the packed TurboQuant cache, for gfx950.
+//
+// What is computed (difai.kr tutorial, 算法概述, with the ||r|| and 1/m that
+// make the QJL term unbiased; "tqlite" README mode table; bit-packing article
+// sec 五: the fused kernels read the packed bytes directly and unpack with
+// shifts and masks):
+//   s_t = (n_t / d) <q', c[idx_t]> + rho_t sqrt(pi/2) / (m sqrt(d)) <S q', 2 bit_t - 1>
+//   (GROUPED: (n0/64) <q'_0, c0[idx]> + (n1/64) <q'_1, c1[idx]> over the halves)
+//   p = softmax(sm_scale s), out = sum_t p_t (code_t * scale_t + zero_t).
+//
+// One workgroup (16 waves) takes one (sequence, KV head, quad of query heads,
+// token chunk).  Its prologue rotates the four queries (q' = H sigma q by an
+// in-LDS butterfly), projects them (S q'), and turns them into lookup tables:
+// for every byte position p of a packed key and every byte value v, the four
+// heads' partial inner products over the coordinates that byte holds, as fp16.
+// A key's score is then one table read per packed byte (48 for a 3-bit prod
+// key) instead of 4 x 256 multiply-adds.  Each wave streams 64-token tiles:
+// lanes take tokens for the scores and the online softmax, then lanes take
+// 8-dim column slices for p.V, which runs on v_dot2_f32_f16 over token pairs
+// with the 2- or 4-bit codes placed directly in fp16 subnormal bit patterns
+// (code * 2^-24 * 4^k), so no conversion is spent per code.  The value scale
+// is folded into the weight (p * scale) and the zero point is summed
+// separately (sum_t p_t zero_t).  The chunk's (max, sum, unnormalised output)
+// goes to the workspace; a second kernel merges chunks in a fixed order.
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+
+#include <atomic>
+
+#include "tq.h"
+#include "tq_internal.h"
+#include "tq_tables.h"
+
+namespace {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
+constexpr int KD = 128;
+constexpr int NW = 16;        // waves per workgroup
+constexpr int NT = NW * 64;   // threads per workgroup
+constexpr int TILE = 64;      // tokens per wave tile
+constexpr int QH = 4;         // query heads per workgroup
+constexpr int PART = KD + 2;  // floats per partial: max, sum, out[128]
+constexpr float LOG2E = 1.4426950408889634f;
+
+constexpr int width_of(int b) { return b == 1 ? 1 : b == 2 ? 2 : 4; }
+constexpr int stride_of(int b) { return b == 3 ? 128 : 256; }  // 3-bit in nibbles: bytes <= 0x77
+
+template <int MODE, int B0, int B1>
+struct Fmt {
+  static constexpr bool GROUPED = MODE == TQ_MODE_GROUPED;
+  static constexpr bool PROD = MODE == TQ_MODE_PROD;
+  static constexpr int PD = GROUPED ? KD / 2 : KD;           // coordinates per part
+  static constexpr int W0 = width_of(B0);
+  static constexpr int W1 = GROUPED ? width_of(B1) : 1;
+  static constexpr int CPB0 = 8 / W0, CPB1 = 8 / W1;           // coordinates per byte
+  static constexpr int P0 = PD * W0 / 8;                        // class-0 byte positions
+  static constexpr int P1 = PROD ? KD / 8 : GROUPED ? PD * W1 / 8 : 0;
+  static constexpr int S0 = stride_of(B0);
+  static constexpr int S1 = GROUPED ? stride_of(B1) : 256;
+  static constexpr int E0 = P0 * S0, E1 = P1 * S1;              // table entries
+  static constexpr int IDXB = P0 + (GROUPED ? P1 : 0);          // idx row bytes
+  static constexpr int KWORDS = (IDXB + (PROD ? KD / 8 : 0)) / 4;  // idx + sign words
+};
+
+struct DecArgs {
+  const unsigned char* tables;
+  const void* q;
+  int q_dtype;
+  int B, Hq, Hkv, G, n_quads;
+  const int* ctx_len;
+  int max_ctx;
+  const uint8_t* idx;
+  const uint8_t* signs;
+  const uint16_t* norm;
+  const uint16_t* rnorm;
+  const uint8_t* vcodes;
+  const uint16_t* vscale;
+  const uint16_t* vzero;
+  float sm_scale;
+  float* scores;
+  float* part;
+  int n_split;
+  int chunk;  // tokens per split (multiple of TILE)
+};
+
+__device__ inline float load_q(const void* q, int dt, long long i) {
+  if (dt == TQ_F32) return ((const float*)q)[i];
+  const uint16_t v = ((const uint16_t*)q)[i];
+  if (dt == TQ_BF16) return __uint_as_float((uint32_t)v << 16);
+  return __half2float(__ushort_as_half(v));
+}
+
+__device__ inline float h2f(uint32_t bits16) { return __half2float(__ushort_as_half((unsigned short)bits16)); }
+
+__device__ inline float wave_max(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m));
+  return v;
+}
+
+__device__ inline float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
+  return v;
+}
+
+template <int MODE, int B0, int B1, int VB>
+__global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
+  using F = Fmt<MODE, B0, B1>;
+  extern __shared__ __align__(16) unsigned char smem[];
+  uint2* lut = (uint2*)smem;                                  // [E0 + E1] x 4 fp16
+  float* qp = (float*)(smem + (size_t)(F::E0 + F::E1) * 8);   // [QH][KD] rotated queries
+  float* qs = qp + QH * KD;                                   // [QH][KD] S q' (PROD)
+  uint32_t* wbuf = (uint32_t*)(qs + QH * KD);                 // [NW][32 pairs][4 groups][QH] half2
+  float* scl = (float*)(wbuf + NW * 32 * 4 * QH);             // [2][QH] table scales
+  int* amax = (int*)(scl + 2 * QH);                           // [2][QH]
+
+  const tq_blob_header* H = (const tq_blob_header*)a.tables;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int split = blockIdx.x, quad = blockIdx.y, bh = blockIdx.z;
+  const int b = bh / a.Hkv, hkv = bh % a.Hkv;
+  const int ctx = a.ctx_len[b];
+  const int t_begin = split * a.chunk;
+  const int t_end = min(ctx, t_begin + a.chunk);
+
+  // ---- prologue: rotate the queries, project them, build the tables
+  if (tid < 2 * QH) amax[tid] = 0;
+  for (int i = tid; i < QH * KD; i += NT) {
+    const int hh = i / KD, j = i % KD;
+    const int gq = QH * quad + hh;  // query head within the GQA group
+    float v = 0.0f;
+    if (gq < a.G) v = load_q(a.q, a.q_dtype, ((long long)b * a.Hq + hkv * a.G + gq) * KD + j);
+    const int part = F::GROUPED ? j / F::PD : 0;
+    const float* sig = (const float*)(a.tables + H->off_sigma[part]);
+    qp[i] = v * sig[j - part * F::PD];
+  }
+  __syncthreads();
+  // Walsh-Hadamard butterflies, one stage per barrier (64-point halves for GROUPED)
+  for (int st = 1; st < F::PD; st <<= 1) {
+    for (int i = tid; i < QH * KD / 2; i += NT) {
+      const int hh = i / (KD / 2), r = i % (KD / 2);
+      const int lo = ((r / st) * 2 * st) + (r % st);
+      float* base = qp + hh * KD;
+      const float x = base[lo], y = base[lo + st];
+      base[lo] = x + y;
+      base[lo + st] = x - y;
+    }
+    __syncthreads();
+  }
+  if constexpr (F::PROD) {
+    const uint16_t* S = (const uint16_t*)(a.tables + H->off_S);
+    for (int i = tid; i < QH * KD; i += NT) {
+      const int hh = i / KD, row = i % KD;
+      const float* x = qp + hh * KD;
+      const uint16_t* srow = S + (size_t)row * KD;
+      float acc = 0.0f;
+      for (int j = 0; j < KD; ++j) acc = fmaf(h2f(srow[j]), x[j], acc);
+      qs[i] = acc;
+    }
+    __syncthreads();
+  }
+  // per-head, per-class magnitude bound -> power-of-two table scale
+  for (int i = tid; i < QH * KD; i += NT) {
+    const int hh = i / KD, j = i % KD;
+    int cls = 0;
+    float v = fabsf(qp[i]);
+    if (F::GROUPED) cls = j / F::PD;
+    atomicMax(&amax[cls * QH + hh], __float_as_int(v));
+    if (F::PROD) atomicMax(&amax[QH + hh], __float_as_int(fabsf(qs[i])));
+  }
+  __syncthreads();
+  if (tid < 2 * QH) {
+    const int cls = tid / QH;
+    const int part = F::GROUPED ? cls : 0;
+    float cmax = 1.0f;
+    int cpb = 8;
+    if (!(F::PROD && cls == 1)) {
+      const int L = H->part_levels[part];
+      cmax = fabsf(((const float*)(a.tables + H->off_centroids[part]))[L - 1]);
+      cpb = cls == 0 ? F::CPB0 : F::CPB1;
+    }
+    const float bound = __int_as_float(amax[tid]) * cmax * cpb;
+    scl[tid] = bound > 0.0f ? exp2f(floorf(log2f(16384.0f / bound))) : 1.0f;
+  }
+  __syncthreads();
+  for (int e = tid; e < F::E0 + F::E1; e += NT) {
+    const bool c1 = e >= F::E0;
+    const int ee = c1 ? e - F::E0 : e;
+    const int S = c1 ? F::S1 : F::S0;
+    const int p = ee / S, v = ee % S;
+    float s[QH] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (c1 && F::PROD) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float sg = ((v >> k) & 1) ? 1.0f : -1.0f;
+#pragma unroll
+        for (int hh = 0; hh < QH; ++hh) s[hh] = fmaf(sg, qs[hh * KD + 8 * p + k], s[hh]);
+      }
+    } else {
+      const int part = c1 ? 1 : 0;
+      const int W = c1 ? F::W1 : F::W0;
+      const int cpb = 8 / W;
+      const int bits = H->part_bits[F::GROUPED ? part : 0];
+      const int fmask = (1 << bits) - 1;
+      const float* cent = (const float*)(a.tables + H->off_centroids[F::GROUPED ? part : 0]);
+      const int j0 = part * F::PD + p * cpb;
+      for (int k = 0; k < cpb; ++k) {
+        const float c = cent[(v >> (W * k)) & fmask];
+#pragma unroll
+        for (int hh = 0; hh < QH; ++hh) s[hh] = fmaf(c, qp[hh * KD + j0 + k], s[hh]);
+      }
+    }
+    const float* sc = scl + (c1 ? QH : 0);
+    const uint32_t lo = (uint32_t)__half_as_ushort(__float2half_rn(s[0] * sc[0])) |
+                        ((uint32_t)__half_as_ushort(__float2half_rn(s[1] * sc[1])) << 16);
+    const uint32_t hi = (uint32_t)__half_as_ushort(__float2half_rn(s[2] * sc[2])) |
+                        ((uint32_t)__half_as_ushort(__float2half_rn(s[3] * sc[3])) << 16);
+    lut[e] = make_uint2(lo, hi);
+  }
+  __syncthreads();
+
+  // per-token multipliers of the two table classes, with the scales undone
+  float mul0[QH], mul1[QH];
+#pragma unroll
+  for (int hh = 0; hh < QH; ++hh) {
+    mul0[hh] = 1.0f / (scl[hh] * (float)F::PD);
+    mul1[hh] = F::PROD ? 1.2533141373155003f / ((float)KD * sqrtf((float)KD) * scl[QH + hh])
+                       : 1.0f / (scl[QH + hh] * (float)F::PD);
+  }
+  const float xscale = a.sm_scale * LOG2E;
+
+  float m_run[QH], l_run[QH], zacc[QH][4], acc[QH][8];
+#pragma unroll
+  for (int hh = 0; hh < QH; ++hh) {
+    m_run[hh] = -INFINITY;
+    l_run[hh] = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) zacc[hh][k] = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc[hh][k] = 0.0f;
+  }
+  const long long rec0 = ((long long)b * a.Hkv + hkv) * a.max_ctx;
+  uint32_t* wmine = wbuf + wave * (32 * 4 * QH);
+  const int slot = lane >> 4, u = lane & 15, grp = u >> 2;
+
+  for (int tb = t_begin + wave * TILE; tb < t_end; tb += NW * TILE) {
+    // ---------------- scores: lane = token
+    const int t = tb + lane;
+    const bool valid = t < t_end;
+    float sc[QH] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    float zz[4] = {0.0f, 0.0f, 0.0f, 0.0f}, ss[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (valid) {
+      const long long rec = rec0 + t;
+      uint32_t kw[F::KWORDS];
+      const uint32_t* ip = (const uint32_t*)(a.idx + rec * F::IDXB);
+#pragma unroll
+      for (int k = 0; k < F::IDXB / 4; ++k) kw[k] = ip[k];
+      if constexpr (F::PROD) {
+        const uint4 sv = *(const uint4*)(a.signs + rec * (KD / 8));
+        kw[F::IDXB / 4 + 0] = sv.x; kw[F::IDXB / 4 + 1] = sv.y;
+        kw[F::IDXB / 4 + 2] = sv.z; kw[F::IDXB / 4 + 3] = sv.w;
+      }
+      float m0, m1 = 0.0f;
+      if constexpr (F::GROUPED) {
+        const uint32_t nn = *(const uint32_t*)(a.norm + 2 * rec);
+        m0 = h2f(nn & 0xFFFFu);
+        m1 = h2f(nn >> 16);
+      } else {
+        m0 = h2f(a.norm[rec]);
+        if (F::PROD) m1 = h2f(a.rnorm[rec]);
+      }
+      float A[QH] = {0, 0, 0, 0}, Bc[QH] = {0, 0, 0, 0};
+#pragma unroll
+      for (int p = 0; p < F::P0; ++p) {
+        uint32_t v = (kw[p >> 2] >> (8 * (p & 3))) & 0xFFu;
+        if (B0 == 3) v &= 0x77u;
+        const uint2 e = lut[p * F::S0 + v];
+        A[0] += h2f(e.x & 0xFFFFu); A[1] += h2f(e.x >> 16);
+        A[2] += h2f(e.y & 0xFFFFu); A[3] += h2f(e.y >> 16);
+      }
+#pragma unroll
+      for (int p = 0; p < F::P1; ++p) {
+        const int byte = F::P0 + p;
+        uint32_t v = (kw[byte >> 2] >> (8 * (byte & 3))) & 0xFFu;
+        if (F::GROUPED && B1 == 3) v &= 0x77u;
+        const uint2 e = lut[F::E0 + p * F::S1 + v];
+        Bc[0] += h2f(e.x & 0xFFFFu); Bc[1] += h2f(e.x >> 16);
+        Bc[2] += h2f(e.y & 0xFFFFu); Bc[3] += h2f(e.y >> 16);
+      }
+#pragma unroll
+      for (int hh = 0; hh < QH; ++hh) sc[hh] = m0 * mul0[hh] * A[hh] + m1 * mul1[hh] * Bc[hh];
+      const uint2 zv = *(const uint2*)(a.vzero + rec * 4);
+      const uint2 sv2 = *(const uint2*)(a.vscale + rec * 4);
+      zz[0] = h2f(zv.x & 0xFFFFu); zz[1] = h2f(zv.x >> 16);
+      zz[2] = h2f(zv.y & 0xFFFFu); zz[3] = h2f(zv.y >> 16);
+      ss[0] = h2f(sv2.x & 0xFFFFu); ss[1] = h2f(sv2.x >> 16);
+      ss[2] = h2f(sv2.y & 0xFFFFu); ss[3] = h2f(sv2.y >> 16);
+      if (a.scores) {
+#pragma unroll
+        for (int hh = 0; hh < QH; ++hh) {
+          const int gq = QH * quad + hh;
+          if (gq < a.G) a.scores[((long long)b * a.Hq + hkv * a.G + gq) * a.max_ctx + t] = sc[hh];
+        }
+      }
+    }
+    // ---------------- online softmax (base 2)
+    float p[QH];
+#pragma unroll
+    for (int hh = 0; hh < QH; ++hh) {
+      const float x = sc[hh] * xscale;  // -inf for missing tokens
+      const float mt = wave_max(x);
+      const float mn = fmaxf(m_run[hh], mt);
+      const float alpha = mn == -INFINITY ? 1.0f : exp2f(m_run[hh] - mn);
+      p[hh] = mn == -INFINITY ? 0.0f : exp2f(x - mn);
+      m_run[hh] = mn;
+      l_run[hh] = l_run[hh] * alpha + p[hh];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) zacc[hh][k] = fmaf(p[hh], zz[k], zacc[hh][k] * alpha);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) acc[hh][k] *= alpha;
+    }
+    // weights p * scale as fp16, paired by token: wbuf[pair][group][head] = (w_even, w_odd)
+    {
+      uint16_t* wb16 = (uint16_t*)wmine;
+      const int pair = lane >> 1, odd = lane & 1;
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+#pragma unroll
+        for (int hh = 0; hh < QH; ++hh)
+          wb16[((pair * 4 + k) * QH + hh) * 2 + odd] = __half_as_ushort(__float2half_rn(p[hh] * ss[k]));
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // ---------------- p.V: lane = (slot, 8-dim slice u)
+#pragma unroll 2
+    for (int k = 0; k < 8; ++k) {
+      const int pr = slot + 4 * k;
+      const int tA = tb + 2 * pr, tB = tA + 1;
+      uint32_t cA = 0, cB = 0;
+      if (VB == 2) {
+        if (tA < t_end) cA = *(const uint16_t*)(a.vcodes + (rec0 + tA) * 32 + 2 * u);
+        if (tB < t_end) cB = *(const uint16_t*)(a.vcodes + (rec0 + tB) * 32 + 2 * u);
+      } else {
+        if (tA < t_end) cA = *(const uint32_t*)(a.vcodes + (rec0 + tA) * 64 + 4 * u);
+        if (tB < t_end) cB = *(const uint32_t*)(a.vcodes + (rec0 + tB) * 64 + 4 * u);
+      }
+      const uint4 wv = *(const uint4*)(wmine + (pr * 4 + grp) * QH);
+      const uint32_t wh[QH] = {wv.x, wv.y, wv.z, wv.w};
+      uint32_t pairs[8];
+      if (VB == 2) {
+        const uint32_t Y = cA | (cB << 16);
+        const uint32_t Y2 = (Y >> 8) & 0x00FF00FFu;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          pairs[i] = Y & (0x00030003u << (2 * i));
+          pairs[4 + i] = Y2 & (0x00030003u << (2 * i));
+        }
+      } else {
+        const uint32_t Ylo = (cA & 0xFFFFu) | (cB << 16);
+        const uint32_t Yhi = (cA >> 16) | (cB & 0xFFFF0000u);
+        const uint32_t Ylo2 = (Ylo >> 8) & 0x00FF00FFu, Yhi2 = (Yhi >> 8) & 0x00FF00FFu;
+        pairs[0] = Ylo & 0x000F000Fu;  pairs[1] = Ylo & 0x00F000F0u;
+        pairs[2] = Ylo2 & 0x000F000Fu; pairs[3] = Ylo2 & 0x00F000F0u;
+        pairs[4] = Yhi & 0x000F000Fu;  pairs[5] = Yhi & 0x00F000F0u;
+        pairs[6] = Yhi2 & 0x000F000Fu; pairs[7] = Yhi2 & 0x00F000F0u;
+      }
+#pragma unroll
+      for (int hh = 0; hh < QH; ++hh) {
+        const half2_t w2 = __builtin_bit_cast(half2_t, wh[hh]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          acc[hh][i] = __builtin_amdgcn_fdot2(w2, __builtin_bit_cast(half2_t, pairs[i]), acc[hh][i], false);
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+
+  // ---- combine: lanes -> wave -> workgroup
+  // undo the subnormal placement: dim i of a slice carries code * 2^-24 * step_i
+  float ocode[QH][8];
+#pragma unroll
+  for (int hh = 0; hh < QH; ++hh)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float step = VB == 2 ? (float)(1 << (2 * (i & 3))) : (float)(1 << (4 * (i & 1)));
+      float v = acc[hh][i];
+      v += __shfl_xor(v, 16);
+      v += __shfl_xor(v, 32);
+      ocode[hh][i] = v * (16777216.0f / step);
+    }
+  float lsum[QH], zsum[QH][4];
+#pragma unroll
+  for (int hh = 0; hh < QH; ++hh) {
+    lsum[hh] = wave_sum(l_run[hh]);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) zsum[hh][k] = wave_sum(zacc[hh][k]);
+  }
+  __syncthreads();  // tables are no longer read: reuse them for the merge
+  float* red = (float*)smem;  // [NW][QH][2 + 4 + KD]
+  constexpr int RS = 2 + 4 + KD;
+  {
+    float* mine = red + wave * QH * RS;
+    if (lane < 16) {
+#pragma unroll
+      for (int hh = 0; hh < QH; ++hh)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) mine[hh * RS + 6 + 8 * u + i] = ocode[hh][i];
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int hh = 0; hh < QH; ++hh) {
+        mine[hh * RS + 0] = m_run[hh];
+        mine[hh * RS + 1] = lsum[hh];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) mine[hh * RS + 2 + k] = zsum[hh][k];
+      }
+    }
+  }
+  __syncthreads();
+  if (tid < QH * KD) {
+    const int hh = tid / KD, j = tid % KD;
+    const int gq = QH * quad + hh;
+    float M = -INFINITY;
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, red[(w * QH + hh) * RS]);
+    float L = 0.0f, O = 0.0f;
+    if (M != -INFINITY) {
+      for (int w = 0; w < NW; ++w) {
+        const float* r = red + (w * QH + hh) * RS;
+        const float f = r[0] == -INFINITY ? 0.0f : exp2f(r[0] - M);
+        L = fmaf(r[1], f, L);
+        O = fmaf(r[6 + j] + r[2 + j / 32], f, O);
+      }
+    }
+    if (gq < a.G) {
+      float* dst = a.part + (((long long)b * a.Hq + hkv * a.G + gq) * a.n_split + split) * PART;
+      if (j == 0) {
+        dst[0] = M;
+        dst[1] = L;
+      }
+      dst[2 + j] = O;
+    }
+  }
+}
+
+// out[b][h][:] = sum_s O_s 2^(M_s - M) / sum_s L_s 2^(M_s - M), in split order.
+__global__ __launch_bounds__(KD) void merge_kernel(const float* part, int n_split, float* out,
+                                                   float* lse) {
+  const int bh = blockIdx.x, j = threadIdx.x;
+  const float* p = part + (long long)bh * n_split * PART;
+  float M = -INFINITY;
+  for (int s = 0; s < n_split; ++s) M = fmaxf(M, p[s * PART]);
+  float L = 0.0f, O = 0.0f;
+  if (M != -INFINITY) {
+    for (int s = 0; s < n_split; ++s) {
+      const float* r = p + s * PART;
+      const float f = r[0] == -INFINITY ? 0.0f : exp2f(r[0] - M);
+      L = fmaf(r[1], f, L);
+      O = fmaf(r[2 + j], f, O);
+    }
+  }
+  out[(long long)bh * KD + j] = L > 0.0f ? O / L : 0.0f;
+  if (lse && j == 0) lse[bh] = L > 0.0f ? (M + log2f(L)) * 0.69314718055994531f : -INFINITY;
+}
+
+int cu_count() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return -1;
+  if (dev >= 0 && dev < 64) {
+    int v = cached[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    return -1;
+  if (dev >= 0 && dev < 64) cached[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+template <int MODE, int B0, int B1>
+size_t smem_bytes() {
+  using F = Fmt<MODE, B0, B1>;
+  return (size_t)(F::E0 + F::E1) * 8 + 2 * QH * KD * 4 + NW * 32 * 4 * QH * 4 + 4 * QH * 4;
+}
+
+template <int MODE, int B0, int B1, int VB>
+hipError_t launch(const DecArgs& a, dim3 grid, hipStream_t s) {
+  const size_t sm = smem_bytes<MODE, B0, B1>();
+  static std::atomic<bool> attr_set{false};
+  if (!attr_set.load(std::memory_order_relaxed)) {
+    hipError_t e = hipFuncSetAttribute((const void*)decode_kernel<MODE, B0, B1, VB>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm);
+    if (e != hipSuccess) return e;
+    attr_set.store(true, std::memory_order_relaxed);
+  }
+  hipLaunchKernelGGL((decode_kernel<MODE, B0, B1, VB>), grid, dim3(NT), sm, s, a);
+  return hipGetLastError();
+}
+
+template <int MODE, int B0, int B1>
+hipError_t launch_vb(int vb, const DecArgs& a, dim3 grid, hipStream_t s) {
+  return vb == 2 ? launch<MODE, B0, B1, 2>(a, grid, s) : launch<MODE, B0, B1, 4>(a, grid, s);
+}
+
+// Formats with a kernel: returns false for the rest.
+bool supported(const tq::Parts& P) {
+  if (P.mode == TQ_MODE_GROUPED) {
+    const int b0 = P.part_bits[0], b1 = P.part_bits[1];
+    return (b0 == 4 && b1 == 2) || (b0 == 2 && b1 == 2) || (b0 == 3 && b1 == 2) || (b0 == 4 && b1 == 1);
+  }
+  return P.part_bits[0] >= 1 && P.part_bits[0] <= 3;
+}
+
+hipError_t dispatch(const tq::Parts& P, int vb, const DecArgs& a, dim3 grid, hipStream_t s) {
+  if (P.mode == TQ_MODE_PROD) {
+    switch (P.part_bits[0]) {
+      case 1: return launch_vb<TQ_MODE_PROD, 1, 0>(vb, a, grid, s);
+      case 2: return launch_vb<TQ_MODE_PROD, 2, 0>(vb, a, grid, s);
+      default: return launch_vb<TQ_MODE_PROD, 3, 0>(vb, a, grid, s);
+    }
+  }
+  if (P.mode == TQ_MODE_MSE) {
+    switch (P.part_bits[0]) {
+      case 1: return launch_vb<TQ_MODE_MSE, 1, 0>(vb, a, grid, s);
+      case 2: return launch_vb<TQ_MODE_MSE, 2, 0>(vb, a, grid, s);
+      default: return launch_vb<TQ_MODE_MSE, 3, 0>(vb, a, grid, s);
+    }
+  }
+  const int b0 = P.part_bits[0], b1 = P.part_bits[1];
+  if (b0 == 4 && b1 == 2) return launch_vb<TQ_MODE_GROUPED, 4, 2>(vb, a, grid, s);
+  if (b0 == 2 && b1 == 2) return launch_vb<TQ_MODE_GROUPED, 2, 2>(vb, a, grid, s);
+  if (b0 == 3 && b1 == 2) return launch_vb<TQ_MODE_GROUPED, 3, 2>(vb, a, grid, s);
+  return launch_vb<TQ_MODE_GROUPED, 4, 1>(vb, a, grid, s);
+}
+
+}  // namespace
+
+extern "C" tq_status tq_decode_attention(const tq_key_config* cfg, const void* tables, const void* q,
+                                        int32_t q_dtype, int32_t B, int32_t Hq, int32_t Hkv,
+                                        const int32_t* ctx_len, int32_t max_ctx, const uint8_t* idx,
+                                        const uint8_t* signs, const uint16_t* norm,
+                                        const uint16_t* rnorm, int32_t v_bits, int32_t v_group,
+                                        const uint8_t* v_codes, const uint16_t* v_scale,
+                                        const uint16_t* v_zero, float sm_scale, float* out,
+                                        float* lse, float* scores, void* workspace,
+                                        size_t* workspace_bytes, void* stream) {
+  tq::Parts P;
+  tq_status st = tq::describe(cfg, &P);
+  if (st != TQ_OK) return st;
+  if (P.d != KD || !supported(P)) return TQ_ERR_UNSUPPORTED;
+  if (v_bits != 2 && v_bits != 4) return TQ_ERR_UNSUPPORTED;
+  if (v_group != 32) return TQ_ERR_UNSUPPORTED;
+  if (q_dtype != TQ_F32 && q_dtype != TQ_BF16 && q_dtype != TQ_F16) return TQ_ERR_ARG;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || max_ctx <= 0) return TQ_ERR_ARG;
+  if (!workspace_bytes) return TQ_ERR_ARG;
+  const int cus = cu_count();
+  if (cus <= 0) return TQ_ERR_HIP;
+  const int G = Hq / Hkv;
+  const int n_quads = (G + QH - 1) / QH;
+  const long long groups = (long long)B * Hkv * n_quads;
+  if ((long long)B * Hkv > 65535 || n_quads > 65535) return TQ_ERR_ARG;
+  // split the context so that the grid covers every CU about once
+  const int max_tiles = (max_ctx + TILE - 1) / TILE;
+  int n_split = (int)((cus + groups - 1) / groups);
+  const int tiles_per_split_min = NW;  // at least one tile per wave
+  if (n_split > (max_tiles + tiles_per_split_min - 1) / tiles_per_split_min)
+    n_split = (max_tiles + tiles_per_split_min - 1) / tiles_per_split_min;
+  if (n_split < 1) n_split = 1;
+  const int chunk_tiles = (max_tiles + n_split - 1) / n_split;
+  n_split = (max_tiles + chunk_tiles - 1) / chunk_tiles;
+  const size_t need = (size_t)B * Hq * n_split * PART * sizeof(float);
+  if (!workspace) {
+    *workspace_bytes = need;
+    return TQ_OK;
+  }
+  if (*workspace_bytes < need) return TQ_ERR_WORKSPACE;
+  if (!tables || !q || !ctx_len || !idx || !norm || !v_codes || !v_scale || !v_zero || !out)
+    return TQ_ERR_ARG;
+  if (P.mode == TQ_MODE_PROD && (!signs || !rnorm)) return TQ_ERR_ARG;
+  if (!tq::aligned16(tables) || !tq::aligned16(idx) || !tq::aligned16(v_codes) ||
+      !tq::aligned16(workspace) || !tq::aligned16(q))
+    return TQ_ERR_ARG;
+  if (P.mode == TQ_MODE_PROD && !tq::aligned16(signs)) return TQ_ERR_ARG;
+  if (((uintptr_t)v_scale & 7) || ((uintptr_t)v_zero & 7) || ((uintptr_t)norm & 3) ||
+      ((uintptr_t)out & 3))
+    return TQ_ERR_ARG;
+  if (max_ctx > 0x7fffffff / 2) return TQ_ERR_ARG;
+
+  DecArgs a;
+  a.tables = (const unsigned char*)tables;
+  a.q = q;
+  a.q_dtype = q_dtype;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.G = G;
+  a.n_quads = n_quads;
+  a.ctx_len = ctx_len;
+  a.max_ctx = max_ctx;
+  a.idx = idx;
+  a.signs = signs;
+  a.norm = norm;
+  a.rnorm = rnorm;
+  a.vcodes = v_codes;
+  a.vscale = v_scale;
+  a.vzero = v_zero;
+  a.sm_scale = sm_scale;
+  a.scores = scores;
+  a.part = (float*)workspace;
+  a.n_split = n_split;
+  a.chunk = chunk_tiles * TILE;
+  hipStream_t s = (hipStream_t)stream;
+  const dim3 grid(n_split, n_quads, B * Hkv);
+  if (dispatch(P, v_bits, a, grid, s) != hipSuccess) return TQ_ERR_HIP;
+  hipLaunchKernelGGL(merge_kernel, dim3(B * Hq), dim3(KD), 0, s, (const float*)workspace, n_split,
+                     out, lse);
+  return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_HIP;
+}

@@ -1,0 +1,510 @@
+// Key and value encoders for gfx950.
+//
+// Keys ("tqlite" README, mode table and 设计要点; difai.kr tutorial 算法概述;
+// bit-packing article sections 二-四):
+//   n = ||k||, y = H (sigma * k) / n  (128-point fast Walsh-Hadamard transform,
+//   O(d log d) as the "tqlite" README's 已知限制 asks), idx_j = #{t : y_j >= t},
+//   PROD: r = y - c[idx], signs [S r >= 0] (the one dense contraction, on
+//   MFMA), rho = n ||r|| / sqrt(d).
+// Values (bit-packing article sections 二/三): per-token groups of 32 channels,
+// asymmetric min/max with fp16 scale and zero, 2- or 4-bit codes.
+//
+// Thread mapping of the key encoder.  A wave encodes 16 keys per tile.  Lane l
+// works on key (l & 15) and holds 32 of its 128 coordinates in registers x[r]:
+// on load, x[8c + i] is coordinate 32c + 8g + i with g = l >> 4.  The
+// transform runs five butterfly stages inside each lane (coordinate bits 0, 1,
+// 2, 5, 6) and two across lanes (bits 3 and 4) with v_permlane16_swap /
+// v_permlane32_swap: each swap hands a lane both inputs of one butterfly, and
+// in doing so trades the lane bit for a register bit.  After the transform x[r]
+// is coordinate 32g + r, so each lane owns a contiguous quarter of the key:
+// exactly the operand layout v_mfma_f32_16x16x32_f16 wants for B = R^T
+// (lane l: column l & 15, eight consecutive k per lane group), and a
+// contiguous run of packed index bytes.
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+
+#include "tq.h"
+#include "tq_internal.h"
+#include "tq_tables.h"
+
+namespace {
+
+__device__ inline int index_width_dev(int bits) { return bits == 1 ? 1 : bits == 2 ? 2 : bits <= 4 ? 4 : 8; }
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+constexpr int KD = 128;        // head dimension of the kernels
+constexpr int TILE_KEYS = 16;  // keys per wave tile
+constexpr int WAVES = 4;       // waves per block
+constexpr int MAX_LEVELS = 256;
+
+struct KeyArgs {
+  const unsigned char* tables;
+  const void* keys;
+  long long n_vec;
+  long long row_stride;  // elements
+  const long long* slots;
+  long long n_records;
+  uint8_t* idx;
+  uint8_t* signs;
+  uint16_t* norm;
+  uint16_t* rnorm;
+  int idx_row_bytes;
+  int n_tiles;
+};
+
+template <int DT>
+__device__ inline void load8(const void* base, long long elem_off, float* out) {
+  if constexpr (DT == TQ_F32) {
+    const float4* p = (const float4*)((const float*)base + elem_off);
+    float4 a = p[0], b = p[1];
+    out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
+    out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
+  } else {
+    const uint4 v = *(const uint4*)((const uint16_t*)base + elem_off);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      if constexpr (DT == TQ_BF16) {
+        out[2 * k] = __uint_as_float(w[k] << 16);
+        out[2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
+      } else {
+        out[2 * k] = __half2float(__ushort_as_half((unsigned short)(w[k] & 0xFFFFu)));
+        out[2 * k + 1] = __half2float(__ushort_as_half((unsigned short)(w[k] >> 16)));
+      }
+    }
+  }
+}
+
+__device__ inline float xor_sum(float v, int m) { return v + __shfl_xor(v, m); }
+
+// In-lane butterflies on register bit `bit` (stride s = 1 << bit).
+template <int S>
+__device__ inline void stage_in_lane(float* x) {
+#pragma unroll
+  for (int r = 0; r < 32; ++r) {
+    if ((r & S) == 0) {
+      float a = x[r], b = x[r + S];
+      x[r] = a + b;
+      x[r + S] = a - b;
+    }
+  }
+}
+
+// Cross-lane butterflies on lane bit 4 (xor 16, paired with register bit 3)
+// and lane bit 5 (xor 32, paired with register bit 4).
+__device__ inline void stage_cross16(float* x) {
+#pragma unroll
+  for (int r = 0; r < 32; ++r) {
+    if ((r & 8) == 0) {
+      auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x[r]), __float_as_uint(x[r + 8]),
+                                                false, false);
+      float a = __uint_as_float(p[0]), b = __uint_as_float(p[1]);
+      x[r] = a + b;
+      x[r + 8] = a - b;
+    }
+  }
+}
+
+__device__ inline void stage_cross32(float* x) {
+#pragma unroll
+  for (int r = 0; r < 32; ++r) {
+    if ((r & 16) == 0) {
+      auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x[r]), __float_as_uint(x[r + 16]),
+                                                false, false);
+      float a = __uint_as_float(p[0]), b = __uint_as_float(p[1]);
+      x[r] = a + b;
+      x[r + 16] = a - b;
+    }
+  }
+}
+
+__device__ inline int bucketize(float y, const tq_hint* hint, int hn, float lo, float scale) {
+  float f = floorf((y - lo) * scale);
+  f = fminf(fmaxf(f, 0.0f), (float)(hn - 1));  // NaN -> 0 (fmax returns the number)
+  const tq_hint h = hint[(int)f];
+  return h.h + (y >= h.t_h ? 1 : 0) + (y >= h.t_h1 ? 1 : 0);
+}
+
+// Pack 32 indices of width W (coordinates 32g .. 32g+31 of one part) and
+// store them at dst (byte offset already applied; 4-byte aligned).
+template <int W>
+__device__ inline void store_fields(uint8_t* dst, const int* q) {
+  constexpr int PER = 32 / W;  // fields per dword
+  uint32_t* d = (uint32_t*)dst;
+#pragma unroll
+  for (int k = 0; k < W; ++k) {
+    uint32_t v = 0;
+#pragma unroll
+    for (int r = 0; r < PER; ++r) v |= (uint32_t)q[k * PER + r] << (W * r);
+    d[k] = v;
+  }
+}
+
+__device__ inline void store_idx(int w, uint8_t* dst, const int* q) {
+  switch (w) {
+    case 1: store_fields<1>(dst, q); break;
+    case 2: store_fields<2>(dst, q); break;
+    case 4: store_fields<4>(dst, q); break;
+    default: store_fields<8>(dst, q); break;
+  }
+}
+
+// MODE: TQ_MODE_MSE / PROD / GROUPED.  DT: input dtype.
+template <int MODE, int DT>
+__global__ __launch_bounds__(WAVES * 64) void encode_keys_kernel(KeyArgs a) {
+  const tq_blob_header* H = (const tq_blob_header*)a.tables;
+  constexpr int NP = MODE == TQ_MODE_GROUPED ? 2 : 1;
+  __shared__ tq_hint s_hint[NP][TQ_MAX_HINT];
+  __shared__ float s_cent[MAX_LEVELS];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int g = lane >> 4;     // lane group: quarter of the key
+  const int kk = lane & 15;    // key within the tile
+
+  int hn[NP];
+  float hlo[NP], hsc[NP];
+  for (int p = 0; p < NP; ++p) {
+    hn[p] = H->hint_n[p];
+    hlo[p] = H->hint_lo[p];
+    hsc[p] = H->hint_scale[p];
+    const tq_hint* src = (const tq_hint*)(a.tables + H->off_hint[p]);
+    for (int i = threadIdx.x; i < hn[p]; i += blockDim.x) s_hint[p][i] = src[i];
+  }
+  if (MODE == TQ_MODE_PROD) {
+    const float* c = (const float*)(a.tables + H->off_centroids[0]);
+    for (int i = threadIdx.x; i < H->part_levels[0]; i += blockDim.x) s_cent[i] = c[i];
+  }
+  __syncthreads();
+
+  // sign mask: bit r set when sigma of the coordinate loaded into x[r] is -1
+  uint32_t sigmask = 0;
+  for (int r = 0; r < 32; ++r) {
+    const int j = 32 * (r >> 3) + 8 * g + (r & 7);
+    float s;
+    if (MODE == TQ_MODE_GROUPED) {
+      const int part = j >= KD / 2;
+      s = ((const float*)(a.tables + H->off_sigma[part]))[j - part * (KD / 2)];
+    } else {
+      s = ((const float*)(a.tables + H->off_sigma[0]))[j];
+    }
+    if (s < 0) sigmask |= 1u << r;
+  }
+
+  // S fragments for A = S (16 rows per tile nt, k = coordinates
+  // 32*(l>>4) + 8*ks + i, matching the B = R^T layout after the transform).
+  half8 sfrag[MODE == TQ_MODE_PROD ? 8 : 1][4];
+  if constexpr (MODE == TQ_MODE_PROD) {
+    const uint16_t* S = (const uint16_t*)(a.tables + H->off_S);
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        sfrag[nt][ks] = *(const half8*)(S + (size_t)(16 * nt + kk) * KD + 32 * g + 8 * ks);
+  }
+
+  const float inv_sqrt_d = 1.0f / sqrtf((float)KD);
+  const int w0 = index_width_dev(H->part_bits[0]);
+  const int w1 = NP == 2 ? index_width_dev(H->part_bits[1]) : 0;
+
+  for (int tile = blockIdx.x * WAVES + wave; tile < a.n_tiles; tile += gridDim.x * WAVES) {
+    const long long row = (long long)tile * TILE_KEYS + kk;
+    const bool valid = row < a.n_vec;
+    float x[32];
+    if (valid) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) load8<DT>(a.keys, row * a.row_stride + 32 * c + 8 * g, x + 8 * c);
+    } else {
+#pragma unroll
+      for (int r = 0; r < 32; ++r) x[r] = 0.0f;
+    }
+    // squared norm per part (part = register bit 4 in this layout)
+    float ss0 = 0.0f, ss1 = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      ss0 = fmaf(x[r], x[r], ss0);
+      ss1 = fmaf(x[r + 16], x[r + 16], ss1);
+    }
+    ss0 = xor_sum(xor_sum(ss0, 16), 32);
+    ss1 = xor_sum(xor_sum(ss1, 16), 32);
+#pragma unroll
+    for (int r = 0; r < 32; ++r)
+      x[r] = __uint_as_float(__float_as_uint(x[r]) ^ (((sigmask >> r) & 1u) << 31));
+
+    stage_in_lane<1>(x);
+    stage_in_lane<2>(x);
+    stage_in_lane<4>(x);
+    stage_in_lane<8>(x);
+    if (MODE != TQ_MODE_GROUPED) stage_in_lane<16>(x);
+    stage_cross16(x);
+    stage_cross32(x);
+
+    // now x[r] is coordinate 32g + r
+    float n_part[2];
+    if (MODE == TQ_MODE_GROUPED) {
+      n_part[0] = sqrtf(ss0);
+      n_part[1] = sqrtf(ss1);
+    } else {
+      n_part[0] = n_part[1] = sqrtf(ss0 + ss1);
+    }
+    const int part = MODE == TQ_MODE_GROUPED ? (g >> 1) : 0;
+    const float n = n_part[part];
+    const float inv = n > 0.0f ? 1.0f / n : 0.0f;
+    int q[32];
+    const tq_hint* hint = s_hint[NP == 2 ? part : 0];
+    const int hnn = NP == 2 ? hn[part] : hn[0];
+    const float hl = NP == 2 ? hlo[part] : hlo[0];
+    const float hs = NP == 2 ? hsc[part] : hsc[0];
+#pragma unroll
+    for (int r = 0; r < 32; ++r) {
+      x[r] *= inv;
+      q[r] = bucketize(x[r], hint, hnn, hl, hs);
+    }
+
+    long long slot = row;
+    if (a.slots && valid) slot = a.slots[row];
+    const bool store = valid && slot >= 0 && slot < a.n_records;
+
+    if (store) {
+      uint8_t* dst = a.idx + slot * a.idx_row_bytes;
+      if (MODE == TQ_MODE_GROUPED) {
+        const int w = part ? w1 : w0;
+        const int off = part ? (KD / 2) * w0 / 8 + 32 * (g - 2) * w / 8 : 32 * g * w / 8;
+        store_idx(w, dst + off, q);
+        if (g == 0) {
+          const uint32_t pk = (uint32_t)__half_as_ushort(__float2half_rn(n_part[0])) |
+                              ((uint32_t)__half_as_ushort(__float2half_rn(n_part[1])) << 16);
+          *(uint32_t*)(a.norm + 2 * slot) = pk;
+        }
+      } else {
+        store_idx(w0, dst + 32 * g * w0 / 8, q);
+        if (g == 0) a.norm[slot] = __half_as_ushort(__float2half_rn(n));
+      }
+    }
+
+    if constexpr (MODE == TQ_MODE_PROD) {
+      float rr = 0.0f;
+      half8 bhi[4], blo[4];
+#pragma unroll
+      for (int r = 0; r < 32; ++r) {
+        const float res = x[r] - s_cent[q[r]];
+        rr = fmaf(res, res, rr);
+        const _Float16 h = (_Float16)res;
+        const _Float16 lo = (_Float16)(res - (float)h);
+        bhi[r >> 3][r & 7] = h;
+        blo[r >> 3][r & 7] = lo;
+      }
+      rr = xor_sum(xor_sum(rr, 16), 32);
+      floatx4 acc[8];
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) {
+        acc[nt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(sfrag[nt][ks], blo[ks], acc[nt], 0, 0, 0);
+          acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(sfrag[nt][ks], bhi[ks], acc[nt], 0, 0, 0);
+        }
+      }
+      // lane holds projections of key kk onto S rows 16nt + 4g + i
+      uint32_t dw[4];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        uint32_t n0 = 0, n1 = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          n0 |= (acc[2 * w][i] >= 0.0f ? 1u : 0u) << i;
+          n1 |= (acc[2 * w + 1][i] >= 0.0f ? 1u : 0u) << i;
+        }
+        uint32_t v = (n0 << (4 * g)) | (n1 << (16 + 4 * g));
+        v |= __shfl_xor(v, 16);
+        v |= __shfl_xor(v, 32);
+        dw[w] = v;
+      }
+      if (store) {
+        const uint32_t mine = g == 0 ? dw[0] : g == 1 ? dw[1] : g == 2 ? dw[2] : dw[3];
+        *(uint32_t*)(a.signs + slot * (KD / 8) + 4 * g) = mine;
+        if (g == 0) {
+          const float rho = n * sqrtf(rr) * inv_sqrt_d;
+          a.rnorm[slot] = __half_as_ushort(__float2half_rn(rho));
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- values
+// Lane l handles 8 consecutive channels of row (4 * wave_tile + l / 16); the
+// four lanes of one 32-channel group agree on min and max through two xor
+// shuffles.
+struct ValArgs {
+  const void* values;
+  long long n_vec;
+  long long row_stride;
+  const long long* slots;
+  long long n_records;
+  uint8_t* codes;
+  uint16_t* scale;
+  uint16_t* zero;
+  long long n_tiles;
+};
+
+template <int BITS, int DT>
+__global__ __launch_bounds__(256) void encode_values_kernel(ValArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int sub = lane & 15;          // 8-channel chunk within the row
+  const long long tiles_per_grid = (long long)gridDim.x * (blockDim.x >> 6);
+  for (long long tile = (long long)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+       tile < a.n_tiles; tile += tiles_per_grid) {
+    const long long row = tile * 4 + (lane >> 4);
+    const bool valid = row < a.n_vec;
+    float v[8];
+    if (valid) {
+      load8<DT>(a.values, row * a.row_stride + 8 * sub, v);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = 0.0f;
+    }
+    float mn = v[0], mx = v[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) {
+      mn = fminf(mn, v[i]);
+      mx = fmaxf(mx, v[i]);
+    }
+    mn = fminf(mn, __shfl_xor(mn, 1));
+    mx = fmaxf(mx, __shfl_xor(mx, 1));
+    mn = fminf(mn, __shfl_xor(mn, 2));
+    mx = fmaxf(mx, __shfl_xor(mx, 2));
+    constexpr float LEVELS = (float)((1 << BITS) - 1);
+    const float s32 = __fdiv_rn(__fsub_rn(mx, mn), LEVELS);
+    const __half s16 = __float2half_rn(s32);
+    const __half z16 = __float2half_rn(mn);
+    const float s = __half2float(s16), z = __half2float(z16);
+    uint32_t packed = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float c = 0.0f;
+      if (s != 0.0f) {
+        c = rintf(__fdiv_rn(__fsub_rn(v[i], z), s));
+        c = fminf(fmaxf(c, 0.0f), LEVELS);
+      }
+      packed |= (uint32_t)c << (BITS * i);
+    }
+    long long slot = row;
+    if (a.slots && valid) slot = a.slots[row];
+    if (valid && slot >= 0 && slot < a.n_records) {
+      if (BITS == 2) {
+        *(uint16_t*)(a.codes + slot * (KD * BITS / 8) + 2 * sub) = (uint16_t)packed;
+      } else {
+        *(uint32_t*)(a.codes + slot * (KD * BITS / 8) + 4 * sub) = packed;
+      }
+      if ((sub & 3) == 0) {
+        a.scale[slot * (KD / 32) + (sub >> 2)] = __half_as_ushort(s16);
+        a.zero[slot * (KD / 32) + (sub >> 2)] = __half_as_ushort(z16);
+      }
+    }
+  }
+}
+
+int grid_for(long long tiles, int per_block) {
+  long long blocks = (tiles + per_block - 1) / per_block;
+  const long long cap = 256LL * 8;  // enough to fill 256 CUs several times
+  if (blocks > cap) blocks = cap;
+  if (blocks < 1) blocks = 1;
+  return (int)blocks;
+}
+
+}  // namespace
+
+extern "C" tq_status tq_encode_keys(const tq_key_config* cfg, const void* tables, const void* keys,
+                                   int32_t dtype, int64_t n_vec, int64_t row_stride,
+                                   const int64_t* slots, int64_t n_records, uint8_t* idx,
+                                   uint8_t* signs, uint16_t* norm, uint16_t* rnorm, void* stream) {
+  tq::Parts P;
+  tq_status st = tq::describe(cfg, &P);
+  if (st != TQ_OK) return st;
+  if (P.d != KD) return TQ_ERR_UNSUPPORTED;
+  if (n_vec < 0 || n_records < 0) return TQ_ERR_ARG;
+  if (dtype != TQ_F32 && dtype != TQ_BF16 && dtype != TQ_F16) return TQ_ERR_ARG;
+  if (n_vec == 0) return TQ_OK;
+  if (!tables || !keys || !idx || !norm) return TQ_ERR_ARG;
+  const int esz = dtype == TQ_F32 ? 4 : 2;
+  if (row_stride < KD || ((row_stride * esz) & 15) || !tq::aligned16(keys)) return TQ_ERR_ARG;
+  if (!tq::aligned16(tables) || !tq::aligned16(idx) || ((uintptr_t)norm & 3)) return TQ_ERR_ARG;
+  if (P.mode == TQ_MODE_PROD) {
+    if (!signs || !rnorm || !tq::aligned16(signs) || ((uintptr_t)rnorm & 1)) return TQ_ERR_ARG;
+  } else if (signs || rnorm) {
+    return TQ_ERR_ARG;
+  }
+  if (slots && ((uintptr_t)slots & 7)) return TQ_ERR_ARG;
+  for (int p = 0; p < P.n_parts; ++p)
+    if (P.part_width[p] * P.part_d[p] / 8 % 4) return TQ_ERR_UNSUPPORTED;
+
+  KeyArgs a;
+  a.tables = (const unsigned char*)tables;
+  a.keys = keys;
+  a.n_vec = n_vec;
+  a.row_stride = row_stride;
+  a.slots = (const long long*)slots;
+  a.n_records = n_records;
+  a.idx = idx;
+  a.signs = signs;
+  a.norm = norm;
+  a.rnorm = rnorm;
+  a.idx_row_bytes = P.idx_row_bytes;
+  const long long tiles = (n_vec + TILE_KEYS - 1) / TILE_KEYS;
+  if (tiles > 0x7fffffffLL) return TQ_ERR_ARG;
+  a.n_tiles = (int)tiles;
+  const dim3 grid(grid_for(tiles, WAVES)), block(WAVES * 64);
+  hipStream_t s = (hipStream_t)stream;
+#define TQ_LAUNCH_KEYS(M)                                                                   \
+  do {                                                                                      \
+    if (dtype == TQ_F32) hipLaunchKernelGGL((encode_keys_kernel<M, TQ_F32>), grid, block, 0, s, a);   \
+    else if (dtype == TQ_BF16) hipLaunchKernelGGL((encode_keys_kernel<M, TQ_BF16>), grid, block, 0, s, a); \
+    else hipLaunchKernelGGL((encode_keys_kernel<M, TQ_F16>), grid, block, 0, s, a);           \
+  } while (0)
+  if (P.mode == TQ_MODE_MSE) TQ_LAUNCH_KEYS(TQ_MODE_MSE);
+  else if (P.mode == TQ_MODE_PROD) TQ_LAUNCH_KEYS(TQ_MODE_PROD);
+  else TQ_LAUNCH_KEYS(TQ_MODE_GROUPED);
+#undef TQ_LAUNCH_KEYS
+  return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_HIP;
+}
+
+extern "C" tq_status tq_encode_values(int32_t bits, int32_t group, int32_t d, const void* values,
+                                     int32_t dtype, int64_t n_vec, int64_t row_stride,
+                                     const int64_t* slots, int64_t n_records, uint8_t* codes,
+                                     uint16_t* scale, uint16_t* zero, void* stream) {
+  if (bits != 2 && bits != 4) return TQ_ERR_UNSUPPORTED;
+  if (group != 32 || d != KD) return TQ_ERR_UNSUPPORTED;
+  if (n_vec < 0 || n_records < 0) return TQ_ERR_ARG;
+  if (dtype != TQ_F32 && dtype != TQ_BF16 && dtype != TQ_F16) return TQ_ERR_ARG;
+  if (n_vec == 0) return TQ_OK;
+  if (!values || !codes || !scale || !zero) return TQ_ERR_ARG;
+  const int esz = dtype == TQ_F32 ? 4 : 2;
+  if (row_stride < KD || ((row_stride * esz) & 15) || !tq::aligned16(values)) return TQ_ERR_ARG;
+  if (!tq::aligned16(codes) || ((uintptr_t)scale & 1) || ((uintptr_t)zero & 1)) return TQ_ERR_ARG;
+  if (slots && ((uintptr_t)slots & 7)) return TQ_ERR_ARG;
+  ValArgs a;
+  a.values = values;
+  a.n_vec = n_vec;
+  a.row_stride = row_stride;
+  a.slots = (const long long*)slots;
+  a.n_records = n_records;
+  a.codes = codes;
+  a.scale = scale;
+  a.zero = zero;
+  a.n_tiles = (n_vec + 3) / 4;
+  const dim3 grid(grid_for(a.n_tiles, 4)), block(256);
+  hipStream_t s = (hipStream_t)stream;
+#define TQ_LAUNCH_VALS(B)                                                                   \
+  do {                                                                                      \
+    if (dtype == TQ_F32) hipLaunchKernelGGL((encode_values_kernel<B, TQ_F32>), grid, block, 0, s, a);  \
+    else if (dtype == TQ_BF16) hipLaunchKernelGGL((encode_values_kernel<B, TQ_BF16>), grid, block, 0, s, a); \
+    else hipLaunchKernelGGL((encode_values_kernel<B, TQ_F16>), grid, block, 0, s, a);          \
+  } while (0)
+  if (bits == 2) TQ_LAUNCH_VALS(2);
+  else TQ_LAUNCH_VALS(4);
+#undef TQ_LAUNCH_VALS
+  return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_HIP;
+}

@@ -105,8 +105,12 @@ def gaussian_matrix(seed: int, tag: int, m: int, d: int) -> np.ndarray:
 
     u1 = (top 53 bits + 1) * 2^-53 in (0,1], u2 = top 53 bits * 2^-53 in [0,1);
     r = sqrt(-2 ln u1); element 2i = r cos(2 pi u2), element 2i+1 = r sin(2 pi u2).
-    Each element is then rounded to float32 (the matrix is stored in float32)
-    and returned as float64 holding that float32 value."""
+    Each element is then rounded to float16 (round to nearest even) and
+    returned as float64 holding that value.
+    Reading: the pages fix no precision for S.  Rounding each N(0,1) draw to
+    fp16 keeps the entries i.i.d. and symmetric; the sign estimator's constant
+    sqrt(pi/2) assumes exact Gaussian rows, and the rounding (relative error
+    <= 2^-11) moves E[sign(s.r)(s.a)] by far less than its sampling noise."""
     n = m * d
     raw = splitmix64_stream(seed, tag, n + (n & 1))
     vals = []
@@ -117,7 +121,7 @@ def gaussian_matrix(seed: int, tag: int, m: int, d: int) -> np.ndarray:
         r = math.sqrt(-2.0 * math.log(u1))
         vals.append(r * math.cos(two_pi * u2))
         vals.append(r * math.sin(two_pi * u2))
-    a = np.array(vals[:n], dtype=np.float64).astype(np.float32).astype(np.float64)
+    a = np.array(vals[:n], dtype=np.float64).astype(np.float16).astype(np.float64)
     return a.reshape(m, d)
 
 

@@ -1,0 +1,216 @@
+"""Host-side checks of libtq (no GPU): exported symbols, the table blob against
+the oracle's independently derived tables, and argument validation that must
+return a status before anything is launched."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle.tq_oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+tq = pytest.importorskip("kv_cache_quantization_encode_amd")
+from kv_cache_quantization_encode_amd import _lib as L  # noqa: E402
+
+
+def test_library_exports_every_declared_symbol():
+    with open(os.path.join(ROOT, "include", "tq.h")) as f:
+        text = f.read()
+    declared = set(re.findall(r"^\s*(?:tq_status|size_t|const char\*)\s+(tq_\w+)\s*\(", text, re.M))
+    assert declared >= {"tq_build_codebook", "tq_encode_keys", "tq_encode_values", "tq_decode_attention"}
+    lib = ctypes.CDLL(L.LIB_PATH)
+    for name in declared:
+        assert hasattr(lib, name), name
+    # and nothing else with the tq_ prefix is exported
+    out = os.popen("nm -D --defined-only %s" % L.LIB_PATH).read()
+    exported = set(re.findall(r" T (tq_\w+)$", out, re.M))
+    assert exported == declared, exported ^ declared
+
+
+CFGS = [dict(mode="mse", bits=b) for b in (1, 2, 3, 4, 8)] + \
+       [dict(mode="prod", bits=b) for b in (2, 3, 4)] + \
+       [dict(mode="grouped", bits_outlier=4, bits_normal=2), dict(mode="grouped", bits_outlier=3, bits_normal=1)]
+
+
+def _oracle_cfg(kw, seed):
+    return O.KeyConfig(d=128, mode=kw["mode"], bits=kw.get("bits", 3), seed=seed,
+                       bits_outlier=kw.get("bits_outlier", 4), bits_normal=kw.get("bits_normal", 2))
+
+
+def _fp32_equal_or_tie(a32, ref64):
+    """float32 tables must equal the float64 value rounded to float32; a 1-ulp
+    difference is accepted only where the float64 value sits within 1e-12
+    (relative) of a rounding midpoint, where two correct float64 solvers may
+    round differently."""
+    want = ref64.astype(np.float32)
+    bad = a32 != want
+    if not bad.any():
+        return True
+    lo = np.nextafter(want, -np.inf).astype(np.float64)
+    hi = np.nextafter(want, np.inf).astype(np.float64)
+    mid = np.minimum(np.abs(ref64 - (want.astype(np.float64) + lo) / 2),
+                     np.abs(ref64 - (want.astype(np.float64) + hi) / 2))
+    return bool(np.all(mid[bad] <= 1e-12 * np.abs(ref64[bad])))
+
+
+@pytest.mark.parametrize("kw", CFGS, ids=lambda k: "-".join(str(v) for v in k.values()))
+@pytest.mark.parametrize("seed", [42, 7])
+def test_tables_match_oracle(kw, seed):
+    cfg = L.key_config(seed=seed, **kw)
+    blob, mse = tq.build_codebook(cfg)
+    h = tq.parse_tables(blob)
+    assert h["magic"] == 0x31425154 and h["total_bytes"] == blob.size
+    T = O.build_tables(_oracle_cfg(kw, seed))
+    if kw["mode"] == "grouped":
+        halves = T.halves
+    else:
+        halves = [dict(centroids=T.centroids, boundaries=T.boundaries, sigma=T.sigma, mse=T.mse,
+                       bits=T.cfg.idx_bits)]
+    assert h["n_parts"] == len(halves)
+    for part, half in zip(h["parts"], halves):
+        c64, t64, D = O.lloyd_max_gaussian(1 << half["bits"])
+        assert _fp32_equal_or_tie(part["centroids"], c64)
+        assert _fp32_equal_or_tie(part["bounds"][:-2], t64)
+        assert np.all(np.isinf(part["bounds"][-2:]))
+        assert np.array_equal(part["sigma"].astype(np.float64), half["sigma"])
+    for got, half in zip(mse, halves):
+        assert abs(got - half["mse"]) < 1e-12
+    if kw["mode"] == "prod":
+        assert np.array_equal(h["S"].astype(np.float64), T.S)
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 4, 5, 8])
+def test_hint_grid_reproduces_bucketize(bits):
+    """The blob's bucketize hint grid, evaluated on the host exactly as the
+    kernel does (float32), agrees with the oracle's count of boundaries."""
+    blob, _ = tq.build_codebook(L.key_config(mode="mse", bits=bits))
+    h = tq.parse_tables(blob)
+    part = h["parts"][0]
+    hint = part["hint"]
+    t = part["bounds"]
+    rng = np.random.default_rng(bits)
+    y = np.concatenate([rng.standard_normal(200000).astype(np.float32) * np.float32(1.7),
+                        t[:-2], np.nextafter(t[:-2], np.float32(-np.inf)), np.float32([0, -0.0, 11.3, -11.3])])
+    y = y.astype(np.float32)
+    lo, sc, n = np.float32(h["hint_lo"][0]), np.float32(h["hint_scale"][0]), h["hint_n"][0]
+    f = np.floor((y - lo) * sc).astype(np.float32)
+    g = np.clip(f, 0, n - 1).astype(np.int64)
+    th = hint[g, 0].view(np.float32)
+    th1 = hint[g, 1].view(np.float32)
+    idx = hint[g, 2] + (y >= th) + (y >= th1)
+    assert np.array_equal(idx, O.bucketize(y.astype(np.float64), t[:-2].astype(np.float64)))
+
+
+def test_idx_row_bytes():
+    assert tq.idx_row_bytes(L.key_config(mode="prod", bits=3)) == 32
+    assert tq.idx_row_bytes(L.key_config(mode="prod", bits=4)) == 64
+    assert tq.idx_row_bytes(L.key_config(mode="mse", bits=8)) == 128
+    assert tq.idx_row_bytes(L.key_config(mode="grouped", bits_outlier=4, bits_normal=2)) == 48
+    assert tq.idx_row_bytes(L.key_config(mode="mse", bits=9)) == 0
+
+
+BAD_CFGS = [dict(d=100), dict(d=8), dict(d=512), dict(mode=7), dict(mode="mse", bits=0),
+            dict(mode="mse", bits=9), dict(mode="prod", bits=1), dict(mode="prod", bits=10),
+            dict(mode="grouped", bits_outlier=0), dict(mode="grouped", bits_normal=9)]
+
+
+@pytest.mark.parametrize("kw", BAD_CFGS, ids=str)
+def test_bad_configs_rejected(kw):
+    cfg = L.key_config(**kw)
+    size = ctypes.c_size_t(0)
+    assert L.lib.tq_build_codebook(ctypes.byref(cfg), None, ctypes.byref(size), None) == L.TQ_ERR_ARG
+    st = L.lib.tq_encode_keys(ctypes.byref(cfg), 256, 256, L.TQ_BF16, 16, 128, None, 16, 256, 256,
+                              256, 256, None)
+    assert st == L.TQ_ERR_ARG
+
+
+def test_reserved_field_must_be_zero():
+    cfg = L.key_config()
+    cfg.reserved = 1
+    size = ctypes.c_size_t(0)
+    assert L.lib.tq_build_codebook(ctypes.byref(cfg), None, ctypes.byref(size), None) == L.TQ_ERR_ARG
+
+
+def test_blob_capacity_checked():
+    cfg = L.key_config()
+    size = ctypes.c_size_t(0)
+    assert L.lib.tq_build_codebook(ctypes.byref(cfg), None, ctypes.byref(size), None) == L.TQ_OK
+    need = size.value
+    buf = (ctypes.c_ubyte * need)()
+    small = ctypes.c_size_t(need - 1)
+    assert L.lib.tq_build_codebook(ctypes.byref(cfg), buf, ctypes.byref(small), None) == L.TQ_ERR_ARG
+    assert small.value == need
+
+
+FAKE = 1 << 20  # an aligned non-null address; validation must fail before any use
+
+
+def _enc(cfg, **kw):
+    a = dict(tables=FAKE, keys=FAKE, dtype=L.TQ_BF16, n=64, stride=128, slots=None, nrec=64,
+             idx=FAKE, signs=FAKE, norm=FAKE, rnorm=FAKE)
+    a.update(kw)
+    return L.lib.tq_encode_keys(ctypes.byref(cfg), a["tables"], a["keys"], a["dtype"], a["n"], a["stride"],
+                                a["slots"], a["nrec"], a["idx"], a["signs"], a["norm"], a["rnorm"], None)
+
+
+def test_encode_keys_argument_errors():
+    prod = L.key_config(mode="prod", bits=3)
+    mse = L.key_config(mode="mse", bits=4)
+    assert _enc(prod, n=0) == L.TQ_OK                          # no-op, nothing launched
+    assert _enc(prod, keys=None) == L.TQ_ERR_ARG
+    assert _enc(prod, keys=FAKE + 2) == L.TQ_ERR_ARG            # misaligned
+    assert _enc(prod, stride=100) == L.TQ_ERR_ARG               # shorter than a row
+    assert _enc(prod, stride=129) == L.TQ_ERR_ARG               # rows not 16-byte aligned
+    assert _enc(prod, signs=None) == L.TQ_ERR_ARG               # PROD needs the sign plane
+    assert _enc(mse) == L.TQ_ERR_ARG                            # MSE must not pass signs/rnorm
+    assert _enc(prod, n=-1) == L.TQ_ERR_ARG
+    assert _enc(prod, dtype=9) == L.TQ_ERR_ARG
+    assert _enc(L.key_config(d=64, mode="prod", bits=3)) == L.TQ_ERR_UNSUPPORTED
+
+
+def test_encode_values_argument_errors():
+    f = L.lib.tq_encode_values
+    args = lambda **kw: [kw.get("bits", 2), kw.get("group", 32), kw.get("d", 128), kw.get("v", FAKE),
+                         L.TQ_BF16, kw.get("n", 4), kw.get("stride", 128), None, 4, FAKE, FAKE, FAKE, None]
+    assert f(*args(bits=3)) == L.TQ_ERR_UNSUPPORTED
+    assert f(*args(group=64)) == L.TQ_ERR_UNSUPPORTED
+    assert f(*args(d=64)) == L.TQ_ERR_UNSUPPORTED
+    assert f(*args(v=None)) == L.TQ_ERR_ARG
+    assert f(*args(n=0)) == L.TQ_OK
+
+
+def _dec(cfg, **kw):
+    a = dict(q=FAKE, B=2, Hq=8, Hkv=2, ctx=FAKE, max_ctx=1024, vb=2, vg=32, ws=None,
+             wsb=ctypes.c_size_t(0), out=FAKE)
+    a.update(kw)
+    return L.lib.tq_decode_attention(ctypes.byref(cfg), FAKE, a["q"], L.TQ_BF16, a["B"], a["Hq"], a["Hkv"],
+                                     a["ctx"], a["max_ctx"], FAKE, FAKE, FAKE, FAKE, a["vb"], a["vg"],
+                                     FAKE, FAKE, FAKE, ctypes.c_float(0.1), a["out"], None, None,
+                                     a["ws"], ctypes.byref(a["wsb"]) if a["wsb"] is not None else None, None)
+
+
+def test_decode_argument_errors():
+    prod = L.key_config(mode="prod", bits=3)
+    assert _dec(prod, Hq=6, Hkv=4) == L.TQ_ERR_ARG             # Hq % Hkv != 0
+    assert _dec(prod, B=0) == L.TQ_ERR_ARG
+    assert _dec(prod, vb=3) == L.TQ_ERR_UNSUPPORTED
+    assert _dec(prod, vg=64) == L.TQ_ERR_UNSUPPORTED
+    assert _dec(prod, wsb=None) == L.TQ_ERR_ARG
+    assert _dec(L.key_config(mode="mse", bits=8)) == L.TQ_ERR_UNSUPPORTED
+    assert _dec(L.key_config(mode="grouped", bits_outlier=4, bits_normal=4)) == L.TQ_ERR_UNSUPPORTED
+
+
+def test_no_device_reports_hip_error():
+    """Without a GPU the workspace query (which needs the device's CU count)
+    returns TQ_ERR_HIP instead of aborting."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert _dec(L.key_config(mode="prod", bits=3)) == L.TQ_ERR_HIP
+
+
+def test_status_strings():
+    for s in (0, -1, -2, -3, -4, 5):
+        assert isinstance(tq.status_string(s), str) and tq.status_string(s)

@@ -39,7 +39,7 @@ def test_rademacher_signs_are_pm1_and_balanced():
 def test_gaussian_matrix_is_standard_normal():
     S = O.gaussian_matrix(42, O.TAG_S, 128, 128)
     x = S.ravel()
-    assert np.all(x.astype(np.float32) == x)          # float32 values
+    assert np.all(x.astype(np.float16) == x)          # fp16 values
     assert scipy.stats.kstest(x, "norm").pvalue > 1e-3
     assert abs(x.mean()) < 4 / math.sqrt(x.size)
     assert abs(x.var() - 1) < 4 * math.sqrt(2 / x.size)
@@ -297,7 +297,7 @@ def test_prod_unbiased_over_S_draws():
     draws = 3000
     g = np.random.default_rng(3)
     for _ in range(draws):
-        T.S = g.standard_normal((128, 128)).astype(np.float32).astype(np.float64)
+        T.S = g.standard_normal((128, 128)).astype(np.float16).astype(np.float64)
         enc = dict(base)
         enc.update(O.prod_given_idx(base["norm"], base["y"], base["idx"], T))
         ests.append(np.sum(q * O.dequant_keys(enc, T), axis=1))
