@@ -1,0 +1,263 @@
+#!/usr/bin/env python3
+"""Benchmark of the TurboQuant KV-cache hot path on one MI355X.
+
+Workload (printed as config.workload): batched GQA decode, 16 sequences x 8 KV
+heads x 32 query heads, head dim 128, context 32768 per sequence; keys in prod
+mode at 3 bits (2-bit Lloyd-Max index + 1-bit QJL signs + fp16 norm and
+residual norm), values at 2 bits in groups of 32 with fp16 scale and zero;
+bf16 queries, keys and values drawn N(0,1) (synthetic, seeded).
+
+One step = one pass of the whole path for one decode step of the batch:
+  encode the step's new key and value of every (sequence, KV head) into the
+  packed cache (norm, rotation, bucketize, QJL signs, packing; value groups),
+  then decode attention over the full 32768-token context (query rotation and
+  projection, lookup-table scores from the packed bytes, online softmax,
+  p.V, split-K merge).
+`value` = KV tokens per second = 16 * 32768 / step time.  Inputs are resident
+in HBM before timing starts.
+
+Also reported (measured outside the timed steps): bulk encode throughput of
+the same cache (4,194,304 keys and values) and of the 28-layer MSE prefill
+workload (1,835,008 bf16 keys at 4 and 8 bits), and the CPU oracle's decode
+throughput on a bounded sample on the host cores.
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0
+B, HKV, HQ, CTX, D = 16, 8, 32, 32768, 128
+KEY_BYTES = 52      # 32 B index + 16 B signs + 2 B norm + 2 B residual norm
+VAL_BYTES = 48      # 32 B codes + 4 groups x (2 B scale + 2 B zero)
+DECODE_BYTES = B * HKV * CTX * (KEY_BYTES + VAL_BYTES)   # 419,430,400 B per decode
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-encode-bench", action="store_true")
+    ap.add_argument("--cpu-groups", type=int, default=24,
+                    help="(sequence, KV head) groups the CPU oracle decodes for its baseline")
+    ap.add_argument("--profile-decode", type=int, default=0,
+                    help="only run this many decode calls after setup (for rocprofv3 runs)")
+    return ap.parse_args()
+
+
+def source_hash(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_from_profile():
+    """HBM bytes per decode launch from the committed counter summary, if it
+    was taken on the current decode source; else None."""
+    p = os.path.join(ROOT, "profiles", "decode_gqa32k_traffic.json")
+    src = os.path.join(ROOT, "kv_cache_quantization_encode_amd", "csrc", "tq_decode.hip")
+    try:
+        with open(p) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256_16") != source_hash(src):
+        return None
+    return t.get("traffic_bytes_per_launch")
+
+
+def cpu_baseline(n_groups):
+    """The oracle (float64 NumPy) decoding one step for `n_groups` (sequence,
+    KV head) groups of the same workload shape: unpack the packed cache,
+    dequantise keys and values, softmax attention for the group's 4 query
+    heads.  Cache contents come from the oracle's own encode (not timed)."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle.tq_oracle as O
+    import tq_workloads as W
+
+    To = O.build_tables(O.KeyConfig(mode="prod", bits=3, seed=42))
+    G = HQ // HKV
+    qv, _ = W.queries(3, 1, G * n_groups)
+    caches = []
+    for gi in range(n_groups):
+        kv, _ = W.kv_rows(3, 1, CTX, row0=gi * CTX)
+        vv, _ = W.kv_rows(3, 2, CTX, row0=gi * CTX)
+        rec = O.pack_key_record(O.encode_keys(kv.astype(np.float64), To), To)
+        vrec = O.pack_value_record(O.encode_values(vv, 2), 2)
+        caches.append((rec, vrec))
+    t0 = time.perf_counter()
+    for gi, (rec, vrec) in enumerate(caches):
+        enc = O.unpack_key_record(rec, To)
+        khat = O.dequant_keys(enc, To)
+        vhat = O.dequant_values(O.unpack_value_record(vrec, 2, D))
+        O.decode_attention(qv[0, gi * G:(gi + 1) * G].astype(np.float64), khat, vhat, CTX)
+    dt = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    tokens_per_s = n_groups * CTX / HKV / dt   # KV tokens/s in the same unit as value
+    return {"value": tokens_per_s, "unit": "KV tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "%d of %d (sequence, KV head) groups x %d tokens, one decode step each "
+                      "(unpack, dequantise, float64 softmax attention); %.1f s; scaled as "
+                      "groups/%d sequences" % (n_groups, B * HKV, CTX, dt, HKV),
+            "seconds": dt, "cpu_count": os.cpu_count()}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only (this path has no multi-GPU mode); got --gpus %d" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import kv_cache_quantization_encode_amd as tq
+    import tq_workloads as W
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    cfg = tq.key_config(mode="prod", bits=3, seed=42)
+    T = tq.Tables(cfg, dev)
+    n_rec = B * HKV * CTX
+    # ---- resident inputs: the cache's keys and values, then the packed cache
+    keys = W.normal_bf16_device(3, 1, (n_rec, D), dev)
+    vals = W.normal_bf16_device(3, 2, (n_rec, D), dev)
+    kp = tq.key_planes(T, n_rec, dev)
+    vp = tq.value_planes(2, n_rec, device=dev)
+    tq.encode_keys(T, keys, kp)
+    tq.encode_values(vals, 2, planes=vp)
+    # per-step new tokens and queries (resident)
+    n_steps_total = args.warmup + max(args.steps, 1)
+    new_k = W.normal_bf16_device(3, 6, (n_steps_total, B * HKV, D), dev)
+    new_v = W.normal_bf16_device(3, 7, (n_steps_total, B * HKV, D), dev)
+    qs = W.normal_bf16_device(3, 3, (n_steps_total, B, HQ, D), dev)
+    slots = (torch.arange(B * HKV, device=dev, dtype=torch.int64) * CTX + (CTX - 1)).contiguous()
+    ctx_len = torch.full((B,), CTX, dtype=torch.int32, device=dev)
+    dec = tq.Decoder(T, B, HQ, HKV, CTX, 2, torch.bfloat16, dev)
+    out = torch.empty((B, HQ, D), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    if args.profile_decode:
+        for i in range(args.profile_decode):
+            dec(qs[i % n_steps_total], ctx_len, kp, vp, out=out)
+        torch.cuda.synchronize()
+        print("profiled %d decode calls" % args.profile_decode)
+        return
+
+    def step(i, ev=None):
+        tq.encode_keys(T, new_k[i], kp, slots=slots, n_records=n_rec)
+        tq.encode_values(new_v[i], 2, planes=vp, slots=slots, n_records=n_rec)
+        if ev is not None:
+            ev[0].record()
+        dec(qs[i], ctx_len, kp, vp, out=out)
+        if ev is not None:
+            ev[1].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(args.warmup + k, evs[k])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    dec_ms = sorted(a.elapsed_time(b) for a, b in evs)
+    dec_ms_mean = sum(dec_ms) / len(dec_ms)
+    dec_ms_median = dec_ms[len(dec_ms) // 2]
+    value = B * CTX / (ms_per_step * 1e-3)
+    achieved = DECODE_BYTES / (dec_ms_mean * 1e-3) / 1e9
+
+    extra = {}
+    if not args.no_encode_bench:
+        extra.update(encode_bench(tq, W, T, keys, vals, dev))
+    del keys, vals
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(args.cpu_groups)
+    traffic = traffic_from_profile()
+    line = {
+        "metric": "decode-attn KV tokens/s & HBM GB/s (% of peak); encode keys/s",
+        "value": value,
+        "unit": "KV tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "gqa-decode-32k", "sequences": B, "kv_heads": HKV, "q_heads": HQ,
+                   "head_dim": D, "context": CTX, "keys": "prod 3-bit (2-bit index + QJL)",
+                   "values": "2-bit group 32", "step": "append-encode 128 K/V rows + decode"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic,
+                     "kernel": "tq_decode_attention (decode_kernel + merge_kernel)",
+                     "algorithmic_bytes": DECODE_BYTES, "ms_mean": dec_ms_mean,
+                     "ms_median": dec_ms_median},
+        "cpu_baseline": cpu,
+    }
+    line.update(extra)
+    print(json.dumps(line))
+
+
+def encode_bench(tq, W, T, keys, vals, dev, reps=3):
+    """Bulk encode throughput (not part of the timed steps)."""
+    import torch
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    n = keys.shape[0]
+    kp = tq.key_planes(T, n, dev)
+    vp = tq.value_planes(2, n, device=dev)
+    ms_k = timed(lambda: tq.encode_keys(T, keys, kp))
+    ms_v = timed(lambda: tq.encode_values(vals, 2, planes=vp))
+    kbytes = n * (2 * D + KEY_BYTES)
+    vbytes = n * (2 * D + VAL_BYTES)
+    res = {"encode_prod3": {"keys": n, "ms": ms_k, "keys_per_s": n / (ms_k * 1e-3),
+                            "gbps": kbytes / (ms_k * 1e-3) / 1e9,
+                            "gflops_qjl": 2.0 * D * D * n / (ms_k * 1e-3) / 1e9},
+           "encode_values2": {"rows": n, "ms": ms_v, "rows_per_s": n / (ms_v * 1e-3),
+                              "gbps": vbytes / (ms_v * 1e-3) / 1e9}}
+    del kp, vp
+    # 28-layer MSE prefill encode, 4 and 8 bits, one seed per layer
+    layers = [W.w2_layer_keys_device(l, dev) for l in range(28)]
+    n2 = sum(x.shape[0] for x in layers)
+    for bits in (4, 8):
+        tabs = [tq.Tables(tq.key_config(mode="mse", bits=bits, seed=42 + l), dev) for l in range(28)]
+        planes = [tq.key_planes(tabs[0], layers[0].shape[0], dev) for _ in range(28)]
+
+        def run():
+            for l in range(28):
+                tq.encode_keys(tabs[l], layers[l], planes[l])
+        ms = timed(run)
+        row = tabs[0].row_bytes + 2
+        res["encode_mse%d_prefill" % bits] = {"keys": n2, "ms": ms, "keys_per_s": n2 / (ms * 1e-3),
+                                             "gbps": n2 * (2 * D + row) / (ms * 1e-3) / 1e9}
+        del planes
+    return res
+
+
+if __name__ == "__main__":
+    main()

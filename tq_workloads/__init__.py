@@ -172,3 +172,45 @@ def w4_needles(q_vals: np.ndarray, Hkv: int, Hq: int, d: int = 128):
         qhat = qv / np.linalg.norm(qv)
         out[h] = (4.0 * qhat)[None, :] + noise[h]
     return to_bf16(out)
+
+
+# --- device-side generation for full-size workloads --------------------------------
+
+def torch_generator(wid: int, tid: int, device):
+    """torch generator on `device` seeded from (42, workload, tensor)."""
+    import torch
+    seed = int(np.random.SeedSequence([BASE_SEED, int(wid), int(tid)]).generate_state(1, dtype=np.uint64)[0]
+               & 0x7FFFFFFFFFFFFFFF)
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return g
+
+
+def normal_bf16_device(wid: int, tid: int, shape, device, scale_cols=None, chunk_rows=1 << 20):
+    """N(0,1) float32 draws on the device, optionally scaled per column,
+    rounded to bfloat16 (torch's conversion is round-to-nearest-even).
+    Generated in row chunks to bound the float32 temporary."""
+    import torch
+    g = torch_generator(wid, tid, device)
+    rows, d = int(np.prod(shape[:-1])), shape[-1]
+    out = torch.empty((rows, d), dtype=torch.bfloat16, device=device)
+    sc = None if scale_cols is None else torch.as_tensor(scale_cols, dtype=torch.float32, device=device)
+    for r0 in range(0, rows, chunk_rows):
+        r1 = min(rows, r0 + chunk_rows)
+        x = torch.randn((r1 - r0, d), generator=g, device=device, dtype=torch.float32)
+        if sc is not None:
+            x *= sc
+        out[r0:r1] = x.to(torch.bfloat16)
+    return out.reshape(*shape)
+
+
+def w2_layer_keys_device(layer: int, device, heads: int = 2, n_tok: int = 32768, d: int = 128):
+    """Device version of w2_layer_keys' recipe: N(0, I) direction scaled to a
+    norm drawn log-uniform in [2, 20], bf16."""
+    import torch
+    g = torch_generator(2, 100 + layer, device)
+    x = torch.randn((heads * n_tok, d), generator=g, device=device, dtype=torch.float32)
+    u = torch.rand((heads * n_tok, 1), generator=g, device=device, dtype=torch.float32)
+    norms = torch.exp(math.log(2.0) + u * (math.log(20.0) - math.log(2.0)))
+    x = x / torch.linalg.vector_norm(x, dim=1, keepdim=True) * norms
+    return x.to(torch.bfloat16)
