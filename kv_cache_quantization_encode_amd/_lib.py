@@ -10,7 +10,8 @@ import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libtq.so")
+# TQ_LIBRARY may name another build of libtq.so (for A/B timing of build options)
+LIB_PATH = os.environ.get("TQ_LIBRARY") or os.path.join(HERE, "libtq.so")
 
 TQ_OK, TQ_ERR_ARG, TQ_ERR_UNSUPPORTED, TQ_ERR_WORKSPACE, TQ_ERR_HIP = 0, -1, -2, -3, -4
 TQ_MODE_MSE, TQ_MODE_PROD, TQ_MODE_GROUPED = 0, 1, 2

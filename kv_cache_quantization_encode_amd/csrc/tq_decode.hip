@@ -26,6 +26,7 @@
 #include <hip/hip_fp16.h>
 
 #include <atomic>
+#include <type_traits>
 
 #include "tq.h"
 #include "tq_internal.h"
@@ -36,7 +37,13 @@ namespace {
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 
 constexpr int KD = 128;
-constexpr int NW = 16;        // waves per workgroup
+#ifndef TQ_DEC_WAVES
+#define TQ_DEC_WAVES 16
+#endif
+#ifndef TQ_DEC_LOOKUP_BATCH
+#define TQ_DEC_LOOKUP_BATCH 8
+#endif
+constexpr int NW = TQ_DEC_WAVES;  // waves per workgroup
 constexpr int NT = NW * 64;   // threads per workgroup
 constexpr int TILE = 64;      // tokens per wave tile
 constexpr int QH = 4;         // query heads per workgroup
@@ -93,6 +100,17 @@ __device__ inline float load_q(const void* q, int dt, long long i) {
 
 __device__ inline float h2f(uint32_t bits16) { return __half2float(__ushort_as_half((unsigned short)bits16)); }
 
+template <int I, int N, typename Fn>
+__device__ inline void static_for(Fn&& fn) {
+  if constexpr (I < N) {
+    fn(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(fn);
+  }
+}
+
+// A value every lane holds alike, moved to a scalar register.
+__device__ inline float uniform(float v) { return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v))); }
+
 __device__ inline float wave_max(float v) {
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m));
@@ -115,6 +133,9 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
   uint32_t* wbuf = (uint32_t*)(qs + QH * KD);                 // [NW][32 pairs][4 groups][QH] half2
   float* scl = (float*)(wbuf + NW * 32 * 4 * QH);             // [2][QH] table scales
   int* amax = (int*)(scl + 2 * QH);                           // [2][QH]
+  float* cen = (float*)(amax + 2 * QH);                       // [2][16] centroids of each part
+  float* abuf = cen + 32;                                     // [2][NW/2][QH] softmax rescale factors
+  float* hmul = abuf + 2 * (NW / 2) * QH;                     // [2][QH] score multipliers
 
   const tq_blob_header* H = (const tq_blob_header*)a.tables;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -126,6 +147,11 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
 
   // ---- prologue: rotate the queries, project them, build the tables
   if (tid < 2 * QH) amax[tid] = 0;
+  if (tid < 32) {
+    const int part = tid >> 4, k = tid & 15;
+    if (part < H->n_parts && k < H->part_levels[part])
+      cen[tid] = ((const float*)(a.tables + H->off_centroids[part]))[k];
+  }
   for (int i = tid; i < QH * KD; i += NT) {
     const int hh = i / KD, j = i % KD;
     const int gq = QH * quad + hh;  // query head within the GQA group
@@ -149,14 +175,33 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
     __syncthreads();
   }
   if constexpr (F::PROD) {
+    // q_s = S q': thread -> (row, 16-column chunk); eight lanes finish a row
     const uint16_t* S = (const uint16_t*)(a.tables + H->off_S);
-    for (int i = tid; i < QH * KD; i += NT) {
-      const int hh = i / KD, row = i % KD;
-      const float* x = qp + hh * KD;
-      const uint16_t* srow = S + (size_t)row * KD;
-      float acc = 0.0f;
-      for (int j = 0; j < KD; ++j) acc = fmaf(h2f(srow[j]), x[j], acc);
-      qs[i] = acc;
+    const int ch = tid & 7;
+    for (int row = tid >> 3; row < KD; row += NT / 8) {
+      const uint4* sp = (const uint4*)(S + (size_t)row * KD + 16 * ch);
+      const uint4 s0 = sp[0], s1 = sp[1];
+      const uint32_t sw[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+      float part[QH] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float lo = h2f(sw[i] & 0xFFFFu), hi = h2f(sw[i] >> 16);
+#pragma unroll
+        for (int hh = 0; hh < QH; ++hh) {
+          part[hh] = fmaf(lo, qp[hh * KD + 16 * ch + 2 * i], part[hh]);
+          part[hh] = fmaf(hi, qp[hh * KD + 16 * ch + 2 * i + 1], part[hh]);
+        }
+      }
+#pragma unroll
+      for (int hh = 0; hh < QH; ++hh) {
+        part[hh] += __shfl_xor(part[hh], 1);
+        part[hh] += __shfl_xor(part[hh], 2);
+        part[hh] += __shfl_xor(part[hh], 4);
+      }
+      if (ch == 0) {
+#pragma unroll
+        for (int hh = 0; hh < QH; ++hh) qs[hh * KD + row] = part[hh];
+      }
     }
     __syncthreads();
   }
@@ -203,7 +248,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
       const int cpb = 8 / W;
       const int bits = H->part_bits[F::GROUPED ? part : 0];
       const int fmask = (1 << bits) - 1;
-      const float* cent = (const float*)(a.tables + H->off_centroids[F::GROUPED ? part : 0]);
+      const float* cent = cen + 16 * (F::GROUPED ? part : 0);
       const int j0 = part * F::PD + p * cpb;
       for (int k = 0; k < cpb; ++k) {
         const float c = cent[(v >> (W * k)) & fmask];
@@ -220,219 +265,302 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
   }
   __syncthreads();
 
-  // per-token multipliers of the two table classes, with the scales undone
-  float mul0[QH], mul1[QH];
-#pragma unroll
-  for (int hh = 0; hh < QH; ++hh) {
-    mul0[hh] = 1.0f / (scl[hh] * (float)F::PD);
-    mul1[hh] = F::PROD ? 1.2533141373155003f / ((float)KD * sqrtf((float)KD) * scl[QH + hh])
-                       : 1.0f / (scl[QH + hh] * (float)F::PD);
-  }
-  const float xscale = a.sm_scale * LOG2E;
-
-  float m_run[QH], l_run[QH], zacc[QH][4], acc[QH][8];
-#pragma unroll
-  for (int hh = 0; hh < QH; ++hh) {
-    m_run[hh] = -INFINITY;
-    l_run[hh] = 0.0f;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) zacc[hh][k] = 0.0f;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) acc[hh][k] = 0.0f;
-  }
-  const long long rec0 = ((long long)b * a.Hkv + hkv) * a.max_ctx;
-  uint32_t* wmine = wbuf + wave * (32 * 4 * QH);
-  const int slot = lane >> 4, u = lane & 15, grp = u >> 2;
-
-  for (int tb = t_begin + wave * TILE; tb < t_end; tb += NW * TILE) {
-    // ---------------- scores: lane = token
-    const int t = tb + lane;
-    const bool valid = t < t_end;
-    float sc[QH] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-    float zz[4] = {0.0f, 0.0f, 0.0f, 0.0f}, ss[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    if (valid) {
-      const long long rec = rec0 + t;
-      uint32_t kw[F::KWORDS];
-      const uint32_t* ip = (const uint32_t*)(a.idx + rec * F::IDXB);
-#pragma unroll
-      for (int k = 0; k < F::IDXB / 4; ++k) kw[k] = ip[k];
-      if constexpr (F::PROD) {
-        const uint4 sv = *(const uint4*)(a.signs + rec * (KD / 8));
-        kw[F::IDXB / 4 + 0] = sv.x; kw[F::IDXB / 4 + 1] = sv.y;
-        kw[F::IDXB / 4 + 2] = sv.z; kw[F::IDXB / 4 + 3] = sv.w;
-      }
-      float m0, m1 = 0.0f;
-      if constexpr (F::GROUPED) {
-        const uint32_t nn = *(const uint32_t*)(a.norm + 2 * rec);
-        m0 = h2f(nn & 0xFFFFu);
-        m1 = h2f(nn >> 16);
-      } else {
-        m0 = h2f(a.norm[rec]);
-        if (F::PROD) m1 = h2f(a.rnorm[rec]);
-      }
-      float A[QH] = {0, 0, 0, 0}, Bc[QH] = {0, 0, 0, 0};
-#pragma unroll
-      for (int p = 0; p < F::P0; ++p) {
-        uint32_t v = (kw[p >> 2] >> (8 * (p & 3))) & 0xFFu;
-        if (B0 == 3) v &= 0x77u;
-        const uint2 e = lut[p * F::S0 + v];
-        A[0] += h2f(e.x & 0xFFFFu); A[1] += h2f(e.x >> 16);
-        A[2] += h2f(e.y & 0xFFFFu); A[3] += h2f(e.y >> 16);
-      }
-#pragma unroll
-      for (int p = 0; p < F::P1; ++p) {
-        const int byte = F::P0 + p;
-        uint32_t v = (kw[byte >> 2] >> (8 * (byte & 3))) & 0xFFu;
-        if (F::GROUPED && B1 == 3) v &= 0x77u;
-        const uint2 e = lut[F::E0 + p * F::S1 + v];
-        Bc[0] += h2f(e.x & 0xFFFFu); Bc[1] += h2f(e.x >> 16);
-        Bc[2] += h2f(e.y & 0xFFFFu); Bc[3] += h2f(e.y >> 16);
-      }
-#pragma unroll
-      for (int hh = 0; hh < QH; ++hh) sc[hh] = m0 * mul0[hh] * A[hh] + m1 * mul1[hh] * Bc[hh];
-      const uint2 zv = *(const uint2*)(a.vzero + rec * 4);
-      const uint2 sv2 = *(const uint2*)(a.vscale + rec * 4);
-      zz[0] = h2f(zv.x & 0xFFFFu); zz[1] = h2f(zv.x >> 16);
-      zz[2] = h2f(zv.y & 0xFFFFu); zz[3] = h2f(zv.y >> 16);
-      ss[0] = h2f(sv2.x & 0xFFFFu); ss[1] = h2f(sv2.x >> 16);
-      ss[2] = h2f(sv2.y & 0xFFFFu); ss[3] = h2f(sv2.y >> 16);
-      if (a.scores) {
-#pragma unroll
-        for (int hh = 0; hh < QH; ++hh) {
-          const int gq = QH * quad + hh;
-          if (gq < a.G) a.scores[((long long)b * a.Hq + hkv * a.G + gq) * a.max_ctx + t] = sc[hh];
-        }
-      }
-    }
-    // ---------------- online softmax (base 2)
-    float p[QH];
-#pragma unroll
-    for (int hh = 0; hh < QH; ++hh) {
-      const float x = sc[hh] * xscale;  // -inf for missing tokens
-      const float mt = wave_max(x);
-      const float mn = fmaxf(m_run[hh], mt);
-      const float alpha = mn == -INFINITY ? 1.0f : exp2f(m_run[hh] - mn);
-      p[hh] = mn == -INFINITY ? 0.0f : exp2f(x - mn);
-      m_run[hh] = mn;
-      l_run[hh] = l_run[hh] * alpha + p[hh];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) zacc[hh][k] = fmaf(p[hh], zz[k], zacc[hh][k] * alpha);
-#pragma unroll
-      for (int k = 0; k < 8; ++k) acc[hh][k] *= alpha;
-    }
-    // weights p * scale as fp16, paired by token: wbuf[pair][group][head] = (w_even, w_odd)
-    {
-      uint16_t* wb16 = (uint16_t*)wmine;
-      const int pair = lane >> 1, odd = lane & 1;
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-#pragma unroll
-        for (int hh = 0; hh < QH; ++hh)
-          wb16[((pair * 4 + k) * QH + hh) * 2 + odd] = __half_as_ushort(__float2half_rn(p[hh] * ss[k]));
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    // ---------------- p.V: lane = (slot, 8-dim slice u)
-#pragma unroll 2
-    for (int k = 0; k < 8; ++k) {
-      const int pr = slot + 4 * k;
-      const int tA = tb + 2 * pr, tB = tA + 1;
-      uint32_t cA = 0, cB = 0;
-      if (VB == 2) {
-        if (tA < t_end) cA = *(const uint16_t*)(a.vcodes + (rec0 + tA) * 32 + 2 * u);
-        if (tB < t_end) cB = *(const uint16_t*)(a.vcodes + (rec0 + tB) * 32 + 2 * u);
-      } else {
-        if (tA < t_end) cA = *(const uint32_t*)(a.vcodes + (rec0 + tA) * 64 + 4 * u);
-        if (tB < t_end) cB = *(const uint32_t*)(a.vcodes + (rec0 + tB) * 64 + 4 * u);
-      }
-      const uint4 wv = *(const uint4*)(wmine + (pr * 4 + grp) * QH);
-      const uint32_t wh[QH] = {wv.x, wv.y, wv.z, wv.w};
-      uint32_t pairs[8];
-      if (VB == 2) {
-        const uint32_t Y = cA | (cB << 16);
-        const uint32_t Y2 = (Y >> 8) & 0x00FF00FFu;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          pairs[i] = Y & (0x00030003u << (2 * i));
-          pairs[4 + i] = Y2 & (0x00030003u << (2 * i));
-        }
-      } else {
-        const uint32_t Ylo = (cA & 0xFFFFu) | (cB << 16);
-        const uint32_t Yhi = (cA >> 16) | (cB & 0xFFFF0000u);
-        const uint32_t Ylo2 = (Ylo >> 8) & 0x00FF00FFu, Yhi2 = (Yhi >> 8) & 0x00FF00FFu;
-        pairs[0] = Ylo & 0x000F000Fu;  pairs[1] = Ylo & 0x00F000F0u;
-        pairs[2] = Ylo2 & 0x000F000Fu; pairs[3] = Ylo2 & 0x00F000F0u;
-        pairs[4] = Yhi & 0x000F000Fu;  pairs[5] = Yhi & 0x00F000F0u;
-        pairs[6] = Yhi2 & 0x000F000Fu; pairs[7] = Yhi2 & 0x00F000F0u;
-      }
-#pragma unroll
-      for (int hh = 0; hh < QH; ++hh) {
-        const half2_t w2 = __builtin_bit_cast(half2_t, wh[hh]);
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-          acc[hh][i] = __builtin_amdgcn_fdot2(w2, __builtin_bit_cast(half2_t, pairs[i]), acc[hh][i], false);
-      }
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  }
-
-  // ---- combine: lanes -> wave -> workgroup
-  // undo the subnormal placement: dim i of a slice carries code * 2^-24 * step_i
-  float ocode[QH][8];
-#pragma unroll
-  for (int hh = 0; hh < QH; ++hh)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float step = VB == 2 ? (float)(1 << (2 * (i & 3))) : (float)(1 << (4 * (i & 1)));
-      float v = acc[hh][i];
-      v += __shfl_xor(v, 16);
-      v += __shfl_xor(v, 32);
-      ocode[hh][i] = v * (16777216.0f / step);
-    }
-  float lsum[QH], zsum[QH][4];
-#pragma unroll
-  for (int hh = 0; hh < QH; ++hh) {
-    lsum[hh] = wave_sum(l_run[hh]);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) zsum[hh][k] = wave_sum(zacc[hh][k]);
-  }
-  __syncthreads();  // tables are no longer read: reuse them for the merge
-  float* red = (float*)smem;  // [NW][QH][2 + 4 + KD]
-  constexpr int RS = 2 + 4 + KD;
-  {
-    float* mine = red + wave * QH * RS;
-    if (lane < 16) {
-#pragma unroll
-      for (int hh = 0; hh < QH; ++hh)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) mine[hh * RS + 6 + 8 * u + i] = ocode[hh][i];
-    }
-    if (lane == 0) {
-#pragma unroll
-      for (int hh = 0; hh < QH; ++hh) {
-        mine[hh * RS + 0] = m_run[hh];
-        mine[hh * RS + 1] = lsum[hh];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) mine[hh * RS + 2 + k] = zsum[hh][k];
-      }
-    }
+  // per-token multipliers of the two table classes, with the scales undone:
+  // hmul[0][h] multiplies the norm, hmul[1][h] the residual norm (PROD) or
+  // the second half's norm (GROUPED).  Kept in LDS, read where used.
+  if (tid < QH) {
+    hmul[tid] = 1.0f / (scl[tid] * (float)F::PD);
+    hmul[QH + tid] = F::PROD ? 1.2533141373155003f / ((float)KD * sqrtf((float)KD) * scl[QH + tid])
+                             : 1.0f / (scl[QH + tid] * (float)F::PD);
   }
   __syncthreads();
-  if (tid < QH * KD) {
-    const int hh = tid / KD, j = tid % KD;
+  const float xscale = a.sm_scale * LOG2E;
+  const long long rec0 = ((long long)b * a.Hkv + hkv) * a.max_ctx;
+
+  // ---- main loop, split between two kinds of waves.  Score waves (the first
+  // half) read key bytes, look up the tables, run the online softmax and
+  // publish fp16 weights p*scale; p.V waves (second half) accumulate those
+  // weights against the value codes one round later.  Wave pw of each half
+  // owns tiles pw, pw + NS, pw + 2 NS, ...; a two-slot LDS ring carries the
+  // weights and the softmax rescale factor from score wave pw to p.V wave pw,
+  // and one barrier per round separates producer and consumer.  Each wave
+  // loads its next tile's data one round ahead.
+  constexpr int NS = NW / 2;
+  constexpr int VROW = KD * VB / 8;  // bytes of a value-code row
+  const bool scorer = wave < NS;
+  const int pw = scorer ? wave : wave - NS;
+  const int slot = lane >> 4, u = lane & 15, grp = u >> 2;
+  const int n_tiles = t_end > t_begin ? (t_end - t_begin + TILE - 1) / TILE : 0;
+  const int rounds = (n_tiles + NS - 1) / NS;
+  auto tile_tb = [&](int r) { return t_begin + (r * NS + pw) * TILE; };
+
+  struct KeyData {
+    uint32_t kw[F::KWORDS];
+    uint32_t nrm, rn;  // fp16 norm(s), fp16 residual norm
+    uint2 zv, sv;      // fp16 zero / scale of the four value groups
+  };
+  auto load_keys = [&](int tb, KeyData& d) {
+    const int t = tb + lane;
+    if (t < t_end) {
+      const long long rec = rec0 + t;
+      const uint32_t* ip = (const uint32_t*)(a.idx + rec * F::IDXB);
+#pragma unroll
+      for (int k = 0; k < F::IDXB / 4; ++k) d.kw[k] = ip[k];
+      if constexpr (F::PROD) {
+        const uint4 sv = *(const uint4*)(a.signs + rec * (KD / 8));
+        d.kw[F::IDXB / 4 + 0] = sv.x; d.kw[F::IDXB / 4 + 1] = sv.y;
+        d.kw[F::IDXB / 4 + 2] = sv.z; d.kw[F::IDXB / 4 + 3] = sv.w;
+        d.rn = a.rnorm[rec];
+      } else {
+        d.rn = 0;
+      }
+      d.nrm = F::GROUPED ? *(const uint32_t*)(a.norm + 2 * rec) : (uint32_t)a.norm[rec];
+      d.zv = *(const uint2*)(a.vzero + rec * 4);
+      d.sv = *(const uint2*)(a.vscale + rec * 4);
+    } else {
+#pragma unroll
+      for (int k = 0; k < F::KWORDS; ++k) d.kw[k] = 0;
+      d.nrm = d.rn = 0;
+      d.zv = d.sv = make_uint2(0, 0);
+    }
+  };
+  // value codes of this lane's token pairs (slot + 4k): [2k] even token, [2k+1] odd token
+  auto load_codes = [&](int tb, uint32_t* c) {
+    const uint8_t* cbase = a.vcodes + (rec0 + tb + 2 * slot) * VROW + VB * u;
+    const bool full = tb + TILE <= t_end;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+#pragma unroll
+      for (int o = 0; o < 2; ++o) {
+        const uint8_t* pa = cbase + (8 * k + o) * VROW;
+        uint32_t v = 0;
+        if (full || tb + 2 * slot + 8 * k + o < t_end)
+          v = VB == 2 ? (uint32_t) * (const uint16_t*)pa : *(const uint32_t*)pa;
+        c[2 * k + o] = v;
+      }
+    }
+  };
+
+  const half2_t e10 = {(_Float16)1.0f, (_Float16)0.0f}, e01 = {(_Float16)0.0f, (_Float16)1.0f};
+  float* red = (float*)smem;  // [NS][QH][2 + 4 + KD], over the tables once every wave is done
+  constexpr int RS = 2 + 4 + KD;
+  float* mine = red + pw * QH * RS;
+  // The two kinds of waves run separate loops with the same number of
+  // barriers (rounds + 1), so neither keeps the other's registers live.
+  if (scorer) {
+    float m_run[QH], l_run[QH], zacc[QH][4];
+#pragma unroll
+    for (int hh = 0; hh < QH; ++hh) {
+      m_run[hh] = -INFINITY;
+      l_run[hh] = 0.0f;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) zacc[hh][k] = 0.0f;
+    }
+    KeyData kd;
+    load_keys(tile_tb(0), kd);
+    for (int r = 0; r <= rounds; ++r) {
+      const int tb = tile_tb(r);
+      if (r < rounds && tb < t_end) {
+        // ---------------- scores: lane = token
+        const int t = tb + lane;
+        const bool valid = t < t_end;
+        float sc[QH];
+        {
+          const float m0 = F::GROUPED ? h2f(kd.nrm & 0xFFFFu) : h2f(kd.nrm);
+          const float m1 = F::GROUPED ? h2f(kd.nrm >> 16) : h2f(kd.rn);
+          // table sums in fp32: fdot2(entry pair, (1,0)) adds one fp16 exactly
+          float A[QH] = {0, 0, 0, 0}, Bc[QH] = {0, 0, 0, 0};
+          // Index nibbles of 3-bit codes have their high bit clear (tq_encode_keys
+          // writes them so), so a byte is a table index as it stands.
+#pragma unroll
+          for (int p = 0; p < F::P0; ++p) {
+            // cap the table reads in flight (each holds two registers)
+            if (p % TQ_DEC_LOOKUP_BATCH == 0) __builtin_amdgcn_sched_barrier(0);
+            const uint32_t v = (kd.kw[p >> 2] >> (8 * (p & 3))) & 0xFFu;
+            const uint2 e = lut[p * F::S0 + v];
+            const half2_t x01 = __builtin_bit_cast(half2_t, e.x), x23 = __builtin_bit_cast(half2_t, e.y);
+            A[0] = __builtin_amdgcn_fdot2(x01, e10, A[0], false);
+            A[1] = __builtin_amdgcn_fdot2(x01, e01, A[1], false);
+            A[2] = __builtin_amdgcn_fdot2(x23, e10, A[2], false);
+            A[3] = __builtin_amdgcn_fdot2(x23, e01, A[3], false);
+          }
+#pragma unroll
+          for (int p = 0; p < F::P1; ++p) {
+            if (p % TQ_DEC_LOOKUP_BATCH == 0) __builtin_amdgcn_sched_barrier(0);
+            const int byte = F::P0 + p;
+            const uint32_t v = (kd.kw[byte >> 2] >> (8 * (byte & 3))) & 0xFFu;
+            const uint2 e = lut[F::E0 + p * F::S1 + v];
+            const half2_t x01 = __builtin_bit_cast(half2_t, e.x), x23 = __builtin_bit_cast(half2_t, e.y);
+            Bc[0] = __builtin_amdgcn_fdot2(x01, e10, Bc[0], false);
+            Bc[1] = __builtin_amdgcn_fdot2(x01, e01, Bc[1], false);
+            Bc[2] = __builtin_amdgcn_fdot2(x23, e10, Bc[2], false);
+            Bc[3] = __builtin_amdgcn_fdot2(x23, e01, Bc[3], false);
+          }
+          const float4 h0 = *(const float4*)hmul, h1 = *(const float4*)(hmul + QH);
+          const float mul0[QH] = {h0.x, h0.y, h0.z, h0.w}, mul1[QH] = {h1.x, h1.y, h1.z, h1.w};
+#pragma unroll
+          for (int hh = 0; hh < QH; ++hh)
+            sc[hh] = valid ? m0 * mul0[hh] * A[hh] + m1 * mul1[hh] * Bc[hh] : -INFINITY;
+          if (a.scores && valid) {
+#pragma unroll
+            for (int hh = 0; hh < QH; ++hh) {
+              const int gq = QH * quad + hh;
+              if (gq < a.G) a.scores[((long long)b * a.Hq + hkv * a.G + gq) * a.max_ctx + t] = sc[hh];
+            }
+          }
+        }
+        // ---------------- online softmax (base 2).  The wave-wide max is
+        // only recomputed when some lane exceeds the running max; otherwise
+        // every p = 2^(x - m) <= 1 already and nothing needs rescaling.
+        float x[QH], alpha[QH] = {1.0f, 1.0f, 1.0f, 1.0f};
+        bool exceed = false;
+#pragma unroll
+        for (int hh = 0; hh < QH; ++hh) {
+          x[hh] = sc[hh] * xscale;  // -inf for missing tokens
+          exceed |= x[hh] > m_run[hh];
+        }
+        if (__builtin_amdgcn_ballot_w64(exceed) != 0) {
+#pragma unroll
+          for (int hh = 0; hh < QH; ++hh) {
+            const float mn = uniform(fmaxf(m_run[hh], wave_max(x[hh])));
+            alpha[hh] = m_run[hh] == -INFINITY ? 0.0f : exp2f(m_run[hh] - mn);
+            m_run[hh] = mn;
+            l_run[hh] *= alpha[hh];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) zacc[hh][k] *= alpha[hh];
+          }
+        }
+        const uint2 zv = kd.zv, sv = kd.sv;
+        // the next tile of this wave, one round ahead
+        load_keys(tile_tb(r + 1), kd);
+        float zz[4], ss[4];
+        zz[0] = h2f(zv.x & 0xFFFFu); zz[1] = h2f(zv.x >> 16);
+        zz[2] = h2f(zv.y & 0xFFFFu); zz[3] = h2f(zv.y >> 16);
+        ss[0] = h2f(sv.x & 0xFFFFu); ss[1] = h2f(sv.x >> 16);
+        ss[2] = h2f(sv.y & 0xFFFFu); ss[3] = h2f(sv.y >> 16);
+        float p[QH];
+#pragma unroll
+        for (int hh = 0; hh < QH; ++hh) {
+          // m_run is finite (lane 0 holds a valid token) and x - m_run <= 0
+          p[hh] = __builtin_amdgcn_exp2f(x[hh] - m_run[hh]);
+          l_run[hh] += p[hh];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) zacc[hh][k] = fmaf(p[hh], zz[k], zacc[hh][k]);
+        }
+        // weights p * scale as fp16, paired by token: [pair][group][head] = (w_even, w_odd)
+        uint16_t* wb16 = (uint16_t*)(wbuf + ((r & 1) * NS + pw) * (32 * 4 * QH));
+        const int pair = lane >> 1, odd = lane & 1;
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+#pragma unroll
+          for (int hh = 0; hh < QH; ++hh)
+            wb16[((pair * 4 + k) * QH + hh) * 2 + odd] = __half_as_ushort(__float2half_rn(p[hh] * ss[k]));
+        if (lane == 0) {
+#pragma unroll
+          for (int hh = 0; hh < QH; ++hh) abuf[((r & 1) * NS + pw) * QH + hh] = alpha[hh];
+        }
+      }
+      __syncthreads();
+    }
+#pragma unroll
+    for (int hh = 0; hh < QH; ++hh) {
+      const float ls = wave_sum(l_run[hh]);
+      float zs[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) zs[k] = wave_sum(zacc[hh][k]);
+      if (lane == 0) {
+        mine[hh * RS + 0] = m_run[hh];
+        mine[hh * RS + 1] = ls;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) mine[hh * RS + 2 + k] = zs[k];
+      }
+    }
+  } else {
+    float acc[QH][8];
+#pragma unroll
+    for (int hh = 0; hh < QH; ++hh)
+#pragma unroll
+      for (int k = 0; k < 8; ++k) acc[hh][k] = 0.0f;
+    uint32_t codes[16];
+    load_codes(tile_tb(0), codes);
+    for (int r = 0; r <= rounds; ++r) {
+      const int tb = r >= 1 ? tile_tb(r - 1) : t_end;
+      if (tb < t_end) {
+        uint32_t cur[16];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) cur[k] = codes[k];
+        load_codes(tile_tb(r), codes);  // next round's tile
+        const uint32_t* wsrc = wbuf + (((r - 1) & 1) * NS + pw) * (32 * 4 * QH);
+        const float4 al = *(const float4*)(abuf + (((r - 1) & 1) * NS + pw) * QH);
+        const float alv[QH] = {uniform(al.x), uniform(al.y), uniform(al.z), uniform(al.w)};
+        if (alv[0] != 1.0f || alv[1] != 1.0f || alv[2] != 1.0f || alv[3] != 1.0f) {
+#pragma unroll
+          for (int hh = 0; hh < QH; ++hh)
+#pragma unroll
+            for (int k = 0; k < 8; ++k) acc[hh][k] *= alv[hh];
+        }
+        // ---------------- p.V: lane = (slot, 8-dim slice u); slot takes token pairs slot + 4k
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int pr = slot + 4 * k;
+          const uint32_t cA = cur[2 * k], cB = cur[2 * k + 1];
+          const uint4 wv = *(const uint4*)(wsrc + (pr * 4 + grp) * QH);
+          const uint32_t wh[QH] = {wv.x, wv.y, wv.z, wv.w};
+          uint32_t pairs[8];
+          if (VB == 2) {
+            const uint32_t Y = cA | (cB << 16);
+            const uint32_t Y2 = __builtin_amdgcn_perm(0u, Y, 0x0c030c01u);  // bytes 1, 3 -> 0, 2
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              pairs[i] = Y & (0x00030003u << (2 * i));
+              pairs[4 + i] = Y2 & (0x00030003u << (2 * i));
+            }
+          } else {
+            const uint32_t Ylo = __builtin_amdgcn_perm(cB, cA, 0x05040100u);  // A.lo16 | B.lo16 << 16
+            const uint32_t Yhi = __builtin_amdgcn_perm(cB, cA, 0x07060302u);  // A.hi16 | B.hi16 << 16
+            const uint32_t Ylo2 = __builtin_amdgcn_perm(0u, Ylo, 0x0c030c01u);
+            const uint32_t Yhi2 = __builtin_amdgcn_perm(0u, Yhi, 0x0c030c01u);
+            pairs[0] = Ylo & 0x000F000Fu;  pairs[1] = Ylo & 0x00F000F0u;
+            pairs[2] = Ylo2 & 0x000F000Fu; pairs[3] = Ylo2 & 0x00F000F0u;
+            pairs[4] = Yhi & 0x000F000Fu;  pairs[5] = Yhi & 0x00F000F0u;
+            pairs[6] = Yhi2 & 0x000F000Fu; pairs[7] = Yhi2 & 0x00F000F0u;
+          }
+#pragma unroll
+          for (int hh = 0; hh < QH; ++hh) {
+            const half2_t w2 = __builtin_bit_cast(half2_t, wh[hh]);
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+              acc[hh][i] = __builtin_amdgcn_fdot2(w2, __builtin_bit_cast(half2_t, pairs[i]), acc[hh][i], false);
+          }
+        }
+      }
+      __syncthreads();
+    }
+    // undo the subnormal placement: dim i of a slice carries code * 2^-24 * step_i
+#pragma unroll
+    for (int hh = 0; hh < QH; ++hh)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float step = VB == 2 ? (float)(1 << (2 * (i & 3))) : (float)(1 << (4 * (i & 1)));
+        float v = acc[hh][i];
+        v += __shfl_xor(v, 16);
+        v += __shfl_xor(v, 32);
+        if (lane < 16) mine[hh * RS + 6 + 8 * u + i] = v * (16777216.0f / step);
+      }
+  }
+  __syncthreads();
+  for (int i = tid; i < QH * KD; i += NT) {
+    const int hh = i / KD, j = i % KD;
     const int gq = QH * quad + hh;
     float M = -INFINITY;
-    for (int w = 0; w < NW; ++w) M = fmaxf(M, red[(w * QH + hh) * RS]);
+    for (int w = 0; w < NS; ++w) M = fmaxf(M, red[(w * QH + hh) * RS]);
     float L = 0.0f, O = 0.0f;
     if (M != -INFINITY) {
-      for (int w = 0; w < NW; ++w) {
-        const float* r = red + (w * QH + hh) * RS;
-        const float f = r[0] == -INFINITY ? 0.0f : exp2f(r[0] - M);
-        L = fmaf(r[1], f, L);
-        O = fmaf(r[6 + j] + r[2 + j / 32], f, O);
+      for (int w = 0; w < NS; ++w) {
+        const float* rr = red + (w * QH + hh) * RS;
+        const float f = rr[0] == -INFINITY ? 0.0f : exp2f(rr[0] - M);
+        L = fmaf(rr[1], f, L);
+        O = fmaf(rr[6 + j] + rr[2 + j / 32], f, O);
       }
     }
     if (gq < a.G) {
@@ -484,7 +612,7 @@ int cu_count() {
 template <int MODE, int B0, int B1>
 size_t smem_bytes() {
   using F = Fmt<MODE, B0, B1>;
-  return (size_t)(F::E0 + F::E1) * 8 + 2 * QH * KD * 4 + NW * 32 * 4 * QH * 4 + 4 * QH * 4;
+  return (size_t)(F::E0 + F::E1) * 8 + 2 * QH * KD * 4 + NW * 32 * 4 * QH * 4 + 4 * QH * 4 + 32 * 4 + 2 * (NW / 2) * QH * 4 + 2 * QH * 4;
 }
 
 template <int MODE, int B0, int B1, int VB>
