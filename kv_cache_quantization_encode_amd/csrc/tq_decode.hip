@@ -65,9 +65,27 @@ struct Fmt {
   static constexpr int P1 = PROD ? KD / 8 : GROUPED ? PD * W1 / 8 : 0;
   static constexpr int S0 = stride_of(B0);
   static constexpr int S1 = GROUPED ? stride_of(B1) : 256;
-  static constexpr int E0 = P0 * S0, E1 = P1 * S1;              // table entries
+  static constexpr int E0 = P0 * S0, E1 = P1 * S1;              // table entries, [position][value]
   static constexpr int IDXB = P0 + (GROUPED ? P1 : 0);          // idx row bytes
   static constexpr int KWORDS = (IDXB + (PROD ? KD / 8 : 0)) / 4;  // idx + sign words
+  // the weight ring also holds the half tables while the lookup tables are built
+  static constexpr int RING_BYTES_W = NW * 32 * 4 * QH * 4;
+  static constexpr int HALF_BYTES = (P0 + P1) * 32 * 16;
+  static constexpr int RING_BYTES = RING_BYTES_W > HALF_BYTES ? RING_BYTES_W : HALF_BYTES;
+};
+
+template <int MODE, int B0, int B1>
+struct Lds {
+  using F = Fmt<MODE, B0, B1>;
+  uint2 lut[F::E0 + F::E1];
+  float qp[QH * KD];
+  float qs[QH * KD];
+  uint32_t ring[F::RING_BYTES / 4];
+  float scl[2 * QH];
+  int amax[2 * QH];
+  float cen[32];
+  float abuf[2 * (NW / 2) * QH];
+  float hmul[2 * QH];
 };
 
 struct DecArgs {
@@ -100,6 +118,26 @@ __device__ inline float load_q(const void* q, int dt, long long i) {
 
 __device__ inline float h2f(uint32_t bits16) { return __half2float(__ushort_as_half((unsigned short)bits16)); }
 
+// Entry of the table at byte offset BASE indexed by byte k of w.  Under
+// 64 KiB the index times 8 is a single SDWA shift and BASE folds into the
+// ds_read immediate; past it, a field extract and a shift-add.
+// (BASE and k are constants once the caller's loop is unrolled.)
+__device__ __forceinline__ uint2 lut_read(const unsigned char* smem, uint32_t BASE, uint32_t w, int k) {
+  uint32_t off;
+  if (BASE + 2048u <= 65536u) {
+    switch (k) {
+      case 0: asm("v_lshlrev_b32_sdwa %0, 3, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_0" : "=v"(off) : "v"(w)); break;
+      case 1: asm("v_lshlrev_b32_sdwa %0, 3, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_1" : "=v"(off) : "v"(w)); break;
+      case 2: asm("v_lshlrev_b32_sdwa %0, 3, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_2" : "=v"(off) : "v"(w)); break;
+      default: asm("v_lshlrev_b32_sdwa %0, 3, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_3" : "=v"(off) : "v"(w)); break;
+    }
+    return *(const uint2*)(smem + off + BASE);
+  } else {
+    off = (__builtin_amdgcn_ubfe(w, 8 * k, 8) << 3) + BASE;
+    return *(const uint2*)(smem + off);
+  }
+}
+
 template <int I, int N, typename Fn>
 __device__ inline void static_for(Fn&& fn) {
   if constexpr (I < N) {
@@ -126,16 +164,19 @@ __device__ inline float wave_sum(float v) {
 template <int MODE, int B0, int B1, int VB>
 __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
   using F = Fmt<MODE, B0, B1>;
-  extern __shared__ __align__(16) unsigned char smem[];
-  uint2* lut = (uint2*)smem;                                  // [E0 + E1] x 4 fp16
-  float* qp = (float*)(smem + (size_t)(F::E0 + F::E1) * 8);   // [QH][KD] rotated queries
-  float* qs = qp + QH * KD;                                   // [QH][KD] S q' (PROD)
-  uint32_t* wbuf = (uint32_t*)(qs + QH * KD);                 // [NW][32 pairs][4 groups][QH] half2
-  float* scl = (float*)(wbuf + NW * 32 * 4 * QH);             // [2][QH] table scales
-  int* amax = (int*)(scl + 2 * QH);                           // [2][QH]
-  float* cen = (float*)(amax + 2 * QH);                       // [2][16] centroids of each part
-  float* abuf = cen + 32;                                     // [2][NW/2][QH] softmax rescale factors
-  float* hmul = abuf + 2 * (NW / 2) * QH;                     // [2][QH] score multipliers
+  // Static LDS (its offsets are known to the compiler, so table offsets fold
+  // into the ds_read immediates).
+  __shared__ Lds<MODE, B0, B1> L;
+  unsigned char* smem = (unsigned char*)&L;
+  uint2* lut = L.lut;       // tables: class 0 [value][position], class 1 [position][value]
+  float* qp = L.qp;         // [QH][KD] rotated queries
+  float* qs = L.qs;         // [QH][KD] S q' (PROD)
+  uint32_t* wbuf = L.ring;  // [2][NW/2][32 pairs][4 groups][QH] half2 weights
+  float* scl = L.scl;       // [2][QH] table scales
+  int* amax = L.amax;       // [2][QH]
+  float* cen = L.cen;       // [2][16] centroids of each part
+  float* abuf = L.abuf;     // [2][NW/2][QH] softmax rescale factors
+  float* hmul = L.hmul;     // [2][QH] score multipliers
 
   const tq_blob_header* H = (const tq_blob_header*)a.tables;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -144,6 +185,77 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
   const int ctx = a.ctx_len[b];
   const int t_begin = split * a.chunk;
   const int t_end = min(ctx, t_begin + a.chunk);
+
+  const long long rec0 = ((long long)b * a.Hkv + hkv) * a.max_ctx;
+  // ---- main loop, split between two kinds of waves.  Score waves (the first
+  // half) read key bytes, look up the tables, run the online softmax and
+  // publish fp16 weights p*scale; p.V waves (second half) accumulate those
+  // weights against the value codes one round later.  Wave pw of each half
+  // owns tiles pw, pw + NS, pw + 2 NS, ...; a two-slot LDS ring carries the
+  // weights and the softmax rescale factor from score wave pw to p.V wave pw,
+  // and one barrier per round separates producer and consumer.  Each wave
+  // loads its next tile's data one round ahead.
+  constexpr int NS = NW / 2;
+  constexpr int VROW = KD * VB / 8;  // bytes of a value-code row
+  const bool scorer = wave < NS;
+  const int pw = scorer ? wave : wave - NS;
+  const int slot = lane >> 4, u = lane & 15, grp = u >> 2;
+  const int n_tiles = t_end > t_begin ? (t_end - t_begin + TILE - 1) / TILE : 0;
+  const int rounds = (n_tiles + NS - 1) / NS;
+  auto tile_tb = [&](int r) { return t_begin + (r * NS + pw) * TILE; };
+
+  struct KeyData {
+    uint32_t kw[F::KWORDS];
+    uint32_t nrm, rn;  // fp16 norm(s), fp16 residual norm
+    uint2 zv, sv;      // fp16 zero / scale of the four value groups
+  };
+  // Token indices are clamped into [t_begin, max(t_end - 1, t_begin)], a
+  // range inside this (sequence, head)'s rows, so loads need no branches;
+  // lanes past t_end get score -inf and weight 0.
+  const int t_last = t_end - 1 > t_begin ? t_end - 1 : t_begin;
+  auto load_keys = [&](int tb, KeyData& d) {
+    const int t = tb + TILE <= t_end ? tb + lane : min(tb + lane, t_last);
+    const long long rec = rec0 + t;
+    const uint32_t* ip = (const uint32_t*)(a.idx + rec * F::IDXB);
+#pragma unroll
+    for (int k = 0; k < F::IDXB / 4; ++k) d.kw[k] = ip[k];
+    if constexpr (F::PROD) {
+      const uint4 sv = *(const uint4*)(a.signs + rec * (KD / 8));
+      d.kw[F::IDXB / 4 + 0] = sv.x; d.kw[F::IDXB / 4 + 1] = sv.y;
+      d.kw[F::IDXB / 4 + 2] = sv.z; d.kw[F::IDXB / 4 + 3] = sv.w;
+      d.rn = a.rnorm[rec];
+    } else {
+      d.rn = 0;
+    }
+    d.nrm = F::GROUPED ? *(const uint32_t*)(a.norm + 2 * rec) : (uint32_t)a.norm[rec];
+    d.zv = *(const uint2*)(a.vzero + rec * 4);
+    d.sv = *(const uint2*)(a.vscale + rec * 4);
+  };
+  // value codes of this lane's token pairs (slot + 4k): [2k] even token, [2k+1] odd token
+  auto load_codes = [&](int tb, uint32_t* c) {
+    if (tb + TILE <= t_end) {  // whole tile: one base address, immediate offsets
+      const uint8_t* base = a.vcodes + (rec0 + tb + 2 * slot) * VROW + VB * u;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const uint8_t* pa = base + ((k >> 1) * 8 + (k & 1)) * VROW;
+        c[k] = VB == 2 ? (uint32_t) * (const uint16_t*)pa : *(const uint32_t*)pa;
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const int t = min(tb + 2 * slot + (k >> 1) * 8 + (k & 1), t_last);
+        const uint8_t* pa = a.vcodes + (rec0 + t) * VROW + VB * u;
+        c[k] = VB == 2 ? (uint32_t) * (const uint16_t*)pa : *(const uint32_t*)pa;
+      }
+    }
+  };
+
+  // The first tile of each wave is requested before the prologue, whose
+  // table building then covers the memory latency.
+  KeyData kd;
+  uint32_t codes[16];
+  if (scorer) load_keys(tile_tb(0), kd);
+  else load_codes(tile_tb(0), codes);
 
   // ---- prologue: rotate the queries, project them, build the tables
   if (tid < 2 * QH) amax[tid] = 0;
@@ -229,38 +341,51 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
     scl[tid] = bound > 0.0f ? exp2f(floorf(log2f(16384.0f / bound))) : 1.0f;
   }
   __syncthreads();
-  for (int e = tid; e < F::E0 + F::E1; e += NT) {
-    const bool c1 = e >= F::E0;
-    const int ee = c1 ? e - F::E0 : e;
-    const int S = c1 ? F::S1 : F::S0;
-    const int p = ee / S, v = ee % S;
+  // Half tables: for each byte position, class, nibble half and nibble value,
+  // the four heads' partial sums over the coordinates (or sign rows) that
+  // nibble holds, already scaled.  A byte's entry is then lo[v & 15] +
+  // hi[v >> 4].  They live in the weight ring, unused until the main loop.
+  float4* halves = (float4*)wbuf;  // [P0 + P1][2][16]
+  for (int i = tid; i < (F::P0 + F::P1) * 32; i += NT) {
+    const int pos = i >> 5, half = (i >> 4) & 1, n = i & 15;
+    const bool c1 = pos >= F::P0;
+    const int p = c1 ? pos - F::P0 : pos;
     float s[QH] = {0.0f, 0.0f, 0.0f, 0.0f};
     if (c1 && F::PROD) {
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const float sg = ((v >> k) & 1) ? 1.0f : -1.0f;
+      for (int k = 0; k < 4; ++k) {
+        const float sg = ((n >> k) & 1) ? 1.0f : -1.0f;
 #pragma unroll
-        for (int hh = 0; hh < QH; ++hh) s[hh] = fmaf(sg, qs[hh * KD + 8 * p + k], s[hh]);
+        for (int hh = 0; hh < QH; ++hh) s[hh] = fmaf(sg, qs[hh * KD + 8 * p + 4 * half + k], s[hh]);
       }
     } else {
       const int part = c1 ? 1 : 0;
       const int W = c1 ? F::W1 : F::W0;
-      const int cpb = 8 / W;
+      const int per = 4 / W;  // coordinates per nibble
       const int bits = H->part_bits[F::GROUPED ? part : 0];
       const int fmask = (1 << bits) - 1;
       const float* cent = cen + 16 * (F::GROUPED ? part : 0);
-      const int j0 = part * F::PD + p * cpb;
-      for (int k = 0; k < cpb; ++k) {
-        const float c = cent[(v >> (W * k)) & fmask];
+      const int j0 = part * F::PD + p * (8 / W) + half * per;
+      for (int k = 0; k < per; ++k) {
+        const float c = cent[(n >> (W * k)) & fmask];
 #pragma unroll
         for (int hh = 0; hh < QH; ++hh) s[hh] = fmaf(c, qp[hh * KD + j0 + k], s[hh]);
       }
     }
     const float* sc = scl + (c1 ? QH : 0);
-    const uint32_t lo = (uint32_t)__half_as_ushort(__float2half_rn(s[0] * sc[0])) |
-                        ((uint32_t)__half_as_ushort(__float2half_rn(s[1] * sc[1])) << 16);
-    const uint32_t hi = (uint32_t)__half_as_ushort(__float2half_rn(s[2] * sc[2])) |
-                        ((uint32_t)__half_as_ushort(__float2half_rn(s[3] * sc[3])) << 16);
+    halves[i] = make_float4(s[0] * sc[0], s[1] * sc[1], s[2] * sc[2], s[3] * sc[3]);
+  }
+  __syncthreads();
+  for (int e = tid; e < F::E0 + F::E1; e += NT) {
+    const bool c1 = e >= F::E0;
+    const int ee = c1 ? e - F::E0 : e;
+    const int S = c1 ? F::S1 : F::S0;
+    const int pos = (c1 ? F::P0 : 0) + ee / S, v = ee % S;
+    const float4 lo4 = halves[pos * 32 + (v & 15)], hi4 = halves[pos * 32 + 16 + (v >> 4)];
+    const uint32_t lo = (uint32_t)__half_as_ushort(__float2half_rn(lo4.x + hi4.x)) |
+                        ((uint32_t)__half_as_ushort(__float2half_rn(lo4.y + hi4.y)) << 16);
+    const uint32_t hi = (uint32_t)__half_as_ushort(__float2half_rn(lo4.z + hi4.z)) |
+                        ((uint32_t)__half_as_ushort(__float2half_rn(lo4.w + hi4.w)) << 16);
     lut[e] = make_uint2(lo, hi);
   }
   __syncthreads();
@@ -275,71 +400,6 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
   }
   __syncthreads();
   const float xscale = a.sm_scale * LOG2E;
-  const long long rec0 = ((long long)b * a.Hkv + hkv) * a.max_ctx;
-
-  // ---- main loop, split between two kinds of waves.  Score waves (the first
-  // half) read key bytes, look up the tables, run the online softmax and
-  // publish fp16 weights p*scale; p.V waves (second half) accumulate those
-  // weights against the value codes one round later.  Wave pw of each half
-  // owns tiles pw, pw + NS, pw + 2 NS, ...; a two-slot LDS ring carries the
-  // weights and the softmax rescale factor from score wave pw to p.V wave pw,
-  // and one barrier per round separates producer and consumer.  Each wave
-  // loads its next tile's data one round ahead.
-  constexpr int NS = NW / 2;
-  constexpr int VROW = KD * VB / 8;  // bytes of a value-code row
-  const bool scorer = wave < NS;
-  const int pw = scorer ? wave : wave - NS;
-  const int slot = lane >> 4, u = lane & 15, grp = u >> 2;
-  const int n_tiles = t_end > t_begin ? (t_end - t_begin + TILE - 1) / TILE : 0;
-  const int rounds = (n_tiles + NS - 1) / NS;
-  auto tile_tb = [&](int r) { return t_begin + (r * NS + pw) * TILE; };
-
-  struct KeyData {
-    uint32_t kw[F::KWORDS];
-    uint32_t nrm, rn;  // fp16 norm(s), fp16 residual norm
-    uint2 zv, sv;      // fp16 zero / scale of the four value groups
-  };
-  auto load_keys = [&](int tb, KeyData& d) {
-    const int t = tb + lane;
-    if (t < t_end) {
-      const long long rec = rec0 + t;
-      const uint32_t* ip = (const uint32_t*)(a.idx + rec * F::IDXB);
-#pragma unroll
-      for (int k = 0; k < F::IDXB / 4; ++k) d.kw[k] = ip[k];
-      if constexpr (F::PROD) {
-        const uint4 sv = *(const uint4*)(a.signs + rec * (KD / 8));
-        d.kw[F::IDXB / 4 + 0] = sv.x; d.kw[F::IDXB / 4 + 1] = sv.y;
-        d.kw[F::IDXB / 4 + 2] = sv.z; d.kw[F::IDXB / 4 + 3] = sv.w;
-        d.rn = a.rnorm[rec];
-      } else {
-        d.rn = 0;
-      }
-      d.nrm = F::GROUPED ? *(const uint32_t*)(a.norm + 2 * rec) : (uint32_t)a.norm[rec];
-      d.zv = *(const uint2*)(a.vzero + rec * 4);
-      d.sv = *(const uint2*)(a.vscale + rec * 4);
-    } else {
-#pragma unroll
-      for (int k = 0; k < F::KWORDS; ++k) d.kw[k] = 0;
-      d.nrm = d.rn = 0;
-      d.zv = d.sv = make_uint2(0, 0);
-    }
-  };
-  // value codes of this lane's token pairs (slot + 4k): [2k] even token, [2k+1] odd token
-  auto load_codes = [&](int tb, uint32_t* c) {
-    const uint8_t* cbase = a.vcodes + (rec0 + tb + 2 * slot) * VROW + VB * u;
-    const bool full = tb + TILE <= t_end;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-#pragma unroll
-      for (int o = 0; o < 2; ++o) {
-        const uint8_t* pa = cbase + (8 * k + o) * VROW;
-        uint32_t v = 0;
-        if (full || tb + 2 * slot + 8 * k + o < t_end)
-          v = VB == 2 ? (uint32_t) * (const uint16_t*)pa : *(const uint32_t*)pa;
-        c[2 * k + o] = v;
-      }
-    }
-  };
 
   const half2_t e10 = {(_Float16)1.0f, (_Float16)0.0f}, e01 = {(_Float16)0.0f, (_Float16)1.0f};
   float* red = (float*)smem;  // [NS][QH][2 + 4 + KD], over the tables once every wave is done
@@ -356,8 +416,6 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
 #pragma unroll
       for (int k = 0; k < 4; ++k) zacc[hh][k] = 0.0f;
     }
-    KeyData kd;
-    load_keys(tile_tb(0), kd);
     for (int r = 0; r <= rounds; ++r) {
       const int tb = tile_tb(r);
       if (r < rounds && tb < t_end) {
@@ -376,8 +434,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
           for (int p = 0; p < F::P0; ++p) {
             // cap the table reads in flight (each holds two registers)
             if (p % TQ_DEC_LOOKUP_BATCH == 0) __builtin_amdgcn_sched_barrier(0);
-            const uint32_t v = (kd.kw[p >> 2] >> (8 * (p & 3))) & 0xFFu;
-            const uint2 e = lut[p * F::S0 + v];
+            const uint2 e = lut_read(smem, (uint32_t)(p * F::S0) * 8u, kd.kw[p >> 2], p & 3);
             const half2_t x01 = __builtin_bit_cast(half2_t, e.x), x23 = __builtin_bit_cast(half2_t, e.y);
             A[0] = __builtin_amdgcn_fdot2(x01, e10, A[0], false);
             A[1] = __builtin_amdgcn_fdot2(x01, e01, A[1], false);
@@ -388,8 +445,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
           for (int p = 0; p < F::P1; ++p) {
             if (p % TQ_DEC_LOOKUP_BATCH == 0) __builtin_amdgcn_sched_barrier(0);
             const int byte = F::P0 + p;
-            const uint32_t v = (kd.kw[byte >> 2] >> (8 * (byte & 3))) & 0xFFu;
-            const uint2 e = lut[F::E0 + p * F::S1 + v];
+            const uint2 e = lut_read(smem, (uint32_t)(F::E0 + p * F::S1) * 8u, kd.kw[byte >> 2], byte & 3);
             const half2_t x01 = __builtin_bit_cast(half2_t, e.x), x23 = __builtin_bit_cast(half2_t, e.y);
             Bc[0] = __builtin_amdgcn_fdot2(x01, e10, Bc[0], false);
             Bc[1] = __builtin_amdgcn_fdot2(x01, e01, Bc[1], false);
@@ -481,15 +537,13 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
     for (int hh = 0; hh < QH; ++hh)
 #pragma unroll
       for (int k = 0; k < 8; ++k) acc[hh][k] = 0.0f;
-    uint32_t codes[16];
-    load_codes(tile_tb(0), codes);
-    for (int r = 0; r <= rounds; ++r) {
+    // two code buffers in turn: a round consumes one while the next tile's
+    // codes arrive in the other
+    uint32_t codes2[16];
+    auto pv_round = [&](int r, const uint32_t* cur, uint32_t* nxt) {
       const int tb = r >= 1 ? tile_tb(r - 1) : t_end;
       if (tb < t_end) {
-        uint32_t cur[16];
-#pragma unroll
-        for (int k = 0; k < 16; ++k) cur[k] = codes[k];
-        load_codes(tile_tb(r), codes);  // next round's tile
+        load_codes(tile_tb(r), nxt);  // next round's tile
         const uint32_t* wsrc = wbuf + (((r - 1) & 1) * NS + pw) * (32 * 4 * QH);
         const float4 al = *(const float4*)(abuf + (((r - 1) & 1) * NS + pw) * QH);
         const float alv[QH] = {uniform(al.x), uniform(al.y), uniform(al.z), uniform(al.w)};
@@ -534,7 +588,14 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
           }
         }
       }
+    };
+    for (int r = 0; r <= rounds; r += 2) {
+      pv_round(r, codes2, codes);
       __syncthreads();
+      if (r + 1 <= rounds) {
+        pv_round(r + 1, codes, codes2);
+        __syncthreads();
+      }
     }
     // undo the subnormal placement: dim i of a slice carries code * 2^-24 * step_i
 #pragma unroll
@@ -609,23 +670,9 @@ int cu_count() {
   return n;
 }
 
-template <int MODE, int B0, int B1>
-size_t smem_bytes() {
-  using F = Fmt<MODE, B0, B1>;
-  return (size_t)(F::E0 + F::E1) * 8 + 2 * QH * KD * 4 + NW * 32 * 4 * QH * 4 + 4 * QH * 4 + 32 * 4 + 2 * (NW / 2) * QH * 4 + 2 * QH * 4;
-}
-
 template <int MODE, int B0, int B1, int VB>
 hipError_t launch(const DecArgs& a, dim3 grid, hipStream_t s) {
-  const size_t sm = smem_bytes<MODE, B0, B1>();
-  static std::atomic<bool> attr_set{false};
-  if (!attr_set.load(std::memory_order_relaxed)) {
-    hipError_t e = hipFuncSetAttribute((const void*)decode_kernel<MODE, B0, B1, VB>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm);
-    if (e != hipSuccess) return e;
-    attr_set.store(true, std::memory_order_relaxed);
-  }
-  hipLaunchKernelGGL((decode_kernel<MODE, B0, B1, VB>), grid, dim3(NT), sm, s, a);
+  hipLaunchKernelGGL((decode_kernel<MODE, B0, B1, VB>), grid, dim3(NT), 0, s, a);
   return hipGetLastError();
 }
 
