@@ -46,10 +46,19 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-encode-bench", action="store_true")
-    ap.add_argument("--cpu-groups", type=int, default=24,
+    ap.add_argument("--cpu-groups", type=int, default=128,
                     help="(sequence, KV head) groups the CPU oracle decodes for its baseline")
     ap.add_argument("--profile-decode", type=int, default=0,
                     help="only run this many decode calls after setup (for rocprofv3 runs)")
+    ap.add_argument("--profile-encode", type=int, default=0,
+                    help="only run this many bulk key and value encodes of the cache (rocprofv3 runs)")
+    ap.add_argument("--profile-copy", type=int, default=0,
+                    help="with --profile-decode: also run five float32 negations of this many MiB "
+                         "(a plain streaming kernel of known size that calibrates HBM counters)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU work: turn two rocprofv3 --pmc counter_collection.csv files "
+                         "(FETCH_SIZE, WRITE_SIZE) of a --profile-decode --profile-copy run into "
+                         "profiles/decode_gqa32k_traffic.json")
     return ap.parse_args()
 
 
@@ -71,6 +80,57 @@ def traffic_from_profile():
     if t.get("source_sha256_16") != source_hash(src):
         return None
     return t.get("traffic_bytes_per_launch")
+
+
+def _pmc_means(path, counter):
+    """Mean per-dispatch value of `counter` by kernel family (decode, merge,
+    calibration copy) from a rocprofv3 counter_collection.csv."""
+    import csv
+    acc = {}
+    with open(path, newline="") as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] != counter:
+                continue
+            name = r["Kernel_Name"]
+            fam = ("decode" if "decode_kernel" in name else "merge" if "merge_kernel" in name
+                   else "copy" if "neg_kernel" in name else None)
+            if fam is None:
+                continue
+            key = (fam, r["Dispatch_Id"])
+            acc[key] = acc.get(key, 0.0) + float(r["Counter_Value"])
+    out = {}
+    for (fam, _), v in acc.items():
+        out.setdefault(fam, []).append(v)
+    return {fam: sum(v) / len(v) for fam, v in out.items()}, {fam: len(v) for fam, v in out.items()}
+
+
+def write_traffic(fetch_csv, write_csv, copy_mib):
+    """HBM traffic of one tq_decode_attention call (decode_kernel +
+    merge_kernel) from FETCH_SIZE / WRITE_SIZE (KiB per dispatch), each scaled
+    by the ratio of the true bytes of the calibration copy to what the same
+    counter reports for it."""
+    fetch, nf = _pmc_means(fetch_csv, "FETCH_SIZE")
+    write, nw = _pmc_means(write_csv, "WRITE_SIZE")
+    copy_bytes = copy_mib * 1024 * 1024
+    f_scale = copy_bytes / (fetch["copy"] * 1024.0)
+    w_scale = copy_bytes / (write["copy"] * 1024.0)
+    rd = (fetch["decode"] + fetch.get("merge", 0.0)) * 1024.0 * f_scale
+    wr = (write["decode"] + write.get("merge", 0.0)) * 1024.0 * w_scale
+    src = os.path.join(ROOT, "kv_cache_quantization_encode_amd", "csrc", "tq_decode.hip")
+    rec = {"source_sha256_16": source_hash(src),
+           "workload": "gqa-decode-32k",
+           "fetch_kib_per_dispatch": fetch, "write_kib_per_dispatch": write,
+           "dispatches": {"fetch": nf, "write": nw},
+           "copy_bytes": copy_bytes, "fetch_scale": f_scale, "write_scale": w_scale,
+           "read_bytes_per_launch": rd, "write_bytes_per_launch": wr,
+           "traffic_bytes_per_launch": rd + wr,
+           "algorithmic_bytes": DECODE_BYTES,
+           "traffic_over_algorithmic": (rd + wr) / DECODE_BYTES}
+    p = os.path.join(ROOT, "profiles", "decode_gqa32k_traffic.json")
+    with open(p, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec, indent=1))
 
 
 def cpu_baseline(n_groups):
@@ -112,6 +172,9 @@ def cpu_baseline(n_groups):
 
 def main():
     args = parse()
+    if args.traffic_from:
+        write_traffic(args.traffic_from[0], args.traffic_from[1], args.profile_copy or 1024)
+        return
     if args.gpus != 1:
         print("bench.py runs on one GPU only (this path has no multi-GPU mode); got --gpus %d" % args.gpus,
               file=sys.stderr)
@@ -148,7 +211,23 @@ def main():
         for i in range(args.profile_decode):
             dec(qs[i % n_steps_total], ctx_len, kp, vp, out=out)
         torch.cuda.synchronize()
-        print("profiled %d decode calls" % args.profile_decode)
+        print("profiled %d decode calls" % args.profile_decode, flush=True)
+        if args.profile_copy:
+            del keys, vals
+            n = args.profile_copy * 1024 * 1024 // 4
+            src = torch.ones(n, dtype=torch.float32, device=dev)
+            dst = torch.empty_like(src)
+            for _ in range(5):
+                torch.neg(src, out=dst)
+            torch.cuda.synchronize()
+            print("profiled 5 copies of %d MiB" % args.profile_copy, flush=True)
+        return
+    if args.profile_encode:
+        for _ in range(args.profile_encode):
+            tq.encode_keys(T, keys, kp)
+            tq.encode_values(vals, 2, planes=vp)
+        torch.cuda.synchronize()
+        print("profiled %d bulk encodes of %d keys and values" % (args.profile_encode, n_rec), flush=True)
         return
 
     def step(i, ev=None):
