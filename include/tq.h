@@ -172,9 +172,10 @@ tq_status tq_encode_values(int32_t bits, int32_t group, int32_t d,
  *              t >= ctx_len[b] are not written).
  *   workspace  device scratch; with workspace == NULL the call only stores the
  *              required size in *workspace_bytes (host) and returns TQ_OK.
- * Supported: d = 128; PROD with bits 3 (2-bit index) or 4 (3-bit index in
- * nibbles); MSE with bits 2 or 4; GROUPED with (4, 2) or (2, 2) or (4, 4)
- * halves; Hq % Hkv == 0.  Other shapes return TQ_ERR_UNSUPPORTED.
+ * Supported: d = 128; PROD with bits 2..4 (index 1..3 bits, 3 in nibbles);
+ * MSE with bits 1..3; GROUPED with (outlier, normal) index bits (4, 2),
+ * (3, 2), (2, 2) or (4, 1); Hq % Hkv == 0.  Other shapes return
+ * TQ_ERR_UNSUPPORTED.  (Encode supports every mode and width above.)
  */
 tq_status tq_decode_attention(const tq_key_config* cfg, const void* tables,
                               const void* q, int32_t q_dtype, int32_t B, int32_t Hq, int32_t Hkv,
