@@ -81,7 +81,6 @@ struct Lds {
   float qp[QH * KD];
   float qs[QH * KD];
   uint32_t ring[F::RING_BYTES / 4];
-  float scl[2 * QH];
   int amax[2 * QH];
   float cen[32];
   float abuf[2 * (NW / 2) * QH];
@@ -146,6 +145,48 @@ __device__ inline void static_for(Fn&& fn) {
   }
 }
 
+// Largest power of two P with P * bound <= 16384 (1 for a zero bound), from
+// the exponent of bound = m 2^e, m in [0.5, 1).
+__device__ inline float pow2_scale(float bound) {
+  if (!(bound > 0.0f)) return 1.0f;
+  int e;
+  const float m = frexpf(bound, &e);
+  int k = (m > 0.5f ? 14 : 15) - e;
+  k = k > 126 ? 126 : k < -126 ? -126 : k;
+  return ldexpf(1.0f, k);
+}
+
+// DPP lane moves (gfx9 encodings): quad permutations, half-row and row mirrors.
+template <int CTRL>
+__device__ inline float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+constexpr int DPP_XOR1 = 0xB1, DPP_XOR2 = 0x4E, DPP_HALF_MIRROR = 0x141, DPP_ROW_MIRROR = 0x140;
+
+// Sum over each aligned group of eight lanes, in all eight.
+__device__ inline float sum8(float v) {
+  v += dpp<DPP_XOR1>(v);
+  v += dpp<DPP_XOR2>(v);
+  return v + dpp<DPP_HALF_MIRROR>(v);
+}
+
+// Maximum over the wave of a value that is already uniform in each aligned
+// group of eight lanes (for any value: pass it through max8 first).
+__device__ inline float wave_max_of_eights(float v) {
+  v = fmaxf(v, dpp<DPP_ROW_MIRROR>(v));
+  const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return fmaxf(fmaxf(a, b), fmaxf(c, d));
+}
+
+__device__ inline float max8(float v) {
+  v = fmaxf(v, dpp<DPP_XOR1>(v));
+  v = fmaxf(v, dpp<DPP_XOR2>(v));
+  return fmaxf(v, dpp<DPP_HALF_MIRROR>(v));
+}
+
 // A value every lane holds alike, moved to a scalar register.
 __device__ inline float uniform(float v) { return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v))); }
 
@@ -172,7 +213,6 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
   float* qp = L.qp;         // [QH][KD] rotated queries
   float* qs = L.qs;         // [QH][KD] S q' (PROD)
   uint32_t* wbuf = L.ring;  // [2][NW/2][32 pairs][4 groups][QH] half2 weights
-  float* scl = L.scl;       // [2][QH] table scales
   int* amax = L.amax;       // [2][QH]
   float* cen = L.cen;       // [2][16] centroids of each part
   float* abuf = L.abuf;     // [2][NW/2][QH] softmax rescale factors
@@ -250,97 +290,120 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
     }
   };
 
-  // The first tile of each wave is requested before the prologue, whose
-  // table building then covers the memory latency.
-  KeyData kd;
-  uint32_t codes[16];
-  if (scorer) load_keys(tile_tb(0), kd);
-  else load_codes(tile_tb(0), codes);
-
-  // ---- prologue: rotate the queries, project them, build the tables
-  if (tid < 2 * QH) amax[tid] = 0;
+  // ---- prologue: rotate the queries, project them, build the tables.
+  // Global reads go out first, in the order they are needed: the queries and
+  // sigma, the rows of S, then each wave's first tile (whose latency the
+  // table building covers).
+  const int n_parts = H->n_parts;
+  const float* cent0 = (const float*)(a.tables + H->off_centroids[0]);
+  const float* cent1 = (const float*)(a.tables + H->off_centroids[n_parts > 1 ? 1 : 0]);
+  const int lev0 = H->part_levels[0], lev1 = H->part_levels[n_parts > 1 ? 1 : 0];
+  // waves 0..QH-1: head `wave` of the quad; lane holds coordinates lane, lane + 64
+  float x0 = 0.0f, x1 = 0.0f, sg0 = 0.0f, sg1 = 0.0f;
+  const int gq_w = QH * quad + wave;  // query head within the GQA group
+  if (wave < QH) {
+    if (gq_w < a.G) {
+      const long long qrow = ((long long)b * a.Hq + hkv * a.G + gq_w) * KD;
+      x0 = load_q(a.q, a.q_dtype, qrow + lane);
+      x1 = load_q(a.q, a.q_dtype, qrow + lane + 64);
+    }
+    const float* sig0 = (const float*)(a.tables + H->off_sigma[0]);
+    const float* sig1 = (const float*)(a.tables + H->off_sigma[n_parts > 1 ? 1 : 0]);
+    sg0 = sig0[lane];
+    sg1 = F::GROUPED ? sig1[lane] : sig0[lane + 64];
+  }
+  // q_s = S q': thread -> (row tid / 8, 16-column chunk tid % 8), all 128 rows at once
+  static_assert(NT == 8 * KD, "S q' takes one row per eight threads");
+  const int srow = tid >> 3, sch = tid & 7;
+  uint4 sA = make_uint4(0, 0, 0, 0), sB = sA;
+  if constexpr (F::PROD) {
+    const uint4* sp = (const uint4*)((const uint16_t*)(a.tables + H->off_S) + (size_t)srow * KD + 16 * sch);
+    sA = sp[0];
+    sB = sp[1];
+  }
   if (tid < 32) {
     const int part = tid >> 4, k = tid & 15;
-    if (part < H->n_parts && k < H->part_levels[part])
-      cen[tid] = ((const float*)(a.tables + H->off_centroids[part]))[k];
+    if (part < n_parts && k < (part ? lev1 : lev0)) cen[tid] = (part ? cent1 : cent0)[k];
   }
-  for (int i = tid; i < QH * KD; i += NT) {
-    const int hh = i / KD, j = i % KD;
-    const int gq = QH * quad + hh;  // query head within the GQA group
-    float v = 0.0f;
-    if (gq < a.G) v = load_q(a.q, a.q_dtype, ((long long)b * a.Hq + hkv * a.G + gq) * KD + j);
-    const int part = F::GROUPED ? j / F::PD : 0;
-    const float* sig = (const float*)(a.tables + H->off_sigma[part]);
-    qp[i] = v * sig[j - part * F::PD];
+  if (!F::GROUPED && tid < QH) amax[QH + tid] = 0;
+
+  // Walsh-Hadamard transform of sigma * q in registers (one 128-point
+  // transform, or two 64-point ones for GROUPED): butterflies on lane bits
+  // through shuffles, the top stage inside the lane.
+  if (wave < QH) {
+    x0 *= sg0;
+    x1 *= sg1;
+    if constexpr (!F::GROUPED) {
+      const float t = x0;
+      x0 = t + x1;
+      x1 = t - x1;
+    }
+#pragma unroll
+    for (int st = 32; st >= 1; st >>= 1) {
+      const float y0 = __shfl_xor(x0, st), y1 = __shfl_xor(x1, st);
+      const bool up = lane & st;
+      x0 = up ? y0 - x0 : x0 + y0;
+      x1 = up ? y1 - x1 : x1 + y1;
+    }
+    qp[wave * KD + lane] = x0;
+    qp[wave * KD + lane + 64] = x1;
+    // largest |q'| per table class (GROUPED: per half)
+    const float m0 = wave_max_of_eights(max8(F::GROUPED ? fabsf(x0) : fmaxf(fabsf(x0), fabsf(x1))));
+    const float m1 = F::GROUPED ? wave_max_of_eights(max8(fabsf(x1))) : 0.0f;
+    if (lane == 0) {
+      amax[wave] = __float_as_int(m0);
+      if (F::GROUPED) amax[QH + wave] = __float_as_int(m1);
+    }
   }
   __syncthreads();
-  // Walsh-Hadamard butterflies, one stage per barrier (64-point halves for GROUPED)
-  for (int st = 1; st < F::PD; st <<= 1) {
-    for (int i = tid; i < QH * KD / 2; i += NT) {
-      const int hh = i / (KD / 2), r = i % (KD / 2);
-      const int lo = ((r / st) * 2 * st) + (r % st);
-      float* base = qp + hh * KD;
-      const float x = base[lo], y = base[lo + st];
-      base[lo] = x + y;
-      base[lo + st] = x - y;
-    }
-    __syncthreads();
-  }
+  KeyData kd;
+  uint32_t codes[16];
   if constexpr (F::PROD) {
-    // q_s = S q': thread -> (row, 16-column chunk); eight lanes finish a row
-    const uint16_t* S = (const uint16_t*)(a.tables + H->off_S);
-    const int ch = tid & 7;
-    for (int row = tid >> 3; row < KD; row += NT / 8) {
-      const uint4* sp = (const uint4*)(S + (size_t)row * KD + 16 * ch);
-      const uint4 s0 = sp[0], s1 = sp[1];
-      const uint32_t sw[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
-      float part[QH] = {0.0f, 0.0f, 0.0f, 0.0f};
+    const uint32_t sw[8] = {sA.x, sA.y, sA.z, sA.w, sB.x, sB.y, sB.z, sB.w};
+    float part[QH] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float lo = h2f(sw[i] & 0xFFFFu), hi = h2f(sw[i] >> 16);
+    for (int hh = 0; hh < QH; ++hh) {
+      const float4* qv = (const float4*)(qp + hh * KD + 16 * sch);
 #pragma unroll
-        for (int hh = 0; hh < QH; ++hh) {
-          part[hh] = fmaf(lo, qp[hh * KD + 16 * ch + 2 * i], part[hh]);
-          part[hh] = fmaf(hi, qp[hh * KD + 16 * ch + 2 * i + 1], part[hh]);
-        }
-      }
-#pragma unroll
-      for (int hh = 0; hh < QH; ++hh) {
-        part[hh] += __shfl_xor(part[hh], 1);
-        part[hh] += __shfl_xor(part[hh], 2);
-        part[hh] += __shfl_xor(part[hh], 4);
-      }
-      if (ch == 0) {
-#pragma unroll
-        for (int hh = 0; hh < QH; ++hh) qs[hh * KD + row] = part[hh];
+      for (int c = 0; c < 4; ++c) {
+        const float4 v = qv[c];
+        part[hh] = fmaf(h2f(sw[2 * c] & 0xFFFFu), v.x, part[hh]);
+        part[hh] = fmaf(h2f(sw[2 * c] >> 16), v.y, part[hh]);
+        part[hh] = fmaf(h2f(sw[2 * c + 1] & 0xFFFFu), v.z, part[hh]);
+        part[hh] = fmaf(h2f(sw[2 * c + 1] >> 16), v.w, part[hh]);
       }
     }
-    __syncthreads();
+#pragma unroll
+    for (int hh = 0; hh < QH; ++hh) {
+      part[hh] = sum8(part[hh]);
+      if (sch == 0) qs[hh * KD + srow] = part[hh];
+      const float m = wave_max_of_eights(fabsf(part[hh]));
+      if (lane == 0) atomicMax(&amax[QH + hh], __float_as_int(m));
+    }
   }
-  // per-head, per-class magnitude bound -> power-of-two table scale
-  for (int i = tid; i < QH * KD; i += NT) {
-    const int hh = i / KD, j = i % KD;
-    int cls = 0;
-    float v = fabsf(qp[i]);
-    if (F::GROUPED) cls = j / F::PD;
-    atomicMax(&amax[cls * QH + hh], __float_as_int(v));
-    if (F::PROD) atomicMax(&amax[QH + hh], __float_as_int(fabsf(qs[i])));
-  }
-  __syncthreads();
-  if (tid < 2 * QH) {
-    const int cls = tid / QH;
-    const int part = F::GROUPED ? cls : 0;
+  // Each wave's first tile goes out now; the table building covers its latency.
+  if (scorer) load_keys(tile_tb(0), kd);
+  else load_codes(tile_tb(0), codes);
+  if constexpr (F::PROD) __syncthreads();
+  // per-head, per-class power-of-two table scale: the largest possible entry
+  // (|q'| bound x largest centroid x coordinates per byte) stays <= 16384
+  auto table_scale = [&](int cls, int hh) {
     float cmax = 1.0f;
     int cpb = 8;
     if (!(F::PROD && cls == 1)) {
-      const int L = H->part_levels[part];
-      cmax = fabsf(((const float*)(a.tables + H->off_centroids[part]))[L - 1]);
+      cmax = fabsf(cls ? cent1[lev1 - 1] : cent0[lev0 - 1]);
       cpb = cls == 0 ? F::CPB0 : F::CPB1;
     }
-    const float bound = __int_as_float(amax[tid]) * cmax * cpb;
-    scl[tid] = bound > 0.0f ? exp2f(floorf(log2f(16384.0f / bound))) : 1.0f;
+    return pow2_scale(__int_as_float(amax[cls * QH + hh]) * cmax * cpb);
+  };
+  // per-token multipliers of the two table classes, with the scales undone:
+  // hmul[0][h] multiplies the norm, hmul[1][h] the residual norm (PROD) or
+  // the second half's norm (GROUPED).  Kept in LDS, read where used.
+  if (tid < QH) {
+    hmul[tid] = 1.0f / (table_scale(0, tid) * (float)F::PD);
+    hmul[QH + tid] = F::PROD ? 1.2533141373155003f / ((float)KD * sqrtf((float)KD) * table_scale(1, tid))
+                             : 1.0f / (table_scale(1, tid) * (float)F::PD);
   }
-  __syncthreads();
   // Half tables: for each byte position, class, nibble half and nibble value,
   // the four heads' partial sums over the coordinates (or sign rows) that
   // nibble holds, already scaled.  A byte's entry is then lo[v & 15] +
@@ -350,53 +413,51 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
     const int pos = i >> 5, half = (i >> 4) & 1, n = i & 15;
     const bool c1 = pos >= F::P0;
     const int p = c1 ? pos - F::P0 : pos;
-    float s[QH] = {0.0f, 0.0f, 0.0f, 0.0f};
+    float sv[QH] = {0.0f, 0.0f, 0.0f, 0.0f};
     if (c1 && F::PROD) {
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const float sg = ((n >> k) & 1) ? 1.0f : -1.0f;
 #pragma unroll
-        for (int hh = 0; hh < QH; ++hh) s[hh] = fmaf(sg, qs[hh * KD + 8 * p + 4 * half + k], s[hh]);
+        for (int hh = 0; hh < QH; ++hh) sv[hh] = fmaf(sg, qs[hh * KD + 8 * p + 4 * half + k], sv[hh]);
       }
     } else {
-      const int part = c1 ? 1 : 0;
       const int W = c1 ? F::W1 : F::W0;
       const int per = 4 / W;  // coordinates per nibble
-      const int bits = H->part_bits[F::GROUPED ? part : 0];
-      const int fmask = (1 << bits) - 1;
-      const float* cent = cen + 16 * (F::GROUPED ? part : 0);
-      const int j0 = part * F::PD + p * (8 / W) + half * per;
+      const int fmask = (1 << (c1 ? B1 : B0)) - 1;
+      const float* cn = cen + (c1 ? 16 : 0);
+      const int j0 = (c1 ? F::PD : 0) + p * (8 / W) + half * per;
       for (int k = 0; k < per; ++k) {
-        const float c = cent[(n >> (W * k)) & fmask];
+        const float c = cn[(n >> (W * k)) & fmask];
 #pragma unroll
-        for (int hh = 0; hh < QH; ++hh) s[hh] = fmaf(c, qp[hh * KD + j0 + k], s[hh]);
+        for (int hh = 0; hh < QH; ++hh) sv[hh] = fmaf(c, qp[hh * KD + j0 + k], sv[hh]);
       }
     }
-    const float* sc = scl + (c1 ? QH : 0);
-    halves[i] = make_float4(s[0] * sc[0], s[1] * sc[1], s[2] * sc[2], s[3] * sc[3]);
+    const int cls = c1 ? 1 : 0;
+    halves[i] = make_float4(sv[0] * table_scale(cls, 0), sv[1] * table_scale(cls, 1),
+                            sv[2] * table_scale(cls, 2), sv[3] * table_scale(cls, 3));
   }
   __syncthreads();
-  for (int e = tid; e < F::E0 + F::E1; e += NT) {
-    const bool c1 = e >= F::E0;
-    const int ee = c1 ? e - F::E0 : e;
+  // One thread per (position, low nibble) walks the high nibbles: its low
+  // half stays in registers, the high halves are read by sixteen lanes at once.
+  for (int t = tid; t < (F::P0 + F::P1) * 16; t += NT) {
+    const int pos = t >> 4, lo = t & 15;
+    const bool c1 = pos >= F::P0;
     const int S = c1 ? F::S1 : F::S0;
-    const int pos = (c1 ? F::P0 : 0) + ee / S, v = ee % S;
-    const float4 lo4 = halves[pos * 32 + (v & 15)], hi4 = halves[pos * 32 + 16 + (v >> 4)];
-    const uint32_t lo = (uint32_t)__half_as_ushort(__float2half_rn(lo4.x + hi4.x)) |
-                        ((uint32_t)__half_as_ushort(__float2half_rn(lo4.y + hi4.y)) << 16);
-    const uint32_t hi = (uint32_t)__half_as_ushort(__float2half_rn(lo4.z + hi4.z)) |
-                        ((uint32_t)__half_as_ushort(__float2half_rn(lo4.w + hi4.w)) << 16);
-    lut[e] = make_uint2(lo, hi);
-  }
-  __syncthreads();
-
-  // per-token multipliers of the two table classes, with the scales undone:
-  // hmul[0][h] multiplies the norm, hmul[1][h] the residual norm (PROD) or
-  // the second half's norm (GROUPED).  Kept in LDS, read where used.
-  if (tid < QH) {
-    hmul[tid] = 1.0f / (scl[tid] * (float)F::PD);
-    hmul[QH + tid] = F::PROD ? 1.2533141373155003f / ((float)KD * sqrtf((float)KD) * scl[QH + tid])
-                             : 1.0f / (scl[QH + tid] * (float)F::PD);
+    uint2* dst = lut + (c1 ? F::E0 + (pos - F::P0) * F::S1 : pos * F::S0);
+    const float4 lo4 = halves[pos * 32 + lo];
+#pragma unroll 4
+    for (int hi = 0; hi < 16; ++hi) {
+      const int v = hi * 16 + lo;
+      if (v < S) {
+        const float4 hi4 = halves[pos * 32 + 16 + hi];
+        const uint32_t e01 = (uint32_t)__half_as_ushort(__float2half_rn(lo4.x + hi4.x)) |
+                             ((uint32_t)__half_as_ushort(__float2half_rn(lo4.y + hi4.y)) << 16);
+        const uint32_t e23 = (uint32_t)__half_as_ushort(__float2half_rn(lo4.z + hi4.z)) |
+                             ((uint32_t)__half_as_ushort(__float2half_rn(lo4.w + hi4.w)) << 16);
+        dst[v] = make_uint2(e01, e23);
+      }
+    }
   }
   __syncthreads();
   const float xscale = a.sm_scale * LOG2E;
@@ -416,7 +477,9 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
 #pragma unroll
       for (int k = 0; k < 4; ++k) zacc[hh][k] = 0.0f;
     }
-    for (int r = 0; r <= rounds; ++r) {
+    // two key buffers in turn: a round scores one while the next tile's
+    // bytes arrive in the other
+    auto s_round = [&](int r, KeyData& kd) {
       const int tb = tile_tb(r);
       if (r < rounds && tb < t_end) {
         // ---------------- scores: lane = token
@@ -487,7 +550,6 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
           }
         }
         const uint2 zv = kd.zv, sv = kd.sv;
-        // the next tile of this wave, one round ahead
         load_keys(tile_tb(r + 1), kd);
         float zz[4], ss[4];
         zz[0] = h2f(zv.x & 0xFFFFu); zz[1] = h2f(zv.x >> 16);
@@ -516,6 +578,9 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
           for (int hh = 0; hh < QH; ++hh) abuf[((r & 1) * NS + pw) * QH + hh] = alpha[hh];
         }
       }
+    };
+    for (int r = 0; r <= rounds; ++r) {
+      s_round(r, kd);
       __syncthreads();
     }
 #pragma unroll
