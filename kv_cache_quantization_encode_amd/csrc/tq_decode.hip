@@ -187,6 +187,14 @@ __device__ inline float max8(float v) {
   return fmaxf(v, dpp<DPP_HALF_MIRROR>(v));
 }
 
+// Workgroup barrier for LDS hand-offs: waits for this wave's LDS accesses
+// only, so global loads already in flight (the next tile) stay in flight.
+__device__ inline void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // A value every lane holds alike, moved to a scalar register.
 __device__ inline float uniform(float v) { return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v))); }
 
@@ -219,7 +227,8 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
   float* hmul = L.hmul;     // [2][QH] score multipliers
 
   const tq_blob_header* H = (const tq_blob_header*)a.tables;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: branches on it are scalar
   const int split = blockIdx.x, quad = blockIdx.y, bh = blockIdx.z;
   const int b = bh / a.Hkv, hkv = bh % a.Hkv;
   const int ctx = a.ctx_len[b];
@@ -384,7 +393,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
   // Each wave's first tile goes out now; the table building covers its latency.
   if (scorer) load_keys(tile_tb(0), kd);
   else load_codes(tile_tb(0), codes);
-  if constexpr (F::PROD) __syncthreads();
+  if constexpr (F::PROD) lds_barrier();
   // per-head, per-class power-of-two table scale: the largest possible entry
   // (|q'| bound x largest centroid x coordinates per byte) stays <= 16384
   auto table_scale = [&](int cls, int hh) {
@@ -437,7 +446,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
     halves[i] = make_float4(sv[0] * table_scale(cls, 0), sv[1] * table_scale(cls, 1),
                             sv[2] * table_scale(cls, 2), sv[3] * table_scale(cls, 3));
   }
-  __syncthreads();
+  lds_barrier();
   // One thread per (position, low nibble) walks the high nibbles: its low
   // half stays in registers, the high halves are read by sixteen lanes at once.
   for (int t = tid; t < (F::P0 + F::P1) * 16; t += NT) {
@@ -459,7 +468,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
       }
     }
   }
-  __syncthreads();
+  lds_barrier();
   const float xscale = a.sm_scale * LOG2E;
 
   const half2_t e10 = {(_Float16)1.0f, (_Float16)0.0f}, e01 = {(_Float16)0.0f, (_Float16)1.0f};
@@ -581,7 +590,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
     };
     for (int r = 0; r <= rounds; ++r) {
       s_round(r, kd);
-      __syncthreads();
+      lds_barrier();
     }
 #pragma unroll
     for (int hh = 0; hh < QH; ++hh) {
@@ -656,10 +665,10 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
     };
     for (int r = 0; r <= rounds; r += 2) {
       pv_round(r, codes2, codes);
-      __syncthreads();
+      lds_barrier();
       if (r + 1 <= rounds) {
         pv_round(r + 1, codes, codes2);
-        __syncthreads();
+        lds_barrier();
       }
     }
     // undo the subnormal placement: dim i of a slice carries code * 2^-24 * step_i
