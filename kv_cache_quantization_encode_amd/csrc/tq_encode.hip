@@ -77,6 +77,54 @@ __device__ inline void load8(const void* base, long long elem_off, float* out) {
   }
 }
 
+// The 32 coordinates a lane loads of one key, as loaded (16-bit types: four
+// uint4; float32: eight), so that the next tile can be in flight while the
+// current one is encoded.
+template <int DT>
+struct RawKey {
+  static constexpr int N = DT == TQ_F32 ? 8 : 4;
+  uint4 v[N];
+};
+
+template <int DT>
+__device__ inline void load_raw(const void* base, long long row_off, int g, RawKey<DT>& r) {
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    if constexpr (DT == TQ_F32) {
+      const uint4* p = (const uint4*)((const float*)base + row_off + 32 * c + 8 * g);
+      r.v[2 * c] = p[0];
+      r.v[2 * c + 1] = p[1];
+    } else {
+      r.v[c] = *(const uint4*)((const uint16_t*)base + row_off + 32 * c + 8 * g);
+    }
+  }
+}
+
+template <int DT>
+__device__ inline void unpack_raw(const RawKey<DT>& r, float* x) {
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    if constexpr (DT == TQ_F32) {
+      const uint32_t w[8] = {r.v[2 * c].x, r.v[2 * c].y, r.v[2 * c].z, r.v[2 * c].w,
+                             r.v[2 * c + 1].x, r.v[2 * c + 1].y, r.v[2 * c + 1].z, r.v[2 * c + 1].w};
+#pragma unroll
+      for (int k = 0; k < 8; ++k) x[8 * c + k] = __uint_as_float(w[k]);
+    } else {
+      const uint32_t w[4] = {r.v[c].x, r.v[c].y, r.v[c].z, r.v[c].w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        if constexpr (DT == TQ_BF16) {
+          x[8 * c + 2 * k] = __uint_as_float(w[k] << 16);
+          x[8 * c + 2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
+        } else {
+          x[8 * c + 2 * k] = __half2float(__ushort_as_half((unsigned short)(w[k] & 0xFFFFu)));
+          x[8 * c + 2 * k + 1] = __half2float(__ushort_as_half((unsigned short)(w[k] >> 16)));
+        }
+      }
+    }
+  }
+}
+
 __device__ inline float xor_sum(float v, int m) { return v + __shfl_xor(v, m); }
 
 // In-lane butterflies on register bit `bit` (stride s = 1 << bit).
@@ -123,8 +171,8 @@ __device__ inline void stage_cross32(float* x) {
 __device__ inline int bucketize(float y, const tq_hint* hint, int hn, float lo, float scale) {
   float f = floorf((y - lo) * scale);
   f = fminf(fmaxf(f, 0.0f), (float)(hn - 1));  // NaN -> 0 (fmax returns the number)
-  const tq_hint h = hint[(int)f];
-  return h.h + (y >= h.t_h ? 1 : 0) + (y >= h.t_h1 ? 1 : 0);
+  const tq_hint* h = hint + (int)f;
+  return h->h + (y >= h->t_h ? 1 : 0) + (y >= h->t_h1 ? 1 : 0);
 }
 
 // Pack 32 indices of width W (coordinates 32g .. 32g+31 of one part) and
@@ -153,70 +201,92 @@ __device__ inline void store_idx(int w, uint8_t* dst, const int* q) {
 
 // MODE: TQ_MODE_MSE / PROD / GROUPED.  DT: input dtype.
 template <int MODE, int DT>
-__global__ __launch_bounds__(WAVES * 64) void encode_keys_kernel(KeyArgs a) {
+__global__ __launch_bounds__(WAVES * 64, 2) void encode_keys_kernel(KeyArgs a) {
   const tq_blob_header* H = (const tq_blob_header*)a.tables;
   constexpr int NP = MODE == TQ_MODE_GROUPED ? 2 : 1;
   __shared__ tq_hint s_hint[NP][TQ_MAX_HINT];
   __shared__ float s_cent[MAX_LEVELS];
+  constexpr int SPITCH = KD + 8;  // halves per padded row of S
+  __shared__ __align__(16) _Float16 s_S[MODE == TQ_MODE_PROD ? KD * SPITCH : 8];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int g = lane >> 4;     // lane group: quarter of the key
   const int kk = lane & 15;    // key within the tile
 
+  // Rows past n_vec load the last row (kept in bounds) and encode zeros.
+  const int tile_step = gridDim.x * WAVES;
+  auto row_of = [&](int tile) {
+    const long long row = (long long)tile * TILE_KEYS + kk;
+    return row < a.n_vec ? row : a.n_vec - 1;
+  };
+  // This wave's first tile goes out before the tables are staged.
+  RawKey<DT> raw, raw_next;
+  int tile = blockIdx.x * WAVES + wave;
+  if (tile < a.n_tiles) load_raw<DT>(a.keys, row_of(tile) * a.row_stride, g, raw);
+
+  // Formats with at most four cells (1- and 2-bit indices, one part) compare
+  // against the boundaries directly (the bounds array pads with +inf); the
+  // others look up a hint grid in LDS.
+  const bool direct = NP == 1 && H->part_levels[0] <= 4;
+  const float* bnd = (const float*)(a.tables + H->off_bounds[0]);
+  const float bt0 = bnd[0], bt1 = bnd[1], bt2 = bnd[2];
+  // sigma of the coordinates loaded into x[r]: 32 (r >> 3) + 8 g + (r & 7)
+  float4 sg[8];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int j = 32 * c + 8 * g;
+    const int part = MODE == TQ_MODE_GROUPED ? j / (KD / 2) : 0;
+    const float4* sp = (const float4*)((const float*)(a.tables + H->off_sigma[part]) + (j - part * (KD / 2)));
+    sg[2 * c] = sp[0];
+    sg[2 * c + 1] = sp[1];
+  }
   int hn[NP];
   float hlo[NP], hsc[NP];
   for (int p = 0; p < NP; ++p) {
     hn[p] = H->hint_n[p];
     hlo[p] = H->hint_lo[p];
     hsc[p] = H->hint_scale[p];
-    const tq_hint* src = (const tq_hint*)(a.tables + H->off_hint[p]);
-    for (int i = threadIdx.x; i < hn[p]; i += blockDim.x) s_hint[p][i] = src[i];
+    if (!direct) {
+      const tq_hint* src = (const tq_hint*)(a.tables + H->off_hint[p]);
+      for (int i = threadIdx.x; i < hn[p]; i += blockDim.x) s_hint[p][i] = src[i];
+    }
   }
   if (MODE == TQ_MODE_PROD) {
     const float* c = (const float*)(a.tables + H->off_centroids[0]);
     for (int i = threadIdx.x; i < H->part_levels[0]; i += blockDim.x) s_cent[i] = c[i];
+    // S in LDS, rows padded to 136 halves so that the sixteen rows one MFMA
+    // fragment read touches fall in distinct banks.  Fragment (nt, ks) of lane
+    // (kk, g): row 16 nt + kk, coordinates 32 g + 8 ks .. + 7, matching the
+    // B = R^T layout after the transform.
+    const uint4* S = (const uint4*)(a.tables + H->off_S);
+    for (int i = threadIdx.x; i < KD * KD / 8; i += blockDim.x)
+      *(uint4*)(s_S + (i / (KD / 8)) * SPITCH + 8 * (i % (KD / 8))) = S[i];
   }
-  __syncthreads();
-
   // sign mask: bit r set when sigma of the coordinate loaded into x[r] is -1
   uint32_t sigmask = 0;
+#pragma unroll
   for (int r = 0; r < 32; ++r) {
-    const int j = 32 * (r >> 3) + 8 * g + (r & 7);
-    float s;
-    if (MODE == TQ_MODE_GROUPED) {
-      const int part = j >= KD / 2;
-      s = ((const float*)(a.tables + H->off_sigma[part]))[j - part * (KD / 2)];
-    } else {
-      s = ((const float*)(a.tables + H->off_sigma[0]))[j];
-    }
-    if (s < 0) sigmask |= 1u << r;
+    const float4 v = sg[r >> 2];
+    const float sv = (r & 3) == 0 ? v.x : (r & 3) == 1 ? v.y : (r & 3) == 2 ? v.z : v.w;
+    if (sv < 0) sigmask |= 1u << r;
   }
-
-  // S fragments for A = S (16 rows per tile nt, k = coordinates
-  // 32*(l>>4) + 8*ks + i, matching the B = R^T layout after the transform).
-  half8 sfrag[MODE == TQ_MODE_PROD ? 8 : 1][4];
-  if constexpr (MODE == TQ_MODE_PROD) {
-    const uint16_t* S = (const uint16_t*)(a.tables + H->off_S);
-#pragma unroll
-    for (int nt = 0; nt < 8; ++nt)
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        sfrag[nt][ks] = *(const half8*)(S + (size_t)(16 * nt + kk) * KD + 32 * g + 8 * ks);
-  }
+  __syncthreads();
 
   const float inv_sqrt_d = 1.0f / sqrtf((float)KD);
   const int w0 = index_width_dev(H->part_bits[0]);
   const int w1 = NP == 2 ? index_width_dev(H->part_bits[1]) : 0;
 
-  for (int tile = blockIdx.x * WAVES + wave; tile < a.n_tiles; tile += gridDim.x * WAVES) {
+  for (; tile < a.n_tiles; tile += tile_step) {
+    // the next tile of this wave is requested before this one is encoded
+    if (tile + tile_step < a.n_tiles) load_raw<DT>(a.keys, row_of(tile + tile_step) * a.row_stride, g, raw_next);
     const long long row = (long long)tile * TILE_KEYS + kk;
     const bool valid = row < a.n_vec;
+    const long long slot = a.slots ? a.slots[row_of(tile)] : row;
     float x[32];
-    if (valid) {
-#pragma unroll
-      for (int c = 0; c < 4; ++c) load8<DT>(a.keys, row * a.row_stride + 32 * c + 8 * g, x + 8 * c);
-    } else {
+    unpack_raw<DT>(raw, x);
+    raw = raw_next;
+    if (!valid) {
 #pragma unroll
       for (int r = 0; r < 32; ++r) x[r] = 0.0f;
     }
@@ -253,18 +323,28 @@ __global__ __launch_bounds__(WAVES * 64) void encode_keys_kernel(KeyArgs a) {
     const float n = n_part[part];
     const float inv = n > 0.0f ? 1.0f / n : 0.0f;
     int q[32];
-    const tq_hint* hint = s_hint[NP == 2 ? part : 0];
-    const int hnn = NP == 2 ? hn[part] : hn[0];
-    const float hl = NP == 2 ? hlo[part] : hlo[0];
-    const float hs = NP == 2 ? hsc[part] : hsc[0];
+    if (direct) {
+      // at most four cells: count the boundaries at or below y
 #pragma unroll
-    for (int r = 0; r < 32; ++r) {
-      x[r] *= inv;
-      q[r] = bucketize(x[r], hint, hnn, hl, hs);
+      for (int r = 0; r < 32; ++r) {
+        x[r] *= inv;
+        q[r] = (x[r] >= bt0 ? 1 : 0) + (x[r] >= bt1 ? 1 : 0) + (x[r] >= bt2 ? 1 : 0);
+      }
+    } else {
+      const tq_hint* hint = s_hint[NP == 2 ? part : 0];
+      const int hnn = NP == 2 ? hn[part] : hn[0];
+      const float hl = NP == 2 ? hlo[part] : hlo[0];
+      const float hs = NP == 2 ? hsc[part] : hsc[0];
+#pragma unroll
+      for (int r = 0; r < 32; ++r) {
+        // eight hint reads in flight at a time (each holds three registers)
+        if (r % 8 == 0) __builtin_amdgcn_sched_barrier(0);
+        x[r] *= inv;
+        q[r] = bucketize(x[r], hint, hnn, hl, hs);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
 
-    long long slot = row;
-    if (a.slots && valid) slot = a.slots[row];
     const bool store = valid && slot >= 0 && slot < a.n_records;
 
     if (store) {
@@ -297,14 +377,19 @@ __global__ __launch_bounds__(WAVES * 64) void encode_keys_kernel(KeyArgs a) {
         blo[r >> 3][r & 7] = lo;
       }
       rr = xor_sum(xor_sum(rr, 16), 32);
+      // The fragment base is made opaque to the compiler each tile, so that it
+      // reads S from LDS per use instead of keeping all 32 fragments live.
+      const _Float16* sbase = s_S + kk * SPITCH + 32 * g;
+      asm volatile("" : "+v"(sbase));
       floatx4 acc[8];
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt) {
         acc[nt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-          acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(sfrag[nt][ks], blo[ks], acc[nt], 0, 0, 0);
-          acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(sfrag[nt][ks], bhi[ks], acc[nt], 0, 0, 0);
+          const half8 sf = *(const half8*)(sbase + (16 * nt) * SPITCH + 8 * ks);
+          acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(sf, blo[ks], acc[nt], 0, 0, 0);
+          acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(sf, bhi[ks], acc[nt], 0, 0, 0);
         }
       }
       // lane holds projections of key kk onto S rows 16nt + 4g + i
@@ -335,9 +420,9 @@ __global__ __launch_bounds__(WAVES * 64) void encode_keys_kernel(KeyArgs a) {
 }
 
 // ---------------------------------------------------------------- values
-// Lane l handles 8 consecutive channels of row (4 * wave_tile + l / 16); the
-// four lanes of one 32-channel group agree on min and max through two xor
-// shuffles.
+// A wave encodes 16 rows per tile, four at a time: lane l handles 8
+// consecutive channels of row 16 tile + 4 j + l / 16; the four lanes of one
+// 32-channel group agree on min and max through two xor shuffles.
 struct ValArgs {
   const void* values;
   long long n_vec;
@@ -357,51 +442,79 @@ __global__ __launch_bounds__(256) void encode_values_kernel(ValArgs a) {
   const long long tiles_per_grid = (long long)gridDim.x * (blockDim.x >> 6);
   for (long long tile = (long long)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
        tile < a.n_tiles; tile += tiles_per_grid) {
-    const long long row = tile * 4 + (lane >> 4);
-    const bool valid = row < a.n_vec;
-    float v[8];
-    if (valid) {
-      load8<DT>(a.values, row * a.row_stride + 8 * sub, v);
-    } else {
+    // sixteen rows per wave: all four loads go out before any is used
+    float vv[4][8];
+    long long slots[4];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = 0.0f;
+    for (int j = 0; j < 4; ++j) {
+      const long long row = tile * 16 + 4 * j + (lane >> 4);
+      const long long rr = row < a.n_vec ? row : a.n_vec - 1;
+      load8<DT>(a.values, rr * a.row_stride + 8 * sub, vv[j]);
+      slots[j] = a.slots ? a.slots[rr] : row;
     }
-    float mn = v[0], mx = v[0];
 #pragma unroll
-    for (int i = 1; i < 8; ++i) {
-      mn = fminf(mn, v[i]);
-      mx = fmaxf(mx, v[i]);
-    }
-    mn = fminf(mn, __shfl_xor(mn, 1));
-    mx = fmaxf(mx, __shfl_xor(mx, 1));
-    mn = fminf(mn, __shfl_xor(mn, 2));
-    mx = fmaxf(mx, __shfl_xor(mx, 2));
-    constexpr float LEVELS = (float)((1 << BITS) - 1);
-    const float s32 = __fdiv_rn(__fsub_rn(mx, mn), LEVELS);
-    const __half s16 = __float2half_rn(s32);
-    const __half z16 = __float2half_rn(mn);
-    const float s = __half2float(s16), z = __half2float(z16);
-    uint32_t packed = 0;
+    for (int j = 0; j < 4; ++j) {
+      const long long row = tile * 16 + 4 * j + (lane >> 4);
+      const bool valid = row < a.n_vec;
+      float v[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      float c = 0.0f;
+      for (int i = 0; i < 8; ++i) v[i] = valid ? vv[j][i] : 0.0f;
+      float mn = v[0], mx = v[0];
+#pragma unroll
+      for (int i = 1; i < 8; ++i) {
+        mn = fminf(mn, v[i]);
+        mx = fmaxf(mx, v[i]);
+      }
+      mn = fminf(mn, __shfl_xor(mn, 1));
+      mx = fmaxf(mx, __shfl_xor(mx, 1));
+      mn = fminf(mn, __shfl_xor(mn, 2));
+      mx = fmaxf(mx, __shfl_xor(mx, 2));
+      constexpr float LEVELS = (float)((1 << BITS) - 1);
+      const float s32 = __fdiv_rn(__fsub_rn(mx, mn), LEVELS);
+      const __half s16 = __float2half_rn(s32);
+      const __half z16 = __float2half_rn(mn);
+      const float s = __half2float(s16), z = __half2float(z16);
+      // code = rint((v - z) / s) with the correctly rounded quotient.  x * rcp(s)
+      // lies within 2^-22 |q| of the exact quotient, and so does the rounded
+      // one.  Quotients that matter lie in [-1, 2^BITS], so unless q is within
+      // 1e-5 of a half-integer both round to the same code; a lane with such a
+      // q redoes its eight codes with full divisions.
+      const float rs = __builtin_amdgcn_rcpf(s);
+      float c[8], x[8];
+      bool near = false;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        x[i] = __fsub_rn(v[i], z);
+        const float q = x[i] * rs;
+        c[i] = rintf(q);
+        near |= fabsf(q - c[i]) > 0.5f - 1e-5f;
+      }
+      if (near) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) c[i] = rintf(__fdiv_rn(x[i], s));
+      }
+      uint32_t packed = 0;
       if (s != 0.0f) {
-        c = rintf(__fdiv_rn(__fsub_rn(v[i], z), s));
-        c = fminf(fmaxf(c, 0.0f), LEVELS);
+        // codes packed in float arithmetic: c 2^(BITS i) is exact below 2^24
+        float lo = 0.0f, hi = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          lo = fmaf(__builtin_amdgcn_fmed3f(c[i], 0.0f, LEVELS), (float)(1u << (BITS * i)), lo);
+          hi = fmaf(__builtin_amdgcn_fmed3f(c[4 + i], 0.0f, LEVELS), (float)(1u << (BITS * i)), hi);
+        }
+        packed = (uint32_t)lo | ((uint32_t)hi << (4 * BITS));
       }
-      packed |= (uint32_t)c << (BITS * i);
-    }
-    long long slot = row;
-    if (a.slots && valid) slot = a.slots[row];
-    if (valid && slot >= 0 && slot < a.n_records) {
-      if (BITS == 2) {
-        *(uint16_t*)(a.codes + slot * (KD * BITS / 8) + 2 * sub) = (uint16_t)packed;
-      } else {
-        *(uint32_t*)(a.codes + slot * (KD * BITS / 8) + 4 * sub) = packed;
-      }
-      if ((sub & 3) == 0) {
-        a.scale[slot * (KD / 32) + (sub >> 2)] = __half_as_ushort(s16);
-        a.zero[slot * (KD / 32) + (sub >> 2)] = __half_as_ushort(z16);
+      const long long slot = slots[j];
+      if (valid && slot >= 0 && slot < a.n_records) {
+        if (BITS == 2) {
+          *(uint16_t*)(a.codes + slot * (KD * BITS / 8) + 2 * sub) = (uint16_t)packed;
+        } else {
+          *(uint32_t*)(a.codes + slot * (KD * BITS / 8) + 4 * sub) = packed;
+        }
+        if ((sub & 3) == 0) {
+          a.scale[slot * (KD / 32) + (sub >> 2)] = __half_as_ushort(s16);
+          a.zero[slot * (KD / 32) + (sub >> 2)] = __half_as_ushort(z16);
+        }
       }
     }
   }
@@ -494,7 +607,7 @@ extern "C" tq_status tq_encode_values(int32_t bits, int32_t group, int32_t d, co
   a.codes = codes;
   a.scale = scale;
   a.zero = zero;
-  a.n_tiles = (n_vec + 3) / 4;
+  a.n_tiles = (n_vec + 15) / 16;
   const dim3 grid(grid_for(a.n_tiles, 4)), block(256);
   hipStream_t s = (hipStream_t)stream;
 #define TQ_LAUNCH_VALS(B)                                                                   \
