@@ -204,7 +204,7 @@ template <int MODE, int DT>
 __global__ __launch_bounds__(WAVES * 64, 2) void encode_keys_kernel(KeyArgs a) {
   const tq_blob_header* H = (const tq_blob_header*)a.tables;
   constexpr int NP = MODE == TQ_MODE_GROUPED ? 2 : 1;
-  __shared__ tq_hint s_hint[NP][TQ_MAX_HINT];
+  __shared__ __align__(16) tq_hint s_hint[NP][TQ_MAX_HINT];
   __shared__ float s_cent[MAX_LEVELS];
   constexpr int SPITCH = KD + 8;  // halves per padded row of S
   __shared__ __align__(16) _Float16 s_S[MODE == TQ_MODE_PROD ? KD * SPITCH : 8];
@@ -248,8 +248,19 @@ __global__ __launch_bounds__(WAVES * 64, 2) void encode_keys_kernel(KeyArgs a) {
     hlo[p] = H->hint_lo[p];
     hsc[p] = H->hint_scale[p];
     if (!direct) {
-      const tq_hint* src = (const tq_hint*)(a.tables + H->off_hint[p]);
-      for (int i = threadIdx.x; i < hn[p]; i += blockDim.x) s_hint[p][i] = src[i];
+      const uint4* src = (const uint4*)(a.tables + H->off_hint[p]);
+      constexpr int PER_THREAD = TQ_MAX_HINT / (WAVES * 64);
+      uint4 hv[PER_THREAD];
+#pragma unroll
+      for (int k = 0; k < PER_THREAD; ++k) {
+        const int i = threadIdx.x + k * WAVES * 64;
+        if (i < hn[p]) hv[k] = src[i];
+      }
+#pragma unroll
+      for (int k = 0; k < PER_THREAD; ++k) {
+        const int i = threadIdx.x + k * WAVES * 64;
+        if (i < hn[p]) *(uint4*)&s_hint[p][i] = hv[k];
+      }
     }
   }
   if (MODE == TQ_MODE_PROD) {
@@ -259,9 +270,17 @@ __global__ __launch_bounds__(WAVES * 64, 2) void encode_keys_kernel(KeyArgs a) {
     // fragment read touches fall in distinct banks.  Fragment (nt, ks) of lane
     // (kk, g): row 16 nt + kk, coordinates 32 g + 8 ks .. + 7, matching the
     // B = R^T layout after the transform.
+    // (all of a thread's reads are issued before its LDS writes)
     const uint4* S = (const uint4*)(a.tables + H->off_S);
-    for (int i = threadIdx.x; i < KD * KD / 8; i += blockDim.x)
-      *(uint4*)(s_S + (i / (KD / 8)) * SPITCH + 8 * (i % (KD / 8))) = S[i];
+    constexpr int PER_THREAD = KD * KD / 8 / (WAVES * 64);
+    uint4 srow[PER_THREAD];
+#pragma unroll
+    for (int k = 0; k < PER_THREAD; ++k) srow[k] = S[threadIdx.x + k * WAVES * 64];
+#pragma unroll
+    for (int k = 0; k < PER_THREAD; ++k) {
+      const int i = threadIdx.x + k * WAVES * 64;
+      *(uint4*)(s_S + (i / (KD / 8)) * SPITCH + 8 * (i % (KD / 8))) = srow[k];
+    }
   }
   // sign mask: bit r set when sigma of the coordinate loaded into x[r] is -1
   uint32_t sigmask = 0;
