@@ -187,6 +187,37 @@ tq_status tq_decode_attention(const tq_key_config* cfg, const void* tables,
                               float sm_scale, float* out, float* lse, float* scores,
                               void* workspace, size_t* workspace_bytes, void* stream);
 
+/*
+ * tq_decode_attention_paged -- tq_decode_attention over a paged cache: the
+ * compressed store appends fixed-size chunks of tokens, each chunk a page of
+ * the planes (bit-packing article sec 五: the store appends packed chunks).
+ * Page p holds page_size consecutive tokens of every KV head: the record of
+ * token t of (sequence b, KV head h) is
+ *     (block_table[b][t / page_size] * Hkv + h) * page_size + t % page_size,
+ * which is also the slot tq_encode_keys / tq_encode_values write it to.
+ *   block_table         int32 [B][max_blocks_per_seq] device array; entries
+ *                       for pages below ctx_len[b] must name pages that exist
+ *                       in the planes (not checked on the device).
+ *   page_size           tokens per page, a positive multiple of 64.
+ *   scores              (nullable) [B][Hq][max_blocks_per_seq * page_size].
+ * Every other argument, the workspace query and the errors are those of
+ * tq_decode_attention with max_ctx = max_blocks_per_seq * page_size; a bad
+ * page_size or max_blocks_per_seq returns TQ_ERR_ARG.  Results equal those of
+ * tq_decode_attention on the same tokens laid out contiguously, bit for bit.
+ */
+tq_status tq_decode_attention_paged(const tq_key_config* cfg, const void* tables,
+                                    const void* q, int32_t q_dtype, int32_t B, int32_t Hq,
+                                    int32_t Hkv, const int32_t* ctx_len,
+                                    const int32_t* block_table, int32_t max_blocks_per_seq,
+                                    int32_t page_size,
+                                    const uint8_t* idx, const uint8_t* signs,
+                                    const uint16_t* norm, const uint16_t* rnorm,
+                                    int32_t v_bits, int32_t v_group,
+                                    const uint8_t* v_codes, const uint16_t* v_scale,
+                                    const uint16_t* v_zero,
+                                    float sm_scale, float* out, float* lse, float* scores,
+                                    void* workspace, size_t* workspace_bytes, void* stream);
+
 /* Static description of a status code (never NULL). */
 const char* tq_status_string(int32_t status);
 

@@ -9,6 +9,12 @@ from __future__ import annotations
 import ctypes
 import os
 
+# torch ships its own HIP runtime.  Importing it first makes libtq.so bind to
+# that same runtime (libtq's libamdhip64.so.7 dependency is then already
+# loaded), so torch's device memory and stream handles are valid in libtq's
+# calls; loading libtq.so first would bring in a second HIP runtime.
+import torch  # noqa: F401
+
 HERE = os.path.dirname(os.path.abspath(__file__))
 # TQ_LIBRARY may name another build of libtq.so (for A/B timing of build options)
 LIB_PATH = os.environ.get("TQ_LIBRARY") or os.path.join(HERE, "libtq.so")
@@ -19,7 +25,7 @@ TQ_F32, TQ_BF16, TQ_F16 = 0, 1, 2
 MODES = {"mse": TQ_MODE_MSE, "prod": TQ_MODE_PROD, "grouped": TQ_MODE_GROUPED}
 
 EXPORTED = ["tq_build_codebook", "tq_encode_keys", "tq_encode_values", "tq_decode_attention",
-            "tq_status_string", "tq_idx_row_bytes"]
+            "tq_decode_attention_paged", "tq_status_string", "tq_idx_row_bytes"]
 
 
 class TqError(RuntimeError):
@@ -59,6 +65,10 @@ def _load():
     lib.tq_decode_attention.argtypes = [CFG, P, P, I32, I32, I32, I32, P, I32, P, P, P, P,
                                         I32, I32, P, P, P, ctypes.c_float, P, P, P, P,
                                         ctypes.POINTER(SZ), P]
+    lib.tq_decode_attention_paged.restype = I32
+    lib.tq_decode_attention_paged.argtypes = [CFG, P, P, I32, I32, I32, I32, P, P, I32, I32, P, P, P, P,
+                                              I32, I32, P, P, P, ctypes.c_float, P, P, P, P,
+                                              ctypes.POINTER(SZ), P]
     return lib
 
 

@@ -140,16 +140,21 @@ def decode_workspace_bytes(tables: Tables, B, Hq, Hkv, max_ctx, q_dtype=torch.bf
 
 
 class Decoder:
-    """Holds the workspace for repeated decode steps of one shape."""
+    """Holds the workspace for repeated decode steps of one shape.  With
+    page_size set, the planes are a paged pool and each call passes the block
+    table ([B, max_ctx // page_size] int32)."""
 
     def __init__(self, tables: Tables, B, Hq, Hkv, max_ctx, v_bits, q_dtype=torch.bfloat16,
-                 device="cuda"):
+                 device="cuda", page_size=None):
         self.tables, self.B, self.Hq, self.Hkv, self.max_ctx, self.v_bits = tables, B, Hq, Hkv, max_ctx, v_bits
+        self.page_size = page_size
+        if page_size is not None:
+            assert max_ctx % page_size == 0
         self.ws_bytes = decode_workspace_bytes(tables, B, Hq, Hkv, max_ctx, q_dtype, v_bits)
         self.ws = torch.empty(max(self.ws_bytes, 16), dtype=torch.uint8, device=device)
 
     def __call__(self, q, ctx_len, kp: dict, vp: dict, sm_scale=None, out=None, lse=None,
-                 scores=None):
+                 scores=None, block_table=None):
         B, Hq, d = q.shape
         assert (B, Hq) == (self.B, self.Hq) and q.is_contiguous()
         if sm_scale is None:
@@ -157,13 +162,24 @@ class Decoder:
         if out is None:
             out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
         size = ctypes.c_size_t(self.ws.numel())
-        st = lib.tq_decode_attention(
-            ctypes.byref(self.tables.cfg), _ptr(self.tables.dev), _ptr(q), _DT[q.dtype], B, Hq, self.Hkv,
-            _ptr(ctx_len), self.max_ctx, _ptr(kp["idx"]), _ptr(kp.get("signs")), _ptr(kp["norm"]),
-            _ptr(kp.get("rnorm")), self.v_bits, 32, _ptr(vp["codes"]), _ptr(vp["scale"]), _ptr(vp["zero"]),
-            ctypes.c_float(sm_scale), _ptr(out), _ptr(lse), _ptr(scores), _ptr(self.ws),
-            ctypes.byref(size), _stream())
-        check("tq_decode_attention", st)
+        keys = (_ptr(kp["idx"]), _ptr(kp.get("signs")), _ptr(kp["norm"]), _ptr(kp.get("rnorm")))
+        vals = (self.v_bits, 32, _ptr(vp["codes"]), _ptr(vp["scale"]), _ptr(vp["zero"]))
+        tail = (ctypes.c_float(sm_scale), _ptr(out), _ptr(lse), _ptr(scores), _ptr(self.ws),
+                ctypes.byref(size), _stream())
+        if self.page_size is None:
+            assert block_table is None
+            st = lib.tq_decode_attention(ctypes.byref(self.tables.cfg), _ptr(self.tables.dev), _ptr(q),
+                                         _DT[q.dtype], B, Hq, self.Hkv, _ptr(ctx_len), self.max_ctx,
+                                         *keys, *vals, *tail)
+            check("tq_decode_attention", st)
+        else:
+            nb = self.max_ctx // self.page_size
+            assert block_table is not None and block_table.dtype == torch.int32
+            assert block_table.is_contiguous() and tuple(block_table.shape) == (B, nb)
+            st = lib.tq_decode_attention_paged(ctypes.byref(self.tables.cfg), _ptr(self.tables.dev), _ptr(q),
+                                               _DT[q.dtype], B, Hq, self.Hkv, _ptr(ctx_len), _ptr(block_table),
+                                               nb, self.page_size, *keys, *vals, *tail)
+            check("tq_decode_attention_paged", st)
         return out
 
 

@@ -106,6 +106,10 @@ struct DecArgs {
   float* part;
   int n_split;
   int chunk;  // tokens per split (multiple of TILE)
+  // paged cache (NULL block_table: records of (b, h) are contiguous)
+  const int* block_table;  // [B][max_blocks] physical page of each logical page
+  int max_blocks;
+  int page_size;  // tokens per page, a multiple of TILE
 };
 
 __device__ inline float load_q(const void* q, int dt, long long i) {
@@ -262,9 +266,20 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
   // range inside this (sequence, head)'s rows, so loads need no branches;
   // lanes past t_end get score -inf and weight 0.
   const int t_last = t_end - 1 > t_begin ? t_end - 1 : t_begin;
+  // Record of token t of the tile starting at tb is tile_base(tb) + t: rec0
+  // for a contiguous cache; for a paged one, through the block table entry of
+  // the tile's page (a tile never straddles pages; tiles past the end use the
+  // page of t_last, where their clamped tokens are).
+  auto tile_base = [&](int tb) -> long long {
+    if (!a.block_table) return rec0;
+    const int tc = min(tb, t_last);
+    const int lp = tc / a.page_size;
+    const int blk = a.block_table[(long long)b * a.max_blocks + lp];
+    return ((long long)blk * a.Hkv + hkv) * a.page_size - (long long)lp * a.page_size;
+  };
   auto load_keys = [&](int tb, KeyData& d) {
     const int t = tb + TILE <= t_end ? tb + lane : min(tb + lane, t_last);
-    const long long rec = rec0 + t;
+    const long long rec = tile_base(tb) + t;
     const uint32_t* ip = (const uint32_t*)(a.idx + rec * F::IDXB);
 #pragma unroll
     for (int k = 0; k < F::IDXB / 4; ++k) d.kw[k] = ip[k];
@@ -282,8 +297,9 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
   };
   // value codes of this lane's token pairs (slot + 4k): [2k] even token, [2k+1] odd token
   auto load_codes = [&](int tb, uint32_t* c) {
+    const long long tbase = tile_base(tb);
     if (tb + TILE <= t_end) {  // whole tile: one base address, immediate offsets
-      const uint8_t* base = a.vcodes + (rec0 + tb + 2 * slot) * VROW + VB * u;
+      const uint8_t* base = a.vcodes + (tbase + tb + 2 * slot) * VROW + VB * u;
 #pragma unroll
       for (int k = 0; k < 16; ++k) {
         const uint8_t* pa = base + ((k >> 1) * 8 + (k & 1)) * VROW;
@@ -293,7 +309,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
 #pragma unroll
       for (int k = 0; k < 16; ++k) {
         const int t = min(tb + 2 * slot + (k >> 1) * 8 + (k & 1), t_last);
-        const uint8_t* pa = a.vcodes + (rec0 + t) * VROW + VB * u;
+        const uint8_t* pa = a.vcodes + (tbase + t) * VROW + VB * u;
         c[k] = VB == 2 ? (uint32_t) * (const uint16_t*)pa : *(const uint32_t*)pa;
       }
     }
@@ -788,15 +804,16 @@ hipError_t dispatch(const tq::Parts& P, int vb, const DecArgs& a, dim3 grid, hip
 
 }  // namespace
 
-extern "C" tq_status tq_decode_attention(const tq_key_config* cfg, const void* tables, const void* q,
-                                        int32_t q_dtype, int32_t B, int32_t Hq, int32_t Hkv,
-                                        const int32_t* ctx_len, int32_t max_ctx, const uint8_t* idx,
-                                        const uint8_t* signs, const uint16_t* norm,
-                                        const uint16_t* rnorm, int32_t v_bits, int32_t v_group,
-                                        const uint8_t* v_codes, const uint16_t* v_scale,
-                                        const uint16_t* v_zero, float sm_scale, float* out,
-                                        float* lse, float* scores, void* workspace,
-                                        size_t* workspace_bytes, void* stream) {
+namespace {
+
+tq_status decode_impl(const tq_key_config* cfg, const void* tables, const void* q, int32_t q_dtype,
+                      int32_t B, int32_t Hq, int32_t Hkv, const int32_t* ctx_len, int32_t max_ctx,
+                      const int32_t* block_table, int32_t max_blocks, int32_t page_size,
+                      const uint8_t* idx, const uint8_t* signs, const uint16_t* norm,
+                      const uint16_t* rnorm, int32_t v_bits, int32_t v_group, const uint8_t* v_codes,
+                      const uint16_t* v_scale, const uint16_t* v_zero, float sm_scale, float* out,
+                      float* lse, float* scores, void* workspace, size_t* workspace_bytes,
+                      void* stream) {
   tq::Parts P;
   tq_status st = tq::describe(cfg, &P);
   if (st != TQ_OK) return st;
@@ -862,10 +879,45 @@ extern "C" tq_status tq_decode_attention(const tq_key_config* cfg, const void* t
   a.part = (float*)workspace;
   a.n_split = n_split;
   a.chunk = chunk_tiles * TILE;
+  a.block_table = block_table;
+  a.max_blocks = max_blocks;
+  a.page_size = page_size;
   hipStream_t s = (hipStream_t)stream;
   const dim3 grid(n_split, n_quads, B * Hkv);
   if (dispatch(P, v_bits, a, grid, s) != hipSuccess) return TQ_ERR_HIP;
   hipLaunchKernelGGL(merge_kernel, dim3(B * Hq), dim3(KD), 0, s, (const float*)workspace, n_split,
                      out, lse);
   return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" tq_status tq_decode_attention(const tq_key_config* cfg, const void* tables, const void* q,
+                                        int32_t q_dtype, int32_t B, int32_t Hq, int32_t Hkv,
+                                        const int32_t* ctx_len, int32_t max_ctx, const uint8_t* idx,
+                                        const uint8_t* signs, const uint16_t* norm,
+                                        const uint16_t* rnorm, int32_t v_bits, int32_t v_group,
+                                        const uint8_t* v_codes, const uint16_t* v_scale,
+                                        const uint16_t* v_zero, float sm_scale, float* out,
+                                        float* lse, float* scores, void* workspace,
+                                        size_t* workspace_bytes, void* stream) {
+  return decode_impl(cfg, tables, q, q_dtype, B, Hq, Hkv, ctx_len, max_ctx, nullptr, 0, 0, idx, signs,
+                     norm, rnorm, v_bits, v_group, v_codes, v_scale, v_zero, sm_scale, out, lse, scores,
+                     workspace, workspace_bytes, stream);
+}
+
+extern "C" tq_status tq_decode_attention_paged(
+    const tq_key_config* cfg, const void* tables, const void* q, int32_t q_dtype, int32_t B, int32_t Hq,
+    int32_t Hkv, const int32_t* ctx_len, const int32_t* block_table, int32_t max_blocks_per_seq,
+    int32_t page_size, const uint8_t* idx, const uint8_t* signs, const uint16_t* norm,
+    const uint16_t* rnorm, int32_t v_bits, int32_t v_group, const uint8_t* v_codes,
+    const uint16_t* v_scale, const uint16_t* v_zero, float sm_scale, float* out, float* lse,
+    float* scores, void* workspace, size_t* workspace_bytes, void* stream) {
+  if (page_size <= 0 || page_size % TILE != 0 || max_blocks_per_seq <= 0) return TQ_ERR_ARG;
+  if ((long long)max_blocks_per_seq * page_size > 0x3fffffffLL) return TQ_ERR_ARG;
+  if (workspace && !block_table) return TQ_ERR_ARG;
+  return decode_impl(cfg, tables, q, q_dtype, B, Hq, Hkv, ctx_len, max_blocks_per_seq * page_size,
+                     block_table, max_blocks_per_seq, page_size, idx, signs, norm, rnorm, v_bits, v_group,
+                     v_codes, v_scale, v_zero, sm_scale, out, lse, scores, workspace, workspace_bytes,
+                     stream);
 }

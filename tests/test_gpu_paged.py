@@ -1,0 +1,142 @@
+"""Paged cache and chunked compressed store on the GPU.
+
+- tq_decode_attention_paged on pages in a shuffled order gives the same bits
+  as tq_decode_attention on the same records laid out contiguously.
+- PagedKVCache: chunks appended one after another (sizes that cross page
+  boundaries, single tokens) encode exactly the bytes a one-shot encode
+  writes, and a decode over the chunks matches the oracle's encode + decode
+  of the concatenated tokens; a needle planted in one chunk wins the argmax.
+"""
+import numpy as np
+import pytest
+
+import oracle.tq_oracle as O
+import tq_workloads as W
+from tests import parity as P
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import kv_cache_quantization_encode_amd as tq  # noqa: E402
+from kv_cache_quantization_encode_amd import _lib as L  # noqa: E402
+
+DEV = "cuda"
+
+
+def _np(t):
+    return t.detach().cpu().numpy()
+
+
+@pytest.mark.parametrize("page_size", [64, 256])
+def test_paged_equals_contiguous(page_size):
+    kw = dict(mode="prod", bits=3)
+    B, Hq, Hkv, max_ctx = 3, 8, 2, 1536
+    ctx = [700, 1, 1536]
+    Tg = tq.Tables(L.key_config(seed=7, **kw), DEV)
+    n = B * Hkv * max_ctx
+    kb = W.kv_rows(21, 1, n)[1]
+    vb = W.kv_rows(21, 2, n)[1]
+    keys = torch.from_numpy(kb.view(np.int16)).view(torch.bfloat16).to(DEV)
+    vals = torch.from_numpy(vb.view(np.int16)).view(torch.bfloat16).to(DEV)
+    kp = tq.encode_keys(Tg, keys)
+    vp = tq.encode_values(vals, 2)
+    q = torch.from_numpy(W.queries(21, B, Hq)[1].view(np.int16)).view(torch.bfloat16).to(DEV)
+    ctx_t = torch.tensor(ctx, dtype=torch.int32, device=DEV)
+    dec = tq.Decoder(Tg, B, Hq, Hkv, max_ctx, 2)
+    lse_c = torch.empty((B, Hq), device=DEV)
+    sc_c = torch.full((B, Hq, max_ctx), float("nan"), device=DEV)
+    out_c = dec(q, ctx_t, kp, vp, lse=lse_c, scores=sc_c)
+    # the same records, pages in a shuffled order inside a larger pool
+    nb = max_ctx // page_size
+    n_pages = B * nb + 5
+    perm = np.random.default_rng(3).permutation(n_pages)[:B * nb].reshape(B, nb)
+    bt = torch.from_numpy(perm.astype(np.int32)).to(DEV)
+    t = torch.arange(max_ctx, device=DEV)
+    src, dst = [], []
+    for b in range(B):
+        for h in range(Hkv):
+            src.append((b * Hkv + h) * max_ctx + t)
+            dst.append((bt[b].long()[t // page_size] * Hkv + h) * page_size + t % page_size)
+    src, dst = torch.cat(src), torch.cat(dst)
+    n_rec = n_pages * Hkv * page_size
+    kpp = {k: torch.zeros((n_rec,) + v.shape[1:], dtype=v.dtype, device=DEV) for k, v in kp.items()}
+    vpp = {k: torch.zeros((n_rec,) + v.shape[1:], dtype=v.dtype, device=DEV) for k, v in vp.items()}
+    for k in kp:
+        kpp[k][dst] = kp[k][src]
+    for k in vp:
+        vpp[k][dst] = vp[k][src]
+    decp = tq.Decoder(Tg, B, Hq, Hkv, max_ctx, 2, page_size=page_size)
+    lse_p = torch.empty((B, Hq), device=DEV)
+    sc_p = torch.full((B, Hq, max_ctx), float("nan"), device=DEV)
+    out_p = decp(q, ctx_t, kpp, vpp, lse=lse_p, scores=sc_p, block_table=bt)
+    torch.cuda.synchronize()
+    assert torch.equal(out_c, out_p)
+    assert torch.equal(lse_c, lse_p)
+    for b in range(B):
+        assert torch.equal(sc_c[b, :, :ctx[b]], sc_p[b, :, :ctx[b]])
+
+
+def test_chunked_store_matches_one_shot_and_oracle():
+    kw = dict(mode="prod", bits=3)
+    Hkv, Hq, d, G = 2, 8, 128, 4
+    chunks = [[300, 1, 64, 2000, 17], [1, 1, 511, 700]]
+    Tg = tq.Tables(L.key_config(seed=42, **kw), DEV)
+    To = O.build_tables(O.KeyConfig(mode="prod", bits=3, seed=42))
+    store = tq.PagedKVCache(Tg, Hkv, 2, n_pages=40, page_size=128, max_seqs=2, max_pages_per_seq=20)
+    qv, qb = W.queries(22, 2, Hq)
+    tokens = []
+    for s, sizes in enumerate(chunks):
+        total = sum(sizes)
+        kv, _ = W.kv_rows(22, 1 + 10 * s, total * Hkv)
+        vv, _ = W.kv_rows(22, 2 + 10 * s, total * Hkv)
+        kv = kv.reshape(total, Hkv, d)
+        vv = vv.reshape(total, Hkv, d)
+        # needle: token 2100 (inside the fourth chunk) of sequence 0, head 1,
+        # along the first query head of that KV head's group
+        if s == 0:
+            qd = qv[0, G].astype(np.float64)
+            kv[2100, 1] = (6.0 * qd / np.linalg.norm(qd)).astype(np.float32)
+        kv = W.bf16_values(W.bf16_bits(kv))
+        vv = W.bf16_values(W.bf16_bits(vv))
+        t0 = 0
+        for n in sizes:
+            kt = torch.from_numpy(kv[t0:t0 + n]).to(DEV).to(torch.bfloat16)
+            vt = torch.from_numpy(vv[t0:t0 + n]).to(DEV).to(torch.bfloat16)
+            store.append(s, kt, vt)
+            t0 += n
+        tokens.append((kv, vv))
+    assert store.lengths == [sum(c) for c in chunks]
+    q = torch.from_numpy(qb.view(np.int16)).view(torch.bfloat16).to(DEV)
+    scores = torch.full((2, Hq, store.max_pages_per_seq * store.page_size), float("nan"), device=DEV)
+    out = _np(store.decode(q, scores=scores))
+    scores = _np(scores)
+    for s, (kv, vv) in enumerate(tokens):
+        total = kv.shape[0]
+        # the appended chunks hold the bytes a one-shot encode of the sequence writes
+        one = tq.encode_keys(Tg, torch.from_numpy(kv.reshape(-1, d)).to(DEV).to(torch.bfloat16))
+        onev = tq.encode_values(torch.from_numpy(vv.reshape(-1, d)).to(DEV).to(torch.bfloat16), 2)
+        sl = store.slots(s, 0, total)
+        for k in one:
+            assert torch.equal(store.kp[k][sl], one[k]), k
+        for k in onev:
+            assert torch.equal(store.vp[k][sl], onev[k]), k
+        # decode over the chunks against the oracle's encode + decode
+        for h in range(Hkv):
+            enc = O.encode_keys(kv[:, h].astype(np.float64), To)
+            khat = O.dequant_keys(enc, To)
+            vhat = O.dequant_values(O.encode_values(vv[:, h], 2))
+            heads = slice(h * G, (h + 1) * G)
+            s_ref, o_ref, _ = O.decode_attention(qv[s, heads].astype(np.float64), khat, vhat, total)
+            P.check_out(out[s, heads], o_ref)
+            # scores agree where the bytes agree with the oracle's (band cases aside)
+            rec = O.pack_key_record(enc, To)
+            same = np.ones(total, dtype=bool)
+            for k in ("idx", "signs", "rnorm", "norm"):
+                g = _np(one[k]).reshape(total, Hkv, -1)[:, h]
+                same &= np.all(g.view(np.uint8) == np.ascontiguousarray(rec[k]).reshape(total, -1).view(np.uint8),
+                               axis=1)
+            P.check_scores(scores[s, heads, :total][:, same], s_ref[:, same])
+    assert int(np.argmax(scores[0, G, :sum(chunks[0])])) == 2100
