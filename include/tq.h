@@ -218,6 +218,38 @@ tq_status tq_decode_attention_paged(const tq_key_config* cfg, const void* tables
                                     float sm_scale, float* out, float* lse, float* scores,
                                     void* workspace, size_t* workspace_bytes, void* stream);
 
+/*
+ * tq_dequantize_keys -- dense k_hat rows from packed key records: the
+ * dequantise path of the "tqlite" README (fake quantisation, prefill) and of
+ * validate_paper.py's prod quantiser:
+ *   k_hat = (n / sqrt(d)) Pi^T c[idx]  (+ rho sqrt(pi/2) / m  Pi^T S^T (2 bit - 1), PROD)
+ * (GROUPED: each half with its own norm, rotation and codebook, no QJL term).
+ *   n_vec       output rows.
+ *   slots       (nullable) int64 [n_vec]: record read for output row i (NULL:
+ *               record i); a slot outside [0, n_records) gives a zero row.
+ *   idx ..      the key planes of tq_encode_keys, n_records rows each.
+ *   out         [n_vec] rows of d elements of out_dtype (TQ_F32 / TQ_BF16 /
+ *               TQ_F16, rounded to nearest even), row i at out + i*out_stride
+ *               elements; 16-byte aligned, out_stride*elemsize a multiple of 16.
+ * Computed in float32.  n_vec == 0 is a no-op; d must be 128.
+ */
+tq_status tq_dequantize_keys(const tq_key_config* cfg, const void* tables, int64_t n_vec,
+                             const int64_t* slots, int64_t n_records,
+                             const uint8_t* idx, const uint8_t* signs, const uint16_t* norm,
+                             const uint16_t* rnorm, void* out, int32_t out_dtype, int64_t out_stride,
+                             void* stream);
+
+/*
+ * tq_dequantize_values -- v_hat = code * s + z (one float32 fma per element)
+ * for n_vec rows of the value planes of tq_encode_values (bit-packing article
+ * sec 二/三 for the code layout).  Slots, output layout and errors as
+ * tq_dequantize_keys; bits 2 or 4, group 32, d 128.
+ */
+tq_status tq_dequantize_values(int32_t bits, int32_t group, int32_t d, int64_t n_vec,
+                               const int64_t* slots, int64_t n_records,
+                               const uint8_t* codes, const uint16_t* scale, const uint16_t* zero,
+                               void* out, int32_t out_dtype, int64_t out_stride, void* stream);
+
 /* Static description of a status code (never NULL). */
 const char* tq_status_string(int32_t status);
 

@@ -25,7 +25,8 @@ TQ_F32, TQ_BF16, TQ_F16 = 0, 1, 2
 MODES = {"mse": TQ_MODE_MSE, "prod": TQ_MODE_PROD, "grouped": TQ_MODE_GROUPED}
 
 EXPORTED = ["tq_build_codebook", "tq_encode_keys", "tq_encode_values", "tq_decode_attention",
-            "tq_decode_attention_paged", "tq_status_string", "tq_idx_row_bytes"]
+            "tq_decode_attention_paged", "tq_dequantize_keys", "tq_dequantize_values",
+            "tq_status_string", "tq_idx_row_bytes"]
 
 
 class TqError(RuntimeError):
@@ -69,6 +70,10 @@ def _load():
     lib.tq_decode_attention_paged.argtypes = [CFG, P, P, I32, I32, I32, I32, P, P, I32, I32, P, P, P, P,
                                               I32, I32, P, P, P, ctypes.c_float, P, P, P, P,
                                               ctypes.POINTER(SZ), P]
+    lib.tq_dequantize_keys.restype = I32
+    lib.tq_dequantize_keys.argtypes = [CFG, P, I64, P, I64, P, P, P, P, P, I32, I64, P]
+    lib.tq_dequantize_values.restype = I32
+    lib.tq_dequantize_values.argtypes = [I32, I32, I32, I64, P, I64, P, P, P, P, I32, I64, P]
     return lib
 
 

@@ -130,6 +130,39 @@ def encode_values(values: torch.Tensor, bits: int, group: int = 32, planes: dict
     return planes
 
 
+def dequantize_keys(tables: Tables, planes: dict, n_vec: int | None = None, slots=None,
+                    dtype=torch.float32, out=None):
+    """Dense k_hat [n_vec, d] from the key planes (rows `slots`, or 0..n_vec-1)."""
+    n_records = planes["idx"].shape[0]
+    if n_vec is None:
+        n_vec = n_records if slots is None else slots.shape[0]
+    if out is None:
+        out = torch.empty((n_vec, tables.cfg.d), dtype=dtype, device=planes["idx"].device)
+    assert out.stride(1) == 1
+    st = lib.tq_dequantize_keys(ctypes.byref(tables.cfg), _ptr(tables.dev), n_vec, _ptr(slots), n_records,
+                                _ptr(planes["idx"]), _ptr(planes.get("signs")), _ptr(planes["norm"]),
+                                _ptr(planes.get("rnorm")), _ptr(out), _DT[out.dtype], out.stride(0), _stream())
+    check("tq_dequantize_keys", st)
+    return out
+
+
+def dequantize_values(planes: dict, bits: int, n_vec: int | None = None, slots=None, dtype=torch.float32,
+                      out=None, group: int = 32):
+    """Dense v_hat [n_vec, d] from the value planes."""
+    n_records = planes["codes"].shape[0]
+    d = planes["codes"].shape[1] * 8 // bits
+    if n_vec is None:
+        n_vec = n_records if slots is None else slots.shape[0]
+    if out is None:
+        out = torch.empty((n_vec, d), dtype=dtype, device=planes["codes"].device)
+    assert out.stride(1) == 1
+    st = lib.tq_dequantize_values(bits, group, d, n_vec, _ptr(slots), n_records, _ptr(planes["codes"]),
+                                  _ptr(planes["scale"]), _ptr(planes["zero"]), _ptr(out), _DT[out.dtype],
+                                  out.stride(0), _stream())
+    check("tq_dequantize_values", st)
+    return out
+
+
 def decode_workspace_bytes(tables: Tables, B, Hq, Hkv, max_ctx, q_dtype=torch.bfloat16, v_bits=2) -> int:
     size = ctypes.c_size_t(0)
     st = lib.tq_decode_attention(ctypes.byref(tables.cfg), None, None, _DT[q_dtype], B, Hq, Hkv, None,

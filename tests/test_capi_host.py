@@ -221,6 +221,42 @@ def test_paged_decode_argument_errors():
     assert _dec_paged(prod, bt=None, ws=FAKE) == L.TQ_ERR_ARG
 
 
+def test_dequantize_argument_errors():
+    prod = L.key_config(mode="prod", bits=3)
+    ok = dict(n=8, slots=None, nrec=8, idx=FAKE, signs=FAKE, norm=FAKE, rnorm=FAKE, out=FAKE, dt=L.TQ_BF16,
+              stride=128)
+
+    def dk(cfg, **kw):
+        a = dict(ok)
+        a.update(kw)
+        return L.lib.tq_dequantize_keys(ctypes.byref(cfg), FAKE, a["n"], a["slots"], a["nrec"], a["idx"],
+                                        a["signs"], a["norm"], a["rnorm"], a["out"], a["dt"], a["stride"], None)
+
+    assert dk(prod, n=0) == L.TQ_OK
+    assert dk(prod, n=-1) == L.TQ_ERR_ARG
+    assert dk(prod, out=None) == L.TQ_ERR_ARG
+    assert dk(prod, out=FAKE + 2) == L.TQ_ERR_ARG           # misaligned output
+    assert dk(prod, stride=100) == L.TQ_ERR_ARG             # row pitch not 16-byte aligned
+    assert dk(prod, stride=64) == L.TQ_ERR_ARG              # pitch shorter than a row
+    assert dk(prod, dt=7) == L.TQ_ERR_ARG
+    assert dk(prod, signs=None) == L.TQ_ERR_ARG             # prod needs signs and rnorm
+    assert dk(prod, slots=FAKE + 4) == L.TQ_ERR_ARG
+    assert dk(L.key_config(mode="mse", bits=4, d=64)) == L.TQ_ERR_UNSUPPORTED
+
+    def dv(**kw):
+        a = dict(bits=2, group=32, d=128, n=8, codes=FAKE, scale=FAKE, zero=FAKE, out=FAKE, dt=L.TQ_F32,
+                 stride=128)
+        a.update(kw)
+        return L.lib.tq_dequantize_values(a["bits"], a["group"], a["d"], a["n"], None, 8, a["codes"],
+                                          a["scale"], a["zero"], a["out"], a["dt"], a["stride"], None)
+
+    assert dv(bits=3) == L.TQ_ERR_UNSUPPORTED
+    assert dv(group=16) == L.TQ_ERR_UNSUPPORTED
+    assert dv(codes=None) == L.TQ_ERR_ARG
+    assert dv(scale=FAKE + 1) == L.TQ_ERR_ARG
+    assert dv(n=0) == L.TQ_OK
+
+
 def test_no_device_reports_hip_error():
     """Without a GPU the workspace query (which needs the device's CU count)
     returns TQ_ERR_HIP instead of aborting."""
