@@ -10,9 +10,10 @@ from .api import (Decoder, Tables, build_codebook, decode_attention, decode_work
                   dequantize_keys, dequantize_values, encode_keys, encode_values, idx_row_bytes, key_planes,
                   parse_tables, value_planes)
 from .store import PagedKVCache
+from . import quality
 
 __all__ = ["KeyConfig", "TqError", "key_config", "status_string", "Tables", "Decoder",
            "build_codebook", "parse_tables", "encode_keys", "encode_values", "decode_attention",
            "decode_workspace_bytes", "key_planes", "value_planes", "idx_row_bytes", "PagedKVCache",
-           "dequantize_keys", "dequantize_values",
+           "dequantize_keys", "dequantize_values", "quality",
            "TQ_F32", "TQ_BF16", "TQ_F16", "TQ_MODE_MSE", "TQ_MODE_PROD", "TQ_MODE_GROUPED"]
