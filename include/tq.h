@@ -250,6 +250,22 @@ tq_status tq_dequantize_values(int32_t bits, int32_t group, int32_t d, int64_t n
                                const uint8_t* codes, const uint16_t* scale, const uint16_t* zero,
                                void* out, int32_t out_dtype, int64_t out_stride, void* stream);
 
+/*
+ * tq_channel_moments -- per-channel sums over n_vec rows of d = 128 channels:
+ * out[0][c] = sum_r x[r][c], out[1][c] = sum_r x[r][c]^2 (float64), from which
+ * the caller takes per-channel variances to pick GROUPED mode's outlier
+ * channels (the "tqlite" README's mode table: higher-variance channels get the
+ * higher bit width).  The channels chosen are then moved to the front of the
+ * keys and of the queries alike, which leaves every q.k unchanged.
+ *   x            n_vec rows of dtype, row r at x + r*row_stride elements.
+ *   out          device float64 [2][128], 8-byte aligned.
+ *   workspace    device scratch (8-byte aligned); NULL: *workspace_bytes
+ *                receives the size and nothing runs.
+ * Deterministic: partial sums over fixed row ranges, added in a fixed order.
+ */
+tq_status tq_channel_moments(const void* x, int32_t dtype, int64_t n_vec, int64_t row_stride, int32_t d,
+                             double* out, void* workspace, size_t* workspace_bytes, void* stream);
+
 /* Static description of a status code (never NULL). */
 const char* tq_status_string(int32_t status);
 

@@ -6,9 +6,9 @@ streams); importing it requires the built libtq.so next to this file.
 """
 from ._lib import (TQ_BF16, TQ_F16, TQ_F32, TQ_MODE_GROUPED, TQ_MODE_MSE, TQ_MODE_PROD, KeyConfig,
                    TqError, key_config, status_string)
-from .api import (Decoder, Tables, build_codebook, decode_attention, decode_workspace_bytes,
-                  dequantize_keys, dequantize_values, encode_keys, encode_values, idx_row_bytes, key_planes,
-                  parse_tables, value_planes)
+from .api import (Decoder, Tables, build_codebook, channel_moments, decode_attention,
+                  decode_workspace_bytes, dequantize_keys, dequantize_values, encode_keys, encode_values,
+                  idx_row_bytes, key_planes, parse_tables, select_outlier_channels, value_planes)
 from .store import PagedKVCache
 from . import quality
 
@@ -16,4 +16,5 @@ __all__ = ["KeyConfig", "TqError", "key_config", "status_string", "Tables", "Dec
            "build_codebook", "parse_tables", "encode_keys", "encode_values", "decode_attention",
            "decode_workspace_bytes", "key_planes", "value_planes", "idx_row_bytes", "PagedKVCache",
            "dequantize_keys", "dequantize_values", "quality",
+           "channel_moments", "select_outlier_channels",
            "TQ_F32", "TQ_BF16", "TQ_F16", "TQ_MODE_MSE", "TQ_MODE_PROD", "TQ_MODE_GROUPED"]

@@ -25,7 +25,7 @@ TQ_F32, TQ_BF16, TQ_F16 = 0, 1, 2
 MODES = {"mse": TQ_MODE_MSE, "prod": TQ_MODE_PROD, "grouped": TQ_MODE_GROUPED}
 
 EXPORTED = ["tq_build_codebook", "tq_encode_keys", "tq_encode_values", "tq_decode_attention",
-            "tq_decode_attention_paged", "tq_dequantize_keys", "tq_dequantize_values",
+            "tq_decode_attention_paged", "tq_dequantize_keys", "tq_dequantize_values", "tq_channel_moments",
             "tq_status_string", "tq_idx_row_bytes"]
 
 
@@ -74,6 +74,8 @@ def _load():
     lib.tq_dequantize_keys.argtypes = [CFG, P, I64, P, I64, P, P, P, P, P, I32, I64, P]
     lib.tq_dequantize_values.restype = I32
     lib.tq_dequantize_values.argtypes = [I32, I32, I32, I64, P, I64, P, P, P, P, I32, I64, P]
+    lib.tq_channel_moments.restype = I32
+    lib.tq_channel_moments.argtypes = [P, I32, I64, I64, I32, P, P, ctypes.POINTER(SZ), P]
     return lib
 
 

@@ -163,6 +163,34 @@ def dequantize_values(planes: dict, bits: int, n_vec: int | None = None, slots=N
     return out
 
 
+def channel_moments(x: torch.Tensor) -> torch.Tensor:
+    """float64 [2, d]: per-channel sum and sum of squares of the rows of x [n, d]."""
+    assert x.dim() == 2 and x.stride(1) == 1
+    n, d = x.shape
+    size = ctypes.c_size_t(0)
+    check("tq_channel_moments", lib.tq_channel_moments(None, _DT[x.dtype], n, x.stride(0), d, None, None,
+                                                       ctypes.byref(size), None))
+    ws = torch.empty(max(size.value, 8), dtype=torch.uint8, device=x.device)
+    out = torch.empty((2, d), dtype=torch.float64, device=x.device)
+    size = ctypes.c_size_t(ws.numel())
+    check("tq_channel_moments", lib.tq_channel_moments(_ptr(x), _DT[x.dtype], n, x.stride(0), d, _ptr(out),
+                                                       _ptr(ws), ctypes.byref(size), _stream()))
+    return out
+
+
+def select_outlier_channels(x: torch.Tensor, n_outlier: int = 64) -> torch.Tensor:
+    """Channel order for GROUPED mode: the n_outlier highest-variance channels
+    of the key rows x [n, d] first, then the rest (each in channel order).
+    Apply it to keys and queries alike: k[:, perm], q[..., perm]."""
+    m = channel_moments(x)
+    n = max(x.shape[0], 1)
+    var = m[1] / n - (m[0] / n) ** 2
+    order = torch.argsort(-var, stable=True)
+    out_ch = torch.sort(order[:n_outlier]).values
+    rest = torch.sort(order[n_outlier:]).values
+    return torch.cat([out_ch, rest])
+
+
 def decode_workspace_bytes(tables: Tables, B, Hq, Hkv, max_ctx, q_dtype=torch.bfloat16, v_bits=2) -> int:
     size = ctypes.c_size_t(0)
     st = lib.tq_decode_attention(ctypes.byref(tables.cfg), None, None, _DT[q_dtype], B, Hq, Hkv, None,

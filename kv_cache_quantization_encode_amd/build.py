@@ -11,7 +11,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libtq.so")
-SOURCES = ["tq_host.cpp", "tq_encode.hip", "tq_decode.hip", "tq_dequant.hip"]
+SOURCES = ["tq_host.cpp", "tq_encode.hip", "tq_decode.hip", "tq_dequant.hip", "tq_stats.hip"]
 ARCH = "gfx950"
 
 

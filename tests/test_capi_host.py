@@ -257,6 +257,18 @@ def test_dequantize_argument_errors():
     assert dv(n=0) == L.TQ_OK
 
 
+def test_channel_moments_workspace_query_and_errors():
+    size = ctypes.c_size_t(0)
+    assert L.lib.tq_channel_moments(None, L.TQ_BF16, 5000, 128, 128, None, None, ctypes.byref(size), None) == L.TQ_OK
+    assert size.value == 5 * 2 * 128 * 8          # one float64 partial pair per 1024 rows
+    assert L.lib.tq_channel_moments(None, L.TQ_BF16, 10, 128, 64, None, None, ctypes.byref(size), None) == \
+        L.TQ_ERR_UNSUPPORTED
+    assert L.lib.tq_channel_moments(None, 9, 10, 128, 128, None, None, ctypes.byref(size), None) == L.TQ_ERR_ARG
+    small = ctypes.c_size_t(8)
+    assert L.lib.tq_channel_moments(FAKE, L.TQ_BF16, 5000, 128, 128, FAKE, FAKE, ctypes.byref(small), None) == \
+        L.TQ_ERR_WORKSPACE
+
+
 def test_no_device_reports_hip_error():
     """Without a GPU the workspace query (which needs the device's CU count)
     returns TQ_ERR_HIP instead of aborting."""
