@@ -44,6 +44,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--settle-seconds", type=float, default=0.5,
+                    help="untimed steps after the warm-up, until the GPU clocks have settled")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-encode-bench", action="store_true")
     ap.add_argument("--cpu-groups", type=int, default=128,
@@ -242,6 +244,17 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
+    # The GPU's clocks take tens of milliseconds of sustained load to settle;
+    # keep stepping (untimed, on the warm-up inputs) until settle_seconds have
+    # passed so that the timed steps measure the steady state.
+    t_settle = time.perf_counter()
+    i = 0
+    while time.perf_counter() - t_settle < args.settle_seconds:
+        step(i % max(args.warmup, 1))
+        i += 1
+        if i % 50 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.steps)]
     torch.cuda.synchronize()
@@ -292,7 +305,7 @@ def main():
     print(json.dumps(line))
 
 
-def encode_bench(tq, W, T, keys, vals, dev, reps=3):
+def encode_bench(tq, W, T, keys, vals, dev, reps=10):
     """Bulk encode throughput (not part of the timed steps)."""
     import torch
 
