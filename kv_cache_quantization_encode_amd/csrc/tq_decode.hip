@@ -745,21 +745,6 @@ __global__ __launch_bounds__(KD) void merge_kernel(const float* part, int n_spli
   if (lse && j == 0) lse[bh] = L > 0.0f ? (M + log2f(L)) * 0.69314718055994531f : -INFINITY;
 }
 
-int cu_count() {
-  static std::atomic<int> cached[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return -1;
-  if (dev >= 0 && dev < 64) {
-    int v = cached[dev].load(std::memory_order_relaxed);
-    if (v > 0) return v;
-  }
-  int n = 0;
-  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-    return -1;
-  if (dev >= 0 && dev < 64) cached[dev].store(n, std::memory_order_relaxed);
-  return n;
-}
-
 template <int MODE, int B0, int B1, int VB>
 hipError_t launch(const DecArgs& a, dim3 grid, hipStream_t s) {
   hipLaunchKernelGGL((decode_kernel<MODE, B0, B1, VB>), grid, dim3(NT), 0, s, a);
@@ -823,7 +808,7 @@ tq_status decode_impl(const tq_key_config* cfg, const void* tables, const void* 
   if (q_dtype != TQ_F32 && q_dtype != TQ_BF16 && q_dtype != TQ_F16) return TQ_ERR_ARG;
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || max_ctx <= 0) return TQ_ERR_ARG;
   if (!workspace_bytes) return TQ_ERR_ARG;
-  const int cus = cu_count();
+  const int cus = tq::cu_count();
   if (cus <= 0) return TQ_ERR_HIP;
   const int G = Hq / Hkv;
   const int n_quads = (G + QH - 1) / QH;

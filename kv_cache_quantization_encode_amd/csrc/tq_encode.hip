@@ -588,13 +588,26 @@ extern "C" tq_status tq_encode_keys(const tq_key_config* cfg, const void* tables
   const long long tiles = (n_vec + TILE_KEYS - 1) / TILE_KEYS;
   if (tiles > 0x7fffffffLL) return TQ_ERR_ARG;
   a.n_tiles = (int)tiles;
-  const dim3 grid(grid_for(tiles, WAVES)), block(WAVES * 64);
+  // Grid: a few blocks per CU, each wave looping over tiles so that a
+  // block's table staging is paid once for several tiles and the next
+  // tile's load overlaps the current one.  Measured on MI355X: two blocks per
+  // CU suit the MSE and grouped encoders (launches of 65536 keys are
+  // dominated by that staging), eight the prod encoder (long launches, where
+  // more blocks in flight keep the loads and the MFMA work overlapped).
+  const int cus = tq::cu_count();
+  if (cus <= 0) return TQ_ERR_HIP;
+  const long long want = (tiles + WAVES - 1) / WAVES;
+  const long long cap = (long long)cus * (P.mode == TQ_MODE_PROD ? 8 : 2);
   hipStream_t s = (hipStream_t)stream;
-#define TQ_LAUNCH_KEYS(M)                                                                   \
-  do {                                                                                      \
-    if (dtype == TQ_F32) hipLaunchKernelGGL((encode_keys_kernel<M, TQ_F32>), grid, block, 0, s, a);   \
-    else if (dtype == TQ_BF16) hipLaunchKernelGGL((encode_keys_kernel<M, TQ_BF16>), grid, block, 0, s, a); \
-    else hipLaunchKernelGGL((encode_keys_kernel<M, TQ_F16>), grid, block, 0, s, a);           \
+  auto launch = [&](auto kernel) {
+    const dim3 grid((unsigned)(want < cap ? want : cap)), block(WAVES * 64);
+    hipLaunchKernelGGL(kernel, grid, block, 0, s, a);
+  };
+#define TQ_LAUNCH_KEYS(M)                                               \
+  do {                                                                  \
+    if (dtype == TQ_F32) launch(encode_keys_kernel<M, TQ_F32>);          \
+    else if (dtype == TQ_BF16) launch(encode_keys_kernel<M, TQ_BF16>);   \
+    else launch(encode_keys_kernel<M, TQ_F16>);                          \
   } while (0)
   if (P.mode == TQ_MODE_MSE) TQ_LAUNCH_KEYS(TQ_MODE_MSE);
   else if (P.mode == TQ_MODE_PROD) TQ_LAUNCH_KEYS(TQ_MODE_PROD);

@@ -12,7 +12,10 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <atomic>
 #include <vector>
+
+#include <hip/hip_runtime_api.h>
 
 #include "tq.h"
 #include "tq_internal.h"
@@ -80,6 +83,20 @@ tq_status describe(const tq_key_config* cfg, Parts* p) {
   }
   p->idx_row_bytes = (int)row;
   return TQ_OK;
+}
+
+int cu_count() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return -1;
+  if (dev >= 0 && dev < 64) {
+    const int v = cached[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return -1;
+  if (dev >= 0 && dev < 64) cached[dev].store(n, std::memory_order_relaxed);
+  return n;
 }
 
 }  // namespace tq

@@ -27,6 +27,9 @@ tq_status describe(const tq_key_config* cfg, Parts* p);
 
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// Compute units of the current device (cached per device); -1 on error.
+int cu_count();
+
 }  // namespace tq
 
 #endif  // TQ_INTERNAL_H_
