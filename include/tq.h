@@ -197,7 +197,8 @@ tq_status tq_decode_attention(const tq_key_config* cfg, const void* tables,
  * which is also the slot tq_encode_keys / tq_encode_values write it to.
  *   block_table         int32 [B][max_blocks_per_seq] device array; entries
  *                       for pages below ctx_len[b] must name pages that exist
- *                       in the planes (not checked on the device).
+ *                       in the planes (not checked on the device); entries
+ *                       past them are never read.
  *   page_size           tokens per page, a positive multiple of 64.
  *   scores              (nullable) [B][Hq][max_blocks_per_seq * page_size].
  * Every other argument, the workspace query and the errors are those of

@@ -45,6 +45,7 @@ constexpr int KD = 128;
 #endif
 constexpr int NW = TQ_DEC_WAVES;  // waves per workgroup
 constexpr int NT = NW * 64;   // threads per workgroup
+constexpr int PAGE_CACHE = 512;  // block-table entries a workgroup keeps in LDS
 constexpr int TILE = 64;      // tokens per wave tile
 constexpr int QH = 4;         // query heads per workgroup
 constexpr int PART = KD + 2;  // floats per partial: max, sum, out[128]
@@ -85,6 +86,7 @@ struct Lds {
   float cen[32];
   float abuf[2 * (NW / 2) * QH];
   float hmul[2 * QH];
+  int pages[PAGE_CACHE];  // block-table entries of this workgroup's token range (paged cache)
 };
 
 struct DecArgs {
@@ -270,11 +272,17 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
   // for a contiguous cache; for a paged one, through the block table entry of
   // the tile's page (a tile never straddles pages; tiles past the end use the
   // page of t_last, where their clamped tokens are).
+  // The workgroup's block-table entries are staged in LDS by the prologue
+  // when they fit (a global read here would have to wait behind the tile
+  // loads already in flight).
+  const int lp0 = a.block_table ? t_begin / a.page_size : 0;
+  const int n_pages_wg = a.block_table && t_end > t_begin ? t_last / a.page_size - lp0 + 1 : 0;
+  const bool pages_in_lds = n_pages_wg <= PAGE_CACHE;
   auto tile_base = [&](int tb) -> long long {
     if (!a.block_table) return rec0;
     const int tc = min(tb, t_last);
     const int lp = tc / a.page_size;
-    const int blk = a.block_table[(long long)b * a.max_blocks + lp];
+    const int blk = pages_in_lds ? L.pages[lp - lp0] : a.block_table[(long long)b * a.max_blocks + lp];
     return ((long long)blk * a.Hkv + hkv) * a.page_size - (long long)lp * a.page_size;
   };
   auto load_keys = [&](int tb, KeyData& d) {
@@ -351,6 +359,8 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
     if (part < n_parts && k < (part ? lev1 : lev0)) cen[tid] = (part ? cent1 : cent0)[k];
   }
   if (!F::GROUPED && tid < QH) amax[QH + tid] = 0;
+  if (pages_in_lds)
+    for (int i = tid; i < n_pages_wg; i += NT) L.pages[i] = a.block_table[(long long)b * a.max_blocks + lp0 + i];
 
   // Walsh-Hadamard transform of sigma * q in registers (one 128-point
   // transform, or two 64-point ones for GROUPED): butterflies on lane bits
@@ -407,8 +417,12 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
     }
   }
   // Each wave's first tile goes out now; the table building covers its latency.
-  if (scorer) load_keys(tile_tb(0), kd);
-  else load_codes(tile_tb(0), codes);
+  // A split past the sequence's end loads nothing (its block-table entries
+  // need not name a page, and no page of it is staged).
+  if (n_tiles > 0) {
+    if (scorer) load_keys(tile_tb(0), kd);
+    else load_codes(tile_tb(0), codes);
+  }
   if constexpr (F::PROD) lds_barrier();
   // per-head, per-class power-of-two table scale: the largest possible entry
   // (|q'| bound x largest centroid x coordinates per byte) stays <= 16384
