@@ -48,6 +48,8 @@ constexpr int NT = NW * 64;   // threads per workgroup
 constexpr int PAGE_CACHE = 512;  // block-table entries a workgroup keeps in LDS
 constexpr int TILE = 64;      // tokens per wave tile
 constexpr int QH = 4;         // query heads per workgroup
+constexpr int WGRP = 32 * QH + 16;  // dwords per value group of a wave's weight slot (padded)
+constexpr int WSLOT = 4 * WGRP;     // dwords of a wave's weight slot
 constexpr int PART = KD + 2;  // floats per partial: max, sum, out[128]
 constexpr float LOG2E = 1.4426950408889634f;
 
@@ -70,7 +72,7 @@ struct Fmt {
   static constexpr int IDXB = P0 + (GROUPED ? P1 : 0);          // idx row bytes
   static constexpr int KWORDS = (IDXB + (PROD ? KD / 8 : 0)) / 4;  // idx + sign words
   // the weight ring also holds the half tables while the lookup tables are built
-  static constexpr int RING_BYTES_W = NW * 32 * 4 * QH * 4;
+  static constexpr int RING_BYTES_W = NW * WSLOT * 4;
   static constexpr int HALF_BYTES = (P0 + P1) * 32 * 16;
   static constexpr int RING_BYTES = RING_BYTES_W > HALF_BYTES ? RING_BYTES_W : HALF_BYTES;
 };
@@ -114,11 +116,11 @@ struct DecArgs {
   int page_size;  // tokens per page, a multiple of TILE
 };
 
-__device__ inline float load_q(const void* q, int dt, long long i) {
-  if (dt == TQ_F32) return ((const float*)q)[i];
-  const uint16_t v = ((const uint16_t*)q)[i];
-  if (dt == TQ_BF16) return __uint_as_float((uint32_t)v << 16);
-  return __half2float(__ushort_as_half(v));
+// a query element as loaded: f32 bits, or bf16 / fp16 bits in the low half
+__device__ inline float q_word_to_float(uint32_t w, int dt) {
+  if (dt == TQ_F32) return __uint_as_float(w);
+  if (dt == TQ_BF16) return __uint_as_float(w << 16);
+  return __half2float(__ushort_as_half((unsigned short)w));
 }
 
 __device__ inline float h2f(uint32_t bits16) { return __half2float(__ushort_as_half((unsigned short)bits16)); }
@@ -226,7 +228,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
   uint2* lut = L.lut;       // tables: class 0 [value][position], class 1 [position][value]
   float* qp = L.qp;         // [QH][KD] rotated queries
   float* qs = L.qs;         // [QH][KD] S q' (PROD)
-  uint32_t* wbuf = L.ring;  // [2][NW/2][32 pairs][4 groups][QH] half2 weights
+  uint32_t* wbuf = L.ring;  // [2][NW/2][4 groups][32 pairs][QH] half2 weights (groups padded)
   int* amax = L.amax;       // [2][QH]
   float* cen = L.cen;       // [2][16] centroids of each part
   float* abuf = L.abuf;     // [2][NW/2][QH] softmax rescale factors
@@ -272,18 +274,17 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
   // for a contiguous cache; for a paged one, through the block table entry of
   // the tile's page (a tile never straddles pages; tiles past the end use the
   // page of t_last, where their clamped tokens are).
-  // The workgroup's block-table entries are staged in LDS by the prologue
-  // when they fit (a global read here would have to wait behind the tile
-  // loads already in flight).
+  // The workgroup's block-table entries are staged in LDS by the prologue (a
+  // global read here would wait behind the tile loads already in flight);
+  // the host sizes the splits so that they fit in PAGE_CACHE entries.
   const int lp0 = a.block_table ? t_begin / a.page_size : 0;
-  const int n_pages_wg = a.block_table && t_end > t_begin ? t_last / a.page_size - lp0 + 1 : 0;
-  const bool pages_in_lds = n_pages_wg <= PAGE_CACHE;
+  const int n_pages_wg =
+      a.block_table && t_end > t_begin ? min(t_last / a.page_size - lp0 + 1, PAGE_CACHE) : 0;
   auto tile_base = [&](int tb) -> long long {
     if (!a.block_table) return rec0;
     const int tc = min(tb, t_last);
     const int lp = tc / a.page_size;
-    const int blk = pages_in_lds ? L.pages[lp - lp0] : a.block_table[(long long)b * a.max_blocks + lp];
-    return ((long long)blk * a.Hkv + hkv) * a.page_size - (long long)lp * a.page_size;
+    return ((long long)L.pages[lp - lp0] * a.Hkv + hkv) * a.page_size - (long long)lp * a.page_size;
   };
   auto load_keys = [&](int tb, KeyData& d) {
     const int t = tb + TILE <= t_end ? tb + lane : min(tb + lane, t_last);
@@ -325,8 +326,8 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
 
   // ---- prologue: rotate the queries, project them, build the tables.
   // Global reads go out first, in the order they are needed: the queries and
-  // sigma, the rows of S, then each wave's first tile (whose latency the
-  // table building covers).
+  // sigma, the rows of S, then (after the first barrier) each wave's first
+  // tile, whose latency the projection and table building cover.
   const int n_parts = H->n_parts;
   const float* cent0 = (const float*)(a.tables + H->off_centroids[0]);
   const float* cent1 = (const float*)(a.tables + H->off_centroids[n_parts > 1 ? 1 : 0]);
@@ -334,12 +335,19 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
   // waves 0..QH-1: head `wave` of the quad; lane holds coordinates lane, lane + 64
   float x0 = 0.0f, x1 = 0.0f, sg0 = 0.0f, sg1 = 0.0f;
   const int gq_w = QH * quad + wave;  // query head within the GQA group
-  if (wave < QH) {
-    if (gq_w < a.G) {
-      const long long qrow = ((long long)b * a.Hq + hkv * a.G + gq_w) * KD;
-      x0 = load_q(a.q, a.q_dtype, qrow + lane);
-      x1 = load_q(a.q, a.q_dtype, qrow + lane + 64);
+  // raw query words first (both halves in flight together), converted below
+  uint32_t qw0 = 0, qw1 = 0;
+  if (wave < QH && gq_w < a.G) {
+    const long long qrow = ((long long)b * a.Hq + hkv * a.G + gq_w) * KD;
+    if (a.q_dtype == TQ_F32) {
+      qw0 = ((const uint32_t*)a.q)[qrow + lane];
+      qw1 = ((const uint32_t*)a.q)[qrow + lane + 64];
+    } else {
+      qw0 = ((const uint16_t*)a.q)[qrow + lane];
+      qw1 = ((const uint16_t*)a.q)[qrow + lane + 64];
     }
+  }
+  if (wave < QH) {
     const float* sig0 = (const float*)(a.tables + H->off_sigma[0]);
     const float* sig1 = (const float*)(a.tables + H->off_sigma[n_parts > 1 ? 1 : 0]);
     sg0 = sig0[lane];
@@ -359,15 +367,14 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
     if (part < n_parts && k < (part ? lev1 : lev0)) cen[tid] = (part ? cent1 : cent0)[k];
   }
   if (!F::GROUPED && tid < QH) amax[QH + tid] = 0;
-  if (pages_in_lds)
-    for (int i = tid; i < n_pages_wg; i += NT) L.pages[i] = a.block_table[(long long)b * a.max_blocks + lp0 + i];
+  for (int i = tid; i < n_pages_wg; i += NT) L.pages[i] = a.block_table[(long long)b * a.max_blocks + lp0 + i];
 
   // Walsh-Hadamard transform of sigma * q in registers (one 128-point
   // transform, or two 64-point ones for GROUPED): butterflies on lane bits
   // through shuffles, the top stage inside the lane.
   if (wave < QH) {
-    x0 *= sg0;
-    x1 *= sg1;
+    x0 = q_word_to_float(qw0, a.q_dtype) * sg0;
+    x1 = q_word_to_float(qw1, a.q_dtype) * sg1;
     if constexpr (!F::GROUPED) {
       const float t = x0;
       x0 = t + x1;
@@ -390,9 +397,21 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
       if (F::GROUPED) amax[QH + wave] = __float_as_int(m1);
     }
   }
-  __syncthreads();
+  // Only LDS data is shared here, so the barrier need not wait for global
+  // loads.  Each wave's first tile goes out now (a split past the sequence's
+  // end loads nothing: its block-table entries need not name a page); the
+  // projection and table building below cover its latency.  The prologue's
+  // own loads (the rows of S) are waited for first: score and p.V waves
+  // issue different numbers of tile loads, and a count-based wait for S
+  // after them would also wait for part of the tile.
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  lds_barrier();
   KeyData kd;
   uint32_t codes[16];
+  if (n_tiles > 0) {
+    if (scorer) load_keys(tile_tb(0), kd);
+    else load_codes(tile_tb(0), codes);
+  }
   if constexpr (F::PROD) {
     const uint32_t sw[8] = {sA.x, sA.y, sA.z, sA.w, sB.x, sB.y, sB.z, sB.w};
     float part[QH] = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -416,13 +435,6 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
       if (lane == 0) atomicMax(&amax[QH + hh], __float_as_int(m));
     }
   }
-  // Each wave's first tile goes out now; the table building covers its latency.
-  // A split past the sequence's end loads nothing (its block-table entries
-  // need not name a page, and no page of it is staged).
-  if (n_tiles > 0) {
-    if (scorer) load_keys(tile_tb(0), kd);
-    else load_codes(tile_tb(0), codes);
-  }
   if constexpr (F::PROD) lds_barrier();
   // per-head, per-class power-of-two table scale: the largest possible entry
   // (|q'| bound x largest centroid x coordinates per byte) stays <= 16384
@@ -430,7 +442,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
     float cmax = 1.0f;
     int cpb = 8;
     if (!(F::PROD && cls == 1)) {
-      cmax = fabsf(cls ? cent1[lev1 - 1] : cent0[lev0 - 1]);
+      cmax = fabsf(cen[cls ? 16 + lev1 - 1 : lev0 - 1]);  // LDS: no wait behind the tile loads
       cpb = cls == 0 ? F::CPB0 : F::CPB1;
     }
     return pow2_scale(__int_as_float(amax[cls * QH + hh]) * cmax * cpb);
@@ -604,14 +616,16 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
 #pragma unroll
           for (int k = 0; k < 4; ++k) zacc[hh][k] = fmaf(p[hh], zz[k], zacc[hh][k]);
         }
-        // weights p * scale as fp16, paired by token: [pair][group][head] = (w_even, w_odd)
-        uint16_t* wb16 = (uint16_t*)(wbuf + ((r & 1) * NS + pw) * (32 * 4 * QH));
+        // weights p * scale as fp16, paired by token: [group][pair][head] = (w_even, w_odd);
+        // the group stride is padded so that neither these stores nor the p.V
+        // waves' 16-byte reads pile onto a few LDS banks
+        uint16_t* wb16 = (uint16_t*)(wbuf + ((r & 1) * NS + pw) * WSLOT);
         const int pair = lane >> 1, odd = lane & 1;
 #pragma unroll
         for (int k = 0; k < 4; ++k)
 #pragma unroll
           for (int hh = 0; hh < QH; ++hh)
-            wb16[((pair * 4 + k) * QH + hh) * 2 + odd] = __half_as_ushort(__float2half_rn(p[hh] * ss[k]));
+            wb16[(k * WGRP + pair * QH + hh) * 2 + odd] = __half_as_ushort(__float2half_rn(p[hh] * ss[k]));
         if (lane == 0) {
 #pragma unroll
           for (int hh = 0; hh < QH; ++hh) abuf[((r & 1) * NS + pw) * QH + hh] = alpha[hh];
@@ -648,7 +662,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
       const int tb = r >= 1 ? tile_tb(r - 1) : t_end;
       if (tb < t_end) {
         load_codes(tile_tb(r), nxt);  // next round's tile
-        const uint32_t* wsrc = wbuf + (((r - 1) & 1) * NS + pw) * (32 * 4 * QH);
+        const uint32_t* wsrc = wbuf + (((r - 1) & 1) * NS + pw) * WSLOT;
         const float4 al = *(const float4*)(abuf + (((r - 1) & 1) * NS + pw) * QH);
         const float alv[QH] = {uniform(al.x), uniform(al.y), uniform(al.z), uniform(al.w)};
         if (alv[0] != 1.0f || alv[1] != 1.0f || alv[2] != 1.0f || alv[3] != 1.0f) {
@@ -662,7 +676,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
         for (int k = 0; k < 8; ++k) {
           const int pr = slot + 4 * k;
           const uint32_t cA = cur[2 * k], cB = cur[2 * k + 1];
-          const uint4 wv = *(const uint4*)(wsrc + (pr * 4 + grp) * QH);
+          const uint4 wv = *(const uint4*)(wsrc + grp * WGRP + pr * QH);
           const uint32_t wh[QH] = {wv.x, wv.y, wv.z, wv.w};
           uint32_t pairs[8];
           if (VB == 2) {
@@ -835,6 +849,12 @@ tq_status decode_impl(const tq_key_config* cfg, const void* tables, const void* 
   if (n_split > (max_tiles + tiles_per_split_min - 1) / tiles_per_split_min)
     n_split = (max_tiles + tiles_per_split_min - 1) / tiles_per_split_min;
   if (n_split < 1) n_split = 1;
+  // paged: a split spans at most chunk / page_size + 2 pages, all staged in LDS
+  if (page_size > 0) {
+    const int max_chunk_tiles = (PAGE_CACHE - 1) * (page_size / TILE);
+    if (n_split < (max_tiles + max_chunk_tiles - 1) / max_chunk_tiles)
+      n_split = (max_tiles + max_chunk_tiles - 1) / max_chunk_tiles;
+  }
   const int chunk_tiles = (max_tiles + n_split - 1) / n_split;
   n_split = (max_tiles + chunk_tiles - 1) / chunk_tiles;
   const size_t need = (size_t)B * Hq * n_split * PART * sizeof(float);
