@@ -191,12 +191,21 @@ def select_outlier_channels(x: torch.Tensor, n_outlier: int = 64) -> torch.Tenso
     return torch.cat([out_ch, rest])
 
 
-def decode_workspace_bytes(tables: Tables, B, Hq, Hkv, max_ctx, q_dtype=torch.bfloat16, v_bits=2) -> int:
+def decode_workspace_bytes(tables: Tables, B, Hq, Hkv, max_ctx, q_dtype=torch.bfloat16, v_bits=2,
+                           page_size=None) -> int:
+    """Workspace size of tq_decode_attention (or, with page_size, of
+    tq_decode_attention_paged with max_ctx // page_size blocks per sequence)."""
     size = ctypes.c_size_t(0)
-    st = lib.tq_decode_attention(ctypes.byref(tables.cfg), None, None, _DT[q_dtype], B, Hq, Hkv, None,
-                                 max_ctx, None, None, None, None, v_bits, 32, None, None, None,
-                                 ctypes.c_float(1.0), None, None, None, None, ctypes.byref(size), None)
-    check("tq_decode_attention", st)
+    keys = (None, None, None, None, v_bits, 32, None, None, None, ctypes.c_float(1.0), None, None, None,
+            None, ctypes.byref(size), None)
+    if page_size is None:
+        st = lib.tq_decode_attention(ctypes.byref(tables.cfg), None, None, _DT[q_dtype], B, Hq, Hkv, None,
+                                     max_ctx, *keys)
+        check("tq_decode_attention", st)
+    else:
+        st = lib.tq_decode_attention_paged(ctypes.byref(tables.cfg), None, None, _DT[q_dtype], B, Hq, Hkv,
+                                           None, None, max_ctx // page_size, page_size, *keys)
+        check("tq_decode_attention_paged", st)
     return size.value
 
 
@@ -211,7 +220,7 @@ class Decoder:
         self.page_size = page_size
         if page_size is not None:
             assert max_ctx % page_size == 0
-        self.ws_bytes = decode_workspace_bytes(tables, B, Hq, Hkv, max_ctx, q_dtype, v_bits)
+        self.ws_bytes = decode_workspace_bytes(tables, B, Hq, Hkv, max_ctx, q_dtype, v_bits, page_size)
         self.ws = torch.empty(max(self.ws_bytes, 16), dtype=torch.uint8, device=device)
 
     def __call__(self, q, ctx_len, kp: dict, vp: dict, sm_scale=None, out=None, lse=None,
