@@ -9,7 +9,8 @@ bf16 queries, keys and values drawn N(0,1) (synthetic, seeded).
 
 One step = one pass of the whole path for one decode step of the batch:
   encode the step's new key and value of every (sequence, KV head) into the
-  packed cache (norm, rotation, bucketize, QJL signs, packing; value groups),
+  packed cache in one launch (norm, rotation, bucketize, QJL signs, packing;
+  value groups),
   then decode attention over the full 32768-token context (query rotation and
   projection, lookup-table scores from the packed bytes, online softmax,
   p.V, split-K merge).
@@ -233,8 +234,7 @@ def main():
         return
 
     def step(i, ev=None):
-        tq.encode_keys(T, new_k[i], kp, slots=slots, n_records=n_rec)
-        tq.encode_values(new_v[i], 2, planes=vp, slots=slots, n_records=n_rec)
+        tq.append_kv(T, new_k[i], new_v[i], 2, kp, vp, slots=slots, n_records=n_rec)
         if ev is not None:
             ev[0].record()
         dec(qs[i], ctx_len, kp, vp, out=out)

@@ -148,6 +148,27 @@ tq_status tq_encode_values(int32_t bits, int32_t group, int32_t d,
                            uint8_t* codes, uint16_t* scale, uint16_t* zero, void* stream);
 
 /*
+ * tq_append_kv -- tq_encode_keys and tq_encode_values of the same n_vec tokens
+ * in one launch (the append step of the compressed store: bit-packing article
+ * sec 五, new tokens are encoded straight into the packed planes).  Key and
+ * value blocks run side by side, so a short append costs one encoder's latency
+ * instead of two.  The outputs equal those of the two calls, bit for bit.
+ *   keys, values  [n_vec rows] x d elements of the same `dtype`, rows at
+ *                 key_stride / value_stride elements (as in the two calls).
+ *   slots         (nullable) shared by keys and values; n_records rows in
+ *                 every plane.
+ * Every other argument, the layouts and the errors are those of
+ * tq_encode_keys (cfg, tables, idx, signs, norm, rnorm) and tq_encode_values
+ * (v_bits, v_group, codes, scale, zero).  n_vec == 0 is a no-op.
+ */
+tq_status tq_append_kv(const tq_key_config* cfg, const void* tables, const void* keys,
+                       const void* values, int32_t dtype, int64_t n_vec, int64_t key_stride,
+                       int64_t value_stride, const int64_t* slots, int64_t n_records,
+                       uint8_t* idx, uint8_t* signs, uint16_t* norm, uint16_t* rnorm,
+                       int32_t v_bits, int32_t v_group, uint8_t* codes, uint16_t* scale,
+                       uint16_t* zero, void* stream);
+
+/*
  * tq_decode_attention -- one decode step of attention over the packed cache.
  * For query head h of sequence b (KV head h / (Hq/Hkv)), over tokens
  * t < ctx_len[b]:

@@ -24,7 +24,7 @@ TQ_MODE_MSE, TQ_MODE_PROD, TQ_MODE_GROUPED = 0, 1, 2
 TQ_F32, TQ_BF16, TQ_F16 = 0, 1, 2
 MODES = {"mse": TQ_MODE_MSE, "prod": TQ_MODE_PROD, "grouped": TQ_MODE_GROUPED}
 
-EXPORTED = ["tq_build_codebook", "tq_encode_keys", "tq_encode_values", "tq_decode_attention",
+EXPORTED = ["tq_build_codebook", "tq_encode_keys", "tq_encode_values", "tq_append_kv", "tq_decode_attention",
             "tq_decode_attention_paged", "tq_dequantize_keys", "tq_dequantize_values", "tq_channel_moments",
             "tq_status_string", "tq_idx_row_bytes"]
 
@@ -62,6 +62,8 @@ def _load():
     lib.tq_encode_keys.argtypes = [CFG, P, P, I32, I64, I64, P, I64, P, P, P, P, P]
     lib.tq_encode_values.restype = I32
     lib.tq_encode_values.argtypes = [I32, I32, I32, P, I32, I64, I64, P, I64, P, P, P, P]
+    lib.tq_append_kv.restype = I32
+    lib.tq_append_kv.argtypes = [CFG, P, P, P, I32, I64, I64, I64, P, I64, P, P, P, P, I32, I32, P, P, P, P]
     lib.tq_decode_attention.restype = I32
     lib.tq_decode_attention.argtypes = [CFG, P, P, I32, I32, I32, I32, P, I32, P, P, P, P,
                                         I32, I32, P, P, P, ctypes.c_float, P, P, P, P,

@@ -130,6 +130,23 @@ def encode_values(values: torch.Tensor, bits: int, group: int = 32, planes: dict
     return planes
 
 
+def append_kv(tables: Tables, keys: torch.Tensor, values: torch.Tensor, v_bits: int, kp: dict, vp: dict,
+              slots=None, n_records: int | None = None, group: int = 32):
+    """Encode keys and values [n, d] (same dtype) of the same tokens into the
+    key planes kp and value planes vp in one launch (tq_append_kv); the
+    planes equal those of encode_keys + encode_values."""
+    assert keys.dim() == 2 and keys.stride(1) == 1 and values.dim() == 2 and values.stride(1) == 1
+    assert keys.shape == values.shape and keys.dtype == values.dtype
+    n = keys.shape[0]
+    if n_records is None:
+        n_records = kp["idx"].shape[0]
+    st = lib.tq_append_kv(ctypes.byref(tables.cfg), _ptr(tables.dev), _ptr(keys), _ptr(values),
+                          _DT[keys.dtype], n, keys.stride(0), values.stride(0), _ptr(slots), n_records,
+                          _ptr(kp["idx"]), _ptr(kp.get("signs")), _ptr(kp["norm"]), _ptr(kp.get("rnorm")),
+                          v_bits, group, _ptr(vp["codes"]), _ptr(vp["scale"]), _ptr(vp["zero"]), _stream())
+    check("tq_append_kv", st)
+
+
 def dequantize_keys(tables: Tables, planes: dict, n_vec: int | None = None, slots=None,
                     dtype=torch.float32, out=None):
     """Dense k_hat [n_vec, d] from the key planes (rows `slots`, or 0..n_vec-1)."""

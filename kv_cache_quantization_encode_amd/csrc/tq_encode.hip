@@ -199,9 +199,10 @@ __device__ inline void store_idx(int w, uint8_t* dst, const int* q) {
   }
 }
 
-// MODE: TQ_MODE_MSE / PROD / GROUPED.  DT: input dtype.
+// MODE: TQ_MODE_MSE / PROD / GROUPED.  DT: input dtype.  Block `bid` of `nb`
+// blocks that share the key tiles.
 template <int MODE, int DT>
-__global__ __launch_bounds__(WAVES * 64, 2) void encode_keys_kernel(KeyArgs a) {
+__device__ __forceinline__ void encode_keys_body(const KeyArgs& a, int bid, int nb) {
   const tq_blob_header* H = (const tq_blob_header*)a.tables;
   constexpr int NP = MODE == TQ_MODE_GROUPED ? 2 : 1;
   __shared__ __align__(16) tq_hint s_hint[NP][TQ_MAX_HINT];
@@ -215,14 +216,14 @@ __global__ __launch_bounds__(WAVES * 64, 2) void encode_keys_kernel(KeyArgs a) {
   const int kk = lane & 15;    // key within the tile
 
   // Rows past n_vec load the last row (kept in bounds) and encode zeros.
-  const int tile_step = gridDim.x * WAVES;
+  const int tile_step = nb * WAVES;
   auto row_of = [&](int tile) {
     const long long row = (long long)tile * TILE_KEYS + kk;
     return row < a.n_vec ? row : a.n_vec - 1;
   };
   // This wave's first tile goes out before the tables are staged.
   RawKey<DT> raw, raw_next;
-  int tile = blockIdx.x * WAVES + wave;
+  int tile = bid * WAVES + wave;
   if (tile < a.n_tiles) load_raw<DT>(a.keys, row_of(tile) * a.row_stride, g, raw);
 
   // Formats with at most four cells (1- and 2-bit indices, one part) compare
@@ -454,12 +455,13 @@ struct ValArgs {
   long long n_tiles;
 };
 
+// Block `bid` of `nb` blocks (of 256 threads) that share the value tiles.
 template <int BITS, int DT>
-__global__ __launch_bounds__(256) void encode_values_kernel(ValArgs a) {
+__device__ __forceinline__ void encode_values_body(const ValArgs& a, int bid, int nb) {
   const int lane = threadIdx.x & 63;
   const int sub = lane & 15;          // 8-channel chunk within the row
-  const long long tiles_per_grid = (long long)gridDim.x * (blockDim.x >> 6);
-  for (long long tile = (long long)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  const long long tiles_per_grid = (long long)nb * (blockDim.x >> 6);
+  for (long long tile = (long long)bid * (blockDim.x >> 6) + (threadIdx.x >> 6);
        tile < a.n_tiles; tile += tiles_per_grid) {
     // sixteen rows per wave: all four loads go out before any is used
     float vv[4][8];
@@ -539,6 +541,25 @@ __global__ __launch_bounds__(256) void encode_values_kernel(ValArgs a) {
   }
 }
 
+template <int MODE, int DT>
+__global__ __launch_bounds__(WAVES * 64, 2) void encode_keys_kernel(KeyArgs a) {
+  encode_keys_body<MODE, DT>(a, blockIdx.x, gridDim.x);
+}
+
+template <int BITS, int DT>
+__global__ __launch_bounds__(256) void encode_values_kernel(ValArgs a) {
+  encode_values_body<BITS, DT>(a, blockIdx.x, gridDim.x);
+}
+
+// Keys and values of the same tokens in one launch: the first key_blocks
+// blocks encode the keys, the rest the values, side by side.
+static_assert(WAVES * 64 == 256, "key and value blocks share one block size");
+template <int MODE, int BITS, int DT>
+__global__ __launch_bounds__(256, 2) void append_kv_kernel(KeyArgs ka, ValArgs va, int key_blocks) {
+  if ((int)blockIdx.x < key_blocks) encode_keys_body<MODE, DT>(ka, blockIdx.x, key_blocks);
+  else encode_values_body<BITS, DT>(va, blockIdx.x - key_blocks, gridDim.x - key_blocks);
+}
+
 int grid_for(long long tiles, int per_block) {
   long long blocks = (tiles + per_block - 1) / per_block;
   const long long cap = 256LL * 8;  // enough to fill 256 CUs several times
@@ -547,19 +568,19 @@ int grid_for(long long tiles, int per_block) {
   return (int)blocks;
 }
 
-}  // namespace
-
-extern "C" tq_status tq_encode_keys(const tq_key_config* cfg, const void* tables, const void* keys,
-                                   int32_t dtype, int64_t n_vec, int64_t row_stride,
-                                   const int64_t* slots, int64_t n_records, uint8_t* idx,
-                                   uint8_t* signs, uint16_t* norm, uint16_t* rnorm, void* stream) {
-  tq::Parts P;
+// Argument checks and kernel arguments of the key encoder.  Returns TQ_OK with
+// *empty set when there is nothing to encode (n_vec == 0).
+tq_status key_args(const tq_key_config* cfg, const void* tables, const void* keys, int32_t dtype,
+                   int64_t n_vec, int64_t row_stride, const int64_t* slots, int64_t n_records,
+                   uint8_t* idx, uint8_t* signs, uint16_t* norm, uint16_t* rnorm, tq::Parts& P,
+                   KeyArgs& a, bool& empty) {
   tq_status st = tq::describe(cfg, &P);
   if (st != TQ_OK) return st;
   if (P.d != KD) return TQ_ERR_UNSUPPORTED;
   if (n_vec < 0 || n_records < 0) return TQ_ERR_ARG;
   if (dtype != TQ_F32 && dtype != TQ_BF16 && dtype != TQ_F16) return TQ_ERR_ARG;
-  if (n_vec == 0) return TQ_OK;
+  empty = n_vec == 0;
+  if (empty) return TQ_OK;
   if (!tables || !keys || !idx || !norm) return TQ_ERR_ARG;
   const int esz = dtype == TQ_F32 ? 4 : 2;
   if (row_stride < KD || ((row_stride * esz) & 15) || !tq::aligned16(keys)) return TQ_ERR_ARG;
@@ -572,8 +593,8 @@ extern "C" tq_status tq_encode_keys(const tq_key_config* cfg, const void* tables
   if (slots && ((uintptr_t)slots & 7)) return TQ_ERR_ARG;
   for (int p = 0; p < P.n_parts; ++p)
     if (P.part_width[p] * P.part_d[p] / 8 % 4) return TQ_ERR_UNSUPPORTED;
-
-  KeyArgs a;
+  const long long tiles = (n_vec + TILE_KEYS - 1) / TILE_KEYS;
+  if (tiles > 0x7fffffffLL) return TQ_ERR_ARG;
   a.tables = (const unsigned char*)tables;
   a.keys = keys;
   a.n_vec = n_vec;
@@ -585,29 +606,69 @@ extern "C" tq_status tq_encode_keys(const tq_key_config* cfg, const void* tables
   a.norm = norm;
   a.rnorm = rnorm;
   a.idx_row_bytes = P.idx_row_bytes;
-  const long long tiles = (n_vec + TILE_KEYS - 1) / TILE_KEYS;
-  if (tiles > 0x7fffffffLL) return TQ_ERR_ARG;
   a.n_tiles = (int)tiles;
-  // Grid: a few blocks per CU, each wave looping over tiles so that a
-  // block's table staging is paid once for several tiles and the next
-  // tile's load overlaps the current one.  Measured on MI355X: two blocks per
-  // CU suit the MSE and grouped encoders (launches of 65536 keys are
-  // dominated by that staging), eight the prod encoder (long launches, where
-  // more blocks in flight keep the loads and the MFMA work overlapped).
+  return TQ_OK;
+}
+
+// Key-encoder blocks: a few per CU, each wave looping over tiles so that a
+// block's table staging is paid once for several tiles and the next tile's
+// load overlaps the current one.  Measured on MI355X: two blocks per CU suit
+// the MSE and grouped encoders (launches of 65536 keys are dominated by that
+// staging), eight the prod encoder (long launches, where more blocks in
+// flight keep the loads and the MFMA work overlapped).
+int key_blocks(const tq::Parts& P, int n_tiles, int cus) {
+  const long long want = ((long long)n_tiles + WAVES - 1) / WAVES;
+  const long long cap = (long long)cus * (P.mode == TQ_MODE_PROD ? 8 : 2);
+  return (int)(want < cap ? want : cap);
+}
+
+tq_status val_args(int32_t bits, int32_t group, int32_t d, const void* values, int32_t dtype,
+                   int64_t n_vec, int64_t row_stride, const int64_t* slots, int64_t n_records,
+                   uint8_t* codes, uint16_t* scale, uint16_t* zero, ValArgs& a, bool& empty) {
+  if (bits != 2 && bits != 4) return TQ_ERR_UNSUPPORTED;
+  if (group != 32 || d != KD) return TQ_ERR_UNSUPPORTED;
+  if (n_vec < 0 || n_records < 0) return TQ_ERR_ARG;
+  if (dtype != TQ_F32 && dtype != TQ_BF16 && dtype != TQ_F16) return TQ_ERR_ARG;
+  empty = n_vec == 0;
+  if (empty) return TQ_OK;
+  if (!values || !codes || !scale || !zero) return TQ_ERR_ARG;
+  const int esz = dtype == TQ_F32 ? 4 : 2;
+  if (row_stride < KD || ((row_stride * esz) & 15) || !tq::aligned16(values)) return TQ_ERR_ARG;
+  if (!tq::aligned16(codes) || ((uintptr_t)scale & 1) || ((uintptr_t)zero & 1)) return TQ_ERR_ARG;
+  if (slots && ((uintptr_t)slots & 7)) return TQ_ERR_ARG;
+  a.values = values;
+  a.n_vec = n_vec;
+  a.row_stride = row_stride;
+  a.slots = (const long long*)slots;
+  a.n_records = n_records;
+  a.codes = codes;
+  a.scale = scale;
+  a.zero = zero;
+  a.n_tiles = (n_vec + 15) / 16;
+  return TQ_OK;
+}
+
+}  // namespace
+
+extern "C" tq_status tq_encode_keys(const tq_key_config* cfg, const void* tables, const void* keys,
+                                   int32_t dtype, int64_t n_vec, int64_t row_stride,
+                                   const int64_t* slots, int64_t n_records, uint8_t* idx,
+                                   uint8_t* signs, uint16_t* norm, uint16_t* rnorm, void* stream) {
+  tq::Parts P;
+  KeyArgs a;
+  bool empty = false;
+  tq_status st = key_args(cfg, tables, keys, dtype, n_vec, row_stride, slots, n_records, idx, signs, norm,
+                          rnorm, P, a, empty);
+  if (st != TQ_OK || empty) return st;
   const int cus = tq::cu_count();
   if (cus <= 0) return TQ_ERR_HIP;
-  const long long want = (tiles + WAVES - 1) / WAVES;
-  const long long cap = (long long)cus * (P.mode == TQ_MODE_PROD ? 8 : 2);
+  const dim3 grid((unsigned)key_blocks(P, a.n_tiles, cus)), block(WAVES * 64);
   hipStream_t s = (hipStream_t)stream;
-  auto launch = [&](auto kernel) {
-    const dim3 grid((unsigned)(want < cap ? want : cap)), block(WAVES * 64);
-    hipLaunchKernelGGL(kernel, grid, block, 0, s, a);
-  };
-#define TQ_LAUNCH_KEYS(M)                                               \
-  do {                                                                  \
-    if (dtype == TQ_F32) launch(encode_keys_kernel<M, TQ_F32>);          \
-    else if (dtype == TQ_BF16) launch(encode_keys_kernel<M, TQ_BF16>);   \
-    else launch(encode_keys_kernel<M, TQ_F16>);                          \
+#define TQ_LAUNCH_KEYS(M)                                                                   \
+  do {                                                                                      \
+    if (dtype == TQ_F32) hipLaunchKernelGGL((encode_keys_kernel<M, TQ_F32>), grid, block, 0, s, a);      \
+    else if (dtype == TQ_BF16) hipLaunchKernelGGL((encode_keys_kernel<M, TQ_BF16>), grid, block, 0, s, a); \
+    else hipLaunchKernelGGL((encode_keys_kernel<M, TQ_F16>), grid, block, 0, s, a);            \
   } while (0)
   if (P.mode == TQ_MODE_MSE) TQ_LAUNCH_KEYS(TQ_MODE_MSE);
   else if (P.mode == TQ_MODE_PROD) TQ_LAUNCH_KEYS(TQ_MODE_PROD);
@@ -620,26 +681,11 @@ extern "C" tq_status tq_encode_values(int32_t bits, int32_t group, int32_t d, co
                                      int32_t dtype, int64_t n_vec, int64_t row_stride,
                                      const int64_t* slots, int64_t n_records, uint8_t* codes,
                                      uint16_t* scale, uint16_t* zero, void* stream) {
-  if (bits != 2 && bits != 4) return TQ_ERR_UNSUPPORTED;
-  if (group != 32 || d != KD) return TQ_ERR_UNSUPPORTED;
-  if (n_vec < 0 || n_records < 0) return TQ_ERR_ARG;
-  if (dtype != TQ_F32 && dtype != TQ_BF16 && dtype != TQ_F16) return TQ_ERR_ARG;
-  if (n_vec == 0) return TQ_OK;
-  if (!values || !codes || !scale || !zero) return TQ_ERR_ARG;
-  const int esz = dtype == TQ_F32 ? 4 : 2;
-  if (row_stride < KD || ((row_stride * esz) & 15) || !tq::aligned16(values)) return TQ_ERR_ARG;
-  if (!tq::aligned16(codes) || ((uintptr_t)scale & 1) || ((uintptr_t)zero & 1)) return TQ_ERR_ARG;
-  if (slots && ((uintptr_t)slots & 7)) return TQ_ERR_ARG;
   ValArgs a;
-  a.values = values;
-  a.n_vec = n_vec;
-  a.row_stride = row_stride;
-  a.slots = (const long long*)slots;
-  a.n_records = n_records;
-  a.codes = codes;
-  a.scale = scale;
-  a.zero = zero;
-  a.n_tiles = (n_vec + 15) / 16;
+  bool empty = false;
+  tq_status st = val_args(bits, group, d, values, dtype, n_vec, row_stride, slots, n_records, codes, scale,
+                          zero, a, empty);
+  if (st != TQ_OK || empty) return st;
   const dim3 grid(grid_for(a.n_tiles, 4)), block(256);
   hipStream_t s = (hipStream_t)stream;
 #define TQ_LAUNCH_VALS(B)                                                                   \
@@ -651,5 +697,46 @@ extern "C" tq_status tq_encode_values(int32_t bits, int32_t group, int32_t d, co
   if (bits == 2) TQ_LAUNCH_VALS(2);
   else TQ_LAUNCH_VALS(4);
 #undef TQ_LAUNCH_VALS
+  return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_HIP;
+}
+
+extern "C" tq_status tq_append_kv(const tq_key_config* cfg, const void* tables, const void* keys,
+                                 const void* values, int32_t dtype, int64_t n_vec, int64_t key_stride,
+                                 int64_t value_stride, const int64_t* slots, int64_t n_records,
+                                 uint8_t* idx, uint8_t* signs, uint16_t* norm, uint16_t* rnorm,
+                                 int32_t v_bits, int32_t v_group, uint8_t* codes, uint16_t* scale,
+                                 uint16_t* zero, void* stream) {
+  tq::Parts P;
+  KeyArgs ka;
+  ValArgs va;
+  bool empty = false;
+  tq_status st = key_args(cfg, tables, keys, dtype, n_vec, key_stride, slots, n_records, idx, signs, norm,
+                          rnorm, P, ka, empty);
+  if (st != TQ_OK) return st;
+  st = val_args(v_bits, v_group, KD, values, dtype, n_vec, value_stride, slots, n_records, codes, scale,
+                zero, va, empty);
+  if (st != TQ_OK || empty) return st;
+  const int cus = tq::cu_count();
+  if (cus <= 0) return TQ_ERR_HIP;
+  const int kb = key_blocks(P, ka.n_tiles, cus);
+  const long long blocks = (long long)kb + grid_for(va.n_tiles, 4);
+  const dim3 grid((unsigned)blocks), block(256);
+  hipStream_t s = (hipStream_t)stream;
+#define TQ_LAUNCH_KV(M, B)                                                                          \
+  do {                                                                                              \
+    if (dtype == TQ_F32) hipLaunchKernelGGL((append_kv_kernel<M, B, TQ_F32>), grid, block, 0, s, ka, va, kb);  \
+    else if (dtype == TQ_BF16) hipLaunchKernelGGL((append_kv_kernel<M, B, TQ_BF16>), grid, block, 0, s, ka, va, kb); \
+    else hipLaunchKernelGGL((append_kv_kernel<M, B, TQ_F16>), grid, block, 0, s, ka, va, kb);          \
+  } while (0)
+#define TQ_LAUNCH_KV_M(M)               \
+  do {                                  \
+    if (v_bits == 2) TQ_LAUNCH_KV(M, 2); \
+    else TQ_LAUNCH_KV(M, 4);             \
+  } while (0)
+  if (P.mode == TQ_MODE_MSE) TQ_LAUNCH_KV_M(TQ_MODE_MSE);
+  else if (P.mode == TQ_MODE_PROD) TQ_LAUNCH_KV_M(TQ_MODE_PROD);
+  else TQ_LAUNCH_KV_M(TQ_MODE_GROUPED);
+#undef TQ_LAUNCH_KV_M
+#undef TQ_LAUNCH_KV
   return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_HIP;
 }

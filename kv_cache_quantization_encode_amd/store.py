@@ -10,13 +10,14 @@ record of token t of (sequence b, KV head h) is
 
 This module only allocates pages, keeps the tables and computes those record
 indices (slots); the quantisation and the attention run in libtq's kernels
-(tq_encode_keys / tq_encode_values with slots, tq_decode_attention_paged).
+(tq_append_kv, or tq_encode_keys / tq_encode_values, with slots;
+tq_decode_attention_paged).
 """
 from __future__ import annotations
 
 import torch
 
-from .api import Decoder, Tables, encode_keys, encode_values, key_planes, value_planes
+from .api import Decoder, Tables, append_kv, encode_keys, encode_values, key_planes, value_planes
 
 
 class PagedKVCache:
@@ -80,9 +81,12 @@ class PagedKVCache:
         t0 = self.lengths[seq]
         self._grow(seq, t0 + n)
         sl = self.slots(seq, t0, n)
-        encode_keys(self.tables, k.reshape(n * self.Hkv, -1), self.kp, slots=sl, n_records=self.n_records)
-        encode_values(v.reshape(n * self.Hkv, -1), self.v_bits, planes=self.vp, slots=sl,
-                      n_records=self.n_records)
+        kr, vr = k.reshape(n * self.Hkv, -1), v.reshape(n * self.Hkv, -1)
+        if kr.dtype == vr.dtype:  # one launch for both
+            append_kv(self.tables, kr, vr, self.v_bits, self.kp, self.vp, slots=sl, n_records=self.n_records)
+        else:
+            encode_keys(self.tables, kr, self.kp, slots=sl, n_records=self.n_records)
+            encode_values(vr, self.v_bits, planes=self.vp, slots=sl, n_records=self.n_records)
         self.lengths[seq] = t0 + n
 
     def decoder(self, B: int, Hq: int, q_dtype=torch.bfloat16) -> Decoder:

@@ -181,6 +181,34 @@ def test_encode_values_argument_errors():
     assert f(*args(n=0)) == L.TQ_OK
 
 
+def _app(cfg, **kw):
+    a = dict(keys=FAKE, values=FAKE, dtype=L.TQ_BF16, n=64, ks=128, vs=128, signs=FAKE, rnorm=FAKE,
+             vb=2, vg=32, codes=FAKE)
+    a.update(kw)
+    return L.lib.tq_append_kv(ctypes.byref(cfg), FAKE, a["keys"], a["values"], a["dtype"], a["n"], a["ks"],
+                              a["vs"], None, 64, FAKE, a["signs"], FAKE, a["rnorm"], a["vb"], a["vg"],
+                              a["codes"], FAKE, FAKE, None)
+
+
+def test_append_kv_argument_errors():
+    """The combined key/value append checks both halves' arguments on the
+    host (as tq_encode_keys and tq_encode_values do) before any launch."""
+    prod = L.key_config(mode="prod", bits=3)
+    assert _app(prod, n=0) == L.TQ_OK                           # no-op
+    assert _app(prod, keys=None) == L.TQ_ERR_ARG
+    assert _app(prod, values=None) == L.TQ_ERR_ARG
+    assert _app(prod, values=FAKE + 2) == L.TQ_ERR_ARG          # misaligned value rows
+    assert _app(prod, ks=100) == L.TQ_ERR_ARG
+    assert _app(prod, vs=129) == L.TQ_ERR_ARG
+    assert _app(prod, signs=None) == L.TQ_ERR_ARG
+    assert _app(L.key_config(mode="mse", bits=4)) == L.TQ_ERR_ARG   # MSE must not pass signs/rnorm
+    assert _app(prod, vb=3) == L.TQ_ERR_UNSUPPORTED
+    assert _app(prod, vg=64) == L.TQ_ERR_UNSUPPORTED
+    assert _app(prod, codes=None) == L.TQ_ERR_ARG
+    assert _app(prod, n=-1) == L.TQ_ERR_ARG
+    assert _app(prod, dtype=9) == L.TQ_ERR_ARG
+
+
 def _dec(cfg, **kw):
     a = dict(q=FAKE, B=2, Hq=8, Hkv=2, ctx=FAKE, max_ctx=1024, vb=2, vg=32, ws=None,
              wsb=ctypes.c_size_t(0), out=FAKE)
