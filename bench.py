@@ -19,8 +19,10 @@ in HBM before timing starts.
 
 Also reported (measured outside the timed steps): bulk encode throughput of
 the same cache (4,194,304 keys and values) and of the 28-layer MSE prefill
-workload (1,835,008 bf16 keys at 4 and 8 bits), and the CPU oracle's decode
-throughput on a bounded sample on the host cores.
+workload (1,835,008 bf16 keys at 4 and 8 bits); the decode-call time of the
+128k-context needle workload (prod 4-bit keys, 4-bit values) and of the 16k
+grouped workload (4/2-bit grouped keys, 4-bit values); and the CPU oracle's
+decode throughput on a bounded sample on the host cores.
 """
 import argparse
 import hashlib
@@ -49,6 +51,8 @@ def parse():
                     help="untimed steps after the warm-up, until the GPU clocks have settled")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-encode-bench", action="store_true")
+    ap.add_argument("--no-other-decodes", action="store_true",
+                    help="skip the decode timings of the 128k needle and 16k grouped workloads")
     ap.add_argument("--cpu-groups", type=int, default=128,
                     help="(sequence, KV head) groups the CPU oracle decodes for its baseline")
     ap.add_argument("--profile-decode", type=int, default=0,
@@ -273,7 +277,9 @@ def main():
     extra = {}
     if not args.no_encode_bench:
         extra.update(encode_bench(tq, W, T, keys, vals, dev))
-    del keys, vals
+    del keys, vals, kp, vp
+    if not args.no_other_decodes:
+        extra.update(other_decodes(tq, W, dev))
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(args.cpu_groups)
@@ -348,6 +354,51 @@ def encode_bench(tq, W, T, keys, vals, dev, reps=10):
         res["encode_mse%d_prefill" % bits] = {"keys": n2, "ms": ms, "keys_per_s": n2 / (ms * 1e-3),
                                              "gbps": n2 * (2 * D + row) / (ms * 1e-3) / 1e9}
         del planes
+    return res
+
+
+def other_decodes(tq, W, dev, reps=50):
+    """Decode-call time of the two other decode workloads (not part of the
+    timed steps; settled clocks, HIP events over `reps` back-to-back calls):
+    1 x 8 x 32 heads at context 131072 with prod 4-bit keys and 4-bit values
+    (164 B per token-head), and 8 x 8 x 32 heads at context 16384 with grouped
+    (4-bit outlier half, 2-bit normal half) keys and 4-bit values (132 B)."""
+    import torch
+
+    res = {}
+    cases = [("decode_needle128k", dict(mode="prod", bits=4), 1, 131072, 4, None, 4, 164),
+             ("decode_grouped16k", dict(mode="grouped", bits_outlier=4, bits_normal=2), 8, 16384, 4,
+              W.w5_col_scale(), 5, 132)]
+    for name, kw, b, ctx, vbits, scale, wid, per in cases:
+        T = tq.Tables(tq.key_config(seed=42, **kw), dev)
+        n = b * HKV * ctx
+        keys = W.normal_bf16_device(wid, 1, (n, D), dev, scale_cols=scale)
+        kp = tq.encode_keys(T, keys)
+        del keys
+        vals = W.normal_bf16_device(wid, 2, (n, D), dev)
+        vp = tq.encode_values(vals, vbits)
+        del vals
+        q = W.normal_bf16_device(wid, 3, (1, b, HQ, D), dev)[0].contiguous()
+        ctx_len = torch.full((b,), ctx, dtype=torch.int32, device=dev)
+        dec = tq.Decoder(T, b, HQ, HKV, ctx, vbits, torch.bfloat16, dev)
+        out = torch.empty((b, HQ, D), dtype=torch.float32, device=dev)
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < 0.2:   # settle the clocks
+            for _ in range(20):
+                dec(q, ctx_len, kp, vp, out=out)
+            torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            dec(q, ctx_len, kp, vp, out=out)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        nbytes = n * per
+        res[name] = {"token_heads": n, "algorithmic_bytes": nbytes, "ms": ms,
+                     "kv_tokens_per_s": b * ctx / (ms * 1e-3), "gbps": nbytes / (ms * 1e-3) / 1e9,
+                     "frac_of_hbm_peak": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS}
+        del kp, vp, dec
     return res
 
 

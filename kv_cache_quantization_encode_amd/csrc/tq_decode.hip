@@ -35,6 +35,7 @@
 namespace {
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
 
 constexpr int KD = 128;
 #ifndef TQ_DEC_WAVES
@@ -502,11 +503,10 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
       const int v = hi * 16 + lo;
       if (v < S) {
         const float4 hi4 = halves[pos * 32 + 16 + hi];
-        const uint32_t e01 = (uint32_t)__half_as_ushort(__float2half_rn(lo4.x + hi4.x)) |
-                             ((uint32_t)__half_as_ushort(__float2half_rn(lo4.y + hi4.y)) << 16);
-        const uint32_t e23 = (uint32_t)__half_as_ushort(__float2half_rn(lo4.z + hi4.z)) |
-                             ((uint32_t)__half_as_ushort(__float2half_rn(lo4.w + hi4.w)) << 16);
-        dst[v] = make_uint2(e01, e23);
+        // round to nearest even, two heads per conversion
+        const half2_t e01 = __builtin_convertvector((float2_t){lo4.x + hi4.x, lo4.y + hi4.y}, half2_t);
+        const half2_t e23 = __builtin_convertvector((float2_t){lo4.z + hi4.z, lo4.w + hi4.w}, half2_t);
+        dst[v] = make_uint2(__builtin_bit_cast(uint32_t, e01), __builtin_bit_cast(uint32_t, e23));
       }
     }
   }
