@@ -134,6 +134,33 @@ tq_status tq_encode_keys(const tq_key_config* cfg, const void* tables,
                          void* stream);
 
 /*
+ * tq_encode_keys_batched -- tq_encode_keys for up to 32 independent key sets
+ * in one launch, e.g. the layers of a prefill, each quantised with its own
+ * tables (the "tqlite" README: every layer draws its rotation from its own
+ * seed).  All sets share cfg's mode and widths, dtype, n_vec, row_stride and
+ * n_records; entry i names the tables, key rows, slots and output planes of
+ * set i, with the meaning, layout and alignment rules of tq_encode_keys.  The
+ * outputs equal n_batch calls of tq_encode_keys, bit for bit; a launch of
+ * many small sets avoids paying a launch and a table staging per set.
+ *   batch    (host) array of n_batch entries, 0 <= n_batch <= 32.
+ * Errors: those of tq_encode_keys for any entry (nothing is launched then),
+ * TQ_ERR_ARG for n_batch outside [0, 32] or a NULL batch.
+ */
+typedef struct {
+  const void* tables;    /* device tables blob of this set (same mode and widths as cfg) */
+  const void* keys;      /* [n_vec rows] of dtype, row_stride elements apart            */
+  const int64_t* slots;  /* nullable, as in tq_encode_keys                              */
+  uint8_t* idx;
+  uint8_t* signs;        /* PROD only, else NULL                                        */
+  uint16_t* norm;
+  uint16_t* rnorm;       /* PROD only, else NULL                                        */
+} tq_key_batch;
+
+tq_status tq_encode_keys_batched(const tq_key_config* cfg, const tq_key_batch* batch, int32_t n_batch,
+                                 int32_t dtype, int64_t n_vec, int64_t row_stride, int64_t n_records,
+                                 void* stream);
+
+/*
  * tq_encode_values -- per-token group quantisation of n_vec value rows
  * (bit-packing article sec 二: 2-bit values four per byte; sec 三: 4-bit two per
  * byte).  For each group of `group` consecutive channels: s = fp16((max-min) /

@@ -24,7 +24,7 @@ TQ_MODE_MSE, TQ_MODE_PROD, TQ_MODE_GROUPED = 0, 1, 2
 TQ_F32, TQ_BF16, TQ_F16 = 0, 1, 2
 MODES = {"mse": TQ_MODE_MSE, "prod": TQ_MODE_PROD, "grouped": TQ_MODE_GROUPED}
 
-EXPORTED = ["tq_build_codebook", "tq_encode_keys", "tq_encode_values", "tq_append_kv", "tq_decode_attention",
+EXPORTED = ["tq_build_codebook", "tq_encode_keys", "tq_encode_keys_batched", "tq_encode_values", "tq_append_kv", "tq_decode_attention",
             "tq_decode_attention_paged", "tq_dequantize_keys", "tq_dequantize_values", "tq_channel_moments",
             "tq_status_string", "tq_idx_row_bytes"]
 
@@ -39,6 +39,13 @@ class KeyConfig(ctypes.Structure):
     _fields_ = [("d", ctypes.c_int32), ("mode", ctypes.c_int32), ("bits", ctypes.c_int32),
                 ("bits_outlier", ctypes.c_int32), ("bits_normal", ctypes.c_int32),
                 ("reserved", ctypes.c_int32), ("seed", ctypes.c_uint64)]
+
+
+class KeyBatch(ctypes.Structure):
+    """tq_key_batch: one key set of tq_encode_keys_batched."""
+    _fields_ = [("tables", ctypes.c_void_p), ("keys", ctypes.c_void_p), ("slots", ctypes.c_void_p),
+                ("idx", ctypes.c_void_p), ("signs", ctypes.c_void_p), ("norm", ctypes.c_void_p),
+                ("rnorm", ctypes.c_void_p)]
 
 
 def key_config(d=128, mode="prod", bits=3, seed=42, bits_outlier=4, bits_normal=2) -> KeyConfig:
@@ -62,6 +69,8 @@ def _load():
     lib.tq_encode_keys.argtypes = [CFG, P, P, I32, I64, I64, P, I64, P, P, P, P, P]
     lib.tq_encode_values.restype = I32
     lib.tq_encode_values.argtypes = [I32, I32, I32, P, I32, I64, I64, P, I64, P, P, P, P]
+    lib.tq_encode_keys_batched.restype = I32
+    lib.tq_encode_keys_batched.argtypes = [CFG, ctypes.POINTER(KeyBatch), I32, I32, I64, I64, I64, P]
     lib.tq_append_kv.restype = I32
     lib.tq_append_kv.argtypes = [CFG, P, P, P, I32, I64, I64, I64, P, I64, P, P, P, P, I32, I32, P, P, P, P]
     lib.tq_decode_attention.restype = I32

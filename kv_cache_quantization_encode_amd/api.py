@@ -9,7 +9,7 @@ import struct
 import numpy as np
 import torch
 
-from ._lib import (TQ_BF16, TQ_F16, TQ_F32, TQ_MODE_GROUPED, TQ_MODE_PROD, KeyConfig, check,
+from ._lib import (TQ_BF16, TQ_F16, TQ_F32, TQ_MODE_GROUPED, TQ_MODE_PROD, KeyBatch, KeyConfig, check,
                    key_config, lib)
 
 _DT = {torch.float32: TQ_F32, torch.bfloat16: TQ_BF16, torch.float16: TQ_F16}
@@ -127,6 +127,34 @@ def encode_values(values: torch.Tensor, bits: int, group: int = 32, planes: dict
                               _ptr(slots), n_records, _ptr(planes["codes"]), _ptr(planes["scale"]),
                               _ptr(planes["zero"]), _stream())
     check("tq_encode_values", st)
+    return planes
+
+
+def encode_keys_batched(tables: list, keys: list, planes: list | None = None, slots: list | None = None,
+                        n_records: int | None = None) -> list:
+    """tq_encode_keys for several key sets (e.g. the layers of a prefill, each
+    with its own Tables of one config) in one launch.  keys: list of [n, d]
+    tensors of one shape, dtype and row stride; returns (or fills) one plane
+    dict per set, equal to what encode_keys writes."""
+    nb = len(tables)
+    assert nb == len(keys) and nb > 0
+    k0 = keys[0]
+    assert k0.dim() == 2 and k0.stride(1) == 1
+    for k in keys:
+        assert k.shape == k0.shape and k.dtype == k0.dtype and k.stride() == k0.stride()
+    n = k0.shape[0]
+    if planes is None:
+        rec = n if n_records is None else n_records
+        planes = [key_planes(t, rec, k0.device) for t in tables]
+    if n_records is None:
+        n_records = planes[0]["idx"].shape[0]
+    slots = slots or [None] * nb
+    arr = (KeyBatch * nb)(*[KeyBatch(_ptr(t.dev), _ptr(k), _ptr(sl), _ptr(p["idx"]), _ptr(p.get("signs")),
+                                     _ptr(p["norm"]), _ptr(p.get("rnorm")))
+                            for t, k, p, sl in zip(tables, keys, planes, slots)])
+    st = lib.tq_encode_keys_batched(ctypes.byref(tables[0].cfg), arr, nb, _DT[k0.dtype], n, k0.stride(0),
+                                    n_records, _stream())
+    check("tq_encode_keys_batched", st)
     return planes
 
 

@@ -551,6 +551,21 @@ __global__ __launch_bounds__(256) void encode_values_kernel(ValArgs a) {
   encode_values_body<BITS, DT>(a, blockIdx.x, gridDim.x);
 }
 
+// Several independent key sets (one per layer, each with its own tables) in
+// one launch: entries take consecutive runs of blocks_per_entry blocks.
+constexpr int MAX_KEY_BATCH = 32;
+struct KeyBatchArgs {
+  KeyArgs e[MAX_KEY_BATCH];  // read in place from the kernel arguments
+  int blocks_per_entry;
+};
+static_assert(sizeof(KeyBatchArgs) <= 4096, "kernel arguments stay within 4 KiB");
+
+template <int MODE, int DT>
+__global__ __launch_bounds__(WAVES * 64, 2) void encode_keys_batched_kernel(KeyBatchArgs b) {
+  const int ent = blockIdx.x / b.blocks_per_entry;
+  encode_keys_body<MODE, DT>(b.e[ent], blockIdx.x - ent * b.blocks_per_entry, b.blocks_per_entry);
+}
+
 // Keys and values of the same tokens in one launch: the first key_blocks
 // blocks encode the keys, the rest the values, side by side.
 static_assert(WAVES * 64 == 256, "key and value blocks share one block size");
@@ -697,6 +712,51 @@ extern "C" tq_status tq_encode_values(int32_t bits, int32_t group, int32_t d, co
   if (bits == 2) TQ_LAUNCH_VALS(2);
   else TQ_LAUNCH_VALS(4);
 #undef TQ_LAUNCH_VALS
+  return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_HIP;
+}
+
+extern "C" tq_status tq_encode_keys_batched(const tq_key_config* cfg, const tq_key_batch* batch,
+                                           int32_t n_batch, int32_t dtype, int64_t n_vec,
+                                           int64_t row_stride, int64_t n_records, void* stream) {
+  if (n_batch < 0 || n_batch > MAX_KEY_BATCH || (n_batch > 0 && !batch)) return TQ_ERR_ARG;
+  tq::Parts P;
+  KeyBatchArgs b;
+  bool empty = false;
+  if (n_batch == 0) {  // nothing to encode; the shared arguments are still checked
+    tq_status st = tq::describe(cfg, &P);
+    if (st != TQ_OK) return st;
+    return n_vec < 0 || n_records < 0 ? TQ_ERR_ARG : TQ_OK;
+  }
+  for (int i = 0; i < n_batch; ++i) {
+    KeyArgs a;
+    tq_status st = key_args(cfg, batch[i].tables, batch[i].keys, dtype, n_vec, row_stride, batch[i].slots,
+                            n_records, batch[i].idx, batch[i].signs, batch[i].norm, batch[i].rnorm, P, a,
+                            empty);
+    if (st != TQ_OK) return st;
+    if (empty) return TQ_OK;
+    b.e[i] = a;
+  }
+  const int cus = tq::cu_count();
+  if (cus <= 0) return TQ_ERR_HIP;
+  // the single-set grid, shared out among the entries (at least one block each)
+  const int n_tiles = b.e[0].n_tiles;
+  int per = key_blocks(P, n_tiles, cus) / n_batch;
+  const int want = (n_tiles + WAVES - 1) / WAVES;
+  if (per > want) per = want;
+  if (per < 1) per = 1;
+  b.blocks_per_entry = per;
+  const dim3 grid((unsigned)(per * n_batch)), block(WAVES * 64);
+  hipStream_t s = (hipStream_t)stream;
+#define TQ_LAUNCH_KB(M)                                                                           \
+  do {                                                                                            \
+    if (dtype == TQ_F32) hipLaunchKernelGGL((encode_keys_batched_kernel<M, TQ_F32>), grid, block, 0, s, b);      \
+    else if (dtype == TQ_BF16) hipLaunchKernelGGL((encode_keys_batched_kernel<M, TQ_BF16>), grid, block, 0, s, b); \
+    else hipLaunchKernelGGL((encode_keys_batched_kernel<M, TQ_F16>), grid, block, 0, s, b);            \
+  } while (0)
+  if (P.mode == TQ_MODE_MSE) TQ_LAUNCH_KB(TQ_MODE_MSE);
+  else if (P.mode == TQ_MODE_PROD) TQ_LAUNCH_KB(TQ_MODE_PROD);
+  else TQ_LAUNCH_KB(TQ_MODE_GROUPED);
+#undef TQ_LAUNCH_KB
   return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_HIP;
 }
 

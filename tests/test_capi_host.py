@@ -209,6 +209,29 @@ def test_append_kv_argument_errors():
     assert _app(prod, dtype=9) == L.TQ_ERR_ARG
 
 
+def _kb(n_batch, cfg=None, entry=None, batch=True):
+    cfg = cfg or L.key_config(mode="prod", bits=3)
+    e = dict(tables=FAKE, keys=FAKE, slots=None, idx=FAKE, signs=FAKE, norm=FAKE, rnorm=FAKE)
+    e.update(entry or {})
+    arr = (L.KeyBatch * max(n_batch, 1))(*[L.KeyBatch(**e) for _ in range(max(n_batch, 1))])
+    return L.lib.tq_encode_keys_batched(ctypes.byref(cfg), arr if batch else None, n_batch, L.TQ_BF16, 64,
+                                        128, 64, None)
+
+
+def test_encode_keys_batched_argument_errors():
+    """Every entry is checked as tq_encode_keys checks its arguments, on the
+    host, before anything is launched."""
+    assert _kb(0) == L.TQ_OK
+    assert _kb(-1) == L.TQ_ERR_ARG
+    assert _kb(33) == L.TQ_ERR_ARG                                   # at most 32 sets
+    assert _kb(2, batch=False) == L.TQ_ERR_ARG
+    assert _kb(3, entry=dict(keys=None)) == L.TQ_ERR_ARG
+    assert _kb(3, entry=dict(keys=FAKE + 2)) == L.TQ_ERR_ARG         # misaligned rows
+    assert _kb(3, entry=dict(signs=None)) == L.TQ_ERR_ARG            # PROD needs signs
+    assert _kb(2, cfg=L.key_config(mode="mse", bits=4)) == L.TQ_ERR_ARG   # MSE must not pass signs
+    assert _kb(2, cfg=L.key_config(d=64, mode="prod", bits=3)) == L.TQ_ERR_UNSUPPORTED
+
+
 def _dec(cfg, **kw):
     a = dict(q=FAKE, B=2, Hq=8, Hkv=2, ctx=FAKE, max_ctx=1024, vb=2, vg=32, ws=None,
              wsb=ctypes.c_size_t(0), out=FAKE)
