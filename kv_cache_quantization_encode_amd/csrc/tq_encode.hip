@@ -738,9 +738,12 @@ extern "C" tq_status tq_encode_keys_batched(const tq_key_config* cfg, const tq_k
   }
   const int cus = tq::cu_count();
   if (cus <= 0) return TQ_ERR_HIP;
-  // the single-set grid, shared out among the entries (at least one block each)
+  // A few blocks per CU shared out among the entries (at least one block
+  // each).  The batch as a whole is a long launch, where four blocks per CU
+  // suit the MSE and grouped encoders better than the two of a single short
+  // set (measured on MI355X: 28 sets of 65536 MSE keys, 0.188 -> 0.175 ms).
   const int n_tiles = b.e[0].n_tiles;
-  int per = key_blocks(P, n_tiles, cus) / n_batch;
+  int per = cus * (P.mode == TQ_MODE_PROD ? 8 : 4) / n_batch;
   const int want = (n_tiles + WAVES - 1) / WAVES;
   if (per > want) per = want;
   if (per < 1) per = 1;
