@@ -316,8 +316,10 @@ def encode_bench(tq, W, T, keys, vals, dev, reps=10):
     import torch
 
     def timed(fn):
-        fn()
-        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < 0.1:   # settle the clocks
+            fn()
+            torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(reps):
