@@ -199,10 +199,153 @@ __device__ inline void store_idx(int w, uint8_t* dst, const int* q) {
   }
 }
 
-// MODE: TQ_MODE_MSE / PROD / GROUPED.  DT: input dtype.  Block `bid` of `nb`
-// blocks that share the key tiles.
-template <int MODE, int DT>
-__device__ __forceinline__ void encode_keys_body(const KeyArgs& a, int bid, int nb) {
+// ---------------------------------------------------------------- values
+// A wave encodes 16 rows per tile, four at a time: lane l handles 8
+// consecutive channels of row 16 tile + 4 j + l / 16; the four lanes of one
+// 32-channel group agree on min and max through two xor shuffles.
+struct ValArgs {
+  const void* values;
+  long long n_vec;
+  long long row_stride;
+  const long long* slots;
+  long long n_records;
+  uint8_t* codes;
+  uint16_t* scale;
+  uint16_t* zero;
+  long long n_tiles;
+};
+
+// Block `bid` of `nb` blocks (of 256 threads) that share the value tiles.
+template <int BITS, int DT>
+__device__ __forceinline__ void encode_values_body(const ValArgs& a, int bid, int nb) {
+  const int lane = threadIdx.x & 63;
+  const int sub = lane & 15;          // 8-channel chunk within the row
+  const long long tiles_per_grid = (long long)nb * (blockDim.x >> 6);
+  for (long long tile = (long long)bid * (blockDim.x >> 6) + (threadIdx.x >> 6);
+       tile < a.n_tiles; tile += tiles_per_grid) {
+    // sixteen rows per wave: all four loads go out before any is used
+    float vv[4][8];
+    long long slots[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const long long row = tile * 16 + 4 * j + (lane >> 4);
+      const long long rr = row < a.n_vec ? row : a.n_vec - 1;
+      load8<DT>(a.values, rr * a.row_stride + 8 * sub, vv[j]);
+      slots[j] = a.slots ? a.slots[rr] : row;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const long long row = tile * 16 + 4 * j + (lane >> 4);
+      const bool valid = row < a.n_vec;
+      float v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = valid ? vv[j][i] : 0.0f;
+      float mn = v[0], mx = v[0];
+#pragma unroll
+      for (int i = 1; i < 8; ++i) {
+        mn = fminf(mn, v[i]);
+        mx = fmaxf(mx, v[i]);
+      }
+      mn = fminf(mn, __shfl_xor(mn, 1));
+      mx = fmaxf(mx, __shfl_xor(mx, 1));
+      mn = fminf(mn, __shfl_xor(mn, 2));
+      mx = fmaxf(mx, __shfl_xor(mx, 2));
+      constexpr float LEVELS = (float)((1 << BITS) - 1);
+      const float s32 = __fdiv_rn(__fsub_rn(mx, mn), LEVELS);
+      const __half s16 = __float2half_rn(s32);
+      const __half z16 = __float2half_rn(mn);
+      const float s = __half2float(s16), z = __half2float(z16);
+      // code = rint((v - z) / s) with the correctly rounded quotient.  x * rcp(s)
+      // lies within 2^-22 |q| of the exact quotient, and so does the rounded
+      // one.  Quotients that matter lie in [-1, 2^BITS], so unless q is within
+      // 1e-5 of a half-integer both round to the same code; a lane with such a
+      // q redoes its eight codes with full divisions.
+      const float rs = __builtin_amdgcn_rcpf(s);
+      float c[8], x[8];
+      bool near = false;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        x[i] = __fsub_rn(v[i], z);
+        const float q = x[i] * rs;
+        c[i] = rintf(q);
+        near |= fabsf(q - c[i]) > 0.5f - 1e-5f;
+      }
+      if (near) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) c[i] = rintf(__fdiv_rn(x[i], s));
+      }
+      uint32_t packed = 0;
+      if (s != 0.0f) {
+        // codes packed in float arithmetic: c 2^(BITS i) is exact below 2^24
+        float lo = 0.0f, hi = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          lo = fmaf(__builtin_amdgcn_fmed3f(c[i], 0.0f, LEVELS), (float)(1u << (BITS * i)), lo);
+          hi = fmaf(__builtin_amdgcn_fmed3f(c[4 + i], 0.0f, LEVELS), (float)(1u << (BITS * i)), hi);
+        }
+        packed = (uint32_t)lo | ((uint32_t)hi << (4 * BITS));
+      }
+      const long long slot = slots[j];
+      if (valid && slot >= 0 && slot < a.n_records) {
+        if (BITS == 2) {
+          *(uint16_t*)(a.codes + slot * (KD * BITS / 8) + 2 * sub) = (uint16_t)packed;
+        } else {
+          *(uint32_t*)(a.codes + slot * (KD * BITS / 8) + 4 * sub) = packed;
+        }
+        if ((sub & 3) == 0) {
+          a.scale[slot * (KD / 32) + (sub >> 2)] = __half_as_ushort(s16);
+          a.zero[slot * (KD / 32) + (sub >> 2)] = __half_as_ushort(z16);
+        }
+      }
+    }
+  }
+}
+
+// Launch kinds of the key encoder: one key set; up to MAX_KEY_BATCH sets, each
+// with its own tables (entries take consecutive runs of blocks_per_entry
+// blocks); or one key set and the value rows of the same tokens (the first
+// key_blocks blocks take the keys, the rest the values).  The encoder body is
+// written once, in the kernel itself: moved into a device function it was
+// compiled to 198 instead of 166 VGPRs (2 instead of 3 waves per SIMD).
+enum { KEYS_ONE = 0, KEYS_BATCH = 1, KEYS_AND_VALUES = 2 };
+constexpr int MAX_KEY_BATCH = 32;
+template <int KIND> struct KeyLaunch { KeyArgs k; };
+template <> struct KeyLaunch<KEYS_BATCH> {
+  KeyArgs e[MAX_KEY_BATCH];  // read in place from the kernel arguments
+  int blocks_per_entry;
+};
+template <> struct KeyLaunch<KEYS_AND_VALUES> {
+  KeyArgs k;
+  ValArgs v;
+  int key_blocks;
+};
+static_assert(sizeof(KeyLaunch<KEYS_BATCH>) <= 4096, "kernel arguments stay within 4 KiB");
+
+template <int KIND>
+__device__ __forceinline__ const KeyArgs& key_set(const KeyLaunch<KIND>& L, int ent) {
+  if constexpr (KIND == KEYS_BATCH) return L.e[ent];
+  else return L.k;
+}
+
+// MODE: TQ_MODE_MSE / PROD / GROUPED.  DT: input dtype.  VB: value bits
+// (KEYS_AND_VALUES only).
+template <int MODE, int DT, int KIND, int VB>
+__global__ __launch_bounds__(WAVES * 64, 2) void encode_keys_kernel(KeyLaunch<KIND> L) {
+  if constexpr (KIND == KEYS_AND_VALUES) {
+    if ((int)blockIdx.x >= L.key_blocks) {
+      encode_values_body<VB, DT>(L.v, blockIdx.x - L.key_blocks, gridDim.x - L.key_blocks);
+      return;
+    }
+  }
+  int ent = 0, bid = blockIdx.x, nb = gridDim.x;
+  if constexpr (KIND == KEYS_BATCH) {
+    ent = blockIdx.x / L.blocks_per_entry;
+    bid = blockIdx.x - ent * L.blocks_per_entry;
+    nb = L.blocks_per_entry;
+  } else if constexpr (KIND == KEYS_AND_VALUES) {
+    nb = L.key_blocks;
+  }
+  const KeyArgs& a = key_set<KIND>(L, ent);
   const tq_blob_header* H = (const tq_blob_header*)a.tables;
   constexpr int NP = MODE == TQ_MODE_GROUPED ? 2 : 1;
   __shared__ __align__(16) tq_hint s_hint[NP][TQ_MAX_HINT];
@@ -439,140 +582,9 @@ __device__ __forceinline__ void encode_keys_body(const KeyArgs& a, int bid, int 
   }
 }
 
-// ---------------------------------------------------------------- values
-// A wave encodes 16 rows per tile, four at a time: lane l handles 8
-// consecutive channels of row 16 tile + 4 j + l / 16; the four lanes of one
-// 32-channel group agree on min and max through two xor shuffles.
-struct ValArgs {
-  const void* values;
-  long long n_vec;
-  long long row_stride;
-  const long long* slots;
-  long long n_records;
-  uint8_t* codes;
-  uint16_t* scale;
-  uint16_t* zero;
-  long long n_tiles;
-};
-
-// Block `bid` of `nb` blocks (of 256 threads) that share the value tiles.
-template <int BITS, int DT>
-__device__ __forceinline__ void encode_values_body(const ValArgs& a, int bid, int nb) {
-  const int lane = threadIdx.x & 63;
-  const int sub = lane & 15;          // 8-channel chunk within the row
-  const long long tiles_per_grid = (long long)nb * (blockDim.x >> 6);
-  for (long long tile = (long long)bid * (blockDim.x >> 6) + (threadIdx.x >> 6);
-       tile < a.n_tiles; tile += tiles_per_grid) {
-    // sixteen rows per wave: all four loads go out before any is used
-    float vv[4][8];
-    long long slots[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const long long row = tile * 16 + 4 * j + (lane >> 4);
-      const long long rr = row < a.n_vec ? row : a.n_vec - 1;
-      load8<DT>(a.values, rr * a.row_stride + 8 * sub, vv[j]);
-      slots[j] = a.slots ? a.slots[rr] : row;
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const long long row = tile * 16 + 4 * j + (lane >> 4);
-      const bool valid = row < a.n_vec;
-      float v[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = valid ? vv[j][i] : 0.0f;
-      float mn = v[0], mx = v[0];
-#pragma unroll
-      for (int i = 1; i < 8; ++i) {
-        mn = fminf(mn, v[i]);
-        mx = fmaxf(mx, v[i]);
-      }
-      mn = fminf(mn, __shfl_xor(mn, 1));
-      mx = fmaxf(mx, __shfl_xor(mx, 1));
-      mn = fminf(mn, __shfl_xor(mn, 2));
-      mx = fmaxf(mx, __shfl_xor(mx, 2));
-      constexpr float LEVELS = (float)((1 << BITS) - 1);
-      const float s32 = __fdiv_rn(__fsub_rn(mx, mn), LEVELS);
-      const __half s16 = __float2half_rn(s32);
-      const __half z16 = __float2half_rn(mn);
-      const float s = __half2float(s16), z = __half2float(z16);
-      // code = rint((v - z) / s) with the correctly rounded quotient.  x * rcp(s)
-      // lies within 2^-22 |q| of the exact quotient, and so does the rounded
-      // one.  Quotients that matter lie in [-1, 2^BITS], so unless q is within
-      // 1e-5 of a half-integer both round to the same code; a lane with such a
-      // q redoes its eight codes with full divisions.
-      const float rs = __builtin_amdgcn_rcpf(s);
-      float c[8], x[8];
-      bool near = false;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        x[i] = __fsub_rn(v[i], z);
-        const float q = x[i] * rs;
-        c[i] = rintf(q);
-        near |= fabsf(q - c[i]) > 0.5f - 1e-5f;
-      }
-      if (near) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) c[i] = rintf(__fdiv_rn(x[i], s));
-      }
-      uint32_t packed = 0;
-      if (s != 0.0f) {
-        // codes packed in float arithmetic: c 2^(BITS i) is exact below 2^24
-        float lo = 0.0f, hi = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          lo = fmaf(__builtin_amdgcn_fmed3f(c[i], 0.0f, LEVELS), (float)(1u << (BITS * i)), lo);
-          hi = fmaf(__builtin_amdgcn_fmed3f(c[4 + i], 0.0f, LEVELS), (float)(1u << (BITS * i)), hi);
-        }
-        packed = (uint32_t)lo | ((uint32_t)hi << (4 * BITS));
-      }
-      const long long slot = slots[j];
-      if (valid && slot >= 0 && slot < a.n_records) {
-        if (BITS == 2) {
-          *(uint16_t*)(a.codes + slot * (KD * BITS / 8) + 2 * sub) = (uint16_t)packed;
-        } else {
-          *(uint32_t*)(a.codes + slot * (KD * BITS / 8) + 4 * sub) = packed;
-        }
-        if ((sub & 3) == 0) {
-          a.scale[slot * (KD / 32) + (sub >> 2)] = __half_as_ushort(s16);
-          a.zero[slot * (KD / 32) + (sub >> 2)] = __half_as_ushort(z16);
-        }
-      }
-    }
-  }
-}
-
-template <int MODE, int DT>
-__global__ __launch_bounds__(WAVES * 64, 2) void encode_keys_kernel(KeyArgs a) {
-  encode_keys_body<MODE, DT>(a, blockIdx.x, gridDim.x);
-}
-
 template <int BITS, int DT>
 __global__ __launch_bounds__(256) void encode_values_kernel(ValArgs a) {
   encode_values_body<BITS, DT>(a, blockIdx.x, gridDim.x);
-}
-
-// Several independent key sets (one per layer, each with its own tables) in
-// one launch: entries take consecutive runs of blocks_per_entry blocks.
-constexpr int MAX_KEY_BATCH = 32;
-struct KeyBatchArgs {
-  KeyArgs e[MAX_KEY_BATCH];  // read in place from the kernel arguments
-  int blocks_per_entry;
-};
-static_assert(sizeof(KeyBatchArgs) <= 4096, "kernel arguments stay within 4 KiB");
-
-template <int MODE, int DT>
-__global__ __launch_bounds__(WAVES * 64, 2) void encode_keys_batched_kernel(KeyBatchArgs b) {
-  const int ent = blockIdx.x / b.blocks_per_entry;
-  encode_keys_body<MODE, DT>(b.e[ent], blockIdx.x - ent * b.blocks_per_entry, b.blocks_per_entry);
-}
-
-// Keys and values of the same tokens in one launch: the first key_blocks
-// blocks encode the keys, the rest the values, side by side.
-static_assert(WAVES * 64 == 256, "key and value blocks share one block size");
-template <int MODE, int BITS, int DT>
-__global__ __launch_bounds__(256, 2) void append_kv_kernel(KeyArgs ka, ValArgs va, int key_blocks) {
-  if ((int)blockIdx.x < key_blocks) encode_keys_body<MODE, DT>(ka, blockIdx.x, key_blocks);
-  else encode_values_body<BITS, DT>(va, blockIdx.x - key_blocks, gridDim.x - key_blocks);
 }
 
 int grid_for(long long tiles, int per_block) {
@@ -679,11 +691,12 @@ extern "C" tq_status tq_encode_keys(const tq_key_config* cfg, const void* tables
   if (cus <= 0) return TQ_ERR_HIP;
   const dim3 grid((unsigned)key_blocks(P, a.n_tiles, cus)), block(WAVES * 64);
   hipStream_t s = (hipStream_t)stream;
-#define TQ_LAUNCH_KEYS(M)                                                                   \
-  do {                                                                                      \
-    if (dtype == TQ_F32) hipLaunchKernelGGL((encode_keys_kernel<M, TQ_F32>), grid, block, 0, s, a);      \
-    else if (dtype == TQ_BF16) hipLaunchKernelGGL((encode_keys_kernel<M, TQ_BF16>), grid, block, 0, s, a); \
-    else hipLaunchKernelGGL((encode_keys_kernel<M, TQ_F16>), grid, block, 0, s, a);            \
+  const KeyLaunch<KEYS_ONE> L{a};
+#define TQ_LAUNCH_KEYS(M)                                                                                  \
+  do {                                                                                                     \
+    if (dtype == TQ_F32) hipLaunchKernelGGL((encode_keys_kernel<M, TQ_F32, KEYS_ONE, 0>), grid, block, 0, s, L);      \
+    else if (dtype == TQ_BF16) hipLaunchKernelGGL((encode_keys_kernel<M, TQ_BF16, KEYS_ONE, 0>), grid, block, 0, s, L); \
+    else hipLaunchKernelGGL((encode_keys_kernel<M, TQ_F16, KEYS_ONE, 0>), grid, block, 0, s, L);            \
   } while (0)
   if (P.mode == TQ_MODE_MSE) TQ_LAUNCH_KEYS(TQ_MODE_MSE);
   else if (P.mode == TQ_MODE_PROD) TQ_LAUNCH_KEYS(TQ_MODE_PROD);
@@ -720,7 +733,7 @@ extern "C" tq_status tq_encode_keys_batched(const tq_key_config* cfg, const tq_k
                                            int64_t row_stride, int64_t n_records, void* stream) {
   if (n_batch < 0 || n_batch > MAX_KEY_BATCH || (n_batch > 0 && !batch)) return TQ_ERR_ARG;
   tq::Parts P;
-  KeyBatchArgs b;
+  KeyLaunch<KEYS_BATCH> b;
   bool empty = false;
   if (n_batch == 0) {  // nothing to encode; the shared arguments are still checked
     tq_status st = tq::describe(cfg, &P);
@@ -750,11 +763,11 @@ extern "C" tq_status tq_encode_keys_batched(const tq_key_config* cfg, const tq_k
   b.blocks_per_entry = per;
   const dim3 grid((unsigned)(per * n_batch)), block(WAVES * 64);
   hipStream_t s = (hipStream_t)stream;
-#define TQ_LAUNCH_KB(M)                                                                           \
-  do {                                                                                            \
-    if (dtype == TQ_F32) hipLaunchKernelGGL((encode_keys_batched_kernel<M, TQ_F32>), grid, block, 0, s, b);      \
-    else if (dtype == TQ_BF16) hipLaunchKernelGGL((encode_keys_batched_kernel<M, TQ_BF16>), grid, block, 0, s, b); \
-    else hipLaunchKernelGGL((encode_keys_batched_kernel<M, TQ_F16>), grid, block, 0, s, b);            \
+#define TQ_LAUNCH_KB(M)                                                                                     \
+  do {                                                                                                      \
+    if (dtype == TQ_F32) hipLaunchKernelGGL((encode_keys_kernel<M, TQ_F32, KEYS_BATCH, 0>), grid, block, 0, s, b);      \
+    else if (dtype == TQ_BF16) hipLaunchKernelGGL((encode_keys_kernel<M, TQ_BF16, KEYS_BATCH, 0>), grid, block, 0, s, b); \
+    else hipLaunchKernelGGL((encode_keys_kernel<M, TQ_F16, KEYS_BATCH, 0>), grid, block, 0, s, b);            \
   } while (0)
   if (P.mode == TQ_MODE_MSE) TQ_LAUNCH_KB(TQ_MODE_MSE);
   else if (P.mode == TQ_MODE_PROD) TQ_LAUNCH_KB(TQ_MODE_PROD);
@@ -785,11 +798,13 @@ extern "C" tq_status tq_append_kv(const tq_key_config* cfg, const void* tables, 
   const long long blocks = (long long)kb + grid_for(va.n_tiles, 4);
   const dim3 grid((unsigned)blocks), block(256);
   hipStream_t s = (hipStream_t)stream;
-#define TQ_LAUNCH_KV(M, B)                                                                          \
-  do {                                                                                              \
-    if (dtype == TQ_F32) hipLaunchKernelGGL((append_kv_kernel<M, B, TQ_F32>), grid, block, 0, s, ka, va, kb);  \
-    else if (dtype == TQ_BF16) hipLaunchKernelGGL((append_kv_kernel<M, B, TQ_BF16>), grid, block, 0, s, ka, va, kb); \
-    else hipLaunchKernelGGL((append_kv_kernel<M, B, TQ_F16>), grid, block, 0, s, ka, va, kb);          \
+  const KeyLaunch<KEYS_AND_VALUES> L{ka, va, kb};
+  static_assert(WAVES * 64 == 256, "key and value blocks share one block size");
+#define TQ_LAUNCH_KV(M, B)                                                                                     \
+  do {                                                                                                         \
+    if (dtype == TQ_F32) hipLaunchKernelGGL((encode_keys_kernel<M, TQ_F32, KEYS_AND_VALUES, B>), grid, block, 0, s, L);      \
+    else if (dtype == TQ_BF16) hipLaunchKernelGGL((encode_keys_kernel<M, TQ_BF16, KEYS_AND_VALUES, B>), grid, block, 0, s, L); \
+    else hipLaunchKernelGGL((encode_keys_kernel<M, TQ_F16, KEYS_AND_VALUES, B>), grid, block, 0, s, L);            \
   } while (0)
 #define TQ_LAUNCH_KV_M(M)               \
   do {                                  \
