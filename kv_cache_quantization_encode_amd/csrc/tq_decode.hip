@@ -616,16 +616,23 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
 #pragma unroll
           for (int k = 0; k < 4; ++k) zacc[hh][k] = fmaf(p[hh], zz[k], zacc[hh][k]);
         }
-        // weights p * scale as fp16, paired by token: [group][pair][head] = (w_even, w_odd);
+        // weights p * scale as fp16 (p rounded to fp16, then two heads per
+        // packed multiply), paired by token: [group][pair][head] = (w_even, w_odd);
         // the group stride is padded so that neither these stores nor the p.V
         // waves' 16-byte reads pile onto a few LDS banks
         uint16_t* wb16 = (uint16_t*)(wbuf + ((r & 1) * NS + pw) * WSLOT);
         const int pair = lane >> 1, odd = lane & 1;
+        const half2_t p01 = __builtin_convertvector((float2_t){p[0], p[1]}, half2_t);
+        const half2_t p23 = __builtin_convertvector((float2_t){p[2], p[3]}, half2_t);
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
-#pragma unroll
-          for (int hh = 0; hh < QH; ++hh)
-            wb16[(k * WGRP + pair * QH + hh) * 2 + odd] = __half_as_ushort(__float2half_rn(p[hh] * ss[k]));
+        for (int k = 0; k < 4; ++k) {
+          const half2_t s2 = {(_Float16)ss[k], (_Float16)ss[k]};
+          const half2_t w01 = p01 * s2, w23 = p23 * s2;
+          wb16[(k * WGRP + pair * QH + 0) * 2 + odd] = __builtin_bit_cast(uint32_t, w01) & 0xFFFFu;
+          wb16[(k * WGRP + pair * QH + 1) * 2 + odd] = __builtin_bit_cast(uint32_t, w01) >> 16;
+          wb16[(k * WGRP + pair * QH + 2) * 2 + odd] = __builtin_bit_cast(uint32_t, w23) & 0xFFFFu;
+          wb16[(k * WGRP + pair * QH + 3) * 2 + odd] = __builtin_bit_cast(uint32_t, w23) >> 16;
+        }
         if (lane == 0) {
 #pragma unroll
           for (int hh = 0; hh < QH; ++hh) abuf[((r & 1) * NS + pw) * QH + hh] = alpha[hh];
