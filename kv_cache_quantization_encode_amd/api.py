@@ -26,6 +26,71 @@ def _stream():
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
+# ---- argument checks.  The C ABI checks pointers, alignment and sizes it is
+# given, but it cannot see how large a tensor is: these checks keep every
+# buffer the kernels touch inside the tensors passed in.
+
+def _need(cond, msg):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _on_device(t, name, dtypes=None, contiguous=False):
+    _need(isinstance(t, torch.Tensor), "%s must be a torch tensor" % name)
+    _need(t.is_cuda, "%s must be on the GPU" % name)
+    _need(t.device.index == torch.cuda.current_device(),
+          "%s is on %s but the current device is cuda:%d" % (name, t.device, torch.cuda.current_device()))
+    if dtypes is not None:
+        dtypes = dtypes if isinstance(dtypes, (tuple, list)) else (dtypes,)
+        _need(t.dtype in dtypes, "%s has dtype %s, expected one of %s" % (name, t.dtype, list(dtypes)))
+    if contiguous:
+        _need(t.is_contiguous(), "%s must be contiguous" % name)
+
+
+def _check_rows(x, name, d=128):
+    _on_device(x, name, tuple(_DT))
+    _need(x.dim() == 2 and x.shape[1] == d and x.stride(1) == 1,
+          "%s must be [n, %d] with unit channel stride, got shape %s strides %s" % (name, d, tuple(x.shape),
+                                                                                 x.stride()))
+
+
+def _check_slots(slots, n, name="slots"):
+    if slots is not None:
+        _on_device(slots, name, torch.int64, contiguous=True)
+        _need(slots.numel() == n, "%s has %d entries for %d rows" % (name, slots.numel(), n))
+
+
+def _check_key_planes(tables, p, n_records):
+    mode = tables.mode
+    d = tables.cfg.d
+    _on_device(p["idx"], "idx plane", torch.uint8, contiguous=True)
+    _need(p["idx"].numel() >= n_records * tables.row_bytes,
+          "idx plane holds %d bytes, %d records need %d" % (p["idx"].numel(), n_records,
+                                                           n_records * tables.row_bytes))
+    _on_device(p["norm"], "norm plane", torch.float16, contiguous=True)
+    _need(p["norm"].numel() >= n_records * (2 if mode == TQ_MODE_GROUPED else 1), "norm plane too small")
+    if mode == TQ_MODE_PROD:
+        _need(p.get("signs") is not None and p.get("rnorm") is not None, "prod keys need signs and rnorm planes")
+        _on_device(p["signs"], "signs plane", torch.uint8, contiguous=True)
+        _need(p["signs"].numel() >= n_records * (d // 8), "signs plane too small")
+        _on_device(p["rnorm"], "rnorm plane", torch.float16, contiguous=True)
+        _need(p["rnorm"].numel() >= n_records, "rnorm plane too small")
+    else:
+        _need(p.get("signs") is None and p.get("rnorm") is None, "only prod keys have signs and rnorm planes")
+
+
+def _check_value_planes(p, bits, n_records, d=128, group=32):
+    _on_device(p["codes"], "codes plane", torch.uint8, contiguous=True)
+    _need(p["codes"].numel() >= n_records * d * bits // 8, "codes plane too small for %d records" % n_records)
+    for k in ("scale", "zero"):
+        _on_device(p[k], "%s plane" % k, torch.float16, contiguous=True)
+        _need(p[k].numel() >= n_records * (d // group), "%s plane too small for %d records" % (k, n_records))
+
+
+def _records(planes: dict, key: str, per_record: int) -> int:
+    return planes[key].numel() // per_record
+
+
 def idx_row_bytes(cfg: KeyConfig) -> int:
     return int(lib.tq_idx_row_bytes(ctypes.byref(cfg)))
 
@@ -101,12 +166,15 @@ def value_planes(bits: int, n_records: int, d=128, group=32, device="cuda") -> d
 def encode_keys(tables: Tables, keys: torch.Tensor, planes: dict | None = None, slots=None,
                 n_records: int | None = None) -> dict:
     """keys: [n, d] float32/bfloat16/float16 CUDA tensor (rows may be strided)."""
-    assert keys.dim() == 2 and keys.stride(1) == 1
+    _check_rows(keys, "keys", tables.cfg.d)
     n = keys.shape[0]
     if n_records is None:
-        n_records = n if planes is None else planes["idx"].shape[0]
+        n_records = n if planes is None else _records(planes, "idx", tables.row_bytes)
     if planes is None:
         planes = key_planes(tables, n_records, keys.device)
+    _check_key_planes(tables, planes, n_records)
+    _check_slots(slots, n)
+    _need(slots is not None or n <= n_records, "%d rows do not fit in %d records" % (n, n_records))
     st = lib.tq_encode_keys(ctypes.byref(tables.cfg), _ptr(tables.dev), _ptr(keys), _DT[keys.dtype],
                             n, keys.stride(0), _ptr(slots), n_records, _ptr(planes["idx"]),
                             _ptr(planes.get("signs")), _ptr(planes["norm"]), _ptr(planes.get("rnorm")),
@@ -117,12 +185,16 @@ def encode_keys(tables: Tables, keys: torch.Tensor, planes: dict | None = None, 
 
 def encode_values(values: torch.Tensor, bits: int, group: int = 32, planes: dict | None = None,
                   slots=None, n_records: int | None = None) -> dict:
-    assert values.dim() == 2 and values.stride(1) == 1
+    _check_rows(values, "values", values.shape[-1] if values.dim() == 2 else 128)
     n, d = values.shape
+    _need(bits in (2, 4), "value bits must be 2 or 4")
     if n_records is None:
-        n_records = n if planes is None else planes["codes"].shape[0]
+        n_records = n if planes is None else _records(planes, "codes", d * bits // 8)
     if planes is None:
         planes = value_planes(bits, n_records, d, group, values.device)
+    _check_value_planes(planes, bits, n_records, d, group)
+    _check_slots(slots, n)
+    _need(slots is not None or n <= n_records, "%d rows do not fit in %d records" % (n, n_records))
     st = lib.tq_encode_values(bits, group, d, _ptr(values), _DT[values.dtype], n, values.stride(0),
                               _ptr(slots), n_records, _ptr(planes["codes"]), _ptr(planes["scale"]),
                               _ptr(planes["zero"]), _stream())
@@ -137,18 +209,26 @@ def encode_keys_batched(tables: list, keys: list, planes: list | None = None, sl
     tensors of one shape, dtype and row stride; returns (or fills) one plane
     dict per set, equal to what encode_keys writes."""
     nb = len(tables)
-    assert nb == len(keys) and nb > 0
+    _need(nb == len(keys) and 0 < nb <= 32, "need 1..32 key sets, one Tables per set")
     k0 = keys[0]
-    assert k0.dim() == 2 and k0.stride(1) == 1
-    for k in keys:
-        assert k.shape == k0.shape and k.dtype == k0.dtype and k.stride() == k0.stride()
+    for i, k in enumerate(keys):
+        _check_rows(k, "keys[%d]" % i, tables[0].cfg.d)
+        _need(k.shape == k0.shape and k.dtype == k0.dtype and k.stride() == k0.stride(),
+              "every key set needs the shape, dtype and strides of the first")
+        _need(tables[i].mode == tables[0].mode and tables[i].row_bytes == tables[0].row_bytes,
+              "every Tables must have the first one's mode and widths")
     n = k0.shape[0]
     if planes is None:
         rec = n if n_records is None else n_records
         planes = [key_planes(t, rec, k0.device) for t in tables]
     if n_records is None:
-        n_records = planes[0]["idx"].shape[0]
+        n_records = min(_records(pl, "idx", tables[0].row_bytes) for pl in planes)
     slots = slots or [None] * nb
+    _need(len(planes) == nb and len(slots) == nb, "one plane dict and one slot map (or None) per set")
+    for t, pl, sl in zip(tables, planes, slots):
+        _check_key_planes(t, pl, n_records)
+        _check_slots(sl, n)
+        _need(sl is not None or n <= n_records, "%d rows do not fit in %d records" % (n, n_records))
     arr = (KeyBatch * nb)(*[KeyBatch(_ptr(t.dev), _ptr(k), _ptr(sl), _ptr(p["idx"]), _ptr(p.get("signs")),
                                      _ptr(p["norm"]), _ptr(p.get("rnorm")))
                             for t, k, p, sl in zip(tables, keys, planes, slots)])
@@ -163,11 +243,17 @@ def append_kv(tables: Tables, keys: torch.Tensor, values: torch.Tensor, v_bits: 
     """Encode keys and values [n, d] (same dtype) of the same tokens into the
     key planes kp and value planes vp in one launch (tq_append_kv); the
     planes equal those of encode_keys + encode_values."""
-    assert keys.dim() == 2 and keys.stride(1) == 1 and values.dim() == 2 and values.stride(1) == 1
-    assert keys.shape == values.shape and keys.dtype == values.dtype
+    _check_rows(keys, "keys", tables.cfg.d)
+    _check_rows(values, "values", tables.cfg.d)
+    _need(keys.shape == values.shape and keys.dtype == values.dtype, "keys and values need one shape and dtype")
+    _need(v_bits in (2, 4), "value bits must be 2 or 4")
     n = keys.shape[0]
     if n_records is None:
-        n_records = kp["idx"].shape[0]
+        n_records = min(_records(kp, "idx", tables.row_bytes), _records(vp, "codes", tables.cfg.d * v_bits // 8))
+    _check_key_planes(tables, kp, n_records)
+    _check_value_planes(vp, v_bits, n_records, tables.cfg.d, group)
+    _check_slots(slots, n)
+    _need(slots is not None or n <= n_records, "%d rows do not fit in %d records" % (n, n_records))
     st = lib.tq_append_kv(ctypes.byref(tables.cfg), _ptr(tables.dev), _ptr(keys), _ptr(values),
                           _DT[keys.dtype], n, keys.stride(0), values.stride(0), _ptr(slots), n_records,
                           _ptr(kp["idx"]), _ptr(kp.get("signs")), _ptr(kp["norm"]), _ptr(kp.get("rnorm")),
@@ -178,12 +264,16 @@ def append_kv(tables: Tables, keys: torch.Tensor, values: torch.Tensor, v_bits: 
 def dequantize_keys(tables: Tables, planes: dict, n_vec: int | None = None, slots=None,
                     dtype=torch.float32, out=None):
     """Dense k_hat [n_vec, d] from the key planes (rows `slots`, or 0..n_vec-1)."""
-    n_records = planes["idx"].shape[0]
+    n_records = _records(planes, "idx", tables.row_bytes)
+    _check_key_planes(tables, planes, n_records)
     if n_vec is None:
         n_vec = n_records if slots is None else slots.shape[0]
+    _check_slots(slots, n_vec)
+    _need(slots is not None or n_vec <= n_records, "%d rows exceed the %d records" % (n_vec, n_records))
     if out is None:
         out = torch.empty((n_vec, tables.cfg.d), dtype=dtype, device=planes["idx"].device)
-    assert out.stride(1) == 1
+    _check_rows(out, "out", tables.cfg.d)
+    _need(out.shape[0] >= n_vec, "out has fewer than %d rows" % n_vec)
     st = lib.tq_dequantize_keys(ctypes.byref(tables.cfg), _ptr(tables.dev), n_vec, _ptr(slots), n_records,
                                 _ptr(planes["idx"]), _ptr(planes.get("signs")), _ptr(planes["norm"]),
                                 _ptr(planes.get("rnorm")), _ptr(out), _DT[out.dtype], out.stride(0), _stream())
@@ -194,13 +284,18 @@ def dequantize_keys(tables: Tables, planes: dict, n_vec: int | None = None, slot
 def dequantize_values(planes: dict, bits: int, n_vec: int | None = None, slots=None, dtype=torch.float32,
                       out=None, group: int = 32):
     """Dense v_hat [n_vec, d] from the value planes."""
-    n_records = planes["codes"].shape[0]
-    d = planes["codes"].shape[1] * 8 // bits
+    _need(bits in (2, 4), "value bits must be 2 or 4")
+    d = planes["codes"].shape[1] * 8 // bits if planes["codes"].dim() == 2 else 128
+    n_records = _records(planes, "codes", d * bits // 8)
+    _check_value_planes(planes, bits, n_records, d, group)
     if n_vec is None:
         n_vec = n_records if slots is None else slots.shape[0]
+    _check_slots(slots, n_vec)
+    _need(slots is not None or n_vec <= n_records, "%d rows exceed the %d records" % (n_vec, n_records))
     if out is None:
         out = torch.empty((n_vec, d), dtype=dtype, device=planes["codes"].device)
-    assert out.stride(1) == 1
+    _check_rows(out, "out", d)
+    _need(out.shape[0] >= n_vec, "out has fewer than %d rows" % n_vec)
     st = lib.tq_dequantize_values(bits, group, d, n_vec, _ptr(slots), n_records, _ptr(planes["codes"]),
                                   _ptr(planes["scale"]), _ptr(planes["zero"]), _ptr(out), _DT[out.dtype],
                                   out.stride(0), _stream())
@@ -210,7 +305,7 @@ def dequantize_values(planes: dict, bits: int, n_vec: int | None = None, slots=N
 
 def channel_moments(x: torch.Tensor) -> torch.Tensor:
     """float64 [2, d]: per-channel sum and sum of squares of the rows of x [n, d]."""
-    assert x.dim() == 2 and x.stride(1) == 1
+    _check_rows(x, "x", x.shape[-1] if x.dim() == 2 else 128)
     n, d = x.shape
     size = ctypes.c_size_t(0)
     check("tq_channel_moments", lib.tq_channel_moments(None, _DT[x.dtype], n, x.stride(0), d, None, None,
@@ -264,33 +359,53 @@ class Decoder:
         self.tables, self.B, self.Hq, self.Hkv, self.max_ctx, self.v_bits = tables, B, Hq, Hkv, max_ctx, v_bits
         self.page_size = page_size
         if page_size is not None:
-            assert max_ctx % page_size == 0
+            _need(page_size > 0 and max_ctx % page_size == 0, "max_ctx must be a multiple of page_size")
         self.ws_bytes = decode_workspace_bytes(tables, B, Hq, Hkv, max_ctx, q_dtype, v_bits, page_size)
         self.ws = torch.empty(max(self.ws_bytes, 16), dtype=torch.uint8, device=device)
 
     def __call__(self, q, ctx_len, kp: dict, vp: dict, sm_scale=None, out=None, lse=None,
                  scores=None, block_table=None):
+        _on_device(q, "q", tuple(_DT), contiguous=True)
+        _need(q.dim() == 3, "q must be [B, Hq, d]")
         B, Hq, d = q.shape
-        assert (B, Hq) == (self.B, self.Hq) and q.is_contiguous()
+        _need((B, Hq, d) == (self.B, self.Hq, self.tables.cfg.d), "q shape %s does not match the decoder's"
+              % (tuple(q.shape),))
+        _on_device(ctx_len, "ctx_len", torch.int32, contiguous=True)
+        _need(ctx_len.numel() == B, "ctx_len needs one entry per sequence")
         if sm_scale is None:
             sm_scale = 1.0 / math.sqrt(d)
         if out is None:
             out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+        _on_device(out, "out", torch.float32, contiguous=True)
+        _need(out.numel() >= B * Hq * d, "out must hold [B, Hq, d]")
+        if lse is not None:
+            _on_device(lse, "lse", torch.float32, contiguous=True)
+            _need(lse.numel() >= B * Hq, "lse must hold [B, Hq]")
+        if scores is not None:
+            _on_device(scores, "scores", torch.float32, contiguous=True)
+            _need(scores.numel() >= B * Hq * self.max_ctx, "scores must hold [B, Hq, max_ctx]")
+        n_rec = min(_records(kp, "idx", self.tables.row_bytes), _records(vp, "codes", d * self.v_bits // 8))
+        if self.page_size is None:
+            _need(n_rec >= B * self.Hkv * self.max_ctx, "the planes hold %d records, B * Hkv * max_ctx = %d"
+                  % (n_rec, B * self.Hkv * self.max_ctx))
+        _check_key_planes(self.tables, kp, n_rec)
+        _check_value_planes(vp, self.v_bits, n_rec, d)
         size = ctypes.c_size_t(self.ws.numel())
         keys = (_ptr(kp["idx"]), _ptr(kp.get("signs")), _ptr(kp["norm"]), _ptr(kp.get("rnorm")))
         vals = (self.v_bits, 32, _ptr(vp["codes"]), _ptr(vp["scale"]), _ptr(vp["zero"]))
         tail = (ctypes.c_float(sm_scale), _ptr(out), _ptr(lse), _ptr(scores), _ptr(self.ws),
                 ctypes.byref(size), _stream())
         if self.page_size is None:
-            assert block_table is None
+            _need(block_table is None, "a contiguous decoder takes no block table")
             st = lib.tq_decode_attention(ctypes.byref(self.tables.cfg), _ptr(self.tables.dev), _ptr(q),
                                          _DT[q.dtype], B, Hq, self.Hkv, _ptr(ctx_len), self.max_ctx,
                                          *keys, *vals, *tail)
             check("tq_decode_attention", st)
         else:
             nb = self.max_ctx // self.page_size
-            assert block_table is not None and block_table.dtype == torch.int32
-            assert block_table.is_contiguous() and tuple(block_table.shape) == (B, nb)
+            _need(block_table is not None, "a paged decoder needs the block table")
+            _on_device(block_table, "block_table", torch.int32, contiguous=True)
+            _need(tuple(block_table.shape) == (B, nb), "block_table must be [B, max_ctx // page_size]")
             st = lib.tq_decode_attention_paged(ctypes.byref(self.tables.cfg), _ptr(self.tables.dev), _ptr(q),
                                                _DT[q.dtype], B, Hq, self.Hkv, _ptr(ctx_len), _ptr(block_table),
                                                nb, self.page_size, *keys, *vals, *tail)

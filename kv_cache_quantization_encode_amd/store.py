@@ -77,7 +77,8 @@ class PagedKVCache:
         """Encode a chunk of new tokens, k and v [n, Hkv, d] (float32 / bf16 /
         fp16), straight into the sequence's pages."""
         n = k.shape[0]
-        assert k.shape[1] == self.Hkv and v.shape[:2] == k.shape[:2]
+        if k.dim() != 3 or k.shape[1] != self.Hkv or v.shape != k.shape:
+            raise ValueError("k and v must both be [n, Hkv=%d, d]" % self.Hkv)
         t0 = self.lengths[seq]
         self._grow(seq, t0 + n)
         sl = self.slots(seq, t0, n)
