@@ -208,7 +208,8 @@ tq_status tq_append_kv(const tq_key_config* cfg, const void* tables, const void*
  * The split-K scheme (partial max, sum and output per token chunk, merged in
  * a second kernel) keeps every result deterministic: no atomics.
  *   q          [B][Hq][d] of q_dtype, contiguous, 16-byte aligned.
- *   ctx_len    int32 [B]; each 0 <= ctx_len[b] <= max_ctx.  A sequence with
+ *   ctx_len    int32 [B]; each 0 <= ctx_len[b] <= max_ctx (values outside are
+ *              clamped into that range on the device).  A sequence with
  *              ctx_len 0 gets out = 0 and lse = -inf.
  *   key planes [B][Hkv][max_ctx] records, as written by tq_encode_keys with
  *              slot = (b*Hkv + h)*max_ctx + t.

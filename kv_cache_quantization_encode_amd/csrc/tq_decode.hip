@@ -240,7 +240,8 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: branches on it are scalar
   const int split = blockIdx.x, quad = blockIdx.y, bh = blockIdx.z;
   const int b = bh / a.Hkv, hkv = bh % a.Hkv;
-  const int ctx = a.ctx_len[b];
+  // lengths outside [0, max_ctx] are clamped into it: no read leaves the sequence's records
+  const int ctx = min(max(a.ctx_len[b], 0), a.max_ctx);
   const int t_begin = split * a.chunk;
   const int t_end = min(ctx, t_begin + a.chunk);
 

@@ -272,3 +272,25 @@ def test_end_to_end_gpu_encode_then_decode():
     for h in range(Hkv):
         _, o_ref, _ = O.decode_attention(qv[0, 4 * h:4 * h + 4].astype(np.float64), khat[0, h], vhat[0, h], N)
         P.check_out(out[0, 4 * h:4 * h + 4], o_ref)
+
+
+def test_decode_clamps_out_of_range_lengths():
+    """ctx_len outside [0, max_ctx] is clamped on the device: a length past
+    max_ctx decodes as max_ctx and a negative one as an empty sequence."""
+    kw = dict(mode="prod", bits=3)
+    B, Hq, Hkv, max_ctx = 2, 4, 1, 256
+    Tg = tq.Tables(L.key_config(seed=3, **kw), DEV)
+    n = B * Hkv * max_ctx
+    keys = torch.from_numpy(W.kv_rows(81, 1, n)[0]).to(DEV).to(torch.bfloat16)
+    vals = torch.from_numpy(W.kv_rows(81, 2, n)[0]).to(DEV).to(torch.bfloat16)
+    kp, vp = tq.encode_keys(Tg, keys), tq.encode_values(vals, 2)
+    q = torch.from_numpy(W.queries(81, B, Hq)[1].view(np.int16)).view(torch.bfloat16).to(DEV)
+    dec = tq.Decoder(Tg, B, Hq, Hkv, max_ctx, 2)
+    res = []
+    for ctx in ([max_ctx + 50, -3], [max_ctx, 0]):
+        lse = torch.empty((B, Hq), device=DEV)
+        out = dec(q, torch.tensor(ctx, dtype=torch.int32, device=DEV), kp, vp, lse=lse)
+        res.append((out.clone(), lse.clone()))
+    torch.cuda.synchronize()
+    assert torch.equal(res[0][0], res[1][0]) and torch.equal(res[0][1], res[1][1])
+    assert torch.all(res[0][0][1] == 0) and torch.all(torch.isinf(res[0][1][1]))
