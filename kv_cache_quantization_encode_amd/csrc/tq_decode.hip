@@ -557,11 +557,19 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
             A[3] = __builtin_amdgcn_fdot2(x23, e01, A[3], false);
           }
 #pragma unroll
-          for (int p = 0; p < F::P1; ++p) {
+          for (int p = 0; p < F::P1; p += (F::PROD ? 2 : 1)) {
             if (p % TQ_DEC_LOOKUP_BATCH == 0) __builtin_amdgcn_sched_barrier(0);
             const int byte = F::P0 + p;
             const uint2 e = lut_read(smem, (uint32_t)(F::E0 + p * F::S1) * 8u, kd.kw[byte >> 2], byte & 3);
-            const half2_t x01 = __builtin_bit_cast(half2_t, e.x), x23 = __builtin_bit_cast(half2_t, e.y);
+            half2_t x01 = __builtin_bit_cast(half2_t, e.x), x23 = __builtin_bit_cast(half2_t, e.y);
+            if constexpr (F::PROD) {
+              // QJL sign bytes two at a time: their fp16 entries are added in
+              // fp16 first (one packed add per head pair), halving the
+              // accumulate work of this smaller term of the score
+              const uint2 f = lut_read(smem, (uint32_t)(F::E0 + (p + 1) * F::S1) * 8u, kd.kw[(byte + 1) >> 2], (byte + 1) & 3);
+              x01 += __builtin_bit_cast(half2_t, f.x);
+              x23 += __builtin_bit_cast(half2_t, f.y);
+            }
             Bc[0] = __builtin_amdgcn_fdot2(x01, e10, Bc[0], false);
             Bc[1] = __builtin_amdgcn_fdot2(x01, e01, Bc[1], false);
             Bc[2] = __builtin_amdgcn_fdot2(x23, e10, Bc[2], false);
