@@ -36,15 +36,20 @@ def _need(cond, msg):
 
 
 def _on_device(t, name, dtypes=None, contiguous=False):
-    _need(isinstance(t, torch.Tensor), "%s must be a torch tensor" % name)
-    _need(t.is_cuda, "%s must be on the GPU" % name)
-    _need(t.device.index == torch.cuda.current_device(),
-          "%s is on %s but the current device is cuda:%d" % (name, t.device, torch.cuda.current_device()))
+    if not isinstance(t, torch.Tensor):
+        raise ValueError("%s must be a torch tensor" % name)
+    dev = t.get_device()
+    if dev < 0:
+        raise ValueError("%s must be on the GPU" % name)
+    if dev != torch.cuda.current_device():
+        raise ValueError("%s is on cuda:%d but the current device is cuda:%d" % (name, dev,
+                                                                              torch.cuda.current_device()))
     if dtypes is not None:
         dtypes = dtypes if isinstance(dtypes, (tuple, list)) else (dtypes,)
-        _need(t.dtype in dtypes, "%s has dtype %s, expected one of %s" % (name, t.dtype, list(dtypes)))
-    if contiguous:
-        _need(t.is_contiguous(), "%s must be contiguous" % name)
+        if t.dtype not in dtypes:
+            raise ValueError("%s has dtype %s, expected one of %s" % (name, t.dtype, list(dtypes)))
+    if contiguous and not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
 
 
 def _check_rows(x, name, d=128):
@@ -202,40 +207,55 @@ def encode_values(values: torch.Tensor, bits: int, group: int = 32, planes: dict
     return planes
 
 
+class KeyBatchEncoder:
+    """A prepared tq_encode_keys_batched launch: the key sets (e.g. the layers
+    of a prefill, each with its own Tables of one config), their output planes
+    and slot maps are checked once here; each call then only enqueues the
+    launch on the current stream (the tensors must stay alive and unchanged
+    in shape).  keys: list of [n, d] tensors of one shape, dtype and stride."""
+
+    def __init__(self, tables: list, keys: list, planes: list | None = None, slots: list | None = None,
+                 n_records: int | None = None):
+        nb = len(tables)
+        _need(nb == len(keys) and 0 < nb <= 32, "need 1..32 key sets, one Tables per set")
+        k0 = keys[0]
+        for i, k in enumerate(keys):
+            _check_rows(k, "keys[%d]" % i, tables[0].cfg.d)
+            _need(k.shape == k0.shape and k.dtype == k0.dtype and k.stride() == k0.stride(),
+                  "every key set needs the shape, dtype and strides of the first")
+            _need(tables[i].mode == tables[0].mode and tables[i].row_bytes == tables[0].row_bytes,
+                  "every Tables must have the first one's mode and widths")
+        n = k0.shape[0]
+        if planes is None:
+            rec = n if n_records is None else n_records
+            planes = [key_planes(t, rec, k0.device) for t in tables]
+        if n_records is None:
+            n_records = min(_records(pl, "idx", tables[0].row_bytes) for pl in planes)
+        slots = slots or [None] * nb
+        _need(len(planes) == nb and len(slots) == nb, "one plane dict and one slot map (or None) per set")
+        for t, pl, sl in zip(tables, planes, slots):
+            _check_key_planes(t, pl, n_records)
+            _check_slots(sl, n)
+            _need(sl is not None or n <= n_records, "%d rows do not fit in %d records" % (n, n_records))
+        self.planes = planes
+        self._keep = (list(tables), list(keys), list(slots))
+        self._arr = (KeyBatch * nb)(*[KeyBatch(_ptr(t.dev), _ptr(k), _ptr(sl), _ptr(p["idx"]),
+                                               _ptr(p.get("signs")), _ptr(p["norm"]), _ptr(p.get("rnorm")))
+                                      for t, k, p, sl in zip(tables, keys, planes, slots)])
+        self._args = (ctypes.byref(tables[0].cfg), self._arr, nb, _DT[k0.dtype], n, k0.stride(0), n_records)
+
+    def __call__(self) -> list:
+        check("tq_encode_keys_batched", lib.tq_encode_keys_batched(*self._args, _stream()))
+        return self.planes
+
+
 def encode_keys_batched(tables: list, keys: list, planes: list | None = None, slots: list | None = None,
                         n_records: int | None = None) -> list:
     """tq_encode_keys for several key sets (e.g. the layers of a prefill, each
-    with its own Tables of one config) in one launch.  keys: list of [n, d]
-    tensors of one shape, dtype and row stride; returns (or fills) one plane
-    dict per set, equal to what encode_keys writes."""
-    nb = len(tables)
-    _need(nb == len(keys) and 0 < nb <= 32, "need 1..32 key sets, one Tables per set")
-    k0 = keys[0]
-    for i, k in enumerate(keys):
-        _check_rows(k, "keys[%d]" % i, tables[0].cfg.d)
-        _need(k.shape == k0.shape and k.dtype == k0.dtype and k.stride() == k0.stride(),
-              "every key set needs the shape, dtype and strides of the first")
-        _need(tables[i].mode == tables[0].mode and tables[i].row_bytes == tables[0].row_bytes,
-              "every Tables must have the first one's mode and widths")
-    n = k0.shape[0]
-    if planes is None:
-        rec = n if n_records is None else n_records
-        planes = [key_planes(t, rec, k0.device) for t in tables]
-    if n_records is None:
-        n_records = min(_records(pl, "idx", tables[0].row_bytes) for pl in planes)
-    slots = slots or [None] * nb
-    _need(len(planes) == nb and len(slots) == nb, "one plane dict and one slot map (or None) per set")
-    for t, pl, sl in zip(tables, planes, slots):
-        _check_key_planes(t, pl, n_records)
-        _check_slots(sl, n)
-        _need(sl is not None or n <= n_records, "%d rows do not fit in %d records" % (n, n_records))
-    arr = (KeyBatch * nb)(*[KeyBatch(_ptr(t.dev), _ptr(k), _ptr(sl), _ptr(p["idx"]), _ptr(p.get("signs")),
-                                     _ptr(p["norm"]), _ptr(p.get("rnorm")))
-                            for t, k, p, sl in zip(tables, keys, planes, slots)])
-    st = lib.tq_encode_keys_batched(ctypes.byref(tables[0].cfg), arr, nb, _DT[k0.dtype], n, k0.stride(0),
-                                    n_records, _stream())
-    check("tq_encode_keys_batched", st)
-    return planes
+    with its own Tables of one config) in one launch; returns (or fills) one
+    plane dict per set, equal to what encode_keys writes.  For repeated
+    launches over the same tensors, KeyBatchEncoder checks them once."""
+    return KeyBatchEncoder(tables, keys, planes, slots, n_records)()
 
 
 def append_kv(tables: Tables, keys: torch.Tensor, values: torch.Tensor, v_bits: int, kp: dict, vp: dict,
