@@ -233,9 +233,9 @@ def test_decode_short_and_empty_contexts():
     _run_decode(dict(mode="prod", bits=3), 2, B=4, Hq=4, Hkv=1, max_ctx=300, ctx=[0, 1, 65, 300])
 
 
-def test_decode_fp32_queries():
-    _run_decode(dict(mode="prod", bits=3), 2, B=1, Hq=4, Hkv=1, max_ctx=1000, ctx=[999],
-                q_dtype=torch.float32)
+@pytest.mark.parametrize("q_dtype", [torch.float32, torch.float16], ids=["f32", "f16"])
+def test_decode_fp32_and_fp16_queries(q_dtype):
+    _run_decode(dict(mode="prod", bits=3), 2, B=1, Hq=4, Hkv=1, max_ctx=1000, ctx=[999], q_dtype=q_dtype)
 
 
 def test_decode_is_deterministic():
