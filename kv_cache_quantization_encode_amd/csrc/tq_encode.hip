@@ -23,6 +23,8 @@
 #include <hip/hip_runtime.h>
 #include <hip/hip_fp16.h>
 
+#include <atomic>
+
 #include "tq.h"
 #include "tq_internal.h"
 #include "tq_tables.h"
@@ -54,29 +56,6 @@ struct KeyArgs {
   int n_tiles;
 };
 
-template <int DT>
-__device__ inline void load8(const void* base, long long elem_off, float* out) {
-  if constexpr (DT == TQ_F32) {
-    const float4* p = (const float4*)((const float*)base + elem_off);
-    float4 a = p[0], b = p[1];
-    out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
-    out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
-  } else {
-    const uint4 v = *(const uint4*)((const uint16_t*)base + elem_off);
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      if constexpr (DT == TQ_BF16) {
-        out[2 * k] = __uint_as_float(w[k] << 16);
-        out[2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
-      } else {
-        out[2 * k] = __half2float(__ushort_as_half((unsigned short)(w[k] & 0xFFFFu)));
-        out[2 * k + 1] = __half2float(__ushort_as_half((unsigned short)(w[k] >> 16)));
-      }
-    }
-  }
-}
-
 // The 32 coordinates a lane loads of one key, as loaded (16-bit types: four
 // uint4; float32: eight), so that the next tile can be in flight while the
 // current one is encoded.
@@ -100,25 +79,32 @@ __device__ inline void load_raw(const void* base, long long row_off, int g, RawK
   }
 }
 
+// x[r] = sigma_r * (coordinate loaded into register r), the sign applied to
+// the bit pattern (sigmask bit r set: sigma_r = -1).  For bfloat16 the low
+// element is the shifted word plus the sign bit (adding 2^31 flips bit 31, so
+// shift and sign are one operation) and the high element is a mask and an
+// xor (again one operation).
 template <int DT>
-__device__ inline void unpack_raw(const RawKey<DT>& r, float* x) {
+__device__ inline void unpack_raw(const RawKey<DT>& r, uint32_t sigmask, float* x) {
+  auto sbit = [&](int i) { return ((sigmask >> i) & 1u) << 31; };
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     if constexpr (DT == TQ_F32) {
       const uint32_t w[8] = {r.v[2 * c].x, r.v[2 * c].y, r.v[2 * c].z, r.v[2 * c].w,
                              r.v[2 * c + 1].x, r.v[2 * c + 1].y, r.v[2 * c + 1].z, r.v[2 * c + 1].w};
 #pragma unroll
-      for (int k = 0; k < 8; ++k) x[8 * c + k] = __uint_as_float(w[k]);
+      for (int k = 0; k < 8; ++k) x[8 * c + k] = __uint_as_float(w[k] ^ sbit(8 * c + k));
     } else {
       const uint32_t w[4] = {r.v[c].x, r.v[c].y, r.v[c].z, r.v[c].w};
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
+        const int i = 8 * c + 2 * k;
         if constexpr (DT == TQ_BF16) {
-          x[8 * c + 2 * k] = __uint_as_float(w[k] << 16);
-          x[8 * c + 2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
+          x[i] = __uint_as_float((w[k] << 16) + sbit(i));
+          x[i + 1] = __uint_as_float((w[k] & 0xFFFF0000u) ^ sbit(i + 1));
         } else {
-          x[8 * c + 2 * k] = __half2float(__ushort_as_half((unsigned short)(w[k] & 0xFFFFu)));
-          x[8 * c + 2 * k + 1] = __half2float(__ushort_as_half((unsigned short)(w[k] >> 16)));
+          x[i] = __uint_as_float(__float_as_uint(__half2float(__ushort_as_half((unsigned short)(w[k] & 0xFFFFu)))) ^ sbit(i));
+          x[i + 1] = __uint_as_float(__float_as_uint(__half2float(__ushort_as_half((unsigned short)(w[k] >> 16)))) ^ sbit(i + 1));
         }
       }
     }
@@ -169,8 +155,9 @@ __device__ inline void stage_cross32(float* x) {
 }
 
 __device__ inline int bucketize(float y, const tq_hint* hint, int hn, float lo, float scale) {
-  float f = floorf((y - lo) * scale);
-  f = fminf(fmaxf(f, 0.0f), (float)(hn - 1));  // NaN -> 0 (fmax returns the number)
+  // grid bin floor((y - lo) * scale) clamped to [0, hn - 1]: clamped first,
+  // the conversion's truncation is the floor (NaN -> 0: fmax returns the number)
+  const float f = fminf(fmaxf((y - lo) * scale, 0.0f), (float)(hn - 1));
   const tq_hint* h = hint + (int)f;
   return h->h + (y >= h->t_h ? 1 : 0) + (y >= h->t_h1 ? 1 : 0);
 }
@@ -215,43 +202,101 @@ struct ValArgs {
   long long n_tiles;
 };
 
+// a / (2^BITS - 1) rounded to nearest even, for a >= 0, in three operations:
+// the quotient by the rounded reciprocal, its remainder (exact by fma), and
+// one correction.  For the divisors 3 and 15 this equals the IEEE quotient
+// for every finite a >= 0 (checked exhaustively over all 2^31 such floats on
+// the host with C fmaf); a = +inf keeps the IEEE result through the select.
+template <int BITS>
+__device__ inline float div_levels(float a) {
+  static_assert(BITS == 2 || BITS == 4, "checked for the divisors 3 and 15");
+  constexpr float L = (float)((1 << BITS) - 1);
+  constexpr float Y = 1.0f / L;
+  const float q0 = a * Y;
+  const float r = __builtin_fmaf(-q0, L, a);
+  const float q = __builtin_fmaf(r, Y, q0);
+  return a == __builtin_huge_valf() ? a : q;
+}
+
+// Eight channels of one row as loaded (16-bit types: one uint4; float32: two),
+// so that the next tile's rows can be in flight while this one is encoded.
+template <int DT>
+struct RawRow8 {
+  uint4 v[DT == TQ_F32 ? 2 : 1];
+};
+
+template <int DT>
+__device__ inline void load_row8(const void* base, long long elem_off, RawRow8<DT>& r) {
+  if constexpr (DT == TQ_F32) {
+    const uint4* p = (const uint4*)((const float*)base + elem_off);
+    r.v[0] = p[0];
+    r.v[1] = p[1];
+  } else {
+    r.v[0] = *(const uint4*)((const uint16_t*)base + elem_off);
+  }
+}
+
+template <int DT>
+__device__ inline void unpack_row8(const RawRow8<DT>& r, float* out) {
+  if constexpr (DT == TQ_F32) {
+    const uint32_t w[8] = {r.v[0].x, r.v[0].y, r.v[0].z, r.v[0].w, r.v[1].x, r.v[1].y, r.v[1].z, r.v[1].w};
+#pragma unroll
+    for (int k = 0; k < 8; ++k) out[k] = __uint_as_float(w[k]);
+  } else {
+    const uint32_t w[4] = {r.v[0].x, r.v[0].y, r.v[0].z, r.v[0].w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      if constexpr (DT == TQ_BF16) {
+        out[2 * k] = __uint_as_float(w[k] << 16);
+        out[2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
+      } else {
+        out[2 * k] = __half2float(__ushort_as_half((unsigned short)(w[k] & 0xFFFFu)));
+        out[2 * k + 1] = __half2float(__ushort_as_half((unsigned short)(w[k] >> 16)));
+      }
+    }
+  }
+}
+
 // Block `bid` of `nb` blocks (of 256 threads) that share the value tiles.
+// Each wave requests its next tile's rows before encoding the current one, so
+// that two tiles per wave are in flight.
 template <int BITS, int DT>
 __device__ __forceinline__ void encode_values_body(const ValArgs& a, int bid, int nb) {
   const int lane = threadIdx.x & 63;
   const int sub = lane & 15;          // 8-channel chunk within the row
   const long long tiles_per_grid = (long long)nb * (blockDim.x >> 6);
-  for (long long tile = (long long)bid * (blockDim.x >> 6) + (threadIdx.x >> 6);
-       tile < a.n_tiles; tile += tiles_per_grid) {
-    // sixteen rows per wave: all four loads go out before any is used
-    float vv[4][8];
-    long long slots[4];
+  RawRow8<DT> raw[4], raw_next[4];
+  auto request = [&](long long tile, RawRow8<DT>* r) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const long long row = tile * 16 + 4 * j + (lane >> 4);
       const long long rr = row < a.n_vec ? row : a.n_vec - 1;
-      load8<DT>(a.values, rr * a.row_stride + 8 * sub, vv[j]);
-      slots[j] = a.slots ? a.slots[rr] : row;
+      load_row8<DT>(a.values, rr * a.row_stride + 8 * sub, r[j]);
     }
+  };
+  long long tile = (long long)bid * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  if (tile < a.n_tiles) request(tile, raw);
+  for (; tile < a.n_tiles; tile += tiles_per_grid) {
+    if (tile + tiles_per_grid < a.n_tiles) request(tile + tiles_per_grid, raw_next);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const long long row = tile * 16 + 4 * j + (lane >> 4);
       const bool valid = row < a.n_vec;
       float v[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = valid ? vv[j][i] : 0.0f;
+      unpack_row8<DT>(raw[j], v);
       float mn = v[0], mx = v[0];
 #pragma unroll
       for (int i = 1; i < 8; ++i) {
         mn = fminf(mn, v[i]);
         mx = fmaxf(mx, v[i]);
       }
+      // the four lanes of a group: xor-1 and xor-2 exchanges
       mn = fminf(mn, __shfl_xor(mn, 1));
       mx = fmaxf(mx, __shfl_xor(mx, 1));
       mn = fminf(mn, __shfl_xor(mn, 2));
       mx = fmaxf(mx, __shfl_xor(mx, 2));
       constexpr float LEVELS = (float)((1 << BITS) - 1);
-      const float s32 = __fdiv_rn(__fsub_rn(mx, mn), LEVELS);
+      const float s32 = div_levels<BITS>(__fsub_rn(mx, mn));
       const __half s16 = __float2half_rn(s32);
       const __half z16 = __float2half_rn(mn);
       const float s = __half2float(s16), z = __half2float(z16);
@@ -262,15 +307,15 @@ __device__ __forceinline__ void encode_values_body(const ValArgs& a, int bid, in
       // q redoes its eight codes with full divisions.
       const float rs = __builtin_amdgcn_rcpf(s);
       float c[8], x[8];
-      bool near = false;
+      float dev = 0.0f;  // largest |q - rint(q)| of the lane
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         x[i] = __fsub_rn(v[i], z);
         const float q = x[i] * rs;
         c[i] = rintf(q);
-        near |= fabsf(q - c[i]) > 0.5f - 1e-5f;
+        dev = fmaxf(dev, fabsf(q - c[i]));
       }
-      if (near) {
+      if (dev > 0.5f - 1e-5f) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) c[i] = rintf(__fdiv_rn(x[i], s));
       }
@@ -285,8 +330,9 @@ __device__ __forceinline__ void encode_values_body(const ValArgs& a, int bid, in
         }
         packed = (uint32_t)lo | ((uint32_t)hi << (4 * BITS));
       }
-      const long long slot = slots[j];
-      if (valid && slot >= 0 && slot < a.n_records) {
+      // destination record (the slot table is read here, where it is used)
+      const long long slot = !valid ? -1 : a.slots ? a.slots[row] : row;
+      if (slot >= 0 && slot < a.n_records) {
         if (BITS == 2) {
           *(uint16_t*)(a.codes + slot * (KD * BITS / 8) + 2 * sub) = (uint16_t)packed;
         } else {
@@ -298,6 +344,8 @@ __device__ __forceinline__ void encode_values_body(const ValArgs& a, int bid, in
         }
       }
     }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) raw[j] = raw_next[j];
   }
 }
 
@@ -329,8 +377,13 @@ __device__ __forceinline__ const KeyArgs& key_set(const KeyLaunch<KIND>& L, int 
 
 // MODE: TQ_MODE_MSE / PROD / GROUPED.  DT: input dtype.  VB: value bits
 // (KEYS_AND_VALUES only).
+// Waves per SIMD the register allocation is held to: three (at most 168
+// VGPRs) for 16-bit inputs in MSE and PROD mode; two for GROUPED and float32
+// inputs, which need more registers and would spill at three.
+constexpr int key_waves_per_simd(int mode, int dt) { return mode == TQ_MODE_GROUPED || dt == TQ_F32 ? 2 : 3; }
+
 template <int MODE, int DT, int KIND, int VB>
-__global__ __launch_bounds__(WAVES * 64, 2) void encode_keys_kernel(KeyLaunch<KIND> L) {
+__global__ __launch_bounds__(WAVES * 64, key_waves_per_simd(MODE, DT)) void encode_keys_kernel(KeyLaunch<KIND> L) {
   if constexpr (KIND == KEYS_AND_VALUES) {
     if ((int)blockIdx.x >= L.key_blocks) {
       encode_values_body<VB, DT>(L.v, blockIdx.x - L.key_blocks, gridDim.x - L.key_blocks);
@@ -358,7 +411,8 @@ __global__ __launch_bounds__(WAVES * 64, 2) void encode_keys_kernel(KeyLaunch<KI
   const int g = lane >> 4;     // lane group: quarter of the key
   const int kk = lane & 15;    // key within the tile
 
-  // Rows past n_vec load the last row (kept in bounds) and encode zeros.
+  // Rows past n_vec load the last row (kept in bounds) and are encoded but
+  // never stored; keys do not mix in any step, the projection included.
   const int tile_step = nb * WAVES;
   auto row_of = [&](int tile) {
     const long long row = (long long)tile * TILE_KEYS + kk;
@@ -372,9 +426,21 @@ __global__ __launch_bounds__(WAVES * 64, 2) void encode_keys_kernel(KeyLaunch<KI
   // Formats with at most four cells (1- and 2-bit indices, one part) compare
   // against the boundaries directly (the bounds array pads with +inf); the
   // others look up a hint grid in LDS.
-  const bool direct = NP == 1 && H->part_levels[0] <= 4;
+  //
+  // Those small codebooks are symmetric (Gaussian Lloyd-Max), so their cells
+  // are equally wide about zero: boundaries {0} (two cells) or {-t, 0, t}
+  // (four cells).  The index is then floor(y / t + 2), resp. [y >= 0], taken
+  // as floor(clamp(fma(x, ua / n, ub), 0, levels - 1)) on the unscaled
+  // coordinate x = n y: three operations per coordinate.  It differs from the
+  // count of boundaries at or below y only where y is within a few ulps of a
+  // boundary.  A table that is not symmetric goes to the hint grid instead.
+  const int lev0 = H->part_levels[0];
   const float* bnd = (const float*)(a.tables + H->off_bounds[0]);
   const float bt0 = bnd[0], bt1 = bnd[1], bt2 = bnd[2];
+  const bool direct = NP == 1 && ((lev0 == 2 && bt0 == 0.0f) ||
+                                  (lev0 == 4 && bt1 == 0.0f && bt2 > 0.0f && bt0 == -bt2));
+  const float ua = lev0 == 2 ? 0x1p64f : 1.0f / bt2, ub = lev0 == 2 ? 1.0f : 2.0f;
+  const float utop = (float)(lev0 - 1);
   // sigma of the coordinates loaded into x[r]: 32 (r >> 3) + 8 g + (r & 7)
   float4 sg[8];
 #pragma unroll
@@ -447,12 +513,8 @@ __global__ __launch_bounds__(WAVES * 64, 2) void encode_keys_kernel(KeyLaunch<KI
     const bool valid = row < a.n_vec;
     const long long slot = a.slots ? a.slots[row_of(tile)] : row;
     float x[32];
-    unpack_raw<DT>(raw, x);
+    unpack_raw<DT>(raw, sigmask, x);
     raw = raw_next;
-    if (!valid) {
-#pragma unroll
-      for (int r = 0; r < 32; ++r) x[r] = 0.0f;
-    }
     // squared norm per part (part = register bit 4 in this layout)
     float ss0 = 0.0f, ss1 = 0.0f;
 #pragma unroll
@@ -462,9 +524,6 @@ __global__ __launch_bounds__(WAVES * 64, 2) void encode_keys_kernel(KeyLaunch<KI
     }
     ss0 = xor_sum(xor_sum(ss0, 16), 32);
     ss1 = xor_sum(xor_sum(ss1, 16), 32);
-#pragma unroll
-    for (int r = 0; r < 32; ++r)
-      x[r] = __uint_as_float(__float_as_uint(x[r]) ^ (((sigmask >> r) & 1u) << 31));
 
     stage_in_lane<1>(x);
     stage_in_lane<2>(x);
@@ -485,14 +544,15 @@ __global__ __launch_bounds__(WAVES * 64, 2) void encode_keys_kernel(KeyLaunch<KI
     const int part = MODE == TQ_MODE_GROUPED ? (g >> 1) : 0;
     const float n = n_part[part];
     const float inv = n > 0.0f ? 1.0f / n : 0.0f;
+    // x stays unscaled (y = x / n = x * inv where needed)
     int q[32];
     if (direct) {
-      // at most four cells: count the boundaries at or below y
+      // symmetric two- or four-cell codebook (see above); clamped to
+      // [0, levels - 1] first, the conversion's truncation is the floor.  A
+      // zero key (n = 0) gets fma(0, 0, ub): the cell of y = 0.
+      const float un = ua * inv;
 #pragma unroll
-      for (int r = 0; r < 32; ++r) {
-        x[r] *= inv;
-        q[r] = (x[r] >= bt0 ? 1 : 0) + (x[r] >= bt1 ? 1 : 0) + (x[r] >= bt2 ? 1 : 0);
-      }
+      for (int r = 0; r < 32; ++r) q[r] = (int)__builtin_amdgcn_fmed3f(fmaf(x[r], un, ub), 0.0f, utop);
     } else {
       const tq_hint* hint = s_hint[NP == 2 ? part : 0];
       const int hnn = NP == 2 ? hn[part] : hn[0];
@@ -502,8 +562,7 @@ __global__ __launch_bounds__(WAVES * 64, 2) void encode_keys_kernel(KeyLaunch<KI
       for (int r = 0; r < 32; ++r) {
         // eight hint reads in flight at a time (each holds three registers)
         if (r % 8 == 0) __builtin_amdgcn_sched_barrier(0);
-        x[r] *= inv;
-        q[r] = bucketize(x[r], hint, hnn, hl, hs);
+        q[r] = bucketize(x[r] * inv, hint, hnn, hl, hs);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -532,7 +591,7 @@ __global__ __launch_bounds__(WAVES * 64, 2) void encode_keys_kernel(KeyLaunch<KI
       half8 bhi[4], blo[4];
 #pragma unroll
       for (int r = 0; r < 32; ++r) {
-        const float res = x[r] - s_cent[q[r]];
+        const float res = fmaf(x[r], inv, -s_cent[q[r]]);
         rr = fmaf(res, res, rr);
         const _Float16 h = (_Float16)res;
         const _Float16 lo = (_Float16)(res - (float)h);
@@ -540,10 +599,12 @@ __global__ __launch_bounds__(WAVES * 64, 2) void encode_keys_kernel(KeyLaunch<KI
         blo[r >> 3][r & 7] = lo;
       }
       rr = xor_sum(xor_sum(rr, 16), 32);
-      // The fragment base is made opaque to the compiler each tile, so that it
-      // reads S from LDS per use instead of keeping all 32 fragments live.
-      const _Float16* sbase = s_S + kk * SPITCH + 32 * g;
-      asm volatile("" : "+v"(sbase));
+      // The fragment offset is made opaque to the compiler each tile, so that it
+      // reads S from LDS per use instead of keeping all 32 fragments live (an
+      // offset, not a pointer, so the reads stay LDS reads and not flat ones).
+      int soff = kk * SPITCH + 32 * g;
+      asm volatile("" : "+v"(soff));
+      const _Float16* sbase = s_S + soff;
       floatx4 acc[8];
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt) {
@@ -593,6 +654,37 @@ int grid_for(long long tiles, int per_block) {
   if (blocks > cap) blocks = cap;
   if (blocks < 1) blocks = 1;
   return (int)blocks;
+}
+
+#ifndef TQ_VAL_ROUNDS
+#define TQ_VAL_ROUNDS 1
+#endif
+// Blocks of the value encoder: one per four tiles, at most as many as the
+// device holds at once.  The blocks loop over the tiles, so a block that had
+// to wait for a free slot would run its whole share late.
+template <int BITS, int DT>
+int value_blocks(long long tiles, int cus) {
+  static std::atomic<int> resident{0};  // blocks per CU (occupancy of the kernel)
+  int r = resident.load(std::memory_order_relaxed);
+  if (r <= 0) {
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&r, encode_values_kernel<BITS, DT>, 256, 0) != hipSuccess ||
+        r <= 0) {
+      (void)hipGetLastError();
+      r = 4;
+    }
+    resident.store(r, std::memory_order_relaxed);
+  }
+  long long blocks = (tiles + 3) / 4;
+  const long long cap = (long long)cus * r * TQ_VAL_ROUNDS;
+  if (blocks > cap) blocks = cap;
+  if (blocks < 1) blocks = 1;
+  return (int)blocks;
+}
+
+template <int BITS, int DT>
+void launch_values(const ValArgs& a, int cus, hipStream_t s) {
+  hipLaunchKernelGGL((encode_values_kernel<BITS, DT>), dim3(value_blocks<BITS, DT>(a.n_tiles, cus)), dim3(256), 0,
+                     s, a);
 }
 
 // Argument checks and kernel arguments of the key encoder.  Returns TQ_OK with
@@ -714,17 +806,18 @@ extern "C" tq_status tq_encode_values(int32_t bits, int32_t group, int32_t d, co
   tq_status st = val_args(bits, group, d, values, dtype, n_vec, row_stride, slots, n_records, codes, scale,
                           zero, a, empty);
   if (st != TQ_OK || empty) return st;
-  const dim3 grid(grid_for(a.n_tiles, 4)), block(256);
+  const int cus = tq::cu_count();
+  if (cus <= 0) return TQ_ERR_HIP;
   hipStream_t s = (hipStream_t)stream;
-#define TQ_LAUNCH_VALS(B)                                                                   \
-  do {                                                                                      \
-    if (dtype == TQ_F32) hipLaunchKernelGGL((encode_values_kernel<B, TQ_F32>), grid, block, 0, s, a);  \
-    else if (dtype == TQ_BF16) hipLaunchKernelGGL((encode_values_kernel<B, TQ_BF16>), grid, block, 0, s, a); \
-    else hipLaunchKernelGGL((encode_values_kernel<B, TQ_F16>), grid, block, 0, s, a);          \
-  } while (0)
-  if (bits == 2) TQ_LAUNCH_VALS(2);
-  else TQ_LAUNCH_VALS(4);
-#undef TQ_LAUNCH_VALS
+  if (bits == 2) {
+    if (dtype == TQ_F32) launch_values<2, TQ_F32>(a, cus, s);
+    else if (dtype == TQ_BF16) launch_values<2, TQ_BF16>(a, cus, s);
+    else launch_values<2, TQ_F16>(a, cus, s);
+  } else {
+    if (dtype == TQ_F32) launch_values<4, TQ_F32>(a, cus, s);
+    else if (dtype == TQ_BF16) launch_values<4, TQ_BF16>(a, cus, s);
+    else launch_values<4, TQ_F16>(a, cus, s);
+  }
   return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_HIP;
 }
 

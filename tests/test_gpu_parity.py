@@ -44,7 +44,7 @@ def _gpu_key_fields(Tg, To, planes, rows=None):
 # ------------------------------------------------------------------ encode
 
 KEY_CFGS = [dict(mode="prod", bits=3), dict(mode="prod", bits=4), dict(mode="prod", bits=2),
-            dict(mode="mse", bits=4), dict(mode="mse", bits=8), dict(mode="mse", bits=1),
+            dict(mode="mse", bits=4), dict(mode="mse", bits=8), dict(mode="mse", bits=1), dict(mode="mse", bits=2),
             dict(mode="mse", bits=3), dict(mode="grouped", bits_outlier=4, bits_normal=2),
             dict(mode="grouped", bits_outlier=3, bits_normal=1)]
 
@@ -97,14 +97,23 @@ def test_encode_keys_strided_fp16_with_slots():
     assert np.all(_np(planes["signs"])[untouched] == 0xAB)
 
 
-def test_encode_zero_key():
-    Tg, To = _tables(dict(mode="prod", bits=3))
+@pytest.mark.parametrize("kw,cell", [(dict(mode="prod", bits=3), 2), (dict(mode="prod", bits=2), 1),
+                                     (dict(mode="mse", bits=2), 2), (dict(mode="mse", bits=4), 8)],
+                         ids=["prod3", "prod2", "mse2", "mse4"])
+def test_encode_zero_key(kw, cell):
+    """A zero key: norms 0, every y = 0 in the cell just above the middle
+    boundary (ties go up), and (prod) the signs of S(-c[idx]) as the oracle
+    gives them."""
+    Tg, To = _tables(kw)
     x = torch.zeros((16, 128), dtype=torch.bfloat16, device=DEV)
     planes = tq.encode_keys(Tg, x)
     torch.cuda.synchronize()
     f = _gpu_key_fields(Tg, To, planes)
-    assert np.all(f["norm16"] == 0) and np.all(f["rnorm16"] == 0)
-    assert np.all(f["idx"] == 2)   # y = 0 goes to the upper middle cell
+    assert np.all(f["norm16"] == 0)
+    assert np.all(f["idx"] == cell)
+    if kw["mode"] == "prod":
+        assert np.all(f["rnorm16"] == 0)
+        P.check_keys(np.zeros((16, 128)), To, f)
 
 
 @pytest.mark.parametrize("bits", [2, 4])
