@@ -170,9 +170,21 @@ __device__ inline void store_fields(uint8_t* dst, const int* q) {
   uint32_t* d = (uint32_t*)dst;
 #pragma unroll
   for (int k = 0; k < W; ++k) {
-    uint32_t v = 0;
+    uint32_t v;
+    if constexpr (W <= 2) {
+      // sixteen or more fields: one shift-or each (the empty asm keeps the
+      // chain from being regrouped into separate shifts and three-input ors)
+      v = (uint32_t)q[k * PER + PER - 1];
 #pragma unroll
-    for (int r = 0; r < PER; ++r) v |= (uint32_t)q[k * PER + r] << (W * r);
+      for (int r = PER - 2; r >= 0; --r) {
+        asm("" : "+v"(v));
+        v = (v << W) | (uint32_t)q[k * PER + r];
+      }
+    } else {
+      v = 0;
+#pragma unroll
+      for (int r = 0; r < PER; ++r) v |= (uint32_t)q[k * PER + r] << (W * r);
+    }
     d[k] = v;
   }
 }
@@ -616,23 +628,33 @@ __global__ __launch_bounds__(WAVES * 64, key_waves_per_simd(MODE, DT)) void enco
           acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(sf, bhi[ks], acc[nt], 0, 0, 0);
         }
       }
-      // lane holds projections of key kk onto S rows 16nt + 4g + i
+      // Lane holds projections of key kk onto S rows 16nt + 4g + i.  Their
+      // sign bits, shifted in one per funnel shift from (nt, i) = (7, 3) down
+      // to (0, 0), give T with bit 4nt + i set for a negative projection
+      // (bit = [z >= 0] is its complement; z = -0 reads as negative, a case
+      // within the zero band).
+      uint32_t T = 0;
+#pragma unroll
+      for (int nt = 7; nt >= 0; --nt)
+#pragma unroll
+        for (int i = 3; i >= 0; --i) T = __builtin_amdgcn_alignbit(T, __float_as_uint(acc[nt][i]), 31);
+      T = ~T;
+      // Sign dword w of the key holds rows 32w .. 32w+31: nibble 2w of T at
+      // bit 4g and nibble 2w+1 at bit 16 + 4g, from each lane group g.
       uint32_t dw[4];
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        uint32_t n0 = 0, n1 = 0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          n0 |= (acc[2 * w][i] >= 0.0f ? 1u : 0u) << i;
-          n1 |= (acc[2 * w + 1][i] >= 0.0f ? 1u : 0u) << i;
-        }
-        uint32_t v = (n0 << (4 * g)) | (n1 << (16 + 4 * g));
-        v |= __shfl_xor(v, 16);
-        v |= __shfl_xor(v, 32);
-        dw[w] = v;
+        const uint32_t byte = (T >> (8 * w)) & 0xFFu;
+        dw[w] = ((byte | (byte << 12)) & 0x000F000Fu) << (4 * g);
       }
+      // OR over the four lane groups, lane group g keeping dword g: swap
+      // halves with the group two away, then single dwords with the neighbour.
+      const int hg = g >> 1, bg = g & 1;
+      const uint32_t keep0 = hg ? dw[2] : dw[0], keep1 = hg ? dw[3] : dw[1];
+      const uint32_t give0 = hg ? dw[0] : dw[2], give1 = hg ? dw[1] : dw[3];
+      const uint32_t m0 = keep0 | __shfl_xor(give0, 32), m1 = keep1 | __shfl_xor(give1, 32);
+      const uint32_t mine = (bg ? m1 : m0) | __shfl_xor(bg ? m0 : m1, 16);
       if (store) {
-        const uint32_t mine = g == 0 ? dw[0] : g == 1 ? dw[1] : g == 2 ? dw[2] : dw[3];
         *(uint32_t*)(a.signs + slot * (KD / 8) + 4 * g) = mine;
         if (g == 0) {
           const float rho = n * sqrtf(rr) * inv_sqrt_d;
