@@ -71,6 +71,23 @@ def test_encode_keys_modes_bf16(kw):
     P.check_keys(kv.astype(np.float64), To, _gpu_key_fields(Tg, To, planes))
 
 
+@pytest.mark.parametrize("kw", [dict(mode="prod", bits=3), dict(mode="mse", bits=4), dict(mode="mse", bits=2),
+                                dict(mode="grouped", bits_outlier=4, bits_normal=2)],
+                         ids=["prod3", "mse4", "mse2", "grouped42"])
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+def test_encode_keys_modes_f32_f16(kw, dtype):
+    """The float32 and fp16 input paths (their own unpack and sign steps) in
+    the direct-bucketize, hint-grid and grouped encoders."""
+    n = 1000  # ragged
+    rng = np.random.default_rng(17)
+    scale = W.w5_col_scale() if kw["mode"] == "grouped" else np.ones(128)
+    x = (rng.standard_normal((n, 128)) * scale).astype(np.float32 if dtype == "f32" else np.float16)
+    Tg, To = _tables(kw, seed=77)
+    planes = tq.encode_keys(Tg, torch.from_numpy(x).to(DEV))
+    torch.cuda.synchronize()
+    P.check_keys(x.astype(np.float64), To, _gpu_key_fields(Tg, To, planes))
+
+
 def test_encode_keys_strided_fp16_with_slots():
     """fp16 rows with a row stride, written through a slot map that permutes,
     skips (-1 and out-of-range) and leaves other records untouched."""
@@ -117,13 +134,17 @@ def test_encode_zero_key(kw, cell):
 
 
 @pytest.mark.parametrize("bits", [2, 4])
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 def test_encode_values_exact(bits, dtype):
     n = 1001
     vv, vb = W.kv_rows(9, 2, n)
     if dtype == "f32":
         vv = W.gaussian(9, 3, (n, 128))
         x = torch.from_numpy(vv).to(DEV)
+    elif dtype == "f16":
+        vh = W.gaussian(9, 4, (n, 128)).astype(np.float16)
+        vv = vh.astype(np.float32)
+        x = torch.from_numpy(vh).to(DEV)
     else:
         x = torch.from_numpy(vb.view(np.int16)).view(torch.bfloat16).to(DEV)
     vv = vv.copy()
