@@ -435,14 +435,12 @@ __global__ __launch_bounds__(WAVES * 64, key_waves_per_simd(MODE, DT)) void enco
   int tile = bid * WAVES + wave;
   if (tile < a.n_tiles) load_raw<DT>(a.keys, row_of(tile) * a.row_stride, g, raw);
 
-  // Formats with at most four cells (1- and 2-bit indices, one part) compare
-  // against the boundaries directly (the bounds array pads with +inf); the
-  // others look up a hint grid in LDS.
-  //
-  // Those small codebooks are symmetric (Gaussian Lloyd-Max), so their cells
-  // are equally wide about zero: boundaries {0} (two cells) or {-t, 0, t}
-  // (four cells).  The index is then floor(y / t + 2), resp. [y >= 0], taken
-  // as floor(clamp(fma(x, ua / n, ub), 0, levels - 1)) on the unscaled
+  // Bucketize.  Formats with two or four cells and one part ("direct") take
+  // the index arithmetically; all others look up a hint grid in LDS.  Those
+  // small codebooks are symmetric (Gaussian Lloyd-Max), so their cells are
+  // equally wide about zero: boundaries {0} (two cells) or {-t, 0, t} (four
+  // cells).  The index is then [y >= 0], resp. floor(y / t + 2), taken as
+  // floor(clamp(fma(x, ua / n, ub), 0, levels - 1)) on the unscaled
   // coordinate x = n y: three operations per coordinate.  It differs from the
   // count of boundaries at or below y only where y is within a few ulps of a
   // boundary.  A table that is not symmetric goes to the hint grid instead.
