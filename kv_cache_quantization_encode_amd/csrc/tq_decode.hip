@@ -366,7 +366,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
   }
   if (tid < 32) {
     const int part = tid >> 4, k = tid & 15;
-    if (part < n_parts && k < (part ? lev1 : lev0)) cen[tid] = (part ? cent1 : cent0)[k];
+    cen[tid] = part < n_parts && k < (part ? lev1 : lev0) ? (part ? cent1 : cent0)[k] : 0.0f;
   }
   if (!F::GROUPED && tid < QH) amax[QH + tid] = 0;
   for (int i = tid; i < n_pages_wg; i += NT) L.pages[i] = a.block_table[(long long)b * a.max_blocks + lp0 + i];
@@ -547,8 +547,13 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
           // writes them so), so a byte is a table index as it stands.
 #pragma unroll
           for (int p = 0; p < F::P0; ++p) {
-            // cap the table reads in flight (each holds two registers)
-            if (p % TQ_DEC_LOOKUP_BATCH == 0) __builtin_amdgcn_sched_barrier(0);
+            // cap the table reads in flight (each holds two registers); the
+            // empty asm keeps each batch's accumulation ahead of the next
+            // batch instead of letting it sink below all the reads
+            if (p % TQ_DEC_LOOKUP_BATCH == 0) {
+              if (p > 0) asm volatile("" : "+v"(A[0]), "+v"(A[1]), "+v"(A[2]), "+v"(A[3]));
+              __builtin_amdgcn_sched_barrier(0);
+            }
             const uint2 e = lut_read(smem, (uint32_t)(p * F::S0) * 8u, kd.kw[p >> 2], p & 3);
             const half2_t x01 = __builtin_bit_cast(half2_t, e.x), x23 = __builtin_bit_cast(half2_t, e.y);
             A[0] = __builtin_amdgcn_fdot2(x01, e10, A[0], false);
@@ -558,7 +563,10 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
           }
 #pragma unroll
           for (int p = 0; p < F::P1; p += (F::PROD ? 2 : 1)) {
-            if (p % TQ_DEC_LOOKUP_BATCH == 0) __builtin_amdgcn_sched_barrier(0);
+            if (p % TQ_DEC_LOOKUP_BATCH == 0) {
+              if (p > 0) asm volatile("" : "+v"(Bc[0]), "+v"(Bc[1]), "+v"(Bc[2]), "+v"(Bc[3]));
+              __builtin_amdgcn_sched_barrier(0);
+            }
             const int byte = F::P0 + p;
             const uint2 e = lut_read(smem, (uint32_t)(F::E0 + p * F::S1) * 8u, kd.kw[byte >> 2], byte & 3);
             half2_t x01 = __builtin_bit_cast(half2_t, e.x), x23 = __builtin_bit_cast(half2_t, e.y);
@@ -578,8 +586,10 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
           const float4 h0 = *(const float4*)hmul, h1 = *(const float4*)(hmul + QH);
           const float mul0[QH] = {h0.x, h0.y, h0.z, h0.w}, mul1[QH] = {h1.x, h1.y, h1.z, h1.w};
 #pragma unroll
-          for (int hh = 0; hh < QH; ++hh)
-            sc[hh] = valid ? m0 * mul0[hh] * A[hh] + m1 * mul1[hh] * Bc[hh] : -INFINITY;
+          for (int hh = 0; hh < QH; ++hh) {
+            if constexpr (F::P1 > 0) sc[hh] = valid ? m0 * mul0[hh] * A[hh] + m1 * mul1[hh] * Bc[hh] : -INFINITY;
+            else sc[hh] = valid ? m0 * mul0[hh] * A[hh] : -INFINITY;  // MSE: one table class
+          }
           if (a.scores && valid) {
 #pragma unroll
             for (int hh = 0; hh < QH; ++hh) {
