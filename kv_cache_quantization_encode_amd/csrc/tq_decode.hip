@@ -706,8 +706,8 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
           const uint32_t wh[QH] = {wv.x, wv.y, wv.z, wv.w};
           uint32_t pairs[8];
           if (VB == 2) {
-            const uint32_t Y = cA | (cB << 16);
-            const uint32_t Y2 = __builtin_amdgcn_perm(0u, Y, 0x0c030c01u);  // bytes 1, 3 -> 0, 2
+            const uint32_t Y = __builtin_amdgcn_perm(cB, cA, 0x05040100u);   // A.lo16 | B.lo16 << 16
+            const uint32_t Y2 = __builtin_amdgcn_perm(cB, cA, 0x0c050c01u);  // A byte 1, B byte 1 -> bytes 0, 2
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               pairs[i] = Y & (0x00030003u << (2 * i));
