@@ -141,7 +141,11 @@ __device__ __forceinline__ uint2 lut_read(const unsigned char* smem, uint32_t BA
     }
     return *(const uint2*)(smem + off + BASE);
   } else {
-    off = (__builtin_amdgcn_ubfe(w, 8 * k, 8) << 3) + BASE;
+    // (the empty asm keeps the byte extract whole, so that shift and add
+    // become one v_lshl_or / v_lshl_add)
+    uint32_t b = __builtin_amdgcn_ubfe(w, 8 * k, 8);
+    asm("" : "+v"(b));
+    off = (b << 3) + BASE;
     return *(const uint2*)(smem + off);
   }
 }
@@ -556,10 +560,14 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
             }
             const uint2 e = lut_read(smem, (uint32_t)(p * F::S0) * 8u, kd.kw[p >> 2], p & 3);
             const half2_t x01 = __builtin_bit_cast(half2_t, e.x), x23 = __builtin_bit_cast(half2_t, e.y);
-            A[0] = __builtin_amdgcn_fdot2(x01, e10, A[0], false);
-            A[1] = __builtin_amdgcn_fdot2(x01, e01, A[1], false);
-            A[2] = __builtin_amdgcn_fdot2(x23, e10, A[2], false);
-            A[3] = __builtin_amdgcn_fdot2(x23, e01, A[3], false);
+            if (p == 0) {  // the first entries start the sums (the same values fdot2 onto 0 gives)
+              A[0] = (float)x01[0]; A[1] = (float)x01[1]; A[2] = (float)x23[0]; A[3] = (float)x23[1];
+            } else {
+              A[0] = __builtin_amdgcn_fdot2(x01, e10, A[0], false);
+              A[1] = __builtin_amdgcn_fdot2(x01, e01, A[1], false);
+              A[2] = __builtin_amdgcn_fdot2(x23, e10, A[2], false);
+              A[3] = __builtin_amdgcn_fdot2(x23, e01, A[3], false);
+            }
           }
 #pragma unroll
           for (int p = 0; p < F::P1; p += (F::PROD ? 2 : 1)) {
@@ -578,10 +586,14 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
               x01 += __builtin_bit_cast(half2_t, f.x);
               x23 += __builtin_bit_cast(half2_t, f.y);
             }
-            Bc[0] = __builtin_amdgcn_fdot2(x01, e10, Bc[0], false);
-            Bc[1] = __builtin_amdgcn_fdot2(x01, e01, Bc[1], false);
-            Bc[2] = __builtin_amdgcn_fdot2(x23, e10, Bc[2], false);
-            Bc[3] = __builtin_amdgcn_fdot2(x23, e01, Bc[3], false);
+            if (p == 0) {
+              Bc[0] = (float)x01[0]; Bc[1] = (float)x01[1]; Bc[2] = (float)x23[0]; Bc[3] = (float)x23[1];
+            } else {
+              Bc[0] = __builtin_amdgcn_fdot2(x01, e10, Bc[0], false);
+              Bc[1] = __builtin_amdgcn_fdot2(x01, e01, Bc[1], false);
+              Bc[2] = __builtin_amdgcn_fdot2(x23, e10, Bc[2], false);
+              Bc[3] = __builtin_amdgcn_fdot2(x23, e01, Bc[3], false);
+            }
           }
           const float4 h0 = *(const float4*)hmul, h1 = *(const float4*)(hmul + QH);
           const float mul0[QH] = {h0.x, h0.y, h0.z, h0.w}, mul1[QH] = {h1.x, h1.y, h1.z, h1.w};
