@@ -716,24 +716,23 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
           const uint32_t cA = cur[2 * k], cB = cur[2 * k + 1];
           const uint4 wv = *(const uint4*)(wsrc + grp * WGRP + pr * QH);
           const uint32_t wh[QH] = {wv.x, wv.y, wv.z, wv.w};
+          // pairs[i] holds, for the two tokens (low and high half), the
+          // prefix of channel i: the channels of its byte up to i, so that
+          // one byte permute serves a whole byte and the last prefix of each
+          // byte needs no mask.  The channel sums are told apart at the end.
           uint32_t pairs[8];
           if (VB == 2) {
-            const uint32_t Y = __builtin_amdgcn_perm(cB, cA, 0x05040100u);   // A.lo16 | B.lo16 << 16
-            const uint32_t Y2 = __builtin_amdgcn_perm(cB, cA, 0x0c050c01u);  // A byte 1, B byte 1 -> bytes 0, 2
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              pairs[i] = Y & (0x00030003u << (2 * i));
-              pairs[4 + i] = Y2 & (0x00030003u << (2 * i));
-            }
+            const uint32_t Y1 = __builtin_amdgcn_perm(cB, cA, 0x0c040c00u);  // byte 0 of A, of B -> bytes 0, 2
+            const uint32_t Y2 = __builtin_amdgcn_perm(cB, cA, 0x0c050c01u);  // byte 1 of A, of B -> bytes 0, 2
+            pairs[0] = Y1 & 0x00030003u; pairs[1] = Y1 & 0x000F000Fu; pairs[2] = Y1 & 0x003F003Fu; pairs[3] = Y1;
+            pairs[4] = Y2 & 0x00030003u; pairs[5] = Y2 & 0x000F000Fu; pairs[6] = Y2 & 0x003F003Fu; pairs[7] = Y2;
           } else {
-            const uint32_t Ylo = __builtin_amdgcn_perm(cB, cA, 0x05040100u);  // A.lo16 | B.lo16 << 16
-            const uint32_t Yhi = __builtin_amdgcn_perm(cB, cA, 0x07060302u);  // A.hi16 | B.hi16 << 16
-            const uint32_t Ylo2 = __builtin_amdgcn_perm(0u, Ylo, 0x0c030c01u);
-            const uint32_t Yhi2 = __builtin_amdgcn_perm(0u, Yhi, 0x0c030c01u);
-            pairs[0] = Ylo & 0x000F000Fu;  pairs[1] = Ylo & 0x00F000F0u;
-            pairs[2] = Ylo2 & 0x000F000Fu; pairs[3] = Ylo2 & 0x00F000F0u;
-            pairs[4] = Yhi & 0x000F000Fu;  pairs[5] = Yhi & 0x00F000F0u;
-            pairs[6] = Yhi2 & 0x000F000Fu; pairs[7] = Yhi2 & 0x00F000F0u;
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {  // byte b of A and of B -> bytes 0, 2
+              const uint32_t Yb = __builtin_amdgcn_perm(cB, cA, 0x0c000c00u | ((4u + b) << 16) | (uint32_t)b);
+              pairs[2 * b] = Yb & 0x000F000Fu;
+              pairs[2 * b + 1] = Yb;
+            }
           }
 #pragma unroll
           for (int hh = 0; hh < QH; ++hh) {
@@ -753,17 +752,28 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
         lds_barrier();
       }
     }
-    // undo the subnormal placement: dim i of a slice carries code * 2^-24 * step_i
+    // Undo the placement: accumulator i holds, in units of 2^-24, the
+    // prefix sum over the channels of its byte up to i, channel j weighted
+    // by its field's place value step_j; a channel's sum is the difference
+    // of consecutive prefixes over its place value.
 #pragma unroll
-    for (int hh = 0; hh < QH; ++hh)
+    for (int hh = 0; hh < QH; ++hh) {
+      float r[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const float step = VB == 2 ? (float)(1 << (2 * (i & 3))) : (float)(1 << (4 * (i & 1)));
-        float v = acc[hh][i];
-        v += __shfl_xor(v, 16);
-        v += __shfl_xor(v, 32);
+        r[i] = acc[hh][i];
+        r[i] += __shfl_xor(r[i], 16);
+        r[i] += __shfl_xor(r[i], 32);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        constexpr int PER = 8 / VB;  // channels per byte
+        const int f = i % PER;       // field within the byte
+        const float step = (float)(1 << (VB * f));
+        const float v = f == 0 ? r[i] : r[i] - r[i - 1];
         if (lane < 16) mine[hh * RS + 6 + 8 * u + i] = v * (16777216.0f / step);
       }
+    }
   }
   __syncthreads();
   for (int i = tid; i < QH * KD; i += NT) {
