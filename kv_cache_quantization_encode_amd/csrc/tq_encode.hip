@@ -315,22 +315,25 @@ __device__ __forceinline__ void encode_values_body(const ValArgs& a, int bid, in
       // code = rint((v - z) / s) with the correctly rounded quotient.  x * rcp(s)
       // lies within 2^-22 |q| of the exact quotient, and so does the rounded
       // one.  Quotients that matter lie in [-1, 2^BITS], so unless q is within
-      // 1e-5 of a half-integer both round to the same code; a lane with such a
-      // q redoes its eight codes with full divisions.
+      // 1e-5 of a half-integer both round to the same code; such a code is
+      // redone with a full division.
       const float rs = __builtin_amdgcn_rcpf(s);
       float c[8], x[8];
-      float dev = 0.0f;  // largest |q - rint(q)| of the lane
+      float dev[8];  // |q - rint(q)| per channel
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         x[i] = __fsub_rn(v[i], z);
         const float q = x[i] * rs;
         c[i] = rintf(q);
-        dev = fmaxf(dev, fabsf(q - c[i]));
+        dev[i] = fabsf(q - c[i]);
       }
-      if (dev > 0.5f - 1e-5f) {
+      // Per channel, so that a wave divides only where one of its lanes has
+      // that channel near a half-integer (bf16 inputs often put a quotient
+      // exactly on one; divisions for all eight channels would be taken by
+      // about a quarter of the row groups).
 #pragma unroll
-        for (int i = 0; i < 8; ++i) c[i] = rintf(__fdiv_rn(x[i], s));
-      }
+      for (int i = 0; i < 8; ++i)
+        if (dev[i] > 0.5f - 1e-5f) c[i] = rintf(__fdiv_rn(x[i], s));
       uint32_t packed = 0;
       if (s != 0.0f) {
         // codes packed in float arithmetic: c 2^(BITS i) is exact below 2^24
