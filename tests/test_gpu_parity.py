@@ -220,6 +220,13 @@ DEC_CASES = [
     (dict(mode="grouped", bits_outlier=4, bits_normal=2), 4),
     (dict(mode="mse", bits=2), 2),
     (dict(mode="mse", bits=3), 4),
+    # every other supported key format, with the other value width
+    (dict(mode="prod", bits=3), 4),
+    (dict(mode="mse", bits=1), 4),
+    (dict(mode="mse", bits=3), 2),
+    (dict(mode="grouped", bits_outlier=3, bits_normal=2), 2),
+    (dict(mode="grouped", bits_outlier=2, bits_normal=2), 4),
+    (dict(mode="grouped", bits_outlier=4, bits_normal=1), 2),
 ]
 
 
