@@ -9,19 +9,22 @@
 //   p = softmax(sm_scale s), out = sum_t p_t (code_t * scale_t + zero_t).
 //
 // One workgroup (16 waves) takes one (sequence, KV head, quad of query heads,
-// token chunk).  Its prologue rotates the four queries (q' = H sigma q by an
-// in-LDS butterfly), projects them (S q'), and turns them into lookup tables:
-// for every byte position p of a packed key and every byte value v, the four
-// heads' partial inner products over the coordinates that byte holds, as fp16.
-// A key's score is then one table read per packed byte (48 for a 3-bit prod
-// key) instead of 4 x 256 multiply-adds.  Each wave streams 64-token tiles:
-// lanes take tokens for the scores and the online softmax, then lanes take
-// 8-dim column slices for p.V, which runs on v_dot2_f32_f16 over token pairs
-// with the 2- or 4-bit codes placed directly in fp16 subnormal bit patterns
-// (code * 2^-24 * 4^k), so no conversion is spent per code.  The value scale
-// is folded into the weight (p * scale) and the zero point is summed
-// separately (sum_t p_t zero_t).  The chunk's (max, sum, unnormalised output)
-// goes to the workspace; a second kernel merges chunks in a fixed order.
+// token chunk).  Its prologue rotates the four queries (q' = H sigma q by
+// shuffle butterflies in registers), projects them (S q'), and turns them into
+// lookup tables: for every byte position p of a packed key and every byte
+// value v, the four heads' partial inner products over the coordinates that
+// byte holds, as fp16.  A key's score is then one table read per packed byte
+// (48 for a 3-bit prod key) instead of 4 x 256 multiply-adds.  Half of the
+// waves score 64-token tiles (lane = token) and run the online softmax; the
+// other half accumulate p.V for those tiles one round later (lane = token-pair
+// slot and 8-channel slice) on v_dot2_f32_f16 over token pairs, with the 2- or
+// 4-bit code fields left in place as fp16 subnormal bit patterns (a byte's
+// fields up to channel i, masked: prefix value * 2^-24), so no conversion is
+// spent per code and per-channel sums are differences of consecutive prefix
+// sums at the end.  The value scale is folded into the weight (p * scale) and
+// the zero point is summed separately (sum_t p_t zero_t).  The chunk's (max,
+// sum, unnormalised output) goes to the workspace; a second kernel merges
+// chunks in a fixed order.
 #include <hip/hip_runtime.h>
 #include <hip/hip_fp16.h>
 
