@@ -108,9 +108,12 @@ def gaussian_matrix(seed: int, tag: int, m: int, d: int) -> np.ndarray:
     Each element is then rounded to float16 (round to nearest even) and
     returned as float64 holding that value.
     Reading: the pages fix no precision for S.  Rounding each N(0,1) draw to
-    fp16 keeps the entries i.i.d. and symmetric; the sign estimator's constant
-    sqrt(pi/2) assumes exact Gaussian rows, and the rounding (relative error
-    <= 2^-11) moves E[sign(s.r)(s.a)] by far less than its sampling noise."""
+    fp16 keeps the entries i.i.d. and symmetric but not exactly Gaussian, and
+    the sign estimator's constant sqrt(pi/2) is exact only for Gaussian rows.
+    The rounding (relative error <= 2^-11 per entry) moves E[sign(s.r)(s.a)]
+    by less than 1e-4 of its value, bounded by a paired experiment in the pins
+    (test_sign_estimator_with_fp16_entries); one key's 128-row estimate has a
+    sampling spread near 10%."""
     n = m * d
     raw = splitmix64_stream(seed, tag, n + (n & 1))
     vals = []

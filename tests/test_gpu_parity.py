@@ -152,9 +152,19 @@ def test_encode_values_exact(bits, dtype):
     if dtype == "f32":
         x[3, :32] = 1.5
         vv[3, :32] = 1.5
+    # a group of exact rounding ties: min 0 and max 2^b - 1 give s = 1, z = 0,
+    # so k + 1/2 must go to the even code (exact in every input type)
+    top = (1 << bits) - 1
+    tie_row = np.ones(32, dtype=np.float32)
+    tie_row[0], tie_row[1] = 0.0, float(top)
+    tie_row[2:2 + top] = np.arange(top, dtype=np.float32) + 0.5
+    vv[5, 32:64] = tie_row
+    x[5, 32:64] = torch.from_numpy(tie_row).to(DEV).to(x.dtype)
     planes = tq.encode_values(x, bits)
     torch.cuda.synchronize()
-    P.check_values(vv, bits, _np(planes["codes"]), _np(planes["scale"]), _np(planes["zero"]))
+    enc = P.check_values(vv, bits, _np(planes["codes"]), _np(planes["scale"]), _np(planes["zero"]))
+    even = [int(t - 0.5) if int(t - 0.5) % 2 == 0 else int(t + 0.5) for t in tie_row[2:2 + top]]
+    assert list(enc["codes"][5, 34:34 + top]) == even
 
 
 # ------------------------------------------------------------------ decode

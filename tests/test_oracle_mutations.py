@@ -66,12 +66,86 @@ def test_dropped_sign_flip_sigma_is_caught(monkeypatch):
 
 
 def test_value_rounding_half_up_is_caught(monkeypatch):
+    """Rounding exact ties up instead of to even."""
     orig = O.encode_values
 
     def mutant(values, bits, group=32):
         e = orig(values, bits, group)
-        e["codes"] = np.clip(np.floor(e["ratio"] + 0.5), 0, (1 << bits) - 1).astype(np.int64) * 0 + \
-            np.clip(np.floor(e["ratio"]), 0, (1 << bits) - 1).astype(np.int64)
+        code = np.clip(np.floor(e["ratio"] + 0.5), 0, (1 << bits) - 1)
+        s16 = np.repeat(e["scale16"], group, axis=-1).reshape(code.shape)
+        e["codes"] = np.where(s16 == 0, 0, code).astype(np.int64)
+        return e
+    monkeypatch.setattr(O, "encode_values", mutant)
+    assert _fails(P.test_value_rounding_ties_to_even, 2)
+    assert _fails(P.test_value_rounding_ties_to_even, 4)
+
+
+def test_value_rounding_truncation_is_caught(monkeypatch):
+    orig = O.encode_values
+
+    def mutant(values, bits, group=32):
+        e = orig(values, bits, group)
+        e["codes"] = np.clip(np.floor(e["ratio"]), 0, (1 << bits) - 1).astype(np.int64)
         return e
     monkeypatch.setattr(O, "encode_values", mutant)
     assert _fails(P.test_value_quantisation_error_bound, 2)
+    assert _fails(P.test_value_rounding_ties_to_even, 2)
+
+
+def test_uncentred_spearman_is_caught(monkeypatch):
+    def mutant(a, b):
+        ra = np.argsort(np.argsort(a)).astype(np.float64)
+        rb = np.argsort(np.argsort(b)).astype(np.float64)
+        return float((ra * rb).sum() / math.sqrt((ra * ra).sum() * (rb * rb).sum()))
+    monkeypatch.setattr(O, "spearman", mutant)
+    assert _fails(P.test_spearman_matches_scipy)
+
+
+def test_recall_of_bottom_k_is_caught(monkeypatch):
+    def mutant(true_scores, est_scores, k):
+        t = np.argsort(true_scores, axis=-1, kind="stable")[:, :k]
+        e = np.argsort(est_scores, axis=-1, kind="stable")[:, :k]
+        return float(np.mean([len(set(a) & set(b)) / k for a, b in zip(t, e)]))
+    monkeypatch.setattr(O, "recall_at_k", mutant)
+    assert _fails(P.test_recall_at_k_worked_example)
+
+
+def test_grouped_shared_norm_is_caught(monkeypatch):
+    """Normalising both halves by the whole key's norm."""
+    orig = O._rotate_unit
+    state = {}
+
+    def mutant(keys, sigma):
+        k = np.asarray(keys, dtype=np.float64)
+        if k.shape[-1] == 64 and "full" in state:
+            n = state["full"]
+            u = k / np.where(n > 0, n, 1.0)[..., None]
+            return n, u @ O.rotation_matrix(sigma).T * 8.0
+        return orig(keys, sigma)
+    enc_orig = O.encode_keys
+
+    def enc_mutant(keys, T):
+        state["full"] = np.sqrt(np.sum(np.asarray(keys, dtype=np.float64) ** 2, axis=-1))
+        try:
+            return enc_orig(keys, T)
+        finally:
+            state.pop("full", None)
+    monkeypatch.setattr(O, "_rotate_unit", mutant)
+    monkeypatch.setattr(O, "encode_keys", enc_mutant)
+    assert _fails(P.test_grouped_key_built_from_centroids)
+
+
+def test_grouped_swapped_rotations_are_caught(monkeypatch):
+    """Encoding each half with the other half's random signs."""
+    enc_orig = O.encode_keys
+
+    def enc_mutant(keys, T):
+        if T.cfg.mode == "grouped":
+            T2 = O.KeyTables()
+            T2.cfg = T.cfg
+            T2.halves = [dict(h) for h in T.halves]
+            T2.halves[0]["sigma"], T2.halves[1]["sigma"] = T.halves[1]["sigma"], T.halves[0]["sigma"]
+            return enc_orig(keys, T2)
+        return enc_orig(keys, T)
+    monkeypatch.setattr(O, "encode_keys", enc_mutant)
+    assert _fails(P.test_grouped_key_built_from_centroids)

@@ -315,6 +315,41 @@ def test_prod_unbiased_over_S_draws():
     assert np.all(np.abs(sd ** 2 / var_theory - 1) < 0.12), sd ** 2 / var_theory
 
 
+def test_sign_estimator_with_fp16_entries():
+    """S is stored in fp16 (each N(0,1) draw rounded to nearest even).  The
+    sign estimator's constant sqrt(pi/2) holds exactly for Gaussian rows:
+    E[sign(s.r)(s.a)] = sqrt(2/pi) <a,r>/||r|| (difai.kr tutorial, the QJL
+    correction).  A paired experiment over 2^20 rows (the same Gaussian draw
+    with and without the fp16 rounding) bounds how far the rounding moves that
+    expectation: below 1e-4 of its value, against a sampling spread of about
+    10% for one key's 128-row estimate.  The unrounded mean is also checked
+    against the closed form."""
+    rng = np.random.default_rng(31)
+    d = 128
+    r = rng.standard_normal(d)
+    a = r / np.linalg.norm(r) + 0.8 * rng.standard_normal(d) / math.sqrt(d)
+    a /= np.linalg.norm(a)
+    exact = math.sqrt(2 / math.pi) * (a @ r) / np.linalg.norm(r)
+    n, chunk = 1 << 20, 1 << 16
+    diff_sum = diff_sq = e64_sum = e64_sq = 0.0
+    for _ in range(n // chunk):
+        S = rng.standard_normal((chunk, d))
+        S16 = O.fp16_round(S).astype(np.float64)
+        e64 = np.where(S @ r >= 0, 1.0, -1.0) * (S @ a)
+        e16 = np.where(S16 @ r >= 0, 1.0, -1.0) * (S16 @ a)
+        dd = e16 - e64
+        diff_sum += dd.sum()
+        diff_sq += (dd * dd).sum()
+        e64_sum += e64.sum()
+        e64_sq += (e64 * e64).sum()
+    dm = diff_sum / n
+    dse = math.sqrt(max(diff_sq / n - dm * dm, 0.0) / n)
+    em = e64_sum / n
+    ese = math.sqrt((e64_sq / n - em * em) / n)
+    assert abs(em - exact) < 4 * ese, (em, exact, ese)
+    assert (abs(dm) + 4 * dse) / exact < 1e-4, (dm, dse, exact)
+
+
 def test_prod_bias_regression_slope_is_zero():
     """Regress (estimate - truth) on <q, k - k_mse_hat> over many pairs: a
     wrong QJL constant alpha shows as slope alpha - 1."""
@@ -355,6 +390,51 @@ def test_prod_distortion_theorem3_and_scaling():
         bound = math.sqrt(3) * math.pi ** 2 * (y @ y) / 128 * 4.0 ** (-b)
         assert D[b] <= bound, (b, D[b], bound)
     assert D[2] / D[3] > 2.0 and D[3] / D[4] > 2.0
+
+
+def test_grouped_key_built_from_centroids():
+    """Each half of the key is (n_j / lam_j) Pi_j^T c_j[idx_j] with its own
+    64-point rotation and codebook ("tqlite" README mode table: outlier and
+    normal channels quantised separately), written here from scipy's Hadamard
+    matrix rather than through the MSE path.  The encoder must return both
+    index halves, both norms and, dequantised, each half scaled by 1/lam_j.  A
+    norm shared by the halves, swapped rotations or codebooks, or one
+    128-point rotation over both halves breaks one of these."""
+    cfg = O.KeyConfig(mode="grouped", bits_outlier=4, bits_normal=2, seed=17)
+    T = O.build_tables(cfg)
+    rng = np.random.default_rng(21)
+    H64 = scipy.linalg.hadamard(64)
+    rows, idxs, lams = [], [], []
+    for n_out, n_norm in ((10.0, 1.0), (0.5, 3.0), (64.0, 0.25)):
+        halves, ih, lh = [], [], []
+        for half, n in zip(T.halves, (n_out, n_norm)):
+            c_all, t = half["centroids"], half["boundaries"]
+            L = len(c_all)
+            while True:
+                idx = rng.integers(0, L, 64)
+                c = c_all[idx]
+                lam = 8.0 / np.linalg.norm(c)             # sqrt(64) / ||c||
+                y = lam * c                               # the rotated, sqrt(h)-scaled half
+                if np.array_equal(np.sum(y[:, None] >= t[None, :], axis=1), idx) and \
+                        np.min(np.abs(y[:, None] - t[None, :])) > 1e-3:
+                    break
+            Pi = H64 * half["sigma"][None, :] / 8.0
+            halves.append(n * (c / np.linalg.norm(c)) @ Pi)
+            ih.append(idx)
+            lh.append(lam)
+        rows.append(np.concatenate(halves))
+        idxs.append(np.concatenate(ih))
+        lams.append(lh)
+    k = np.array(rows)
+    enc = O.encode_keys(k, T)
+    assert np.array_equal(enc["idx"], np.array(idxs))
+    norms = np.array([[10.0, 1.0], [0.5, 3.0], [64.0, 0.25]])
+    assert np.allclose(enc["norm"], norms, rtol=1e-12)
+    assert np.array_equal(enc["norm16"].astype(np.float64), norms)   # exact in fp16
+    kh = O.dequant_keys(enc, T)
+    lam = np.array(lams)
+    assert np.allclose(kh[:, :64], k[:, :64] / lam[:, :1], atol=1e-12)
+    assert np.allclose(kh[:, 64:], k[:, 64:] / lam[:, 1:], atol=1e-12)
 
 
 def test_grouped_halves_are_independent_mse():
@@ -413,6 +493,27 @@ def test_value_quantisation_error_bound(bits):
     ax = vg.argmax(-1)
     assert np.all(np.take_along_axis(codes, am[..., None], -1) == 0)
     assert np.all(np.take_along_axis(codes, ax[..., None], -1) == (1 << bits) - 1)
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_value_rounding_ties_to_even(bits):
+    """A group with min 0 and max 2^b - 1 has s = 1 and z = 0 exactly, so
+    every value k + 1/2 is an exact rounding tie: ties go to the even code
+    (0.5 -> 0, 1.5 -> 2, 2.5 -> 2, ...), the reading taken for the value
+    quantiser.  Half-up would give 1, 2, 3, ...; truncation 0, 1, 2, ..."""
+    top = (1 << bits) - 1
+    ties = np.arange(top, dtype=np.float64) + 0.5            # 0.5 .. top - 0.5
+    row = np.zeros(32)
+    row[0], row[1] = 0.0, float(top)
+    row[2:2 + len(ties)] = ties
+    row[2 + len(ties):] = 1.0
+    v = np.tile(row, 4)[None, :].astype(np.float32)
+    enc = O.encode_values(v, bits)
+    assert np.all(enc["scale16"] == 1.0) and np.all(enc["zero16"] == 0.0)
+    want = np.array([int(t - 0.5) if int(t - 0.5) % 2 == 0 else int(t + 0.5) for t in ties])
+    got = enc["codes"][0, 2:2 + len(ties)]
+    assert np.array_equal(got, want), (got, want)
+    assert enc["codes"][0, 0] == 0 and enc["codes"][0, 1] == top
 
 
 def test_value_cosine_at_4_bits_matches_pack_article():
@@ -476,6 +577,33 @@ def test_recall_and_rank_correlation_thresholds():
         rho[b] = np.mean([O.spearman(true[i], est[i]) for i in range(32)])
     assert rec[3] >= 0.40 and rec[4] >= 0.55 and rec[4] > rec[3], rec
     assert rho[3] > 0.75 and rho[4] > 0.90, rho
+
+
+def test_spearman_matches_scipy():
+    """The rank correlation is Spearman's rho: on tie-free data it equals
+    scipy.stats.spearmanr, and it is invariant under monotone maps."""
+    rng = np.random.default_rng(15)
+    for n in (5, 64, 2048):
+        a = rng.standard_normal(n)
+        b = 0.6 * a + rng.standard_normal(n)
+        ref = scipy.stats.spearmanr(a, b).statistic
+        assert abs(O.spearman(a, b) - ref) < 1e-12, (n, O.spearman(a, b), ref)
+        assert abs(O.spearman(np.exp(a), b ** 3) - ref) < 1e-12
+    # worked example: ranks (0,1,2,3,4) against (0,2,1,4,3): d^2 = 4, rho = 1 - 6*4/(5*24) = 0.8
+    assert abs(O.spearman(np.array([1., 2, 3, 4, 5]), np.array([10., 30, 20, 50, 40])) - 0.8) < 1e-12
+    assert abs(O.spearman(np.arange(6.0), -np.arange(6.0)) + 1.0) < 1e-12
+
+
+def test_recall_at_k_worked_example():
+    """recall@k = |top-k(true) & top-k(est)| / k, averaged over queries."""
+    true = np.array([[5., 4, 3, 2, 1], [1., 2, 3, 4, 5]])
+    est = np.array([[5., 3, 4, 1, 2], [5., 4, 3, 2, 1]])
+    # query 0: true top-2 {0,1}, est top-2 {0,2} -> 1/2; query 1: {4,3} vs {0,1} -> 0
+    assert O.recall_at_k(true, est, 2) == 0.25
+    # top-3: {0,1,2} vs {0,2,1} -> 1; {4,3,2} vs {0,1,2} -> 1/3
+    assert abs(O.recall_at_k(true, est, 3) - (1 + 1 / 3) / 2) < 1e-15
+    assert O.recall_at_k(true, true, 4) == 1.0
+    assert O.recall_at_k(true, est, 5) == 1.0
 
 
 def test_needle_argmax_over_dequantised_keys():
