@@ -15,9 +15,10 @@
  *   - Pointers are DEVICE memory unless the argument is marked (host).
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *     Calls only enqueue work on it; none synchronises or allocates device
- *     memory, and the library keeps no mutable global state (calls from
- *     several host threads are safe; calls that write the same buffers race
- *     exactly as the kernels they enqueue would).
+ *     memory, and the library keeps no mutable global state apart from
+ *     tq_decode_attention_noalloc's device array and its cached address
+ *     (calls from several host threads are safe; calls that write the same
+ *     buffers race exactly as the kernels they enqueue would).
  *   - The caller owns every buffer.
  *   - Arguments are validated on the host before anything is launched; a bad
  *     argument returns TQ_ERR_ARG / TQ_ERR_UNSUPPORTED and enqueues nothing.
@@ -235,6 +236,31 @@ tq_status tq_decode_attention(const tq_key_config* cfg, const void* tables,
                               const uint8_t* v_codes, const uint16_t* v_scale, const uint16_t* v_zero,
                               float sm_scale, float* out, float* lse, float* scores,
                               void* workspace, size_t* workspace_bytes, void* stream);
+
+/*
+ * tq_decode_attention_noalloc -- tq_decode_attention for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, results (bit for bit) and
+ * errors as tq_decode_attention, without the workspace: the split-K partials
+ * go to an 8 MiB device array owned by the library, one per GPU, held until
+ * the process ends.  Its device address is looked up on the first call on
+ * each device (with that device current); no call allocates or frees memory.
+ * A shape whose partials (B * Hq * n_split * 130 floats, the size
+ * tq_decode_attention's workspace query reports) exceed 8 MiB returns
+ * TQ_ERR_WORKSPACE and enqueues nothing.  Every call on one GPU shares its
+ * array: calls that overlap on one GPU (two streams, or host threads on one
+ * device) race on it and must be serialised by the caller; calls on one
+ * stream are ordered and safe.  Nothing in the array needs clearing between
+ * calls (every partial a call reads, that call writes first).
+ */
+tq_status tq_decode_attention_noalloc(const tq_key_config* cfg, const void* tables,
+                                      const void* q, int32_t q_dtype, int32_t B, int32_t Hq, int32_t Hkv,
+                                      const int32_t* ctx_len, int32_t max_ctx,
+                                      const uint8_t* idx, const uint8_t* signs,
+                                      const uint16_t* norm, const uint16_t* rnorm,
+                                      int32_t v_bits, int32_t v_group,
+                                      const uint8_t* v_codes, const uint16_t* v_scale, const uint16_t* v_zero,
+                                      float sm_scale, float* out, float* lse, float* scores, void* stream);
 
 /*
  * tq_decode_attention_paged -- tq_decode_attention over a paged cache: the

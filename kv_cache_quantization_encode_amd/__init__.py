@@ -7,6 +7,7 @@ streams); importing it requires the built libtq.so next to this file.
 from ._lib import (TQ_BF16, TQ_F16, TQ_F32, TQ_MODE_GROUPED, TQ_MODE_MSE, TQ_MODE_PROD, KeyConfig,
                    TqError, key_config, status_string)
 from .api import (Decoder, KeyBatchEncoder, Tables, append_kv, build_codebook, channel_moments, decode_attention,
+                  decode_attention_noalloc,
                   decode_workspace_bytes, dequantize_keys, dequantize_values, encode_keys, encode_keys_batched,
                   encode_values,
                   idx_row_bytes, key_planes, parse_tables, select_outlier_channels, value_planes)
@@ -15,6 +16,7 @@ from . import quality
 
 __all__ = ["KeyConfig", "TqError", "key_config", "status_string", "Tables", "Decoder",
            "build_codebook", "parse_tables", "encode_keys", "encode_keys_batched", "KeyBatchEncoder", "encode_values", "append_kv", "decode_attention",
+           "decode_attention_noalloc",
            "decode_workspace_bytes", "key_planes", "value_planes", "idx_row_bytes", "PagedKVCache",
            "dequantize_keys", "dequantize_values", "quality",
            "channel_moments", "select_outlier_channels",

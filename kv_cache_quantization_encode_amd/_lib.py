@@ -25,7 +25,7 @@ TQ_F32, TQ_BF16, TQ_F16 = 0, 1, 2
 MODES = {"mse": TQ_MODE_MSE, "prod": TQ_MODE_PROD, "grouped": TQ_MODE_GROUPED}
 
 EXPORTED = ["tq_build_codebook", "tq_encode_keys", "tq_encode_keys_batched", "tq_encode_values", "tq_append_kv", "tq_decode_attention",
-            "tq_decode_attention_paged", "tq_dequantize_keys", "tq_dequantize_values", "tq_channel_moments",
+            "tq_decode_attention_noalloc", "tq_decode_attention_paged", "tq_dequantize_keys", "tq_dequantize_values", "tq_channel_moments",
             "tq_status_string", "tq_idx_row_bytes"]
 
 
@@ -77,6 +77,9 @@ def _load():
     lib.tq_decode_attention.argtypes = [CFG, P, P, I32, I32, I32, I32, P, I32, P, P, P, P,
                                         I32, I32, P, P, P, ctypes.c_float, P, P, P, P,
                                         ctypes.POINTER(SZ), P]
+    lib.tq_decode_attention_noalloc.restype = I32
+    lib.tq_decode_attention_noalloc.argtypes = [CFG, P, P, I32, I32, I32, I32, P, I32, P, P, P, P,
+                                                I32, I32, P, P, P, ctypes.c_float, P, P, P, P]
     lib.tq_decode_attention_paged.restype = I32
     lib.tq_decode_attention_paged.argtypes = [CFG, P, P, I32, I32, I32, I32, P, P, I32, I32, P, P, P, P,
                                               I32, I32, P, P, P, ctypes.c_float, P, P, P, P,

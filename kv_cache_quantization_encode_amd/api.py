@@ -433,6 +433,43 @@ class Decoder:
         return out
 
 
+def decode_attention_noalloc(tables: Tables, q, ctx_len, kp: dict, vp: dict, v_bits: int, max_ctx: int,
+                             Hkv: int, out, sm_scale=None, lse=None, scores=None):
+    """tq_decode_attention_noalloc: the decode step without a workspace (the
+    library's own per-GPU array holds the split-K partials), for callers that
+    cannot allocate.  out [B, Hq, d] float32 (and lse / scores, if given) are
+    the caller's; nothing is allocated here either."""
+    _on_device(q, "q", tuple(_DT), contiguous=True)
+    _need(q.dim() == 3, "q must be [B, Hq, d]")
+    B, Hq, d = q.shape
+    _need(d == tables.cfg.d, "q has head dim %d, the tables %d" % (d, tables.cfg.d))
+    _on_device(ctx_len, "ctx_len", torch.int32, contiguous=True)
+    _need(ctx_len.numel() == B, "ctx_len needs one entry per sequence")
+    _on_device(out, "out", torch.float32, contiguous=True)
+    _need(out.numel() >= B * Hq * d, "out must hold [B, Hq, d]")
+    if lse is not None:
+        _on_device(lse, "lse", torch.float32, contiguous=True)
+        _need(lse.numel() >= B * Hq, "lse must hold [B, Hq]")
+    if scores is not None:
+        _on_device(scores, "scores", torch.float32, contiguous=True)
+        _need(scores.numel() >= B * Hq * max_ctx, "scores must hold [B, Hq, max_ctx]")
+    n_rec = min(_records(kp, "idx", tables.row_bytes), _records(vp, "codes", d * v_bits // 8))
+    _need(n_rec >= B * Hkv * max_ctx, "the planes hold %d records, B * Hkv * max_ctx = %d"
+          % (n_rec, B * Hkv * max_ctx))
+    _check_key_planes(tables, kp, n_rec)
+    _check_value_planes(vp, v_bits, n_rec, d)
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(d)
+    st = lib.tq_decode_attention_noalloc(ctypes.byref(tables.cfg), _ptr(tables.dev), _ptr(q), _DT[q.dtype],
+                                         B, Hq, Hkv, _ptr(ctx_len), max_ctx, _ptr(kp["idx"]),
+                                         _ptr(kp.get("signs")), _ptr(kp["norm"]), _ptr(kp.get("rnorm")),
+                                         v_bits, 32, _ptr(vp["codes"]), _ptr(vp["scale"]), _ptr(vp["zero"]),
+                                         ctypes.c_float(sm_scale), _ptr(out), _ptr(lse), _ptr(scores),
+                                         _stream())
+    check("tq_decode_attention_noalloc", st)
+    return out
+
+
 def decode_attention(tables: Tables, q, ctx_len, kp, vp, v_bits, max_ctx, sm_scale=None,
                      with_lse=False, with_scores=False):
     B, Hq, d = q.shape

@@ -962,6 +962,69 @@ tq_status decode_impl(const tq_key_config* cfg, const void* tables, const void* 
 
 }  // namespace
 
+// ---- the allocation-free variant: the split-K partials live in a device
+// array of the library's own, one copy per GPU, held until the process ends.
+// In host code `scratch` names a host-side stand-in, not device memory: its
+// device address is looked up once per device (hipGetSymbolAddress, with that
+// device current) and only that address is ever passed to a kernel.
+namespace {
+
+constexpr size_t NOALLOC_SCRATCH_BYTES = size_t(8) << 20;
+__device__ __align__(256) unsigned char scratch[NOALLOC_SCRATCH_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+std::atomic<void*> g_scratch[MAX_DEVICES];
+
+// Device address of this device's scratch array, or NULL (status in *st).
+void* scratch_of_current_device(tq_status* st) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    *st = TQ_ERR_HIP;
+    return nullptr;
+  }
+  if (dev < 0 || dev >= MAX_DEVICES) {
+    *st = TQ_ERR_UNSUPPORTED;
+    return nullptr;
+  }
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (!p) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      (void)hipGetLastError();
+      *st = TQ_ERR_HIP;
+      return nullptr;
+    }
+    g_scratch[dev].store(p, std::memory_order_release);
+  }
+  *st = TQ_OK;
+  return p;
+}
+
+}  // namespace
+
+extern "C" tq_status tq_decode_attention_noalloc(const tq_key_config* cfg, const void* tables, const void* q,
+                                                int32_t q_dtype, int32_t B, int32_t Hq, int32_t Hkv,
+                                                const int32_t* ctx_len, int32_t max_ctx, const uint8_t* idx,
+                                                const uint8_t* signs, const uint16_t* norm,
+                                                const uint16_t* rnorm, int32_t v_bits, int32_t v_group,
+                                                const uint8_t* v_codes, const uint16_t* v_scale,
+                                                const uint16_t* v_zero, float sm_scale, float* out,
+                                                float* lse, float* scores, void* stream) {
+  // size of the partials for this shape (a query: nothing is launched)
+  size_t need = 0;
+  tq_status st = decode_impl(cfg, tables, q, q_dtype, B, Hq, Hkv, ctx_len, max_ctx, nullptr, 0, 0, idx,
+                             signs, norm, rnorm, v_bits, v_group, v_codes, v_scale, v_zero, sm_scale, out,
+                             lse, scores, nullptr, &need, stream);
+  if (st != TQ_OK) return st;
+  if (need > NOALLOC_SCRATCH_BYTES) return TQ_ERR_WORKSPACE;
+  void* ws = scratch_of_current_device(&st);
+  if (!ws) return st;
+  size_t have = NOALLOC_SCRATCH_BYTES;
+  return decode_impl(cfg, tables, q, q_dtype, B, Hq, Hkv, ctx_len, max_ctx, nullptr, 0, 0, idx, signs, norm,
+                     rnorm, v_bits, v_group, v_codes, v_scale, v_zero, sm_scale, out, lse, scores, ws, &have,
+                     stream);
+}
+
 extern "C" tq_status tq_decode_attention(const tq_key_config* cfg, const void* tables, const void* q,
                                         int32_t q_dtype, int32_t B, int32_t Hq, int32_t Hkv,
                                         const int32_t* ctx_len, int32_t max_ctx, const uint8_t* idx,
