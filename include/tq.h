@@ -271,21 +271,25 @@ tq_status tq_decode_attention_noalloc(const tq_key_config* cfg, const void* tabl
  *     (block_table[b][t / page_size] * Hkv + h) * page_size + t % page_size,
  * which is also the slot tq_encode_keys / tq_encode_values write it to.
  *   block_table         int32 [B][max_blocks_per_seq] device array; entries
- *                       for pages below ctx_len[b] must name pages that exist
- *                       in the planes (not checked on the device); entries
- *                       past them are never read.
+ *                       for pages below ctx_len[b] name pages of the pool;
+ *                       entries past them are never read.  An entry outside
+ *                       [0, n_pages) is clamped into it on the device, so a
+ *                       stale table reads wrong tokens but never outside the
+ *                       planes.
  *   page_size           tokens per page, a positive multiple of 64.
+ *   n_pages             pages in the pool: the planes hold n_pages * Hkv *
+ *                       page_size records.
  *   scores              (nullable) [B][Hq][max_blocks_per_seq * page_size].
  * Every other argument, the workspace query and the errors are those of
  * tq_decode_attention with max_ctx = max_blocks_per_seq * page_size; a bad
- * page_size or max_blocks_per_seq returns TQ_ERR_ARG.  Results equal those of
+ * page_size, max_blocks_per_seq or n_pages returns TQ_ERR_ARG.  Results equal those of
  * tq_decode_attention on the same tokens laid out contiguously, bit for bit.
  */
 tq_status tq_decode_attention_paged(const tq_key_config* cfg, const void* tables,
                                     const void* q, int32_t q_dtype, int32_t B, int32_t Hq,
                                     int32_t Hkv, const int32_t* ctx_len,
                                     const int32_t* block_table, int32_t max_blocks_per_seq,
-                                    int32_t page_size,
+                                    int32_t page_size, int32_t n_pages,
                                     const uint8_t* idx, const uint8_t* signs,
                                     const uint16_t* norm, const uint16_t* rnorm,
                                     int32_t v_bits, int32_t v_group,

@@ -81,7 +81,7 @@ def _load():
     lib.tq_decode_attention_noalloc.argtypes = [CFG, P, P, I32, I32, I32, I32, P, I32, P, P, P, P,
                                                 I32, I32, P, P, P, ctypes.c_float, P, P, P, P]
     lib.tq_decode_attention_paged.restype = I32
-    lib.tq_decode_attention_paged.argtypes = [CFG, P, P, I32, I32, I32, I32, P, P, I32, I32, P, P, P, P,
+    lib.tq_decode_attention_paged.argtypes = [CFG, P, P, I32, I32, I32, I32, P, P, I32, I32, I32, P, P, P, P,
                                               I32, I32, P, P, P, ctypes.c_float, P, P, P, P,
                                               ctypes.POINTER(SZ), P]
     lib.tq_dequantize_keys.restype = I32

@@ -364,7 +364,7 @@ def decode_workspace_bytes(tables: Tables, B, Hq, Hkv, max_ctx, q_dtype=torch.bf
         check("tq_decode_attention", st)
     else:
         st = lib.tq_decode_attention_paged(ctypes.byref(tables.cfg), None, None, _DT[q_dtype], B, Hq, Hkv,
-                                           None, None, max_ctx // page_size, page_size, *keys)
+                                           None, None, max_ctx // page_size, page_size, 1, *keys)
         check("tq_decode_attention_paged", st)
     return size.value
 
@@ -426,9 +426,12 @@ class Decoder:
             _need(block_table is not None, "a paged decoder needs the block table")
             _on_device(block_table, "block_table", torch.int32, contiguous=True)
             _need(tuple(block_table.shape) == (B, nb), "block_table must be [B, max_ctx // page_size]")
+            # pages of the pool: the planes' records over the records of one page
+            n_pages = n_rec // (self.Hkv * self.page_size)
+            _need(n_pages > 0, "the planes hold less than one page")
             st = lib.tq_decode_attention_paged(ctypes.byref(self.tables.cfg), _ptr(self.tables.dev), _ptr(q),
                                                _DT[q.dtype], B, Hq, self.Hkv, _ptr(ctx_len), _ptr(block_table),
-                                               nb, self.page_size, *keys, *vals, *tail)
+                                               nb, self.page_size, n_pages, *keys, *vals, *tail)
             check("tq_decode_attention_paged", st)
         return out
 

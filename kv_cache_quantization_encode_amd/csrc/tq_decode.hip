@@ -10,21 +10,30 @@
 //
 // One workgroup (16 waves) takes one (sequence, KV head, quad of query heads,
 // token chunk).  Its prologue rotates the four queries (q' = H sigma q by
-// shuffle butterflies in registers), projects them (S q'), and turns them into
-// lookup tables: for every byte position p of a packed key and every byte
+// shuffle butterflies in registers), projects them (S q', on MFMA: the QJL
+// matrix product is the one dense contraction of the method) and turns them
+// into lookup tables: for every byte position p of a packed key and every byte
 // value v, the four heads' partial inner products over the coordinates that
-// byte holds, as fp16.  A key's score is then one table read per packed byte
-// (48 for a 3-bit prod key) instead of 4 x 256 multiply-adds.  Half of the
-// waves score 64-token tiles (lane = token) and run the online softmax; the
-// other half accumulate p.V for those tiles one round later (lane = token-pair
-// slot and 8-channel slice) on v_dot2_f32_f16 over token pairs, with the 2- or
-// 4-bit code fields left in place as fp16 subnormal bit patterns (a byte's
-// fields up to channel i, masked: prefix value * 2^-24), so no conversion is
-// spent per code and per-channel sums are differences of consecutive prefix
-// sums at the end.  The value scale is folded into the weight (p * scale) and
-// the zero point is summed separately (sum_t p_t zero_t).  The chunk's (max,
-// sum, unnormalised output) goes to the workspace; a second kernel merges
-// chunks in a fixed order.
+// byte holds.  An entry is an integer in [0, 16383] in units of a per-head
+// step, offset by the smallest value of its position (both derived from |q'|
+// and the codebook's end points), four heads packed in 64 bits.  A key's
+// score is then one table read per packed byte (48 for a 3-bit prod key):
+// four reads are added with one 64-bit add each (the 16-bit fields cannot
+// carry into each other) and then folded into 32-bit sums per head with
+// v_dot2_u32_u16, so the sums are exact integers.
+// Half of the waves score 64-token tiles (lane = token) and run the online
+// softmax; the other half accumulate p.V for those tiles one round later
+// (lane = token-pair slot and 8-channel slice) on v_dot2_f32_f16 over token
+// pairs, with the 2- or 4-bit code fields left in place as fp16 subnormal bit
+// patterns (a byte's fields up to channel i, masked: prefix value * 2^-24), so
+// no conversion is spent per code and per-channel sums are differences of
+// consecutive prefix sums at the end.  The value scale is folded into the
+// weight (p * scale, as fp16) and the zero point is summed separately
+// (sum_t p_t zero_t, fp32).  Softmax weights are carried as p * 2^14 and the
+// scales of each tile are renormalised by a power of two, so weights keep the
+// fp16 normal range whatever the values' magnitude.  The chunk's (max, sum,
+// unnormalised output) goes to the workspace; a second kernel merges chunks
+// in a fixed order.
 #include <hip/hip_runtime.h>
 #include <hip/hip_fp16.h>
 
@@ -38,60 +47,79 @@
 namespace {
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float2_t __attribute__((ext_vector_type(2)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef unsigned short ushort2_t __attribute__((ext_vector_type(2)));
 
 constexpr int KD = 128;
 #ifndef TQ_DEC_WAVES
 #define TQ_DEC_WAVES 16
 #endif
-#ifndef TQ_DEC_LOOKUP_BATCH
-#define TQ_DEC_LOOKUP_BATCH 8
-#endif
 constexpr int NW = TQ_DEC_WAVES;  // waves per workgroup
-constexpr int NT = NW * 64;   // threads per workgroup
-constexpr int PAGE_CACHE = 512;  // block-table entries a workgroup keeps in LDS
-constexpr int TILE = 64;      // tokens per wave tile
-constexpr int QH = 4;         // query heads per workgroup
+constexpr int NT = NW * 64;       // threads per workgroup
+constexpr int NS = NW / 2;        // score waves (and p.V waves)
+constexpr int PAGE_CACHE = 512;   // block-table entries a workgroup keeps in LDS
+constexpr int TILE = 64;          // tokens per wave tile
+constexpr int QH = 4;             // query heads per workgroup
 constexpr int WGRP = 32 * QH + 16;  // dwords per value group of a wave's weight slot (padded)
 constexpr int WSLOT = 4 * WGRP;     // dwords of a wave's weight slot
-constexpr int PART = KD + 2;  // floats per partial: max, sum, out[128]
+constexpr int PART = KD + 2;      // floats per partial: max, sum, out[128]
 constexpr float LOG2E = 1.4426950408889634f;
+constexpr int CHAIN = 4;          // table reads summed in 16-bit fields before a flush
+constexpr float EMAX = 16382.0f;  // entries round into [0, 16383]: four fit a 16-bit field
+constexpr float PSCALE = 14.0f;   // softmax weights are carried as p * 2^14
+constexpr float SQRT_HALF_PI = 1.2533141373155003f;
 
 constexpr int width_of(int b) { return b == 1 ? 1 : b == 2 ? 2 : 4; }
 constexpr int stride_of(int b) { return b == 3 ? 128 : 256; }  // 3-bit in nibbles: bytes <= 0x77
 
+// Table classes of a key format, in key-byte order: the index bytes of part 0,
+// (GROUPED) the index bytes of part 1, (PROD) the QJL sign bytes.
 template <int MODE, int B0, int B1>
 struct Fmt {
   static constexpr bool GROUPED = MODE == TQ_MODE_GROUPED;
-  static constexpr bool PROD = MODE == TQ_MODE_PROD;
-  static constexpr int PD = GROUPED ? KD / 2 : KD;           // coordinates per part
+  static constexpr bool QJL = MODE == TQ_MODE_PROD;
+  static constexpr int NPART = GROUPED ? 2 : 1;
+  static constexpr int PD = KD / NPART;  // coordinates per part
   static constexpr int W0 = width_of(B0);
   static constexpr int W1 = GROUPED ? width_of(B1) : 1;
-  static constexpr int CPB0 = 8 / W0, CPB1 = 8 / W1;           // coordinates per byte
-  static constexpr int P0 = PD * W0 / 8;                        // class-0 byte positions
-  static constexpr int P1 = PROD ? KD / 8 : GROUPED ? PD * W1 / 8 : 0;
-  static constexpr int S0 = stride_of(B0);
-  static constexpr int S1 = GROUPED ? stride_of(B1) : 256;
-  static constexpr int E0 = P0 * S0, E1 = P1 * S1;              // table entries, [position][value]
-  static constexpr int IDXB = P0 + (GROUPED ? P1 : 0);          // idx row bytes
-  static constexpr int KWORDS = (IDXB + (PROD ? KD / 8 : 0)) / 4;  // idx + sign words
+  static constexpr int IP0 = PD * W0 / 8;
+  static constexpr int IP1 = GROUPED ? PD * W1 / 8 : 0;
+  static constexpr int SP = QJL ? KD / 8 : 0;
+  static constexpr int IDXB = IP0 + IP1;                 // idx row bytes
+  static constexpr int KWORDS = (IDXB + SP) / 4;         // idx + sign words per key
+  static constexpr int NC = NPART + (QJL ? 1 : 0);       // table classes
+  // class c: 0 / 1 index part, 2 sign bytes
+  static constexpr int kind(int c) { return c == 0 ? 0 : (GROUPED ? 1 : 2); }
+  static constexpr int npos(int c) { return c == 0 ? IP0 : (GROUPED ? IP1 : SP); }
+  static constexpr int stride(int c) { return kind(c) == 0 ? stride_of(B0) : kind(c) == 1 ? stride_of(B1) : 256; }
+  static constexpr int kbyte(int c) { return c == 0 ? 0 : IP0; }       // first key byte of the class
+  static constexpr int ent(int c) { return c == 0 ? 0 : npos(0) * stride(0); }  // first table entry
+  static constexpr int ENTRIES = ent(NC - 1) + npos(NC - 1) * stride(NC - 1);
+  static constexpr int POSITIONS = IDXB + SP;
+  static_assert(IP0 % CHAIN == 0 && IP1 % CHAIN == 0 && SP % CHAIN == 0, "whole chains per class");
   // the weight ring also holds the half tables while the lookup tables are built
   static constexpr int RING_BYTES_W = NW * WSLOT * 4;
-  static constexpr int HALF_BYTES = (P0 + P1) * 32 * 16;
+  static constexpr int HALF_BYTES = POSITIONS * 32 * 16;
   static constexpr int RING_BYTES = RING_BYTES_W > HALF_BYTES ? RING_BYTES_W : HALF_BYTES;
 };
 
-template <int MODE, int B0, int B1>
+template <int MODE, int B0, int B1, int VB>
 struct Lds {
   using F = Fmt<MODE, B0, B1>;
-  uint2 lut[F::E0 + F::E1];
+  uint64_t lut[F::ENTRIES];
   float qp[QH * KD];
   float qs[QH * KD];
   uint32_t ring[F::RING_BYTES / 4];
-  int amax[2 * QH];
   float cen[32];
+  float rng[3][QH];    // largest byte range of each class and head (float bits, atomicMax)
+  float offi[2][QH];   // index classes: sum over coordinates of the smallest term
+  float sgp[8][QH];    // sign class: sum of |S q'| over each 16-row tile
+  float uu[3][QH];     // per class and head: score step and offset, in log2 softmax units
+  float oo[3][QH];
   float abuf[2 * (NW / 2) * QH];
-  float hmul[2 * QH];
+  int ksf[NW / 2];     // final value-scale exponent of each score wave
   int pages[PAGE_CACHE];  // block-table entries of this workgroup's token range (paged cache)
 };
 
@@ -118,6 +146,7 @@ struct DecArgs {
   const int* block_table;  // [B][max_blocks] physical page of each logical page
   int max_blocks;
   int page_size;  // tokens per page, a multiple of TILE
+  int n_pages;    // pages in the pool (block-table entries are clamped below it)
 };
 
 // a query element as loaded: f32 bits, or bf16 / fp16 bits in the low half
@@ -133,7 +162,7 @@ __device__ inline float h2f(uint32_t bits16) { return __half2float(__ushort_as_h
 // 64 KiB the index times 8 is a single SDWA shift and BASE folds into the
 // ds_read immediate; past it, a field extract and a shift-add.
 // (BASE and k are constants once the caller's loop is unrolled.)
-__device__ __forceinline__ uint2 lut_read(const unsigned char* smem, uint32_t BASE, uint32_t w, int k) {
+__device__ __forceinline__ uint64_t lut_read(const unsigned char* smem, uint32_t BASE, uint32_t w, int k) {
   uint32_t off;
   if (BASE + 2048u <= 65536u) {
     switch (k) {
@@ -142,14 +171,14 @@ __device__ __forceinline__ uint2 lut_read(const unsigned char* smem, uint32_t BA
       case 2: asm("v_lshlrev_b32_sdwa %0, 3, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_2" : "=v"(off) : "v"(w)); break;
       default: asm("v_lshlrev_b32_sdwa %0, 3, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_3" : "=v"(off) : "v"(w)); break;
     }
-    return *(const uint2*)(smem + off + BASE);
+    return *(const uint64_t*)(smem + off + BASE);
   } else {
     // (the empty asm keeps the byte extract whole, so that shift and add
     // become one v_lshl_or / v_lshl_add)
     uint32_t b = __builtin_amdgcn_ubfe(w, 8 * k, 8);
     asm("" : "+v"(b));
     off = (b << 3) + BASE;
-    return *(const uint2*)(smem + off);
+    return *(const uint64_t*)(smem + off);
   }
 }
 
@@ -161,17 +190,6 @@ __device__ inline void static_for(Fn&& fn) {
   }
 }
 
-// Largest power of two P with P * bound <= 16384 (1 for a zero bound), from
-// the exponent of bound = m 2^e, m in [0.5, 1).
-__device__ inline float pow2_scale(float bound) {
-  if (!(bound > 0.0f)) return 1.0f;
-  int e;
-  const float m = frexpf(bound, &e);
-  int k = (m > 0.5f ? 14 : 15) - e;
-  k = k > 126 ? 126 : k < -126 ? -126 : k;
-  return ldexpf(1.0f, k);
-}
-
 // DPP lane moves (gfx9 encodings): quad permutations, half-row and row mirrors.
 template <int CTRL>
 __device__ inline float dpp(float v) {
@@ -179,28 +197,13 @@ __device__ inline float dpp(float v) {
 }
 constexpr int DPP_XOR1 = 0xB1, DPP_XOR2 = 0x4E, DPP_HALF_MIRROR = 0x141, DPP_ROW_MIRROR = 0x140;
 
-// Sum over each aligned group of eight lanes, in all eight.
-__device__ inline float sum8(float v) {
-  v += dpp<DPP_XOR1>(v);
-  v += dpp<DPP_XOR2>(v);
-  return v + dpp<DPP_HALF_MIRROR>(v);
-}
-
-// Maximum over the wave of a value that is already uniform in each aligned
-// group of eight lanes (for any value: pass it through max8 first).
-__device__ inline float wave_max_of_eights(float v) {
-  v = fmaxf(v, dpp<DPP_ROW_MIRROR>(v));
-  const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
-  const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
-  const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
-  const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
-  return fmaxf(fmaxf(a, b), fmaxf(c, d));
-}
-
-__device__ inline float max8(float v) {
-  v = fmaxf(v, dpp<DPP_XOR1>(v));
-  v = fmaxf(v, dpp<DPP_XOR2>(v));
-  return fmaxf(v, dpp<DPP_HALF_MIRROR>(v));
+// Sum over each aligned group of N (1, 2, 4 or 8) lanes, in all N.
+template <int N>
+__device__ inline float group_sum(float v) {
+  if constexpr (N >= 2) v += dpp<DPP_XOR1>(v);
+  if constexpr (N >= 4) v += dpp<DPP_XOR2>(v);
+  if constexpr (N >= 8) v += dpp<DPP_HALF_MIRROR>(v);
+  return v;
 }
 
 // Workgroup barrier for LDS hand-offs: waits for this wave's LDS accesses
@@ -214,16 +217,53 @@ __device__ inline void lds_barrier() {
 // A value every lane holds alike, moved to a scalar register.
 __device__ inline float uniform(float v) { return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v))); }
 
+// x[l] + x[l ^ 16] and x[l] + x[l ^ 32] in every lane: a permlane swap of a
+// value with itself hands each lane pair both values, one in each output.
+__device__ inline float sum_xor16(float v) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ inline float sum_xor32(float v) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ inline float max_xor16(float v) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ inline float max_xor32(float v) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+
+// Over the whole wave, in every lane: within rows of 16 by DPP, across rows
+// by permlane swaps (no LDS traffic).
 __device__ inline float wave_max(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m));
-  return v;
+  v = fmaxf(v, dpp<DPP_XOR1>(v));
+  v = fmaxf(v, dpp<DPP_XOR2>(v));
+  v = fmaxf(v, dpp<DPP_HALF_MIRROR>(v));
+  v = fmaxf(v, dpp<DPP_ROW_MIRROR>(v));
+  return max_xor32(max_xor16(v));
 }
 
 __device__ inline float wave_sum(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
-  return v;
+  v += dpp<DPP_XOR1>(v);
+  v += dpp<DPP_XOR2>(v);
+  v += dpp<DPP_HALF_MIRROR>(v);
+  v += dpp<DPP_ROW_MIRROR>(v);
+  return sum_xor32(sum_xor16(v));
+}
+
+// Largest of a non-negative integer over the wave (row reductions by DPP,
+// then the four rows through readlane).
+__device__ inline uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, DPP_XOR1, 0xF, 0xF, true));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, DPP_XOR2, 0xF, 0xF, true));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, DPP_HALF_MIRROR, 0xF, 0xF, true));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, DPP_ROW_MIRROR, 0xF, 0xF, true));
+  const uint32_t a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
+  const uint32_t c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
+  return max(max(a, b), max(c, d));
 }
 
 template <int MODE, int B0, int B1, int VB>
@@ -231,22 +271,33 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
   using F = Fmt<MODE, B0, B1>;
   // Static LDS (its offsets are known to the compiler, so table offsets fold
   // into the ds_read immediates).
-  __shared__ Lds<MODE, B0, B1> L;
+  __shared__ Lds<MODE, B0, B1, VB> L;
   unsigned char* smem = (unsigned char*)&L;
-  uint2* lut = L.lut;       // tables: class 0 [value][position], class 1 [position][value]
+  uint64_t* lut = L.lut;    // tables: per class [position][value], four 16-bit heads
   float* qp = L.qp;         // [QH][KD] rotated queries
   float* qs = L.qs;         // [QH][KD] S q' (PROD)
   uint32_t* wbuf = L.ring;  // [2][NW/2][4 groups][32 pairs][QH] half2 weights (groups padded)
-  int* amax = L.amax;       // [2][QH]
   float* cen = L.cen;       // [2][16] centroids of each part
-  float* abuf = L.abuf;     // [2][NW/2][QH] softmax rescale factors
-  float* hmul = L.hmul;     // [2][QH] score multipliers
+  float* abuf = L.abuf;     // [2][NW/2][QH] p.V rescale factors
 
   const tq_blob_header* H = (const tq_blob_header*)a.tables;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: branches on it are scalar
   const int split = blockIdx.x, quad = blockIdx.y, bh = blockIdx.z;
   const int b = bh / a.Hkv, hkv = bh % a.Hkv;
+
+  // Tables built for another format than this kernel's: nothing is read past
+  // the header; the workgroup's partials become NaN (and so the outputs).
+  const bool tables_ok = H->magic == TQ_BLOB_MAGIC && H->d == KD && H->mode == MODE && H->part_bits[0] == B0 &&
+                         (!F::GROUPED || H->part_bits[1] == B1) && (!F::QJL || H->m == KD);
+  if (!tables_ok) {
+    for (int i = tid; i < QH * PART; i += NT) {
+      const int gq = QH * quad + i / PART;
+      if (gq < a.G)
+        a.part[(((long long)b * a.Hq + hkv * a.G + gq) * a.n_split + split) * PART + i % PART] = __builtin_nanf("");
+    }
+    return;
+  }
   // lengths outside [0, max_ctx] are clamped into it: no read leaves the sequence's records
   const int ctx = min(max(a.ctx_len[b], 0), a.max_ctx);
   const int t_begin = split * a.chunk;
@@ -258,10 +309,9 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
   // publish fp16 weights p*scale; p.V waves (second half) accumulate those
   // weights against the value codes one round later.  Wave pw of each half
   // owns tiles pw, pw + NS, pw + 2 NS, ...; a two-slot LDS ring carries the
-  // weights and the softmax rescale factor from score wave pw to p.V wave pw,
-  // and one barrier per round separates producer and consumer.  Each wave
-  // loads its next tile's data one round ahead.
-  constexpr int NS = NW / 2;
+  // weights and the rescale factor from score wave pw to p.V wave pw, and one
+  // barrier per round separates producer and consumer.  Each wave loads its
+  // next tile's data one round ahead.
   constexpr int VROW = KD * VB / 8;  // bytes of a value-code row
   const bool scorer = wave < NS;
   const int pw = scorer ? wave : wave - NS;
@@ -282,7 +332,8 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
   // Record of token t of the tile starting at tb is tile_base(tb) + t: rec0
   // for a contiguous cache; for a paged one, through the block table entry of
   // the tile's page (a tile never straddles pages; tiles past the end use the
-  // page of t_last, where their clamped tokens are).
+  // page of t_last, where their clamped tokens are).  Entries are clamped
+  // into the pool, so a stale block table cannot send a read outside it.
   // The workgroup's block-table entries are staged in LDS by the prologue (a
   // global read here would wait behind the tile loads already in flight);
   // the host sizes the splits so that they fit in PAGE_CACHE entries.
@@ -301,7 +352,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
     const uint32_t* ip = (const uint32_t*)(a.idx + rec * F::IDXB);
 #pragma unroll
     for (int k = 0; k < F::IDXB / 4; ++k) d.kw[k] = ip[k];
-    if constexpr (F::PROD) {
+    if constexpr (F::QJL) {
       const uint4 sv = *(const uint4*)(a.signs + rec * (KD / 8));
       d.kw[F::IDXB / 4 + 0] = sv.x; d.kw[F::IDXB / 4 + 1] = sv.y;
       d.kw[F::IDXB / 4 + 2] = sv.z; d.kw[F::IDXB / 4 + 3] = sv.w;
@@ -356,31 +407,44 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
       qw1 = ((const uint16_t*)a.q)[qrow + lane + 64];
     }
   }
+  float cmin0 = 0.0f, cmax0 = 0.0f, cmin1 = 0.0f, cmax1 = 0.0f;
   if (wave < QH) {
     const float* sig0 = (const float*)(a.tables + H->off_sigma[0]);
     const float* sig1 = (const float*)(a.tables + H->off_sigma[n_parts > 1 ? 1 : 0]);
     sg0 = sig0[lane];
     sg1 = F::GROUPED ? sig1[lane] : sig0[lane + 64];
+    cmin0 = cent0[0];
+    cmax0 = cent0[lev0 - 1];
+    cmin1 = cent1[0];
+    cmax1 = cent1[lev1 - 1];
   }
-  // q_s = S q': thread -> (row tid / 8, 16-column chunk tid % 8), all 128 rows at once
-  static_assert(NT == 8 * KD, "S q' takes one row per eight threads");
-  const int srow = tid >> 3, sch = tid & 7;
-  uint4 sA = make_uint4(0, 0, 0, 0), sB = sA;
-  if constexpr (F::PROD) {
-    const uint4* sp = (const uint4*)((const uint16_t*)(a.tables + H->off_S) + (size_t)srow * KD + 16 * sch);
-    sA = sp[0];
-    sB = sp[1];
+  // S q' on MFMA: wave w < 8 takes rows 16w .. 16w + 15 of S (operand A: row
+  // 16w + (lane & 15), coordinates 32 ks + 8 (lane >> 4) .. + 7 of step ks).
+  uint4 sfrag[4] = {};
+  if constexpr (F::QJL) {
+    if (wave < 8) {
+      const uint4* sp = (const uint4*)((const uint16_t*)(a.tables + H->off_S) +
+                                       (size_t)(16 * wave + (lane & 15)) * KD + 8 * (lane >> 4));
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) sfrag[ks] = sp[4 * ks];
+    }
   }
   if (tid < 32) {
     const int part = tid >> 4, k = tid & 15;
     cen[tid] = part < n_parts && k < (part ? lev1 : lev0) ? (part ? cent1 : cent0)[k] : 0.0f;
   }
-  if (!F::GROUPED && tid < QH) amax[QH + tid] = 0;
-  for (int i = tid; i < n_pages_wg; i += NT) L.pages[i] = a.block_table[(long long)b * a.max_blocks + lp0 + i];
+  if (F::QJL && tid < QH) L.rng[F::NC - 1][tid] = 0.0f;
+  for (int i = tid; i < n_pages_wg; i += NT) {
+    const int pg = a.block_table[(long long)b * a.max_blocks + lp0 + i];
+    L.pages[i] = min(max(pg, 0), a.n_pages - 1);
+  }
 
   // Walsh-Hadamard transform of sigma * q in registers (one 128-point
   // transform, or two 64-point ones for GROUPED): butterflies on lane bits
-  // through shuffles, the top stage inside the lane.
+  // through shuffles, the top stage inside the lane.  Then, per index class,
+  // the table step and offset: a byte holding coordinates J takes values
+  // sum_{j in J} q'_j c[f_j]; its range is (c_max - c_min) sum_J |q'_j| and
+  // its smallest value sum_J min(q'_j c_min, q'_j c_max).
   if (wave < QH) {
     x0 = q_word_to_float(qw0, a.q_dtype) * sg0;
     x1 = q_word_to_float(qw1, a.q_dtype) * sg1;
@@ -398,12 +462,27 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
     }
     qp[wave * KD + lane] = x0;
     qp[wave * KD + lane + 64] = x1;
-    // largest |q'| per table class (GROUPED: per half)
-    const float m0 = wave_max_of_eights(max8(F::GROUPED ? fabsf(x0) : fmaxf(fabsf(x0), fabsf(x1))));
-    const float m1 = F::GROUPED ? wave_max_of_eights(max8(fabsf(x1))) : 0.0f;
-    if (lane == 0) {
-      amax[wave] = __float_as_int(m0);
-      if (F::GROUPED) amax[QH + wave] = __float_as_int(m1);
+    constexpr int CPB0 = 8 / F::W0, CPB1 = 8 / F::W1;
+    const float g0 = group_sum<CPB0>(fabsf(x0));
+    const float lo0 = fminf(x0 * cmin0, x0 * cmax0);
+    if constexpr (F::GROUPED) {
+      const float g1 = group_sum<CPB1>(fabsf(x1));
+      const float r0 = wave_max(g0) * (cmax0 - cmin0), r1 = wave_max(g1) * (cmax1 - cmin1);
+      const float o0 = wave_sum(lo0), o1 = wave_sum(fminf(x1 * cmin1, x1 * cmax1));
+      if (lane == 0) {
+        L.rng[0][wave] = r0;
+        L.rng[1][wave] = r1;
+        L.offi[0][wave] = o0;
+        L.offi[1][wave] = o1;
+      }
+    } else {
+      const float g1 = group_sum<CPB0>(fabsf(x1));
+      const float r0 = wave_max(fmaxf(g0, g1)) * (cmax0 - cmin0);
+      const float o0 = wave_sum(lo0 + fminf(x1 * cmin0, x1 * cmax0));
+      if (lane == 0) {
+        L.rng[0][wave] = r0;
+        L.offi[0][wave] = o0;
+      }
     }
   }
   // Only LDS data is shared here, so the barrier need not wait for global
@@ -421,105 +500,138 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
     if (scorer) load_keys(tile_tb(0), kd);
     else load_codes(tile_tb(0), codes);
   }
-  if constexpr (F::PROD) {
-    const uint32_t sw[8] = {sA.x, sA.y, sA.z, sA.w, sB.x, sB.y, sB.z, sB.w};
-    float part[QH] = {0.0f, 0.0f, 0.0f, 0.0f};
+  if constexpr (F::QJL) {
+    if (wave < 8) {
+      // operand B: query head n = lane & 15 (heads past QH are zero), the
+      // same coordinates as A's; q' split into fp16 hi + lo (S is fp16, so
+      // each product is exact and the sum is fp32)
+      const int n = lane & 15;
+      floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int hh = 0; hh < QH; ++hh) {
-      const float4* qv = (const float4*)(qp + hh * KD + 16 * sch);
+      for (int ks = 0; ks < 4; ++ks) {
+        half8_t bh = {}, bl = {};
+        if (n < QH) {
+          const float4* src = (const float4*)(qp + n * KD + 32 * ks + 8 * (lane >> 4));
+          const float4 v0 = src[0], v1 = src[1];
+          const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const float4 v = qv[c];
-        part[hh] = fmaf(h2f(sw[2 * c] & 0xFFFFu), v.x, part[hh]);
-        part[hh] = fmaf(h2f(sw[2 * c] >> 16), v.y, part[hh]);
-        part[hh] = fmaf(h2f(sw[2 * c + 1] & 0xFFFFu), v.z, part[hh]);
-        part[hh] = fmaf(h2f(sw[2 * c + 1] >> 16), v.w, part[hh]);
+          for (int i = 0; i < 8; ++i) {
+            bh[i] = (_Float16)v[i];
+            bl[i] = (_Float16)(v[i] - (float)bh[i]);
+          }
+        }
+        const half8_t af = __builtin_bit_cast(half8_t, sfrag[ks]);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bl, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bh, acc, 0, 0, 0);
+      }
+      // lane holds S q' of head n for rows 16 wave + 4 (lane >> 4) + i
+      if (n < QH) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) qs[n * KD + 16 * wave + 4 * (lane >> 4) + i] = acc[i];
+      }
+      // sign bytes 2 wave (lanes 0..31) and 2 wave + 1 (lanes 32..63): a
+      // byte's values are sum_i +-(S q')_i over its 8 rows, range 2 sum |.|
+      float v = fabsf(acc[0]) + fabsf(acc[1]) + fabsf(acc[2]) + fabsf(acc[3]);
+      v = sum_xor16(v);
+      const float rmax = 2.0f * max_xor32(v);
+      const float tot = sum_xor32(v);
+      if (lane < QH) {
+        atomicMax((int*)&L.rng[F::NC - 1][lane], __float_as_int(rmax));
+        L.sgp[wave][lane] = tot;
       }
     }
-#pragma unroll
-    for (int hh = 0; hh < QH; ++hh) {
-      part[hh] = sum8(part[hh]);
-      if (sch == 0) qs[hh * KD + srow] = part[hh];
-      const float m = wave_max_of_eights(fabsf(part[hh]));
-      if (lane == 0) atomicMax(&amax[QH + hh], __float_as_int(m));
-    }
+    lds_barrier();
   }
-  if constexpr (F::PROD) lds_barrier();
-  // per-head, per-class power-of-two table scale: the largest possible entry
-  // (|q'| bound x largest centroid x coordinates per byte) stays <= 16384
-  auto table_scale = [&](int cls, int hh) {
-    float cmax = 1.0f;
-    int cpb = 8;
-    if (!(F::PROD && cls == 1)) {
-      cmax = fabsf(cen[cls ? 16 + lev1 - 1 : lev0 - 1]);  // LDS: no wait behind the tile loads
-      cpb = cls == 0 ? F::CPB0 : F::CPB1;
-    }
-    return pow2_scale(__int_as_float(amax[cls * QH + hh]) * cmax * cpb);
-  };
-  // per-token multipliers of the two table classes, with the scales undone:
-  // hmul[0][h] multiplies the norm, hmul[1][h] the residual norm (PROD) or
-  // the second half's norm (GROUPED).  Kept in LDS, read where used.
-  if (tid < QH) {
-    hmul[tid] = 1.0f / (table_scale(0, tid) * (float)F::PD);
-    hmul[QH + tid] = F::PROD ? 1.2533141373155003f / ((float)KD * sqrtf((float)KD) * table_scale(1, tid))
-                             : 1.0f / (table_scale(1, tid) * (float)F::PD);
-  }
-  // Half tables: for each byte position, class, nibble half and nibble value,
-  // the four heads' partial sums over the coordinates (or sign rows) that
-  // nibble holds, already scaled.  A byte's entry is then lo[v & 15] +
-  // hi[v >> 4].  They live in the weight ring, unused until the main loop.
-  float4* halves = (float4*)wbuf;  // [P0 + P1][2][16]
-  for (int i = tid; i < (F::P0 + F::P1) * 32; i += NT) {
+  // Half tables: for each byte position, nibble half and nibble value, the
+  // four heads' partial sums over the coordinates (or sign rows) that nibble
+  // holds, less the smallest such sum, in table steps (the low half carries
+  // the +1/2 of the rounding).  A byte's entry is then lo[v & 15] + hi[v >> 4]
+  // rounded down.  They live in the weight ring, unused until the main loop.
+  float4* halves = (float4*)wbuf;  // [POSITIONS][2][16]
+  for (int i = tid; i < F::POSITIONS * 32; i += NT) {
     const int pos = i >> 5, half = (i >> 4) & 1, n = i & 15;
-    const bool c1 = pos >= F::P0;
-    const int p = c1 ? pos - F::P0 : pos;
-    float sv[QH] = {0.0f, 0.0f, 0.0f, 0.0f};
-    if (c1 && F::PROD) {
+    const int c = pos < F::npos(0) ? 0 : 1;
+    const int p = pos - (c ? F::npos(0) : 0);
+    const int kind = c == 0 ? 0 : F::kind(1);
+    float sv[QH] = {0.0f, 0.0f, 0.0f, 0.0f}, mn[QH] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (kind == 2) {
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const float sg = ((n >> k) & 1) ? 1.0f : -1.0f;
+        const bool one = (n >> k) & 1;
 #pragma unroll
-        for (int hh = 0; hh < QH; ++hh) sv[hh] = fmaf(sg, qs[hh * KD + 8 * p + 4 * half + k], sv[hh]);
+        for (int hh = 0; hh < QH; ++hh) {
+          const float z = qs[hh * KD + 8 * p + 4 * half + k];
+          sv[hh] += one ? z : -z;
+          mn[hh] -= fabsf(z);
+        }
       }
     } else {
-      const int W = c1 ? F::W1 : F::W0;
+      const int W = kind ? F::W1 : F::W0;
       const int per = 4 / W;  // coordinates per nibble
-      const int fmask = (1 << (c1 ? B1 : B0)) - 1;
-      const float* cn = cen + (c1 ? 16 : 0);
-      const int j0 = (c1 ? F::PD : 0) + p * (8 / W) + half * per;
+      const int fmask = (1 << (kind ? B1 : B0)) - 1;
+      const float* cn = cen + (kind ? 16 : 0);
+      const float c_lo = cn[0], c_hi = cn[(kind ? lev1 : lev0) - 1];
+      const int j0 = (kind ? F::PD : 0) + p * (8 / W) + half * per;
       for (int k = 0; k < per; ++k) {
-        const float c = cn[(n >> (W * k)) & fmask];
+        const float cv = cn[(n >> (W * k)) & fmask];
 #pragma unroll
-        for (int hh = 0; hh < QH; ++hh) sv[hh] = fmaf(c, qp[hh * KD + j0 + k], sv[hh]);
+        for (int hh = 0; hh < QH; ++hh) {
+          const float z = qp[hh * KD + j0 + k];
+          sv[hh] = fmaf(cv, z, sv[hh]);
+          mn[hh] += fminf(z * c_lo, z * c_hi);
+        }
       }
     }
-    const int cls = c1 ? 1 : 0;
-    halves[i] = make_float4(sv[0] * table_scale(cls, 0), sv[1] * table_scale(cls, 1),
-                            sv[2] * table_scale(cls, 2), sv[3] * table_scale(cls, 3));
+    const float4 rg = *(const float4*)L.rng[c];
+    const float rgv[QH] = {rg.x, rg.y, rg.z, rg.w};
+    float o[QH];
+#pragma unroll
+    for (int hh = 0; hh < QH; ++hh) {
+      const float inv = rgv[hh] > 0.0f ? EMAX / rgv[hh] : 0.0f;
+      o[hh] = fmaf(sv[hh] - mn[hh], inv, half ? 0.0f : 0.5f);
+    }
+    halves[i] = make_float4(o[0], o[1], o[2], o[3]);
   }
   lds_barrier();
   // One thread per (position, low nibble) walks the high nibbles: its low
   // half stays in registers, the high halves are read by sixteen lanes at once.
-  for (int t = tid; t < (F::P0 + F::P1) * 16; t += NT) {
+  for (int t = tid; t < F::POSITIONS * 16; t += NT) {
     const int pos = t >> 4, lo = t & 15;
-    const bool c1 = pos >= F::P0;
-    const int S = c1 ? F::S1 : F::S0;
-    uint2* dst = lut + (c1 ? F::E0 + (pos - F::P0) * F::S1 : pos * F::S0);
+    const int c = pos < F::npos(0) ? 0 : 1;
+    const int S = c ? F::stride(1) : F::stride(0);
+    uint64_t* dst = lut + (c ? F::ent(1) + (pos - F::npos(0)) * F::stride(1) : pos * F::stride(0));
     const float4 lo4 = halves[pos * 32 + lo];
 #pragma unroll 4
     for (int hi = 0; hi < 16; ++hi) {
       const int v = hi * 16 + lo;
       if (v < S) {
         const float4 hi4 = halves[pos * 32 + 16 + hi];
-        // round to nearest even, two heads per conversion
-        const half2_t e01 = __builtin_convertvector((float2_t){lo4.x + hi4.x, lo4.y + hi4.y}, half2_t);
-        const half2_t e23 = __builtin_convertvector((float2_t){lo4.z + hi4.z, lo4.w + hi4.w}, half2_t);
-        dst[v] = make_uint2(__builtin_bit_cast(uint32_t, e01), __builtin_bit_cast(uint32_t, e23));
+        const uint32_t e0 = (uint32_t)(lo4.x + hi4.x), e1 = (uint32_t)(lo4.y + hi4.y);
+        const uint32_t e2 = (uint32_t)(lo4.z + hi4.z), e3 = (uint32_t)(lo4.w + hi4.w);
+        dst[v] = (uint64_t)(e0 | (e1 << 16)) | ((uint64_t)(e2 | (e3 << 16)) << 32);
       }
     }
   }
-  lds_barrier();
+  // per class and head: the table step (range / EMAX) and the summed
+  // offsets, with the score multiplier of the class and the softmax scale
+  // (log2 units) folded in
   const float xscale = a.sm_scale * LOG2E;
+  if (tid < F::NC * QH) {
+    const int c = tid >> 2, hh = tid & 3;
+    const int kind = c == 0 ? 0 : F::kind(1);
+    float off;
+    if (kind == 2) {
+      off = 0.0f;
+      for (int w = 0; w < 8; ++w) off -= L.sgp[w][hh];
+    } else {
+      off = L.offi[kind][hh];
+    }
+    const float mul = kind == 2 ? SQRT_HALF_PI / ((float)KD * sqrtf((float)KD)) : 1.0f / (float)F::PD;
+    const float unit = L.rng[c][hh] / EMAX;
+    L.uu[c][hh] = mul * unit * xscale;
+    L.oo[c][hh] = mul * off * xscale;
+  }
+  lds_barrier();
 
   const half2_t e10 = {(_Float16)1.0f, (_Float16)0.0f}, e01 = {(_Float16)0.0f, (_Float16)1.0f};
   float* red = (float*)smem;  // [NS][QH][2 + 4 + KD], over the tables once every wave is done
@@ -528,6 +640,13 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
   // The two kinds of waves run separate loops with the same number of
   // barriers (rounds + 1), so neither keeps the other's registers live.
   if (scorer) {
+    float UU[F::NC][QH], OO[F::NC][QH];
+#pragma unroll
+    for (int c = 0; c < F::NC; ++c) {
+      const float4 uv = *(const float4*)L.uu[c], ov = *(const float4*)L.oo[c];
+      UU[c][0] = uniform(uv.x); UU[c][1] = uniform(uv.y); UU[c][2] = uniform(uv.z); UU[c][3] = uniform(uv.w);
+      OO[c][0] = uniform(ov.x); OO[c][1] = uniform(ov.y); OO[c][2] = uniform(ov.z); OO[c][3] = uniform(ov.w);
+    }
     float m_run[QH], l_run[QH], zacc[QH][4];
 #pragma unroll
     for (int hh = 0; hh < QH; ++hh) {
@@ -536,93 +655,105 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
 #pragma unroll
       for (int k = 0; k < 4; ++k) zacc[hh][k] = 0.0f;
     }
-    // two key buffers in turn: a round scores one while the next tile's
-    // bytes arrive in the other
+    // value scales are multiplied by 2^ks (ks in [-15, 15], one per tile,
+    // kept while the tile's largest scale times 2^ks stays in [2^-8, 2))
+    int ks = 0;
+    float ksc = 1.0f;
     auto s_round = [&](int r, KeyData& kd) {
       const int tb = tile_tb(r);
       if (r < rounds && tb < t_end) {
         // ---------------- scores: lane = token
         const int t = tb + lane;
         const bool valid = t < t_end;
-        float sc[QH];
+        float x[QH];
         {
+          // per-token multipliers of the classes: norm (part 0), residual
+          // norm (PROD) or second half's norm (GROUPED)
           const float m0 = F::GROUPED ? h2f(kd.nrm & 0xFFFFu) : h2f(kd.nrm);
           const float m1 = F::GROUPED ? h2f(kd.nrm >> 16) : h2f(kd.rn);
-          // table sums in fp32: fdot2(entry pair, (1,0)) adds one fp16 exactly
-          float A[QH] = {0, 0, 0, 0}, Bc[QH] = {0, 0, 0, 0};
-          // Index nibbles of 3-bit codes have their high bit clear (tq_encode_keys
-          // writes them so), so a byte is a table index as it stands.
+          // The table reads run in batches of two chains (eight reads),
+          // software-pipelined: batch i + 1 is issued before batch i is
+          // summed, so one batch's latency hides behind the other's.
+          constexpr int NCH0 = F::npos(0) / CHAIN;
+          constexpr int NCH = NCH0 + (F::NC > 1 ? F::npos(1) / CHAIN : 0);
+          constexpr int NB = NCH / 2;
+          static_assert(NCH % 2 == 0, "whole batches of two chains");
+          uint32_t acc[F::NC][QH];
+          uint64_t E[2][2 * CHAIN];
+          auto issue = [&](auto bb, uint64_t* dst) {
+            constexpr int bt = decltype(bb)::value;
 #pragma unroll
-          for (int p = 0; p < F::P0; ++p) {
-            // cap the table reads in flight (each holds two registers); the
-            // empty asm keeps each batch's accumulation ahead of the next
-            // batch instead of letting it sink below all the reads
-            if (p % TQ_DEC_LOOKUP_BATCH == 0) {
-              if (p > 0) asm volatile("" : "+v"(A[0]), "+v"(A[1]), "+v"(A[2]), "+v"(A[3]));
-              __builtin_amdgcn_sched_barrier(0);
+            for (int j = 0; j < 2 * CHAIN; ++j) {
+              const int g = 2 * bt + j / CHAIN;
+              const int c = g < NCH0 ? 0 : 1;
+              const int pos = (g - (c ? NCH0 : 0)) * CHAIN + j % CHAIN;
+              const int byte = (c ? F::kbyte(1) : 0) + pos;
+              const uint32_t base = (uint32_t)((c ? F::ent(1) : 0) + pos * (c ? F::stride(1) : F::stride(0))) * 8u;
+              dst[j] = lut_read(smem, base, kd.kw[byte >> 2], byte & 3);
             }
-            const uint2 e = lut_read(smem, (uint32_t)(p * F::S0) * 8u, kd.kw[p >> 2], p & 3);
-            const half2_t x01 = __builtin_bit_cast(half2_t, e.x), x23 = __builtin_bit_cast(half2_t, e.y);
-            if (p == 0) {  // the first entries start the sums (the same values fdot2 onto 0 gives)
-              A[0] = (float)x01[0]; A[1] = (float)x01[1]; A[2] = (float)x23[0]; A[3] = (float)x23[1];
-            } else {
-              A[0] = __builtin_amdgcn_fdot2(x01, e10, A[0], false);
-              A[1] = __builtin_amdgcn_fdot2(x01, e01, A[1], false);
-              A[2] = __builtin_amdgcn_fdot2(x23, e10, A[2], false);
-              A[3] = __builtin_amdgcn_fdot2(x23, e01, A[3], false);
-            }
-          }
+          };
+          auto reduce = [&](auto bb, const uint64_t* src) {
+            constexpr int bt = decltype(bb)::value;
 #pragma unroll
-          for (int p = 0; p < F::P1; p += (F::PROD ? 2 : 1)) {
-            if (p % TQ_DEC_LOOKUP_BATCH == 0) {
-              if (p > 0) asm volatile("" : "+v"(Bc[0]), "+v"(Bc[1]), "+v"(Bc[2]), "+v"(Bc[3]));
-              __builtin_amdgcn_sched_barrier(0);
+            for (int i = 0; i < 2; ++i) {
+              const int g = 2 * bt + i;
+              const int c = g < NCH0 ? 0 : 1;
+              const int q = g - (c ? NCH0 : 0);
+              const uint64_t sum = src[CHAIN * i] + src[CHAIN * i + 1] + src[CHAIN * i + 2] + src[CHAIN * i + 3];
+              const uint32_t lo = (uint32_t)sum, hi = (uint32_t)(sum >> 32);
+              if (q == 0) {
+                acc[c][0] = lo & 0xFFFFu;
+                acc[c][1] = lo >> 16;
+                acc[c][2] = hi & 0xFFFFu;
+                acc[c][3] = hi >> 16;
+              } else {
+                const ushort2_t l2 = __builtin_bit_cast(ushort2_t, lo), h2 = __builtin_bit_cast(ushort2_t, hi);
+                const ushort2_t u10 = {1, 0}, u01 = {0, 1};
+                acc[c][0] = __builtin_amdgcn_udot2(l2, u10, acc[c][0], false);
+                acc[c][1] = __builtin_amdgcn_udot2(l2, u01, acc[c][1], false);
+                acc[c][2] = __builtin_amdgcn_udot2(h2, u10, acc[c][2], false);
+                acc[c][3] = __builtin_amdgcn_udot2(h2, u01, acc[c][3], false);
+              }
             }
-            const int byte = F::P0 + p;
-            const uint2 e = lut_read(smem, (uint32_t)(F::E0 + p * F::S1) * 8u, kd.kw[byte >> 2], byte & 3);
-            half2_t x01 = __builtin_bit_cast(half2_t, e.x), x23 = __builtin_bit_cast(half2_t, e.y);
-            if constexpr (F::PROD) {
-              // QJL sign bytes two at a time: their fp16 entries are added in
-              // fp16 first (one packed add per head pair), halving the
-              // accumulate work of this smaller term of the score
-              const uint2 f = lut_read(smem, (uint32_t)(F::E0 + (p + 1) * F::S1) * 8u, kd.kw[(byte + 1) >> 2], (byte + 1) & 3);
-              x01 += __builtin_bit_cast(half2_t, f.x);
-              x23 += __builtin_bit_cast(half2_t, f.y);
-            }
-            if (p == 0) {
-              Bc[0] = (float)x01[0]; Bc[1] = (float)x01[1]; Bc[2] = (float)x23[0]; Bc[3] = (float)x23[1];
-            } else {
-              Bc[0] = __builtin_amdgcn_fdot2(x01, e10, Bc[0], false);
-              Bc[1] = __builtin_amdgcn_fdot2(x01, e01, Bc[1], false);
-              Bc[2] = __builtin_amdgcn_fdot2(x23, e10, Bc[2], false);
-              Bc[3] = __builtin_amdgcn_fdot2(x23, e01, Bc[3], false);
-            }
-          }
-          const float4 h0 = *(const float4*)hmul, h1 = *(const float4*)(hmul + QH);
-          const float mul0[QH] = {h0.x, h0.y, h0.z, h0.w}, mul1[QH] = {h1.x, h1.y, h1.z, h1.w};
+          };
+#ifdef TQ_DEC_PIPE
+          static_for<0, NB + 1>([&](auto bb) {
+            constexpr int bt = decltype(bb)::value;
+            if constexpr (bt < NB) issue(std::integral_constant<int, bt>{}, E[bt & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (bt >= 1) reduce(std::integral_constant<int, bt - 1>{}, E[(bt - 1) & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+          });
+#else
+          static_for<0, NB>([&](auto bb) {
+            issue(bb, E[0]);
+            __builtin_amdgcn_sched_barrier(0);
+            reduce(bb, E[0]);
+            __builtin_amdgcn_sched_barrier(0);
+          });
+#endif
 #pragma unroll
           for (int hh = 0; hh < QH; ++hh) {
-            if constexpr (F::P1 > 0) sc[hh] = valid ? m0 * mul0[hh] * A[hh] + m1 * mul1[hh] * Bc[hh] : -INFINITY;
-            else sc[hh] = valid ? m0 * mul0[hh] * A[hh] : -INFINITY;  // MSE: one table class
+            float v = m0 * fmaf((float)acc[0][hh], UU[0][hh], OO[0][hh]);
+            if constexpr (F::NC > 1) v = fmaf(m1, fmaf((float)acc[1][hh], UU[1][hh], OO[1][hh]), v);
+            x[hh] = valid ? v : -INFINITY;  // log2 softmax units
           }
           if (a.scores && valid) {
+            const float inv_x = 1.0f / xscale;
 #pragma unroll
             for (int hh = 0; hh < QH; ++hh) {
               const int gq = QH * quad + hh;
-              if (gq < a.G) a.scores[((long long)b * a.Hq + hkv * a.G + gq) * a.max_ctx + t] = sc[hh];
+              if (gq < a.G) a.scores[((long long)b * a.Hq + hkv * a.G + gq) * a.max_ctx + t] = x[hh] * inv_x;
             }
           }
         }
         // ---------------- online softmax (base 2).  The wave-wide max is
         // only recomputed when some lane exceeds the running max; otherwise
         // every p = 2^(x - m) <= 1 already and nothing needs rescaling.
-        float x[QH], alpha[QH] = {1.0f, 1.0f, 1.0f, 1.0f};
+        float alpha[QH] = {1.0f, 1.0f, 1.0f, 1.0f};
         bool exceed = false;
 #pragma unroll
-        for (int hh = 0; hh < QH; ++hh) {
-          x[hh] = sc[hh] * xscale;  // -inf for missing tokens
-          exceed |= x[hh] > m_run[hh];
-        }
+        for (int hh = 0; hh < QH; ++hh) exceed |= x[hh] > m_run[hh];
         if (__builtin_amdgcn_ballot_w64(exceed) != 0) {
 #pragma unroll
           for (int hh = 0; hh < QH; ++hh) {
@@ -634,33 +765,54 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
             for (int k = 0; k < 4; ++k) zacc[hh][k] *= alpha[hh];
           }
         }
+        // the tile's largest value scale (fp16 >= 0: compared as integers);
+        // a new power of two when it leaves [2^-8, 2) times the current one
+        const uint32_t smx2 = max(kd.sv.x & 0x7FFF7FFFu, kd.sv.y & 0x7FFF7FFFu);
+        const uint32_t smx = wave_max_u32(max(smx2 & 0xFFFFu, smx2 >> 16));
+        float fac = 1.0f;
+        {
+          const float smax = h2f(smx);
+          const float rel = smax * ksc;
+          if (smax > 0.0f && (rel >= 2.0f || rel < 0.00390625f)) {
+            int e;
+            (void)frexpf(smax, &e);        // smax = m 2^e, m in [0.5, 1)
+            const int knew = min(max(1 - e, -15), 15);
+            fac = ldexpf(1.0f, knew - ks);
+            ks = knew;
+            ksc = ldexpf(1.0f, ks);
+          }
+        }
         const uint2 zv = kd.zv, sv = kd.sv;
+        // the next tile's key bytes go out now, into the buffer this tile's
+        // lookups are done with
         load_keys(tile_tb(r + 1), kd);
-        float zz[4], ss[4];
+        float zz[4];
         zz[0] = h2f(zv.x & 0xFFFFu); zz[1] = h2f(zv.x >> 16);
         zz[2] = h2f(zv.y & 0xFFFFu); zz[3] = h2f(zv.y >> 16);
-        ss[0] = h2f(sv.x & 0xFFFFu); ss[1] = h2f(sv.x >> 16);
-        ss[2] = h2f(sv.y & 0xFFFFu); ss[3] = h2f(sv.y >> 16);
         float p[QH];
 #pragma unroll
         for (int hh = 0; hh < QH; ++hh) {
-          // m_run is finite (lane 0 holds a valid token) and x - m_run <= 0
-          p[hh] = __builtin_amdgcn_exp2f(x[hh] - m_run[hh]);
+          // p * 2^14 (m_run is finite: lane 0 holds a valid token)
+          p[hh] = __builtin_amdgcn_exp2f(x[hh] - (m_run[hh] - PSCALE));
           l_run[hh] += p[hh];
 #pragma unroll
           for (int k = 0; k < 4; ++k) zacc[hh][k] = fmaf(p[hh], zz[k], zacc[hh][k]);
         }
-        // weights p * scale as fp16 (p rounded to fp16, then two heads per
-        // packed multiply), paired by token: [group][pair][head] = (w_even, w_odd);
-        // the group stride is padded so that neither these stores nor the p.V
-        // waves' 16-byte reads pile onto a few LDS banks
+        // weights (p 2^14) * (scale 2^ks) as fp16 (both factors rounded to
+        // fp16, then two heads per packed multiply), paired by token:
+        // [group][pair][head] = (w_even, w_odd); the group stride is padded so
+        // that neither these stores nor the p.V waves' 16-byte reads pile
+        // onto a few LDS banks
         uint16_t* wb16 = (uint16_t*)(wbuf + ((r & 1) * NS + pw) * WSLOT);
         const int pair = lane >> 1, odd = lane & 1;
         const half2_t p01 = __builtin_convertvector((float2_t){p[0], p[1]}, half2_t);
         const half2_t p23 = __builtin_convertvector((float2_t){p[2], p[3]}, half2_t);
+        const half2_t kk2 = {(_Float16)ksc, (_Float16)ksc};
+        const half2_t s01 = __builtin_bit_cast(half2_t, sv.x) * kk2, s23 = __builtin_bit_cast(half2_t, sv.y) * kk2;
+        const _Float16 sk[4] = {s01[0], s01[1], s23[0], s23[1]};
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          const half2_t s2 = {(_Float16)ss[k], (_Float16)ss[k]};
+          const half2_t s2 = {sk[k], sk[k]};
           const half2_t w01 = p01 * s2, w23 = p23 * s2;
           wb16[(k * WGRP + pair * QH + 0) * 2 + odd] = __builtin_bit_cast(uint32_t, w01) & 0xFFFFu;
           wb16[(k * WGRP + pair * QH + 1) * 2 + odd] = __builtin_bit_cast(uint32_t, w01) >> 16;
@@ -669,7 +821,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
         }
         if (lane == 0) {
 #pragma unroll
-          for (int hh = 0; hh < QH; ++hh) abuf[((r & 1) * NS + pw) * QH + hh] = alpha[hh];
+          for (int hh = 0; hh < QH; ++hh) abuf[((r & 1) * NS + pw) * QH + hh] = alpha[hh] * fac;
         }
       }
     };
@@ -690,14 +842,15 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
         for (int k = 0; k < 4; ++k) mine[hh * RS + 2 + k] = zs[k];
       }
     }
+    if (lane == 0) L.ksf[pw] = ks;
   } else {
     float acc[QH][8];
 #pragma unroll
     for (int hh = 0; hh < QH; ++hh)
 #pragma unroll
       for (int k = 0; k < 8; ++k) acc[hh][k] = 0.0f;
-    // two code buffers in turn: a round consumes one while the next tile's
-    // codes arrive in the other
+    // two code buffers in turn: round r consumes tile r - 1 while the codes
+    // of tile r arrive in the other
     uint32_t codes2[16];
     auto pv_round = [&](int r, const uint32_t* cur, uint32_t* nxt) {
       const int tb = r >= 1 ? tile_tb(r - 1) : t_end;
@@ -731,10 +884,10 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
             pairs[4] = Y2 & 0x00030003u; pairs[5] = Y2 & 0x000F000Fu; pairs[6] = Y2 & 0x003F003Fu; pairs[7] = Y2;
           } else {
 #pragma unroll
-            for (int b = 0; b < 4; ++b) {  // byte b of A and of B -> bytes 0, 2
-              const uint32_t Yb = __builtin_amdgcn_perm(cB, cA, 0x0c000c00u | ((4u + b) << 16) | (uint32_t)b);
-              pairs[2 * b] = Yb & 0x000F000Fu;
-              pairs[2 * b + 1] = Yb;
+            for (int bb = 0; bb < 4; ++bb) {  // byte bb of A and of B -> bytes 0, 2
+              const uint32_t Yb = __builtin_amdgcn_perm(cB, cA, 0x0c000c00u | ((4u + bb) << 16) | (uint32_t)bb);
+              pairs[2 * bb] = Yb & 0x000F000Fu;
+              pairs[2 * bb + 1] = Yb;
             }
           }
 #pragma unroll
@@ -764,9 +917,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
       float r[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        r[i] = acc[hh][i];
-        r[i] += __shfl_xor(r[i], 16);
-        r[i] += __shfl_xor(r[i], 32);
+        r[i] = sum_xor32(sum_xor16(acc[hh][i]));
       }
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -779,25 +930,27 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
     }
   }
   __syncthreads();
+  // Combine the NS streams (score wave pw + p.V wave pw) of this workgroup:
+  // p.V sums are in units of 2^ks of their stream's final value scale.
   for (int i = tid; i < QH * KD; i += NT) {
     const int hh = i / KD, j = i % KD;
     const int gq = QH * quad + hh;
     float M = -INFINITY;
     for (int w = 0; w < NS; ++w) M = fmaxf(M, red[(w * QH + hh) * RS]);
-    float L = 0.0f, O = 0.0f;
+    float Ls = 0.0f, O = 0.0f;
     if (M != -INFINITY) {
       for (int w = 0; w < NS; ++w) {
         const float* rr = red + (w * QH + hh) * RS;
         const float f = rr[0] == -INFINITY ? 0.0f : exp2f(rr[0] - M);
-        L = fmaf(rr[1], f, L);
-        O = fmaf(rr[6 + j] + rr[2 + j / 32], f, O);
+        Ls = fmaf(rr[1], f, Ls);
+        O = fmaf(fmaf(rr[6 + j], ldexpf(1.0f, -L.ksf[w]), rr[2 + j / 32]), f, O);
       }
     }
     if (gq < a.G) {
       float* dst = a.part + (((long long)b * a.Hq + hkv * a.G + gq) * a.n_split + split) * PART;
       if (j == 0) {
         dst[0] = M;
-        dst[1] = L;
+        dst[1] = Ls;
       }
       dst[2 + j] = O;
     }
@@ -805,23 +958,30 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
 }
 
 // out[b][h][:] = sum_s O_s 2^(M_s - M) / sum_s L_s 2^(M_s - M), in split order.
+// A NaN sum (tables that do not match the kernel's format) makes the row NaN.
 __global__ __launch_bounds__(KD) void merge_kernel(const float* part, int n_split, float* out,
                                                    float* lse) {
   const int bh = blockIdx.x, j = threadIdx.x;
   const float* p = part + (long long)bh * n_split * PART;
   float M = -INFINITY;
-  for (int s = 0; s < n_split; ++s) M = fmaxf(M, p[s * PART]);
-  float L = 0.0f, O = 0.0f;
+  bool bad = false;
+  for (int s = 0; s < n_split; ++s) {
+    M = fmaxf(M, p[s * PART]);
+    bad |= p[s * PART + 1] != p[s * PART + 1];
+  }
+  float Ls = 0.0f, O = 0.0f;
   if (M != -INFINITY) {
     for (int s = 0; s < n_split; ++s) {
       const float* r = p + s * PART;
       const float f = r[0] == -INFINITY ? 0.0f : exp2f(r[0] - M);
-      L = fmaf(r[1], f, L);
+      Ls = fmaf(r[1], f, Ls);
       O = fmaf(r[2 + j], f, O);
     }
   }
-  out[(long long)bh * KD + j] = L > 0.0f ? O / L : 0.0f;
-  if (lse && j == 0) lse[bh] = L > 0.0f ? (M + log2f(L)) * 0.69314718055994531f : -INFINITY;
+  const float nan = __builtin_nanf("");
+  out[(long long)bh * KD + j] = bad ? nan : Ls > 0.0f ? O / Ls : 0.0f;
+  if (lse && j == 0)
+    lse[bh] = bad ? nan : Ls > 0.0f ? (M + log2f(Ls) - PSCALE) * 0.69314718055994531f : -INFINITY;
 }
 
 template <int MODE, int B0, int B1, int VB>
@@ -872,7 +1032,7 @@ namespace {
 
 tq_status decode_impl(const tq_key_config* cfg, const void* tables, const void* q, int32_t q_dtype,
                       int32_t B, int32_t Hq, int32_t Hkv, const int32_t* ctx_len, int32_t max_ctx,
-                      const int32_t* block_table, int32_t max_blocks, int32_t page_size,
+                      const int32_t* block_table, int32_t max_blocks, int32_t page_size, int32_t n_pages,
                       const uint8_t* idx, const uint8_t* signs, const uint16_t* norm,
                       const uint16_t* rnorm, int32_t v_bits, int32_t v_group, const uint8_t* v_codes,
                       const uint16_t* v_scale, const uint16_t* v_zero, float sm_scale, float* out,
@@ -952,6 +1112,7 @@ tq_status decode_impl(const tq_key_config* cfg, const void* tables, const void* 
   a.block_table = block_table;
   a.max_blocks = max_blocks;
   a.page_size = page_size;
+  a.n_pages = n_pages;
   hipStream_t s = (hipStream_t)stream;
   const dim3 grid(n_split, n_quads, B * Hkv);
   if (dispatch(P, v_bits, a, grid, s) != hipSuccess) return TQ_ERR_HIP;
@@ -1012,7 +1173,7 @@ extern "C" tq_status tq_decode_attention_noalloc(const tq_key_config* cfg, const
                                                 float* lse, float* scores, void* stream) {
   // size of the partials for this shape (a query: nothing is launched)
   size_t need = 0;
-  tq_status st = decode_impl(cfg, tables, q, q_dtype, B, Hq, Hkv, ctx_len, max_ctx, nullptr, 0, 0, idx,
+  tq_status st = decode_impl(cfg, tables, q, q_dtype, B, Hq, Hkv, ctx_len, max_ctx, nullptr, 0, 0, 0, idx,
                              signs, norm, rnorm, v_bits, v_group, v_codes, v_scale, v_zero, sm_scale, out,
                              lse, scores, nullptr, &need, stream);
   if (st != TQ_OK) return st;
@@ -1020,7 +1181,7 @@ extern "C" tq_status tq_decode_attention_noalloc(const tq_key_config* cfg, const
   void* ws = scratch_of_current_device(&st);
   if (!ws) return st;
   size_t have = NOALLOC_SCRATCH_BYTES;
-  return decode_impl(cfg, tables, q, q_dtype, B, Hq, Hkv, ctx_len, max_ctx, nullptr, 0, 0, idx, signs, norm,
+  return decode_impl(cfg, tables, q, q_dtype, B, Hq, Hkv, ctx_len, max_ctx, nullptr, 0, 0, 0, idx, signs, norm,
                      rnorm, v_bits, v_group, v_codes, v_scale, v_zero, sm_scale, out, lse, scores, ws, &have,
                      stream);
 }
@@ -1034,7 +1195,7 @@ extern "C" tq_status tq_decode_attention(const tq_key_config* cfg, const void* t
                                         const uint16_t* v_zero, float sm_scale, float* out,
                                         float* lse, float* scores, void* workspace,
                                         size_t* workspace_bytes, void* stream) {
-  return decode_impl(cfg, tables, q, q_dtype, B, Hq, Hkv, ctx_len, max_ctx, nullptr, 0, 0, idx, signs,
+  return decode_impl(cfg, tables, q, q_dtype, B, Hq, Hkv, ctx_len, max_ctx, nullptr, 0, 0, 0, idx, signs,
                      norm, rnorm, v_bits, v_group, v_codes, v_scale, v_zero, sm_scale, out, lse, scores,
                      workspace, workspace_bytes, stream);
 }
@@ -1042,15 +1203,16 @@ extern "C" tq_status tq_decode_attention(const tq_key_config* cfg, const void* t
 extern "C" tq_status tq_decode_attention_paged(
     const tq_key_config* cfg, const void* tables, const void* q, int32_t q_dtype, int32_t B, int32_t Hq,
     int32_t Hkv, const int32_t* ctx_len, const int32_t* block_table, int32_t max_blocks_per_seq,
-    int32_t page_size, const uint8_t* idx, const uint8_t* signs, const uint16_t* norm,
+    int32_t page_size, int32_t n_pages, const uint8_t* idx, const uint8_t* signs, const uint16_t* norm,
     const uint16_t* rnorm, int32_t v_bits, int32_t v_group, const uint8_t* v_codes,
     const uint16_t* v_scale, const uint16_t* v_zero, float sm_scale, float* out, float* lse,
     float* scores, void* workspace, size_t* workspace_bytes, void* stream) {
-  if (page_size <= 0 || page_size % TILE != 0 || max_blocks_per_seq <= 0) return TQ_ERR_ARG;
+  if (page_size <= 0 || page_size % TILE != 0 || max_blocks_per_seq <= 0 || n_pages <= 0) return TQ_ERR_ARG;
+  if ((long long)n_pages * Hkv * page_size > 0x7fffffffffffLL) return TQ_ERR_ARG;
   if ((long long)max_blocks_per_seq * page_size > 0x3fffffffLL) return TQ_ERR_ARG;
   if (workspace && !block_table) return TQ_ERR_ARG;
   return decode_impl(cfg, tables, q, q_dtype, B, Hq, Hkv, ctx_len, max_blocks_per_seq * page_size,
-                     block_table, max_blocks_per_seq, page_size, idx, signs, norm, rnorm, v_bits, v_group,
+                     block_table, max_blocks_per_seq, page_size, n_pages, idx, signs, norm, rnorm, v_bits, v_group,
                      v_codes, v_scale, v_zero, sm_scale, out, lse, scores, workspace, workspace_bytes,
                      stream);
 }

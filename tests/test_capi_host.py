@@ -253,21 +253,24 @@ def test_decode_argument_errors():
     assert _dec(L.key_config(mode="grouped", bits_outlier=4, bits_normal=4)) == L.TQ_ERR_UNSUPPORTED
 
 
-def _dec_paged(cfg, page_size=128, max_blocks=8, bt=FAKE, ws=None):
+def _dec_paged(cfg, page_size=128, max_blocks=8, bt=FAKE, ws=None, n_pages=64):
     wsb = ctypes.c_size_t(1 << 30)
     return L.lib.tq_decode_attention_paged(ctypes.byref(cfg), FAKE, FAKE, L.TQ_BF16, 2, 8, 2, FAKE, bt,
-                                           max_blocks, page_size, FAKE, FAKE, FAKE, FAKE, 2, 32, FAKE,
+                                           max_blocks, page_size, n_pages, FAKE, FAKE, FAKE, FAKE, 2, 32, FAKE,
                                            FAKE, FAKE, ctypes.c_float(0.1), FAKE, None, None, ws,
                                            ctypes.byref(wsb), None)
 
 
 def test_paged_decode_argument_errors():
-    """Page sizes that are not positive multiples of 64, no pages, or a
-    missing block table are rejected on the host, before any device call."""
+    """Page sizes that are not positive multiples of 64, no pages, an empty
+    pool, or a missing block table are rejected on the host, before any
+    device call."""
     prod = L.key_config(mode="prod", bits=3)
     for ps in (0, -64, 16, 100):
         assert _dec_paged(prod, page_size=ps) == L.TQ_ERR_ARG
     assert _dec_paged(prod, max_blocks=0) == L.TQ_ERR_ARG
+    assert _dec_paged(prod, n_pages=0) == L.TQ_ERR_ARG
+    assert _dec_paged(prod, n_pages=-3) == L.TQ_ERR_ARG
     assert _dec_paged(prod, max_blocks=1 << 24, page_size=1 << 10) == L.TQ_ERR_ARG   # too many tokens
     assert _dec_paged(prod, bt=None, ws=FAKE) == L.TQ_ERR_ARG
 
