@@ -206,6 +206,30 @@ __device__ inline float group_sum(float v) {
   return v;
 }
 
+// The value of lane l ^ ST, without LDS traffic: quad permutes (1, 2), row
+// rotations by 4 and 12 written into alternate banks of four lanes (4), a
+// row rotation by 8 (8), permlane swaps (16, 32; the swap's two outputs hold
+// the upper and the lower lane of each pair).
+template <int ST>
+__device__ inline float lane_xor(float v, int lane) {
+  if constexpr (ST == 1) return dpp<DPP_XOR1>(v);
+  if constexpr (ST == 2) return dpp<DPP_XOR2>(v);
+  if constexpr (ST == 4) {
+    const int up = __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x12C, 0xF, 0x5, false);  // banks 0, 2: lane + 4
+    return __int_as_float(__builtin_amdgcn_update_dpp(up, __float_as_int(v), 0x124, 0xF, 0xA, false));  // 1, 3: lane - 4
+  }
+  if constexpr (ST == 8) return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false));
+  if constexpr (ST == 16) {
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float((lane & 16) ? p[0] : p[1]);
+  }
+  if constexpr (ST == 32) {
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float((lane & 32) ? p[0] : p[1]);
+  }
+  return v;
+}
+
 // Workgroup barrier for LDS hand-offs: waits for this wave's LDS accesses
 // only, so global loads already in flight (the next tile) stay in flight.
 __device__ inline void lds_barrier() {
@@ -453,13 +477,13 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
       x0 = t + x1;
       x1 = t - x1;
     }
-#pragma unroll
-    for (int st = 32; st >= 1; st >>= 1) {
-      const float y0 = __shfl_xor(x0, st), y1 = __shfl_xor(x1, st);
+    static_for<0, 6>([&](auto ii) {
+      constexpr int st = 32 >> decltype(ii)::value;
+      const float y0 = lane_xor<st>(x0, lane), y1 = lane_xor<st>(x1, lane);
       const bool up = lane & st;
       x0 = up ? y0 - x0 : x0 + y0;
       x1 = up ? y1 - x1 : x1 + y1;
-    }
+    });
     qp[wave * KD + lane] = x0;
     qp[wave * KD + lane + 64] = x1;
     constexpr int CPB0 = 8 / F::W0, CPB1 = 8 / F::W1;

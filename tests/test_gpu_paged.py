@@ -79,6 +79,38 @@ def test_paged_equals_contiguous(page_size):
         assert torch.equal(sc_c[b, :, :ctx[b]], sc_p[b, :, :ctx[b]])
 
 
+def test_paged_block_table_clamped_into_the_pool():
+    """A block table naming the pool's last page works as any other; an
+    entry past the pool (or negative) is clamped into [0, n_pages) on the
+    device, so it reads the pool's last (first) page instead of memory past
+    the planes: the results equal those of the table with that page."""
+    kw = dict(mode="prod", bits=3)
+    B, Hq, Hkv, page_size, nb = 2, 8, 2, 64, 4
+    max_ctx = nb * page_size
+    n_pages = 9
+    Tg = tq.Tables(L.key_config(seed=5, **kw), DEV)
+    n_rec = n_pages * Hkv * page_size
+    kb = W.kv_rows(22, 1, n_rec)[1]
+    vb = W.kv_rows(22, 2, n_rec)[1]
+    kp = tq.encode_keys(Tg, torch.from_numpy(kb.view(np.int16)).view(torch.bfloat16).to(DEV))
+    vp = tq.encode_values(torch.from_numpy(vb.view(np.int16)).view(torch.bfloat16).to(DEV), 2)
+    q = torch.from_numpy(W.queries(22, B, Hq)[1].view(np.int16)).view(torch.bfloat16).to(DEV)
+    ctx_t = torch.tensor([max_ctx, max_ctx - 10], dtype=torch.int32, device=DEV)
+    decp = tq.Decoder(Tg, B, Hq, Hkv, max_ctx, 2, page_size=page_size)
+
+    def run(table):
+        bt = torch.tensor(table, dtype=torch.int32, device=DEV)
+        out = decp(q, ctx_t, kp, vp, block_table=bt)
+        torch.cuda.synchronize()
+        return out.clone()
+
+    ref = run([[3, n_pages - 1, 0, 5], [n_pages - 1, 2, 7, 1]])   # last page named directly
+    assert torch.equal(run([[3, n_pages + 6, 0, 5], [1 << 30, 2, 7, 1]]), ref)
+    ref0 = run([[3, 0, 0, 5], [n_pages - 1, 2, 7, 1]])
+    assert torch.equal(run([[3, -4, 0, 5], [n_pages - 1, 2, 7, 1]]), ref0)
+    assert torch.isfinite(ref).all() and torch.isfinite(ref0).all()
+
+
 def test_chunked_store_matches_one_shot_and_oracle():
     kw = dict(mode="prod", bits=3)
     Hkv, Hq, d, G = 2, 8, 128, 4
