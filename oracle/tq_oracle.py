@@ -43,6 +43,16 @@ Functions and their pins (what each is checked against, outside itself):
                          mean cosine at 4 bits (0.997 on the pack article, sec 三).
   decode_attention       one token -> o = v_hat; equal scores -> mean; masking;
                          torch.softmax on the CPU as a second opinion.
+  grouped_prod           the sketch equals S applied to the block-rotated
+                         original-domain residual built densely from scipy's
+                         Hadamard matrix; rho = ||k - k_grouped_hat||; keys on
+                         centroids give rho = 0 and exact k_hat; unbiasedness
+                         over S draws and the regression slope.
+  select_outlier_channels  hand-worked variances (ties to the lower channel);
+                         brute force over all channel subsets of a small key.
+  attention_quality      scipy's entropy (KL) and cosine distance; identical
+                         caches give KL 0, cosine 1, full top-k agreement; a
+                         worked top-k example; the two-token KL closed form.
 """
 from __future__ import annotations
 
@@ -62,6 +72,7 @@ __all__ = [
     "fp16_round", "encode_values", "dequant_values",
     "decode_attention", "record_bytes",
     "recall_at_k", "spearman",
+    "grouped_prod_given_idx", "select_outlier_channels", "attention_quality",
 ]
 
 # ---------------------------------------------------------------------------
@@ -279,7 +290,7 @@ def nearest_centroid(y: np.ndarray, centroids: np.ndarray) -> np.ndarray:
 # ---------------------------------------------------------------------------
 
 class KeyConfig:
-    """mode: "mse" | "prod" | "grouped".
+    """mode: "mse" | "prod" | "grouped" | "grouped_prod".
 
     mse:     index bits = bits ([tqlite] mode table: d*bits).
     prod:    bits = total bits per coordinate; index bits = bits - 1, plus one
@@ -289,7 +300,15 @@ class KeyConfig:
              (b-1)+1 split is taken.  m = d rows of S.
     grouped: channels [0, d/2) take bits_outlier, [d/2, d) bits_normal, each
              half its own norm, rotation and codebook, no QJL ([tqlite] mode
-             table: d_out*b_out + d_n*b_n)."""
+             table: d_out*b_out + d_n*b_n).
+    grouped_prod: the grouped quantiser as above, then one QJL stage over the
+             whole key's residual: m = d sign bits and one fp16 residual norm.
+             Reading: the pages describe grouped mode without a residual stage
+             and the QJL stage on a single-rotation MSE quantiser; [tqlite]'s
+             mode table charges the QJL stage d + 32 bits on top of the MSE
+             stage's own bits, so here bits_outlier / bits_normal stay the
+             halves' index bits and the signs come on top.  The residual is
+             sketched as one d-vector (see grouped_prod_given_idx)."""
 
     def __init__(self, d=128, mode="prod", bits=3, seed=42, bits_outlier=4, bits_normal=2):
         self.d = int(d)
@@ -300,7 +319,7 @@ class KeyConfig:
         self.bits_normal = int(bits_normal)
         if self.d & (self.d - 1) or self.d < 2:
             raise ValueError("d must be a power of two")
-        if mode not in ("mse", "prod", "grouped"):
+        if mode not in ("mse", "prod", "grouped", "grouped_prod"):
             raise ValueError(mode)
 
     @property
@@ -319,13 +338,15 @@ class KeyTables:
 def build_tables(cfg: KeyConfig) -> KeyTables:
     T = KeyTables()
     T.cfg = cfg
-    if cfg.mode == "grouped":
+    if cfg.mode in ("grouped", "grouped_prod"):
         h = cfg.d // 2
         T.halves = []
         for tag, b in ((TAG_SIGMA_OUT, cfg.bits_outlier), (TAG_SIGMA_NORMAL, cfg.bits_normal)):
             c, t, D = codebook(b)
             T.halves.append(dict(d=h, bits=b, sigma=rademacher_signs(cfg.seed, tag, h),
                                  centroids=c, boundaries=t, mse=D))
+        if cfg.mode == "grouped_prod":
+            T.S = gaussian_matrix(cfg.seed, TAG_S, cfg.m, cfg.d)
         return T
     c, t, D = codebook(cfg.idx_bits)
     T.centroids, T.boundaries, T.mse = c, t, D
@@ -382,7 +403,7 @@ def encode_keys(keys: np.ndarray, T: KeyTables) -> dict:
     cfg = T.cfg
     keys = np.asarray(keys, dtype=np.float64)
     out = {}
-    if cfg.mode == "grouped":
+    if cfg.mode in ("grouped", "grouped_prod"):
         h = cfg.d // 2
         idxs, norms, ys = [], [], []
         for half, sl in zip(T.halves, (slice(0, h), slice(h, cfg.d))):
@@ -394,6 +415,8 @@ def encode_keys(keys: np.ndarray, T: KeyTables) -> dict:
         out["norm"] = np.stack(norms, axis=1)
         out["norm16"] = fp16_round(out["norm"])
         out["y"] = np.concatenate(ys, axis=1)
+        if cfg.mode == "grouped_prod":
+            out.update(grouped_prod_given_idx(out["norm"], out["y"], out["idx"], T))
         return out
     n, y = _rotate_unit(keys, T.sigma)
     idx = bucketize(y, T.boundaries)
@@ -414,23 +437,58 @@ def prod_given_idx(n: np.ndarray, y: np.ndarray, idx: np.ndarray, T: KeyTables) 
     return dict(r=r, z=z, bits=bits, rnorm=rho, rnorm16=fp16_round(rho))
 
 
+def grouped_prod_given_idx(norms: np.ndarray, y: np.ndarray, idx: np.ndarray, T: KeyTables) -> dict:
+    """QJL stage of grouped_prod for given half indices.
+
+    Half j (h = d/2 channels) has the rotated, sqrt(h)-scaled coordinates y_j,
+    the residual r_j = y_j - c_j[idx_j] and, in the original domain, the
+    residual e_j = (n_j / sqrt(h)) Pi_j^T r_j.  The sketch takes
+    w = concat_j (n_j / sqrt(h)) r_j = blockdiag(Pi_o, Pi_n) e: the whole
+    key's residual in the block-rotated frame, where the queries are rotated
+    too.  z = S w, bit_i = [z_i >= 0], rho = ||w|| = ||k - k_grouped_hat||.
+    Reading: [difai] "算法概述" sketches the residual k - decompress(codes)
+    with one Gaussian S; blockdiag(Pi) is orthogonal, so S blockdiag(Pi) again
+    has i.i.d. N(0, 1) entries and the estimator is unchanged."""
+    d = T.cfg.d
+    h = d // 2
+    parts = []
+    for j, half in enumerate(T.halves):
+        sl = slice(j * h, (j + 1) * h)
+        r = y[:, sl] - half["centroids"][idx[:, sl]]
+        parts.append((norms[:, j] / math.sqrt(h))[:, None] * r)
+    w = np.concatenate(parts, axis=1)
+    z = w @ T.S.T
+    bits = (z >= 0).astype(np.uint8)
+    rho = np.sqrt(np.sum(w * w, axis=-1))
+    return dict(w=w, z=z, bits=bits, rnorm=rho, rnorm16=fp16_round(rho))
+
+
 def dequant_keys(enc: dict, T: KeyTables) -> np.ndarray:
     """Dense k_hat [n, d] from the stored fields (fp16 norms as stored).
 
     mse:  k_hat = (n16 / sqrt(d)) Pi^T c[idx]
     prod: + rho16 * sqrt(pi/2) / m * Pi^T S^T (2 bit - 1)
+    grouped: each half (n16_j / sqrt(h)) Pi_j^T c_j[idx_j]
+    grouped_prod: + rho16 * sqrt(pi/2) / m * blockdiag(Pi_o, Pi_n)^T S^T (2 bit - 1)
     Reading: [difai] prints the QJL term as sqrt(pi/2) * (S@q)^T * sign_bits,
     without ||r|| and 1/m; both are required for E[<q, k_hat>] = <q, k>
     (E[sign(s.r)(s.a)] = sqrt(2/pi) <a, r>/||r|| for s ~ N(0, I))."""
     cfg = T.cfg
-    if cfg.mode == "grouped":
+    if cfg.mode in ("grouped", "grouped_prod"):
         h = cfg.d // 2
         parts = []
+        if cfg.mode == "grouped_prod":
+            sgn = 2.0 * enc["bits"].astype(np.float64) - 1.0
+            rho16 = enc["rnorm16"].astype(np.float64)
+            t = (rho16 * math.sqrt(math.pi / 2.0) / cfg.m)[:, None] * (sgn @ T.S)   # block-rotated frame
         for j, half in enumerate(T.halves):
             Pi = rotation_matrix(half["sigma"])
             c = half["centroids"][enc["idx"][:, j * h:(j + 1) * h]]
             n16 = enc["norm16"][:, j].astype(np.float64)
-            parts.append((n16 / math.sqrt(h))[:, None] * (c @ Pi))
+            part = (n16 / math.sqrt(h))[:, None] * (c @ Pi)
+            if cfg.mode == "grouped_prod":
+                part = part + t[:, j * h:(j + 1) * h] @ Pi
+            parts.append(part)
         return np.concatenate(parts, axis=1)
     d = cfg.d
     Pi = rotation_matrix(T.sigma)
@@ -499,11 +557,15 @@ def unpack_signs(packed: np.ndarray, m: int) -> np.ndarray:
 def pack_key_record(enc: dict, T: KeyTables) -> dict:
     """Packed planes of an encoded key set: idx bytes, sign bytes, fp16 norms."""
     cfg = T.cfg
-    if cfg.mode == "grouped":
+    if cfg.mode in ("grouped", "grouped_prod"):
         h = cfg.d // 2
         parts = [pack_fields(enc["idx"][:, j * h:(j + 1) * h], index_width(half["bits"]))
                  for j, half in enumerate(T.halves)]
-        return dict(idx=np.concatenate(parts, axis=1), norm=enc["norm16"])
+        rec = dict(idx=np.concatenate(parts, axis=1), norm=enc["norm16"])
+        if cfg.mode == "grouped_prod":
+            rec["signs"] = pack_signs(enc["bits"])
+            rec["rnorm"] = enc["rnorm16"]
+        return rec
     rec = dict(idx=pack_fields(enc["idx"], index_width(cfg.idx_bits)), norm=enc["norm16"])
     if cfg.mode == "prod":
         rec["signs"] = pack_signs(enc["bits"])
@@ -513,13 +575,17 @@ def pack_key_record(enc: dict, T: KeyTables) -> dict:
 
 def unpack_key_record(rec: dict, T: KeyTables) -> dict:
     cfg = T.cfg
-    if cfg.mode == "grouped":
+    if cfg.mode in ("grouped", "grouped_prod"):
         h = cfg.d // 2
         w0, w1 = (index_width(half["bits"]) for half in T.halves)
         nb0 = h * w0 // 8
         idx = np.concatenate([unpack_fields(rec["idx"][:, :nb0], w0, h),
                               unpack_fields(rec["idx"][:, nb0:], w1, h)], axis=1)
-        return dict(idx=idx, norm16=np.asarray(rec["norm"], dtype=np.float16))
+        enc = dict(idx=idx, norm16=np.asarray(rec["norm"], dtype=np.float16))
+        if cfg.mode == "grouped_prod":
+            enc["bits"] = unpack_signs(rec["signs"], cfg.m)
+            enc["rnorm16"] = np.asarray(rec["rnorm"], dtype=np.float16)
+        return enc
     enc = dict(idx=unpack_fields(rec["idx"], index_width(cfg.idx_bits), cfg.d),
                norm16=np.asarray(rec["norm"], dtype=np.float16))
     if cfg.mode == "prod":
@@ -530,9 +596,10 @@ def unpack_key_record(rec: dict, T: KeyTables) -> dict:
 
 def record_bytes(cfg: KeyConfig) -> int:
     """Bytes of one packed key record (planes summed)."""
-    if cfg.mode == "grouped":
+    if cfg.mode in ("grouped", "grouped_prod"):
         h = cfg.d // 2
-        return (h * index_width(cfg.bits_outlier) + h * index_width(cfg.bits_normal)) // 8 + 4
+        b = (h * index_width(cfg.bits_outlier) + h * index_width(cfg.bits_normal)) // 8 + 4
+        return b + (cfg.m // 8 + 2 if cfg.mode == "grouped_prod" else 0)
     b = cfg.d * index_width(cfg.idx_bits) // 8 + 2
     if cfg.mode == "prod":
         b += cfg.m // 8 + 2
@@ -633,3 +700,80 @@ def spearman(a: np.ndarray, b: np.ndarray) -> float:
     ra -= ra.mean()
     rb -= rb.mean()
     return float((ra * rb).sum() / math.sqrt((ra * ra).sum() * (rb * rb).sum()))
+
+
+# ---------------------------------------------------------------------------
+# Outlier channels for grouped mode ([tqlite] mode table: "高方差通道分配更高
+# bit", the high-variance channels get the higher bit width).
+# Reading: the page names the criterion but not the estimator or tie rule:
+# population variance of each channel over the given key rows, the n_outlier
+# largest taken (equal variances: the lower channel first); the result lists
+# the chosen channels in increasing order, then the others in increasing
+# order.  Keys and queries are both reordered by it, which leaves q.k as it is.
+# ---------------------------------------------------------------------------
+
+def select_outlier_channels(keys: np.ndarray, n_outlier: int) -> np.ndarray:
+    k = np.asarray(keys, dtype=np.float64)
+    d = k.shape[1]
+    if not 0 <= n_outlier <= d:
+        raise ValueError("n_outlier out of range")
+    if k.shape[0] == 0:
+        var = np.zeros(d)
+    else:
+        mean = k.mean(axis=0)
+        var = ((k - mean) ** 2).mean(axis=0)
+    ranked = sorted(range(d), key=lambda c: (-var[c], c))
+    chosen = sorted(ranked[:n_outlier])
+    rest = sorted(ranked[n_outlier:])
+    return np.array(chosen + rest, dtype=np.int64)
+
+
+# ---------------------------------------------------------------------------
+# Attention quality of a compressed cache against the exact one ([difai]
+# compare.py output items 3 and 5: cosine similarity, Top-1/5 agreement and KL
+# divergence of the attention scores at 2/3/4 bits).
+# Reading: "attention score" comparisons are taken per query head over one
+# KV head's tokens: cosine of the raw score vectors q.k vs q.k_hat; KL of the
+# exact softmax weights to the compressed ones, KL(p || p_hat); Top-1 agreement
+# of the highest-scoring token; Top-k overlap |top_k(s) & top_k(s_hat)| / k.
+# The attention outputs' cosine (p v against p_hat v_hat) is added, since the
+# value cache is compressed too.
+# ---------------------------------------------------------------------------
+
+def _cosine(a, b) -> float:
+    """<a, b> / (||a|| ||b||); NaN when either vector is zero."""
+    den = math.sqrt(float(a @ a) * float(b @ b))
+    return float(a @ b) / den if den > 0 else float("nan")
+
+
+def attention_quality(q: np.ndarray, k: np.ndarray, v: np.ndarray, khat: np.ndarray,
+                      vhat: np.ndarray, sm_scale: float | None = None, topk: int = 5) -> dict:
+    """q [G, d] query heads of one KV head, k/v the exact cache [N, d],
+    khat/vhat the compressed one.  Returns per-query-head float64 arrays
+    score_cosine, kl, top1 (0/1), topk_overlap, out_cosine, and the squared
+    score error and squared exact score summed over tokens (err2, ref2)."""
+    q = np.asarray(q, dtype=np.float64)
+    d = q.shape[-1]
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(d)
+    s = q @ np.asarray(k, dtype=np.float64).T
+    sh = q @ np.asarray(khat, dtype=np.float64).T
+    res = {key: [] for key in ("score_cosine", "kl", "top1", "topk_overlap", "out_cosine", "err2", "ref2")}
+    for g in range(q.shape[0]):
+        a, b = s[g], sh[g]
+        res["score_cosine"].append(_cosine(a, b))
+        xa, xb = sm_scale * a, sm_scale * b
+        la = xa - xa.max() - math.log(float(np.sum(np.exp(xa - xa.max()))))
+        lb = xb - xb.max() - math.log(float(np.sum(np.exp(xb - xb.max()))))
+        p, ph = np.exp(la), np.exp(lb)
+        res["kl"].append(float(np.sum(p * (la - lb))))
+        order_a = sorted(range(len(a)), key=lambda t: (-a[t], t))
+        order_b = sorted(range(len(b)), key=lambda t: (-b[t], t))
+        res["top1"].append(1.0 if order_a[0] == order_b[0] else 0.0)
+        res["topk_overlap"].append(len(set(order_a[:topk]) & set(order_b[:topk])) / topk)
+        o = p @ np.asarray(v, dtype=np.float64)
+        oh = ph @ np.asarray(vhat, dtype=np.float64)
+        res["out_cosine"].append(_cosine(o, oh))
+        res["err2"].append(float(np.sum((b - a) ** 2)))
+        res["ref2"].append(float(np.sum(a * a)))
+    return {key: np.array(val) for key, val in res.items()}

@@ -149,3 +149,86 @@ def test_grouped_swapped_rotations_are_caught(monkeypatch):
         return enc_orig(keys, T)
     monkeypatch.setattr(O, "encode_keys", enc_mutant)
     assert _fails(P.test_grouped_key_built_from_centroids)
+
+
+def _grouped_prod_mutant(weight=True, rotate=True):
+    """grouped_prod_given_idx with the norm weights dropped or the residual
+    sketched in the original domain instead of the block-rotated frame."""
+    def fn(norms, y, idx, T):
+        d, h = T.cfg.d, T.cfg.d // 2
+        parts = []
+        for j, half in enumerate(T.halves):
+            sl = slice(j * h, (j + 1) * h)
+            r = y[:, sl] - half["centroids"][idx[:, sl]]
+            r = r * (norms[:, j:j + 1] if weight else 1.0) / math.sqrt(h)
+            parts.append(r if rotate else r @ O.rotation_matrix(half["sigma"]))
+        w = np.concatenate(parts, axis=1)
+        z = w @ T.S.T
+        rho = np.sqrt(np.sum(w * w, axis=-1))
+        return dict(w=w, z=z, bits=(z >= 0).astype(np.uint8), rnorm=rho, rnorm16=O.fp16_round(rho))
+    return fn
+
+
+def test_grouped_prod_unweighted_halves_are_caught(monkeypatch):
+    monkeypatch.setattr(O, "grouped_prod_given_idx", _grouped_prod_mutant(weight=False))
+    assert _fails(P.test_grouped_prod_sketch_is_the_block_rotated_residual)
+
+
+def test_grouped_prod_unrotated_residual_is_caught(monkeypatch):
+    monkeypatch.setattr(O, "grouped_prod_given_idx", _grouped_prod_mutant(rotate=False))
+    assert _fails(P.test_grouped_prod_sketch_is_the_block_rotated_residual)
+
+
+def test_grouped_prod_wrong_qjl_constant_is_caught(monkeypatch):
+    orig = O.dequant_keys
+
+    def mutant(enc, T):
+        e = dict(enc)
+        if "rnorm16" in e:
+            e["rnorm16"] = (e["rnorm16"].astype(np.float64) * 1.15).astype(np.float16)
+        return orig(e, T)
+    monkeypatch.setattr(O, "dequant_keys", mutant)
+    assert _fails(P.test_grouped_prod_bias_regression_slope_is_zero)
+
+
+def test_outlier_ties_to_higher_channel_are_caught(monkeypatch):
+    def mutant(keys, n_outlier):
+        k = np.asarray(keys, dtype=np.float64)
+        var = k.var(axis=0)
+        ranked = sorted(range(k.shape[1]), key=lambda c: (-var[c], -c))
+        return np.array(sorted(ranked[:n_outlier]) + sorted(ranked[n_outlier:]))
+    monkeypatch.setattr(O, "select_outlier_channels", mutant)
+    assert _fails(P.test_select_outlier_channels_worked_example)
+
+
+def test_outlier_by_mean_square_is_caught(monkeypatch):
+    """Ranking by the uncentred second moment instead of the variance."""
+    def mutant(keys, n_outlier):
+        k = np.asarray(keys, dtype=np.float64)
+        ms = (k * k).mean(axis=0)
+        ranked = sorted(range(k.shape[1]), key=lambda c: (-ms[c], c))
+        return np.array(sorted(ranked[:n_outlier]) + sorted(ranked[n_outlier:]))
+    monkeypatch.setattr(O, "select_outlier_channels", mutant)
+    assert _fails(P.test_select_outlier_channels_worked_example)
+
+
+def test_reversed_kl_is_caught(monkeypatch):
+    orig = O.attention_quality
+
+    def mutant(q, k, v, khat, vhat, sm_scale=None, topk=5):
+        r = orig(q, khat, vhat, k, v, sm_scale, topk)     # KL(p_hat || p), cosines symmetric
+        return r
+    monkeypatch.setattr(O, "attention_quality", mutant)
+    assert _fails(P.test_attention_quality_against_scipy)
+
+
+def test_output_cosine_with_exact_weights_is_caught(monkeypatch):
+    orig = O.attention_quality
+
+    def mutant(q, k, v, khat, vhat, sm_scale=None, topk=5):
+        r = orig(q, k, v, khat, vhat, sm_scale, topk)
+        r2 = orig(q, k, v, k, vhat, sm_scale, topk)       # p v against p v_hat
+        r["out_cosine"] = r2["out_cosine"]
+        return r
+    monkeypatch.setattr(O, "attention_quality", mutant)
+    assert _fails(P.test_attention_quality_against_scipy)

@@ -200,6 +200,9 @@ def test_record_bytes():
     assert O.record_bytes(O.KeyConfig(mode="mse", bits=4)) == 66
     assert O.record_bytes(O.KeyConfig(mode="mse", bits=8)) == 130
     assert O.record_bytes(O.KeyConfig(mode="grouped", bits_outlier=4, bits_normal=2)) == 52
+    # the grouped quantiser's 52 bytes plus m = 128 sign bits and one fp16 norm
+    # ("tqlite" README mode table: the QJL stage adds d + 32 bits, the norm here fp16)
+    assert O.record_bytes(O.KeyConfig(mode="grouped_prod", bits_outlier=4, bits_normal=2)) == 52 + 16 + 2
 
 
 # ---------------------------------------------------------------- MSE encode
@@ -456,11 +459,236 @@ def test_grouped_halves_are_independent_mse():
     assert rel.mean() < 0.02
 
 
+# ---------------------------------------------------------------- grouped + QJL
+
+def _grouped_prod_setup(seed=42, bo=4, bn=2):
+    return O.build_tables(O.KeyConfig(mode="grouped_prod", bits_outlier=bo, bits_normal=bn, seed=seed))
+
+
+def _dense_grouped_hat(k, enc, T, norms):
+    """k_hat of the grouped stage written out with scipy's Hadamard matrix:
+    half j is (n_j / 8) c_j[idx_j] Pi_j with Pi_j = H_64 diag(sigma_j) / 8."""
+    H64 = scipy.linalg.hadamard(64)
+    parts, rots = [], []
+    for j, half in enumerate(T.halves):
+        Pi = H64 * half["sigma"][None, :] / 8.0
+        c = half["centroids"][enc["idx"][:, 64 * j:64 * (j + 1)]]
+        parts.append((norms[:, j] / 8.0)[:, None] * (c @ Pi))
+        rots.append(Pi)
+    return np.concatenate(parts, axis=1), rots
+
+
+def test_grouped_prod_sketch_is_the_block_rotated_residual():
+    """The sign bits sketch the whole key's residual k - k_grouped_hat (float64
+    norms) after rotating each half by its own Pi_j: z = S blockdiag(Pi_o,
+    Pi_n) (k - k_grouped_hat), and rho = ||k - k_grouped_hat||.  The residual
+    is formed here in the original domain from a dense Hadamard matrix, not
+    through the encoder's rotated coordinates, so a dropped norm weight, a
+    missing 1/sqrt(h), one norm for both halves or an unrotated residual
+    fails."""
+    T = _grouped_prod_setup()
+    rng = np.random.default_rng(61)
+    k = rng.standard_normal((40, 128)) * np.r_[np.full(64, 6.0), np.full(64, 0.5)]
+    k[:10, 64:] *= 30.0                          # some keys with the larger normal half
+    enc = O.encode_keys(k, T)
+    norms = np.stack([np.linalg.norm(k[:, :64], axis=1), np.linalg.norm(k[:, 64:], axis=1)], axis=1)
+    kg, rots = _dense_grouped_hat(k, enc, T, norms)
+    e = k - kg
+    w = np.concatenate([e[:, :64] @ rots[0].T, e[:, 64:] @ rots[1].T], axis=1)
+    z = w @ T.S.T
+    scale = np.linalg.norm(k, axis=1, keepdims=True)
+    assert np.allclose(enc["z"], z, rtol=0, atol=1e-11 * scale.max())
+    clear = np.abs(z) > 1e-9 * scale
+    assert np.array_equal(enc["bits"][clear], (z[clear] >= 0).astype(np.uint8))
+    assert np.allclose(enc["rnorm"], np.linalg.norm(e, axis=1), rtol=1e-12)
+    assert np.array_equal(enc["rnorm16"], np.linalg.norm(e, axis=1).astype(np.float16))
+
+
+def test_grouped_prod_keys_along_centroids_closed_form():
+    """A half built along a centroid row, y_j = lam_j c_j[idx_j] with
+    lam_j = 8 / ||c_j[idx_j]|| (the rotated half then has norm sqrt(64) and
+    keeps its indices), has residual r_j = (lam_j - 1) c_j[idx_j], so
+    rho = sqrt(sum_j n_j^2 (1 - 1/lam_j)^2) and the grouped stage returns
+    k_j / lam_j."""
+    T = _grouped_prod_setup(seed=17)
+    rng = np.random.default_rng(62)
+    H64 = scipy.linalg.hadamard(64)
+    for n_out, n_norm in ((8.0, 0.5), (0.25, 3.0)):
+        halves, lams = [], []
+        for half, n in zip(T.halves, (n_out, n_norm)):
+            c_all, t = half["centroids"], half["boundaries"]
+            while True:
+                idx = rng.integers(0, len(c_all), 64)
+                c = c_all[idx]
+                lam = 8.0 / np.linalg.norm(c)
+                y = lam * c
+                if np.array_equal(np.sum(y[:, None] >= t[None, :], axis=1), idx) and \
+                        np.min(np.abs(y[:, None] - t[None, :])) > 1e-3:
+                    break
+            Pi = H64 * half["sigma"][None, :] / 8.0
+            halves.append(n * (c / np.linalg.norm(c)) @ Pi)
+            lams.append(lam)
+        k = np.concatenate(halves)[None, :]
+        enc = O.encode_keys(k, T)
+        rho = math.sqrt(n_out ** 2 * (1 - 1 / lams[0]) ** 2 + n_norm ** 2 * (1 - 1 / lams[1]) ** 2)
+        assert math.isclose(enc["rnorm"][0], rho, rel_tol=1e-12)
+        g_only = dict(enc)
+        g_only["rnorm16"] = np.zeros(1, dtype=np.float16)
+        kh = O.dequant_keys(g_only, T)
+        assert np.allclose(kh[0, :64], k[0, :64] / lams[0], atol=1e-12)
+        assert np.allclose(kh[0, 64:], k[0, 64:] / lams[1], atol=1e-12)
+
+
+def test_grouped_prod_unbiased_over_S_draws():
+    """Theorem 2 for the grouped sketch: with the indices and fp16-exact half
+    norms fixed, the mean of q.k_hat over independent Gaussian S (fp16
+    entries) is q.k, and its variance is ((pi/2)||w||^2||a||^2 - <a,w>^2)/m
+    with a = blockdiag(Pi) q the query in the sketch's frame."""
+    T = _grouped_prod_setup(seed=5)
+    rng = np.random.default_rng(63)
+    k = rng.standard_normal((4, 128))
+    k[:, :64] *= 4.0 / np.linalg.norm(k[:, :64], axis=1, keepdims=True)    # half norms 4 and 0.75,
+    k[:, 64:] *= 0.75 / np.linalg.norm(k[:, 64:], axis=1, keepdims=True)   # exact in fp16
+    q = rng.standard_normal((4, 128))
+    base = O.encode_keys(k, T)
+    assert np.array_equal(base["norm16"].astype(np.float64), np.tile([4.0, 0.75], (4, 1)))
+    true = np.sum(q * k, axis=1)
+    ests = []
+    draws = 3000
+    g = np.random.default_rng(64)
+    for _ in range(draws):
+        T.S = g.standard_normal((128, 128)).astype(np.float16).astype(np.float64)
+        enc = dict(base)
+        enc.update(O.grouped_prod_given_idx(base["norm"], base["y"], base["idx"], T))
+        ests.append(np.sum(q * O.dequant_keys(enc, T), axis=1))
+    ests = np.array(ests)
+    mean, sd = ests.mean(0), ests.std(0)
+    assert np.all(np.abs(mean - true) < 4 * sd / math.sqrt(draws)), (mean, true)
+    H64 = scipy.linalg.hadamard(64)
+    a = np.concatenate([q[:, 64 * j:64 * (j + 1)] @ (H64 * T.halves[j]["sigma"][None, :] / 8.0).T
+                        for j in (0, 1)], axis=1)
+    w = base["w"]
+    var_theory = ((math.pi / 2) * np.sum(w * w, 1) * np.sum(a * a, 1) - np.sum(a * w, 1) ** 2) / 128
+    assert np.all(np.abs(sd ** 2 / var_theory - 1) < 0.12), sd ** 2 / var_theory
+
+
+def test_grouped_prod_bias_regression_slope_is_zero():
+    """As for prod: the estimate's error has no component along the grouped
+    stage's residual term <q, k - k_grouped_hat>."""
+    T = _grouped_prod_setup(seed=7)
+    rng = np.random.default_rng(65)
+    k = rng.standard_normal((3000, 128)) * np.r_[np.full(64, 5.0), np.ones(64)]
+    q = rng.standard_normal((3000, 128))
+    enc = O.encode_keys(k, T)
+    est = np.sum(q * O.dequant_keys(enc, T), axis=1)
+    g_only = dict(enc)
+    g_only["rnorm16"] = np.zeros_like(enc["rnorm16"])
+    kg = O.dequant_keys(g_only, T)
+    a = np.sum(q * (k - kg), axis=1)
+    e = est - np.sum(q * k, axis=1)
+    slope = np.sum(e * a) / np.sum(a * a)
+    resid = e - slope * a
+    se = math.sqrt(np.sum(resid ** 2) / (len(a) - 1) / np.sum(a * a))
+    assert abs(slope) < 4 * se + 0.02, (slope, se)
+    # with q isotropic and independent of the residual w, E<a, w>^2 = ||w||^2 ||a||^2 / d,
+    # so the unbiased estimate's mean squared error is (pi/2 - 1/d) times that of the
+    # grouped stage alone (whose error is -<a, w>); a QJL constant alpha scales it by alpha^2
+    ratio = np.mean(e ** 2) / np.mean(a ** 2)
+    assert abs(ratio / (math.pi / 2 - 1 / 128) - 1) < 0.1, ratio
+    qjl = est - np.sum(q * kg, axis=1)
+    assert np.corrcoef(qjl, a)[0, 1] > 0.5
+
+
+# ---------------------------------------------------------------- outlier channels
+
+def test_select_outlier_channels_worked_example():
+    """Six channels over four rows with variances 1, 9, 4, 9, 0, 2.25 (channel
+    2 shifted by 5 and channel 4 constant, which leave variance as it is)."""
+    alt = np.array([1.0, -1.0, 1.0, -1.0])
+    k = np.stack([alt, 3 * alt, 2 * alt + 5, -3 * alt, np.full(4, 7.0), 1.5 * alt], axis=1)
+    assert np.array_equal(O.select_outlier_channels(k, 3), [1, 2, 3, 0, 4, 5])
+    assert np.array_equal(O.select_outlier_channels(k, 1), [1, 0, 2, 3, 4, 5])   # tie 1/3: lower first
+    assert np.array_equal(O.select_outlier_channels(k, 2), [1, 3, 0, 2, 4, 5])
+    assert np.array_equal(O.select_outlier_channels(k, 5), [0, 1, 2, 3, 5, 4])
+    assert np.array_equal(O.select_outlier_channels(k, 0), np.arange(6))
+    assert np.array_equal(O.select_outlier_channels(k, 6), np.arange(6))
+
+
+def test_select_outlier_channels_brute_force():
+    """Over all 70 four-channel subsets of an 8-channel key set, the chosen
+    outlier channels have the largest total variance."""
+    import itertools
+    rng = np.random.default_rng(66)
+    k = rng.standard_normal((200, 8)) * rng.uniform(0.1, 5.0, 8) + rng.uniform(-3, 3, 8)
+    var = np.var(k, axis=0)
+    best = max(itertools.combinations(range(8), 4), key=lambda c: sum(var[list(c)]))
+    perm = O.select_outlier_channels(k, 4)
+    assert sorted(perm.tolist()) == list(range(8))
+    assert tuple(perm[:4]) == best and list(perm[4:]) == sorted(set(range(8)) - set(best))
+
+
+# ---------------------------------------------------------------- attention quality
+
+def test_attention_quality_against_scipy():
+    """KL of the exact softmax weights to the compressed ones against
+    scipy.stats.entropy(p, p_hat); score and output cosines against
+    scipy.spatial.distance.cosine."""
+    import scipy.spatial.distance as SD
+    import scipy.special as SS
+    rng = np.random.default_rng(67)
+    G, N, d = 3, 300, 16
+    q, k, v = rng.standard_normal((G, d)) * 2, rng.standard_normal((N, d)), rng.standard_normal((N, d))
+    kh = k + 0.3 * rng.standard_normal((N, d))
+    vh = v + 0.1 * rng.standard_normal((N, d))
+    r = O.attention_quality(q, k, v, kh, vh, sm_scale=0.4)
+    for g in range(G):
+        s, sh = k @ q[g], kh @ q[g]
+        p, ph = SS.softmax(0.4 * s), SS.softmax(0.4 * sh)
+        assert math.isclose(r["kl"][g], scipy.stats.entropy(p, ph), rel_tol=1e-9)
+        assert math.isclose(r["score_cosine"][g], 1 - SD.cosine(s, sh), rel_tol=1e-12)
+        assert math.isclose(r["out_cosine"][g], 1 - SD.cosine(p @ v, ph @ vh), rel_tol=1e-12)
+        assert math.isclose(r["err2"][g], np.sum((sh - s) ** 2), rel_tol=1e-12)
+        assert math.isclose(r["ref2"][g], np.sum(s * s), rel_tol=1e-12)
+    assert r["kl"].min() > 0
+
+
+def test_attention_quality_identical_cache_and_worked_topk():
+    rng = np.random.default_rng(68)
+    q, k, v = rng.standard_normal((2, 8)), rng.standard_normal((50, 8)), rng.standard_normal((50, 8))
+    r = O.attention_quality(q, k, v, k, v)
+    assert np.all(np.abs(r["kl"]) < 1e-14) and np.allclose(r["score_cosine"], 1, atol=1e-14)
+    assert np.all(r["top1"] == 1) and np.all(r["topk_overlap"] == 1) and np.allclose(r["out_cosine"], 1)
+    # scores 5, 4, 3, 2, 1, 0 against 5, 3, 4, 0, 1, 2: the same top token; top-5 sets
+    # {0, 1, 2, 3, 4} and {0, 2, 1, 5, 4} share four; top-3 sets are equal
+    q1 = np.array([[1.0, 0.0]])
+    ka = np.array([[5, 0], [4, 0], [3, 0], [2, 0], [1, 0], [0, 0]], dtype=float)
+    kb = np.array([[5, 0], [3, 0], [4, 0], [0, 0], [1, 0], [2, 0]], dtype=float)
+    r5 = O.attention_quality(q1, ka, ka, kb, ka, topk=5)
+    r3 = O.attention_quality(q1, ka, ka, kb, ka, topk=3)
+    assert r5["top1"][0] == 1 and r5["topk_overlap"][0] == 0.8 and r3["topk_overlap"][0] == 1.0
+    kc = np.array([[4, 0], [5, 0], [3, 0], [2, 0], [1, 0], [0, 0]], dtype=float)   # top token 1, not 0
+    r1 = O.attention_quality(q1, ka, ka, kc, ka, topk=1)
+    assert r1["top1"][0] == 0 and r1["topk_overlap"][0] == 0
+
+
+def test_attention_quality_two_token_kl_closed_form():
+    """Two tokens with logits (0, a) and (0, b): KL = sum_i p_i log(p_i / p_hat_i)
+    with p_1 = 1 / (1 + e^-a)."""
+    for a, b in ((1.0, 0.5), (3.0, -2.0), (0.25, 4.0)):
+        q = np.array([[1.0]])
+        r = O.attention_quality(q, np.array([[0.0], [a]]), np.ones((2, 1)), np.array([[0.0], [b]]),
+                                np.ones((2, 1)), sm_scale=1.0)
+        p1, h1 = 1 / (1 + math.exp(-a)), 1 / (1 + math.exp(-b))
+        kl = (1 - p1) * math.log((1 - p1) / (1 - h1)) + p1 * math.log(p1 / h1)
+        assert math.isclose(r["kl"][0], kl, rel_tol=1e-12, abs_tol=1e-15)
+
+
 def test_packed_record_round_trip_all_modes():
     rng = np.random.default_rng(8)
     k = rng.standard_normal((64, 128))
     for cfg in (O.KeyConfig(mode="prod", bits=3), O.KeyConfig(mode="prod", bits=4),
-                O.KeyConfig(mode="mse", bits=8), O.KeyConfig(mode="grouped")):
+                O.KeyConfig(mode="mse", bits=8), O.KeyConfig(mode="grouped"),
+                O.KeyConfig(mode="grouped_prod", bits_outlier=3, bits_normal=2)):
         T = O.build_tables(cfg)
         enc = O.encode_keys(k, T)
         rec = O.pack_key_record(enc, T)
