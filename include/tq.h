@@ -34,9 +34,9 @@
  *   the projection is >= 0).  Norms, scales and zeros are IEEE fp16 (RNE).
  *   Records are structure-of-arrays planes, one row per record:
  *     idx   [n_records][tq_idx_row_bytes(cfg)]     uint8
- *     signs [n_records][d/8]                        uint8   (prod only)
- *     norm  [n_records]  fp16  (grouped: [n_records][2], outlier half first)
- *     rnorm [n_records]  fp16  residual norm ||k - k_mse_hat||   (prod only)
+ *     signs [n_records][d/8]                        uint8   (PROD, GROUPED_PROD)
+ *     norm  [n_records]  fp16  (grouped modes: [n_records][2], outlier half first)
+ *     rnorm [n_records]  fp16  residual norm ||k - k_mse_hat||   (PROD, GROUPED_PROD)
  *     codes [n_records][d*bits/8] uint8, scale/zero [n_records][d/group] fp16
  *   A 128-d prod key with 3 bits is 32 + 16 + 2 + 2 = 52 bytes, the record the
  *   bit-packing article (sec 四) counts.
@@ -63,7 +63,9 @@ typedef enum {
 typedef enum {
   TQ_MODE_MSE = 0,      /* rotation + Lloyd-Max codebook, d*bits bits per key      */
   TQ_MODE_PROD = 1,     /* MSE at (bits-1) index bits + 1-bit QJL residual signs   */
-  TQ_MODE_GROUPED = 2   /* two halves, each its own norm, rotation and codebook    */
+  TQ_MODE_GROUPED = 2,  /* two halves, each its own norm, rotation and codebook    */
+  TQ_MODE_GROUPED_PROD = 3  /* GROUPED, then 1-bit QJL signs of the whole key's
+                               residual (m = d rows) and its fp16 norm           */
 } tq_mode;
 
 typedef enum { TQ_F32 = 0, TQ_BF16 = 1, TQ_F16 = 2 } tq_dtype;
@@ -75,10 +77,18 @@ typedef struct {
   int32_t bits;         /* MSE: index bits 1..8.  PROD: total bits 2..9, the index
                            takes bits-1 and the QJL sign 1 (the pages disagree on
                            this split; (b-1)+1 is the reading taken).  Ignored for
-                           GROUPED.                                                 */
-  int32_t bits_outlier; /* GROUPED: index bits 1..8 of channels [0, d/2)           */
-  int32_t bits_normal;  /* GROUPED: index bits 1..8 of channels [d/2, d)           */
-  int32_t reserved;     /* must be 0                                                */
+                           GROUPED and GROUPED_PROD (whose QJL sign comes on top
+                           of the halves' index bits: the "tqlite" README's mode
+                           table charges the QJL stage d + 32 bits on top of the
+                           MSE stage's).                                           */
+  int32_t bits_outlier; /* GROUPED(_PROD): index bits 1..8 of channels [0, d_outlier) */
+  int32_t bits_normal;  /* GROUPED(_PROD): index bits 1..8 of the other channels      */
+  int32_t d_outlier;    /* GROUPED(_PROD): channels in the outlier half; 0 or d/2,
+                           both meaning d/2 (each half needs its own power-of-two
+                           Walsh-Hadamard transform, and d/2 is the only split of
+                           d into two powers of two).  The outlier channels are
+                           moved to the front of keys and queries first
+                           (tq_select_outlier_channels).  MSE / PROD: must be 0.   */
   uint64_t seed;        /* derives sigma and S; use one seed per layer ("tqlite"
                            README, 设计要点: independent seed per layer)            */
 } tq_key_config;
@@ -95,8 +105,8 @@ size_t tq_idx_row_bytes(const tq_key_config* cfg);
  *     get_codebook(d, bits) / "mse_total" (test_mse_codebook_table1);
  *   - the random signs sigma of Pi = H diag(sigma) / sqrt(d) ("tqlite" README:
  *     rotation = Hadamard x random signs);
- *   - PROD: the QJL matrix S, d x d i.i.d. N(0,1) stored as fp16 (difai.kr
- *     tutorial, 算法概述: sign(S @ residual)).
+ *   - PROD, GROUPED_PROD: the QJL matrix S, d x d i.i.d. N(0,1) stored as
+ *     fp16 (difai.kr tutorial, 算法概述: sign(S @ residual)).
  * sigma and S come from SplitMix64 (Steele, Lea & Flood 2014) seeded with
  * seed XOR tag*0x9E3779B97F4A7C15 (tags 1 sigma, 2 S, 3 outlier sigma,
  * 4 normal sigma), S through Box-Muller on 53-bit uniforms.
@@ -119,13 +129,25 @@ tq_status tq_build_codebook(const tq_key_config* cfg, void* blob_host, size_t* b
  * transform, the "tqlite" README's 已知限制 asking for O(d log d)); each y_j
  * goes to the Lloyd-Max cell #{t : y_j >= t}; PROD also forms the residual
  * r = y - c[idx], the signs [S r >= 0] and rho = n ||r|| / sqrt(d).
+ * GROUPED does the same per half (d/2-point transform, own norm n_j, sigma and
+ * codebook); GROUPED_PROD then sketches the whole key's residual in the frame
+ * of the two rotations, w = concat_j (n_j / sqrt(d/2)) r_j: signs [S w >= 0],
+ * rho = ||w|| = ||k - k_grouped_hat||.
+ * Norm range: the norm is formed with a power-of-two prescale where the plain
+ * fp32 sum of squares would under- or overflow, so index and sign bytes are
+ * exact for keys with 2^-126 <= ||k|| <= 2^120.  A stored fp16 norm (or rho)
+ * saturates: above 65504 it is +inf, below 2^-25 it is 0 (the bytes are still
+ * those of the unit vector k / ||k||); scale such keys before encoding when
+ * they are to be decoded.
  *   tables     device copy of the tq_build_codebook blob for `cfg`.
  *   keys       [n_vec rows] x d elements of `dtype`, row i at keys + i*row_stride
  *              elements; 16-byte aligned, row_stride*elemsize a multiple of 16.
  *   slots      (nullable) int64 [n_vec]: record index that row i is written to;
  *              a slot outside [0, n_records) skips the row.  NULL: slot = i.
  *   n_records  rows of every output plane.
- *   idx, norm  always; signs, rnorm for PROD only (NULL otherwise).
+ *   idx, norm  always; signs, rnorm for PROD and GROUPED_PROD (NULL otherwise).
+ * The kernel compares the tables' header (mode, d, index bits, rows of S) with
+ * cfg and writes nothing for tables built for another configuration.
  * Output planes must be 16-byte aligned.  n_vec == 0 is a no-op.
  */
 tq_status tq_encode_keys(const tq_key_config* cfg, const void* tables,
@@ -152,9 +174,9 @@ typedef struct {
   const void* keys;      /* [n_vec rows] of dtype, row_stride elements apart            */
   const int64_t* slots;  /* nullable, as in tq_encode_keys                              */
   uint8_t* idx;
-  uint8_t* signs;        /* PROD only, else NULL                                        */
+  uint8_t* signs;        /* PROD / GROUPED_PROD, else NULL                              */
   uint16_t* norm;
-  uint16_t* rnorm;       /* PROD only, else NULL                                        */
+  uint16_t* rnorm;       /* PROD / GROUPED_PROD, else NULL                              */
 } tq_key_batch;
 
 tq_status tq_encode_keys_batched(const tq_key_config* cfg, const tq_key_batch* batch, int32_t n_batch,
@@ -204,7 +226,9 @@ tq_status tq_append_kv(const tq_key_config* cfg, const void* tables, const void*
  *         (n_t/d) <q', c[idx_t]> + rho_t sqrt(pi/2)/(d sqrt(d)) <S q', 2 bit_t - 1>
  *         with q' = H (sigma * q)  (difai.kr tutorial, 算法概述: <q,k_hat> +
  *         sqrt(pi/2) (S@q)^T sign_bits, with the ||r|| and 1/m that make it
- *         unbiased); MSE/GROUPED keep the first term (per half);
+ *         unbiased); MSE/GROUPED keep the first term (per half); GROUPED_PROD
+ *         sums the halves' first terms and rho_t sqrt(pi/2)/(d sqrt(d/2))
+ *         <S q'', 2 bit_t - 1> with q'' the two halves' transforms;
  *   p = softmax(sm_scale * s), out = sum_t p_t v_hat_t, v_hat = code*s + z.
  * The split-K scheme (partial max, sum and output per token chunk, merged in
  * a second kernel) keeps every result deterministic: no atomics.
@@ -224,7 +248,9 @@ tq_status tq_append_kv(const tq_key_config* cfg, const void* tables, const void*
  *              required size in *workspace_bytes (host) and returns TQ_OK.
  * Supported: d = 128; PROD with bits 2..4 (index 1..3 bits, 3 in nibbles);
  * MSE with bits 1..3; GROUPED with (outlier, normal) index bits (4, 2),
- * (3, 2), (2, 2) or (4, 1); Hq % Hkv == 0.  Other shapes return
+ * (3, 2), (2, 2) or (4, 1); GROUPED_PROD with (3, 2) or (4, 1) (the lookup
+ * tables of (4, 2) plus signs exceed a workgroup's 160 KiB of LDS);
+ * Hq % Hkv == 0.  Other shapes return
  * TQ_ERR_UNSUPPORTED.  (Encode supports every mode and width above.)
  */
 tq_status tq_decode_attention(const tq_key_config* cfg, const void* tables,
@@ -303,7 +329,9 @@ tq_status tq_decode_attention_paged(const tq_key_config* cfg, const void* tables
  * dequantise path of the "tqlite" README (fake quantisation, prefill) and of
  * validate_paper.py's prod quantiser:
  *   k_hat = (n / sqrt(d)) Pi^T c[idx]  (+ rho sqrt(pi/2) / m  Pi^T S^T (2 bit - 1), PROD)
- * (GROUPED: each half with its own norm, rotation and codebook, no QJL term).
+ * (GROUPED: each half with its own norm, rotation and codebook, no QJL term;
+ * GROUPED_PROD: those halves plus rho sqrt(pi/2) / m blockdiag(Pi_o, Pi_n)^T
+ * S^T (2 bit - 1)).
  *   n_vec       output rows.
  *   slots       (nullable) int64 [n_vec]: record read for output row i (NULL:
  *               record i); a slot outside [0, n_records) gives a zero row.
@@ -345,6 +373,28 @@ tq_status tq_dequantize_values(int32_t bits, int32_t group, int32_t d, int64_t n
  */
 tq_status tq_channel_moments(const void* x, int32_t dtype, int64_t n_vec, int64_t row_stride, int32_t d,
                              double* out, void* workspace, size_t* workspace_bytes, void* stream);
+
+/*
+ * tq_select_outlier_channels -- the channel order of GROUPED(_PROD) mode from
+ * n_vec key rows (the "tqlite" README's mode table: the high-variance channels
+ * get the higher bit width).  Each channel's population variance
+ * Q/n - (S/n)^2 is formed in float64 from the sums of tq_channel_moments; the
+ * n_outlier largest are chosen (equal variances: the lower channel first).
+ * perm[0 .. n_outlier) lists the chosen channels in increasing order, then
+ * perm[n_outlier .. d) the others in increasing order.  Apply it to keys and
+ * queries alike (k[:, perm], q[..., perm]); q.k is unchanged.  n_vec == 0
+ * gives the identity.  The one-pass variance loses accuracy only for a
+ * channel whose mean exceeds its spread by about 10^6.
+ *   x, dtype, n_vec, row_stride, d   as tq_channel_moments (d = 128).
+ *   n_outlier  0 <= n_outlier <= d (d/2 for GROUPED mode).
+ *   perm       device int32 [d].
+ *   workspace  device scratch (8-byte aligned); NULL: *workspace_bytes
+ *              receives the size and nothing runs.
+ * Deterministic (fixed reduction order).
+ */
+tq_status tq_select_outlier_channels(const void* x, int32_t dtype, int64_t n_vec, int64_t row_stride,
+                                     int32_t d, int32_t n_outlier, int32_t* perm, void* workspace,
+                                     size_t* workspace_bytes, void* stream);
 
 /* Static description of a status code (never NULL). */
 const char* tq_status_string(int32_t status);

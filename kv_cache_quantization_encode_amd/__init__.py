@@ -4,7 +4,7 @@ decode attention, as HIP kernels for gfx950 behind the C ABI in include/tq.h.
 The Python layer only marshals arguments (torch provides device memory and
 streams); importing it requires the built libtq.so next to this file.
 """
-from ._lib import (TQ_BF16, TQ_F16, TQ_F32, TQ_MODE_GROUPED, TQ_MODE_MSE, TQ_MODE_PROD, KeyConfig,
+from ._lib import (TQ_BF16, TQ_F16, TQ_F32, TQ_MODE_GROUPED, TQ_MODE_GROUPED_PROD, TQ_MODE_MSE, TQ_MODE_PROD, KeyConfig,
                    TqError, key_config, status_string)
 from .api import (Decoder, KeyBatchEncoder, Tables, append_kv, build_codebook, channel_moments, decode_attention,
                   decode_attention_noalloc,
@@ -20,4 +20,5 @@ __all__ = ["KeyConfig", "TqError", "key_config", "status_string", "Tables", "Dec
            "decode_workspace_bytes", "key_planes", "value_planes", "idx_row_bytes", "PagedKVCache",
            "dequantize_keys", "dequantize_values", "quality",
            "channel_moments", "select_outlier_channels",
-           "TQ_F32", "TQ_BF16", "TQ_F16", "TQ_MODE_MSE", "TQ_MODE_PROD", "TQ_MODE_GROUPED"]
+           "TQ_F32", "TQ_BF16", "TQ_F16", "TQ_MODE_MSE", "TQ_MODE_PROD", "TQ_MODE_GROUPED",
+           "TQ_MODE_GROUPED_PROD"]

@@ -20,13 +20,13 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("TQ_LIBRARY") or os.path.join(HERE, "libtq.so")
 
 TQ_OK, TQ_ERR_ARG, TQ_ERR_UNSUPPORTED, TQ_ERR_WORKSPACE, TQ_ERR_HIP = 0, -1, -2, -3, -4
-TQ_MODE_MSE, TQ_MODE_PROD, TQ_MODE_GROUPED = 0, 1, 2
+TQ_MODE_MSE, TQ_MODE_PROD, TQ_MODE_GROUPED, TQ_MODE_GROUPED_PROD = 0, 1, 2, 3
 TQ_F32, TQ_BF16, TQ_F16 = 0, 1, 2
-MODES = {"mse": TQ_MODE_MSE, "prod": TQ_MODE_PROD, "grouped": TQ_MODE_GROUPED}
+MODES = {"mse": TQ_MODE_MSE, "prod": TQ_MODE_PROD, "grouped": TQ_MODE_GROUPED, "grouped_prod": TQ_MODE_GROUPED_PROD}
 
 EXPORTED = ["tq_build_codebook", "tq_encode_keys", "tq_encode_keys_batched", "tq_encode_values", "tq_append_kv", "tq_decode_attention",
             "tq_decode_attention_noalloc", "tq_decode_attention_paged", "tq_dequantize_keys", "tq_dequantize_values", "tq_channel_moments",
-            "tq_status_string", "tq_idx_row_bytes"]
+            "tq_select_outlier_channels", "tq_status_string", "tq_idx_row_bytes"]
 
 
 class TqError(RuntimeError):
@@ -38,7 +38,7 @@ class TqError(RuntimeError):
 class KeyConfig(ctypes.Structure):
     _fields_ = [("d", ctypes.c_int32), ("mode", ctypes.c_int32), ("bits", ctypes.c_int32),
                 ("bits_outlier", ctypes.c_int32), ("bits_normal", ctypes.c_int32),
-                ("reserved", ctypes.c_int32), ("seed", ctypes.c_uint64)]
+                ("d_outlier", ctypes.c_int32), ("seed", ctypes.c_uint64)]
 
 
 class KeyBatch(ctypes.Structure):
@@ -48,9 +48,9 @@ class KeyBatch(ctypes.Structure):
                 ("rnorm", ctypes.c_void_p)]
 
 
-def key_config(d=128, mode="prod", bits=3, seed=42, bits_outlier=4, bits_normal=2) -> KeyConfig:
+def key_config(d=128, mode="prod", bits=3, seed=42, bits_outlier=4, bits_normal=2, d_outlier=0) -> KeyConfig:
     m = MODES[mode] if isinstance(mode, str) else int(mode)
-    return KeyConfig(d, m, bits, bits_outlier, bits_normal, 0, seed)
+    return KeyConfig(d, m, bits, bits_outlier, bits_normal, d_outlier, seed)
 
 
 def _load():
@@ -90,6 +90,8 @@ def _load():
     lib.tq_dequantize_values.argtypes = [I32, I32, I32, I64, P, I64, P, P, P, P, I32, I64, P]
     lib.tq_channel_moments.restype = I32
     lib.tq_channel_moments.argtypes = [P, I32, I64, I64, I32, P, P, ctypes.POINTER(SZ), P]
+    lib.tq_select_outlier_channels.restype = I32
+    lib.tq_select_outlier_channels.argtypes = [P, I32, I64, I64, I32, I32, P, P, ctypes.POINTER(SZ), P]
     return lib
 
 

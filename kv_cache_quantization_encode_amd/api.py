@@ -9,7 +9,8 @@ import struct
 import numpy as np
 import torch
 
-from ._lib import (TQ_BF16, TQ_F16, TQ_F32, TQ_MODE_GROUPED, TQ_MODE_PROD, KeyBatch, KeyConfig, check,
+from ._lib import (TQ_BF16, TQ_F16, TQ_F32, TQ_MODE_GROUPED, TQ_MODE_GROUPED_PROD, TQ_MODE_PROD, KeyBatch,
+                   KeyConfig, check,
                    key_config, lib)
 
 _DT = {torch.float32: TQ_F32, torch.bfloat16: TQ_BF16, torch.float16: TQ_F16}
@@ -65,6 +66,14 @@ def _check_slots(slots, n, name="slots"):
         _need(slots.numel() == n, "%s has %d entries for %d rows" % (name, slots.numel(), n))
 
 
+def _grouped(mode) -> bool:
+    return mode in (TQ_MODE_GROUPED, TQ_MODE_GROUPED_PROD)
+
+
+def _qjl(mode) -> bool:
+    return mode in (TQ_MODE_PROD, TQ_MODE_GROUPED_PROD)
+
+
 def _check_key_planes(tables, p, n_records):
     mode = tables.mode
     d = tables.cfg.d
@@ -73,15 +82,15 @@ def _check_key_planes(tables, p, n_records):
           "idx plane holds %d bytes, %d records need %d" % (p["idx"].numel(), n_records,
                                                            n_records * tables.row_bytes))
     _on_device(p["norm"], "norm plane", torch.float16, contiguous=True)
-    _need(p["norm"].numel() >= n_records * (2 if mode == TQ_MODE_GROUPED else 1), "norm plane too small")
-    if mode == TQ_MODE_PROD:
-        _need(p.get("signs") is not None and p.get("rnorm") is not None, "prod keys need signs and rnorm planes")
+    _need(p["norm"].numel() >= n_records * (2 if _grouped(mode) else 1), "norm plane too small")
+    if _qjl(mode):
+        _need(p.get("signs") is not None and p.get("rnorm") is not None, "QJL keys need signs and rnorm planes")
         _on_device(p["signs"], "signs plane", torch.uint8, contiguous=True)
         _need(p["signs"].numel() >= n_records * (d // 8), "signs plane too small")
         _on_device(p["rnorm"], "rnorm plane", torch.float16, contiguous=True)
         _need(p["rnorm"].numel() >= n_records, "rnorm plane too small")
     else:
-        _need(p.get("signs") is None and p.get("rnorm") is None, "only prod keys have signs and rnorm planes")
+        _need(p.get("signs") is None and p.get("rnorm") is None, "only QJL keys have signs and rnorm planes")
 
 
 def _check_value_planes(p, bits, n_records, d=128, group=32):
@@ -108,7 +117,7 @@ def build_codebook(cfg: KeyConfig):
     buf = np.zeros(size.value, dtype=np.uint8)
     check("tq_build_codebook", lib.tq_build_codebook(ctypes.byref(cfg), buf.ctypes.data_as(ctypes.c_void_p),
                                                       ctypes.byref(size), mse))
-    n = 2 if cfg.mode == TQ_MODE_GROUPED else 1
+    n = 2 if _grouped(cfg.mode) else 1
     return buf, [mse[i] for i in range(n)]
 
 
@@ -128,7 +137,7 @@ def parse_tables(blob: np.ndarray) -> dict:
         hint = blob[h["off_hint"][i]:h["off_hint"][i] + 16 * h["hint_n"][i]].view(np.int32).reshape(-1, 4)
         parts.append(dict(centroids=c.copy(), bounds=t.copy(), sigma=s.copy(), hint=hint.copy()))
     h["parts"] = parts
-    if h["mode"] == TQ_MODE_PROD:
+    if h["m"] > 0:
         n = h["m"] * h["d"]
         h["S"] = blob[h["off_S"]:h["off_S"] + 2 * n].view(np.float16).reshape(h["m"], h["d"]).copy()
     return h
@@ -152,11 +161,11 @@ class Tables:
 def key_planes(tables: Tables, n_records: int, device="cuda") -> dict:
     d = tables.cfg.d
     p = dict(idx=torch.empty((n_records, tables.row_bytes), dtype=torch.uint8, device=device))
-    if tables.mode == TQ_MODE_GROUPED:
+    if _grouped(tables.mode):
         p["norm"] = torch.empty((n_records, 2), dtype=torch.float16, device=device)
     else:
         p["norm"] = torch.empty((n_records,), dtype=torch.float16, device=device)
-    if tables.mode == TQ_MODE_PROD:
+    if _qjl(tables.mode):
         p["signs"] = torch.empty((n_records, d // 8), dtype=torch.uint8, device=device)
         p["rnorm"] = torch.empty((n_records,), dtype=torch.float16, device=device)
     return p
@@ -339,16 +348,23 @@ def channel_moments(x: torch.Tensor) -> torch.Tensor:
 
 
 def select_outlier_channels(x: torch.Tensor, n_outlier: int = 64) -> torch.Tensor:
-    """Channel order for GROUPED mode: the n_outlier highest-variance channels
-    of the key rows x [n, d] first, then the rest (each in channel order).
-    Apply it to keys and queries alike: k[:, perm], q[..., perm]."""
-    m = channel_moments(x)
-    n = max(x.shape[0], 1)
-    var = m[1] / n - (m[0] / n) ** 2
-    order = torch.argsort(-var, stable=True)
-    out_ch = torch.sort(order[:n_outlier]).values
-    rest = torch.sort(order[n_outlier:]).values
-    return torch.cat([out_ch, rest])
+    """Channel order for the grouped modes (tq_select_outlier_channels): the
+    n_outlier highest-variance channels of the key rows x [n, d] first, then
+    the rest (each in channel order), int64 on x's device.  Apply it to keys
+    and queries alike: k[:, perm], q[..., perm]."""
+    _check_rows(x, "x", x.shape[-1] if x.dim() == 2 else 128)
+    n, d = x.shape
+    size = ctypes.c_size_t(0)
+    check("tq_select_outlier_channels", lib.tq_select_outlier_channels(None, _DT[x.dtype], n, x.stride(0), d,
+                                                                       n_outlier, None, None, ctypes.byref(size),
+                                                                       None))
+    ws = torch.empty(max(size.value, 8), dtype=torch.uint8, device=x.device)
+    perm = torch.empty(d, dtype=torch.int32, device=x.device)
+    size = ctypes.c_size_t(ws.numel())
+    check("tq_select_outlier_channels", lib.tq_select_outlier_channels(_ptr(x), _DT[x.dtype], n, x.stride(0), d,
+                                                                       n_outlier, _ptr(perm), _ptr(ws),
+                                                                       ctypes.byref(size), _stream()))
+    return perm.long()
 
 
 def decode_workspace_bytes(tables: Tables, B, Hq, Hkv, max_ctx, q_dtype=torch.bfloat16, v_bits=2,

@@ -75,11 +75,12 @@ constexpr int width_of(int b) { return b == 1 ? 1 : b == 2 ? 2 : 4; }
 constexpr int stride_of(int b) { return b == 3 ? 128 : 256; }  // 3-bit in nibbles: bytes <= 0x77
 
 // Table classes of a key format, in key-byte order: the index bytes of part 0,
-// (GROUPED) the index bytes of part 1, (PROD) the QJL sign bytes.
+// (GROUPED, GROUPED_PROD) the index bytes of part 1, (PROD, GROUPED_PROD) the
+// QJL sign bytes.
 template <int MODE, int B0, int B1>
 struct Fmt {
-  static constexpr bool GROUPED = MODE == TQ_MODE_GROUPED;
-  static constexpr bool QJL = MODE == TQ_MODE_PROD;
+  static constexpr bool GROUPED = MODE == TQ_MODE_GROUPED || MODE == TQ_MODE_GROUPED_PROD;
+  static constexpr bool QJL = MODE == TQ_MODE_PROD || MODE == TQ_MODE_GROUPED_PROD;
   static constexpr int NPART = GROUPED ? 2 : 1;
   static constexpr int PD = KD / NPART;  // coordinates per part
   static constexpr int W0 = width_of(B0);
@@ -90,12 +91,16 @@ struct Fmt {
   static constexpr int IDXB = IP0 + IP1;                 // idx row bytes
   static constexpr int KWORDS = (IDXB + SP) / 4;         // idx + sign words per key
   static constexpr int NC = NPART + (QJL ? 1 : 0);       // table classes
-  // class c: 0 / 1 index part, 2 sign bytes
-  static constexpr int kind(int c) { return c == 0 ? 0 : (GROUPED ? 1 : 2); }
-  static constexpr int npos(int c) { return c == 0 ? IP0 : (GROUPED ? IP1 : SP); }
+  // kind of class c: 0 / 1 index part, 2 sign bytes
+  static constexpr int kind(int c) { return c == 0 ? 0 : c == 2 ? 2 : (GROUPED ? 1 : 2); }
+  static constexpr int npos(int c) { return kind(c) == 0 ? IP0 : kind(c) == 1 ? IP1 : SP; }
   static constexpr int stride(int c) { return kind(c) == 0 ? stride_of(B0) : kind(c) == 1 ? stride_of(B1) : 256; }
-  static constexpr int kbyte(int c) { return c == 0 ? 0 : IP0; }       // first key byte of the class
-  static constexpr int ent(int c) { return c == 0 ? 0 : npos(0) * stride(0); }  // first table entry
+  static constexpr int kbyte(int c) { return c == 0 ? 0 : kbyte(c - 1) + npos(c - 1); }  // first key byte
+  static constexpr int ent(int c) { return c == 0 ? 0 : ent(c - 1) + npos(c - 1) * stride(c - 1); }  // first entry
+  static constexpr int cls(int pos) { return pos < kbyte(1) || NC == 1 ? 0 : (NC == 2 || pos < kbyte(2)) ? 1 : 2; }
+  // table-read chains (CHAIN positions each), class by class
+  static constexpr int chain0(int c) { return kbyte(c) / CHAIN; }
+  static constexpr int chain_cls(int g) { return cls(g * CHAIN); }
   static constexpr int ENTRIES = ent(NC - 1) + npos(NC - 1) * stride(NC - 1);
   static constexpr int POSITIONS = IDXB + SP;
   static_assert(IP0 % CHAIN == 0 && IP1 % CHAIN == 0 && SP % CHAIN == 0, "whole chains per class");
@@ -574,9 +579,9 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
   float4* halves = (float4*)wbuf;  // [POSITIONS][2][16]
   for (int i = tid; i < F::POSITIONS * 32; i += NT) {
     const int pos = i >> 5, half = (i >> 4) & 1, n = i & 15;
-    const int c = pos < F::npos(0) ? 0 : 1;
-    const int p = pos - (c ? F::npos(0) : 0);
-    const int kind = c == 0 ? 0 : F::kind(1);
+    const int c = F::cls(pos);
+    const int p = pos - F::kbyte(c);
+    const int kind = F::kind(c);
     float sv[QH] = {0.0f, 0.0f, 0.0f, 0.0f}, mn[QH] = {0.0f, 0.0f, 0.0f, 0.0f};
     if (kind == 2) {
 #pragma unroll
@@ -621,9 +626,9 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
   // half stays in registers, the high halves are read by sixteen lanes at once.
   for (int t = tid; t < F::POSITIONS * 16; t += NT) {
     const int pos = t >> 4, lo = t & 15;
-    const int c = pos < F::npos(0) ? 0 : 1;
-    const int S = c ? F::stride(1) : F::stride(0);
-    uint64_t* dst = lut + (c ? F::ent(1) + (pos - F::npos(0)) * F::stride(1) : pos * F::stride(0));
+    const int c = F::cls(pos);
+    const int S = F::stride(c);
+    uint64_t* dst = lut + F::ent(c) + (pos - F::kbyte(c)) * S;
     const float4 lo4 = halves[pos * 32 + lo];
 #pragma unroll 4
     for (int hi = 0; hi < 16; ++hi) {
@@ -642,7 +647,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
   const float xscale = a.sm_scale * LOG2E;
   if (tid < F::NC * QH) {
     const int c = tid >> 2, hh = tid & 3;
-    const int kind = c == 0 ? 0 : F::kind(1);
+    const int kind = F::kind(c);
     float off;
     if (kind == 2) {
       off = 0.0f;
@@ -650,7 +655,9 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
     } else {
       off = L.offi[kind][hh];
     }
-    const float mul = kind == 2 ? SQRT_HALF_PI / ((float)KD * sqrtf((float)KD)) : 1.0f / (float)F::PD;
+    // q' holds sqrt(PD) Pi q (per half when GROUPED): the sign class's
+    // rho sqrt(pi/2) / m <S Pi q, .> is rho sqrt(pi/2) / (m sqrt(PD)) <S q', .>
+    const float mul = kind == 2 ? SQRT_HALF_PI / ((float)KD * sqrtf((float)F::PD)) : 1.0f / (float)F::PD;
     const float unit = L.rng[c][hh] / EMAX;
     L.uu[c][hh] = mul * unit * xscale;
     L.oo[c][hh] = mul * off * xscale;
@@ -691,15 +698,15 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
         const bool valid = t < t_end;
         float x[QH];
         {
-          // per-token multipliers of the classes: norm (part 0), residual
-          // norm (PROD) or second half's norm (GROUPED)
+          // per-token multipliers of the classes: norm (part 0), then the
+          // second half's norm (GROUPED) and the residual norm (QJL)
           const float m0 = F::GROUPED ? h2f(kd.nrm & 0xFFFFu) : h2f(kd.nrm);
           const float m1 = F::GROUPED ? h2f(kd.nrm >> 16) : h2f(kd.rn);
+          const float m2 = h2f(kd.rn);
           // The table reads run in batches of two chains (eight reads),
           // software-pipelined: batch i + 1 is issued before batch i is
           // summed, so one batch's latency hides behind the other's.
-          constexpr int NCH0 = F::npos(0) / CHAIN;
-          constexpr int NCH = NCH0 + (F::NC > 1 ? F::npos(1) / CHAIN : 0);
+          constexpr int NCH = F::POSITIONS / CHAIN;
           constexpr int NB = NCH / 2;
           static_assert(NCH % 2 == 0, "whole batches of two chains");
           uint32_t acc[F::NC][QH];
@@ -709,10 +716,10 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
 #pragma unroll
             for (int j = 0; j < 2 * CHAIN; ++j) {
               const int g = 2 * bt + j / CHAIN;
-              const int c = g < NCH0 ? 0 : 1;
-              const int pos = (g - (c ? NCH0 : 0)) * CHAIN + j % CHAIN;
-              const int byte = (c ? F::kbyte(1) : 0) + pos;
-              const uint32_t base = (uint32_t)((c ? F::ent(1) : 0) + pos * (c ? F::stride(1) : F::stride(0))) * 8u;
+              const int c = F::chain_cls(g);
+              const int pos = (g - F::chain0(c)) * CHAIN + j % CHAIN;
+              const int byte = F::kbyte(c) + pos;
+              const uint32_t base = (uint32_t)(F::ent(c) + pos * F::stride(c)) * 8u;
               dst[j] = lut_read(smem, base, kd.kw[byte >> 2], byte & 3);
             }
           };
@@ -721,8 +728,8 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
               const int g = 2 * bt + i;
-              const int c = g < NCH0 ? 0 : 1;
-              const int q = g - (c ? NCH0 : 0);
+              const int c = F::chain_cls(g);
+              const int q = g - F::chain0(c);
               const uint64_t sum = src[CHAIN * i] + src[CHAIN * i + 1] + src[CHAIN * i + 2] + src[CHAIN * i + 3];
               const uint32_t lo = (uint32_t)sum, hi = (uint32_t)(sum >> 32);
               if (q == 0) {
@@ -760,6 +767,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
           for (int hh = 0; hh < QH; ++hh) {
             float v = m0 * fmaf((float)acc[0][hh], UU[0][hh], OO[0][hh]);
             if constexpr (F::NC > 1) v = fmaf(m1, fmaf((float)acc[1][hh], UU[1][hh], OO[1][hh]), v);
+            if constexpr (F::NC > 2) v = fmaf(m2, fmaf((float)acc[2][hh], UU[2][hh], OO[2][hh]), v);
             x[hh] = valid ? v : -INFINITY;  // log2 softmax units
           }
           if (a.scores && valid) {
@@ -1021,6 +1029,10 @@ hipError_t launch_vb(int vb, const DecArgs& a, dim3 grid, hipStream_t s) {
 
 // Formats with a kernel: returns false for the rest.
 bool supported(const tq::Parts& P) {
+  if (P.mode == TQ_MODE_GROUPED_PROD) {
+    const int b0 = P.part_bits[0], b1 = P.part_bits[1];
+    return (b0 == 3 && b1 == 2) || (b0 == 4 && b1 == 1);
+  }
   if (P.mode == TQ_MODE_GROUPED) {
     const int b0 = P.part_bits[0], b1 = P.part_bits[1];
     return (b0 == 4 && b1 == 2) || (b0 == 2 && b1 == 2) || (b0 == 3 && b1 == 2) || (b0 == 4 && b1 == 1);
@@ -1044,6 +1056,10 @@ hipError_t dispatch(const tq::Parts& P, int vb, const DecArgs& a, dim3 grid, hip
     }
   }
   const int b0 = P.part_bits[0], b1 = P.part_bits[1];
+  if (P.mode == TQ_MODE_GROUPED_PROD) {
+    if (b0 == 3 && b1 == 2) return launch_vb<TQ_MODE_GROUPED_PROD, 3, 2>(vb, a, grid, s);
+    return launch_vb<TQ_MODE_GROUPED_PROD, 4, 1>(vb, a, grid, s);
+  }
   if (b0 == 4 && b1 == 2) return launch_vb<TQ_MODE_GROUPED, 4, 2>(vb, a, grid, s);
   if (b0 == 2 && b1 == 2) return launch_vb<TQ_MODE_GROUPED, 2, 2>(vb, a, grid, s);
   if (b0 == 3 && b1 == 2) return launch_vb<TQ_MODE_GROUPED, 3, 2>(vb, a, grid, s);
@@ -1100,11 +1116,11 @@ tq_status decode_impl(const tq_key_config* cfg, const void* tables, const void* 
   if (*workspace_bytes < need) return TQ_ERR_WORKSPACE;
   if (!tables || !q || !ctx_len || !idx || !norm || !v_codes || !v_scale || !v_zero || !out)
     return TQ_ERR_ARG;
-  if (P.mode == TQ_MODE_PROD && (!signs || !rnorm)) return TQ_ERR_ARG;
+  if (P.m > 0 && (!signs || !rnorm)) return TQ_ERR_ARG;
   if (!tq::aligned16(tables) || !tq::aligned16(idx) || !tq::aligned16(v_codes) ||
       !tq::aligned16(workspace) || !tq::aligned16(q))
     return TQ_ERR_ARG;
-  if (P.mode == TQ_MODE_PROD && !tq::aligned16(signs)) return TQ_ERR_ARG;
+  if (P.m > 0 && !tq::aligned16(signs)) return TQ_ERR_ARG;
   if (((uintptr_t)v_scale & 7) || ((uintptr_t)v_zero & 7) || ((uintptr_t)norm & 3) ||
       ((uintptr_t)out & 3))
     return TQ_ERR_ARG;

@@ -7,7 +7,8 @@
 // with Pi^T = diag(sigma) H / sqrt(d), so k_hat = sigma * H(w) / sqrt(d): the
 // same 128-point Walsh-Hadamard transform as the encoder, run on w in the
 // lane's registers (two 64-point transforms for GROUPED, each half with its
-// own norm, codebook and sigma).  The QJL term S^T (2 bit - 1) takes two sign
+// own norm, codebook and sigma; GROUPED_PROD adds the QJL term, built in the
+// halves' rotated frame, before the two transforms).  The QJL term S^T (2 bit - 1) takes two sign
 // rows per v_dot2_f32_f16 against S stored in LDS as fp16 row pairs; every lane
 // reads the same pair at once (an LDS broadcast).
 // Values (sixteen lanes per row, eight channels each): v_hat = code * s + z.
@@ -90,7 +91,8 @@ __device__ inline void fwht(float* v) {
 // MODE: tq_mode; W0/W1: storage widths (bits) of the index fields of each part.
 template <int MODE, int W0, int W1>
 __global__ __launch_bounds__(DQ_THREADS) void dequant_keys_kernel(DqKeyArgs a) {
-  constexpr bool GROUPED = MODE == TQ_MODE_GROUPED, PROD = MODE == TQ_MODE_PROD;
+  constexpr bool GROUPED = MODE == TQ_MODE_GROUPED || MODE == TQ_MODE_GROUPED_PROD;
+  constexpr bool PROD = MODE == TQ_MODE_PROD || MODE == TQ_MODE_GROUPED_PROD;  // QJL term
   constexpr int NP = GROUPED ? 2 : 1;
   constexpr int PD = KD / NP;                                  // coordinates per part
   constexpr int IDXB = PD * W0 / 8 + (GROUPED ? PD * W1 / 8 : 0);
@@ -270,7 +272,7 @@ hipError_t launch_keys_w1(int w1, const DqKeyArgs& a, dim3 g, hipStream_t s) {
 
 template <int MODE>
 hipError_t launch_keys(int w0, int w1, const DqKeyArgs& a, dim3 g, hipStream_t s) {
-  if (MODE != TQ_MODE_GROUPED) w1 = 1;
+  if (MODE != TQ_MODE_GROUPED && MODE != TQ_MODE_GROUPED_PROD) w1 = 1;
   switch (w0) {
     case 1: return launch_keys_w1<MODE, 1>(w1, a, g, s);
     case 2: return launch_keys_w1<MODE, 2>(w1, a, g, s);
@@ -301,7 +303,7 @@ extern "C" tq_status tq_dequantize_keys(const tq_key_config* cfg, const void* ta
   if (n_vec == 0) return TQ_OK;
   if (!tables || !idx || !norm || !tq::aligned16(tables) || !tq::aligned16(idx) || ((uintptr_t)norm & 3))
     return TQ_ERR_ARG;
-  if (P.mode == TQ_MODE_PROD && (!signs || !rnorm || !tq::aligned16(signs) || ((uintptr_t)rnorm & 1)))
+  if (P.m > 0 && (!signs || !rnorm || !tq::aligned16(signs) || ((uintptr_t)rnorm & 1)))
     return TQ_ERR_ARG;
   if (slots && ((uintptr_t)slots & 7)) return TQ_ERR_ARG;
   DqKeyArgs a;
@@ -324,7 +326,8 @@ extern "C" tq_status tq_dequantize_keys(const tq_key_config* cfg, const void* ta
   hipError_t e;
   if (P.mode == TQ_MODE_MSE) e = launch_keys<TQ_MODE_MSE>(P.part_width[0], 1, a, g, s);
   else if (P.mode == TQ_MODE_PROD) e = launch_keys<TQ_MODE_PROD>(P.part_width[0], 1, a, g, s);
-  else e = launch_keys<TQ_MODE_GROUPED>(P.part_width[0], P.part_width[1], a, g, s);
+  else if (P.mode == TQ_MODE_GROUPED) e = launch_keys<TQ_MODE_GROUPED>(P.part_width[0], P.part_width[1], a, g, s);
+  else e = launch_keys<TQ_MODE_GROUPED_PROD>(P.part_width[0], P.part_width[1], a, g, s);
   return e == hipSuccess ? TQ_OK : TQ_ERR_HIP;
 }
 

@@ -6,6 +6,10 @@
 //   O(d log d) as the "tqlite" README's 已知限制 asks), idx_j = #{t : y_j >= t},
 //   PROD: r = y - c[idx], signs [S r >= 0] (the one dense contraction, on
 //   MFMA), rho = n ||r|| / sqrt(d).
+//   GROUPED: the same per half of 64 channels (own norm, sigma, codebook).
+//   GROUPED_PROD: GROUPED, then the signs of S w for the whole key's residual
+//   in the halves' rotated frame, w = concat_j (n_j / 8) r_j (difai.kr
+//   tutorial 算法概述: one sketch of k - decompress(k)), rho = ||w||.
 // Values (bit-packing article sections 二/三): per-token groups of 32 channels,
 // asymmetric min/max with fp16 scale and zero, 2- or 4-bit codes.
 //
@@ -54,6 +58,11 @@ struct KeyArgs {
   uint16_t* rnorm;
   int idx_row_bytes;
   int n_tiles;
+  // the configuration as the host describes it: index bits and storage
+  // widths per part, rows of S.  The kernel checks the tables' header against
+  // them and stores with these widths, so tables of another configuration
+  // cannot make it write past a record.
+  int bits0, bits1, w0, w1, m;
 };
 
 // The 32 coordinates a lane loads of one key, as loaded (16-bit types: four
@@ -390,12 +399,14 @@ __device__ __forceinline__ const KeyArgs& key_set(const KeyLaunch<KIND>& L, int 
   else return L.k;
 }
 
-// MODE: TQ_MODE_MSE / PROD / GROUPED.  DT: input dtype.  VB: value bits
+// MODE: TQ_MODE_MSE / PROD / GROUPED / GROUPED_PROD.  DT: input dtype.  VB: value bits
 // (KEYS_AND_VALUES only).
 // Waves per SIMD the register allocation is held to: three (at most 168
 // VGPRs) for 16-bit inputs in MSE and PROD mode; two for GROUPED and float32
 // inputs, which need more registers and would spill at three.
-constexpr int key_waves_per_simd(int mode, int dt) { return mode == TQ_MODE_GROUPED || dt == TQ_F32 ? 2 : 3; }
+constexpr bool grouped_mode(int mode) { return mode == TQ_MODE_GROUPED || mode == TQ_MODE_GROUPED_PROD; }
+constexpr bool qjl_mode(int mode) { return mode == TQ_MODE_PROD || mode == TQ_MODE_GROUPED_PROD; }
+constexpr int key_waves_per_simd(int mode, int dt) { return grouped_mode(mode) || dt == TQ_F32 ? 2 : 3; }
 
 template <int MODE, int DT, int KIND, int VB>
 __global__ __launch_bounds__(WAVES * 64, key_waves_per_simd(MODE, DT)) void encode_keys_kernel(KeyLaunch<KIND> L) {
@@ -415,11 +426,16 @@ __global__ __launch_bounds__(WAVES * 64, key_waves_per_simd(MODE, DT)) void enco
   }
   const KeyArgs& a = key_set<KIND>(L, ent);
   const tq_blob_header* H = (const tq_blob_header*)a.tables;
-  constexpr int NP = MODE == TQ_MODE_GROUPED ? 2 : 1;
+  constexpr bool GRP = grouped_mode(MODE), QJL = qjl_mode(MODE);
+  constexpr int NP = GRP ? 2 : 1;
+  // tables of another configuration: nothing is written (uniform per block)
+  if (H->magic != TQ_BLOB_MAGIC || H->d != KD || H->mode != MODE || H->n_parts != NP ||
+      H->part_bits[0] != a.bits0 || (NP == 2 && H->part_bits[1] != a.bits1) || H->m != a.m)
+    return;
   __shared__ __align__(16) tq_hint s_hint[NP][TQ_MAX_HINT];
-  __shared__ float s_cent[MAX_LEVELS];
+  __shared__ float s_cent[QJL ? NP * MAX_LEVELS : 1];
   constexpr int SPITCH = KD + 8;  // halves per padded row of S
-  __shared__ __align__(16) _Float16 s_S[MODE == TQ_MODE_PROD ? KD * SPITCH : 8];
+  __shared__ __align__(16) _Float16 s_S[QJL ? KD * SPITCH : 8];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -442,24 +458,25 @@ __global__ __launch_bounds__(WAVES * 64, key_waves_per_simd(MODE, DT)) void enco
   // the index arithmetically; all others look up a hint grid in LDS.  Those
   // small codebooks are symmetric (Gaussian Lloyd-Max), so their cells are
   // equally wide about zero: boundaries {0} (two cells) or {-t, 0, t} (four
-  // cells).  The index is then [y >= 0], resp. floor(y / t + 2), taken as
-  // floor(clamp(fma(x, ua / n, ub), 0, levels - 1)) on the unscaled
-  // coordinate x = n y: three operations per coordinate.  It differs from the
-  // count of boundaries at or below y only where y is within a few ulps of a
-  // boundary.  A table that is not symmetric goes to the hint grid instead.
+  // cells).  The index is then [y >= 0], taken as [x >= 0] on the unscaled
+  // coordinate x = n y (exact), resp. floor(y / t + 2), taken as
+  // floor(clamp(fma(x, 1 / (t n), 2), 0, 3)): three operations per
+  // coordinate, differing from the count of boundaries at or below y only
+  // where y is within a few ulps of a boundary.  A table that is not
+  // symmetric goes to the hint grid instead.
   const int lev0 = H->part_levels[0];
   const float* bnd = (const float*)(a.tables + H->off_bounds[0]);
   const float bt0 = bnd[0], bt1 = bnd[1], bt2 = bnd[2];
-  const bool direct = NP == 1 && ((lev0 == 2 && bt0 == 0.0f) ||
-                                  (lev0 == 4 && bt1 == 0.0f && bt2 > 0.0f && bt0 == -bt2));
-  const float ua = lev0 == 2 ? 0x1p64f : 1.0f / bt2, ub = lev0 == 2 ? 1.0f : 2.0f;
+  const bool direct2 = NP == 1 && lev0 == 2 && bt0 == 0.0f;
+  const bool direct = direct2 || (NP == 1 && lev0 == 4 && bt1 == 0.0f && bt2 > 0.0f && bt0 == -bt2);
+  const float ua = 1.0f / bt2, ub = 2.0f;
   const float utop = (float)(lev0 - 1);
   // sigma of the coordinates loaded into x[r]: 32 (r >> 3) + 8 g + (r & 7)
   float4 sg[8];
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     const int j = 32 * c + 8 * g;
-    const int part = MODE == TQ_MODE_GROUPED ? j / (KD / 2) : 0;
+    const int part = GRP ? j / (KD / 2) : 0;
     const float4* sp = (const float4*)((const float*)(a.tables + H->off_sigma[part]) + (j - part * (KD / 2)));
     sg[2 * c] = sp[0];
     sg[2 * c + 1] = sp[1];
@@ -486,9 +503,11 @@ __global__ __launch_bounds__(WAVES * 64, key_waves_per_simd(MODE, DT)) void enco
       }
     }
   }
-  if (MODE == TQ_MODE_PROD) {
-    const float* c = (const float*)(a.tables + H->off_centroids[0]);
-    for (int i = threadIdx.x; i < H->part_levels[0]; i += blockDim.x) s_cent[i] = c[i];
+  if (QJL) {
+    for (int p = 0; p < NP; ++p) {
+      const float* c = (const float*)(a.tables + H->off_centroids[p]);
+      for (int i = threadIdx.x; i < H->part_levels[p]; i += blockDim.x) s_cent[p * MAX_LEVELS + i] = c[i];
+    }
     // S in LDS, rows padded to 136 halves so that the sixteen rows one MFMA
     // fragment read touches fall in distinct banks.  Fragment (nt, ks) of lane
     // (kk, g): row 16 nt + kk, coordinates 32 g + 8 ks .. + 7, matching the
@@ -516,8 +535,8 @@ __global__ __launch_bounds__(WAVES * 64, key_waves_per_simd(MODE, DT)) void enco
   __syncthreads();
 
   const float inv_sqrt_d = 1.0f / sqrtf((float)KD);
-  const int w0 = index_width_dev(H->part_bits[0]);
-  const int w1 = NP == 2 ? index_width_dev(H->part_bits[1]) : 0;
+  const int w0 = a.w0;
+  const int w1 = NP == 2 ? a.w1 : 0;
 
   for (; tile < a.n_tiles; tile += tile_step) {
     // the next tile of this wave is requested before this one is encoded
@@ -537,32 +556,74 @@ __global__ __launch_bounds__(WAVES * 64, key_waves_per_simd(MODE, DT)) void enco
     }
     ss0 = xor_sum(xor_sum(ss0, 16), 32);
     ss1 = xor_sum(xor_sum(ss1, 16), 32);
+    // A sum of squares outside [2^-100, 2^100] may have lost range (fp32
+    // squares underflow for keys below about 1e-19 and overflow above about
+    // 1.8e19; zero keys come here too): it is redone on the coordinates
+    // scaled by the power of two that brings the largest into [1, 2), and
+    // the norm scaled back.  Decided per wave, so ordinary tiles pay one test.
+    float nsc0 = 1.0f, nsc1 = 1.0f;  // norm = sqrt(ss) * nsc
+    {
+      const float st = GRP ? fminf(ss0, ss1) : ss0 + ss1;
+      const float sb = GRP ? fmaxf(ss0, ss1) : ss0 + ss1;
+      const bool odd = !(st >= 0x1p-100f && sb <= 0x1p100f);
+      if (__builtin_amdgcn_ballot_w64(odd) != 0) {
+        float m0 = 0.0f, m1 = 0.0f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          m0 = fmaxf(m0, fabsf(x[r]));
+          m1 = fmaxf(m1, fabsf(x[r + 16]));
+        }
+        m0 = fmaxf(m0, __shfl_xor(m0, 16));
+        m0 = fmaxf(m0, __shfl_xor(m0, 32));
+        m1 = fmaxf(m1, __shfl_xor(m1, 16));
+        m1 = fmaxf(m1, __shfl_xor(m1, 32));
+        if (!GRP) m0 = m1 = fmaxf(m0, m1);
+        const int e0 = m0 > 0.0f ? max(ilogbf(m0), -126) : 0;
+        const int e1 = m1 > 0.0f ? max(ilogbf(m1), -126) : 0;
+        const float s0 = ldexpf(1.0f, -e0), s1 = ldexpf(1.0f, -e1);
+        ss0 = 0.0f;
+        ss1 = 0.0f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float u0 = x[r] * s0, u1 = x[r + 16] * s1;
+          ss0 = fmaf(u0, u0, ss0);
+          ss1 = fmaf(u1, u1, ss1);
+        }
+        ss0 = xor_sum(xor_sum(ss0, 16), 32);
+        ss1 = xor_sum(xor_sum(ss1, 16), 32);
+        nsc0 = ldexpf(1.0f, e0);
+        nsc1 = ldexpf(1.0f, e1);
+      }
+    }
 
     stage_in_lane<1>(x);
     stage_in_lane<2>(x);
     stage_in_lane<4>(x);
     stage_in_lane<8>(x);
-    if (MODE != TQ_MODE_GROUPED) stage_in_lane<16>(x);
+    if (!GRP) stage_in_lane<16>(x);
     stage_cross16(x);
     stage_cross32(x);
 
     // now x[r] is coordinate 32g + r
     float n_part[2];
-    if (MODE == TQ_MODE_GROUPED) {
-      n_part[0] = sqrtf(ss0);
-      n_part[1] = sqrtf(ss1);
+    if (GRP) {
+      n_part[0] = sqrtf(ss0) * nsc0;
+      n_part[1] = sqrtf(ss1) * nsc1;
     } else {
-      n_part[0] = n_part[1] = sqrtf(ss0 + ss1);
+      n_part[0] = n_part[1] = sqrtf(ss0 + ss1) * nsc0;
     }
-    const int part = MODE == TQ_MODE_GROUPED ? (g >> 1) : 0;
+    const int part = GRP ? (g >> 1) : 0;
     const float n = n_part[part];
     const float inv = n > 0.0f ? 1.0f / n : 0.0f;
     // x stays unscaled (y = x / n = x * inv where needed)
     int q[32];
-    if (direct) {
-      // symmetric two- or four-cell codebook (see above); clamped to
-      // [0, levels - 1] first, the conversion's truncation is the floor.  A
-      // zero key (n = 0) gets fma(0, 0, ub): the cell of y = 0.
+    if (direct2) {
+#pragma unroll
+      for (int r = 0; r < 32; ++r) q[r] = x[r] >= 0.0f ? 1 : 0;
+    } else if (direct) {
+      // symmetric four-cell codebook (see above); clamped to [0, levels - 1]
+      // first, the conversion's truncation is the floor.  A zero key (n = 0)
+      // gets fma(0, 0, ub): the cell of y = 0.
       const float un = ua * inv;
 #pragma unroll
       for (int r = 0; r < 32; ++r) q[r] = (int)__builtin_amdgcn_fmed3f(fmaf(x[r], un, ub), 0.0f, utop);
@@ -584,7 +645,7 @@ __global__ __launch_bounds__(WAVES * 64, key_waves_per_simd(MODE, DT)) void enco
 
     if (store) {
       uint8_t* dst = a.idx + slot * a.idx_row_bytes;
-      if (MODE == TQ_MODE_GROUPED) {
+      if (GRP) {
         const int w = part ? w1 : w0;
         const int off = part ? (KD / 2) * w0 / 8 + 32 * (g - 2) * w / 8 : 32 * g * w / 8;
         store_idx(w, dst + off, q);
@@ -599,12 +660,21 @@ __global__ __launch_bounds__(WAVES * 64, key_waves_per_simd(MODE, DT)) void enco
       }
     }
 
-    if constexpr (MODE == TQ_MODE_PROD) {
+    if constexpr (QJL) {
+      // GROUPED_PROD weights each half's residual by n_j / max(n_o, n_n):
+      // w / (max / 8), in [0, 1] times the residual's own scale for fp16
+      float wgt = 1.0f, nmax = n;
+      if constexpr (GRP) {
+        nmax = fmaxf(n_part[0], n_part[1]);
+        wgt = nmax > 0.0f ? n / nmax : 0.0f;
+      }
+      const float* cp = s_cent + (GRP ? part * MAX_LEVELS : 0);
       float rr = 0.0f;
       half8 bhi[4], blo[4];
 #pragma unroll
       for (int r = 0; r < 32; ++r) {
-        const float res = fmaf(x[r], inv, -s_cent[q[r]]);
+        float res = fmaf(x[r], inv, -cp[q[r]]);
+        if constexpr (GRP) res *= wgt;
         rr = fmaf(res, res, rr);
         const _Float16 h = (_Float16)res;
         const _Float16 lo = (_Float16)(res - (float)h);
@@ -658,7 +728,8 @@ __global__ __launch_bounds__(WAVES * 64, key_waves_per_simd(MODE, DT)) void enco
       if (store) {
         *(uint32_t*)(a.signs + slot * (KD / 8) + 4 * g) = mine;
         if (g == 0) {
-          const float rho = n * sqrtf(rr) * inv_sqrt_d;
+          // rho = n ||r|| / sqrt(d), or ||w|| = max ||w / (max / 8)|| / 8
+          const float rho = GRP ? nmax * sqrtf(rr) * 0.125f : n * sqrtf(rr) * inv_sqrt_d;
           a.rnorm[slot] = __half_as_ushort(__float2half_rn(rho));
         }
       }
@@ -727,7 +798,7 @@ tq_status key_args(const tq_key_config* cfg, const void* tables, const void* key
   const int esz = dtype == TQ_F32 ? 4 : 2;
   if (row_stride < KD || ((row_stride * esz) & 15) || !tq::aligned16(keys)) return TQ_ERR_ARG;
   if (!tq::aligned16(tables) || !tq::aligned16(idx) || ((uintptr_t)norm & 3)) return TQ_ERR_ARG;
-  if (P.mode == TQ_MODE_PROD) {
+  if (P.m > 0) {
     if (!signs || !rnorm || !tq::aligned16(signs) || ((uintptr_t)rnorm & 1)) return TQ_ERR_ARG;
   } else if (signs || rnorm) {
     return TQ_ERR_ARG;
@@ -749,6 +820,11 @@ tq_status key_args(const tq_key_config* cfg, const void* tables, const void* key
   a.rnorm = rnorm;
   a.idx_row_bytes = P.idx_row_bytes;
   a.n_tiles = (int)tiles;
+  a.bits0 = P.part_bits[0];
+  a.bits1 = P.n_parts > 1 ? P.part_bits[1] : 0;
+  a.w0 = P.part_width[0];
+  a.w1 = P.n_parts > 1 ? P.part_width[1] : 0;
+  a.m = P.m;
   return TQ_OK;
 }
 
@@ -760,7 +836,7 @@ tq_status key_args(const tq_key_config* cfg, const void* tables, const void* key
 // flight keep the loads and the MFMA work overlapped).
 int key_blocks(const tq::Parts& P, int n_tiles, int cus) {
   const long long want = ((long long)n_tiles + WAVES - 1) / WAVES;
-  const long long cap = (long long)cus * (P.mode == TQ_MODE_PROD ? 8 : 2);
+  const long long cap = (long long)cus * (P.m > 0 ? 8 : 2);
   return (int)(want < cap ? want : cap);
 }
 
@@ -815,7 +891,8 @@ extern "C" tq_status tq_encode_keys(const tq_key_config* cfg, const void* tables
   } while (0)
   if (P.mode == TQ_MODE_MSE) TQ_LAUNCH_KEYS(TQ_MODE_MSE);
   else if (P.mode == TQ_MODE_PROD) TQ_LAUNCH_KEYS(TQ_MODE_PROD);
-  else TQ_LAUNCH_KEYS(TQ_MODE_GROUPED);
+  else if (P.mode == TQ_MODE_GROUPED) TQ_LAUNCH_KEYS(TQ_MODE_GROUPED);
+  else TQ_LAUNCH_KEYS(TQ_MODE_GROUPED_PROD);
 #undef TQ_LAUNCH_KEYS
   return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_HIP;
 }
@@ -872,7 +949,7 @@ extern "C" tq_status tq_encode_keys_batched(const tq_key_config* cfg, const tq_k
   // suit the MSE and grouped encoders better than the two of a single short
   // set (measured on MI355X: 28 sets of 65536 MSE keys, 0.188 -> 0.175 ms).
   const int n_tiles = b.e[0].n_tiles;
-  int per = cus * (P.mode == TQ_MODE_PROD ? 8 : 4) / n_batch;
+  int per = cus * (P.m > 0 ? 8 : 4) / n_batch;
   const int want = (n_tiles + WAVES - 1) / WAVES;
   if (per > want) per = want;
   if (per < 1) per = 1;
@@ -887,7 +964,8 @@ extern "C" tq_status tq_encode_keys_batched(const tq_key_config* cfg, const tq_k
   } while (0)
   if (P.mode == TQ_MODE_MSE) TQ_LAUNCH_KB(TQ_MODE_MSE);
   else if (P.mode == TQ_MODE_PROD) TQ_LAUNCH_KB(TQ_MODE_PROD);
-  else TQ_LAUNCH_KB(TQ_MODE_GROUPED);
+  else if (P.mode == TQ_MODE_GROUPED) TQ_LAUNCH_KB(TQ_MODE_GROUPED);
+  else TQ_LAUNCH_KB(TQ_MODE_GROUPED_PROD);
 #undef TQ_LAUNCH_KB
   return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_HIP;
 }
@@ -929,7 +1007,8 @@ extern "C" tq_status tq_append_kv(const tq_key_config* cfg, const void* tables, 
   } while (0)
   if (P.mode == TQ_MODE_MSE) TQ_LAUNCH_KV_M(TQ_MODE_MSE);
   else if (P.mode == TQ_MODE_PROD) TQ_LAUNCH_KV_M(TQ_MODE_PROD);
-  else TQ_LAUNCH_KV_M(TQ_MODE_GROUPED);
+  else if (P.mode == TQ_MODE_GROUPED) TQ_LAUNCH_KV_M(TQ_MODE_GROUPED);
+  else TQ_LAUNCH_KV_M(TQ_MODE_GROUPED_PROD);
 #undef TQ_LAUNCH_KV_M
 #undef TQ_LAUNCH_KV
   return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_HIP;

@@ -46,7 +46,12 @@ tq_status describe(const tq_key_config* cfg, Parts* p) {
   if (!cfg || !p) return TQ_ERR_ARG;
   const int d = cfg->d;
   if (d < 16 || d > 256 || (d & (d - 1))) return TQ_ERR_ARG;
-  if (cfg->reserved != 0) return TQ_ERR_ARG;
+  const bool grouped = cfg->mode == TQ_MODE_GROUPED || cfg->mode == TQ_MODE_GROUPED_PROD;
+  if (!grouped && cfg->d_outlier != 0) return TQ_ERR_ARG;
+  if (grouped && cfg->d_outlier != 0 && cfg->d_outlier != d / 2) {
+    // only the even split gives two power-of-two halves
+    return cfg->d_outlier > 0 && cfg->d_outlier < d ? TQ_ERR_UNSUPPORTED : TQ_ERR_ARG;
+  }
   memset(p, 0, sizeof(*p));
   p->d = d;
   p->mode = cfg->mode;
@@ -65,12 +70,14 @@ tq_status describe(const tq_key_config* cfg, Parts* p) {
       p->m = d;
       break;
     case TQ_MODE_GROUPED:
+    case TQ_MODE_GROUPED_PROD:
       if (cfg->bits_outlier < 1 || cfg->bits_outlier > 8) return TQ_ERR_ARG;
       if (cfg->bits_normal < 1 || cfg->bits_normal > 8) return TQ_ERR_ARG;
       p->n_parts = 2;
       p->part_d[0] = p->part_d[1] = d / 2;
       p->part_bits[0] = cfg->bits_outlier;
       p->part_bits[1] = cfg->bits_normal;
+      if (cfg->mode == TQ_MODE_GROUPED_PROD) p->m = d;
       break;
     default:
       return TQ_ERR_ARG;
@@ -336,7 +343,7 @@ extern "C" tq_status tq_build_codebook(const tq_key_config* cfg, void* blob_host
     H.hint_scale[i] = hsc[i];
     H.mse[i] = D[i];
   }
-  if (P.mode == TQ_MODE_PROD) {
+  if (P.m > 0) {
     H.off_S = (uint32_t)off;
     off = align_up(off + sizeof(uint16_t) * (size_t)P.m * P.d);
   }
@@ -370,13 +377,13 @@ extern "C" tq_status tq_build_codebook(const tq_key_config* cfg, void* blob_host
     bd[L - 1] = INFINITY;
     bd[L] = INFINITY;
     // sigma_j = +1 if the top bit of output j is 0, else -1
-    const uint64_t tag = P.mode == TQ_MODE_GROUPED ? (i == 0 ? 3 : 4) : 1;
+    const uint64_t tag = P.n_parts == 2 ? (i == 0 ? 3 : 4) : 1;
     Stream sg(cfg->seed, tag);
     float* sig = (float*)(b + H.off_sigma[i]);
     for (int j = 0; j < P.part_d[i]; ++j) sig[j] = (sg.next() >> 63) ? -1.0f : 1.0f;
     memcpy(b + H.off_hint[i], hint[i].data(), sizeof(tq_hint) * hint[i].size());
   }
-  if (P.mode == TQ_MODE_PROD) {
+  if (P.m > 0) {
     // S: m x d i.i.d. N(0,1) by Box-Muller on consecutive outputs, each value
     // rounded to fp16.  u1 in (0,1], u2 in [0,1) from the top 53 bits.
     Stream ss(cfg->seed, 2);

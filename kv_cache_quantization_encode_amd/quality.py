@@ -24,8 +24,9 @@ FP16_BYTES_PER_TOKEN_HEAD = 2 * 128 * 2  # K and V, fp16, head dim 128
 def key_record_bytes(mode: str, bits: int = 3, bits_outlier: int = 4, bits_normal: int = 2, d: int = 128) -> int:
     """Bytes of one packed key (index row, signs, fp16 norms)."""
     width = lambda b: 1 if b == 1 else 2 if b == 2 else 4 if b <= 4 else 8  # noqa: E731
-    if mode == "grouped":
-        return d // 2 * width(bits_outlier) // 8 + d // 2 * width(bits_normal) // 8 + 4
+    if mode in ("grouped", "grouped_prod"):
+        b = d // 2 * width(bits_outlier) // 8 + d // 2 * width(bits_normal) // 8 + 4
+        return b + (d // 8 + 2 if mode == "grouped_prod" else 0)
     if mode == "prod":
         return d * width(bits - 1) // 8 + d // 8 + 4
     return d * width(bits) // 8 + 2
@@ -52,15 +53,18 @@ def memory_table(contexts=(1024, 4096, 16384, 32768, 65536, 131072), kv_heads: i
 
 @torch.no_grad()
 def attention_quality(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, key_cfg: dict, v_bits: int,
-                      seed: int = 42, topk: int = 5) -> dict:
+                      seed: int = 42, topk: int = 5, per_head: bool = False) -> dict:
     """q [B, Hq, d], k and v [B, Hkv, N, d] (any float dtype, on the GPU).
     Encodes k and v with the HIP path, runs one decode step returning scores,
     and compares with exact float32 attention:
+      score_cosine mean cosine similarity of the score vectors q.k vs q.k_hat
       out_cosine   mean cosine similarity of attention outputs
       kl           mean KL(p_exact || p_quant) of the attention weights
-      top1         fraction of heads whose highest-weight token agrees
+      top1         fraction of heads whose highest-scoring token agrees
       topk_overlap mean |top-k exact & top-k quant| / k
-      score_rel_rms  RMS of the score error over the RMS of the exact scores"""
+      score_rel_rms  RMS of the score error over the RMS of the exact scores
+    With per_head, also "heads": the per-head values ([B, Hq] arrays on the
+    host), the quantised scores and the decoded outputs."""
     B, Hq, d = q.shape
     _, Hkv, N, _ = k.shape
     G = Hq // Hkv
@@ -81,10 +85,18 @@ def attention_quality(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, key_cfg
     logp_q = torch.log_softmax(scores * scale, dim=-1)
     kl = torch.sum(p_ex * (torch.log(p_ex.clamp_min(1e-30)) - logp_q), dim=-1)
     cos = torch.nn.functional.cosine_similarity(out, o_ex, dim=-1)
+    scos = torch.nn.functional.cosine_similarity(scores, s_ex, dim=-1)
     top_ex = torch.topk(s_ex, topk, dim=-1).indices
     top_q = torch.topk(scores, topk, dim=-1).indices
     overlap = (top_ex.unsqueeze(-1) == top_q.unsqueeze(-2)).any(-1).float().sum(-1) / topk
+    top1 = (top_ex[..., 0] == top_q[..., 0]).float()
     rel = torch.sqrt(torch.mean((scores - s_ex) ** 2) / torch.mean(s_ex ** 2))
-    return dict(out_cosine=float(cos.mean()), kl=float(kl.mean()),
-                top1=float((top_ex[..., 0] == top_q[..., 0]).float().mean()),
-                topk_overlap=float(overlap.mean()), score_rel_rms=float(rel))
+    res = dict(score_cosine=float(scos.mean()), out_cosine=float(cos.mean()), kl=float(kl.mean()),
+               top1=float(top1.mean()), topk_overlap=float(overlap.mean()), score_rel_rms=float(rel))
+    if per_head:
+        res["heads"] = dict(score_cosine=scos.cpu().numpy(), out_cosine=cos.cpu().numpy(), kl=kl.cpu().numpy(),
+                            top1=top1.cpu().numpy(), topk_overlap=overlap.cpu().numpy(),
+                            err2=torch.sum((scores - s_ex) ** 2, dim=-1).cpu().numpy(),
+                            ref2=torch.sum(s_ex ** 2, dim=-1).cpu().numpy(), scores=scores.cpu().numpy(),
+                            out=out.cpu().numpy())
+    return res

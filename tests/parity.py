@@ -3,7 +3,8 @@ infrastructure; imports the oracle).
 
 Bytes: index and sign bytes equal the oracle's, except coordinates whose
 oracle float64 value lies within 1e-6 of a decision boundary (index) or of
-zero (sign), measured in the unit-norm domain; those are counted and must be
+zero (sign), measured in the unit-norm domain (the sketch of the unit key's
+residual, z / sqrt(d) for prod and z / ||k|| for grouped_prod); those are counted and must be
 at most 1e-4 of all coordinates.  A key whose index legitimately differs at a
 boundary gets its sign bits and residual norm checked against the oracle's
 QJL stage rerun with the GPU's indices (both choices are correct there).
@@ -41,14 +42,15 @@ def _boundary_distance(y, boundaries):
 
 def check_keys(rows_keys, T, gpu: dict, report: dict | None = None):
     """rows_keys: [n, d] float64 inputs; gpu: unpacked planes for those rows
-    (idx [n, d] int, norm16, and for prod bits [n, m], rnorm16)."""
+    (idx [n, d] int, norm16, and for the QJL modes bits [n, m], rnorm16)."""
     cfg = T.cfg
     d = cfg.d
     enc = O.encode_keys(rows_keys, T)
     n = rows_keys.shape[0]
     stats = dict(n=n, idx_band=0, sign_band=0)
     # ---- indices
-    if cfg.mode == "grouped":
+    qjl = cfg.mode in ("prod", "grouped_prod")
+    if cfg.mode in ("grouped", "grouped_prod"):
         h = d // 2
         dist = np.concatenate([_boundary_distance(enc["y"][:, :h], T.halves[0]["boundaries"]),
                                _boundary_distance(enc["y"][:, h:], T.halves[1]["boundaries"])], axis=1)
@@ -62,24 +64,30 @@ def check_keys(rows_keys, T, gpu: dict, report: dict | None = None):
     # ---- norms
     ul = fp16_ulps(gpu["norm16"], enc["norm16"])
     assert ul.max(initial=0) <= 1, "norm differs by %d ulp" % ul.max()
-    if cfg.mode == "prod":
+    if qjl:
         keys_diff = diff.any(axis=1)
         z = enc["z"].copy()
         ref_bits = enc["bits"].copy()
         ref_rn = enc["rnorm16"].copy()
         if keys_diff.any():
-            re = O.prod_given_idx(enc["norm"][keys_diff], enc["y"][keys_diff], gpu["idx"][keys_diff], T)
+            stage = O.prod_given_idx if cfg.mode == "prod" else O.grouped_prod_given_idx
+            re = stage(enc["norm"][keys_diff], enc["y"][keys_diff], gpu["idx"][keys_diff], T)
             z[keys_diff] = re["z"]
             ref_bits[keys_diff] = re["bits"]
             ref_rn[keys_diff] = re["rnorm16"]
+        if cfg.mode == "prod":
+            zu = np.abs(z) / math.sqrt(d)
+        else:
+            kn = np.sqrt(np.sum(enc["norm"] ** 2, axis=1))
+            zu = np.abs(z) / np.where(kn > 0, kn, 1.0)[:, None]
         sdiff = gpu["bits"] != ref_bits
-        sbad = sdiff & (np.abs(z) / math.sqrt(d) >= BAND)
+        sbad = sdiff & (zu >= BAND)
         assert not sbad.any(), "sign mismatch outside the band at %s (|z|=%s)" % (
             np.argwhere(sbad)[:5].tolist(), np.abs(z[sbad])[:5])
         stats["sign_band"] = int(sdiff.sum())
         rul = fp16_ulps(gpu["rnorm16"], ref_rn)
         assert rul.max(initial=0) <= 1, "rnorm differs by %d ulp" % rul.max()
-    total = n * d * (2 if cfg.mode == "prod" else 1)
+    total = n * d * (2 if qjl else 1)
     assert stats["idx_band"] + stats["sign_band"] <= max(1, BAND_FRACTION * total), stats
     if report is not None:
         report.update(stats)
@@ -89,12 +97,13 @@ def check_keys(rows_keys, T, gpu: dict, report: dict | None = None):
 def unpack_gpu_keys(T, planes: dict) -> dict:
     """GPU planes (numpy) -> fields comparable with the oracle's."""
     rec = dict(idx=planes["idx"], norm=planes["norm"].view(np.float16))
-    if T.cfg.mode == "prod":
+    qjl = T.cfg.mode in ("prod", "grouped_prod")
+    if qjl:
         rec["signs"] = planes["signs"]
         rec["rnorm"] = planes["rnorm"].view(np.float16)
     u = O.unpack_key_record(rec, T)
     out = dict(idx=u["idx"], norm16=u["norm16"])
-    if T.cfg.mode == "prod":
+    if qjl:
         out["bits"] = u["bits"]
         out["rnorm16"] = u["rnorm16"]
     return out

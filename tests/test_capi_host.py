@@ -31,7 +31,8 @@ def test_library_exports_every_declared_symbol():
 
 CFGS = [dict(mode="mse", bits=b) for b in (1, 2, 3, 4, 8)] + \
        [dict(mode="prod", bits=b) for b in (2, 3, 4)] + \
-       [dict(mode="grouped", bits_outlier=4, bits_normal=2), dict(mode="grouped", bits_outlier=3, bits_normal=1)]
+       [dict(mode="grouped", bits_outlier=4, bits_normal=2), dict(mode="grouped", bits_outlier=3, bits_normal=1),
+        dict(mode="grouped_prod", bits_outlier=3, bits_normal=2), dict(mode="grouped_prod", bits_outlier=4, bits_normal=1)]
 
 
 def _oracle_cfg(kw, seed):
@@ -63,7 +64,7 @@ def test_tables_match_oracle(kw, seed):
     h = tq.parse_tables(blob)
     assert h["magic"] == 0x31425154 and h["total_bytes"] == blob.size
     T = O.build_tables(_oracle_cfg(kw, seed))
-    if kw["mode"] == "grouped":
+    if kw["mode"] in ("grouped", "grouped_prod"):
         halves = T.halves
     else:
         halves = [dict(centroids=T.centroids, boundaries=T.boundaries, sigma=T.sigma, mse=T.mse,
@@ -77,8 +78,11 @@ def test_tables_match_oracle(kw, seed):
         assert np.array_equal(part["sigma"].astype(np.float64), half["sigma"])
     for got, half in zip(mse, halves):
         assert abs(got - half["mse"]) < 1e-12
-    if kw["mode"] == "prod":
+    if kw["mode"] in ("prod", "grouped_prod"):
+        assert h["m"] == 128
         assert np.array_equal(h["S"].astype(np.float64), T.S)
+    else:
+        assert h["m"] == 0
 
 
 @pytest.mark.parametrize("bits", [1, 2, 3, 4, 5, 8])
@@ -108,6 +112,7 @@ def test_idx_row_bytes():
     assert tq.idx_row_bytes(L.key_config(mode="prod", bits=4)) == 64
     assert tq.idx_row_bytes(L.key_config(mode="mse", bits=8)) == 128
     assert tq.idx_row_bytes(L.key_config(mode="grouped", bits_outlier=4, bits_normal=2)) == 48
+    assert tq.idx_row_bytes(L.key_config(mode="grouped_prod", bits_outlier=3, bits_normal=2)) == 48
     assert tq.idx_row_bytes(L.key_config(mode="mse", bits=9)) == 0
 
 
@@ -126,11 +131,25 @@ def test_bad_configs_rejected(kw):
     assert st == L.TQ_ERR_ARG
 
 
-def test_reserved_field_must_be_zero():
-    cfg = L.key_config()
-    cfg.reserved = 1
+def _blob_status(cfg):
     size = ctypes.c_size_t(0)
-    assert L.lib.tq_build_codebook(ctypes.byref(cfg), None, ctypes.byref(size), None) == L.TQ_ERR_ARG
+    return L.lib.tq_build_codebook(ctypes.byref(cfg), None, ctypes.byref(size), None)
+
+
+def test_d_outlier_field():
+    """d_outlier: 0 or d/2 for the grouped modes (both the even split); any
+    other split inside (0, d) is unsupported, values outside it invalid; the
+    single-part modes must leave it 0."""
+    for mode in ("grouped", "grouped_prod"):
+        assert _blob_status(L.key_config(mode=mode, d_outlier=0)) == L.TQ_OK
+        assert _blob_status(L.key_config(mode=mode, d_outlier=64)) == L.TQ_OK
+        assert _blob_status(L.key_config(mode=mode, d_outlier=32)) == L.TQ_ERR_UNSUPPORTED
+        assert _blob_status(L.key_config(mode=mode, d_outlier=128)) == L.TQ_ERR_ARG
+        assert _blob_status(L.key_config(mode=mode, d_outlier=-4)) == L.TQ_ERR_ARG
+    for mode in ("mse", "prod"):
+        assert _blob_status(L.key_config(mode=mode, d_outlier=64)) == L.TQ_ERR_ARG
+    a, b = (tq.build_codebook(L.key_config(mode="grouped", d_outlier=v))[0] for v in (0, 64))
+    assert np.array_equal(a, b)
 
 
 def test_blob_capacity_checked():
@@ -165,6 +184,10 @@ def test_encode_keys_argument_errors():
     assert _enc(prod, stride=129) == L.TQ_ERR_ARG               # rows not 16-byte aligned
     assert _enc(prod, signs=None) == L.TQ_ERR_ARG               # PROD needs the sign plane
     assert _enc(mse) == L.TQ_ERR_ARG                            # MSE must not pass signs/rnorm
+    gp = L.key_config(mode="grouped_prod", bits_outlier=3, bits_normal=2)
+    assert _enc(gp, rnorm=None) == L.TQ_ERR_ARG                 # GROUPED_PROD needs both QJL planes
+    assert _enc(L.key_config(mode="grouped"), signs=None) == L.TQ_ERR_ARG   # grouped: neither QJL plane
+    assert _enc(L.key_config(mode="grouped"), signs=None, rnorm=None, n=0) == L.TQ_OK
     assert _enc(prod, n=-1) == L.TQ_ERR_ARG
     assert _enc(prod, dtype=9) == L.TQ_ERR_ARG
     assert _enc(L.key_config(d=64, mode="prod", bits=3)) == L.TQ_ERR_UNSUPPORTED
@@ -335,3 +358,20 @@ def test_no_device_reports_hip_error():
 def test_status_strings():
     for s in (0, -1, -2, -3, -4, 5):
         assert isinstance(tq.status_string(s), str) and tq.status_string(s)
+
+
+def test_select_outlier_channels_workspace_query_and_errors():
+    f = L.lib.tq_select_outlier_channels
+    size = ctypes.c_size_t(0)
+    assert f(None, L.TQ_BF16, 5000, 128, 128, 64, None, None, ctypes.byref(size), None) == L.TQ_OK
+    assert size.value == 5 * 2 * 128 * 8                       # five 1024-row blocks of float64 sums
+    assert f(None, L.TQ_BF16, 0, 128, 128, 64, None, None, ctypes.byref(size), None) == L.TQ_OK
+    assert f(None, L.TQ_BF16, 10, 128, 64, 32, None, None, ctypes.byref(size), None) == L.TQ_ERR_UNSUPPORTED
+    assert f(None, L.TQ_BF16, 10, 128, 128, 129, None, None, ctypes.byref(size), None) == L.TQ_ERR_ARG
+    assert f(None, L.TQ_BF16, 10, 128, 128, -1, None, None, ctypes.byref(size), None) == L.TQ_ERR_ARG
+    assert f(None, 9, 10, 128, 128, 64, None, None, ctypes.byref(size), None) == L.TQ_ERR_ARG
+    small = ctypes.c_size_t(8)
+    assert f(FAKE, L.TQ_BF16, 5000, 128, 128, 64, FAKE, FAKE, ctypes.byref(small), None) == L.TQ_ERR_WORKSPACE
+    big = ctypes.c_size_t(1 << 20)
+    assert f(FAKE, L.TQ_BF16, 5000, 128, 128, 64, None, FAKE, ctypes.byref(big), None) == L.TQ_ERR_ARG   # perm
+    assert f(None, L.TQ_BF16, 5000, 128, 128, 64, FAKE, FAKE, ctypes.byref(big), None) == L.TQ_ERR_ARG   # x

@@ -21,7 +21,8 @@ CASES = [(dict(mode="prod", bits=3), torch.bfloat16, 2),
          (dict(mode="prod", bits=4), torch.bfloat16, 4),
          (dict(mode="mse", bits=4), torch.float32, 4),
          (dict(mode="mse", bits=8), torch.float16, 2),
-         (dict(mode="grouped", bits_outlier=4, bits_normal=2), torch.float16, 4)]
+         (dict(mode="grouped", bits_outlier=4, bits_normal=2), torch.float16, 4),
+         (dict(mode="grouped_prod", bits_outlier=3, bits_normal=2), torch.bfloat16, 2)]
 
 
 def _sentinel_planes(T, v_bits, n_rec):
@@ -38,7 +39,7 @@ def _sentinel_planes(T, v_bits, n_rec):
 def test_append_kv_equals_two_encodes(case, n):
     kw, dtype, v_bits = case
     T = tq.Tables(L.key_config(seed=13, **kw), DEV)
-    scale = W.w5_col_scale() if kw["mode"] == "grouped" else None
+    scale = W.w5_col_scale() if kw["mode"].startswith("grouped") else None
     keys = torch.from_numpy(W.kv_rows(61, 1, n, scale_cols=scale)[0]).to(DEV).to(dtype)
     vals = torch.from_numpy(W.kv_rows(61, 2, n)[0]).to(DEV).to(dtype)
     n_rec = n + 37

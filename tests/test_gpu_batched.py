@@ -20,7 +20,8 @@ CASES = [(dict(mode="mse", bits=4), torch.bfloat16, 3, 1000, False),
          (dict(mode="mse", bits=8), torch.bfloat16, 28, 512, False),
          (dict(mode="prod", bits=3), torch.bfloat16, 2, 4096, True),
          (dict(mode="prod", bits=4), torch.float32, 5, 333, False),
-         (dict(mode="grouped", bits_outlier=4, bits_normal=2), torch.float16, 4, 1, True)]
+         (dict(mode="grouped", bits_outlier=4, bits_normal=2), torch.float16, 4, 1, True),
+         (dict(mode="grouped_prod", bits_outlier=4, bits_normal=1), torch.bfloat16, 3, 700, True)]
 
 
 @pytest.mark.parametrize("case", CASES, ids=lambda c: "%s-%s-x%d-n%d" % (
@@ -28,7 +29,7 @@ CASES = [(dict(mode="mse", bits=4), torch.bfloat16, 3, 1000, False),
 def test_batched_equals_per_set_encode(case):
     kw, dtype, nb, n, with_slots = case
     tables = [tq.Tables(L.key_config(seed=100 + i, **kw), DEV) for i in range(nb)]
-    scale = W.w5_col_scale() if kw["mode"] == "grouped" else None
+    scale = W.w5_col_scale() if kw["mode"].startswith("grouped") else None
     keys = [torch.from_numpy(W.kv_rows(70 + i, 1, n, scale_cols=scale)[0]).to(DEV).to(dtype) for i in range(nb)]
     n_rec = n + 9
     slots = None

@@ -1,8 +1,9 @@
 """Outlier-channel selection for GROUPED mode on the GPU.
 
-Keys whose 64 high-variance channels sit at scattered positions: the
-per-channel moments match float64 sums on the host, the selection recovers
-exactly the planted channels, and grouped encode + decode on the reordered
+The selection equals the oracle's variance ranking.  Keys whose 64
+high-variance channels sit at scattered positions: the per-channel moments
+match float64 sums on the host, the selection recovers exactly the planted
+channels, and grouped encode + decode on the reordered
 keys and queries (a common channel permutation leaves q.k unchanged) agrees
 with the oracle and beats the fixed split that ignores the variances."""
 import numpy as np
@@ -39,6 +40,29 @@ def test_channel_moments_match_float64_sums():
     k = kv.astype(np.float64)
     assert np.allclose(m[0], k.sum(0), rtol=0, atol=1e-12 * np.abs(k).sum(0).max())
     assert np.allclose(m[1], (k * k).sum(0), rtol=1e-12, atol=0)
+
+
+def test_selection_matches_oracle():
+    """tq_select_outlier_channels against the oracle's variance ranking,
+    element for element: channel scales spread over two decades (ranks are
+    far apart at this sample size), a copy of a channel (an exact tie: the
+    lower channel wins on both sides), a constant channel, a ragged row count,
+    and the degenerate splits 0 and 128 and an empty key set (identity)."""
+    rng = np.random.default_rng(52)
+    n = 3001
+    scale = np.exp(rng.uniform(np.log(0.1), np.log(10.0), 128)).astype(np.float32)
+    kv, kb = W.kv_rows(52, 1, n, scale_cols=scale)
+    kv = kv.copy()
+    kv[:, 90] = kv[:, 17]                         # exact tie with channel 17
+    kv[:, 5] = 2.5                                # constant channel: variance 0
+    kv, kb = W.to_bf16(kv)                        # (both edits are bf16 values already)
+    x = torch.from_numpy(kb.view(np.int16)).view(torch.bfloat16).to(DEV)
+    for n_out in (64, 1, 0, 128, 37):
+        got = tq.select_outlier_channels(x, n_out).cpu().numpy()
+        want = O.select_outlier_channels(kv.astype(np.float64), n_out)
+        assert np.array_equal(got, want), (n_out, got[:8], want[:8])
+    empty = tq.select_outlier_channels(x[:0], 64).cpu().numpy()
+    assert np.array_equal(empty, np.arange(128))
 
 
 def test_selection_recovers_planted_channels_and_grouped_parity():

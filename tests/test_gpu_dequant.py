@@ -31,7 +31,9 @@ DEV = "cuda"
 CFGS = [dict(mode="prod", bits=2), dict(mode="prod", bits=3), dict(mode="prod", bits=4),
         dict(mode="mse", bits=1), dict(mode="mse", bits=2), dict(mode="mse", bits=3), dict(mode="mse", bits=4),
         dict(mode="mse", bits=8), dict(mode="grouped", bits_outlier=4, bits_normal=2),
-        dict(mode="grouped", bits_outlier=3, bits_normal=1)]
+        dict(mode="grouped", bits_outlier=3, bits_normal=1),
+        dict(mode="grouped_prod", bits_outlier=3, bits_normal=2),
+        dict(mode="grouped_prod", bits_outlier=4, bits_normal=2)]
 
 
 def _ocfg(kw):
@@ -42,7 +44,7 @@ def _ocfg(kw):
 def _planes(rec, mode):
     p = dict(idx=torch.from_numpy(rec["idx"]).to(DEV),
              norm=torch.from_numpy(np.ascontiguousarray(rec["norm"]).view(np.float16)).to(DEV))
-    if mode == "prod":
+    if mode in ("prod", "grouped_prod"):
         p["signs"] = torch.from_numpy(rec["signs"]).to(DEV)
         p["rnorm"] = torch.from_numpy(np.ascontiguousarray(rec["rnorm"]).view(np.float16)).to(DEV)
     return p
@@ -52,7 +54,7 @@ def _planes(rec, mode):
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 def test_dequantize_keys_matches_oracle(kw, dtype):
     n = 1000  # ragged: not a multiple of the 256-row block
-    scale = W.w5_col_scale() if kw["mode"] == "grouped" else None
+    scale = W.w5_col_scale() if kw["mode"].startswith("grouped") else None
     kv, _ = W.kv_rows(31, 1, n, scale_cols=scale)
     To = O.build_tables(_ocfg(kw))
     enc = O.encode_keys(kv.astype(np.float64), To)

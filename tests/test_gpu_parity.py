@@ -46,7 +46,13 @@ def _gpu_key_fields(Tg, To, planes, rows=None):
 KEY_CFGS = [dict(mode="prod", bits=3), dict(mode="prod", bits=4), dict(mode="prod", bits=2),
             dict(mode="mse", bits=4), dict(mode="mse", bits=8), dict(mode="mse", bits=1), dict(mode="mse", bits=2),
             dict(mode="mse", bits=3), dict(mode="grouped", bits_outlier=4, bits_normal=2),
-            dict(mode="grouped", bits_outlier=3, bits_normal=1)]
+            dict(mode="grouped", bits_outlier=3, bits_normal=1),
+            dict(mode="grouped_prod", bits_outlier=3, bits_normal=2),
+            dict(mode="grouped_prod", bits_outlier=4, bits_normal=1)]
+
+
+def _grouped(kw):
+    return kw["mode"].startswith("grouped")
 
 
 def test_encode_w1_unit_keys_fp32():
@@ -63,7 +69,7 @@ def test_encode_w1_unit_keys_fp32():
 @pytest.mark.parametrize("kw", KEY_CFGS, ids=lambda k: "-".join(str(v) for v in k.values()))
 def test_encode_keys_modes_bf16(kw):
     n = 3001  # ragged: not a multiple of the 16-key tile
-    kv, kb = W.kv_rows(9, 1, n, scale_cols=W.w5_col_scale() if kw["mode"] == "grouped" else None)
+    kv, kb = W.kv_rows(9, 1, n, scale_cols=W.w5_col_scale() if _grouped(kw) else None)
     Tg, To = _tables(kw, seed=1234)
     x = torch.from_numpy(kb.view(np.int16)).view(torch.bfloat16).to(DEV)
     planes = tq.encode_keys(Tg, x)
@@ -72,15 +78,16 @@ def test_encode_keys_modes_bf16(kw):
 
 
 @pytest.mark.parametrize("kw", [dict(mode="prod", bits=3), dict(mode="mse", bits=4), dict(mode="mse", bits=2),
-                                dict(mode="grouped", bits_outlier=4, bits_normal=2)],
-                         ids=["prod3", "mse4", "mse2", "grouped42"])
+                                dict(mode="grouped", bits_outlier=4, bits_normal=2),
+                                dict(mode="grouped_prod", bits_outlier=3, bits_normal=2)],
+                         ids=["prod3", "mse4", "mse2", "grouped42", "grouped_prod32"])
 @pytest.mark.parametrize("dtype", ["f32", "f16"])
 def test_encode_keys_modes_f32_f16(kw, dtype):
     """The float32 and fp16 input paths (their own unpack and sign steps) in
     the direct-bucketize, hint-grid and grouped encoders."""
     n = 1000  # ragged
     rng = np.random.default_rng(17)
-    scale = W.w5_col_scale() if kw["mode"] == "grouped" else np.ones(128)
+    scale = W.w5_col_scale() if _grouped(kw) else np.ones(128)
     x = (rng.standard_normal((n, 128)) * scale).astype(np.float32 if dtype == "f32" else np.float16)
     Tg, To = _tables(kw, seed=77)
     planes = tq.encode_keys(Tg, torch.from_numpy(x).to(DEV))
@@ -183,9 +190,9 @@ def _oracle_cache(kw, v_bits, B, Hkv, max_ctx, wid=11, seed=42, key_scale=None):
     vhat = O.dequant_values(venc).reshape(B, Hkv, max_ctx, 128)
     planes = dict(idx=torch.from_numpy(rec["idx"]).to(DEV),
                   norm=torch.from_numpy(np.ascontiguousarray(rec["norm"]).view(np.float16)).to(DEV))
-    if kw["mode"] == "prod":
+    if "signs" in rec:
         planes["signs"] = torch.from_numpy(rec["signs"]).to(DEV)
-        planes["rnorm"] = torch.from_numpy(rec["rnorm"]).to(DEV)
+        planes["rnorm"] = torch.from_numpy(np.ascontiguousarray(rec["rnorm"]).view(np.float16)).to(DEV)
     vpl = dict(codes=torch.from_numpy(vrec["codes"]).to(DEV), scale=torch.from_numpy(vrec["scale"]).to(DEV),
                zero=torch.from_numpy(vrec["zero"]).to(DEV))
     return To, planes, vpl, khat, vhat
@@ -237,12 +244,16 @@ DEC_CASES = [
     (dict(mode="grouped", bits_outlier=3, bits_normal=2), 2),
     (dict(mode="grouped", bits_outlier=2, bits_normal=2), 4),
     (dict(mode="grouped", bits_outlier=4, bits_normal=1), 2),
+    # grouped halves with the QJL sketch of the whole residual (three table classes)
+    (dict(mode="grouped_prod", bits_outlier=3, bits_normal=2), 2),
+    (dict(mode="grouped_prod", bits_outlier=3, bits_normal=2), 4),
+    (dict(mode="grouped_prod", bits_outlier=4, bits_normal=1), 4),
 ]
 
 
 @pytest.mark.parametrize("kw,vb", DEC_CASES, ids=lambda x: str(x))
 def test_decode_oracle_packed(kw, vb):
-    key_scale = W.w5_col_scale() if kw["mode"] == "grouped" else None
+    key_scale = W.w5_col_scale() if _grouped(kw) else None
     worst = _run_decode(kw, vb, B=2, Hq=8, Hkv=2, max_ctx=2500, ctx=[2500, 1337], key_scale=key_scale)
     print("worst relative score error", worst)
 
@@ -341,3 +352,63 @@ def test_decode_clamps_out_of_range_lengths():
     torch.cuda.synchronize()
     assert torch.equal(res[0][0], res[1][0]) and torch.equal(res[0][1], res[1][1])
     assert torch.all(res[0][0][1] == 0) and torch.all(torch.isinf(res[0][1][1]))
+
+
+@pytest.mark.parametrize("kw", [dict(mode="mse", bits=4), dict(mode="mse", bits=1), dict(mode="prod", bits=3),
+                                dict(mode="grouped", bits_outlier=4, bits_normal=2),
+                                dict(mode="grouped_prod", bits_outlier=3, bits_normal=2)],
+                         ids=["mse4", "mse1", "prod3", "grouped42", "grouped_prod32"])
+def test_encode_extreme_norms(kw):
+    """Finite bf16 keys of norm about 1e-30 and 1e30 (their fp32 sums of
+    squares would underflow to 0 or overflow to inf), and grouped keys whose
+    halves differ by 60 decades: index and sign bytes as the oracle's; the
+    stored fp16 norms are 0 and +inf, as the oracle's fp16 rounding gives."""
+    n = 48
+    base, _ = W.kv_rows(81, 1, 3 * n)
+    x = base.astype(np.float64) / np.sqrt(128.0)
+    x[:n] *= 1e-30
+    x[n:2 * n] *= 1e30
+    x[2 * n:, :64] *= 1e30
+    x[2 * n:, 64:] *= 1e-30
+    xv, xb = W.to_bf16(x.astype(np.float32))
+    assert np.all(np.isfinite(xv)) and np.all(np.abs(xv[:n]).max(axis=1) > 0)
+    Tg, To = _tables(kw)
+    planes = tq.encode_keys(Tg, torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).to(DEV))
+    torch.cuda.synchronize()
+    f = _gpu_key_fields(Tg, To, planes)
+    P.check_keys(xv.astype(np.float64), To, f)
+    nrm = f["norm16"].astype(np.float64).reshape(3 * n, -1)
+    assert np.all(nrm[:n] == 0) and np.all(np.isposinf(nrm[n:2 * n]))
+
+
+def test_encode_writes_nothing_with_foreign_tables():
+    """Tables built for another configuration (8-bit MSE tables given with a
+    2-bit MSE configuration, whose rows are four times shorter): the key
+    encoder checks the tables' header against the configuration and leaves
+    every plane untouched."""
+    T2 = tq.Tables(L.key_config(mode="mse", bits=2), DEV)
+    T8 = tq.Tables(L.key_config(mode="mse", bits=8), DEV)
+    T2.dev = T8.dev
+    planes = tq.key_planes(T2, 64, DEV)
+    for v in planes.values():
+        v.view(torch.uint8).fill_(0xAB)
+    x = W.normal_bf16_device(5, 1, (64, 128), DEV)
+    tq.encode_keys(T2, x, planes)
+    torch.cuda.synchronize()
+    for v in planes.values():
+        assert torch.all(v.view(torch.uint8) == 0xAB)
+
+
+def test_encode_zero_key_grouped_prod():
+    """A zero key in grouped + QJL mode: both norms and rho 0, each half's
+    y = 0 in the cell above its middle boundary, and every sign bit 1 (the
+    weighted residual is 0, and [0 >= 0])."""
+    kw = dict(mode="grouped_prod", bits_outlier=3, bits_normal=2)
+    Tg, To = _tables(kw)
+    planes = tq.encode_keys(Tg, torch.zeros((16, 128), dtype=torch.bfloat16, device=DEV))
+    torch.cuda.synchronize()
+    f = _gpu_key_fields(Tg, To, planes)
+    assert np.all(f["norm16"] == 0) and np.all(f["rnorm16"] == 0)
+    assert np.all(f["idx"][:, :64] == 4) and np.all(f["idx"][:, 64:] == 2)
+    assert np.all(f["bits"] == 1)
+    P.check_keys(np.zeros((16, 128)), To, f)

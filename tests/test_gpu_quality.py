@@ -3,11 +3,17 @@ synthetic N(0,1) inputs (GQA 8/2, 4096 tokens): more key bits give smaller
 score error, smaller KL and no worse top-k agreement, and more value bits
 give attention outputs closer to the exact ones.  (With N(0,1) queries and
 keys the weights are spread over many tokens, so an output is an average of
-many values and its relative error is larger than a single value's.)"""
+many values and its relative error is larger than a single value's.)
+The same numbers are then checked head by head against the oracle's metrics
+computed in float64 from its own encode of the same inputs."""
+import math
+
 import numpy as np
 import pytest
 
+import oracle.tq_oracle as O
 import tq_workloads as W
+from tests import parity as P
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -45,3 +51,65 @@ def test_value_bits_drive_output_cosine():
     c2 = Q.attention_quality(q, k, v, dict(mode="prod", bits=4), 2)["out_cosine"]
     c4 = Q.attention_quality(q, k, v, dict(mode="prod", bits=4), 4)["out_cosine"]
     assert c4 > c2
+
+
+def _tie(row, k, margin):
+    """Whether the k-th and (k+1)-th largest entries of row are within margin."""
+    top = np.sort(row)[::-1][:k + 1]
+    return top[k - 1] - top[k] < margin
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_quality_matches_oracle_head_by_head(bits):
+    """The GPU's quality numbers against the oracle's (float64 metrics of its
+    own encode of the same bf16 inputs; the difai.kr tutorial's compare.py
+    output items: score cosine, Top-1/5 agreement, KL), per head:
+    score cosine within 2e-3, KL within 5 % (+1e-4), the output within the
+    parity tolerance of the oracle's and its cosine within what that output
+    difference allows,
+    Top-1 and Top-5 agreement equal except where the oracle's exact or
+    compressed scores are tied within 1 % of their RMS at the cut."""
+    B, Hq, Hkv, N = 2, 8, 2, 4096
+    q, k, v = _inputs(B, Hq, Hkv, N)
+    res = Q.attention_quality(q, k, v, dict(mode="prod", bits=bits), 4, per_head=True)
+    g = res["heads"]
+    To = O.build_tables(O.KeyConfig(mode="prod", bits=bits, seed=42))
+    qn, kn, vn = (t.float().cpu().numpy().astype(np.float64) for t in (q, k, v))
+    G = Hq // Hkv
+    err2 = ref2 = 0.0
+    skipped = 0
+    for b in range(B):
+        for h in range(Hkv):
+            heads = slice(h * G, (h + 1) * G)
+            kh = O.dequant_keys(O.encode_keys(kn[b, h], To), To)
+            vh = O.dequant_values(O.encode_values(vn[b, h].astype(np.float32), 4))
+            r = O.attention_quality(qn[b, heads], kn[b, h], vn[b, h], kh, vh, topk=5)
+            s_ex = qn[b, heads] @ kn[b, h].T
+            s_q = qn[b, heads] @ kh.T
+            err2 += r["err2"].sum()
+            ref2 += r["ref2"].sum()
+            for i, hq in enumerate(range(h * G, (h + 1) * G)):
+                assert abs(g["score_cosine"][b, hq] - r["score_cosine"][i]) <= 2e-3
+                # the output cosine moves with the decoded output itself: by at
+                # most 2 ||o - o_ref|| / ||o_ref||, where o is within the output
+                # tolerance of the oracle's p_hat v_hat
+                x = s_q[i] / math.sqrt(128)
+                ph = np.exp(x - x.max())
+                o_ref = (ph / ph.sum()) @ vh
+                o = g["out"][b, hq].astype(np.float64)
+                P.check_out(o, o_ref)
+                bound = 2 * np.linalg.norm(o - o_ref) / np.linalg.norm(o_ref) + 1e-6
+                assert abs(g["out_cosine"][b, hq] - r["out_cosine"][i]) <= bound
+                assert abs(g["kl"][b, hq] - r["kl"][i]) <= 0.05 * r["kl"][i] + 1e-4, (g["kl"][b, hq], r["kl"][i])
+                m_ex = 1e-2 * np.sqrt(np.mean(s_ex[i] ** 2))
+                m_q = 1e-2 * np.sqrt(np.mean(s_q[i] ** 2))
+                if _tie(s_ex[i], 1, m_ex) or _tie(s_q[i], 1, m_q):
+                    skipped += 1
+                else:
+                    assert g["top1"][b, hq] == r["top1"][i]
+                if not (_tie(s_ex[i], 5, m_ex) or _tie(s_q[i], 5, m_q)):
+                    assert abs(g["topk_overlap"][b, hq] - r["topk_overlap"][i]) < 1e-6
+    rel_oracle = math.sqrt(err2 / ref2)
+    print("bits %d: score rel RMS gpu %.5f oracle %.5f; top-1 near ties %d" % (bits, res["score_rel_rms"],
+                                                                               rel_oracle, skipped))
+    assert abs(res["score_rel_rms"] / rel_oracle - 1) < 0.02

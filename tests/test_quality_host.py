@@ -6,7 +6,8 @@ import oracle.tq_oracle as O
 q = pytest.importorskip("kv_cache_quantization_encode_amd.quality")
 
 
-@pytest.mark.parametrize("mode,bits", [("prod", 3), ("prod", 4), ("mse", 4), ("mse", 8), ("grouped", None)])
+@pytest.mark.parametrize("mode,bits", [("prod", 3), ("prod", 4), ("mse", 4), ("mse", 8), ("grouped", None),
+                                       ("grouped_prod", None)])
 def test_key_record_bytes_match_the_oracle(mode, bits):
     cfg = O.KeyConfig(mode=mode, bits=bits or 3, bits_outlier=4, bits_normal=2)
     assert q.key_record_bytes(mode, bits or 3) == O.record_bytes(cfg)
