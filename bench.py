@@ -21,8 +21,11 @@ Also reported (measured outside the timed steps): bulk encode throughput of
 the same cache (4,194,304 keys and values) and of the 28-layer MSE prefill
 workload (1,835,008 bf16 keys at 4 and 8 bits); the decode-call time of the
 128k-context needle workload (prod 4-bit keys, 4-bit values) and of the 16k
-grouped workload (4/2-bit grouped keys, 4-bit values); and the CPU oracle's
-decode throughput on a bounded sample on the host cores.
+grouped workload (4/2-bit grouped keys, 4-bit values), with the needle
+workload's top-5 score recall against exact float32 attention and the ranks
+of its planted needles; the bandwidth of a plain device copy (the practical
+HBM ceiling); and the CPU oracle's decode throughput on a bounded sample on
+the host cores.
 """
 import argparse
 import hashlib
@@ -60,12 +63,13 @@ def parse():
     ap.add_argument("--profile-encode", type=int, default=0,
                     help="only run this many bulk key and value encodes of the cache (rocprofv3 runs)")
     ap.add_argument("--profile-copy", type=int, default=0,
-                    help="with --profile-decode: also run five float32 negations of this many MiB "
-                         "(a plain streaming kernel of known size that calibrates HBM counters)")
+                    help="with --profile-decode or --profile-encode: also run five float32 negations of "
+                         "this many MiB (a plain streaming kernel of known size that calibrates HBM counters)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="no GPU work: turn two rocprofv3 --pmc counter_collection.csv files "
-                         "(FETCH_SIZE, WRITE_SIZE) of a --profile-decode --profile-copy run into "
-                         "profiles/decode_gqa32k_traffic.json")
+                         "(FETCH_SIZE, WRITE_SIZE) of a --profile-decode (or --profile-encode) "
+                         "--profile-copy run into profiles/decode_gqa32k_traffic.json (or "
+                         "profiles/encode_gqa32k_traffic.json)")
     return ap.parse_args()
 
 
@@ -100,7 +104,8 @@ def _pmc_means(path, counter):
                 continue
             name = r["Kernel_Name"]
             fam = ("decode" if "decode_kernel" in name else "merge" if "merge_kernel" in name
-                   else "copy" if "neg_kernel" in name else None)
+                   else "copy" if "neg_kernel" in name else "encode_keys" if "encode_keys_kernel" in name
+                   else "encode_values" if "encode_values_kernel" in name else None)
             if fam is None:
                 continue
             key = (fam, r["Dispatch_Id"])
@@ -121,6 +126,8 @@ def write_traffic(fetch_csv, write_csv, copy_mib):
     copy_bytes = copy_mib * 1024 * 1024
     f_scale = copy_bytes / (fetch["copy"] * 1024.0)
     w_scale = copy_bytes / (write["copy"] * 1024.0)
+    if "decode" not in fetch:
+        return write_encode_traffic(fetch, write, nf, nw, copy_bytes, f_scale, w_scale)
     rd = (fetch["decode"] + fetch.get("merge", 0.0)) * 1024.0 * f_scale
     wr = (write["decode"] + write.get("merge", 0.0)) * 1024.0 * w_scale
     src = os.path.join(ROOT, "kv_cache_quantization_encode_amd", "csrc", "tq_decode.hip")
@@ -134,6 +141,28 @@ def write_traffic(fetch_csv, write_csv, copy_mib):
            "algorithmic_bytes": DECODE_BYTES,
            "traffic_over_algorithmic": (rd + wr) / DECODE_BYTES}
     p = os.path.join(ROOT, "profiles", "decode_gqa32k_traffic.json")
+    with open(p, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec, indent=1))
+
+
+def write_encode_traffic(fetch, write, nf, nw, copy_bytes, f_scale, w_scale):
+    """HBM traffic of the bulk encode of the 32k GQA cache (4,194,304 keys,
+    then as many value rows) from a --profile-encode --profile-copy run."""
+    n = B * HKV * CTX
+    src = os.path.join(ROOT, "kv_cache_quantization_encode_amd", "csrc", "tq_encode.hip")
+    rec = {"source_sha256_16": source_hash(src), "workload": "gqa-decode-32k cache encode",
+           "copy_bytes": copy_bytes, "fetch_scale": f_scale, "write_scale": w_scale}
+    for fam, algo in (("encode_keys", n * (2 * D + KEY_BYTES)), ("encode_values", n * (2 * D + VAL_BYTES))):
+        rd = fetch[fam] * 1024.0 * f_scale
+        wr = write[fam] * 1024.0 * w_scale
+        rec[fam] = {"fetch_kib_per_dispatch": fetch[fam], "write_kib_per_dispatch": write[fam],
+                    "dispatches": {"fetch": nf[fam], "write": nw[fam]},
+                    "read_bytes_per_launch": rd, "write_bytes_per_launch": wr,
+                    "traffic_bytes_per_launch": rd + wr, "algorithmic_bytes": algo,
+                    "traffic_over_algorithmic": (rd + wr) / algo}
+    p = os.path.join(ROOT, "profiles", "encode_gqa32k_traffic.json")
     with open(p, "w") as f:
         json.dump(rec, f, indent=1)
         f.write("\n")
@@ -221,13 +250,7 @@ def main():
         print("profiled %d decode calls" % args.profile_decode, flush=True)
         if args.profile_copy:
             del keys, vals
-            n = args.profile_copy * 1024 * 1024 // 4
-            src = torch.ones(n, dtype=torch.float32, device=dev)
-            dst = torch.empty_like(src)
-            for _ in range(5):
-                torch.neg(src, out=dst)
-            torch.cuda.synchronize()
-            print("profiled 5 copies of %d MiB" % args.profile_copy, flush=True)
+            profile_copies(args.profile_copy, dev)
         return
     if args.profile_encode:
         for _ in range(args.profile_encode):
@@ -235,6 +258,8 @@ def main():
             tq.encode_values(vals, 2, planes=vp)
         torch.cuda.synchronize()
         print("profiled %d bulk encodes of %d keys and values" % (args.profile_encode, n_rec), flush=True)
+        if args.profile_copy:
+            profile_copies(args.profile_copy, dev)
         return
 
     def step(i, ev=None):
@@ -284,6 +309,7 @@ def main():
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(args.cpu_groups)
     traffic = traffic_from_profile()
+    copy_gbps = copy_bandwidth()
     line = {
         "metric": "decode-attn KV tokens/s & HBM GB/s (% of peak); encode keys/s",
         "value": value,
@@ -295,7 +321,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "u16 lookup tables + fp16 softmax weights, f32 accumulate",
         "data": "synthetic",
         "config": {"workload": "gqa-decode-32k", "sequences": B, "kv_heads": HKV, "q_heads": HQ,
                    "head_dim": D, "context": CTX, "keys": "prod 3-bit (2-bit index + QJL)",
@@ -304,11 +330,47 @@ def main():
                      "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic,
                      "kernel": "tq_decode_attention (decode_kernel + merge_kernel)",
                      "algorithmic_bytes": DECODE_BYTES, "ms_mean": dec_ms_mean,
-                     "ms_median": dec_ms_median},
+                     "ms_median": dec_ms_median,
+                     "achievable_copy_gbps": copy_gbps, "frac_of_copy": achieved / copy_gbps},
         "cpu_baseline": cpu,
     }
     line.update(extra)
     print(json.dumps(line))
+
+
+def profile_copies(mib, dev):
+    """Five float32 negations of `mib` MiB: the counter calibration kernel."""
+    import torch
+    n = mib * 1024 * 1024 // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print("profiled 5 copies of %d MiB" % mib, flush=True)
+
+
+def copy_bandwidth(mib=2048, reps=20):
+    """HBM bandwidth a plain device-to-device copy reaches (read + write
+    bytes over time; torch's copy kernel, 2 GiB, settled clocks): the
+    practical ceiling next to the 8 TB/s specification."""
+    import torch
+    n = mib * 1024 * 1024 // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < 0.2:
+        dst.copy_(src)
+        torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del src, dst
+    return 2.0 * n * 4 / (ms * 1e-3) / 1e9
 
 
 def encode_bench(tq, W, T, keys, vals, dev, reps=10):
@@ -366,6 +428,7 @@ def other_decodes(tq, W, dev, reps=50):
     import torch
 
     res = {}
+    G = HQ // HKV
     cases = [("decode_needle128k", dict(mode="prod", bits=4), 1, 131072, 4, None, 4, 164),
              ("decode_grouped16k", dict(mode="grouped", bits_outlier=4, bits_normal=2), 8, 16384, 4,
               W.w5_col_scale(), 5, 132)]
@@ -373,12 +436,20 @@ def other_decodes(tq, W, dev, reps=50):
         T = tq.Tables(tq.key_config(seed=42, **kw), dev)
         n = b * HKV * ctx
         keys = W.normal_bf16_device(wid, 1, (n, D), dev, scale_cols=scale)
+        q = W.normal_bf16_device(wid, 3, (1, b, HQ, D), dev)[0].contiguous()
+        needles = name == "decode_needle128k"
+        if needles:
+            # five needles per KV head at the pages' depths, along the first
+            # query head of the group (4 x its unit direction + N(0, 0.1^2))
+            nv, _ = W.w4_needles(q.float().cpu().numpy(), HKV, HQ)
+            pos = W.needle_positions(ctx)
+            for h in range(HKV):
+                for i, p in enumerate(pos):
+                    keys[h * ctx + p] = torch.from_numpy(nv[h, i]).to(dev).to(torch.bfloat16)
         kp = tq.encode_keys(T, keys)
-        del keys
         vals = W.normal_bf16_device(wid, 2, (n, D), dev)
         vp = tq.encode_values(vals, vbits)
         del vals
-        q = W.normal_bf16_device(wid, 3, (1, b, HQ, D), dev)[0].contiguous()
         ctx_len = torch.full((b,), ctx, dtype=torch.int32, device=dev)
         dec = tq.Decoder(T, b, HQ, HKV, ctx, vbits, torch.bfloat16, dev)
         out = torch.empty((b, HQ, D), dtype=torch.float32, device=dev)
@@ -398,7 +469,28 @@ def other_decodes(tq, W, dev, reps=50):
         res[name] = {"token_heads": n, "algorithmic_bytes": nbytes, "ms": ms,
                      "kv_tokens_per_s": b * ctx / (ms * 1e-3), "gbps": nbytes / (ms * 1e-3) / 1e9,
                      "frac_of_hbm_peak": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS}
-        del kp, vp, dec
+        if needles:
+            # top-5 recall of the decoded scores against exact float32 q.k over
+            # the original keys, and the needles' ranks (one decode call with
+            # scores, outside the timing)
+            scores = torch.empty((b, HQ, ctx), dtype=torch.float32, device=dev)
+            dec(q, ctx_len, kp, vp, out=out, scores=scores)
+            kf = keys.view(HKV, ctx, D).float()
+            rec, ranks = [], []
+            for hq in range(HQ):
+                h = hq // G
+                exact = kf[h] @ q[0, hq].float()
+                te = set(torch.topk(exact, 5).indices.tolist())
+                tg = set(torch.topk(scores[0, hq], 5).indices.tolist())
+                rec.append(len(te & tg) / 5.0)
+                if hq % G == 0:
+                    order = torch.argsort(scores[0, hq], descending=True)
+                    rank = torch.empty_like(order)
+                    rank[order] = torch.arange(ctx, device=dev)
+                    ranks.append([int(rank[p]) for p in pos])
+            res[name].update(recall_at_5=sum(rec) / len(rec), needle_ranks=ranks, needles_per_kv_head=len(pos))
+            del kf, scores
+        del kp, vp, dec, keys
     return res
 
 

@@ -344,7 +344,19 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
   constexpr int VROW = KD * VB / 8;  // bytes of a value-code row
   const bool scorer = wave < NS;
   const int pw = scorer ? wave : wave - NS;
-  const int slot = lane >> 4, u = lane & 15, grp = u >> 2;
+  // p.V lanes: a lane takes CH channels (CB code bytes per token: 16
+  // channels at 2 bits, one dword; else 8), u = lane % NSL of the NSL
+  // slices, and the token pairs slot + NSLOT k of a tile, slot = lane / NSL
+#ifndef TQ_PV_CH2
+#define TQ_PV_CH2 16
+#endif
+  // (16 channels only for key formats of at most 48 bytes: with more key
+  // words the score waves' registers and the p.V waves' 64 sums do not fit
+  // in 128 VGPRs together)
+  constexpr int CH = VB == 2 && F::KWORDS <= 12 ? TQ_PV_CH2 : 8, CB = CH * VB / 8, NSL = KD / CH, NSLOT = 64 / NSL;
+  constexpr int NPAIR = TILE / 2 / NSLOT;  // token pairs of a lane per tile
+  constexpr int NCODE = 2 * NPAIR;         // code dwords of a lane per tile
+  const int slot = lane / NSL, u = lane % NSL, grp = u * CH / 32;
   const int n_tiles = t_end > t_begin ? (t_end - t_begin + TILE - 1) / TILE : 0;
   const int rounds = (n_tiles + NS - 1) / NS;
   auto tile_tb = [&](int r) { return t_begin + (r * NS + pw) * TILE; };
@@ -393,22 +405,23 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
     d.zv = *(const uint2*)(a.vzero + rec * 4);
     d.sv = *(const uint2*)(a.vscale + rec * 4);
   };
-  // value codes of this lane's token pairs (slot + 4k): [2k] even token, [2k+1] odd token
+  // value codes of this lane's token pairs (slot + NSLOT k): c[2k] the
+  // pair's even token, c[2k + 1] its odd one
   auto load_codes = [&](int tb, uint32_t* c) {
     const long long tbase = tile_base(tb);
     if (tb + TILE <= t_end) {  // whole tile: one base address, immediate offsets
-      const uint8_t* base = a.vcodes + (tbase + tb + 2 * slot) * VROW + VB * u;
+      const uint8_t* base = a.vcodes + (tbase + tb + 2 * slot) * VROW + CB * u;
 #pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        const uint8_t* pa = base + ((k >> 1) * 8 + (k & 1)) * VROW;
-        c[k] = VB == 2 ? (uint32_t) * (const uint16_t*)pa : *(const uint32_t*)pa;
+      for (int k = 0; k < NCODE; ++k) {
+        const uint8_t* pa = base + ((k >> 1) * 2 * NSLOT + (k & 1)) * VROW;
+        c[k] = CB == 2 ? (uint32_t) * (const uint16_t*)pa : *(const uint32_t*)pa;
       }
     } else {
 #pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        const int t = min(tb + 2 * slot + (k >> 1) * 8 + (k & 1), t_last);
-        const uint8_t* pa = a.vcodes + (tbase + t) * VROW + VB * u;
-        c[k] = VB == 2 ? (uint32_t) * (const uint16_t*)pa : *(const uint32_t*)pa;
+      for (int k = 0; k < NCODE; ++k) {
+        const int t = min(tb + 2 * slot + (k >> 1) * 2 * NSLOT + (k & 1), t_last);
+        const uint8_t* pa = a.vcodes + (tbase + t) * VROW + CB * u;
+        c[k] = CB == 2 ? (uint32_t) * (const uint16_t*)pa : *(const uint32_t*)pa;
       }
     }
   };
@@ -524,7 +537,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   lds_barrier();
   KeyData kd;
-  uint32_t codes[16];
+  uint32_t codes[NCODE];
   if (n_tiles > 0) {
     if (scorer) load_keys(tile_tb(0), kd);
     else load_codes(tile_tb(0), codes);
@@ -876,14 +889,14 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
     }
     if (lane == 0) L.ksf[pw] = ks;
   } else {
-    float acc[QH][8];
+    float acc[QH][CH];
 #pragma unroll
     for (int hh = 0; hh < QH; ++hh)
 #pragma unroll
-      for (int k = 0; k < 8; ++k) acc[hh][k] = 0.0f;
+      for (int k = 0; k < CH; ++k) acc[hh][k] = 0.0f;
     // two code buffers in turn: round r consumes tile r - 1 while the codes
     // of tile r arrive in the other
-    uint32_t codes2[16];
+    uint32_t codes2[NCODE];
     auto pv_round = [&](int r, const uint32_t* cur, uint32_t* nxt) {
       const int tb = r >= 1 ? tile_tb(r - 1) : t_end;
       if (tb < t_end) {
@@ -895,29 +908,29 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
 #pragma unroll
           for (int hh = 0; hh < QH; ++hh)
 #pragma unroll
-            for (int k = 0; k < 8; ++k) acc[hh][k] *= alv[hh];
+            for (int k = 0; k < CH; ++k) acc[hh][k] *= alv[hh];
         }
-        // ---------------- p.V: lane = (slot, 8-dim slice u); slot takes token pairs slot + 4k
+        // ---------------- p.V: lane = (slot, CH-channel slice u)
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const int pr = slot + 4 * k;
-          const uint32_t cA = cur[2 * k], cB = cur[2 * k + 1];
+        for (int k = 0; k < NPAIR; ++k) {
+          const int pr = slot + NSLOT * k;
           const uint4 wv = *(const uint4*)(wsrc + grp * WGRP + pr * QH);
           const uint32_t wh[QH] = {wv.x, wv.y, wv.z, wv.w};
           // pairs[i] holds, for the two tokens (low and high half), the
           // prefix of channel i: the channels of its byte up to i, so that
           // one byte permute serves a whole byte and the last prefix of each
           // byte needs no mask.  The channel sums are told apart at the end.
-          uint32_t pairs[8];
-          if (VB == 2) {
-            const uint32_t Y1 = __builtin_amdgcn_perm(cB, cA, 0x0c040c00u);  // byte 0 of A, of B -> bytes 0, 2
-            const uint32_t Y2 = __builtin_amdgcn_perm(cB, cA, 0x0c050c01u);  // byte 1 of A, of B -> bytes 0, 2
-            pairs[0] = Y1 & 0x00030003u; pairs[1] = Y1 & 0x000F000Fu; pairs[2] = Y1 & 0x003F003Fu; pairs[3] = Y1;
-            pairs[4] = Y2 & 0x00030003u; pairs[5] = Y2 & 0x000F000Fu; pairs[6] = Y2 & 0x003F003Fu; pairs[7] = Y2;
-          } else {
+          uint32_t pairs[CH];
+          const uint32_t cA = cur[2 * k], cB = cur[2 * k + 1];
 #pragma unroll
-            for (int bb = 0; bb < 4; ++bb) {  // byte bb of A and of B -> bytes 0, 2
-              const uint32_t Yb = __builtin_amdgcn_perm(cB, cA, 0x0c000c00u | ((4u + bb) << 16) | (uint32_t)bb);
+          for (int bb = 0; bb < CB; ++bb) {  // byte bb of A and of B -> bytes 0, 2
+            const uint32_t Yb = __builtin_amdgcn_perm(cB, cA, 0x0c000c00u | ((4u + bb) << 16) | (uint32_t)bb);
+            if constexpr (VB == 2) {
+              pairs[4 * bb + 0] = Yb & 0x00030003u;
+              pairs[4 * bb + 1] = Yb & 0x000F000Fu;
+              pairs[4 * bb + 2] = Yb & 0x003F003Fu;
+              pairs[4 * bb + 3] = Yb;
+            } else {
               pairs[2 * bb] = Yb & 0x000F000Fu;
               pairs[2 * bb + 1] = Yb;
             }
@@ -926,7 +939,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
           for (int hh = 0; hh < QH; ++hh) {
             const half2_t w2 = __builtin_bit_cast(half2_t, wh[hh]);
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
+            for (int i = 0; i < CH; ++i)
               acc[hh][i] = __builtin_amdgcn_fdot2(w2, __builtin_bit_cast(half2_t, pairs[i]), acc[hh][i], false);
           }
         }
@@ -946,18 +959,20 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
     // of consecutive prefixes over its place value.
 #pragma unroll
     for (int hh = 0; hh < QH; ++hh) {
-      float r[8];
+      float r[CH];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        r[i] = sum_xor32(sum_xor16(acc[hh][i]));
+      for (int i = 0; i < CH; ++i) {  // over the slots (lane bits above the slice)
+        float v = acc[hh][i];
+        if constexpr (NSL == 8) v += lane_xor<8>(v, lane);
+        r[i] = sum_xor32(sum_xor16(v));
       }
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int i = 0; i < CH; ++i) {
         constexpr int PER = 8 / VB;  // channels per byte
         const int f = i % PER;       // field within the byte
         const float step = (float)(1 << (VB * f));
         const float v = f == 0 ? r[i] : r[i] - r[i - 1];
-        if (lane < 16) mine[hh * RS + 6 + 8 * u + i] = v * (16777216.0f / step);
+        if (lane < NSL) mine[hh * RS + 6 + CH * u + i] = v * (16777216.0f / step);
       }
     }
   }

@@ -24,6 +24,15 @@
 // exactly the operand layout v_mfma_f32_16x16x32_f16 wants for B = R^T
 // (lane l: column l & 15, eight consecutive k per lane group), and a
 // contiguous run of packed index bytes.
+//
+// That is the float32 path.  For bf16 and fp16 keys the loaded words are
+// already MFMA operands: register group c of lane (key n, g) holds the eight
+// coordinates 32c + 8g .. + 7, the B layout of v_mfma_f32_16x16x32_{bf16,f16}
+// for a K step over the 32 coordinates of block c.  The transform's five
+// stages on coordinate bits 0-4 then run as one such MFMA per block and
+// output half, against a +-1 matrix that also holds sigma (exact products,
+// fp32 sums); the stages on bits 5 and 6 stay in the lane.  Afterwards
+// x[8c + j] is coordinate 32c + 8g + j: four runs of eight.
 #include <hip/hip_runtime.h>
 #include <hip/hip_fp16.h>
 
@@ -38,6 +47,7 @@ namespace {
 __device__ inline int index_width_dev(int bits) { return bits == 1 ? 1 : bits == 2 ? 2 : bits <= 4 ? 4 : 8; }
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 constexpr int KD = 128;        // head dimension of the kernels
@@ -205,6 +215,34 @@ __device__ inline void store_idx(int w, uint8_t* dst, const int* q) {
     case 4: store_fields<4>(dst, q); break;
     default: store_fields<8>(dst, q); break;
   }
+}
+
+// Pack 8 indices of width w (eight consecutive coordinates) and store their
+// w bytes at dst (w-byte aligned).
+__device__ __forceinline__ void store_run(int w, uint8_t* dst, const int* q) {
+  if (w == 8) {
+    uint2 v;
+    v.x = (uint32_t)q[0] | ((uint32_t)q[1] << 8) | ((uint32_t)q[2] << 16) | ((uint32_t)q[3] << 24);
+    v.y = (uint32_t)q[4] | ((uint32_t)q[5] << 8) | ((uint32_t)q[6] << 16) | ((uint32_t)q[7] << 24);
+    *(uint2*)dst = v;
+    return;
+  }
+  uint32_t v = 0;
+#pragma unroll
+  for (int r = 0; r < 8; ++r) v |= (uint32_t)q[r] << (w * r);
+  if (w == 4) *(uint32_t*)dst = v;
+  else if (w == 2) *(uint16_t*)dst = (uint16_t)v;
+  else *dst = (uint8_t)v;
+}
+
+// The MFMA transform's fixed operand for block c and output half mt (see the
+// header): row m of the 16 x 32 A fragment is output coordinate
+// 8 (m / 4) + 4 mt + m % 4 of the block, column k input coordinate k, entry
+// (-1)^popcount(row & k) times sigma of input 32c + k, as bf16 or fp16 bits.
+__device__ inline uint16_t hadamard_entry(int mt, int m, int k, float sigma, bool bf16) {
+  const int row = 8 * (m >> 2) + 4 * mt + (m & 3);
+  const bool neg = (__popc(row & k) & 1) != (sigma < 0.0f);
+  return bf16 ? (neg ? 0xBF80u : 0x3F80u) : (neg ? 0xBC00u : 0x3C00u);
 }
 
 // ---------------------------------------------------------------- values
@@ -430,12 +468,16 @@ __global__ __launch_bounds__(WAVES * 64, key_waves_per_simd(MODE, DT)) void enco
   constexpr int NP = GRP ? 2 : 1;
   // tables of another configuration: nothing is written (uniform per block)
   if (H->magic != TQ_BLOB_MAGIC || H->d != KD || H->mode != MODE || H->n_parts != NP ||
-      H->part_bits[0] != a.bits0 || (NP == 2 && H->part_bits[1] != a.bits1) || H->m != a.m)
+      H->part_bits[0] != a.bits0 || (NP == 2 && H->part_bits[1] != a.bits1) || H->m != a.m ||
+      H->hint_n[0] > TQ_MAX_HINT || (NP == 2 && H->hint_n[1] > TQ_MAX_HINT))
     return;
   __shared__ __align__(16) tq_hint s_hint[NP][TQ_MAX_HINT];
   __shared__ float s_cent[QJL ? NP * MAX_LEVELS : 1];
   constexpr int SPITCH = KD + 8;  // halves per padded row of S
   __shared__ __align__(16) _Float16 s_S[QJL ? KD * SPITCH : 8];
+  constexpr bool MF = DT != TQ_F32;  // transform bits 0-4 on MFMA (16-bit inputs)
+  // A fragments of the transform: [block c][half mt][lane][8]
+  __shared__ __align__(16) uint16_t s_H[MF ? 4 * 2 * 64 * 8 : 8];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -490,12 +532,11 @@ __global__ __launch_bounds__(WAVES * 64, key_waves_per_simd(MODE, DT)) void enco
     if (!direct) {
       const uint4* src = (const uint4*)(a.tables + H->off_hint[p]);
       constexpr int PER_THREAD = TQ_MAX_HINT / (WAVES * 64);
+      // (unconditional reads of clamped entries keep hv in registers)
+      const int last = max(hn[p], 1) - 1;
       uint4 hv[PER_THREAD];
 #pragma unroll
-      for (int k = 0; k < PER_THREAD; ++k) {
-        const int i = threadIdx.x + k * WAVES * 64;
-        if (i < hn[p]) hv[k] = src[i];
-      }
+      for (int k = 0; k < PER_THREAD; ++k) hv[k] = src[min((int)threadIdx.x + k * WAVES * 64, last)];
 #pragma unroll
       for (int k = 0; k < PER_THREAD; ++k) {
         const int i = threadIdx.x + k * WAVES * 64;
@@ -510,8 +551,9 @@ __global__ __launch_bounds__(WAVES * 64, key_waves_per_simd(MODE, DT)) void enco
     }
     // S in LDS, rows padded to 136 halves so that the sixteen rows one MFMA
     // fragment read touches fall in distinct banks.  Fragment (nt, ks) of lane
-    // (kk, g): row 16 nt + kk, coordinates 32 g + 8 ks .. + 7, matching the
-    // B = R^T layout after the transform.
+    // (kk, g): row 16 nt + kk, coordinates 32 g + 8 ks .. + 7 (float32 path)
+    // or 32 ks + 8 g .. + 7 (MFMA path), matching the B = R^T layout after
+    // the transform.
     // (all of a thread's reads are issued before its LDS writes)
     const uint4* S = (const uint4*)(a.tables + H->off_S);
     constexpr int PER_THREAD = KD * KD / 8 / (WAVES * 64);
@@ -522,6 +564,16 @@ __global__ __launch_bounds__(WAVES * 64, key_waves_per_simd(MODE, DT)) void enco
     for (int k = 0; k < PER_THREAD; ++k) {
       const int i = threadIdx.x + k * WAVES * 64;
       *(uint4*)(s_S + (i / (KD / 8)) * SPITCH + 8 * (i % (KD / 8))) = srow[k];
+    }
+  }
+  if constexpr (MF) {
+    for (int i = threadIdx.x; i < 4 * 2 * 64 * 8; i += blockDim.x) {
+      const int c = i >> 10, mt = (i >> 9) & 1, ln = (i >> 3) & 63, e = i & 7;
+      const int k = 8 * (ln >> 4) + e;
+      const int part = GRP ? c >> 1 : 0;
+      const int j = GRP ? 32 * (c & 1) + k : 32 * c + k;  // coordinate within the part
+      const float sv = ((const float*)(a.tables + H->off_sigma[part]))[j];
+      s_H[i] = hadamard_entry(mt, ln & 15, k, sv, DT == TQ_BF16);
     }
   }
   // sign mask: bit r set when sigma of the coordinate loaded into x[r] is -1
@@ -545,9 +597,38 @@ __global__ __launch_bounds__(WAVES * 64, key_waves_per_simd(MODE, DT)) void enco
     const bool valid = row < a.n_vec;
     const long long slot = a.slots ? a.slots[row_of(tile)] : row;
     float x[32];
-    unpack_raw<DT>(raw, sigmask, x);
-    raw = raw_next;
-    // squared norm per part (part = register bit 4 in this layout)
+    if constexpr (MF) {
+      // coordinate bits 0-4 of each block c by MFMA (see the header): the
+      // loaded words of block c are the B operand, fragment (c, mt) of the
+      // +-1 matrix with sigma the A operand; output half mt of block c lands
+      // in x[8c + 4mt .. + 3] as coordinates 32c + 8g + 4mt .. + 3
+      const uint4* hfr = (const uint4*)s_H + lane;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+          const uint4 af = hfr[(2 * c + mt) * 64];
+          floatx4 d;
+          if constexpr (DT == TQ_BF16)
+            d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, af),
+                                                        __builtin_bit_cast(bf16x8, raw.v[c]),
+                                                        floatx4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+          else
+            d = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, af), __builtin_bit_cast(half8, raw.v[c]),
+                                                       floatx4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) x[8 * c + 4 * mt + i] = d[i];
+        }
+      }
+      raw = raw_next;
+      stage_in_lane<8>(x);              // coordinate bit 5
+      if (!GRP) stage_in_lane<16>(x);   // coordinate bit 6
+    } else {
+      unpack_raw<DT>(raw, sigmask, x);
+      raw = raw_next;
+    }
+    // squared norm per part (part = register bit 4 in both layouts); after the
+    // MFMA transform the sums are of y = H (sigma k), PD times those of k
     float ss0 = 0.0f, ss1 = 0.0f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -596,25 +677,29 @@ __global__ __launch_bounds__(WAVES * 64, key_waves_per_simd(MODE, DT)) void enco
       }
     }
 
-    stage_in_lane<1>(x);
-    stage_in_lane<2>(x);
-    stage_in_lane<4>(x);
-    stage_in_lane<8>(x);
-    if (!GRP) stage_in_lane<16>(x);
-    stage_cross16(x);
-    stage_cross32(x);
-
-    // now x[r] is coordinate 32g + r
+    if constexpr (!MF) {
+      stage_in_lane<1>(x);
+      stage_in_lane<2>(x);
+      stage_in_lane<4>(x);
+      stage_in_lane<8>(x);
+      if (!GRP) stage_in_lane<16>(x);
+      stage_cross16(x);
+      stage_cross32(x);
+      // now x[r] is coordinate 32g + r
+    }
+    // (1/PD is a power of two: the sums scale exactly)
+    constexpr float INV_PD = MF ? (GRP ? 1.0f / 64.0f : 1.0f / 128.0f) : 1.0f;
     float n_part[2];
     if (GRP) {
-      n_part[0] = sqrtf(ss0) * nsc0;
-      n_part[1] = sqrtf(ss1) * nsc1;
+      n_part[0] = sqrtf(ss0 * INV_PD) * nsc0;
+      n_part[1] = sqrtf(ss1 * INV_PD) * nsc1;
     } else {
-      n_part[0] = n_part[1] = sqrtf(ss0 + ss1) * nsc0;
+      n_part[0] = n_part[1] = sqrtf((ss0 + ss1) * INV_PD) * nsc0;
     }
-    const int part = GRP ? (g >> 1) : 0;
-    const float n = n_part[part];
-    const float inv = n > 0.0f ? 1.0f / n : 0.0f;
+    // the part of register r: lane group (float32 layout) or register bit 4
+    auto part_of = [&](int r) { return GRP ? (MF ? (r >> 4) : (g >> 1)) : 0; };
+    const float inv_p[2] = {n_part[0] > 0.0f ? 1.0f / n_part[0] : 0.0f, n_part[1] > 0.0f ? 1.0f / n_part[1] : 0.0f};
+    const float n = n_part[0], inv = inv_p[0];  // single-part modes
     // x stays unscaled (y = x / n = x * inv where needed)
     int q[32];
     if (direct2) {
@@ -628,15 +713,12 @@ __global__ __launch_bounds__(WAVES * 64, key_waves_per_simd(MODE, DT)) void enco
 #pragma unroll
       for (int r = 0; r < 32; ++r) q[r] = (int)__builtin_amdgcn_fmed3f(fmaf(x[r], un, ub), 0.0f, utop);
     } else {
-      const tq_hint* hint = s_hint[NP == 2 ? part : 0];
-      const int hnn = NP == 2 ? hn[part] : hn[0];
-      const float hl = NP == 2 ? hlo[part] : hlo[0];
-      const float hs = NP == 2 ? hsc[part] : hsc[0];
 #pragma unroll
       for (int r = 0; r < 32; ++r) {
         // eight hint reads in flight at a time (each holds three registers)
         if (r % 8 == 0) __builtin_amdgcn_sched_barrier(0);
-        q[r] = bucketize(x[r] * inv, hint, hnn, hl, hs);
+        const int pr = NP == 2 ? part_of(r) : 0;
+        q[r] = bucketize(x[r] * inv_p[pr], s_hint[pr], hn[pr], hlo[pr], hsc[pr]);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -645,36 +727,50 @@ __global__ __launch_bounds__(WAVES * 64, key_waves_per_simd(MODE, DT)) void enco
 
     if (store) {
       uint8_t* dst = a.idx + slot * a.idx_row_bytes;
-      if (GRP) {
+      if constexpr (MF) {
+        // four runs of eight coordinates, 32c + 8g .. + 7
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int pc = GRP ? c >> 1 : 0;
+          const int w = pc ? w1 : w0;
+          const int cs = GRP ? 32 * (c & 1) + 8 * g : 32 * c + 8 * g;  // first coordinate within the part
+          store_run(w, dst + (pc ? (KD / 2) * w0 / 8 : 0) + cs * w / 8, q + 8 * c);
+        }
+      } else if (GRP) {
+        const int part = g >> 1;
         const int w = part ? w1 : w0;
         const int off = part ? (KD / 2) * w0 / 8 + 32 * (g - 2) * w / 8 : 32 * g * w / 8;
         store_idx(w, dst + off, q);
-        if (g == 0) {
+      } else {
+        store_idx(w0, dst + 32 * g * w0 / 8, q);
+      }
+      if (g == 0) {
+        if (GRP) {
           const uint32_t pk = (uint32_t)__half_as_ushort(__float2half_rn(n_part[0])) |
                               ((uint32_t)__half_as_ushort(__float2half_rn(n_part[1])) << 16);
           *(uint32_t*)(a.norm + 2 * slot) = pk;
+        } else {
+          a.norm[slot] = __half_as_ushort(__float2half_rn(n));
         }
-      } else {
-        store_idx(w0, dst + 32 * g * w0 / 8, q);
-        if (g == 0) a.norm[slot] = __half_as_ushort(__float2half_rn(n));
       }
     }
 
     if constexpr (QJL) {
       // GROUPED_PROD weights each half's residual by n_j / max(n_o, n_n):
       // w / (max / 8), in [0, 1] times the residual's own scale for fp16
-      float wgt = 1.0f, nmax = n;
+      float wgt_p[2] = {1.0f, 1.0f}, nmax = n;
       if constexpr (GRP) {
         nmax = fmaxf(n_part[0], n_part[1]);
-        wgt = nmax > 0.0f ? n / nmax : 0.0f;
+        wgt_p[0] = nmax > 0.0f ? n_part[0] / nmax : 0.0f;
+        wgt_p[1] = nmax > 0.0f ? n_part[1] / nmax : 0.0f;
       }
-      const float* cp = s_cent + (GRP ? part * MAX_LEVELS : 0);
       float rr = 0.0f;
       half8 bhi[4], blo[4];
 #pragma unroll
       for (int r = 0; r < 32; ++r) {
-        float res = fmaf(x[r], inv, -cp[q[r]]);
-        if constexpr (GRP) res *= wgt;
+        const int pr = part_of(r);
+        float res = fmaf(x[r], inv_p[pr], -s_cent[pr * MAX_LEVELS + q[r]]);
+        if constexpr (GRP) res *= wgt_p[pr];
         rr = fmaf(res, res, rr);
         const _Float16 h = (_Float16)res;
         const _Float16 lo = (_Float16)(res - (float)h);
@@ -685,7 +781,9 @@ __global__ __launch_bounds__(WAVES * 64, key_waves_per_simd(MODE, DT)) void enco
       // The fragment offset is made opaque to the compiler each tile, so that it
       // reads S from LDS per use instead of keeping all 32 fragments live (an
       // offset, not a pointer, so the reads stay LDS reads and not flat ones).
-      int soff = kk * SPITCH + 32 * g;
+      // K step ks covers the lane's register group ks: coordinates 32g + 8ks
+      // (float32 layout) or 32ks + 8g (MFMA layout) .. + 7.
+      int soff = kk * SPITCH + (MF ? 8 : 32) * g;
       asm volatile("" : "+v"(soff));
       const _Float16* sbase = s_S + soff;
       floatx4 acc[8];
@@ -694,7 +792,7 @@ __global__ __launch_bounds__(WAVES * 64, key_waves_per_simd(MODE, DT)) void enco
         acc[nt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-          const half8 sf = *(const half8*)(sbase + (16 * nt) * SPITCH + 8 * ks);
+          const half8 sf = *(const half8*)(sbase + (16 * nt) * SPITCH + (MF ? 32 : 8) * ks);
           acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(sf, blo[ks], acc[nt], 0, 0, 0);
           acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(sf, bhi[ks], acc[nt], 0, 0, 0);
         }

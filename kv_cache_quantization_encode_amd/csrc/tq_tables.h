@@ -10,7 +10,7 @@
 #define TQ_BLOB_VERSION 1u
 #define TQ_BLOB_ALIGN 256u
 #define TQ_MAX_PARTS 2
-#define TQ_MAX_HINT 1024 /* bins of a bucketize hint grid (the 8-bit codebook needs 512) */
+#define TQ_MAX_HINT 512 /* bins of a bucketize hint grid (the 8-bit codebook needs 512, the others 16-256) */
 
 // One "part" is a group of channels quantised with its own norm, rotation and
 // codebook: the whole key for MSE/PROD, each half for GROUPED.

@@ -59,7 +59,8 @@ def _overwrite(kp, vp, rows, rec, vrec):
 
 def _full_decode_case(kw, v_bits, B, Hkv, Hq, ctx, keys, vals, q, q_vals, samples, label):
     """keys/vals: [B*Hkv*ctx, D] bf16 device tensors; q: [B, Hq, D] bf16.
-    Returns GPU scores of the GPU-encoded cache (for quality metrics)."""
+    Returns GPU scores of the GPU-encoded cache (for quality metrics) and the
+    oracle's scores of the sampled groups ({(b, h): [G, ctx]})."""
     seed = 42
     Tg = tq.Tables(L.key_config(seed=seed, **kw), DEV)
     To = O.build_tables(O.KeyConfig(d=D, seed=seed, mode=kw["mode"], bits=kw.get("bits", 3),
@@ -106,7 +107,7 @@ def _full_decode_case(kw, v_bits, B, Hkv, Hq, ctx, keys, vals, q, q_vals, sample
         assert np.all(np.abs(lse[b, heads] - lse_ref) <= 5e-3 * np.maximum(1.0, np.abs(lse_ref)))
     print("%s: worst relative score error %.3g over %d sampled groups" % (label, worst, len(refs)), flush=True)
     del kp, vp
-    return scores_e2e
+    return scores_e2e, {k: v[0] for k, v in refs.items()}
 
 
 def test_gqa_decode_32k_full_size():
@@ -141,8 +142,8 @@ def test_needle_decode_128k_full_size():
     keys = torch.from_numpy(kb.view(np.int16)).view(torch.bfloat16).to(DEV)
     vals = torch.from_numpy(vb.view(np.int16)).view(torch.bfloat16).to(DEV)
     q = torch.from_numpy(qb.view(np.int16)).view(torch.bfloat16).to(DEV)
-    scores = _full_decode_case(dict(mode="prod", bits=4), 4, B, Hkv, Hq, ctx, keys, vals, q, qv,
-                               [(0, 0), (0, 5)], "needle-decode-128k")
+    scores, oracle_scores = _full_decode_case(dict(mode="prod", bits=4), 4, B, Hkv, Hq, ctx, keys, vals, q, qv,
+                                              [(0, 0), (0, 5)], "needle-decode-128k")
     s_gpu = _np(scores)[0]
     recalls, ranks = [], []
     for hq in range(Hq):
@@ -159,10 +160,24 @@ def test_needle_decode_128k_full_size():
     recall = float(np.mean(recalls))
     print("needle-decode-128k: top-5 recall vs exact fp32 %.3f; needle ranks per KV head %s" % (recall, ranks),
           flush=True)
-    # A quality floor, not parity: the oracle's own estimator, run on the CPU
-    # for KV heads 0, 3 and 5 of these inputs, recalls 0.5 of the exact top-5
-    # on average (per head 0.0 .. 1.0) and ranks every needle within the top 21.
-    assert recall >= 0.3, recall
+    # Head by head on the sampled KV heads: the GPU's recall equals the
+    # oracle's (the same estimator on the CPU, from its own encode of these
+    # keys), except where the oracle's 5th and 6th scores are within 2 % of
+    # their RMS, where either may make the top 5 (then they may differ by one).
+    compared = 0
+    for (b, h), s_or in oracle_scores.items():
+        for i in range(G):
+            hq = h * G + i
+            exact = kv[h * ctx:(h + 1) * ctx] @ qv[0, hq]
+            te = set(np.argsort(-exact, kind="stable")[:5].tolist())
+            to = np.argsort(-s_or[i], kind="stable")
+            r_or = len(te & set(to[:5].tolist())) / 5.0
+            srt = s_or[i][to[:6]]
+            tied = srt[4] - srt[5] < 2e-2 * math.sqrt(float(np.mean(s_or[i] ** 2)))
+            assert abs(recalls[hq] - r_or) <= (0.2 if tied else 1e-9), (hq, recalls[hq], r_or)
+            compared += 1
+    assert compared == 2 * G
+    # and the needles themselves stay at the top (the pages' needle retrieval)
     assert max(max(r) for r in ranks) < ctx // 1000, ranks
 
 
