@@ -246,8 +246,10 @@ tq_status tq_append_kv(const tq_key_config* cfg, const void* tables, const void*
  *              t >= ctx_len[b] are not written).
  *   workspace  device scratch; with workspace == NULL the call only stores the
  *              required size in *workspace_bytes (host) and returns TQ_OK.
- * Supported: d = 128; PROD with bits 2..4 (index 1..3 bits, 3 in nibbles);
- * MSE with bits 1..3; GROUPED with (outlier, normal) index bits (4, 2),
+ * Supported: d = 128; PROD with bits 2..7 (index 1..6 bits); MSE with bits
+ * 1..6 (indices of 4 to 6 bits are scored with one lookup table per
+ * coordinate instead of one per byte; MSE 7..8-bit tables would exceed LDS);
+ * GROUPED with (outlier, normal) index bits (4, 2),
  * (3, 2), (2, 2) or (4, 1); GROUPED_PROD with (3, 2) or (4, 1) (the lookup
  * tables of (4, 2) plus signs exceed a workgroup's 160 KiB of LDS);
  * Hq % Hkv == 0.  Other shapes return

@@ -66,21 +66,30 @@ constexpr int WGRP = 32 * QH + 16;  // dwords per value group of a wave's weight
 constexpr int WSLOT = 4 * WGRP;     // dwords of a wave's weight slot
 constexpr int PART = KD + 2;      // floats per partial: max, sum, out[128]
 constexpr float LOG2E = 1.4426950408889634f;
-constexpr int CHAIN = 4;          // table reads summed in 16-bit fields before a flush
-constexpr float EMAX = 16382.0f;  // entries round into [0, 16383]: four fit a 16-bit field
+// Table reads are summed in 16-bit fields, CHAIN at a time, before a flush
+// into 32-bit sums: entries round into [0, EMAX + 1] so that CHAIN of them
+// fit.  Formats with per-coordinate tables (128 reads per key, each rounded)
+// take chains of two and twice the resolution.
+template <bool COORD> constexpr int chain_len() { return COORD ? 2 : 4; }
+template <bool COORD> constexpr float entry_max() { return COORD ? 32766.0f : 16382.0f; }
 constexpr float PSCALE = 14.0f;   // softmax weights are carried as p * 2^14
 constexpr float SQRT_HALF_PI = 1.2533141373155003f;
 
-constexpr int width_of(int b) { return b == 1 ? 1 : b == 2 ? 2 : 4; }
+constexpr int width_of(int b) { return b == 1 ? 1 : b == 2 ? 2 : b <= 4 ? 4 : 8; }
 constexpr int stride_of(int b) { return b == 3 ? 128 : 256; }  // 3-bit in nibbles: bytes <= 0x77
+constexpr int CEN = 64;  // centroids staged per part (index widths up to 6 bits)
 
 // Table classes of a key format, in key-byte order: the index bytes of part 0,
 // (GROUPED, GROUPED_PROD) the index bytes of part 1, (PROD, GROUPED_PROD) the
-// QJL sign bytes.
+// QJL sign bytes.  Indices of 4 to 6 bits (one part) use one table per
+// coordinate instead of one per byte (kind 3): a byte table of 4-bit fields
+// would have 256 entries for each of 64 bytes (128 KiB), and a 5- or 6-bit
+// index fills a byte alone, so its table has 2^b entries.
 template <int MODE, int B0, int B1>
 struct Fmt {
   static constexpr bool GROUPED = MODE == TQ_MODE_GROUPED || MODE == TQ_MODE_GROUPED_PROD;
   static constexpr bool QJL = MODE == TQ_MODE_PROD || MODE == TQ_MODE_GROUPED_PROD;
+  static constexpr bool COORD = !GROUPED && B0 >= 4;  // per-coordinate tables for the index
   static constexpr int NPART = GROUPED ? 2 : 1;
   static constexpr int PD = KD / NPART;  // coordinates per part
   static constexpr int W0 = width_of(B0);
@@ -91,22 +100,33 @@ struct Fmt {
   static constexpr int IDXB = IP0 + IP1;                 // idx row bytes
   static constexpr int KWORDS = (IDXB + SP) / 4;         // idx + sign words per key
   static constexpr int NC = NPART + (QJL ? 1 : 0);       // table classes
-  // kind of class c: 0 / 1 index part, 2 sign bytes
-  static constexpr int kind(int c) { return c == 0 ? 0 : c == 2 ? 2 : (GROUPED ? 1 : 2); }
-  static constexpr int npos(int c) { return kind(c) == 0 ? IP0 : kind(c) == 1 ? IP1 : SP; }
-  static constexpr int stride(int c) { return kind(c) == 0 ? stride_of(B0) : kind(c) == 1 ? stride_of(B1) : 256; }
-  static constexpr int kbyte(int c) { return c == 0 ? 0 : kbyte(c - 1) + npos(c - 1); }  // first key byte
+  // kind of class c: 0 / 1 index bytes of part 0 / 1, 2 sign bytes, 3 index
+  // coordinates of part 0 (one table per coordinate)
+  static constexpr int kind(int c) { return c == 0 ? (COORD ? 3 : 0) : c == 2 ? 2 : (GROUPED ? 1 : 2); }
+  // positions (tables) of class c and the key bytes it spans
+  static constexpr int npos(int c) { return kind(c) == 3 ? PD : kind(c) == 0 ? IP0 : kind(c) == 1 ? IP1 : SP; }
+  static constexpr int nbytes(int c) { return kind(c) == 3 ? IP0 : npos(c); }
+  static constexpr int stride(int c) {
+    return kind(c) == 3 ? (1 << B0) : kind(c) == 0 ? stride_of(B0) : kind(c) == 1 ? stride_of(B1) : 256;
+  }
+  static constexpr int kbyte(int c) { return c == 0 ? 0 : kbyte(c - 1) + nbytes(c - 1); }  // first key byte
+  static constexpr int pos0(int c) { return c == 0 ? 0 : pos0(c - 1) + npos(c - 1); }     // first position
   static constexpr int ent(int c) { return c == 0 ? 0 : ent(c - 1) + npos(c - 1) * stride(c - 1); }  // first entry
-  static constexpr int cls(int pos) { return pos < kbyte(1) || NC == 1 ? 0 : (NC == 2 || pos < kbyte(2)) ? 1 : 2; }
+  static constexpr int cls(int pos) { return pos < pos0(1) || NC == 1 ? 0 : (NC == 2 || pos < pos0(2)) ? 1 : 2; }
   // table-read chains (CHAIN positions each), class by class
-  static constexpr int chain0(int c) { return kbyte(c) / CHAIN; }
+  static constexpr int CHAIN = chain_len<COORD>();
+  static constexpr float EMAX = entry_max<COORD>();
+  static constexpr int chain0(int c) { return pos0(c) / CHAIN; }
   static constexpr int chain_cls(int g) { return cls(g * CHAIN); }
+  // coordinates one position of the index class of part p covers (table range)
+  static constexpr int cpb(int p) { return COORD ? 1 : 8 / (p ? W1 : W0); }
   static constexpr int ENTRIES = ent(NC - 1) + npos(NC - 1) * stride(NC - 1);
-  static constexpr int POSITIONS = IDXB + SP;
+  static constexpr int POSITIONS = pos0(NC - 1) + npos(NC - 1);
+  static constexpr int HPOS0 = COORD ? PD : 0;  // first position built from nibble halves
   static_assert(IP0 % CHAIN == 0 && IP1 % CHAIN == 0 && SP % CHAIN == 0, "whole chains per class");
   // the weight ring also holds the half tables while the lookup tables are built
   static constexpr int RING_BYTES_W = NW * WSLOT * 4;
-  static constexpr int HALF_BYTES = POSITIONS * 32 * 16;
+  static constexpr int HALF_BYTES = (POSITIONS - HPOS0) * 32 * 16;
   static constexpr int RING_BYTES = RING_BYTES_W > HALF_BYTES ? RING_BYTES_W : HALF_BYTES;
 };
 
@@ -117,7 +137,7 @@ struct Lds {
   float qp[QH * KD];
   float qs[QH * KD];
   uint32_t ring[F::RING_BYTES / 4];
-  float cen[32];
+  float cen[2 * CEN];
   float rng[3][QH];    // largest byte range of each class and head (float bits, atomicMax)
   float offi[2][QH];   // index classes: sum over coordinates of the smallest term
   float sgp[8][QH];    // sign class: sum of |S q'| over each 16-row tile
@@ -185,6 +205,14 @@ __device__ __forceinline__ uint64_t lut_read(const unsigned char* smem, uint32_t
     off = (b << 3) + BASE;
     return *(const uint64_t*)(smem + off);
   }
+}
+
+// Entry of the table at byte offset BASE indexed by nibble k of w (a field
+// extract and a shift-add).
+__device__ __forceinline__ uint64_t lut_read_nib(const unsigned char* smem, uint32_t BASE, uint32_t w, int k) {
+  uint32_t b = __builtin_amdgcn_ubfe(w, 4 * k, 4);
+  asm("" : "+v"(b));
+  return *(const uint64_t*)(smem + (b << 3) + BASE);
 }
 
 template <int I, int N, typename Fn>
@@ -306,7 +334,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
   float* qp = L.qp;         // [QH][KD] rotated queries
   float* qs = L.qs;         // [QH][KD] S q' (PROD)
   uint32_t* wbuf = L.ring;  // [2][NW/2][4 groups][32 pairs][QH] half2 weights (groups padded)
-  float* cen = L.cen;       // [2][16] centroids of each part
+  float* cen = L.cen;       // [2][CEN] centroids of each part
   float* abuf = L.abuf;     // [2][NW/2][QH] p.V rescale factors
 
   const tq_blob_header* H = (const tq_blob_header*)a.tables;
@@ -471,8 +499,8 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
       for (int ks = 0; ks < 4; ++ks) sfrag[ks] = sp[4 * ks];
     }
   }
-  if (tid < 32) {
-    const int part = tid >> 4, k = tid & 15;
+  if (tid < 2 * CEN) {
+    const int part = tid / CEN, k = tid % CEN;
     cen[tid] = part < n_parts && k < (part ? lev1 : lev0) ? (part ? cent1 : cent0)[k] : 0.0f;
   }
   if (F::QJL && tid < QH) L.rng[F::NC - 1][tid] = 0.0f;
@@ -504,7 +532,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
     });
     qp[wave * KD + lane] = x0;
     qp[wave * KD + lane + 64] = x1;
-    constexpr int CPB0 = 8 / F::W0, CPB1 = 8 / F::W1;
+    constexpr int CPB0 = F::cpb(0), CPB1 = F::cpb(1);
     const float g0 = group_sum<CPB0>(fabsf(x0));
     const float lo0 = fminf(x0 * cmin0, x0 * cmax0);
     if constexpr (F::GROUPED) {
@@ -589,11 +617,11 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
   // holds, less the smallest such sum, in table steps (the low half carries
   // the +1/2 of the rounding).  A byte's entry is then lo[v & 15] + hi[v >> 4]
   // rounded down.  They live in the weight ring, unused until the main loop.
-  float4* halves = (float4*)wbuf;  // [POSITIONS][2][16]
-  for (int i = tid; i < F::POSITIONS * 32; i += NT) {
-    const int pos = i >> 5, half = (i >> 4) & 1, n = i & 15;
+  float4* halves = (float4*)wbuf;  // [POSITIONS - HPOS0][2][16]
+  for (int i = tid; i < (F::POSITIONS - F::HPOS0) * 32; i += NT) {
+    const int pos = F::HPOS0 + (i >> 5), half = (i >> 4) & 1, n = i & 15;
     const int c = F::cls(pos);
-    const int p = pos - F::kbyte(c);
+    const int p = pos - F::pos0(c);
     const int kind = F::kind(c);
     float sv[QH] = {0.0f, 0.0f, 0.0f, 0.0f}, mn[QH] = {0.0f, 0.0f, 0.0f, 0.0f};
     if (kind == 2) {
@@ -611,7 +639,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
       const int W = kind ? F::W1 : F::W0;
       const int per = 4 / W;  // coordinates per nibble
       const int fmask = (1 << (kind ? B1 : B0)) - 1;
-      const float* cn = cen + (kind ? 16 : 0);
+      const float* cn = cen + (kind ? CEN : 0);
       const float c_lo = cn[0], c_hi = cn[(kind ? lev1 : lev0) - 1];
       const int j0 = (kind ? F::PD : 0) + p * (8 / W) + half * per;
       for (int k = 0; k < per; ++k) {
@@ -629,25 +657,45 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
     float o[QH];
 #pragma unroll
     for (int hh = 0; hh < QH; ++hh) {
-      const float inv = rgv[hh] > 0.0f ? EMAX / rgv[hh] : 0.0f;
+      const float inv = rgv[hh] > 0.0f ? F::EMAX / rgv[hh] : 0.0f;
       o[hh] = fmaf(sv[hh] - mn[hh], inv, half ? 0.0f : 0.5f);
     }
     halves[i] = make_float4(o[0], o[1], o[2], o[3]);
   }
+  if constexpr (F::COORD) {
+    // per-coordinate tables of the index class: entry (j, v) =
+    // q'_j c[v] - min(q'_j c_lo, q'_j c_hi) in table steps, rounded
+    const float4 rg = *(const float4*)L.rng[0];
+    const float rgv[QH] = {rg.x, rg.y, rg.z, rg.w};
+    const float c_lo = cen[0], c_hi = cen[lev0 - 1];
+    for (int i = tid; i < F::PD << B0; i += NT) {
+      const int j = i >> B0, v = i & ((1 << B0) - 1);
+      const float cv = cen[v];
+      uint32_t e[QH];
+#pragma unroll
+      for (int hh = 0; hh < QH; ++hh) {
+        const float z = qp[hh * KD + j];
+        const float inv = rgv[hh] > 0.0f ? F::EMAX / rgv[hh] : 0.0f;
+        e[hh] = (uint32_t)fmaf(fmaf(cv, z, -fminf(z * c_lo, z * c_hi)), inv, 0.5f);
+      }
+      lut[F::ent(0) + i] = (uint64_t)(e[0] | (e[1] << 16)) | ((uint64_t)(e[2] | (e[3] << 16)) << 32);
+    }
+  }
   lds_barrier();
   // One thread per (position, low nibble) walks the high nibbles: its low
   // half stays in registers, the high halves are read by sixteen lanes at once.
-  for (int t = tid; t < F::POSITIONS * 16; t += NT) {
-    const int pos = t >> 4, lo = t & 15;
+  for (int t = tid; t < (F::POSITIONS - F::HPOS0) * 16; t += NT) {
+    const int hp = t >> 4, lo = t & 15;  // half-table position
+    const int pos = F::HPOS0 + hp;
     const int c = F::cls(pos);
     const int S = F::stride(c);
-    uint64_t* dst = lut + F::ent(c) + (pos - F::kbyte(c)) * S;
-    const float4 lo4 = halves[pos * 32 + lo];
+    uint64_t* dst = lut + F::ent(c) + (pos - F::pos0(c)) * S;
+    const float4 lo4 = halves[hp * 32 + lo];
 #pragma unroll 4
     for (int hi = 0; hi < 16; ++hi) {
       const int v = hi * 16 + lo;
       if (v < S) {
-        const float4 hi4 = halves[pos * 32 + 16 + hi];
+        const float4 hi4 = halves[hp * 32 + 16 + hi];
         const uint32_t e0 = (uint32_t)(lo4.x + hi4.x), e1 = (uint32_t)(lo4.y + hi4.y);
         const uint32_t e2 = (uint32_t)(lo4.z + hi4.z), e3 = (uint32_t)(lo4.w + hi4.w);
         dst[v] = (uint64_t)(e0 | (e1 << 16)) | ((uint64_t)(e2 | (e3 << 16)) << 32);
@@ -666,12 +714,12 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
       off = 0.0f;
       for (int w = 0; w < 8; ++w) off -= L.sgp[w][hh];
     } else {
-      off = L.offi[kind][hh];
+      off = L.offi[kind == 3 ? 0 : kind][hh];
     }
     // q' holds sqrt(PD) Pi q (per half when GROUPED): the sign class's
     // rho sqrt(pi/2) / m <S Pi q, .> is rho sqrt(pi/2) / (m sqrt(PD)) <S q', .>
     const float mul = kind == 2 ? SQRT_HALF_PI / ((float)KD * sqrtf((float)F::PD)) : 1.0f / (float)F::PD;
-    const float unit = L.rng[c][hh] / EMAX;
+    const float unit = L.rng[c][hh] / F::EMAX;
     L.uu[c][hh] = mul * unit * xscale;
     L.oo[c][hh] = mul * off * xscale;
   }
@@ -719,31 +767,41 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
           // The table reads run in batches of two chains (eight reads),
           // software-pipelined: batch i + 1 is issued before batch i is
           // summed, so one batch's latency hides behind the other's.
+          constexpr int CHAIN = F::CHAIN;
           constexpr int NCH = F::POSITIONS / CHAIN;
-          constexpr int NB = NCH / 2;
-          static_assert(NCH % 2 == 0, "whole batches of two chains");
+          // chains per batch: two, or one for 5- and 6-bit indices (a whole
+          // 128-byte index row in registers leaves no room for eight reads)
+          constexpr int BCH = F::COORD && F::W0 == 8 ? 1 : 2;
+          constexpr int NB = NCH / BCH;
+          static_assert(NCH % BCH == 0, "whole batches of chains");
           uint32_t acc[F::NC][QH];
-          uint64_t E[2][2 * CHAIN];
+          uint64_t E[BCH * CHAIN];
           auto issue = [&](auto bb, uint64_t* dst) {
             constexpr int bt = decltype(bb)::value;
 #pragma unroll
-            for (int j = 0; j < 2 * CHAIN; ++j) {
-              const int g = 2 * bt + j / CHAIN;
+            for (int j = 0; j < BCH * CHAIN; ++j) {
+              const int g = BCH * bt + j / CHAIN;
               const int c = F::chain_cls(g);
               const int pos = (g - F::chain0(c)) * CHAIN + j % CHAIN;
-              const int byte = F::kbyte(c) + pos;
               const uint32_t base = (uint32_t)(F::ent(c) + pos * F::stride(c)) * 8u;
-              dst[j] = lut_read(smem, base, kd.kw[byte >> 2], byte & 3);
+              if (F::kind(c) == 3 && F::W0 == 4) {
+                dst[j] = lut_read_nib(smem, base, kd.kw[pos >> 3], pos & 7);  // coordinate = nibble
+              } else {
+                const int byte = F::kbyte(c) + pos;  // (kind 3 with 8-bit fields: coordinate = byte)
+                dst[j] = lut_read(smem, base, kd.kw[byte >> 2], byte & 3);
+              }
             }
           };
           auto reduce = [&](auto bb, const uint64_t* src) {
             constexpr int bt = decltype(bb)::value;
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-              const int g = 2 * bt + i;
+            for (int i = 0; i < BCH; ++i) {
+              const int g = BCH * bt + i;
               const int c = F::chain_cls(g);
               const int q = g - F::chain0(c);
-              const uint64_t sum = src[CHAIN * i] + src[CHAIN * i + 1] + src[CHAIN * i + 2] + src[CHAIN * i + 3];
+              uint64_t sum = src[CHAIN * i];
+#pragma unroll
+              for (int k = 1; k < CHAIN; ++k) sum += src[CHAIN * i + k];
               const uint32_t lo = (uint32_t)sum, hi = (uint32_t)(sum >> 32);
               if (q == 0) {
                 acc[c][0] = lo & 0xFFFFu;
@@ -760,22 +818,12 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
               }
             }
           };
-#ifdef TQ_DEC_PIPE
-          static_for<0, NB + 1>([&](auto bb) {
-            constexpr int bt = decltype(bb)::value;
-            if constexpr (bt < NB) issue(std::integral_constant<int, bt>{}, E[bt & 1]);
-            __builtin_amdgcn_sched_barrier(0);
-            if constexpr (bt >= 1) reduce(std::integral_constant<int, bt - 1>{}, E[(bt - 1) & 1]);
-            __builtin_amdgcn_sched_barrier(0);
-          });
-#else
           static_for<0, NB>([&](auto bb) {
-            issue(bb, E[0]);
+            issue(bb, E);
             __builtin_amdgcn_sched_barrier(0);
-            reduce(bb, E[0]);
+            reduce(bb, E);
             __builtin_amdgcn_sched_barrier(0);
           });
-#endif
 #pragma unroll
           for (int hh = 0; hh < QH; ++hh) {
             float v = m0 * fmaf((float)acc[0][hh], UU[0][hh], OO[0][hh]);
@@ -1052,7 +1100,7 @@ bool supported(const tq::Parts& P) {
     const int b0 = P.part_bits[0], b1 = P.part_bits[1];
     return (b0 == 4 && b1 == 2) || (b0 == 2 && b1 == 2) || (b0 == 3 && b1 == 2) || (b0 == 4 && b1 == 1);
   }
-  return P.part_bits[0] >= 1 && P.part_bits[0] <= 3;
+  return P.part_bits[0] >= 1 && P.part_bits[0] <= 6;
 }
 
 hipError_t dispatch(const tq::Parts& P, int vb, const DecArgs& a, dim3 grid, hipStream_t s) {
@@ -1060,14 +1108,20 @@ hipError_t dispatch(const tq::Parts& P, int vb, const DecArgs& a, dim3 grid, hip
     switch (P.part_bits[0]) {
       case 1: return launch_vb<TQ_MODE_PROD, 1, 0>(vb, a, grid, s);
       case 2: return launch_vb<TQ_MODE_PROD, 2, 0>(vb, a, grid, s);
-      default: return launch_vb<TQ_MODE_PROD, 3, 0>(vb, a, grid, s);
+      case 3: return launch_vb<TQ_MODE_PROD, 3, 0>(vb, a, grid, s);
+      case 4: return launch_vb<TQ_MODE_PROD, 4, 0>(vb, a, grid, s);
+      case 5: return launch_vb<TQ_MODE_PROD, 5, 0>(vb, a, grid, s);
+      default: return launch_vb<TQ_MODE_PROD, 6, 0>(vb, a, grid, s);
     }
   }
   if (P.mode == TQ_MODE_MSE) {
     switch (P.part_bits[0]) {
       case 1: return launch_vb<TQ_MODE_MSE, 1, 0>(vb, a, grid, s);
       case 2: return launch_vb<TQ_MODE_MSE, 2, 0>(vb, a, grid, s);
-      default: return launch_vb<TQ_MODE_MSE, 3, 0>(vb, a, grid, s);
+      case 3: return launch_vb<TQ_MODE_MSE, 3, 0>(vb, a, grid, s);
+      case 4: return launch_vb<TQ_MODE_MSE, 4, 0>(vb, a, grid, s);
+      case 5: return launch_vb<TQ_MODE_MSE, 5, 0>(vb, a, grid, s);
+      default: return launch_vb<TQ_MODE_MSE, 6, 0>(vb, a, grid, s);
     }
   }
   const int b0 = P.part_bits[0], b1 = P.part_bits[1];

@@ -273,6 +273,8 @@ def test_decode_argument_errors():
     assert _dec(prod, vg=64) == L.TQ_ERR_UNSUPPORTED
     assert _dec(prod, wsb=None) == L.TQ_ERR_ARG
     assert _dec(L.key_config(mode="mse", bits=8)) == L.TQ_ERR_UNSUPPORTED
+    assert _dec(L.key_config(mode="mse", bits=7)) == L.TQ_ERR_UNSUPPORTED    # 128 x 128 entries: over LDS
+    assert _dec(L.key_config(mode="prod", bits=8)) == L.TQ_ERR_UNSUPPORTED
     assert _dec(L.key_config(mode="grouped", bits_outlier=4, bits_normal=4)) == L.TQ_ERR_UNSUPPORTED
 
 

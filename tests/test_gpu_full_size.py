@@ -119,7 +119,7 @@ def test_gqa_decode_32k_full_size():
     vals = W.normal_bf16_device(3, 2, (n, D), DEV)
     q = W.normal_bf16_device(3, 3, (1, B, Hq, D), DEV)[0].contiguous()
     _full_decode_case(dict(mode="prod", bits=3), 2, B, Hkv, Hq, ctx, keys, vals, q, _np(q.float()),
-                      [(0, 0), (6, 3), (15, 7)], "gqa-decode-32k")
+                      [(0, 0), (2, 5), (6, 3), (9, 1), (11, 6), (15, 7)], "gqa-decode-32k")
 
 
 def test_needle_decode_128k_full_size():
@@ -143,7 +143,7 @@ def test_needle_decode_128k_full_size():
     vals = torch.from_numpy(vb.view(np.int16)).view(torch.bfloat16).to(DEV)
     q = torch.from_numpy(qb.view(np.int16)).view(torch.bfloat16).to(DEV)
     scores, oracle_scores = _full_decode_case(dict(mode="prod", bits=4), 4, B, Hkv, Hq, ctx, keys, vals, q, qv,
-                                              [(0, 0), (0, 5)], "needle-decode-128k")
+                                              [(0, 0), (0, 3), (0, 5), (0, 7)], "needle-decode-128k")
     s_gpu = _np(scores)[0]
     recalls, ranks = [], []
     for hq in range(Hq):
@@ -176,7 +176,7 @@ def test_needle_decode_128k_full_size():
             tied = srt[4] - srt[5] < 2e-2 * math.sqrt(float(np.mean(s_or[i] ** 2)))
             assert abs(recalls[hq] - r_or) <= (0.2 if tied else 1e-9), (hq, recalls[hq], r_or)
             compared += 1
-    assert compared == 2 * G
+    assert compared == len(oracle_scores) * G
     # and the needles themselves stay at the top (the pages' needle retrieval)
     assert max(max(r) for r in ranks) < ctx // 1000, ranks
 
@@ -191,14 +191,14 @@ def test_outlier_grouped_16k_full_size():
     vals = W.normal_bf16_device(5, 2, (n, D), DEV)
     q = W.normal_bf16_device(5, 3, (1, B, Hq, D), DEV)[0].contiguous()
     _full_decode_case(dict(mode="grouped", bits_outlier=4, bits_normal=2), 4, B, Hkv, Hq, ctx, keys, vals, q,
-                      _np(q.float()), [(0, 0), (3, 6), (7, 7)], "outlier-grouped-16k")
+                      _np(q.float()), [(0, 0), (1, 2), (3, 6), (5, 4), (7, 7)], "outlier-grouped-16k")
 
 
 @pytest.mark.parametrize("bits", [4, 8])
 def test_mse_prefill_encode_full_size(bits):
     """28 layers x 2 KV heads x 32768 bf16 keys (norms log-uniform in [2, 20]),
     MSE mode at 4 and 8 bits, one seed per layer: all layers are encoded in
-    one batched launch (as the benchmark times them); sampled rows of three
+    one batched launch (as the benchmark times them); sampled rows of five
     layers are checked against the oracle."""
     n_layer = 2 * 32768
     rng = np.random.default_rng(2024)
@@ -206,7 +206,7 @@ def test_mse_prefill_encode_full_size(bits):
     tabs = [tq.Tables(L.key_config(mode="mse", bits=bits, seed=42 + layer), DEV) for layer in range(28)]
     kps = tq.encode_keys_batched(tabs, xs)
     torch.cuda.synchronize()
-    for layer in (0, 13, 27):
+    for layer in (0, 6, 13, 20, 27):
         x, kp = xs[layer], kps[layer]
         To = O.build_tables(O.KeyConfig(d=D, mode="mse", bits=bits, seed=42 + layer))
         rows = np.concatenate([np.arange(1024), n_layer - 1024 + np.arange(1024),

@@ -248,6 +248,13 @@ DEC_CASES = [
     (dict(mode="grouped_prod", bits_outlier=3, bits_normal=2), 2),
     (dict(mode="grouped_prod", bits_outlier=3, bits_normal=2), 4),
     (dict(mode="grouped_prod", bits_outlier=4, bits_normal=1), 4),
+    # indices of 4 to 6 bits: one lookup table per coordinate (nibbles or bytes)
+    (dict(mode="mse", bits=4), 2),
+    (dict(mode="mse", bits=5), 4),
+    (dict(mode="mse", bits=6), 2),
+    (dict(mode="prod", bits=5), 4),
+    (dict(mode="prod", bits=6), 2),
+    (dict(mode="prod", bits=7), 4),
 ]
 
 
