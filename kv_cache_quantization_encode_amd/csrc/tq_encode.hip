@@ -764,18 +764,32 @@ __global__ __launch_bounds__(WAVES * 64, key_waves_per_simd(MODE, DT)) void enco
         wgt_p[0] = nmax > 0.0f ? n_part[0] / nmax : 0.0f;
         wgt_p[1] = nmax > 0.0f ? n_part[1] / nmax : 0.0f;
       }
+      // residual split into fp16 hi + lo, two coordinates at a time: hi
+      // rounded toward zero (any hi works: res - hi is then below hi's ulp and
+      // of res's sign, so lo carries the next 11 bits), lo = res - hi as one
+      // mixed-precision fma per coordinate
       float rr = 0.0f;
       half8 bhi[4], blo[4];
 #pragma unroll
-      for (int r = 0; r < 32; ++r) {
-        const int pr = part_of(r);
-        float res = fmaf(x[r], inv_p[pr], -s_cent[pr * MAX_LEVELS + q[r]]);
-        if constexpr (GRP) res *= wgt_p[pr];
-        rr = fmaf(res, res, rr);
-        const _Float16 h = (_Float16)res;
-        const _Float16 lo = (_Float16)(res - (float)h);
-        bhi[r >> 3][r & 7] = h;
-        blo[r >> 3][r & 7] = lo;
+      for (int r = 0; r < 32; r += 2) {
+        float res[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int pr = part_of(r + e);
+          res[e] = fmaf(x[r + e], inv_p[pr], -s_cent[pr * MAX_LEVELS + q[r + e]]);
+          if constexpr (GRP) res[e] *= wgt_p[pr];
+          rr = fmaf(res[e], res[e], rr);
+        }
+        const auto h2 = __builtin_amdgcn_cvt_pkrtz(res[0], res[1]);
+        const uint32_t hw = __builtin_bit_cast(uint32_t, h2);
+        float l0, l1;  // res - hi, each from one half of hw (exact)
+        asm("v_fma_mix_f32 %0, -%1, 1.0, %2 op_sel_hi:[1,0,0]" : "=v"(l0) : "v"(hw), "v"(res[0]));
+        asm("v_fma_mix_f32 %0, -%1, 1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(l1) : "v"(hw), "v"(res[1]));
+        const auto lo2 = __builtin_amdgcn_cvt_pkrtz(l0, l1);
+        bhi[r >> 3][r & 7] = (_Float16)h2[0];
+        bhi[r >> 3][(r & 7) + 1] = (_Float16)h2[1];
+        blo[r >> 3][r & 7] = (_Float16)lo2[0];
+        blo[r >> 3][(r & 7) + 1] = (_Float16)lo2[1];
       }
       rr = xor_sum(xor_sum(rr, 16), 32);
       // The fragment offset is made opaque to the compiler each tile, so that it
