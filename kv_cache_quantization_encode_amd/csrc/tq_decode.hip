@@ -22,14 +22,14 @@
 // carry into each other) and then folded into 32-bit sums per head with
 // v_dot2_u32_u16, so the sums are exact integers.
 // Half of the waves score 64-token tiles (lane = token) and run the online
-// softmax; the other half accumulate p.V for those tiles one round later
-// (lane = token-pair slot and 8-channel slice) on v_dot2_f32_f16 over token
-// pairs, with the 2- or 4-bit code fields left in place as fp16 subnormal bit
-// patterns (a byte's fields up to channel i, masked: prefix value * 2^-24), so
-// no conversion is spent per code and per-channel sums are differences of
-// consecutive prefix sums at the end.  The value scale is folded into the
-// weight (p * scale, as fp16) and the zero point is summed separately
-// (sum_t p_t zero_t, fp32).  Softmax weights are carried as p * 2^14 and the
+// softmax; the other half accumulate p.V for those tiles one round later on
+// MFMA (v_mfma_f32_16x16x32_f16: A = the weights, rows value group x head;
+// B = the codes, one column per channel), with the 2- or 4-bit code fields
+// left in place as fp16 subnormal bit patterns (a byte's fields up to field
+// f, masked: prefix value * 2^-24), so no conversion is spent per code and
+// per-channel sums are differences of consecutive prefix sums at the end.
+// The value scale is folded into the weight (p * scale, as fp16) and the
+// zero point is summed separately (sum_t p_t zero_t, fp32).  Softmax weights are carried as p * 2^14 and the
 // scales of each tile are renormalised by a power of two, so weights keep the
 // fp16 normal range whatever the values' magnitude.  The chunk's (max, sum,
 // unnormalised output) goes to the workspace; a second kernel merges chunks
@@ -51,6 +51,7 @@ typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float2_t __attribute__((ext_vector_type(2)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef unsigned short ushort2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int KD = 128;
 #ifndef TQ_DEC_WAVES
@@ -62,8 +63,12 @@ constexpr int NS = NW / 2;        // score waves (and p.V waves)
 constexpr int PAGE_CACHE = 512;   // block-table entries a workgroup keeps in LDS
 constexpr int TILE = 64;          // tokens per wave tile
 constexpr int QH = 4;             // query heads per workgroup
-constexpr int WGRP = 32 * QH + 16;  // dwords per value group of a wave's weight slot (padded)
-constexpr int WSLOT = 4 * WGRP;     // dwords of a wave's weight slot
+// A wave's weight slot holds the MFMA A operand of its tile's p.V: rows
+// m = 4 group + head, 64 tokens, fp16, as [chunk][token group kq][m][j] with
+// token 32 chunk + 4 j + kq; each (chunk, kq) block is padded by 16 halves so
+// that the score lanes' 2-byte stores spread over the LDS banks.
+constexpr int ABLK = 16 * 8 + 16;   // halves per (chunk, kq) block
+constexpr int WSLOT = 8 * ABLK / 2; // dwords of a wave's weight slot
 constexpr int PART = KD + 2;      // floats per partial: max, sum, out[128]
 constexpr float LOG2E = 1.4426950408889634f;
 // Table reads are summed in 16-bit fields, CHAIN at a time, before a flush
@@ -372,19 +377,17 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
   constexpr int VROW = KD * VB / 8;  // bytes of a value-code row
   const bool scorer = wave < NS;
   const int pw = scorer ? wave : wave - NS;
-  // p.V lanes: a lane takes CH channels (CB code bytes per token: 16
-  // channels at 2 bits, one dword; else 8), u = lane % NSL of the NSL
-  // slices, and the token pairs slot + NSLOT k of a tile, slot = lane / NSL
-#ifndef TQ_PV_CH2
-#define TQ_PV_CH2 16
-#endif
-  // (16 channels only for key formats of at most 48 bytes: with more key
-  // words the score waves' registers and the p.V waves' 64 sums do not fit
-  // in 128 VGPRs together)
-  constexpr int CH = VB == 2 && F::KWORDS <= 12 ? TQ_PV_CH2 : 8, CB = CH * VB / 8, NSL = KD / CH, NSLOT = 64 / NSL;
-  constexpr int NPAIR = TILE / 2 / NSLOT;  // token pairs of a lane per tile
-  constexpr int NCODE = 2 * NPAIR;         // code dwords of a lane per tile
-  const int slot = lane / NSL, u = lane % NSL, grp = u * CH / 32;
+  // p.V lanes: lane = (column n = lane & 15, token group kq = lane >> 4) of
+  // the MFMA B operand.  Column n of block beta (0..7) is channel 8 n + beta,
+  // so a lane needs the same 8 channels (two bytes of 2-bit codes, four of
+  // 4-bit ones) of each of its 16 tokens 32 chunk + 4 j + kq (j = 0..7).  It
+  // loads the aligned dword holding them (2-bit: lanes 2i and 2i + 1 load the
+  // same one, each picks its half): one load instruction of the wave covers
+  // four consecutive rows.
+  constexpr int NCODE = 16;  // code dwords of a lane per tile: [chunk][j]
+  const int pn = lane & 15, kq = lane >> 4;
+  const int cbyte = VB == 2 ? 4 * (pn >> 1) : 4 * pn;  // dword of the lane's channels in a row
+  const uint32_t cb0 = VB == 2 ? 2 * (pn & 1) : 0;     // their first byte in that dword
   const int n_tiles = t_end > t_begin ? (t_end - t_begin + TILE - 1) / TILE : 0;
   const int rounds = (n_tiles + NS - 1) / NS;
   auto tile_tb = [&](int r) { return t_begin + (r * NS + pw) * TILE; };
@@ -433,25 +436,22 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
     d.zv = *(const uint2*)(a.vzero + rec * 4);
     d.sv = *(const uint2*)(a.vscale + rec * 4);
   };
-  // value codes of this lane's token pairs (slot + NSLOT k): c[2k] the
-  // pair's even token, c[2k + 1] its odd one
+  // value codes of this lane's tokens: c[8 chunk + j] for token 32 chunk + 4 j + kq.
+  // Buffer loads against a range of the tile's rows below t_end: a load past
+  // it returns 0 without touching memory (its token's weight is 0), so the
+  // addresses are one offset per lane plus immediates, with no clamping.
+  const int voff = kq * VROW + cbyte;
   auto load_codes = [&](int tb, uint32_t* c) {
-    const long long tbase = tile_base(tb);
-    if (tb + TILE <= t_end) {  // whole tile: one base address, immediate offsets
-      const uint8_t* base = a.vcodes + (tbase + tb + 2 * slot) * VROW + CB * u;
+    // (the tile's base and row count are wave-uniform: moved to scalar
+    // registers, the descriptor needs no per-lane loop)
+    const unsigned long long p = (unsigned long long)(a.vcodes + (tile_base(tb) + tb) * VROW);
+    const unsigned long long pu = (unsigned long long)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)p) |
+                                  ((unsigned long long)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(p >> 32)) << 32);
+    const int rows = __builtin_amdgcn_readfirstlane(min(max(t_end - tb, 0), TILE));
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)pu, 0, rows * VROW, 0x00020000);
 #pragma unroll
-      for (int k = 0; k < NCODE; ++k) {
-        const uint8_t* pa = base + ((k >> 1) * 2 * NSLOT + (k & 1)) * VROW;
-        c[k] = CB == 2 ? (uint32_t) * (const uint16_t*)pa : *(const uint32_t*)pa;
-      }
-    } else {
-#pragma unroll
-      for (int k = 0; k < NCODE; ++k) {
-        const int t = min(tb + 2 * slot + (k >> 1) * 2 * NSLOT + (k & 1), t_last);
-        const uint8_t* pa = a.vcodes + (tbase + t) * VROW + CB * u;
-        c[k] = CB == 2 ? (uint32_t) * (const uint16_t*)pa : *(const uint32_t*)pa;
-      }
-    }
+    for (int k = 0; k < NCODE; ++k)
+      c[k] = __builtin_amdgcn_raw_buffer_load_b32(rs, voff + (32 * (k >> 3) + 4 * (k & 7)) * VROW, 0, 0);
   };
 
   // ---- prologue: rotate the queries, project them, build the tables.
@@ -892,12 +892,10 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
           for (int k = 0; k < 4; ++k) zacc[hh][k] = fmaf(p[hh], zz[k], zacc[hh][k]);
         }
         // weights (p 2^14) * (scale 2^ks) as fp16 (both factors rounded to
-        // fp16, then two heads per packed multiply), paired by token:
-        // [group][pair][head] = (w_even, w_odd); the group stride is padded so
-        // that neither these stores nor the p.V waves' 16-byte reads pile
-        // onto a few LDS banks
-        uint16_t* wb16 = (uint16_t*)(wbuf + ((r & 1) * NS + pw) * WSLOT);
-        const int pair = lane >> 1, odd = lane & 1;
+        // fp16, then two heads per packed multiply) into the A operand of the
+        // p.V wave: row 4 group + head, this token's place (chunk, kq, j)
+        uint16_t* wb16 = (uint16_t*)(wbuf + ((r & 1) * NS + pw) * WSLOT) +
+                         ((lane >> 5) * 4 + (lane & 3)) * ABLK + ((lane >> 2) & 7);
         const half2_t p01 = __builtin_convertvector((float2_t){p[0], p[1]}, half2_t);
         const half2_t p23 = __builtin_convertvector((float2_t){p[2], p[3]}, half2_t);
         const half2_t kk2 = {(_Float16)ksc, (_Float16)ksc};
@@ -907,10 +905,10 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
         for (int k = 0; k < 4; ++k) {
           const half2_t s2 = {sk[k], sk[k]};
           const half2_t w01 = p01 * s2, w23 = p23 * s2;
-          wb16[(k * WGRP + pair * QH + 0) * 2 + odd] = __builtin_bit_cast(uint32_t, w01) & 0xFFFFu;
-          wb16[(k * WGRP + pair * QH + 1) * 2 + odd] = __builtin_bit_cast(uint32_t, w01) >> 16;
-          wb16[(k * WGRP + pair * QH + 2) * 2 + odd] = __builtin_bit_cast(uint32_t, w23) & 0xFFFFu;
-          wb16[(k * WGRP + pair * QH + 3) * 2 + odd] = __builtin_bit_cast(uint32_t, w23) >> 16;
+          wb16[(4 * k + 0) * 8] = __builtin_bit_cast(uint32_t, w01) & 0xFFFFu;
+          wb16[(4 * k + 1) * 8] = __builtin_bit_cast(uint32_t, w01) >> 16;
+          wb16[(4 * k + 2) * 8] = __builtin_bit_cast(uint32_t, w23) & 0xFFFFu;
+          wb16[(4 * k + 3) * 8] = __builtin_bit_cast(uint32_t, w23) >> 16;
         }
         if (lane == 0) {
 #pragma unroll
@@ -937,11 +935,11 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
     }
     if (lane == 0) L.ksf[pw] = ks;
   } else {
-    float acc[QH][CH];
+    // acc[beta]: the MFMA accumulator of column block beta; lane holds rows
+    // 4 kq + i (value group kq, head i) of column pn (channel 8 pn + beta)
+    floatx4 acc[8];
 #pragma unroll
-    for (int hh = 0; hh < QH; ++hh)
-#pragma unroll
-      for (int k = 0; k < CH; ++k) acc[hh][k] = 0.0f;
+    for (int k = 0; k < 8; ++k) acc[k] = (floatx4){0.0f, 0.0f, 0.0f, 0.0f};
     // two code buffers in turn: round r consumes tile r - 1 while the codes
     // of tile r arrive in the other
     uint32_t codes2[NCODE];
@@ -954,41 +952,45 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
         const float alv[QH] = {uniform(al.x), uniform(al.y), uniform(al.z), uniform(al.w)};
         if (alv[0] != 1.0f || alv[1] != 1.0f || alv[2] != 1.0f || alv[3] != 1.0f) {
 #pragma unroll
-          for (int hh = 0; hh < QH; ++hh)
+          for (int k = 0; k < 8; ++k)
 #pragma unroll
-            for (int k = 0; k < CH; ++k) acc[hh][k] *= alv[hh];
+            for (int i = 0; i < QH; ++i) acc[k][i] *= alv[i];
         }
-        // ---------------- p.V: lane = (slot, CH-channel slice u)
+        // ---------------- p.V on MFMA: per 32-token chunk, A = the weights
+        // (rows group x head), B = the codes (column n of block beta: channel
+        // 8 n + beta).  B elements are the code fields left in place as fp16
+        // subnormal bit patterns: a byte's fields up to field f, masked, so
+        // one byte permute serves a whole byte and the byte's last field
+        // needs no mask; block beta then sums prefixes, told apart at the end.
+        // byte bb of the lane's channels in tokens A, B -> bytes 0 and 2
+        uint32_t psel[VB];
 #pragma unroll
-        for (int k = 0; k < NPAIR; ++k) {
-          const int pr = slot + NSLOT * k;
-          const uint4 wv = *(const uint4*)(wsrc + grp * WGRP + pr * QH);
-          const uint32_t wh[QH] = {wv.x, wv.y, wv.z, wv.w};
-          // pairs[i] holds, for the two tokens (low and high half), the
-          // prefix of channel i: the channels of its byte up to i, so that
-          // one byte permute serves a whole byte and the last prefix of each
-          // byte needs no mask.  The channel sums are told apart at the end.
-          uint32_t pairs[CH];
-          const uint32_t cA = cur[2 * k], cB = cur[2 * k + 1];
+        for (int bb = 0; bb < VB; ++bb) psel[bb] = 0x0c000c00u | ((4u + cb0 + bb) << 16) | (cb0 + bb);
 #pragma unroll
-          for (int bb = 0; bb < CB; ++bb) {  // byte bb of A and of B -> bytes 0, 2
-            const uint32_t Yb = __builtin_amdgcn_perm(cB, cA, 0x0c000c00u | ((4u + bb) << 16) | (uint32_t)bb);
-            if constexpr (VB == 2) {
-              pairs[4 * bb + 0] = Yb & 0x00030003u;
-              pairs[4 * bb + 1] = Yb & 0x000F000Fu;
-              pairs[4 * bb + 2] = Yb & 0x003F003Fu;
-              pairs[4 * bb + 3] = Yb;
-            } else {
-              pairs[2 * bb] = Yb & 0x000F000Fu;
-              pairs[2 * bb + 1] = Yb;
+        for (int cc = 0; cc < 2; ++cc) {
+          const half8_t A = *(const half8_t*)(wsrc + ((cc * 4 + kq) * ABLK + pn * 8) / 2);
+          // per code byte bb: Y[i] = byte bb of tokens 2i and 2i + 1 in bytes
+          // 0 and 2, then the blocks of the byte's fields
+#pragma unroll
+          for (int bb = 0; bb < VB; ++bb) {
+            uint32_t Y[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const uint32_t cA = cur[8 * cc + 2 * i], cB = cur[8 * cc + 2 * i + 1];
+              Y[i] = __builtin_amdgcn_perm(cB, cA, psel[bb]);
             }
-          }
+            constexpr int PER = 8 / VB;  // fields per byte
 #pragma unroll
-          for (int hh = 0; hh < QH; ++hh) {
-            const half2_t w2 = __builtin_bit_cast(half2_t, wh[hh]);
+            for (int f = 0; f < PER; ++f) {
+              // prefix of fields 0..f of the byte (the last one unmasked)
+              const uint32_t mask = (VB == 2 ? (f == 0 ? 0x00030003u : f == 1 ? 0x000F000Fu : f == 2 ? 0x003F003Fu : 0x00FF00FFu)
+                                             : (f == 0 ? 0x000F000Fu : 0x00FF00FFu));
+              const bool bare = f == PER - 1;
+              u32x4_t bv;
 #pragma unroll
-            for (int i = 0; i < CH; ++i)
-              acc[hh][i] = __builtin_amdgcn_fdot2(w2, __builtin_bit_cast(half2_t, pairs[i]), acc[hh][i], false);
+              for (int i = 0; i < 4; ++i) bv[i] = bare ? Y[i] : Y[i] & mask;
+              acc[PER * bb + f] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, __builtin_bit_cast(half8_t, bv), acc[PER * bb + f], 0, 0, 0);
+            }
           }
         }
       }
@@ -1001,26 +1003,22 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
         lds_barrier();
       }
     }
-    // Undo the placement: accumulator i holds, in units of 2^-24, the
-    // prefix sum over the channels of its byte up to i, channel j weighted
-    // by its field's place value step_j; a channel's sum is the difference
-    // of consecutive prefixes over its place value.
+    // Undo the placement: block beta holds, in units of 2^-24, the prefix
+    // sum over the fields of its byte up to beta's, field f weighted by its
+    // place value 2^(VB f); a channel's sum is the difference of consecutive
+    // prefixes over its place value.  Channel 8 pn + beta is in value group
+    // pn / 4, so the lanes whose rows are that group hold it.
+    if (kq == (pn >> 2)) {
 #pragma unroll
-    for (int hh = 0; hh < QH; ++hh) {
-      float r[CH];
+      for (int k = 0; k < 8; ++k) {
+        constexpr int PER = 8 / VB;  // fields per byte
+        const int f = k % PER;
+        const float unit = 16777216.0f / (float)(1 << (VB * f));
 #pragma unroll
-      for (int i = 0; i < CH; ++i) {  // over the slots (lane bits above the slice)
-        float v = acc[hh][i];
-        if constexpr (NSL == 8) v += lane_xor<8>(v, lane);
-        r[i] = sum_xor32(sum_xor16(v));
-      }
-#pragma unroll
-      for (int i = 0; i < CH; ++i) {
-        constexpr int PER = 8 / VB;  // channels per byte
-        const int f = i % PER;       // field within the byte
-        const float step = (float)(1 << (VB * f));
-        const float v = f == 0 ? r[i] : r[i] - r[i - 1];
-        if (lane < NSL) mine[hh * RS + 6 + CH * u + i] = v * (16777216.0f / step);
+        for (int i = 0; i < QH; ++i) {
+          const float v = f == 0 ? acc[k][i] : acc[k][i] - acc[k - 1][i];
+          mine[i * RS + 6 + 8 * pn + k] = v * unit;
+        }
       }
     }
   }
