@@ -440,6 +440,8 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
   // Buffer loads against a range of the tile's rows below t_end: a load past
   // it returns 0 without touching memory (its token's weight is 0), so the
   // addresses are one offset per lane plus immediates, with no clamping.
+  // They are nontemporal (nt: streamed past the caches; the codes are read
+  // once, and each load of the wave covers whole lines).
   const int voff = kq * VROW + cbyte;
   auto load_codes = [&](int tb, uint32_t* c) {
     // (the tile's base and row count are wave-uniform: moved to scalar
@@ -451,7 +453,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)pu, 0, rows * VROW, 0x00020000);
 #pragma unroll
     for (int k = 0; k < NCODE; ++k)
-      c[k] = __builtin_amdgcn_raw_buffer_load_b32(rs, voff + (32 * (k >> 3) + 4 * (k & 7)) * VROW, 0, 0);
+      c[k] = __builtin_amdgcn_raw_buffer_load_b32(rs, voff + (32 * (k >> 3) + 4 * (k & 7)) * VROW, 0, 2);
   };
 
   // ---- prologue: rotate the queries, project them, build the tables.
