@@ -310,6 +310,7 @@ def main():
         cpu = cpu_baseline(args.cpu_groups)
     traffic = traffic_from_profile()
     copy_gbps = copy_bandwidth()
+    read_gbps = read_bandwidth(tq)
     line = {
         "metric": "decode-attn KV tokens/s & HBM GB/s (% of peak); encode keys/s",
         "value": value,
@@ -331,7 +332,8 @@ def main():
                      "kernel": "tq_decode_attention (decode_kernel + merge_kernel)",
                      "algorithmic_bytes": DECODE_BYTES, "ms_mean": dec_ms_mean,
                      "ms_median": dec_ms_median,
-                     "achievable_copy_gbps": copy_gbps, "frac_of_copy": achieved / copy_gbps},
+                     "achievable_copy_gbps": copy_gbps, "frac_of_copy": achieved / copy_gbps,
+                     "achievable_read_gbps": read_gbps, "frac_of_read": achieved / read_gbps},
         "cpu_baseline": cpu,
     }
     line.update(extra)
@@ -371,6 +373,30 @@ def copy_bandwidth(mib=2048, reps=20):
     ms = e0.elapsed_time(e1) / reps
     del src, dst
     return 2.0 * n * 4 / (ms * 1e-3) / 1e9
+
+
+def read_bandwidth(tq, mib=2048, reps=20):
+    """Read bandwidth of one streaming pass with 16-byte nontemporal loads
+    (tq_stream_read over 2 GiB, settled clocks): the access pattern of the
+    decode's reads of the packed cache, so the ceiling its achieved bytes per
+    second compare against on this GPU."""
+    import torch
+    src = torch.ones(mib * 1024 * 1024 // 4, dtype=torch.int32, device="cuda:0")
+    sink = torch.empty(65536, dtype=torch.int32, device="cuda:0")
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < 0.2:
+        tq.stream_read(src, sink)
+        torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        tq.stream_read(src, sink)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    nbytes = src.numel() * 4
+    del src, sink
+    return nbytes / (ms * 1e-3) / 1e9
 
 
 def encode_bench(tq, W, T, keys, vals, dev, reps=10):

@@ -398,6 +398,21 @@ tq_status tq_select_outlier_channels(const void* x, int32_t dtype, int64_t n_vec
                                      int32_t d, int32_t n_outlier, int32_t* perm, void* workspace,
                                      size_t* workspace_bytes, void* stream);
 
+/*
+ * tq_stream_read -- the measurement reference for the decode's roofline (not
+ * part of the method): one pass over `bytes` of device memory with 16-byte
+ * nontemporal loads, the way the decode streams the packed cache.  Timing it
+ * gives the read bandwidth the GPU actually sustains, next to the
+ * specification's peak.
+ *   src     device buffer, 16-byte aligned; bytes > 0, a multiple of 16.
+ *   sink    device uint32 [TQ_STREAM_READ_SINK]: one xor of the words each
+ *           thread read (keeps the loads; no other meaning), overwritten.
+ * Errors: TQ_ERR_ARG for a null or misaligned pointer or a bad size; launch
+ * failures as TQ_ERR_HIP.
+ */
+#define TQ_STREAM_READ_SINK 65536
+tq_status tq_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream);
+
 /* Static description of a status code (never NULL). */
 const char* tq_status_string(int32_t status);
 

@@ -10,7 +10,7 @@ from .api import (Decoder, KeyBatchEncoder, Tables, append_kv, build_codebook, c
                   decode_attention_noalloc,
                   decode_workspace_bytes, dequantize_keys, dequantize_values, encode_keys, encode_keys_batched,
                   encode_values,
-                  idx_row_bytes, key_planes, parse_tables, select_outlier_channels, value_planes)
+                  idx_row_bytes, key_planes, parse_tables, select_outlier_channels, stream_read, value_planes)
 from .store import PagedKVCache
 from . import quality
 
@@ -19,6 +19,6 @@ __all__ = ["KeyConfig", "TqError", "key_config", "status_string", "Tables", "Dec
            "decode_attention_noalloc",
            "decode_workspace_bytes", "key_planes", "value_planes", "idx_row_bytes", "PagedKVCache",
            "dequantize_keys", "dequantize_values", "quality",
-           "channel_moments", "select_outlier_channels",
+           "channel_moments", "select_outlier_channels", "stream_read",
            "TQ_F32", "TQ_BF16", "TQ_F16", "TQ_MODE_MSE", "TQ_MODE_PROD", "TQ_MODE_GROUPED",
            "TQ_MODE_GROUPED_PROD"]

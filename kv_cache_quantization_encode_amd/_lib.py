@@ -22,11 +22,12 @@ LIB_PATH = os.environ.get("TQ_LIBRARY") or os.path.join(HERE, "libtq.so")
 TQ_OK, TQ_ERR_ARG, TQ_ERR_UNSUPPORTED, TQ_ERR_WORKSPACE, TQ_ERR_HIP = 0, -1, -2, -3, -4
 TQ_MODE_MSE, TQ_MODE_PROD, TQ_MODE_GROUPED, TQ_MODE_GROUPED_PROD = 0, 1, 2, 3
 TQ_F32, TQ_BF16, TQ_F16 = 0, 1, 2
+TQ_STREAM_READ_SINK = 65536
 MODES = {"mse": TQ_MODE_MSE, "prod": TQ_MODE_PROD, "grouped": TQ_MODE_GROUPED, "grouped_prod": TQ_MODE_GROUPED_PROD}
 
 EXPORTED = ["tq_build_codebook", "tq_encode_keys", "tq_encode_keys_batched", "tq_encode_values", "tq_append_kv", "tq_decode_attention",
             "tq_decode_attention_noalloc", "tq_decode_attention_paged", "tq_dequantize_keys", "tq_dequantize_values", "tq_channel_moments",
-            "tq_select_outlier_channels", "tq_status_string", "tq_idx_row_bytes"]
+            "tq_select_outlier_channels", "tq_status_string", "tq_idx_row_bytes", "tq_stream_read"]
 
 
 class TqError(RuntimeError):
@@ -92,6 +93,8 @@ def _load():
     lib.tq_channel_moments.argtypes = [P, I32, I64, I64, I32, P, P, ctypes.POINTER(SZ), P]
     lib.tq_select_outlier_channels.restype = I32
     lib.tq_select_outlier_channels.argtypes = [P, I32, I64, I64, I32, I32, P, P, ctypes.POINTER(SZ), P]
+    lib.tq_stream_read.restype = I32
+    lib.tq_stream_read.argtypes = [P, SZ, P, P]
     return lib
 
 

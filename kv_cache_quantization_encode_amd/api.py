@@ -9,8 +9,8 @@ import struct
 import numpy as np
 import torch
 
-from ._lib import (TQ_BF16, TQ_F16, TQ_F32, TQ_MODE_GROUPED, TQ_MODE_GROUPED_PROD, TQ_MODE_PROD, KeyBatch,
-                   KeyConfig, check,
+from ._lib import (TQ_BF16, TQ_F16, TQ_F32, TQ_MODE_GROUPED, TQ_MODE_GROUPED_PROD, TQ_MODE_PROD,
+                   TQ_STREAM_READ_SINK, KeyBatch, KeyConfig, check,
                    key_config, lib)
 
 _DT = {torch.float32: TQ_F32, torch.bfloat16: TQ_BF16, torch.float16: TQ_F16}
@@ -345,6 +345,17 @@ def channel_moments(x: torch.Tensor) -> torch.Tensor:
     check("tq_channel_moments", lib.tq_channel_moments(_ptr(x), _DT[x.dtype], n, x.stride(0), d, _ptr(out),
                                                        _ptr(ws), ctypes.byref(size), _stream()))
     return out
+
+
+def stream_read(src: torch.Tensor, sink: torch.Tensor) -> None:
+    """One nontemporal streaming pass over src's bytes (tq_stream_read), the
+    read-bandwidth reference the decode's roofline is set against; sink is a
+    device int32/uint32 tensor of TQ_STREAM_READ_SINK elements."""
+    if not src.is_cuda or not src.is_contiguous() or not sink.is_cuda or sink.numel() < TQ_STREAM_READ_SINK:
+        raise ValueError("stream_read: contiguous device src and a device sink of %d words" % TQ_STREAM_READ_SINK)
+    if sink.element_size() != 4:
+        raise ValueError("stream_read: sink must hold 32-bit words")
+    check("tq_stream_read", lib.tq_stream_read(_ptr(src), src.numel() * src.element_size(), _ptr(sink), _stream()))
 
 
 def select_outlier_channels(x: torch.Tensor, n_outlier: int = 64) -> torch.Tensor:

@@ -377,3 +377,15 @@ def test_select_outlier_channels_workspace_query_and_errors():
     big = ctypes.c_size_t(1 << 20)
     assert f(FAKE, L.TQ_BF16, 5000, 128, 128, 64, None, FAKE, ctypes.byref(big), None) == L.TQ_ERR_ARG   # perm
     assert f(None, L.TQ_BF16, 5000, 128, 128, 64, FAKE, FAKE, ctypes.byref(big), None) == L.TQ_ERR_ARG   # x
+
+
+def test_stream_read_rejects_bad_arguments():
+    """The read-bandwidth reference returns TQ_ERR_ARG before any launch for
+    a null source or sink, an empty or non-multiple-of-16 size."""
+    lib = L.lib
+    p = ctypes.c_void_p(0x1000)
+    assert lib.tq_stream_read(None, 16, p, None) == L.TQ_ERR_ARG
+    assert lib.tq_stream_read(p, 16, None, None) == L.TQ_ERR_ARG
+    assert lib.tq_stream_read(p, 0, p, None) == L.TQ_ERR_ARG
+    assert lib.tq_stream_read(p, 24, p, None) == L.TQ_ERR_ARG
+    assert lib.tq_stream_read(ctypes.c_void_p(0x1008), 32, p, None) == L.TQ_ERR_ARG
