@@ -150,6 +150,8 @@ struct Lds {
   float oo[3][QH];
   float abuf[2 * (NW / 2) * QH];
   int ksf[NW / 2];     // final value-scale exponent of each score wave
+  int prod[NW / 2];    // rounds the score wave of each pair has published
+  int cons[NW / 2];    // rounds the p.V wave of each pair has finished
   int pages[PAGE_CACHE];  // block-table entries of this workgroup's token range (paged cache)
 };
 
@@ -276,6 +278,23 @@ __device__ inline void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Pairwise hand-over through LDS counters: a release publishes this wave's
+// LDS writes (LDS only, so global loads in flight stay in flight); a wait
+// spins until the partner's counter reaches v.  Every wait of the protocol
+// ends (the partner only ever waits on rounds already finished); the spin is
+// also capped, so that a wait can never outlive the kernel.
+__device__ inline void pair_publish(int* c, int v) {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __hip_atomic_store(c, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ inline void pair_wait(int* c, int v) {
+  for (int spin = 0; spin < (1 << 22); ++spin) {
+    if (__hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= v) break;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // A value every lane holds alike, moved to a scalar register.
 __device__ inline float uniform(float v) { return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v))); }
 
@@ -371,9 +390,11 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
   // publish fp16 weights p*scale; p.V waves (second half) accumulate those
   // weights against the value codes one round later.  Wave pw of each half
   // owns tiles pw, pw + NS, pw + 2 NS, ...; a two-slot LDS ring carries the
-  // weights and the rescale factor from score wave pw to p.V wave pw, and one
-  // barrier per round separates producer and consumer.  Each wave loads its
-  // next tile's data one round ahead.
+  // weights and the rescale factor from score wave pw to p.V wave pw, and a
+  // pair of LDS counters orders producer and consumer.  No barrier holds the
+  // pairs in step, so the score waves' table-lookup phases drift apart and
+  // share the LDS instead of all contending for it at once.  Each wave loads
+  // its next tile's data one round ahead.
   constexpr int VROW = KD * VB / 8;  // bytes of a value-code row
   const bool scorer = wave < NS;
   const int pw = scorer ? wave : wave - NS;
@@ -506,6 +527,10 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
     cen[tid] = part < n_parts && k < (part ? lev1 : lev0) ? (part ? cent1 : cent0)[k] : 0.0f;
   }
   if (F::QJL && tid < QH) L.rng[F::NC - 1][tid] = 0.0f;
+  if (tid < NW / 2) {
+    L.prod[tid] = 0;
+    L.cons[tid] = 0;
+  }
   for (int i = tid; i < n_pages_wg; i += NT) {
     const int pg = a.block_table[(long long)b * a.max_blocks + lp0 + i];
     L.pages[i] = min(max(pg, 0), a.n_pages - 1);
@@ -731,8 +756,8 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
   float* red = (float*)smem;  // [NS][QH][2 + 4 + KD], over the tables once every wave is done
   constexpr int RS = 2 + 4 + KD;
   float* mine = red + pw * QH * RS;
-  // The two kinds of waves run separate loops with the same number of
-  // barriers (rounds + 1), so neither keeps the other's registers live.
+  // The two kinds of waves run separate loops (one barrier after each), so
+  // neither keeps the other's registers live.
   if (scorer) {
     float UU[F::NC][QH], OO[F::NC][QH];
 #pragma unroll
@@ -919,9 +944,11 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
       }
     };
     for (int r = 0; r <= rounds; ++r) {
+      if (r >= 2) pair_wait(&L.cons[pw], r - 1);  // slot r & 1 read by the p.V wave
       s_round(r, kd);
-      lds_barrier();
+      pair_publish(&L.prod[pw], r + 1);
     }
+    lds_barrier();  // every wave is done with the tables before the sums go over them
 #pragma unroll
     for (int hh = 0; hh < QH; ++hh) {
       const float ls = wave_sum(l_run[hh]);
@@ -998,13 +1025,16 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
       }
     };
     for (int r = 0; r <= rounds; r += 2) {
+      pair_wait(&L.prod[pw], r);
       pv_round(r, codes2, codes);
-      lds_barrier();
+      pair_publish(&L.cons[pw], r);
       if (r + 1 <= rounds) {
+        pair_wait(&L.prod[pw], r + 1);
         pv_round(r + 1, codes, codes2);
-        lds_barrier();
+        pair_publish(&L.cons[pw], r + 1);
       }
     }
+    lds_barrier();
     // Undo the placement: block beta holds, in units of 2^-24, the prefix
     // sum over the fields of its byte up to beta's, field f weighted by its
     // place value 2^(VB f); a channel's sum is the difference of consecutive
