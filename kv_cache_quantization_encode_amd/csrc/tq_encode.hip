@@ -444,10 +444,18 @@ __device__ __forceinline__ const KeyArgs& key_set(const KeyLaunch<KIND>& L, int 
 // inputs, which need more registers and would spill at three.
 constexpr bool grouped_mode(int mode) { return mode == TQ_MODE_GROUPED || mode == TQ_MODE_GROUPED_PROD; }
 constexpr bool qjl_mode(int mode) { return mode == TQ_MODE_PROD || mode == TQ_MODE_GROUPED_PROD; }
-constexpr int key_waves_per_simd(int mode, int dt) { return grouped_mode(mode) || dt == TQ_F32 ? 2 : 3; }
+constexpr int key_waves_per_simd(int mode, int dt) { return grouped_mode(mode) || dt == TQ_F32 ? 2 : qjl_mode(mode) ? 3 : 4; }
+// Waves per key-encoder block: eight for the MSE encoder of 16-bit keys (at
+// most 128 VGPRs, four waves per SIMD, two blocks per CU sharing the LDS of
+// two), four otherwise (LDS holds three blocks per CU).  Launches that mix key
+// and value blocks use four.
+constexpr int key_block_waves(int mode, int dt, int kind) {
+  return kind != KEYS_AND_VALUES && mode == TQ_MODE_MSE && dt != TQ_F32 ? 8 : 4;
+}
 
 template <int MODE, int DT, int KIND, int VB>
-__global__ __launch_bounds__(WAVES * 64, key_waves_per_simd(MODE, DT)) void encode_keys_kernel(KeyLaunch<KIND> L) {
+__global__ __launch_bounds__(key_block_waves(MODE, DT, KIND) * 64, key_waves_per_simd(MODE, DT)) void encode_keys_kernel(KeyLaunch<KIND> L) {
+  constexpr int WAVES = key_block_waves(MODE, DT, KIND);
   if constexpr (KIND == KEYS_AND_VALUES) {
     if ((int)blockIdx.x >= L.key_blocks) {
       encode_values_body<VB, DT>(L.v, blockIdx.x - L.key_blocks, gridDim.x - L.key_blocks);
@@ -946,8 +954,8 @@ tq_status key_args(const tq_key_config* cfg, const void* tables, const void* key
 // the MSE and grouped encoders (launches of 65536 keys are dominated by that
 // staging), eight the prod encoder (long launches, where more blocks in
 // flight keep the loads and the MFMA work overlapped).
-int key_blocks(const tq::Parts& P, int n_tiles, int cus) {
-  const long long want = ((long long)n_tiles + WAVES - 1) / WAVES;
+int key_blocks(const tq::Parts& P, int n_tiles, int cus, int kw) {
+  const long long want = ((long long)n_tiles + kw - 1) / kw;
   const long long cap = (long long)cus * (P.m > 0 ? 8 : 2);
   return (int)(want < cap ? want : cap);
 }
@@ -992,7 +1000,8 @@ extern "C" tq_status tq_encode_keys(const tq_key_config* cfg, const void* tables
   if (st != TQ_OK || empty) return st;
   const int cus = tq::cu_count();
   if (cus <= 0) return TQ_ERR_HIP;
-  const dim3 grid((unsigned)key_blocks(P, a.n_tiles, cus)), block(WAVES * 64);
+  const int kw = key_block_waves(P.mode, dtype, KEYS_ONE);
+  const dim3 grid((unsigned)key_blocks(P, a.n_tiles, cus, kw)), block(kw * 64);
   hipStream_t s = (hipStream_t)stream;
   const KeyLaunch<KEYS_ONE> L{a};
 #define TQ_LAUNCH_KEYS(M)                                                                                  \
@@ -1062,11 +1071,12 @@ extern "C" tq_status tq_encode_keys_batched(const tq_key_config* cfg, const tq_k
   // set (measured on MI355X: 28 sets of 65536 MSE keys, 0.188 -> 0.175 ms).
   const int n_tiles = b.e[0].n_tiles;
   int per = cus * (P.m > 0 ? 8 : 4) / n_batch;
-  const int want = (n_tiles + WAVES - 1) / WAVES;
+  const int kw = key_block_waves(P.mode, dtype, KEYS_BATCH);
+  const int want = (n_tiles + kw - 1) / kw;
   if (per > want) per = want;
   if (per < 1) per = 1;
   b.blocks_per_entry = per;
-  const dim3 grid((unsigned)(per * n_batch)), block(WAVES * 64);
+  const dim3 grid((unsigned)(per * n_batch)), block(kw * 64);
   hipStream_t s = (hipStream_t)stream;
 #define TQ_LAUNCH_KB(M)                                                                                     \
   do {                                                                                                      \
@@ -1100,12 +1110,13 @@ extern "C" tq_status tq_append_kv(const tq_key_config* cfg, const void* tables, 
   if (st != TQ_OK || empty) return st;
   const int cus = tq::cu_count();
   if (cus <= 0) return TQ_ERR_HIP;
-  const int kb = key_blocks(P, ka.n_tiles, cus);
+  const int kb = key_blocks(P, ka.n_tiles, cus, 4);
   const long long blocks = (long long)kb + grid_for(va.n_tiles, 4);
   const dim3 grid((unsigned)blocks), block(256);
   hipStream_t s = (hipStream_t)stream;
   const KeyLaunch<KEYS_AND_VALUES> L{ka, va, kb};
-  static_assert(WAVES * 64 == 256, "key and value blocks share one block size");
+  static_assert(key_block_waves(TQ_MODE_MSE, TQ_BF16, KEYS_AND_VALUES) * 64 == 256,
+                "key and value blocks share one block size");
 #define TQ_LAUNCH_KV(M, B)                                                                                     \
   do {                                                                                                         \
     if (dtype == TQ_F32) hipLaunchKernelGGL((encode_keys_kernel<M, TQ_F32, KEYS_AND_VALUES, B>), grid, block, 0, s, L);      \
