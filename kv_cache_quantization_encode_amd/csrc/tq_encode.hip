@@ -531,6 +531,39 @@ __global__ __launch_bounds__(key_block_waves(MODE, DT, KIND) * 64, key_waves_per
     sg[2 * c] = sp[0];
     sg[2 * c + 1] = sp[1];
   }
+  // The other staged tables (rows of S, centroids, sigma for the transform's
+  // A fragments) are read into registers here, all at once, and written to
+  // LDS further down: a launch of a few tiles per block (an append) waits on
+  // this staging, so it is one round of global reads rather than a chain.
+  constexpr int NT = WAVES * 64;
+  static_assert(MAX_LEVELS <= NT, "one centroid per thread");
+  constexpr int S_PER_THREAD = KD * KD / 8 / NT;
+  uint4 srow[QJL ? S_PER_THREAD : 1];
+  float cv[NP];
+  if constexpr (QJL) {
+    const uint4* S = (const uint4*)(a.tables + H->off_S);
+#pragma unroll
+    for (int k = 0; k < S_PER_THREAD; ++k) srow[k] = S[threadIdx.x + k * NT];
+    // at most MAX_LEVELS (<= NT) centroids per part: one per thread
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const float* c = (const float*)(a.tables + H->off_centroids[p]);
+      cv[p] = (int)threadIdx.x < min(H->part_levels[p], MAX_LEVELS) ? c[threadIdx.x] : 0.0f;
+    }
+  }
+  constexpr int H_PER_THREAD = 4 * 2 * 64 * 8 / NT;
+  float svh[MF ? H_PER_THREAD : 1];
+  if constexpr (MF) {
+#pragma unroll
+    for (int m = 0; m < H_PER_THREAD; ++m) {
+      const int i = threadIdx.x + m * NT;
+      const int c = i >> 10, ln = (i >> 3) & 63, e = i & 7;
+      const int k = 8 * (ln >> 4) + e;
+      const int part = GRP ? c >> 1 : 0;
+      const int j = GRP ? 32 * (c & 1) + k : 32 * c + k;  // coordinate within the part
+      svh[m] = ((const float*)(a.tables + H->off_sigma[part]))[j];
+    }
+  }
   int hn[NP];
   float hlo[NP], hsc[NP];
   for (int p = 0; p < NP; ++p) {
@@ -552,36 +585,27 @@ __global__ __launch_bounds__(key_block_waves(MODE, DT, KIND) * 64, key_waves_per
       }
     }
   }
-  if (QJL) {
-    for (int p = 0; p < NP; ++p) {
-      const float* c = (const float*)(a.tables + H->off_centroids[p]);
-      for (int i = threadIdx.x; i < H->part_levels[p]; i += blockDim.x) s_cent[p * MAX_LEVELS + i] = c[i];
-    }
+  if constexpr (QJL) {
+#pragma unroll
+    for (int p = 0; p < NP; ++p)
+      if ((int)threadIdx.x < min(H->part_levels[p], MAX_LEVELS)) s_cent[p * MAX_LEVELS + threadIdx.x] = cv[p];
     // S in LDS, rows padded to 136 halves so that the sixteen rows one MFMA
     // fragment read touches fall in distinct banks.  Fragment (nt, ks) of lane
     // (kk, g): row 16 nt + kk, coordinates 32 g + 8 ks .. + 7 (float32 path)
     // or 32 ks + 8 g .. + 7 (MFMA path), matching the B = R^T layout after
     // the transform.
-    // (all of a thread's reads are issued before its LDS writes)
-    const uint4* S = (const uint4*)(a.tables + H->off_S);
-    constexpr int PER_THREAD = KD * KD / 8 / (WAVES * 64);
-    uint4 srow[PER_THREAD];
 #pragma unroll
-    for (int k = 0; k < PER_THREAD; ++k) srow[k] = S[threadIdx.x + k * WAVES * 64];
-#pragma unroll
-    for (int k = 0; k < PER_THREAD; ++k) {
-      const int i = threadIdx.x + k * WAVES * 64;
+    for (int k = 0; k < S_PER_THREAD; ++k) {
+      const int i = threadIdx.x + k * NT;
       *(uint4*)(s_S + (i / (KD / 8)) * SPITCH + 8 * (i % (KD / 8))) = srow[k];
     }
   }
   if constexpr (MF) {
-    for (int i = threadIdx.x; i < 4 * 2 * 64 * 8; i += blockDim.x) {
-      const int c = i >> 10, mt = (i >> 9) & 1, ln = (i >> 3) & 63, e = i & 7;
-      const int k = 8 * (ln >> 4) + e;
-      const int part = GRP ? c >> 1 : 0;
-      const int j = GRP ? 32 * (c & 1) + k : 32 * c + k;  // coordinate within the part
-      const float sv = ((const float*)(a.tables + H->off_sigma[part]))[j];
-      s_H[i] = hadamard_entry(mt, ln & 15, k, sv, DT == TQ_BF16);
+#pragma unroll
+    for (int m = 0; m < H_PER_THREAD; ++m) {
+      const int i = threadIdx.x + m * NT;
+      const int mt = (i >> 9) & 1, ln = (i >> 3) & 63, e = i & 7;
+      s_H[i] = hadamard_entry(mt, ln & 15, 8 * (ln >> 4) + e, svh[m], DT == TQ_BF16);
     }
   }
   // sign mask: bit r set when sigma of the coordinate loaded into x[r] is -1
