@@ -43,6 +43,9 @@ B, HKV, HQ, CTX, D = 16, 8, 32, 32768, 128
 KEY_BYTES = 52      # 32 B index + 16 B signs + 2 B norm + 2 B residual norm
 VAL_BYTES = 48      # 32 B codes + 4 groups x (2 B scale + 2 B zero)
 DECODE_BYTES = B * HKV * CTX * (KEY_BYTES + VAL_BYTES)   # 419,430,400 B per decode
+# the appending decode reads the cache without the new token's record, the new
+# bf16 key and value rows, and writes that record: 65,536 B more per step
+STEP_BYTES = DECODE_BYTES + B * HKV * 2 * D * 2
 
 
 def parse():
@@ -53,6 +56,9 @@ def parse():
     ap.add_argument("--settle-seconds", type=float, default=0.5,
                     help="untimed steps after the warm-up, until the GPU clocks have settled")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--two-launch-step", action="store_true",
+                    help="append with tq_append_kv, then decode (two launches) instead of appending inside "
+                         "the decode launch; the timed call is then the decode alone")
     ap.add_argument("--no-encode-bench", action="store_true")
     ap.add_argument("--no-other-decodes", action="store_true",
                     help="skip the decode timings of the 128k needle and 16k grouped workloads")
@@ -117,7 +123,7 @@ def _pmc_means(path, counter):
 
 
 def write_traffic(fetch_csv, write_csv, copy_mib):
-    """HBM traffic of one tq_decode_attention call (decode_kernel +
+    """HBM traffic of one tq_decode_attention_append call (decode_kernel +
     merge_kernel) from FETCH_SIZE / WRITE_SIZE (KiB per dispatch), each scaled
     by the ratio of the true bytes of the calibration copy to what the same
     counter reports for it."""
@@ -138,8 +144,8 @@ def write_traffic(fetch_csv, write_csv, copy_mib):
            "copy_bytes": copy_bytes, "fetch_scale": f_scale, "write_scale": w_scale,
            "read_bytes_per_launch": rd, "write_bytes_per_launch": wr,
            "traffic_bytes_per_launch": rd + wr,
-           "algorithmic_bytes": DECODE_BYTES,
-           "traffic_over_algorithmic": (rd + wr) / DECODE_BYTES}
+           "algorithmic_bytes": STEP_BYTES,
+           "traffic_over_algorithmic": (rd + wr) / STEP_BYTES}
     p = os.path.join(ROOT, "profiles", "decode_gqa32k_traffic.json")
     with open(p, "w") as f:
         json.dump(rec, f, indent=1)
@@ -243,9 +249,15 @@ def main():
     out = torch.empty((B, HQ, D), dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
 
+    def call(i):
+        if args.two_launch_step:
+            dec(qs[i], ctx_len, kp, vp, out=out)
+        else:
+            dec(qs[i], ctx_len, kp, vp, out=out, k_new=new_k[i].view(B, HKV, D), v_new=new_v[i].view(B, HKV, D))
+
     if args.profile_decode:
         for i in range(args.profile_decode):
-            dec(qs[i % n_steps_total], ctx_len, kp, vp, out=out)
+            call(i % n_steps_total)
         torch.cuda.synchronize()
         print("profiled %d decode calls" % args.profile_decode, flush=True)
         if args.profile_copy:
@@ -263,10 +275,11 @@ def main():
         return
 
     def step(i, ev=None):
-        tq.append_kv(T, new_k[i], new_v[i], 2, kp, vp, slots=slots, n_records=n_rec)
+        if args.two_launch_step:
+            tq.append_kv(T, new_k[i], new_v[i], 2, kp, vp, slots=slots, n_records=n_rec)
         if ev is not None:
             ev[0].record()
-        dec(qs[i], ctx_len, kp, vp, out=out)
+        call(i)
         if ev is not None:
             ev[1].record()
 
@@ -297,7 +310,8 @@ def main():
     dec_ms_mean = sum(dec_ms) / len(dec_ms)
     dec_ms_median = dec_ms[len(dec_ms) // 2]
     value = B * CTX / (ms_per_step * 1e-3)
-    achieved = DECODE_BYTES / (dec_ms_mean * 1e-3) / 1e9
+    call_bytes = DECODE_BYTES if args.two_launch_step else STEP_BYTES
+    achieved = call_bytes / (dec_ms_mean * 1e-3) / 1e9
 
     extra = {}
     if not args.no_encode_bench:
@@ -326,11 +340,14 @@ def main():
         "data": "synthetic",
         "config": {"workload": "gqa-decode-32k", "sequences": B, "kv_heads": HKV, "q_heads": HQ,
                    "head_dim": D, "context": CTX, "keys": "prod 3-bit (2-bit index + QJL)",
-                   "values": "2-bit group 32", "step": "append-encode 128 K/V rows + decode"},
+                   "values": "2-bit group 32",
+                   "step": ("append-encode 128 K/V rows (tq_append_kv), then decode" if args.two_launch_step else
+                            "one launch: append-encode 128 K/V rows and decode (tq_decode_attention_append)")},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic,
-                     "kernel": "tq_decode_attention (decode_kernel + merge_kernel)",
-                     "algorithmic_bytes": DECODE_BYTES, "ms_mean": dec_ms_mean,
+                     "kernel": ("tq_decode_attention" if args.two_launch_step else "tq_decode_attention_append")
+                     + " (decode_kernel + merge_kernel)",
+                     "algorithmic_bytes": call_bytes, "ms_mean": dec_ms_mean,
                      "ms_median": dec_ms_median,
                      "achievable_copy_gbps": copy_gbps, "frac_of_copy": achieved / copy_gbps,
                      "achievable_read_gbps": read_gbps, "frac_of_read": achieved / read_gbps},

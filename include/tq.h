@@ -266,6 +266,42 @@ tq_status tq_decode_attention(const tq_key_config* cfg, const void* tables,
                               void* workspace, size_t* workspace_bytes, void* stream);
 
 /*
+ * tq_decode_attention_append -- one decode step that first appends the step's
+ * new token: for every sequence b with ctx_len[b] > 0 and every KV head h, the
+ * key k_new[b][h] and value v_new[b][h] become token t = ctx_len[b] - 1 of the
+ * cache (bit-packing article sec 五: the store appends each new token's packed
+ * record), and the step attends over tokens 0 .. t as tq_decode_attention
+ * does.  The key is encoded as tq_encode_keys encodes it ("tqlite" README
+ * 设计要点; difai.kr tutorial 算法概述: norm, random signs and Walsh-Hadamard
+ * rotation, Lloyd-Max index, for PROD the QJL signs of the residual and its
+ * norm), the value as tq_encode_values does (per 32-channel group, fp16 scale
+ * and zero); the records are stored at slot (b*Hkv + h)*max_ctx + t of the
+ * planes, which are therefore writable here.  Within this call token t is
+ * attended from its encoding: its score is computed in float32 from the
+ * record (not through the lookup tables) and its value is the record's
+ * dequantised value.  One launch does both, so the append costs no launch of
+ * its own.
+ *   k_new, v_new  [B][Hkv][d] of kv_dtype (TQ_F32, TQ_BF16, TQ_F16),
+ *              contiguous, aligned to their element size; both non-NULL.
+ *   other arguments as tq_decode_attention (same workspace size).
+ * Supported: the MSE and PROD formats tq_decode_attention supports
+ * (GROUPED and GROUPED_PROD return TQ_ERR_UNSUPPORTED), contiguous planes.
+ * Records of the appended tokens may differ from tq_encode_keys' where a
+ * rotated coordinate lies within float32 rounding of a codebook boundary or
+ * a projection within rounding of zero (each side's float32 arithmetic
+ * decides those ties); values are bit-identical.
+ */
+tq_status tq_decode_attention_append(const tq_key_config* cfg, const void* tables,
+                                     const void* q, int32_t q_dtype, int32_t B, int32_t Hq, int32_t Hkv,
+                                     const int32_t* ctx_len, int32_t max_ctx,
+                                     const void* k_new, const void* v_new, int32_t kv_dtype,
+                                     uint8_t* idx, uint8_t* signs, uint16_t* norm, uint16_t* rnorm,
+                                     int32_t v_bits, int32_t v_group,
+                                     uint8_t* v_codes, uint16_t* v_scale, uint16_t* v_zero,
+                                     float sm_scale, float* out, float* lse, float* scores,
+                                     void* workspace, size_t* workspace_bytes, void* stream);
+
+/*
  * tq_decode_attention_noalloc -- tq_decode_attention for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc).  Same arguments, results (bit for bit) and

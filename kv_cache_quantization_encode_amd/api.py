@@ -411,7 +411,11 @@ class Decoder:
         self.ws = torch.empty(max(self.ws_bytes, 16), dtype=torch.uint8, device=device)
 
     def __call__(self, q, ctx_len, kp: dict, vp: dict, sm_scale=None, out=None, lse=None,
-                 scores=None, block_table=None):
+                 scores=None, block_table=None, k_new=None, v_new=None):
+        """One decode step.  With k_new and v_new ([B, Hkv, d], one dtype of
+        float32 / bfloat16 / float16) the step first appends them as token
+        ctx_len[b] - 1 of each sequence (tq_decode_attention_append: encoded,
+        stored into the planes and attended, in the same launch)."""
         _on_device(q, "q", tuple(_DT), contiguous=True)
         _need(q.dim() == 3, "q must be [B, Hq, d]")
         B, Hq, d = q.shape
@@ -442,7 +446,19 @@ class Decoder:
         vals = (self.v_bits, 32, _ptr(vp["codes"]), _ptr(vp["scale"]), _ptr(vp["zero"]))
         tail = (ctypes.c_float(sm_scale), _ptr(out), _ptr(lse), _ptr(scores), _ptr(self.ws),
                 ctypes.byref(size), _stream())
-        if self.page_size is None:
+        if k_new is not None or v_new is not None:
+            _need(self.page_size is None, "appending inside the decode needs contiguous planes")
+            _need(block_table is None, "a contiguous decoder takes no block table")
+            for name, t in (("k_new", k_new), ("v_new", v_new)):
+                _on_device(t, name, tuple(_DT), contiguous=True)
+                _need(tuple(t.shape) == (B, self.Hkv, d), "%s must be [B, Hkv, d]" % name)
+            _need(k_new.dtype == v_new.dtype, "k_new and v_new must have one dtype")
+            st = lib.tq_decode_attention_append(ctypes.byref(self.tables.cfg), _ptr(self.tables.dev), _ptr(q),
+                                                _DT[q.dtype], B, Hq, self.Hkv, _ptr(ctx_len), self.max_ctx,
+                                                _ptr(k_new), _ptr(v_new), _DT[k_new.dtype],
+                                                *keys, *vals, *tail)
+            check("tq_decode_attention_append", st)
+        elif self.page_size is None:
             _need(block_table is None, "a contiguous decoder takes no block table")
             st = lib.tq_decode_attention(ctypes.byref(self.tables.cfg), _ptr(self.tables.dev), _ptr(q),
                                          _DT[q.dtype], B, Hq, self.Hkv, _ptr(ctx_len), self.max_ctx,
@@ -501,12 +517,12 @@ def decode_attention_noalloc(tables: Tables, q, ctx_len, kp: dict, vp: dict, v_b
 
 
 def decode_attention(tables: Tables, q, ctx_len, kp, vp, v_bits, max_ctx, sm_scale=None,
-                     with_lse=False, with_scores=False):
+                     with_lse=False, with_scores=False, k_new=None, v_new=None):
     B, Hq, d = q.shape
     Hkv = kp["idx"].shape[0] // (B * max_ctx)
     dec = Decoder(tables, B, Hq, Hkv, max_ctx, v_bits, q.dtype, q.device)
     lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device) if with_lse else None
     scores = torch.full((B, Hq, max_ctx), float("nan"), dtype=torch.float32, device=q.device) \
         if with_scores else None
-    out = dec(q, ctx_len, kp, vp, sm_scale, lse=lse, scores=scores)
+    out = dec(q, ctx_len, kp, vp, sm_scale, lse=lse, scores=scores, k_new=k_new, v_new=v_new)
     return out, lse, scores

@@ -62,6 +62,11 @@ constexpr int NT = NW * 64;       // threads per workgroup
 constexpr int NS = NW / 2;        // score waves (and p.V waves)
 constexpr int PAGE_CACHE = 512;   // block-table entries a workgroup keeps in LDS
 constexpr int TILE = 64;          // tokens per wave tile
+// Record of an appended token in LDS (dwords): index row, QJL sign row, fp16
+// norm, fp16 residual norm, four fp16 zeros, four fp16 scales, value codes.
+constexpr int NR_IDX = 0, NR_SIGN = 32, NR_NORM = 36, NR_RNORM = 37, NR_Z = 38, NR_S = 40, NR_CODE = 48;
+constexpr int NREC = 64;
+constexpr int KENC_WAVE = 8, VENC_WAVE = 9;  // waves that encode an appended key / value (idle then)
 constexpr int QH = 4;             // query heads per workgroup
 // A wave's weight slot holds the MFMA A operand of its tile's p.V: rows
 // m = 4 group + head, 64 tokens, fp16, as [chunk][token group kq][m][j] with
@@ -139,8 +144,12 @@ template <int MODE, int B0, int B1, int VB>
 struct Lds {
   using F = Fmt<MODE, B0, B1>;
   uint64_t lut[F::ENTRIES];
-  float qp[QH * KD];
+  float qp[(QH + 1) * KD];  // rotated queries, then (appending) the new key's residual
   float qs[QH * KD];
+  uint32_t nrec[NREC];     // appending: the new token's record (see NR_*)
+  unsigned char nb8[2 * KD];  // appending: its index and value-code fields, one per byte
+  float vhat[KD];          // appending: its dequantised value
+  float xnew[QH];          // appending: its score per head (log2 softmax units)
   uint32_t ring[F::RING_BYTES / 4];
   float cen[2 * CEN];
   float rng[3][QH];    // largest byte range of each class and head (float bits, atomicMax)
@@ -179,6 +188,19 @@ struct DecArgs {
   int max_blocks;
   int page_size;  // tokens per page, a multiple of TILE
   int n_pages;    // pages in the pool (block-table entries are clamped below it)
+  // appending (knew != NULL): token ctx_len[b] - 1 of every (b, KV head) is
+  // encoded from knew / vnew ([B][Hkv][KD], kv_dtype) inside this launch,
+  // attended from the encoding and stored into the planes below
+  const void* knew;
+  const void* vnew;
+  int kv_dtype;
+  uint8_t* w_idx;
+  uint8_t* w_signs;
+  uint16_t* w_norm;
+  uint16_t* w_rnorm;
+  uint8_t* w_vcodes;
+  uint16_t* w_vscale;
+  uint16_t* w_vzero;
 };
 
 // a query element as loaded: f32 bits, or bf16 / fp16 bits in the low half
@@ -382,7 +404,12 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
   // lengths outside [0, max_ctx] are clamped into it: no read leaves the sequence's records
   const int ctx = min(max(a.ctx_len[b], 0), a.max_ctx);
   const int t_begin = split * a.chunk;
-  const int t_end = min(ctx, t_begin + a.chunk);
+  // Appending (knew set): token tn = ctx - 1, the last of its split's range,
+  // is encoded in this launch.  The loop covers the range without it; it
+  // enters the workgroup's final combine as one more softmax term.
+  const int tn = a.knew && ctx > 0 ? ctx - 1 : -1;
+  const bool has_new = tn >= t_begin && tn < min(ctx, t_begin + a.chunk);
+  const int t_end = has_new ? tn : min(ctx, t_begin + a.chunk);
 
   const long long rec0 = ((long long)b * a.Hkv + hkv) * a.max_ctx;
   // ---- main loop, split between two kinds of waves.  Score waves (the first
@@ -536,6 +563,144 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
     L.pages[i] = min(max(pg, 0), a.n_pages - 1);
   }
 
+  // ---- appending: the workgroup whose range holds token tn encodes that
+  // token's key and value from knew / vnew (the key in wave KENC_WAVE, the
+  // value in VENC_WAVE, both idle until the first barrier).  The record goes
+  // to LDS; quad 0's workgroup stores it into the planes for later calls.
+  // Nothing in this launch reads it back from global memory: its score and
+  // value are taken from the encoding itself.
+  // Key ("tqlite" README 设计要点; difai.kr tutorial 算法概述): n = ||k||,
+  // y = H (sigma * k) / n, idx_j = number of boundaries <= y_j; PROD:
+  // r = y - c[idx], signs [S r >= 0] (S r on the MFMA below, as a fifth
+  // column next to the queries), rho = n ||r|| / sqrt(d).  Value
+  // (bit-packing article, sections 二/三): per 32-channel group
+  // s = fp16((max - min) / (2^VB - 1)), z = fp16(min),
+  // code = clamp(rint((v - z) / s), 0, 2^VB - 1) in float32, 0 when s = 0.
+  if constexpr (!F::GROUPED) {
+    if (has_new && wave == KENC_WAVE) {
+      const long long kr = ((long long)b * a.Hkv + hkv) * KD;
+      uint32_t w0, w1;
+      if (a.kv_dtype == TQ_F32) {
+        w0 = ((const uint32_t*)a.knew)[kr + lane];
+        w1 = ((const uint32_t*)a.knew)[kr + lane + 64];
+      } else {
+        w0 = ((const uint16_t*)a.knew)[kr + lane];
+        w1 = ((const uint16_t*)a.knew)[kr + lane + 64];
+      }
+      const float* sig = (const float*)(a.tables + H->off_sigma[0]);
+      const float* bnd = (const float*)(a.tables + H->off_bounds[0]);
+      const float sgk0 = sig[lane], sgk1 = sig[lane + 64];
+      const float bl = lane < lev0 - 1 ? bnd[lane] : INFINITY;  // boundary `lane`
+      float k0 = q_word_to_float(w0, a.kv_dtype), k1 = q_word_to_float(w1, a.kv_dtype);
+      // the sum of squares on the coordinates scaled by the power of two
+      // that brings the largest into [1, 2): no fp32 under- or overflow for
+      // finite keys; the norm is scaled back
+      const float kmax = wave_max(fmaxf(fabsf(k0), fabsf(k1)));
+      const int ke = kmax > 0.0f ? min(max(ilogbf(kmax), -126), 127) : 0;
+      k0 = ldexpf(k0, -ke);
+      k1 = ldexpf(k1, -ke);
+      const float ss = wave_sum(fmaf(k0, k0, k1 * k1));
+      const float inv_n = ss > 0.0f ? 1.0f / sqrtf(ss) : 0.0f;  // a zero key has y = 0
+      float y0 = k0 * sgk0, y1 = k1 * sgk1;
+      {
+        const float t = y0;
+        y0 = t + y1;
+        y1 = t - y1;
+      }
+      static_for<0, 6>([&](auto ii) {
+        constexpr int st = 32 >> decltype(ii)::value;
+        const float z0 = lane_xor<st>(y0, lane), z1 = lane_xor<st>(y1, lane);
+        const bool up = lane & st;
+        y0 = up ? z0 - y0 : y0 + z0;
+        y1 = up ? z1 - y1 : y1 + z1;
+      });
+      y0 *= inv_n;
+      y1 *= inv_n;
+      int i0 = 0, i1 = 0;
+      for (int t = 0; t < lev0 - 1; ++t) {
+        const float bt = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bl), t));
+        i0 += y0 >= bt ? 1 : 0;
+        i1 += y1 >= bt ? 1 : 0;
+      }
+      L.nb8[lane] = (unsigned char)i0;
+      L.nb8[lane + 64] = (unsigned char)i1;
+      const float nrm = ldexpf(sqrtf(ss), ke);
+      float rho = 0.0f;
+      if constexpr (F::QJL) {
+        const float r0 = y0 - cent0[i0], r1 = y1 - cent0[i1];
+        qp[QH * KD + lane] = r0;
+        qp[QH * KD + lane + 64] = r1;
+        const float rr = wave_sum(fmaf(r0, r0, r1 * r1));
+        rho = ldexpf(sqrtf(ss) * sqrtf(rr) * 0.088388347648318441f, ke);  // n ||r|| / sqrt(128)
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+      if (lane < F::IDXB / 4) {
+        constexpr int W = F::W0, PER = 32 / W;
+        uint32_t v = 0;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) v |= (uint32_t)L.nb8[lane * PER + i] << (W * i);
+        L.nrec[NR_IDX + lane] = v;
+      }
+      if (lane == 0) {
+        L.nrec[NR_NORM] = __half_as_ushort(__float2half_rn(nrm));
+        L.nrec[NR_RNORM] = __half_as_ushort(__float2half_rn(rho));
+      }
+    }
+    if (has_new && wave == VENC_WAVE) {
+      const long long vr = ((long long)b * a.Hkv + hkv) * KD;
+      uint32_t w0, w1;
+      if (a.kv_dtype == TQ_F32) {
+        w0 = ((const uint32_t*)a.vnew)[vr + lane];
+        w1 = ((const uint32_t*)a.vnew)[vr + lane + 64];
+      } else {
+        w0 = ((const uint16_t*)a.vnew)[vr + lane];
+        w1 = ((const uint16_t*)a.vnew)[vr + lane + 64];
+      }
+      // channel lane is in group lane / 32, channel lane + 64 in 2 + lane / 32
+      const float v0 = q_word_to_float(w0, a.kv_dtype), v1 = q_word_to_float(w1, a.kv_dtype);
+      float mn0 = v0, mx0 = v0, mn1 = v1, mx1 = v1;
+#pragma unroll
+      for (int m = 1; m < 32; m <<= 1) {
+        mn0 = fminf(mn0, __shfl_xor(mn0, m));
+        mx0 = fmaxf(mx0, __shfl_xor(mx0, m));
+        mn1 = fminf(mn1, __shfl_xor(mn1, m));
+        mx1 = fmaxf(mx1, __shfl_xor(mx1, m));
+      }
+      constexpr float LV = (float)((1 << VB) - 1);
+      const __half s0h = __float2half_rn(__fdiv_rn(mx0 - mn0, LV)), s1h = __float2half_rn(__fdiv_rn(mx1 - mn1, LV));
+      const __half z0h = __float2half_rn(mn0), z1h = __float2half_rn(mn1);
+      const float s0 = __half2float(s0h), s1 = __half2float(s1h);
+      const float z0 = __half2float(z0h), z1 = __half2float(z1h);
+      const int c0 = s0 == 0.0f ? 0 : (int)fminf(fmaxf(rintf(__fdiv_rn(v0 - z0, s0)), 0.0f), LV);
+      const int c1 = s1 == 0.0f ? 0 : (int)fminf(fmaxf(rintf(__fdiv_rn(v1 - z1, s1)), 0.0f), LV);
+      L.nb8[KD + lane] = (unsigned char)c0;
+      L.nb8[KD + lane + 64] = (unsigned char)c1;
+      L.vhat[lane] = fmaf((float)c0, s0, z0);  // the value as the cache holds it
+      L.vhat[lane + 64] = fmaf((float)c1, s1, z1);
+      if ((lane & 31) == 0) {
+        const int g = lane >> 5;
+        uint16_t* zz = (uint16_t*)&L.nrec[NR_Z];
+        uint16_t* sz = (uint16_t*)&L.nrec[NR_S];
+        zz[g] = __half_as_ushort(z0h);
+        zz[2 + g] = __half_as_ushort(z1h);
+        sz[g] = __half_as_ushort(s0h);
+        sz[2 + g] = __half_as_ushort(s1h);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+      if (lane < VROW / 4) {
+        constexpr int PER = 32 / VB;
+        uint32_t v = 0;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) v |= (uint32_t)L.nb8[KD + lane * PER + i] << (VB * i);
+        L.nrec[NR_CODE + lane] = v;
+      }
+    }
+  }
+
   // Walsh-Hadamard transform of sigma * q in registers (one 128-point
   // transform, or two 64-point ones for GROUPED): butterflies on lane bits
   // through shuffles, the top stage inside the lane.  Then, per index class,
@@ -607,7 +772,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         half8_t bh = {}, bl = {};
-        if (n < QH) {
+        if (n < QH || (n == QH && has_new)) {
           const float4* src = (const float4*)(qp + n * KD + 32 * ks + 8 * (lane >> 4));
           const float4 v0 = src[0], v1 = src[1];
           const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
@@ -626,6 +791,18 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) qs[n * KD + 16 * wave + 4 * (lane >> 4) + i] = acc[i];
       }
+      if (has_new) {
+        // the appended key's sign bits: column QH, rows 16 wave + 4 g + i in
+        // lane 16 g + QH; bit 4 g + i of the wave's two sign bytes
+        uint32_t bits16 = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint64_t bm = __builtin_amdgcn_ballot_w64(acc[i] >= 0.0f);
+#pragma unroll
+          for (int g = 0; g < 4; ++g) bits16 |= (uint32_t)((bm >> (16 * g + QH)) & 1u) << (4 * g + i);
+        }
+        if (lane == 0) ((uint16_t*)&L.nrec[NR_SIGN])[wave] = (uint16_t)bits16;
+      }
       // sign bytes 2 wave (lanes 0..31) and 2 wave + 1 (lanes 32..63): a
       // byte's values are sum_i +-(S q')_i over its 8 rows, range 2 sum |.|
       float v = fabsf(acc[0]) + fabsf(acc[1]) + fabsf(acc[2]) + fabsf(acc[3]);
@@ -638,6 +815,48 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
       }
     }
     lds_barrier();
+  }
+  // the appended record (complete in LDS now) into the planes, by quad 0
+  if (has_new && quad == 0 && wave == KENC_WAVE) {
+    const long long rec = tile_base(tn) + tn;
+    if (lane < F::IDXB / 4) ((uint32_t*)(a.w_idx + rec * F::IDXB))[lane] = L.nrec[NR_IDX + lane];
+    if (F::QJL && lane >= NR_SIGN && lane < NR_SIGN + 4)
+      ((uint32_t*)(a.w_signs + rec * (KD / 8)))[lane - NR_SIGN] = L.nrec[lane];
+    if (lane == NR_NORM) a.w_norm[rec] = (uint16_t)L.nrec[NR_NORM];
+    if (F::QJL && lane == NR_RNORM) a.w_rnorm[rec] = (uint16_t)L.nrec[NR_RNORM];
+    if (lane == NR_Z || lane == NR_Z + 1) ((uint32_t*)(a.w_vzero + rec * 4))[lane - NR_Z] = L.nrec[lane];
+    if (lane == NR_S || lane == NR_S + 1) ((uint32_t*)(a.w_vscale + rec * 4))[lane - NR_S] = L.nrec[lane];
+    if (lane >= NR_CODE && lane < NR_CODE + VROW / 4) ((uint32_t*)(a.w_vcodes + rec * VROW))[lane - NR_CODE] = L.nrec[lane];
+  }
+  if constexpr (!F::GROUPED) {
+    if (has_new && wave == KENC_WAVE) {
+      // the appended token's score from its record, in float32:
+      // <q, k_hat> = (n / PD) sum_j q'_j c[idx_j]
+      //            + rho sqrt(pi/2) / (m sqrt(PD)) sum_i (S q')_i (2 bit_i - 1)
+      // with the stored fp16 norms (what a later call reads back)
+      const float n16 = h2f(L.nrec[NR_NORM]), r16 = h2f(L.nrec[NR_RNORM]);
+      const float c0 = cen[L.nb8[lane]], c1 = cen[L.nb8[lane + 64]];
+      float sg0 = 0.0f, sg1 = 0.0f;
+      if constexpr (F::QJL) {
+        sg0 = (L.nrec[NR_SIGN + (lane >> 5)] >> (lane & 31)) & 1u ? 1.0f : -1.0f;
+        sg1 = (L.nrec[NR_SIGN + 2 + (lane >> 5)] >> (lane & 31)) & 1u ? 1.0f : -1.0f;
+      }
+      const float xs = a.sm_scale * LOG2E;
+#pragma unroll
+      for (int hh = 0; hh < QH; ++hh) {
+        const float di = wave_sum(fmaf(qp[hh * KD + lane], c0, qp[hh * KD + lane + 64] * c1));
+        float dot = n16 / (float)F::PD * di;
+        if constexpr (F::QJL) {
+          const float ds = wave_sum(fmaf(qs[hh * KD + lane], sg0, qs[hh * KD + lane + 64] * sg1));
+          dot = fmaf(r16 * (SQRT_HALF_PI / ((float)KD * sqrtf((float)F::PD))), ds, dot);
+        }
+        if (lane == 0) {
+          L.xnew[hh] = dot * xs;
+          const int gq = QH * quad + hh;
+          if (a.scores && gq < a.G) a.scores[((long long)b * a.Hq + hkv * a.G + gq) * a.max_ctx + tn] = dot;
+        }
+      }
+    }
   }
   // Half tables: for each byte position, nibble half and nibble value, the
   // four heads' partial sums over the coordinates (or sign rows) that nibble
@@ -1062,6 +1281,8 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
     const int gq = QH * quad + hh;
     float M = -INFINITY;
     for (int w = 0; w < NS; ++w) M = fmaxf(M, red[(w * QH + hh) * RS]);
+    const float xn = has_new ? L.xnew[hh] : -INFINITY;  // the appended token (weight 2^PSCALE at its own max)
+    M = fmaxf(M, xn);
     float Ls = 0.0f, O = 0.0f;
     if (M != -INFINITY) {
       for (int w = 0; w < NS; ++w) {
@@ -1069,6 +1290,11 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
         const float f = rr[0] == -INFINITY ? 0.0f : exp2f(rr[0] - M);
         Ls = fmaf(rr[1], f, Ls);
         O = fmaf(fmaf(rr[6 + j], ldexpf(1.0f, -L.ksf[w]), rr[2 + j / 32]), f, O);
+      }
+      if (has_new) {
+        const float f = exp2f(xn - (M - PSCALE));
+        Ls += f;
+        O = fmaf(L.vhat[j], f, O);
       }
     }
     if (gq < a.G) {
@@ -1176,7 +1402,8 @@ tq_status decode_impl(const tq_key_config* cfg, const void* tables, const void* 
                       const uint16_t* rnorm, int32_t v_bits, int32_t v_group, const uint8_t* v_codes,
                       const uint16_t* v_scale, const uint16_t* v_zero, float sm_scale, float* out,
                       float* lse, float* scores, void* workspace, size_t* workspace_bytes,
-                      void* stream) {
+                      void* stream, const void* k_new = nullptr, const void* v_new = nullptr,
+                      int32_t kv_dtype = TQ_F32) {
   tq::Parts P;
   tq_status st = tq::describe(cfg, &P);
   if (st != TQ_OK) return st;
@@ -1224,6 +1451,13 @@ tq_status decode_impl(const tq_key_config* cfg, const void* tables, const void* 
       ((uintptr_t)out & 3))
     return TQ_ERR_ARG;
   if (max_ctx > 0x7fffffff / 2) return TQ_ERR_ARG;
+  if (k_new || v_new) {
+    if (!k_new || !v_new) return TQ_ERR_ARG;
+    if (P.mode != TQ_MODE_MSE && P.mode != TQ_MODE_PROD) return TQ_ERR_UNSUPPORTED;
+    if (kv_dtype != TQ_F32 && kv_dtype != TQ_BF16 && kv_dtype != TQ_F16) return TQ_ERR_ARG;
+    const uintptr_t al = kv_dtype == TQ_F32 ? 3 : 1;
+    if (((uintptr_t)k_new & al) || ((uintptr_t)v_new & al)) return TQ_ERR_ARG;
+  }
 
   DecArgs a;
   a.tables = (const unsigned char*)tables;
@@ -1252,6 +1486,17 @@ tq_status decode_impl(const tq_key_config* cfg, const void* tables, const void* 
   a.max_blocks = max_blocks;
   a.page_size = page_size;
   a.n_pages = n_pages;
+  a.knew = k_new;
+  a.vnew = v_new;
+  a.kv_dtype = kv_dtype;
+  // appending stores the new records into the planes the decode reads
+  a.w_idx = const_cast<uint8_t*>(idx);
+  a.w_signs = const_cast<uint8_t*>(signs);
+  a.w_norm = const_cast<uint16_t*>(norm);
+  a.w_rnorm = const_cast<uint16_t*>(rnorm);
+  a.w_vcodes = const_cast<uint8_t*>(v_codes);
+  a.w_vscale = const_cast<uint16_t*>(v_scale);
+  a.w_vzero = const_cast<uint16_t*>(v_zero);
   hipStream_t s = (hipStream_t)stream;
   const dim3 grid(n_split, n_quads, B * Hkv);
   if (dispatch(P, v_bits, a, grid, s) != hipSuccess) return TQ_ERR_HIP;
@@ -1354,4 +1599,19 @@ extern "C" tq_status tq_decode_attention_paged(
                      block_table, max_blocks_per_seq, page_size, n_pages, idx, signs, norm, rnorm, v_bits, v_group,
                      v_codes, v_scale, v_zero, sm_scale, out, lse, scores, workspace, workspace_bytes,
                      stream);
+}
+
+extern "C" tq_status tq_decode_attention_append(const tq_key_config* cfg, const void* tables, const void* q,
+                                               int32_t q_dtype, int32_t B, int32_t Hq, int32_t Hkv,
+                                               const int32_t* ctx_len, int32_t max_ctx, const void* k_new,
+                                               const void* v_new, int32_t kv_dtype, uint8_t* idx,
+                                               uint8_t* signs, uint16_t* norm, uint16_t* rnorm,
+                                               int32_t v_bits, int32_t v_group, uint8_t* v_codes,
+                                               uint16_t* v_scale, uint16_t* v_zero, float sm_scale,
+                                               float* out, float* lse, float* scores, void* workspace,
+                                               size_t* workspace_bytes, void* stream) {
+  if (workspace && (!k_new || !v_new)) return TQ_ERR_ARG;
+  return decode_impl(cfg, tables, q, q_dtype, B, Hq, Hkv, ctx_len, max_ctx, nullptr, 0, 0, 0, idx, signs,
+                     norm, rnorm, v_bits, v_group, v_codes, v_scale, v_zero, sm_scale, out, lse, scores,
+                     workspace, workspace_bytes, stream, k_new, v_new, kv_dtype);
 }
