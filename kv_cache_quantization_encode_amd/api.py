@@ -416,6 +416,15 @@ class Decoder:
         float32 / bfloat16 / float16) the step first appends them as token
         ctx_len[b] - 1 of each sequence (tq_decode_attention_append: encoded,
         stored into the planes and attended, in the same launch)."""
+        return self.bind(q, ctx_len, kp, vp, sm_scale, out, lse, scores, block_table, k_new, v_new)()
+
+    def bind(self, q, ctx_len, kp: dict, vp: dict, sm_scale=None, out=None, lse=None,
+             scores=None, block_table=None, k_new=None, v_new=None):
+        """Checks the arguments of one decode step (as __call__ takes them) once
+        and returns a function of no arguments that enqueues that step on the
+        stream current now, on the same tensors, and returns out: for loops
+        that repeat a step without paying the checks each time.  The tensors
+        must stay alive and in place while the function is used."""
         _on_device(q, "q", tuple(_DT), contiguous=True)
         _need(q.dim() == 3, "q must be [B, Hq, d]")
         B, Hq, d = q.shape
@@ -453,17 +462,14 @@ class Decoder:
                 _on_device(t, name, tuple(_DT), contiguous=True)
                 _need(tuple(t.shape) == (B, self.Hkv, d), "%s must be [B, Hkv, d]" % name)
             _need(k_new.dtype == v_new.dtype, "k_new and v_new must have one dtype")
-            st = lib.tq_decode_attention_append(ctypes.byref(self.tables.cfg), _ptr(self.tables.dev), _ptr(q),
-                                                _DT[q.dtype], B, Hq, self.Hkv, _ptr(ctx_len), self.max_ctx,
-                                                _ptr(k_new), _ptr(v_new), _DT[k_new.dtype],
-                                                *keys, *vals, *tail)
-            check("tq_decode_attention_append", st)
+            name, fn = "tq_decode_attention_append", lib.tq_decode_attention_append
+            args = (ctypes.byref(self.tables.cfg), _ptr(self.tables.dev), _ptr(q), _DT[q.dtype], B, Hq, self.Hkv,
+                    _ptr(ctx_len), self.max_ctx, _ptr(k_new), _ptr(v_new), _DT[k_new.dtype], *keys, *vals, *tail)
         elif self.page_size is None:
             _need(block_table is None, "a contiguous decoder takes no block table")
-            st = lib.tq_decode_attention(ctypes.byref(self.tables.cfg), _ptr(self.tables.dev), _ptr(q),
-                                         _DT[q.dtype], B, Hq, self.Hkv, _ptr(ctx_len), self.max_ctx,
-                                         *keys, *vals, *tail)
-            check("tq_decode_attention", st)
+            name, fn = "tq_decode_attention", lib.tq_decode_attention
+            args = (ctypes.byref(self.tables.cfg), _ptr(self.tables.dev), _ptr(q), _DT[q.dtype], B, Hq, self.Hkv,
+                    _ptr(ctx_len), self.max_ctx, *keys, *vals, *tail)
         else:
             nb = self.max_ctx // self.page_size
             _need(block_table is not None, "a paged decoder needs the block table")
@@ -472,11 +478,14 @@ class Decoder:
             # pages of the pool: the planes' records over the records of one page
             n_pages = n_rec // (self.Hkv * self.page_size)
             _need(n_pages > 0, "the planes hold less than one page")
-            st = lib.tq_decode_attention_paged(ctypes.byref(self.tables.cfg), _ptr(self.tables.dev), _ptr(q),
-                                               _DT[q.dtype], B, Hq, self.Hkv, _ptr(ctx_len), _ptr(block_table),
-                                               nb, self.page_size, n_pages, *keys, *vals, *tail)
-            check("tq_decode_attention_paged", st)
-        return out
+            name, fn = "tq_decode_attention_paged", lib.tq_decode_attention_paged
+            args = (ctypes.byref(self.tables.cfg), _ptr(self.tables.dev), _ptr(q), _DT[q.dtype], B, Hq, self.Hkv,
+                    _ptr(ctx_len), _ptr(block_table), nb, self.page_size, n_pages, *keys, *vals, *tail)
+
+        def run():
+            check(name, fn(*args))
+            return out
+        return run
 
 
 def decode_attention_noalloc(tables: Tables, q, ctx_len, kp: dict, vp: dict, v_bits: int, max_ctx: int,

@@ -68,6 +68,8 @@ constexpr int NR_IDX = 0, NR_SIGN = 32, NR_NORM = 36, NR_RNORM = 37, NR_Z = 38, 
 constexpr int NREC = 64;
 constexpr int KENC_WAVE = 8, VENC_WAVE = 9;  // waves that encode an appended key / value (idle then)
 constexpr int QH = 4;             // query heads per workgroup
+static_assert(KENC_WAVE >= 8 && VENC_WAVE >= 8 && KENC_WAVE + QH <= NW && VENC_WAVE < NW,
+              "the encoding waves are neither the S q' MFMA waves nor past the workgroup");
 // A wave's weight slot holds the MFMA A operand of its tile's p.V: rows
 // m = 4 group + head, 64 tokens, fp16, as [chunk][token group kq][m][j] with
 // token 32 chunk + 4 j + kq; each (chunk, kq) block is padded by 16 halves so
@@ -591,6 +593,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
       const float* bnd = (const float*)(a.tables + H->off_bounds[0]);
       const float sgk0 = sig[lane], sgk1 = sig[lane + 64];
       const float bl = lane < lev0 - 1 ? bnd[lane] : INFINITY;  // boundary `lane`
+      const float cl = lane < lev0 ? cent0[lane] : 0.0f;        // centroid `lane` (gathered by shuffle below)
       float k0 = q_word_to_float(w0, a.kv_dtype), k1 = q_word_to_float(w1, a.kv_dtype);
       // the sum of squares on the coordinates scaled by the power of two
       // that brings the largest into [1, 2): no fp32 under- or overflow for
@@ -627,7 +630,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
       const float nrm = ldexpf(sqrtf(ss), ke);
       float rho = 0.0f;
       if constexpr (F::QJL) {
-        const float r0 = y0 - cent0[i0], r1 = y1 - cent0[i1];
+        const float r0 = y0 - __shfl(cl, i0), r1 = y1 - __shfl(cl, i1);
         qp[QH * KD + lane] = r0;
         qp[QH * KD + lane + 64] = r1;
         const float rr = wave_sum(fmaf(r0, r0, r1 * r1));
@@ -829,32 +832,27 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
     if (lane >= NR_CODE && lane < NR_CODE + VROW / 4) ((uint32_t*)(a.w_vcodes + rec * VROW))[lane - NR_CODE] = L.nrec[lane];
   }
   if constexpr (!F::GROUPED) {
-    if (has_new && wave == KENC_WAVE) {
-      // the appended token's score from its record, in float32:
+    if (has_new && wave >= KENC_WAVE && wave < KENC_WAVE + QH) {
+      // the appended token's score for head hh = wave - KENC_WAVE, from its
+      // record, in float32:
       // <q, k_hat> = (n / PD) sum_j q'_j c[idx_j]
       //            + rho sqrt(pi/2) / (m sqrt(PD)) sum_i (S q')_i (2 bit_i - 1)
       // with the stored fp16 norms (what a later call reads back)
+      const int hh = wave - KENC_WAVE;
       const float n16 = h2f(L.nrec[NR_NORM]), r16 = h2f(L.nrec[NR_RNORM]);
       const float c0 = cen[L.nb8[lane]], c1 = cen[L.nb8[lane + 64]];
-      float sg0 = 0.0f, sg1 = 0.0f;
+      const float di = wave_sum(fmaf(qp[hh * KD + lane], c0, qp[hh * KD + lane + 64] * c1));
+      float dot = n16 / (float)F::PD * di;
       if constexpr (F::QJL) {
-        sg0 = (L.nrec[NR_SIGN + (lane >> 5)] >> (lane & 31)) & 1u ? 1.0f : -1.0f;
-        sg1 = (L.nrec[NR_SIGN + 2 + (lane >> 5)] >> (lane & 31)) & 1u ? 1.0f : -1.0f;
+        const float sg0 = (L.nrec[NR_SIGN + (lane >> 5)] >> (lane & 31)) & 1u ? 1.0f : -1.0f;
+        const float sg1 = (L.nrec[NR_SIGN + 2 + (lane >> 5)] >> (lane & 31)) & 1u ? 1.0f : -1.0f;
+        const float ds = wave_sum(fmaf(qs[hh * KD + lane], sg0, qs[hh * KD + lane + 64] * sg1));
+        dot = fmaf(r16 * (SQRT_HALF_PI / ((float)KD * sqrtf((float)F::PD))), ds, dot);
       }
-      const float xs = a.sm_scale * LOG2E;
-#pragma unroll
-      for (int hh = 0; hh < QH; ++hh) {
-        const float di = wave_sum(fmaf(qp[hh * KD + lane], c0, qp[hh * KD + lane + 64] * c1));
-        float dot = n16 / (float)F::PD * di;
-        if constexpr (F::QJL) {
-          const float ds = wave_sum(fmaf(qs[hh * KD + lane], sg0, qs[hh * KD + lane + 64] * sg1));
-          dot = fmaf(r16 * (SQRT_HALF_PI / ((float)KD * sqrtf((float)F::PD))), ds, dot);
-        }
-        if (lane == 0) {
-          L.xnew[hh] = dot * xs;
-          const int gq = QH * quad + hh;
-          if (a.scores && gq < a.G) a.scores[((long long)b * a.Hq + hkv * a.G + gq) * a.max_ctx + tn] = dot;
-        }
+      if (lane == 0) {
+        L.xnew[hh] = dot * (a.sm_scale * LOG2E);
+        const int gq = QH * quad + hh;
+        if (a.scores && gq < a.G) a.scores[((long long)b * a.Hq + hkv * a.G + gq) * a.max_ctx + tn] = dot;
       }
     }
   }
