@@ -122,6 +122,58 @@ def test_gqa_decode_32k_full_size():
                       [(0, 0), (2, 5), (6, 3), (9, 1), (11, 6), (15, 7)], "gqa-decode-32k")
 
 
+def test_gqa_decode_32k_append_step_full_size():
+    """The benchmark's step at full size: one tq_decode_attention_append call
+    over 16 x 8 KV heads x 32 query heads at context 32768 that appends token
+    32767 of every (sequence, KV head).  All 128 appended records against the
+    oracle's encoding of the new rows; on sampled groups, the scores (the new
+    token's included), outputs and lse against the oracle's attention over the
+    dequantised records the planes hold after the call."""
+    B, Hkv, Hq, ctx = 16, 8, 32, 32768
+    G = Hq // Hkv
+    n = B * Hkv * ctx
+    keys = W.normal_bf16_device(3, 1, (n, D), DEV)
+    vals = W.normal_bf16_device(3, 2, (n, D), DEV)
+    k_new = W.normal_bf16_device(3, 6, (1, B * Hkv, D), DEV)[0].contiguous()
+    v_new = W.normal_bf16_device(3, 7, (1, B * Hkv, D), DEV)[0].contiguous()
+    q = W.normal_bf16_device(3, 3, (1, B, Hq, D), DEV)[0].contiguous()
+    kw = dict(mode="prod", bits=3)
+    Tg = tq.Tables(L.key_config(seed=42, **kw), DEV)
+    To = O.build_tables(O.KeyConfig(d=D, seed=42, mode="prod", bits=3))
+    kp = tq.encode_keys(Tg, keys)
+    vp = tq.encode_values(vals, 2)
+    del keys, vals
+    ctx_t = torch.full((B,), ctx, dtype=torch.int32, device=DEV)
+    dec = tq.Decoder(Tg, B, Hq, Hkv, ctx, 2, q.dtype, DEV)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=DEV)
+    scores = torch.full((B, Hq, ctx), float("nan"), dtype=torch.float32, device=DEV)
+    out = dec(q, ctx_t, kp, vp, lse=lse, scores=scores, k_new=k_new.view(B, Hkv, D), v_new=v_new.view(B, Hkv, D))
+    torch.cuda.synchronize()
+    out, lse = _np(out), _np(lse)
+    rows = np.arange(B * Hkv) * ctx + ctx - 1
+    rep = {}
+    P.check_keys(k_new.float().cpu().numpy().astype(np.float64), To, _gpu_fields(To, kp, rows), rep)
+    P.check_values(v_new.float().cpu().numpy(), 2, _np(vp["codes"][rows]), _np(vp["scale"][rows]),
+                   _np(vp["zero"][rows]))
+    print("appended records: band cases %s" % rep, flush=True)
+    qv = _np(q.float())
+    worst = 0.0
+    for (b, h) in [(0, 0), (7, 4), (15, 7)]:
+        g = b * Hkv + h
+        sl = slice(g * ctx, (g + 1) * ctx)
+        khat = O.dequant_keys(_gpu_fields(To, kp, sl), To)
+        vc = _np(vp["codes"][sl])
+        venc = dict(codes=O.unpack_fields(vc, O.index_width(2), D), scale16=_np(vp["scale"][sl]).view(np.float16),
+                    zero16=_np(vp["zero"][sl]).view(np.float16))
+        vhat = O.dequant_values(venc)
+        heads = slice(h * G, (h + 1) * G)
+        s_ref, o_ref, lse_ref = O.decode_attention(qv[b, heads].astype(np.float64), khat, vhat, ctx)
+        worst = max(worst, P.check_scores(_np(scores[b, heads]), s_ref))
+        P.check_out(out[b, heads], o_ref)
+        assert np.all(np.abs(lse[b, heads] - lse_ref) <= 5e-3 * np.maximum(1.0, np.abs(lse_ref)))
+    print("gqa-decode-32k append step: worst relative score error %.3g" % worst, flush=True)
+
+
 def test_needle_decode_128k_full_size():
     """1 sequence x 8 KV heads x 32 query heads, context 131072, prod 4-bit
     keys (3-bit index in nibbles + QJL), 4-bit values, five planted needles
