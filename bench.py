@@ -294,14 +294,17 @@ def main():
     # The GPU's clocks take tens of milliseconds of sustained load to settle;
     # keep stepping (untimed, on the warm-up inputs) until settle_seconds have
     # passed so that the timed steps measure the steady state.
-    t_settle = time.perf_counter()
-    i = 0
-    while time.perf_counter() - t_settle < args.settle_seconds:
-        step(i % max(args.warmup, 1))
-        i += 1
-        if i % 50 == 0:
-            torch.cuda.synchronize()
-    torch.cuda.synchronize()
+    def settle(seconds):
+        t_settle = time.perf_counter()
+        i = 0
+        while time.perf_counter() - t_settle < seconds:
+            step(i % max(args.warmup, 1))
+            i += 1
+            if i % 50 == 0:
+                torch.cuda.synchronize()
+        torch.cuda.synchronize()
+
+    settle(args.settle_seconds)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
@@ -314,6 +317,7 @@ def main():
     # records would sit between the launches).
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.steps)]
+    settle(0.2 * args.settle_seconds)  # clocks back at steady load after the pause above
     for k in range(args.steps):
         step(args.warmup + k, evs[k])
     torch.cuda.synchronize()

@@ -1308,18 +1308,35 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
 
 // out[b][h][:] = sum_s O_s 2^(M_s - M) / sum_s L_s 2^(M_s - M), in split order.
 // A NaN sum (tables that do not match the kernel's format) makes the row NaN.
+// The largest M_s is found by the block's threads together (a strided share
+// each, then a reduction); the weighted sums run in split order, unrolled so
+// that several splits' partials are in flight at once (a long context has
+// tens of splits per head).
 __global__ __launch_bounds__(KD) void merge_kernel(const float* part, int n_split, float* out,
                                                    float* lse) {
+  static_assert(KD == 128, "two waves per block");
   const int bh = blockIdx.x, j = threadIdx.x;
   const float* p = part + (long long)bh * n_split * PART;
+  __shared__ float s_max[2];
+  __shared__ int s_bad[2];
   float M = -INFINITY;
   bool bad = false;
-  for (int s = 0; s < n_split; ++s) {
+  for (int s = j; s < n_split; s += KD) {
     M = fmaxf(M, p[s * PART]);
     bad |= p[s * PART + 1] != p[s * PART + 1];
   }
+  M = wave_max(M);
+  const bool wbad = __builtin_amdgcn_ballot_w64(bad) != 0;
+  if ((j & 63) == 0) {
+    s_max[j >> 6] = M;
+    s_bad[j >> 6] = wbad;
+  }
+  __syncthreads();
+  M = fmaxf(s_max[0], s_max[1]);
+  bad = s_bad[0] | s_bad[1];
   float Ls = 0.0f, O = 0.0f;
   if (M != -INFINITY) {
+#pragma unroll 8
     for (int s = 0; s < n_split; ++s) {
       const float* r = p + s * PART;
       const float f = r[0] == -INFINITY ? 0.0f : exp2f(r[0] - M);
