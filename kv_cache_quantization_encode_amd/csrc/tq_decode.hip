@@ -1426,6 +1426,14 @@ tq_status decode_impl(const tq_key_config* cfg, const void* tables, const void* 
   if (v_bits != 2 && v_bits != 4) return TQ_ERR_UNSUPPORTED;
   if (v_group != 32) return TQ_ERR_UNSUPPORTED;
   if (q_dtype != TQ_F32 && q_dtype != TQ_BF16 && q_dtype != TQ_F16) return TQ_ERR_ARG;
+  // appending (tq_decode_attention_append): both new rows, MSE or PROD keys
+  if (k_new || v_new) {
+    if (!k_new || !v_new) return TQ_ERR_ARG;
+    if (P.mode != TQ_MODE_MSE && P.mode != TQ_MODE_PROD) return TQ_ERR_UNSUPPORTED;
+    if (kv_dtype != TQ_F32 && kv_dtype != TQ_BF16 && kv_dtype != TQ_F16) return TQ_ERR_ARG;
+    const uintptr_t al = kv_dtype == TQ_F32 ? 3 : 1;
+    if (((uintptr_t)k_new & al) || ((uintptr_t)v_new & al)) return TQ_ERR_ARG;
+  }
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || max_ctx <= 0) return TQ_ERR_ARG;
   if (!workspace_bytes) return TQ_ERR_ARG;
   const int cus = tq::cu_count();
@@ -1466,13 +1474,6 @@ tq_status decode_impl(const tq_key_config* cfg, const void* tables, const void* 
       ((uintptr_t)out & 3))
     return TQ_ERR_ARG;
   if (max_ctx > 0x7fffffff / 2) return TQ_ERR_ARG;
-  if (k_new || v_new) {
-    if (!k_new || !v_new) return TQ_ERR_ARG;
-    if (P.mode != TQ_MODE_MSE && P.mode != TQ_MODE_PROD) return TQ_ERR_UNSUPPORTED;
-    if (kv_dtype != TQ_F32 && kv_dtype != TQ_BF16 && kv_dtype != TQ_F16) return TQ_ERR_ARG;
-    const uintptr_t al = kv_dtype == TQ_F32 ? 3 : 1;
-    if (((uintptr_t)k_new & al) || ((uintptr_t)v_new & al)) return TQ_ERR_ARG;
-  }
 
   DecArgs a;
   a.tables = (const unsigned char*)tables;

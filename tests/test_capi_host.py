@@ -278,6 +278,27 @@ def test_decode_argument_errors():
     assert _dec(L.key_config(mode="grouped", bits_outlier=4, bits_normal=4)) == L.TQ_ERR_UNSUPPORTED
 
 
+def _dec_append(cfg, kn=FAKE, vn=FAKE, dt=L.TQ_BF16, ws=None):
+    wsb = ctypes.c_size_t(0 if ws is None else 1 << 30)
+    return L.lib.tq_decode_attention_append(ctypes.byref(cfg), FAKE, FAKE, L.TQ_BF16, 2, 8, 2, FAKE, 1024, kn, vn,
+                                            dt, FAKE, FAKE, FAKE, FAKE, 2, 32, FAKE, FAKE, FAKE, ctypes.c_float(0.1),
+                                            FAKE, None, None, ws, ctypes.byref(wsb), None)
+
+
+def test_append_decode_argument_errors():
+    """tq_decode_attention_append: the new rows are checked on the host
+    before anything is launched (both present, MSE or PROD keys, a known
+    dtype, aligned to the element size)."""
+    prod = L.key_config(mode="prod", bits=3)
+    assert _dec_append(L.key_config(mode="grouped", bits_outlier=4, bits_normal=2)) == L.TQ_ERR_UNSUPPORTED
+    assert _dec_append(L.key_config(mode="grouped_prod", bits_outlier=3, bits_normal=2)) == L.TQ_ERR_UNSUPPORTED
+    assert _dec_append(prod, dt=7) == L.TQ_ERR_ARG
+    assert _dec_append(prod, kn=FAKE + 1) == L.TQ_ERR_ARG           # bf16 rows on an odd address
+    assert _dec_append(prod, vn=FAKE + 2, dt=L.TQ_F32) == L.TQ_ERR_ARG
+    assert _dec_append(prod, kn=None) == L.TQ_ERR_ARG
+    assert _dec_append(prod, vn=None, ws=FAKE) == L.TQ_ERR_ARG
+
+
 def _dec_paged(cfg, page_size=128, max_blocks=8, bt=FAKE, ws=None, n_pages=64):
     wsb = ctypes.c_size_t(1 << 30)
     return L.lib.tq_decode_attention_paged(ctypes.byref(cfg), FAKE, FAKE, L.TQ_BF16, 2, 8, 2, FAKE, bt,
