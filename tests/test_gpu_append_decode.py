@@ -19,7 +19,7 @@ if not torch.cuda.is_available():  # collected on CPU runs, skipped there
 
 import kv_cache_quantization_encode_amd as tq  # noqa: E402
 from kv_cache_quantization_encode_amd import _lib as L  # noqa: E402
-from tests.test_gpu_parity import _ocfg, _oracle_cache  # noqa: E402
+from tests.test_gpu_parity import _oracle_cache  # noqa: E402
 
 DEV = "cuda"
 
@@ -162,3 +162,36 @@ def test_append_decode_rejects_grouped():
     with pytest.raises(L.TqError) as e:
         dec(q, torch.tensor([10], dtype=torch.int32, device=DEV), kp, vp, k_new=kn, v_new=kn)
     assert e.value.status == L.TQ_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("kw", [dict(mode="prod", bits=3), dict(mode="mse", bits=4), dict(mode="mse", bits=1)],
+                         ids=["prod3", "mse4", "mse1"])
+def test_append_decode_extreme_norms(kw):
+    """New keys of norm about 1e-30 and 1e30 (fp32 sums of their squares would
+    underflow or overflow) and an all-zero key, appended inside the decode:
+    index and sign bytes as the oracle's, stored fp16 norms 0, +inf and 0 as
+    the oracle's rounding gives."""
+    B, Hkv, Hq, max_ctx = 8, 6, 24, 128
+    n = B * Hkv
+    base, _ = W.kv_rows(82, 1, n)
+    x = base.astype(np.float64) / np.sqrt(128.0)
+    x[:16] *= 1e-30
+    x[16:32] *= 1e30
+    x[-1] = 0.0
+    xv, xb = W.to_bf16(x.astype(np.float32))
+    vv, vb = W.kv_rows(82, 2, n)
+    To, kp, vp, _, _ = _oracle_cache(kw, 2, B, Hkv, max_ctx, wid=11)
+    Tg = tq.Tables(L.key_config(seed=42, **kw), DEV)
+    q = torch.from_numpy(W.queries(82, B, Hq)[1].view(np.int16)).view(torch.bfloat16).to(DEV)
+    kn = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).to(DEV).view(B, Hkv, 128)
+    vn = torch.from_numpy(vb.view(np.int16)).view(torch.bfloat16).to(DEV).view(B, Hkv, 128)
+    ctx = torch.full((B,), 70, dtype=torch.int32, device=DEV)
+    tq.decode_attention(Tg, q, ctx, kp, vp, 2, max_ctx, k_new=kn, v_new=vn)
+    torch.cuda.synchronize()
+    rows = np.arange(n) * max_ctx + 69
+    g = P.unpack_gpu_keys(To, {k: _np(v)[rows] for k, v in kp.items()})
+    P.check_keys(xv.astype(np.float64), To, g)
+    nrm = g["norm16"].astype(np.float64)
+    assert np.all(nrm[:16] == 0) and np.all(np.isposinf(nrm[16:32])) and nrm[-1] == 0
+    P.check_values(vn.view(n, 128).float().cpu().numpy(), 2, _np(vp["codes"])[rows], _np(vp["scale"])[rows],
+                   _np(vp["zero"])[rows])
