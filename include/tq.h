@@ -285,7 +285,8 @@ tq_status tq_decode_attention(const tq_key_config* cfg, const void* tables,
  *              contiguous, aligned to their element size; both non-NULL.
  *   other arguments as tq_decode_attention (same workspace size).
  * Supported: the MSE and PROD formats tq_decode_attention supports
- * (GROUPED and GROUPED_PROD return TQ_ERR_UNSUPPORTED), contiguous planes.
+ * (GROUPED and GROUPED_PROD return TQ_ERR_UNSUPPORTED); contiguous planes
+ * here, a paged pool with tq_decode_attention_paged_append.
  * Records of the appended tokens may differ from tq_encode_keys' where a
  * rotated coordinate lies within float32 rounding of a codebook boundary or
  * a projection within rounding of zero (each side's float32 arithmetic
@@ -361,6 +362,29 @@ tq_status tq_decode_attention_paged(const tq_key_config* cfg, const void* tables
                                     const uint16_t* v_zero,
                                     float sm_scale, float* out, float* lse, float* scores,
                                     void* workspace, size_t* workspace_bytes, void* stream);
+
+/*
+ * tq_decode_attention_paged_append -- tq_decode_attention_append over a paged
+ * pool (bit-packing article sec 五: each new token's packed record goes into
+ * the store's current chunk, and the kernels read the chunks in place): the
+ * new token t = ctx_len[b] - 1 of (b, h) is encoded into record
+ *     (block_table[b][t / page_size] * Hkv + h) * page_size + t % page_size
+ * (the entry clamped into [0, n_pages) as every entry is) and attended in the
+ * same launch.  The block table must already name the page of t (a new
+ * page, when t opens one).  Arguments as tq_decode_attention_paged, plus
+ * k_new, v_new and kv_dtype as tq_decode_attention_append; same support and
+ * errors as those two.
+ */
+tq_status tq_decode_attention_paged_append(const tq_key_config* cfg, const void* tables, const void* q,
+                                           int32_t q_dtype, int32_t B, int32_t Hq, int32_t Hkv,
+                                           const int32_t* ctx_len, const int32_t* block_table,
+                                           int32_t max_blocks_per_seq, int32_t page_size, int32_t n_pages,
+                                           const void* k_new, const void* v_new, int32_t kv_dtype,
+                                           uint8_t* idx, uint8_t* signs, uint16_t* norm, uint16_t* rnorm,
+                                           int32_t v_bits, int32_t v_group,
+                                           uint8_t* v_codes, uint16_t* v_scale, uint16_t* v_zero,
+                                           float sm_scale, float* out, float* lse, float* scores,
+                                           void* workspace, size_t* workspace_bytes, void* stream);
 
 /*
  * tq_dequantize_keys -- dense k_hat rows from packed key records: the

@@ -26,7 +26,7 @@ TQ_STREAM_READ_SINK = 65536
 MODES = {"mse": TQ_MODE_MSE, "prod": TQ_MODE_PROD, "grouped": TQ_MODE_GROUPED, "grouped_prod": TQ_MODE_GROUPED_PROD}
 
 EXPORTED = ["tq_build_codebook", "tq_encode_keys", "tq_encode_keys_batched", "tq_encode_values", "tq_append_kv", "tq_decode_attention",
-            "tq_decode_attention_append", "tq_decode_attention_noalloc", "tq_decode_attention_paged", "tq_dequantize_keys", "tq_dequantize_values", "tq_channel_moments",
+            "tq_decode_attention_append", "tq_decode_attention_noalloc", "tq_decode_attention_paged_append", "tq_decode_attention_paged", "tq_dequantize_keys", "tq_dequantize_values", "tq_channel_moments",
             "tq_select_outlier_channels", "tq_status_string", "tq_idx_row_bytes", "tq_stream_read"]
 
 
@@ -89,6 +89,10 @@ def _load():
     lib.tq_decode_attention_paged.argtypes = [CFG, P, P, I32, I32, I32, I32, P, P, I32, I32, I32, P, P, P, P,
                                               I32, I32, P, P, P, ctypes.c_float, P, P, P, P,
                                               ctypes.POINTER(SZ), P]
+    lib.tq_decode_attention_paged_append.restype = I32
+    lib.tq_decode_attention_paged_append.argtypes = [CFG, P, P, I32, I32, I32, I32, P, P, I32, I32, I32, P, P, I32,
+                                                     P, P, P, P, I32, I32, P, P, P, ctypes.c_float, P, P, P, P,
+                                                     ctypes.POINTER(SZ), P]
     lib.tq_dequantize_keys.restype = I32
     lib.tq_dequantize_keys.argtypes = [CFG, P, I64, P, I64, P, P, P, P, P, I32, I64, P]
     lib.tq_dequantize_values.restype = I32

@@ -455,21 +455,23 @@ class Decoder:
         vals = (self.v_bits, 32, _ptr(vp["codes"]), _ptr(vp["scale"]), _ptr(vp["zero"]))
         tail = (ctypes.c_float(sm_scale), _ptr(out), _ptr(lse), _ptr(scores), _ptr(self.ws),
                 ctypes.byref(size), _stream())
-        if k_new is not None or v_new is not None:
-            _need(self.page_size is None, "appending inside the decode needs contiguous planes")
-            _need(block_table is None, "a contiguous decoder takes no block table")
+        appending = k_new is not None or v_new is not None
+        if appending:
             for name, t in (("k_new", k_new), ("v_new", v_new)):
                 _on_device(t, name, tuple(_DT), contiguous=True)
                 _need(tuple(t.shape) == (B, self.Hkv, d), "%s must be [B, Hkv, d]" % name)
             _need(k_new.dtype == v_new.dtype, "k_new and v_new must have one dtype")
-            name, fn = "tq_decode_attention_append", lib.tq_decode_attention_append
-            args = (ctypes.byref(self.tables.cfg), _ptr(self.tables.dev), _ptr(q), _DT[q.dtype], B, Hq, self.Hkv,
-                    _ptr(ctx_len), self.max_ctx, _ptr(k_new), _ptr(v_new), _DT[k_new.dtype], *keys, *vals, *tail)
-        elif self.page_size is None:
+            new = (_ptr(k_new), _ptr(v_new), _DT[k_new.dtype])
+        head = (ctypes.byref(self.tables.cfg), _ptr(self.tables.dev), _ptr(q), _DT[q.dtype], B, Hq, self.Hkv,
+                _ptr(ctx_len))
+        if self.page_size is None:
             _need(block_table is None, "a contiguous decoder takes no block table")
-            name, fn = "tq_decode_attention", lib.tq_decode_attention
-            args = (ctypes.byref(self.tables.cfg), _ptr(self.tables.dev), _ptr(q), _DT[q.dtype], B, Hq, self.Hkv,
-                    _ptr(ctx_len), self.max_ctx, *keys, *vals, *tail)
+            if appending:
+                name, fn = "tq_decode_attention_append", lib.tq_decode_attention_append
+                args = head + (self.max_ctx,) + new + keys + vals + tail
+            else:
+                name, fn = "tq_decode_attention", lib.tq_decode_attention
+                args = head + (self.max_ctx,) + keys + vals + tail
         else:
             nb = self.max_ctx // self.page_size
             _need(block_table is not None, "a paged decoder needs the block table")
@@ -478,9 +480,13 @@ class Decoder:
             # pages of the pool: the planes' records over the records of one page
             n_pages = n_rec // (self.Hkv * self.page_size)
             _need(n_pages > 0, "the planes hold less than one page")
-            name, fn = "tq_decode_attention_paged", lib.tq_decode_attention_paged
-            args = (ctypes.byref(self.tables.cfg), _ptr(self.tables.dev), _ptr(q), _DT[q.dtype], B, Hq, self.Hkv,
-                    _ptr(ctx_len), _ptr(block_table), nb, self.page_size, n_pages, *keys, *vals, *tail)
+            paged = (_ptr(block_table), nb, self.page_size, n_pages)
+            if appending:
+                name, fn = "tq_decode_attention_paged_append", lib.tq_decode_attention_paged_append
+                args = head + paged + new + keys + vals + tail
+            else:
+                name, fn = "tq_decode_attention_paged", lib.tq_decode_attention_paged
+                args = head + paged + keys + vals + tail
 
         def run():
             check(name, fn(*args))

@@ -459,9 +459,11 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
   // The workgroup's block-table entries are staged in LDS by the prologue (a
   // global read here would wait behind the tile loads already in flight);
   // the host sizes the splits so that they fit in PAGE_CACHE entries.
+  // (an appended token tn, outside the loop's range, may open a page of its own: staged too)
+  const int t_stage = has_new ? tn : t_last;
   const int lp0 = a.block_table ? t_begin / a.page_size : 0;
-  const int n_pages_wg =
-      a.block_table && t_end > t_begin ? min(t_last / a.page_size - lp0 + 1, PAGE_CACHE) : 0;
+  const int n_pages_wg = a.block_table && (t_end > t_begin || has_new)
+                             ? min(t_stage / a.page_size - lp0 + 1, PAGE_CACHE) : 0;
   auto tile_base = [&](int tb) -> long long {
     if (!a.block_table) return rec0;
     const int tc = min(tb, t_last);
@@ -821,7 +823,10 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
   }
   // the appended record (complete in LDS now) into the planes, by quad 0
   if (has_new && quad == 0 && wave == KENC_WAVE) {
-    const long long rec = tile_base(tn) + tn;
+    // its record: rec0 + tn, or through the staged entry of tn's page
+    const long long rec = a.block_table ? ((long long)L.pages[tn / a.page_size - lp0] * a.Hkv + hkv) * a.page_size +
+                                              tn % a.page_size
+                                        : rec0 + tn;
     if (lane < F::IDXB / 4) ((uint32_t*)(a.w_idx + rec * F::IDXB))[lane] = L.nrec[NR_IDX + lane];
     if (F::QJL && lane >= NR_SIGN && lane < NR_SIGN + 4)
       ((uint32_t*)(a.w_signs + rec * (KD / 8)))[lane - NR_SIGN] = L.nrec[lane];
@@ -1630,4 +1635,21 @@ extern "C" tq_status tq_decode_attention_append(const tq_key_config* cfg, const 
   return decode_impl(cfg, tables, q, q_dtype, B, Hq, Hkv, ctx_len, max_ctx, nullptr, 0, 0, 0, idx, signs,
                      norm, rnorm, v_bits, v_group, v_codes, v_scale, v_zero, sm_scale, out, lse, scores,
                      workspace, workspace_bytes, stream, k_new, v_new, kv_dtype);
+}
+
+extern "C" tq_status tq_decode_attention_paged_append(
+    const tq_key_config* cfg, const void* tables, const void* q, int32_t q_dtype, int32_t B, int32_t Hq,
+    int32_t Hkv, const int32_t* ctx_len, const int32_t* block_table, int32_t max_blocks_per_seq,
+    int32_t page_size, int32_t n_pages, const void* k_new, const void* v_new, int32_t kv_dtype, uint8_t* idx,
+    uint8_t* signs, uint16_t* norm, uint16_t* rnorm, int32_t v_bits, int32_t v_group, uint8_t* v_codes,
+    uint16_t* v_scale, uint16_t* v_zero, float sm_scale, float* out, float* lse, float* scores, void* workspace,
+    size_t* workspace_bytes, void* stream) {
+  if (page_size <= 0 || page_size % TILE != 0 || max_blocks_per_seq <= 0 || n_pages <= 0) return TQ_ERR_ARG;
+  if ((long long)n_pages * Hkv * page_size > 0x7fffffffffffLL) return TQ_ERR_ARG;
+  if ((long long)max_blocks_per_seq * page_size > 0x3fffffffLL) return TQ_ERR_ARG;
+  if (workspace && (!block_table || !k_new || !v_new)) return TQ_ERR_ARG;
+  return decode_impl(cfg, tables, q, q_dtype, B, Hq, Hkv, ctx_len, max_blocks_per_seq * page_size, block_table,
+                     max_blocks_per_seq, page_size, n_pages, idx, signs, norm, rnorm, v_bits, v_group, v_codes,
+                     v_scale, v_zero, sm_scale, out, lse, scores, workspace, workspace_bytes, stream, k_new, v_new,
+                     kv_dtype);
 }

@@ -11,7 +11,8 @@ record of token t of (sequence b, KV head h) is
 This module only allocates pages, keeps the tables and computes those record
 indices (slots); the quantisation and the attention run in libtq's kernels
 (tq_append_kv, or tq_encode_keys / tq_encode_values, with slots;
-tq_decode_attention_paged).
+tq_decode_attention_paged; tq_decode_attention_paged_append for a decode
+step that appends its token in the same launch).
 """
 from __future__ import annotations
 
@@ -103,3 +104,22 @@ class PagedKVCache:
         ctx = torch.tensor([self.lengths[s] for s in seqs], dtype=torch.int32, device=self.device)
         bt = self.block_table[torch.tensor(seqs, dtype=torch.long, device=self.device)].contiguous()
         return dec(q, ctx, self.kp, self.vp, block_table=bt, **kw)
+
+    def decode_step(self, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seqs=None, dec: Decoder | None = None,
+                    **kw):
+        """One decode step that appends one token per sequence: k and v are
+        [B, Hkv, d] (one dtype of float32 / bf16 / fp16), q is [B, Hq, d].  The
+        token is encoded into its page and attended in one launch
+        (tq_decode_attention_paged_append); returns out [B, Hq, d] float32."""
+        B, Hq, _ = q.shape
+        seqs = list(range(B)) if seqs is None else list(seqs)
+        if tuple(k.shape[:2]) != (B, self.Hkv) or v.shape != k.shape:
+            raise ValueError("k and v must both be [B, Hkv=%d, d]" % self.Hkv)
+        for s in seqs:
+            self._grow(s, self.lengths[s] + 1)
+        for s in seqs:
+            self.lengths[s] += 1
+        dec = dec or self.decoder(B, Hq, q.dtype)
+        ctx = torch.tensor([self.lengths[s] for s in seqs], dtype=torch.int32, device=self.device)
+        bt = self.block_table[torch.tensor(seqs, dtype=torch.long, device=self.device)].contiguous()
+        return dec(q, ctx, self.kp, self.vp, block_table=bt, k_new=k, v_new=v, **kw)

@@ -299,6 +299,23 @@ def test_append_decode_argument_errors():
     assert _dec_append(prod, vn=None, ws=FAKE) == L.TQ_ERR_ARG
 
 
+def _dec_paged_append(cfg, page_size=128, bt=FAKE, kn=FAKE, ws=None):
+    wsb = ctypes.c_size_t(1 << 30)
+    return L.lib.tq_decode_attention_paged_append(ctypes.byref(cfg), FAKE, FAKE, L.TQ_BF16, 2, 8, 2, FAKE, bt, 8,
+                                                  page_size, 64, kn, FAKE, L.TQ_BF16, FAKE, FAKE, FAKE, FAKE, 2, 32,
+                                                  FAKE, FAKE, FAKE, ctypes.c_float(0.1), FAKE, None, None, ws,
+                                                  ctypes.byref(wsb), None)
+
+
+def test_paged_append_decode_argument_errors():
+    prod = L.key_config(mode="prod", bits=3)
+    assert _dec_paged_append(prod, page_size=100) == L.TQ_ERR_ARG
+    assert _dec_paged_append(prod, bt=None, ws=FAKE) == L.TQ_ERR_ARG
+    assert _dec_paged_append(prod, kn=None, ws=FAKE) == L.TQ_ERR_ARG
+    assert _dec_paged_append(prod, kn=FAKE + 1) == L.TQ_ERR_ARG
+    assert _dec_paged_append(L.key_config(mode="grouped", bits_outlier=4, bits_normal=2)) == L.TQ_ERR_UNSUPPORTED
+
+
 def _dec_paged(cfg, page_size=128, max_blocks=8, bt=FAKE, ws=None, n_pages=64):
     wsb = ctypes.c_size_t(1 << 30)
     return L.lib.tq_decode_attention_paged(ctypes.byref(cfg), FAKE, FAKE, L.TQ_BF16, 2, 8, 2, FAKE, bt,

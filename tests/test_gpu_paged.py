@@ -79,6 +79,121 @@ def test_paged_equals_contiguous(page_size):
         assert torch.equal(sc_c[b, :, :ctx[b]], sc_p[b, :, :ctx[b]])
 
 
+@pytest.mark.parametrize("page_size", [64, 256])
+def test_paged_append_equals_contiguous_append(page_size):
+    """tq_decode_attention_paged_append against tq_decode_attention_append on
+    the same records in shuffled pages: outputs, lse and scores bit for bit,
+    the new records equal at their paged and contiguous slots, every other
+    record untouched.  The lengths include a token that opens a page of its
+    own, a one-token sequence and a full one."""
+    kw = dict(mode="prod", bits=3)
+    B, Hq, Hkv, max_ctx = 3, 8, 2, 1536
+    ctx = [page_size + 1, 1, 1536]
+    Tg = tq.Tables(L.key_config(seed=7, **kw), DEV)
+    n = B * Hkv * max_ctx
+    kb = W.kv_rows(23, 1, n)[1]
+    vb = W.kv_rows(23, 2, n)[1]
+    kp = tq.encode_keys(Tg, torch.from_numpy(kb.view(np.int16)).view(torch.bfloat16).to(DEV))
+    vp = tq.encode_values(torch.from_numpy(vb.view(np.int16)).view(torch.bfloat16).to(DEV), 2)
+    q = torch.from_numpy(W.queries(23, B, Hq)[1].view(np.int16)).view(torch.bfloat16).to(DEV)
+    knb = W.kv_rows(24, 1, B * Hkv)[1]
+    vnb = W.kv_rows(24, 2, B * Hkv)[1]
+    kn = torch.from_numpy(knb.view(np.int16)).view(torch.bfloat16).to(DEV).view(B, Hkv, 128)
+    vn = torch.from_numpy(vnb.view(np.int16)).view(torch.bfloat16).to(DEV).view(B, Hkv, 128)
+    ctx_t = torch.tensor(ctx, dtype=torch.int32, device=DEV)
+    # the paged copy of the records, taken before the contiguous call writes
+    nb = max_ctx // page_size
+    n_pages = B * nb + 5
+    perm = np.random.default_rng(4).permutation(n_pages)[:B * nb].reshape(B, nb)
+    bt = torch.from_numpy(perm.astype(np.int32)).to(DEV)
+    t = torch.arange(max_ctx, device=DEV)
+    src, dst = [], []
+    for b in range(B):
+        for h in range(Hkv):
+            src.append((b * Hkv + h) * max_ctx + t)
+            dst.append((bt[b].long()[t // page_size] * Hkv + h) * page_size + t % page_size)
+    src, dst = torch.cat(src), torch.cat(dst)
+    n_rec = n_pages * Hkv * page_size
+    kpp = {k: torch.zeros((n_rec,) + v.shape[1:], dtype=v.dtype, device=DEV) for k, v in kp.items()}
+    vpp = {k: torch.zeros((n_rec,) + v.shape[1:], dtype=v.dtype, device=DEV) for k, v in vp.items()}
+    for k in kp:
+        kpp[k][dst] = kp[k][src]
+    for k in vp:
+        vpp[k][dst] = vp[k][src]
+    before = {k: v.clone() for k, v in list(kpp.items()) + [("v_" + k, v) for k, v in vpp.items()]}
+    dec = tq.Decoder(Tg, B, Hq, Hkv, max_ctx, 2)
+    lse_c = torch.empty((B, Hq), device=DEV)
+    sc_c = torch.full((B, Hq, max_ctx), float("nan"), device=DEV)
+    out_c = dec(q, ctx_t, kp, vp, lse=lse_c, scores=sc_c, k_new=kn, v_new=vn)
+    decp = tq.Decoder(Tg, B, Hq, Hkv, max_ctx, 2, page_size=page_size)
+    lse_p = torch.empty((B, Hq), device=DEV)
+    sc_p = torch.full((B, Hq, max_ctx), float("nan"), device=DEV)
+    out_p = decp(q, ctx_t, kpp, vpp, lse=lse_p, scores=sc_p, block_table=bt, k_new=kn, v_new=vn)
+    torch.cuda.synchronize()
+    assert torch.equal(out_c, out_p)
+    assert torch.equal(lse_c, lse_p)
+    for b in range(B):
+        assert torch.equal(sc_c[b, :, :ctx[b]], sc_p[b, :, :ctx[b]])
+    for k in kp:
+        assert torch.equal(kpp[k][dst], kp[k][src]), k
+    for k in vp:
+        assert torch.equal(vpp[k][dst], vp[k][src]), k
+    # records other than the new tokens' are as before
+    new = torch.tensor([int(dst[(b * Hkv + h) * max_ctx + ctx[b] - 1]) for b in range(B) for h in range(Hkv)],
+                       device=DEV)
+    keep = torch.ones(n_rec, dtype=torch.bool, device=DEV)
+    keep[new] = False
+    for k, v in list(kpp.items()) + [("v_" + k, v) for k, v in vpp.items()]:
+        assert torch.equal(v[keep], before[k][keep]), k
+
+
+def test_store_decode_step_appends_in_the_launch():
+    """PagedKVCache.decode_step (one launch per step: the new token encoded
+    into its page and attended) against append() of that token followed by a
+    plain paged decode: the same records and the same outputs, over steps that
+    cross a page boundary."""
+    kw = dict(mode="prod", bits=3)
+    Tg = tq.Tables(L.key_config(seed=9, **kw), DEV)
+    B, Hq, Hkv, page_size = 2, 8, 2, 64
+    a = tq.PagedKVCache(Tg, Hkv, 2, n_pages=16, page_size=page_size, max_seqs=B, max_pages_per_seq=4)
+    c = tq.PagedKVCache(Tg, Hkv, 2, n_pages=16, page_size=page_size, max_seqs=B, max_pages_per_seq=4)
+    n0 = 62
+    for s in range(B):
+        kb = W.kv_rows(25 + s, 1, n0 * Hkv)[1]
+        vb = W.kv_rows(25 + s, 2, n0 * Hkv)[1]
+        k = torch.from_numpy(kb.view(np.int16)).view(torch.bfloat16).to(DEV).view(n0, Hkv, 128)
+        v = torch.from_numpy(vb.view(np.int16)).view(torch.bfloat16).to(DEV).view(n0, Hkv, 128)
+        a.append(s, k, v)
+        c.append(s, k, v)
+    for step in range(4):   # tokens 62 .. 65: the third opens page 1
+        q = torch.from_numpy(W.queries(30 + step, B, Hq)[1].view(np.int16)).view(torch.bfloat16).to(DEV)
+        kb = W.kv_rows(40 + step, 1, B * Hkv)[1]
+        vb = W.kv_rows(40 + step, 2, B * Hkv)[1]
+        k = torch.from_numpy(kb.view(np.int16)).view(torch.bfloat16).to(DEV).view(B, Hkv, 128)
+        v = torch.from_numpy(vb.view(np.int16)).view(torch.bfloat16).to(DEV).view(B, Hkv, 128)
+        out_a = a.decode_step(q, k, v)
+        for s in range(B):
+            c.append(s, k[s:s + 1], v[s:s + 1])
+        out_c = c.decode(q)
+        torch.cuda.synchronize()
+        assert a.lengths == c.lengths
+        assert torch.equal(a.block_table, c.block_table)
+        for s in range(B):
+            sl = a.slots(s, 0, a.lengths[s])
+            old_rows = a.slots(s, 0, n0)
+            for k_ in a.vp:     # value records: bit-exact in both encoders
+                assert torch.equal(a.vp[k_][sl], c.vp[k_][sl]), (step, s, k_)
+            for k_ in a.kp:     # the cached tokens' key records: untouched
+                assert torch.equal(a.kp[k_][old_rows], c.kp[k_][old_rows]), (step, s, k_)
+                # the appended ones: two float32 encoders, equal but for
+                # coordinates within rounding of a boundary (at most a byte here)
+                diff = (a.kp[k_][sl] != c.kp[k_][sl]).sum().item()
+                assert diff <= 1, (step, s, k_, diff)
+        # the new token's score is float32 from its record in one, a table
+        # lookup in the other: outputs agree to well inside the parity bound
+        assert float((out_a - out_c).abs().max()) <= 2e-3
+
+
 def test_paged_block_table_clamped_into_the_pool():
     """A block table naming the pool's last page works as any other; an
     entry past the pool (or negative) is clamped into [0, n_pages) on the
