@@ -284,9 +284,11 @@ tq_status tq_decode_attention(const tq_key_config* cfg, const void* tables,
  *   k_new, v_new  [B][Hkv][d] of kv_dtype (TQ_F32, TQ_BF16, TQ_F16),
  *              contiguous, aligned to their element size; both non-NULL.
  *   other arguments as tq_decode_attention (same workspace size).
- * Supported: the MSE and PROD formats tq_decode_attention supports
- * (GROUPED and GROUPED_PROD return TQ_ERR_UNSUPPORTED); contiguous planes
- * here, a paged pool with tq_decode_attention_paged_append.
+ * Supported: every key format tq_decode_attention supports (the grouped
+ * modes encode each half with its own norm, transform and codebook, and
+ * GROUPED_PROD sketches the halves' weighted residuals together, as
+ * tq_encode_keys does); contiguous planes here, a paged pool with
+ * tq_decode_attention_paged_append.
  * Records of the appended tokens may differ from tq_encode_keys' where a
  * rotated coordinate lies within float32 rounding of a codebook boundary or
  * a projection within rounding of zero (each side's float32 arithmetic

@@ -580,8 +580,11 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
   // (bit-packing article, sections 二/三): per 32-channel group
   // s = fp16((max - min) / (2^VB - 1)), z = fp16(min),
   // code = clamp(rint((v - z) / s), 0, 2^VB - 1) in float32, 0 when s = 0.
-  if constexpr (!F::GROUPED) {
+  {
     if (has_new && wave == KENC_WAVE) {
+      // lane holds coordinates lane and lane + 64: one 128-point transform,
+      // or (GROUPED) the two halves' 64-point ones, each half with its own
+      // norm, sigma and codebook
       const long long kr = ((long long)b * a.Hkv + hkv) * KD;
       uint32_t w0, w1;
       if (a.kv_dtype == TQ_F32) {
@@ -591,23 +594,33 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
         w0 = ((const uint16_t*)a.knew)[kr + lane];
         w1 = ((const uint16_t*)a.knew)[kr + lane + 64];
       }
-      const float* sig = (const float*)(a.tables + H->off_sigma[0]);
-      const float* bnd = (const float*)(a.tables + H->off_bounds[0]);
-      const float sgk0 = sig[lane], sgk1 = sig[lane + 64];
-      const float bl = lane < lev0 - 1 ? bnd[lane] : INFINITY;  // boundary `lane`
-      const float cl = lane < lev0 ? cent0[lane] : 0.0f;        // centroid `lane` (gathered by shuffle below)
+      const float* sig0 = (const float*)(a.tables + H->off_sigma[0]);
+      const float* sig1 = (const float*)(a.tables + H->off_sigma[F::GROUPED ? 1 : 0]);
+      const float* bnd0 = (const float*)(a.tables + H->off_bounds[0]);
+      const float* bnd1 = (const float*)(a.tables + H->off_bounds[F::GROUPED ? 1 : 0]);
+      const float sgk0 = sig0[lane], sgk1 = F::GROUPED ? sig1[lane] : sig0[lane + 64];
+      const int nl1 = F::GROUPED ? lev1 : lev0;  // levels of the codebook of coordinate lane + 64
+      // boundary / centroid `lane` of each part (gathered by readlane / shuffle below)
+      const float bl0 = lane < lev0 - 1 ? bnd0[lane] : INFINITY;
+      const float bl1 = lane < nl1 - 1 ? bnd1[lane] : INFINITY;
+      const float cl0 = lane < lev0 ? cent0[lane] : 0.0f;
+      const float cl1 = lane < nl1 ? (F::GROUPED ? cent1 : cent0)[lane] : 0.0f;
       float k0 = q_word_to_float(w0, a.kv_dtype), k1 = q_word_to_float(w1, a.kv_dtype);
-      // the sum of squares on the coordinates scaled by the power of two
-      // that brings the largest into [1, 2): no fp32 under- or overflow for
-      // finite keys; the norm is scaled back
-      const float kmax = wave_max(fmaxf(fabsf(k0), fabsf(k1)));
-      const int ke = kmax > 0.0f ? min(max(ilogbf(kmax), -126), 127) : 0;
-      k0 = ldexpf(k0, -ke);
-      k1 = ldexpf(k1, -ke);
-      const float ss = wave_sum(fmaf(k0, k0, k1 * k1));
-      const float inv_n = ss > 0.0f ? 1.0f / sqrtf(ss) : 0.0f;  // a zero key has y = 0
+      // sums of squares on the coordinates scaled by the power of two that
+      // brings the largest (of the key, or of each half) into [1, 2): no
+      // fp32 under- or overflow for finite keys; the norms are scaled back
+      float kmax0 = wave_max(fabsf(k0)), kmax1 = wave_max(fabsf(k1));
+      if (!F::GROUPED) kmax0 = kmax1 = fmaxf(kmax0, kmax1);
+      const int ke0 = kmax0 > 0.0f ? min(max(ilogbf(kmax0), -126), 127) : 0;
+      const int ke1 = kmax1 > 0.0f ? min(max(ilogbf(kmax1), -126), 127) : 0;
+      k0 = ldexpf(k0, -ke0);
+      k1 = ldexpf(k1, -ke1);
+      float ss0 = wave_sum(k0 * k0), ss1 = wave_sum(k1 * k1);
+      if (!F::GROUPED) ss0 = ss1 = ss0 + ss1;
+      const float inv0 = ss0 > 0.0f ? 1.0f / sqrtf(ss0) : 0.0f;  // a zero key (half) has y = 0
+      const float inv1 = ss1 > 0.0f ? 1.0f / sqrtf(ss1) : 0.0f;
       float y0 = k0 * sgk0, y1 = k1 * sgk1;
-      {
+      if constexpr (!F::GROUPED) {
         const float t = y0;
         y0 = t + y1;
         y1 = t - y1;
@@ -619,37 +632,54 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
         y0 = up ? z0 - y0 : y0 + z0;
         y1 = up ? z1 - y1 : y1 + z1;
       });
-      y0 *= inv_n;
-      y1 *= inv_n;
+      y0 *= inv0;
+      y1 *= inv1;
       int i0 = 0, i1 = 0;
-      for (int t = 0; t < lev0 - 1; ++t) {
-        const float bt = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bl), t));
-        i0 += y0 >= bt ? 1 : 0;
-        i1 += y1 >= bt ? 1 : 0;
-      }
+      for (int t = 0; t < lev0 - 1; ++t)
+        i0 += y0 >= __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bl0), t)) ? 1 : 0;
+      for (int t = 0; t < nl1 - 1; ++t)
+        i1 += y1 >= __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bl1), t)) ? 1 : 0;
       L.nb8[lane] = (unsigned char)i0;
       L.nb8[lane + 64] = (unsigned char)i1;
-      const float nrm = ldexpf(sqrtf(ss), ke);
+      const float n0 = ldexpf(sqrtf(ss0), ke0), n1 = ldexpf(sqrtf(ss1), ke1);
       float rho = 0.0f;
       if constexpr (F::QJL) {
-        const float r0 = y0 - __shfl(cl, i0), r1 = y1 - __shfl(cl, i1);
+        float r0 = y0 - __shfl(cl0, i0), r1 = y1 - __shfl(cl1, i1);
+        if constexpr (F::GROUPED) {
+          // the sketch takes w = concat_j (n_j / 8) r_j, here divided by
+          // max(n_0, n_1) / 8 (the signs do not change), rho = ||w||
+          const float nmax = fmaxf(n0, n1);
+          r0 *= nmax > 0.0f ? n0 / nmax : 0.0f;
+          r1 *= nmax > 0.0f ? n1 / nmax : 0.0f;
+          rho = nmax * sqrtf(wave_sum(fmaf(r0, r0, r1 * r1))) * 0.125f;
+        } else {
+          rho = ldexpf(sqrtf(ss0) * sqrtf(wave_sum(fmaf(r0, r0, r1 * r1))) * 0.088388347648318441f,
+                       ke0);  // n ||r|| / sqrt(128)
+        }
         qp[QH * KD + lane] = r0;
         qp[QH * KD + lane + 64] = r1;
-        const float rr = wave_sum(fmaf(r0, r0, r1 * r1));
-        rho = ldexpf(sqrtf(ss) * sqrtf(rr) * 0.088388347648318441f, ke);  // n ||r|| / sqrt(128)
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
-      if (lane < F::IDXB / 4) {
+      // index row: part 0's fields (W0 bits, coordinates 0 ..), then part 1's
+      // (W1 bits, coordinates 64 ..) for GROUPED
+      if (lane < F::IP0 / 4) {
         constexpr int W = F::W0, PER = 32 / W;
         uint32_t v = 0;
 #pragma unroll
         for (int i = 0; i < PER; ++i) v |= (uint32_t)L.nb8[lane * PER + i] << (W * i);
         L.nrec[NR_IDX + lane] = v;
+      } else if (F::GROUPED && lane < F::IDXB / 4) {
+        constexpr int W = F::W1, PER = 32 / W;
+        uint32_t v = 0;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) v |= (uint32_t)L.nb8[64 + (lane - F::IP0 / 4) * PER + i] << (W * i);
+        L.nrec[NR_IDX + lane] = v;
       }
       if (lane == 0) {
-        L.nrec[NR_NORM] = __half_as_ushort(__float2half_rn(nrm));
+        const uint32_t h0 = __half_as_ushort(__float2half_rn(n0)), h1 = __half_as_ushort(__float2half_rn(n1));
+        L.nrec[NR_NORM] = F::GROUPED ? h0 | (h1 << 16) : h0;
         L.nrec[NR_RNORM] = __half_as_ushort(__float2half_rn(rho));
       }
     }
@@ -830,24 +860,34 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
     if (lane < F::IDXB / 4) ((uint32_t*)(a.w_idx + rec * F::IDXB))[lane] = L.nrec[NR_IDX + lane];
     if (F::QJL && lane >= NR_SIGN && lane < NR_SIGN + 4)
       ((uint32_t*)(a.w_signs + rec * (KD / 8)))[lane - NR_SIGN] = L.nrec[lane];
-    if (lane == NR_NORM) a.w_norm[rec] = (uint16_t)L.nrec[NR_NORM];
+    if (lane == NR_NORM) {
+      if (F::GROUPED) *(uint32_t*)(a.w_norm + 2 * rec) = L.nrec[NR_NORM];  // the two halves' norms
+      else a.w_norm[rec] = (uint16_t)L.nrec[NR_NORM];
+    }
     if (F::QJL && lane == NR_RNORM) a.w_rnorm[rec] = (uint16_t)L.nrec[NR_RNORM];
     if (lane == NR_Z || lane == NR_Z + 1) ((uint32_t*)(a.w_vzero + rec * 4))[lane - NR_Z] = L.nrec[lane];
     if (lane == NR_S || lane == NR_S + 1) ((uint32_t*)(a.w_vscale + rec * 4))[lane - NR_S] = L.nrec[lane];
     if (lane >= NR_CODE && lane < NR_CODE + VROW / 4) ((uint32_t*)(a.w_vcodes + rec * VROW))[lane - NR_CODE] = L.nrec[lane];
   }
-  if constexpr (!F::GROUPED) {
+  {
     if (has_new && wave >= KENC_WAVE && wave < KENC_WAVE + QH) {
       // the appended token's score for head hh = wave - KENC_WAVE, from its
       // record, in float32:
-      // <q, k_hat> = (n / PD) sum_j q'_j c[idx_j]
+      // <q, k_hat> = (n / PD) sum_j q'_j c[idx_j]   (GROUPED: per half, with
+      //              the half's norm, transform and codebook)
       //            + rho sqrt(pi/2) / (m sqrt(PD)) sum_i (S q')_i (2 bit_i - 1)
       // with the stored fp16 norms (what a later call reads back)
       const int hh = wave - KENC_WAVE;
-      const float n16 = h2f(L.nrec[NR_NORM]), r16 = h2f(L.nrec[NR_RNORM]);
-      const float c0 = cen[L.nb8[lane]], c1 = cen[L.nb8[lane + 64]];
-      const float di = wave_sum(fmaf(qp[hh * KD + lane], c0, qp[hh * KD + lane + 64] * c1));
-      float dot = n16 / (float)F::PD * di;
+      const float r16 = h2f(L.nrec[NR_RNORM]);
+      const float c0 = cen[L.nb8[lane]], c1 = cen[(F::GROUPED ? CEN : 0) + L.nb8[lane + 64]];
+      float dot;
+      if constexpr (F::GROUPED) {  // (n_j / PD) <q'_j, c_j[idx_j]> per half
+        const float d0 = wave_sum(qp[hh * KD + lane] * c0), d1 = wave_sum(qp[hh * KD + lane + 64] * c1);
+        dot = fmaf(h2f(L.nrec[NR_NORM] & 0xFFFFu) / (float)F::PD, d0, h2f(L.nrec[NR_NORM] >> 16) / (float)F::PD * d1);
+      } else {
+        const float di = wave_sum(fmaf(qp[hh * KD + lane], c0, qp[hh * KD + lane + 64] * c1));
+        dot = h2f(L.nrec[NR_NORM]) / (float)F::PD * di;
+      }
       if constexpr (F::QJL) {
         const float sg0 = (L.nrec[NR_SIGN + (lane >> 5)] >> (lane & 31)) & 1u ? 1.0f : -1.0f;
         const float sg1 = (L.nrec[NR_SIGN + 2 + (lane >> 5)] >> (lane & 31)) & 1u ? 1.0f : -1.0f;
@@ -1431,10 +1471,9 @@ tq_status decode_impl(const tq_key_config* cfg, const void* tables, const void* 
   if (v_bits != 2 && v_bits != 4) return TQ_ERR_UNSUPPORTED;
   if (v_group != 32) return TQ_ERR_UNSUPPORTED;
   if (q_dtype != TQ_F32 && q_dtype != TQ_BF16 && q_dtype != TQ_F16) return TQ_ERR_ARG;
-  // appending (tq_decode_attention_append): both new rows, MSE or PROD keys
+  // appending (tq_decode_attention_append): both new rows
   if (k_new || v_new) {
     if (!k_new || !v_new) return TQ_ERR_ARG;
-    if (P.mode != TQ_MODE_MSE && P.mode != TQ_MODE_PROD) return TQ_ERR_UNSUPPORTED;
     if (kv_dtype != TQ_F32 && kv_dtype != TQ_BF16 && kv_dtype != TQ_F16) return TQ_ERR_ARG;
     const uintptr_t al = kv_dtype == TQ_F32 ? 3 : 1;
     if (((uintptr_t)k_new & al) || ((uintptr_t)v_new & al)) return TQ_ERR_ARG;

@@ -287,11 +287,11 @@ def _dec_append(cfg, kn=FAKE, vn=FAKE, dt=L.TQ_BF16, ws=None):
 
 def test_append_decode_argument_errors():
     """tq_decode_attention_append: the new rows are checked on the host
-    before anything is launched (both present, MSE or PROD keys, a known
-    dtype, aligned to the element size)."""
+    before anything is launched (both present, a key format the decode
+    supports, a known dtype, aligned to the element size)."""
     prod = L.key_config(mode="prod", bits=3)
-    assert _dec_append(L.key_config(mode="grouped", bits_outlier=4, bits_normal=2)) == L.TQ_ERR_UNSUPPORTED
-    assert _dec_append(L.key_config(mode="grouped_prod", bits_outlier=3, bits_normal=2)) == L.TQ_ERR_UNSUPPORTED
+    assert _dec_append(L.key_config(mode="mse", bits=8)) == L.TQ_ERR_UNSUPPORTED   # no decode for 8-bit MSE
+    assert _dec_append(L.key_config(mode="grouped", bits_outlier=4, bits_normal=4)) == L.TQ_ERR_UNSUPPORTED
     assert _dec_append(prod, dt=7) == L.TQ_ERR_ARG
     assert _dec_append(prod, kn=FAKE + 1) == L.TQ_ERR_ARG           # bf16 rows on an odd address
     assert _dec_append(prod, vn=FAKE + 2, dt=L.TQ_F32) == L.TQ_ERR_ARG
@@ -313,7 +313,7 @@ def test_paged_append_decode_argument_errors():
     assert _dec_paged_append(prod, bt=None, ws=FAKE) == L.TQ_ERR_ARG
     assert _dec_paged_append(prod, kn=None, ws=FAKE) == L.TQ_ERR_ARG
     assert _dec_paged_append(prod, kn=FAKE + 1) == L.TQ_ERR_ARG
-    assert _dec_paged_append(L.key_config(mode="grouped", bits_outlier=4, bits_normal=2)) == L.TQ_ERR_UNSUPPORTED
+    assert _dec_paged_append(L.key_config(mode="mse", bits=8)) == L.TQ_ERR_UNSUPPORTED
 
 
 def _dec_paged(cfg, page_size=128, max_blocks=8, bt=FAKE, ws=None, n_pages=64):

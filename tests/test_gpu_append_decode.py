@@ -128,6 +128,12 @@ APPEND_CASES = [
     (dict(mode="mse", bits=3), 4),
     (dict(mode="mse", bits=4), 2),
     (dict(mode="mse", bits=6), 4),
+    (dict(mode="grouped", bits_outlier=4, bits_normal=2), 4),
+    (dict(mode="grouped", bits_outlier=3, bits_normal=2), 2),
+    (dict(mode="grouped", bits_outlier=2, bits_normal=2), 4),
+    (dict(mode="grouped", bits_outlier=4, bits_normal=1), 2),
+    (dict(mode="grouped_prod", bits_outlier=3, bits_normal=2), 2),
+    (dict(mode="grouped_prod", bits_outlier=4, bits_normal=1), 4),
 ]
 
 
@@ -151,32 +157,37 @@ def test_append_decode_two_quads_and_consecutive_steps():
     _run(dict(mode="prod", bits=3), 2, B=2, Hq=16, Hkv=2, max_ctx=1200, ctxs=[[900, 1], [901, 2], [902, 3]])
 
 
-def test_append_decode_rejects_grouped():
-    kw = dict(mode="grouped", bits_outlier=4, bits_normal=2)
+def test_append_decode_rejects_formats_without_a_decode():
+    kw = dict(mode="mse", bits=8)   # 8-bit MSE keys have no decode kernel (their tables exceed LDS)
     Tg = tq.Tables(L.key_config(seed=42, **kw), DEV)
     kp = tq.key_planes(Tg, 64, DEV)
     vp = tq.value_planes(2, 64, device=DEV)
     q = torch.zeros((1, 4, 128), dtype=torch.bfloat16, device=DEV)
     kn = torch.zeros((1, 1, 128), dtype=torch.bfloat16, device=DEV)
-    dec = tq.Decoder(Tg, 1, 4, 1, 64, 2, q.dtype, DEV)
-    with pytest.raises(L.TqError) as e:
+    with pytest.raises(L.TqError) as e:   # (already the decoder's workspace query)
+        dec = tq.Decoder(Tg, 1, 4, 1, 64, 2, q.dtype, DEV)
         dec(q, torch.tensor([10], dtype=torch.int32, device=DEV), kp, vp, k_new=kn, v_new=kn)
     assert e.value.status == L.TQ_ERR_UNSUPPORTED
 
 
-@pytest.mark.parametrize("kw", [dict(mode="prod", bits=3), dict(mode="mse", bits=4), dict(mode="mse", bits=1)],
-                         ids=["prod3", "mse4", "mse1"])
+@pytest.mark.parametrize("kw", [dict(mode="prod", bits=3), dict(mode="mse", bits=4), dict(mode="mse", bits=1),
+                                dict(mode="grouped", bits_outlier=4, bits_normal=2),
+                                dict(mode="grouped_prod", bits_outlier=3, bits_normal=2)],
+                         ids=["prod3", "mse4", "mse1", "grouped42", "grouped_prod32"])
 def test_append_decode_extreme_norms(kw):
     """New keys of norm about 1e-30 and 1e30 (fp32 sums of their squares would
-    underflow or overflow) and an all-zero key, appended inside the decode:
-    index and sign bytes as the oracle's, stored fp16 norms 0, +inf and 0 as
-    the oracle's rounding gives."""
+    underflow or overflow), keys whose halves differ by 60 decades and an
+    all-zero key, appended inside the decode: index and sign bytes as the
+    oracle's, stored fp16 norms 0, +inf (per half for the grouped modes) and
+    0 as the oracle's rounding gives."""
     B, Hkv, Hq, max_ctx = 8, 6, 24, 128
     n = B * Hkv
     base, _ = W.kv_rows(82, 1, n)
     x = base.astype(np.float64) / np.sqrt(128.0)
     x[:16] *= 1e-30
     x[16:32] *= 1e30
+    x[32:40, :64] *= 1e30
+    x[32:40, 64:] *= 1e-30
     x[-1] = 0.0
     xv, xb = W.to_bf16(x.astype(np.float32))
     vv, vb = W.kv_rows(82, 2, n)
@@ -191,7 +202,7 @@ def test_append_decode_extreme_norms(kw):
     rows = np.arange(n) * max_ctx + 69
     g = P.unpack_gpu_keys(To, {k: _np(v)[rows] for k, v in kp.items()})
     P.check_keys(xv.astype(np.float64), To, g)
-    nrm = g["norm16"].astype(np.float64)
-    assert np.all(nrm[:16] == 0) and np.all(np.isposinf(nrm[16:32])) and nrm[-1] == 0
+    nrm = g["norm16"].astype(np.float64).reshape(n, -1)
+    assert np.all(nrm[:16] == 0) and np.all(np.isposinf(nrm[16:32])) and np.all(nrm[-1] == 0)
     P.check_values(vn.view(n, 128).float().cpu().numpy(), 2, _np(vp["codes"])[rows], _np(vp["scale"])[rows],
                    _np(vp["zero"])[rows])
