@@ -34,6 +34,10 @@
 // fp16 normal range whatever the values' magnitude.  The chunk's (max, sum,
 // unnormalised output) goes to the workspace; a second kernel merges chunks
 // in a fixed order.
+// Appending (tq_decode_attention_append): the workgroup whose chunk ends with
+// the step's new token encodes that token's key and value in its prologue,
+// stores the record, and adds the token to its combine with a float32 score
+// computed from the record; the loop covers the chunk without it.
 #include <hip/hip_runtime.h>
 #include <hip/hip_fp16.h>
 
@@ -573,10 +577,12 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
   // to LDS; quad 0's workgroup stores it into the planes for later calls.
   // Nothing in this launch reads it back from global memory: its score and
   // value are taken from the encoding itself.
-  // Key ("tqlite" README 设计要点; difai.kr tutorial 算法概述): n = ||k||,
-  // y = H (sigma * k) / n, idx_j = number of boundaries <= y_j; PROD:
-  // r = y - c[idx], signs [S r >= 0] (S r on the MFMA below, as a fifth
-  // column next to the queries), rho = n ||r|| / sqrt(d).  Value
+  // Key ("tqlite" README 设计要点 and mode table; difai.kr tutorial 算法概述):
+  // n = ||k||, y = H (sigma * k) / n, idx_j = number of boundaries <= y_j
+  // (GROUPED: per half); PROD: r = y - c[idx], signs [S r >= 0] (S r on the
+  // MFMA below, as a fifth column next to the queries), rho = n ||r|| /
+  // sqrt(d); GROUPED_PROD: the signs of S w, w = concat_j (n_j / 8) r_j, and
+  // rho = ||w||.  Value
   // (bit-packing article, sections 二/三): per 32-channel group
   // s = fp16((max - min) / (2^VB - 1)), z = fp16(min),
   // code = clamp(rint((v - z) / s), 0, 2^VB - 1) in float32, 0 when s = 0.
