@@ -246,9 +246,10 @@ tq_status tq_append_kv(const tq_key_config* cfg, const void* tables, const void*
  *              t >= ctx_len[b] are not written).
  *   workspace  device scratch; with workspace == NULL the call only stores the
  *              required size in *workspace_bytes (host) and returns TQ_OK.
- * Supported: d = 128; PROD with bits 2..7 (index 1..6 bits); MSE with bits
- * 1..6 (indices of 4 to 6 bits are scored with one lookup table per
- * coordinate instead of one per byte; MSE 7..8-bit tables would exceed LDS);
+ * Supported: d = 128; PROD with bits 2..9 (index 1..8 bits); MSE with bits
+ * 1..8 (indices of 4 to 6 bits are scored with one lookup table per
+ * coordinate instead of one per byte; indices of 7 and 8 bits, whose tables
+ * would exceed LDS, directly as sum_j q'_j c[idx_j] in float32);
  * GROUPED with (outlier, normal) index bits (4, 2),
  * (3, 2), (2, 2) or (4, 1); GROUPED_PROD with (3, 2) or (4, 1) (the lookup
  * tables of (4, 2) plus signs exceed a workgroup's 160 KiB of LDS);
@@ -284,10 +285,12 @@ tq_status tq_decode_attention(const tq_key_config* cfg, const void* tables,
  *   k_new, v_new  [B][Hkv][d] of kv_dtype (TQ_F32, TQ_BF16, TQ_F16),
  *              contiguous, aligned to their element size; both non-NULL.
  *   other arguments as tq_decode_attention (same workspace size).
- * Supported: every key format tq_decode_attention supports (the grouped
- * modes encode each half with its own norm, transform and codebook, and
- * GROUPED_PROD sketches the halves' weighted residuals together, as
- * tq_encode_keys does); contiguous planes here, a paged pool with
+ * Supported: every key format tq_decode_attention supports except indices
+ * of 7 or 8 bits, which return TQ_ERR_UNSUPPORTED (the appending encoder
+ * keeps a codebook's boundaries one per lane of one wave, at most 64).  The
+ * grouped modes encode each half with its own norm, transform and codebook,
+ * and GROUPED_PROD sketches the halves' weighted residuals together, as
+ * tq_encode_keys does.  Contiguous planes here, a paged pool with
  * tq_decode_attention_paged_append.
  * Records of the appended tokens may differ from tq_encode_keys' where a
  * rotated coordinate lies within float32 rounding of a codebook boundary or

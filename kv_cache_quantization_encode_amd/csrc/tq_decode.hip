@@ -100,12 +100,16 @@ constexpr int CEN = 64;  // centroids staged per part (index widths up to 6 bits
 // QJL sign bytes.  Indices of 4 to 6 bits (one part) use one table per
 // coordinate instead of one per byte (kind 3): a byte table of 4-bit fields
 // would have 256 entries for each of 64 bytes (128 KiB), and a 5- or 6-bit
-// index fills a byte alone, so its table has 2^b entries.
+// index fills a byte alone, so its table has 2^b entries.  Indices of 7 and 8
+// bits (kind 4) would need 128 such tables of 128 or 256 entries, more than
+// LDS holds: they are scored directly, sum_j q'_j c[idx_j] in float32 with the
+// codebook in LDS, and have no table positions.
 template <int MODE, int B0, int B1>
 struct Fmt {
   static constexpr bool GROUPED = MODE == TQ_MODE_GROUPED || MODE == TQ_MODE_GROUPED_PROD;
   static constexpr bool QJL = MODE == TQ_MODE_PROD || MODE == TQ_MODE_GROUPED_PROD;
-  static constexpr bool COORD = !GROUPED && B0 >= 4;  // per-coordinate tables for the index
+  static constexpr bool DIRECT = !GROUPED && B0 >= 7;  // index scored directly (no tables)
+  static constexpr bool COORD = !GROUPED && B0 >= 4 && !DIRECT;  // per-coordinate tables for the index
   static constexpr int NPART = GROUPED ? 2 : 1;
   static constexpr int PD = KD / NPART;  // coordinates per part
   static constexpr int W0 = width_of(B0);
@@ -117,13 +121,18 @@ struct Fmt {
   static constexpr int KWORDS = (IDXB + SP) / 4;         // idx + sign words per key
   static constexpr int NC = NPART + (QJL ? 1 : 0);       // table classes
   // kind of class c: 0 / 1 index bytes of part 0 / 1, 2 sign bytes, 3 index
-  // coordinates of part 0 (one table per coordinate)
-  static constexpr int kind(int c) { return c == 0 ? (COORD ? 3 : 0) : c == 2 ? 2 : (GROUPED ? 1 : 2); }
+  // coordinates of part 0 (one table per coordinate), 4 index coordinates of
+  // part 0 scored directly (no table)
+  static constexpr int kind(int c) {
+    return c == 0 ? (DIRECT ? 4 : COORD ? 3 : 0) : c == 2 ? 2 : (GROUPED ? 1 : 2);
+  }
   // positions (tables) of class c and the key bytes it spans
-  static constexpr int npos(int c) { return kind(c) == 3 ? PD : kind(c) == 0 ? IP0 : kind(c) == 1 ? IP1 : SP; }
-  static constexpr int nbytes(int c) { return kind(c) == 3 ? IP0 : npos(c); }
+  static constexpr int npos(int c) {
+    return kind(c) == 4 ? 0 : kind(c) == 3 ? PD : kind(c) == 0 ? IP0 : kind(c) == 1 ? IP1 : SP;
+  }
+  static constexpr int nbytes(int c) { return kind(c) >= 3 ? IP0 : npos(c); }
   static constexpr int stride(int c) {
-    return kind(c) == 3 ? (1 << B0) : kind(c) == 0 ? stride_of(B0) : kind(c) == 1 ? stride_of(B1) : 256;
+    return kind(c) == 4 ? 1 : kind(c) == 3 ? (1 << B0) : kind(c) == 0 ? stride_of(B0) : kind(c) == 1 ? stride_of(B1) : 256;
   }
   static constexpr int kbyte(int c) { return c == 0 ? 0 : kbyte(c - 1) + nbytes(c - 1); }  // first key byte
   static constexpr int pos0(int c) { return c == 0 ? 0 : pos0(c - 1) + npos(c - 1); }     // first position
@@ -137,6 +146,8 @@ struct Fmt {
   // coordinates one position of the index class of part p covers (table range)
   static constexpr int cpb(int p) { return COORD ? 1 : 8 / (p ? W1 : W0); }
   static constexpr int ENTRIES = ent(NC - 1) + npos(NC - 1) * stride(NC - 1);
+  // the table region also holds the workgroup's end sums (NS x QH x (6 + KD) floats)
+  static constexpr int LUT_ENTRIES = ENTRIES > 2176 ? ENTRIES : 2176;
   static constexpr int POSITIONS = pos0(NC - 1) + npos(NC - 1);
   static constexpr int HPOS0 = COORD ? PD : 0;  // first position built from nibble halves
   static_assert(IP0 % CHAIN == 0 && IP1 % CHAIN == 0 && SP % CHAIN == 0, "whole chains per class");
@@ -149,7 +160,7 @@ struct Fmt {
 template <int MODE, int B0, int B1, int VB>
 struct Lds {
   using F = Fmt<MODE, B0, B1>;
-  uint64_t lut[F::ENTRIES];
+  uint64_t lut[F::LUT_ENTRIES];
   float qp[(QH + 1) * KD];  // rotated queries, then (appending) the new key's residual
   float qs[QH * KD];
   uint32_t nrec[NREC];     // appending: the new token's record (see NR_*)
@@ -158,6 +169,8 @@ struct Lds {
   float xnew[QH];          // appending: its score per head (log2 softmax units)
   uint32_t ring[F::RING_BYTES / 4];
   float cen[2 * CEN];
+  float c8[F::DIRECT ? 1 << B0 : 1];       // DIRECT: the codebook
+  float qT[F::DIRECT ? KD * QH : 4];       // DIRECT: rotated queries as [coordinate][head]
   float rng[3][QH];    // largest byte range of each class and head (float bits, atomicMax)
   float offi[2][QH];   // index classes: sum over coordinates of the smallest term
   float sgp[8][QH];    // sign class: sum of |S q'| over each 16-row tile
@@ -561,6 +574,9 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
     const int part = tid / CEN, k = tid % CEN;
     cen[tid] = part < n_parts && k < (part ? lev1 : lev0) ? (part ? cent1 : cent0)[k] : 0.0f;
   }
+  if constexpr (F::DIRECT) {
+    if (tid < (1 << B0)) L.c8[tid] = tid < lev0 ? cent0[tid] : 0.0f;
+  }
   if (F::QJL && tid < QH) L.rng[F::NC - 1][tid] = 0.0f;
   if (tid < NW / 2) {
     L.prod[tid] = 0;
@@ -765,6 +781,10 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
     });
     qp[wave * KD + lane] = x0;
     qp[wave * KD + lane + 64] = x1;
+    if constexpr (F::DIRECT) {
+      L.qT[lane * QH + wave] = x0;
+      L.qT[(lane + 64) * QH + wave] = x1;
+    }
     constexpr int CPB0 = F::cpb(0), CPB1 = F::cpb(1);
     const float g0 = group_sum<CPB0>(fabsf(x0));
     const float lo0 = fminf(x0 * cmin0, x0 * cmax0);
@@ -1005,7 +1025,9 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
     const int c = tid >> 2, hh = tid & 3;
     const int kind = F::kind(c);
     float off;
-    if (kind == 2) {
+    if (kind == 4) {
+      off = 0.0f;  // (the direct class sums q'_j c[idx_j] as they are)
+    } else if (kind == 2) {
       off = 0.0f;
       for (int w = 0; w < 8; ++w) off -= L.sgp[w][hh];
     } else {
@@ -1014,7 +1036,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
     // q' holds sqrt(PD) Pi q (per half when GROUPED): the sign class's
     // rho sqrt(pi/2) / m <S Pi q, .> is rho sqrt(pi/2) / (m sqrt(PD)) <S q', .>
     const float mul = kind == 2 ? SQRT_HALF_PI / ((float)KD * sqrtf((float)F::PD)) : 1.0f / (float)F::PD;
-    const float unit = L.rng[c][hh] / F::EMAX;
+    const float unit = kind == 4 ? 1.0f : L.rng[c][hh] / F::EMAX;
     L.uu[c][hh] = mul * unit * xscale;
     L.oo[c][hh] = mul * off * xscale;
   }
@@ -1023,6 +1045,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
   const half2_t e10 = {(_Float16)1.0f, (_Float16)0.0f}, e01 = {(_Float16)0.0f, (_Float16)1.0f};
   float* red = (float*)smem;  // [NS][QH][2 + 4 + KD], over the tables once every wave is done
   constexpr int RS = 2 + 4 + KD;
+  static_assert(sizeof(L.lut) >= NS * QH * RS * sizeof(float), "the end sums fit over the tables");
   float* mine = red + pw * QH * RS;
   // The two kinds of waves run separate loops (one barrier after each), so
   // neither keeps the other's registers live.
@@ -1119,9 +1142,27 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
             reduce(bb, E);
             __builtin_amdgcn_sched_barrier(0);
           });
+          // DIRECT: the index class as sum_j q'_j c[idx_j] in float32, the
+          // centroid gathered from LDS by the index byte, the four heads' q'_j
+          // one broadcast read
+          float accf[QH] = {0.0f, 0.0f, 0.0f, 0.0f};
+          if constexpr (F::DIRECT) {
+            const float4* qT4 = (const float4*)L.qT;
+            const unsigned char* c8b = (const unsigned char*)L.c8;
+#pragma unroll
+            for (int j = 0; j < KD; ++j) {
+              const uint32_t off = ((kd.kw[j >> 2] >> (8 * (j & 3))) & 0xFFu) * 4u;
+              const float c = *(const float*)(c8b + off);
+              const float4 qv = qT4[j];
+              accf[0] = fmaf(qv.x, c, accf[0]);
+              accf[1] = fmaf(qv.y, c, accf[1]);
+              accf[2] = fmaf(qv.z, c, accf[2]);
+              accf[3] = fmaf(qv.w, c, accf[3]);
+            }
+          }
 #pragma unroll
           for (int hh = 0; hh < QH; ++hh) {
-            float v = m0 * fmaf((float)acc[0][hh], UU[0][hh], OO[0][hh]);
+            float v = F::DIRECT ? m0 * (accf[hh] * UU[0][hh]) : m0 * fmaf((float)acc[0][hh], UU[0][hh], OO[0][hh]);
             if constexpr (F::NC > 1) v = fmaf(m1, fmaf((float)acc[1][hh], UU[1][hh], OO[1][hh]), v);
             if constexpr (F::NC > 2) v = fmaf(m2, fmaf((float)acc[2][hh], UU[2][hh], OO[2][hh]), v);
             x[hh] = valid ? v : -INFINITY;  // log2 softmax units
@@ -1422,7 +1463,7 @@ bool supported(const tq::Parts& P) {
     const int b0 = P.part_bits[0], b1 = P.part_bits[1];
     return (b0 == 4 && b1 == 2) || (b0 == 2 && b1 == 2) || (b0 == 3 && b1 == 2) || (b0 == 4 && b1 == 1);
   }
-  return P.part_bits[0] >= 1 && P.part_bits[0] <= 6;
+  return P.part_bits[0] >= 1 && P.part_bits[0] <= 8;
 }
 
 hipError_t dispatch(const tq::Parts& P, int vb, const DecArgs& a, dim3 grid, hipStream_t s) {
@@ -1433,7 +1474,9 @@ hipError_t dispatch(const tq::Parts& P, int vb, const DecArgs& a, dim3 grid, hip
       case 3: return launch_vb<TQ_MODE_PROD, 3, 0>(vb, a, grid, s);
       case 4: return launch_vb<TQ_MODE_PROD, 4, 0>(vb, a, grid, s);
       case 5: return launch_vb<TQ_MODE_PROD, 5, 0>(vb, a, grid, s);
-      default: return launch_vb<TQ_MODE_PROD, 6, 0>(vb, a, grid, s);
+      case 6: return launch_vb<TQ_MODE_PROD, 6, 0>(vb, a, grid, s);
+      case 7: return launch_vb<TQ_MODE_PROD, 7, 0>(vb, a, grid, s);
+      default: return launch_vb<TQ_MODE_PROD, 8, 0>(vb, a, grid, s);
     }
   }
   if (P.mode == TQ_MODE_MSE) {
@@ -1443,7 +1486,9 @@ hipError_t dispatch(const tq::Parts& P, int vb, const DecArgs& a, dim3 grid, hip
       case 3: return launch_vb<TQ_MODE_MSE, 3, 0>(vb, a, grid, s);
       case 4: return launch_vb<TQ_MODE_MSE, 4, 0>(vb, a, grid, s);
       case 5: return launch_vb<TQ_MODE_MSE, 5, 0>(vb, a, grid, s);
-      default: return launch_vb<TQ_MODE_MSE, 6, 0>(vb, a, grid, s);
+      case 6: return launch_vb<TQ_MODE_MSE, 6, 0>(vb, a, grid, s);
+      case 7: return launch_vb<TQ_MODE_MSE, 7, 0>(vb, a, grid, s);
+      default: return launch_vb<TQ_MODE_MSE, 8, 0>(vb, a, grid, s);
     }
   }
   const int b0 = P.part_bits[0], b1 = P.part_bits[1];
@@ -1477,9 +1522,11 @@ tq_status decode_impl(const tq_key_config* cfg, const void* tables, const void* 
   if (v_bits != 2 && v_bits != 4) return TQ_ERR_UNSUPPORTED;
   if (v_group != 32) return TQ_ERR_UNSUPPORTED;
   if (q_dtype != TQ_F32 && q_dtype != TQ_BF16 && q_dtype != TQ_F16) return TQ_ERR_ARG;
-  // appending (tq_decode_attention_append): both new rows
+  // appending (tq_decode_attention_append): both new rows; not for indices
+  // of 7 or 8 bits (their codebooks exceed the one-wave encoder's lanes)
   if (k_new || v_new) {
     if (!k_new || !v_new) return TQ_ERR_ARG;
+    if (P.mode != TQ_MODE_GROUPED && P.mode != TQ_MODE_GROUPED_PROD && P.part_bits[0] >= 7) return TQ_ERR_UNSUPPORTED;
     if (kv_dtype != TQ_F32 && kv_dtype != TQ_BF16 && kv_dtype != TQ_F16) return TQ_ERR_ARG;
     const uintptr_t al = kv_dtype == TQ_F32 ? 3 : 1;
     if (((uintptr_t)k_new & al) || ((uintptr_t)v_new & al)) return TQ_ERR_ARG;

@@ -272,9 +272,9 @@ def test_decode_argument_errors():
     assert _dec(prod, vb=3) == L.TQ_ERR_UNSUPPORTED
     assert _dec(prod, vg=64) == L.TQ_ERR_UNSUPPORTED
     assert _dec(prod, wsb=None) == L.TQ_ERR_ARG
-    assert _dec(L.key_config(mode="mse", bits=8)) == L.TQ_ERR_UNSUPPORTED
-    assert _dec(L.key_config(mode="mse", bits=7)) == L.TQ_ERR_UNSUPPORTED    # 128 x 128 entries: over LDS
-    assert _dec(L.key_config(mode="prod", bits=8)) == L.TQ_ERR_UNSUPPORTED
+    for cfg in (L.key_config(mode="mse", bits=8), L.key_config(mode="mse", bits=7),
+                L.key_config(mode="prod", bits=8), L.key_config(mode="prod", bits=9)):
+        assert _dec(cfg) != L.TQ_ERR_UNSUPPORTED                   # 7- and 8-bit indices: scored directly
     assert _dec(L.key_config(mode="grouped", bits_outlier=4, bits_normal=4)) == L.TQ_ERR_UNSUPPORTED
 
 
@@ -288,9 +288,10 @@ def _dec_append(cfg, kn=FAKE, vn=FAKE, dt=L.TQ_BF16, ws=None):
 def test_append_decode_argument_errors():
     """tq_decode_attention_append: the new rows are checked on the host
     before anything is launched (both present, a key format the decode
-    supports, a known dtype, aligned to the element size)."""
+    supports with indices of at most 6 bits, a known dtype, aligned to the
+    element size)."""
     prod = L.key_config(mode="prod", bits=3)
-    assert _dec_append(L.key_config(mode="mse", bits=8)) == L.TQ_ERR_UNSUPPORTED   # no decode for 8-bit MSE
+    assert _dec_append(L.key_config(mode="mse", bits=8)) == L.TQ_ERR_UNSUPPORTED   # no appending 8-bit encoder
     assert _dec_append(L.key_config(mode="grouped", bits_outlier=4, bits_normal=4)) == L.TQ_ERR_UNSUPPORTED
     assert _dec_append(prod, dt=7) == L.TQ_ERR_ARG
     assert _dec_append(prod, kn=FAKE + 1) == L.TQ_ERR_ARG           # bf16 rows on an odd address

@@ -157,15 +157,17 @@ def test_append_decode_two_quads_and_consecutive_steps():
     _run(dict(mode="prod", bits=3), 2, B=2, Hq=16, Hkv=2, max_ctx=1200, ctxs=[[900, 1], [901, 2], [902, 3]])
 
 
-def test_append_decode_rejects_formats_without_a_decode():
-    kw = dict(mode="mse", bits=8)   # 8-bit MSE keys have no decode kernel (their tables exceed LDS)
+def test_append_decode_rejects_8bit_indices():
+    """8-bit MSE keys decode (scored directly) but are not appended inside the
+    decode: the one-wave encoder holds at most 64 boundaries in its lanes."""
+    kw = dict(mode="mse", bits=8)
     Tg = tq.Tables(L.key_config(seed=42, **kw), DEV)
     kp = tq.key_planes(Tg, 64, DEV)
     vp = tq.value_planes(2, 64, device=DEV)
     q = torch.zeros((1, 4, 128), dtype=torch.bfloat16, device=DEV)
     kn = torch.zeros((1, 1, 128), dtype=torch.bfloat16, device=DEV)
-    with pytest.raises(L.TqError) as e:   # (already the decoder's workspace query)
-        dec = tq.Decoder(Tg, 1, 4, 1, 64, 2, q.dtype, DEV)
+    dec = tq.Decoder(Tg, 1, 4, 1, 64, 2, q.dtype, DEV)
+    with pytest.raises(L.TqError) as e:
         dec(q, torch.tensor([10], dtype=torch.int32, device=DEV), kp, vp, k_new=kn, v_new=kn)
     assert e.value.status == L.TQ_ERR_UNSUPPORTED
 

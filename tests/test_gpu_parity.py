@@ -255,6 +255,11 @@ DEC_CASES = [
     (dict(mode="prod", bits=5), 4),
     (dict(mode="prod", bits=6), 2),
     (dict(mode="prod", bits=7), 4),
+    # indices of 7 and 8 bits: scored directly (float32, the codebook in LDS)
+    (dict(mode="mse", bits=8), 2),
+    (dict(mode="mse", bits=7), 4),
+    (dict(mode="prod", bits=8), 4),
+    (dict(mode="prod", bits=9), 2),
 ]
 
 
