@@ -1401,14 +1401,26 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecArgs a) {
 // out[b][h][:] = sum_s O_s 2^(M_s - M) / sum_s L_s 2^(M_s - M), in split order.
 // A NaN sum (tables that do not match the kernel's format) makes the row NaN.
 // The largest M_s is found by the block's threads together (a strided share
-// each, then a reduction); the weighted sums run in split order, unrolled so
-// that several splits' partials are in flight at once (a long context has
-// tens of splits per head).
+// each, then a reduction); the weighted sums run in split order, the first
+// splits' partials already loaded with the maxima, the rest unrolled so that
+// several splits' partials are in flight at once (a long context has tens of
+// splits per head).
 __global__ __launch_bounds__(KD) void merge_kernel(const float* part, int n_split, float* out,
                                                    float* lse) {
   static_assert(KD == 128, "two waves per block");
   const int bh = blockIdx.x, j = threadIdx.x;
   const float* p = part + (long long)bh * n_split * PART;
+  // the first PRE splits' (max, sum, output element) go out with the loads
+  // of the maxima, so that a short merge reads the partials in one round
+  constexpr int PRE = 8;
+  float pm[PRE], pl[PRE], po[PRE];
+#pragma unroll
+  for (int s = 0; s < PRE; ++s) {
+    const bool in = s < n_split;
+    pm[s] = in ? p[s * PART] : -INFINITY;
+    pl[s] = in ? p[s * PART + 1] : 0.0f;
+    po[s] = in ? p[s * PART + 2 + j] : 0.0f;
+  }
   __shared__ float s_max[2];
   __shared__ int s_bad[2];
   float M = -INFINITY;
@@ -1428,8 +1440,16 @@ __global__ __launch_bounds__(KD) void merge_kernel(const float* part, int n_spli
   bad = s_bad[0] | s_bad[1];
   float Ls = 0.0f, O = 0.0f;
   if (M != -INFINITY) {
+#pragma unroll
+    for (int s = 0; s < PRE; ++s) {
+      if (s < n_split) {
+        const float f = pm[s] == -INFINITY ? 0.0f : exp2f(pm[s] - M);
+        Ls = fmaf(pl[s], f, Ls);
+        O = fmaf(po[s], f, O);
+      }
+    }
 #pragma unroll 8
-    for (int s = 0; s < n_split; ++s) {
+    for (int s = PRE; s < n_split; ++s) {
       const float* r = p + s * PART;
       const float f = r[0] == -INFINITY ? 0.0f : exp2f(r[0] - M);
       Ls = fmaf(r[1], f, Ls);
