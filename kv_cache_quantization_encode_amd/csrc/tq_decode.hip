@@ -157,8 +157,12 @@ struct Fmt {
   static constexpr int RING_BYTES = RING_BYTES_W > HALF_BYTES ? RING_BYTES_W : HALF_BYTES;
 };
 
+// 16-byte aligned, so that the compiler can read and write the float4 /
+// 16-byte fields below (the MFMA operands in the ring, per-head factors,
+// staged queries) with single ds_read_b128 / ds_write_b128 instructions; at
+// the 8-byte alignment of its uint64 tables it splits them into pairs.
 template <int MODE, int B0, int B1, int VB>
-struct Lds {
+struct alignas(16) Lds {
   using F = Fmt<MODE, B0, B1>;
   uint64_t lut[F::LUT_ENTRIES];
   float qp[(QH + 1) * KD];  // rotated queries, then (appending) the new key's residual
@@ -169,8 +173,6 @@ struct Lds {
   float xnew[QH];          // appending: its score per head (log2 softmax units)
   uint32_t ring[F::RING_BYTES / 4];
   float cen[2 * CEN];
-  float c8[F::DIRECT ? 1 << B0 : 1];       // DIRECT: the codebook
-  float qT[F::DIRECT ? KD * QH : 4];       // DIRECT: rotated queries as [coordinate][head]
   float rng[3][QH];    // largest byte range of each class and head (float bits, atomicMax)
   float offi[2][QH];   // index classes: sum over coordinates of the smallest term
   float sgp[8][QH];    // sign class: sum of |S q'| over each 16-row tile
@@ -181,6 +183,9 @@ struct Lds {
   int prod[NW / 2];    // rounds the score wave of each pair has published
   int cons[NW / 2];    // rounds the p.V wave of each pair has finished
   int pages[PAGE_CACHE];  // block-table entries of this workgroup's token range (paged cache)
+  // last, so that the fields above keep their offsets in every format
+  alignas(16) float qT[F::DIRECT ? KD * QH : 4];  // DIRECT: rotated queries as [coordinate][head]
+  float c8[F::DIRECT ? 1 << B0 : 4];              // DIRECT: the codebook
 };
 
 struct DecArgs {
