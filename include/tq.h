@@ -54,7 +54,7 @@ extern "C" {
 typedef enum {
   TQ_OK = 0,
   TQ_ERR_ARG = -1,          /* NULL / misaligned pointer, bad size or shape        */
-  TQ_ERR_UNSUPPORTED = -2,  /* valid in principle, not implemented by this build   */
+  TQ_ERR_UNSUPPORTED = -2,  /* valid in principle, not implemented by this library */
   TQ_ERR_WORKSPACE = -3,    /* workspace missing or smaller than required          */
   TQ_ERR_HIP = -4           /* a HIP runtime call failed (no device, launch error) */
 } tq_status;
